@@ -1,0 +1,233 @@
+/*
+ * gdn_oracle.c -- plain, slow, float64 CPU oracle of the Gated DeltaNet core.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load or run this code.  It shares nothing
+ * with the GPU library: no headers, no helpers, no constants.
+ *
+ * Every input is widened exactly to double by the caller; every step below is
+ * carried out in double, token by token, with no chunking, blocking or
+ * reordering beyond what the formulas state.  Build flags: no fast-math and
+ * -ffp-contract=off, so each multiply and add rounds as written.
+ *
+ * Sources (the pages this follows):
+ *  - dingfen.github.io, "从 Full Attention 到 Gated DeltaNet", sections 9-10:
+ *    the decay gate g = -exp(A_log) * softplus(a + dt_bias), alpha = exp(g),
+ *    softplus(x) = log(1 + e^x), write strength beta = sigmoid(b), read-out
+ *    y_t = S_t^T q_t.
+ *  - rainlin-net.pages.dev "Qwen3.5", section "GDN详解": the gated delta rule
+ *    S_t = alpha_t S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T, expanded
+ *    into five steps: decay, read at address k, scaled difference, rank-one
+ *    write, read-out with q.  The state is stored here as S[d_k][d_v] (the
+ *    indexing of that page's eager loop: read S^T k, write k delta^T, output
+ *    S^T q), i.e. the transpose of the d_v x d_k matrix in the formula.
+ *  - zhichai.net "Gated DeltaNet-2", sections "Gated Delta Rule-2" and
+ *    "退化兼容性": decoupled erase gate b_t (per key channel) and write gate
+ *    w_t (per value channel), channel-wise decay D_t:
+ *    S_t = (I - k_t e_t^T) D_t S_{t-1} + k_t z_t^T, e = b (.) k, z = w (.) v,
+ *    expanded as Sbar = D S, r = Sbar^T e, S = Sbar + k (z - r)^T.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* softplus(x) = log(1 + e^x) (dingfen page, section 9), evaluated without
+ * overflow: for x > 0, log(1 + e^x) = x + log(1 + e^-x). */
+double oracle_softplus(double x) {
+    if (x > 0.0) return x + log1p(exp(-x));
+    return log1p(exp(x));
+}
+
+/* sigmoid(x) = 1 / (1 + e^-x) (dingfen page, section 10: beta = sigma(b)). */
+double oracle_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* Gate preparation for GDN (dingfen page sections 9-10; rainlin page module
+ * code): for n token rows of Hv value heads,
+ *   g[r,h]    = -exp(A_log[h]) * softplus(a[r,h] + dt_bias[h])   (log decay)
+ *   beta[r,h] = sigmoid(b[r,h]).
+ * One decay and one write strength per (token, value head). */
+void oracle_gdn_gates(long n, int Hv, const double *a, const double *b,
+                      const double *A_log, const double *dt_bias,
+                      double *g, double *beta) {
+    for (long r = 0; r < n; ++r)
+        for (int h = 0; h < Hv; ++h) {
+            long i = r * Hv + h;
+            g[i] = -exp(A_log[h]) * oracle_softplus(a[i] + dt_bias[h]);
+            beta[i] = oracle_sigmoid(b[i]);
+        }
+}
+
+/* The gated delta rule, token by token (rainlin page, five-step form).
+ *   q, k : [B,T,Hk,Dk]   v, out : [B,T,Hv,Dv]   g, beta : [B,T,Hv]
+ *   S0, ST : [B,Hv,Dk,Dv] (S0 may be NULL: zero initial state; ST may be NULL)
+ * Value head hv reads key/query head hv / (Hv/Hk).  For every token:
+ *   S <- alpha S;  kv = S^T k;  delta = beta (v - kv);  S <- S + k delta^T;
+ *   out = scale * S^T q. */
+void oracle_gdn_core(int B, int T, int Hk, int Hv, int Dk, int Dv,
+                     const double *q, const double *k, const double *v,
+                     const double *g, const double *beta, double scale,
+                     const double *S0, double *out, double *ST) {
+    const int grp = Hv / Hk;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int u = 0; u < B * Hv; ++u) {
+        const int bb = u / Hv, hv = u % Hv, hk = hv / grp;
+        double *S = (double *)malloc(sizeof(double) * (size_t)Dk * Dv);
+        double *kv = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *d = (double *)malloc(sizeof(double) * (size_t)Dv);
+        if (S0) memcpy(S, S0 + (size_t)u * Dk * Dv, sizeof(double) * (size_t)Dk * Dv);
+        else memset(S, 0, sizeof(double) * (size_t)Dk * Dv);
+        for (int t = 0; t < T; ++t) {
+            const double *qt = q + (((size_t)bb * T + t) * Hk + hk) * Dk;
+            const double *kt = k + (((size_t)bb * T + t) * Hk + hk) * Dk;
+            const double *vt = v + (((size_t)bb * T + t) * Hv + hv) * Dv;
+            const size_t gi = ((size_t)bb * T + t) * Hv + hv;
+            const double alpha = exp(g[gi]);
+            const double be = beta[gi];
+            /* 1. decay the old state */
+            for (int i = 0; i < Dk; ++i)
+                for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] *= alpha;
+            /* 2. read what the memory holds at address k */
+            for (int j = 0; j < Dv; ++j) kv[j] = 0.0;
+            for (int i = 0; i < Dk; ++i)
+                for (int j = 0; j < Dv; ++j) kv[j] += S[(size_t)i * Dv + j] * kt[i];
+            /* 3. scaled difference to the target */
+            for (int j = 0; j < Dv; ++j) d[j] = be * (vt[j] - kv[j]);
+            /* 4. rank-one write at address k */
+            for (int i = 0; i < Dk; ++i)
+                for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] += kt[i] * d[j];
+            /* 5. read-out with the query, after the write */
+            double *ot = out + (((size_t)bb * T + t) * Hv + hv) * Dv;
+            for (int j = 0; j < Dv; ++j) ot[j] = 0.0;
+            for (int i = 0; i < Dk; ++i)
+                for (int j = 0; j < Dv; ++j) ot[j] += S[(size_t)i * Dv + j] * qt[i];
+            for (int j = 0; j < Dv; ++j) ot[j] *= scale;
+        }
+        if (ST) memcpy(ST + (size_t)u * Dk * Dv, S, sizeof(double) * (size_t)Dk * Dv);
+        free(S);
+        free(kv);
+        free(d);
+    }
+}
+
+/* GDN forward from raw gate logits: oracle_gdn_gates followed by
+ * oracle_gdn_core.  a, b : [B,T,Hv]; A_log, dt_bias : [Hv]. */
+void oracle_gdn_fwd(int B, int T, int Hk, int Hv, int Dk, int Dv,
+                    const double *q, const double *k, const double *v,
+                    const double *a, const double *b, const double *A_log,
+                    const double *dt_bias, double scale, const double *S0,
+                    double *out, double *ST) {
+    const size_t n = (size_t)B * T * Hv;
+    double *g = (double *)malloc(sizeof(double) * (n ? n : 1));
+    double *beta = (double *)malloc(sizeof(double) * (n ? n : 1));
+    oracle_gdn_gates((long)B * T, Hv, a, b, A_log, dt_bias, g, beta);
+    oracle_gdn_core(B, T, Hk, Hv, Dk, Dv, q, k, v, g, beta, scale, S0, out, ST);
+    free(g);
+    free(beta);
+}
+
+/* Gate preparation for Gated DeltaNet-2.  The zhichai page fixes only that the
+ * decay is channel-wise and that the erase gate lies in [0,1]^{d_k} and the
+ * write gate in [0,1]^{d_v}; the forms below are this oracle's reading: the GDN
+ * decay parametrisation per key channel (without dt_bias) and sigmoids of
+ * raw logits.  Per (token row r, value head h, key channel c)
+ *   g[r,h,c]  = -exp(A_log[h,c]) * softplus(a[r,h,c])   (channel-wise log decay)
+ *   eb[r,h,c] = sigmoid(erase[r,h,c])                     (erase gate b_t)
+ * and per value channel j: wb[r,h,j] = sigmoid(write[r,h,j]) (write gate w_t). */
+void oracle_gdn2_gates(long n, int Hv, int Dk, int Dv, const double *a,
+                       const double *A_log, const double *erase,
+                       const double *write, double *g, double *eb, double *wb) {
+    for (long r = 0; r < n; ++r)
+        for (int h = 0; h < Hv; ++h) {
+            for (int c = 0; c < Dk; ++c) {
+                size_t i = ((size_t)r * Hv + h) * Dk + c;
+                g[i] = -exp(A_log[(size_t)h * Dk + c]) * oracle_softplus(a[i]);
+                eb[i] = oracle_sigmoid(erase[i]);
+            }
+            for (int j = 0; j < Dv; ++j) {
+                size_t i = ((size_t)r * Hv + h) * Dv + j;
+                wb[i] = oracle_sigmoid(write[i]);
+            }
+        }
+}
+
+/* Gated Delta Rule-2, token by token (zhichai page, expanded form):
+ *   D = exp(g) (per key channel);  Sbar = diag(D) S;  e = eb (.) k;
+ *   z = wb (.) v;  r = Sbar^T e;  S = Sbar + k (z - r)^T;  out = scale S^T q.
+ *   g, eb : [B,T,Hv,Dk]   wb : [B,T,Hv,Dv]; other layouts as oracle_gdn_core. */
+void oracle_gdn2_core(int B, int T, int Hk, int Hv, int Dk, int Dv,
+                      const double *q, const double *k, const double *v,
+                      const double *g, const double *eb, const double *wb,
+                      double scale, const double *S0, double *out, double *ST) {
+    const int grp = Hv / Hk;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int u = 0; u < B * Hv; ++u) {
+        const int bb = u / Hv, hv = u % Hv, hk = hv / grp;
+        double *S = (double *)malloc(sizeof(double) * (size_t)Dk * Dv);
+        double *e = (double *)malloc(sizeof(double) * (size_t)Dk);
+        double *r = (double *)malloc(sizeof(double) * (size_t)Dv);
+        if (S0) memcpy(S, S0 + (size_t)u * Dk * Dv, sizeof(double) * (size_t)Dk * Dv);
+        else memset(S, 0, sizeof(double) * (size_t)Dk * Dv);
+        for (int t = 0; t < T; ++t) {
+            const double *qt = q + (((size_t)bb * T + t) * Hk + hk) * Dk;
+            const double *kt = k + (((size_t)bb * T + t) * Hk + hk) * Dk;
+            const double *vt = v + (((size_t)bb * T + t) * Hv + hv) * Dv;
+            const size_t ci = (((size_t)bb * T + t) * Hv + hv) * Dk;
+            const size_t vi = (((size_t)bb * T + t) * Hv + hv) * Dv;
+            /* Sbar = diag(D) S: row i of S (key channel i) decays by exp(g_i) */
+            for (int i = 0; i < Dk; ++i) {
+                const double Di = exp(g[ci + i]);
+                for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] *= Di;
+            }
+            /* e = erase gate (.) k */
+            for (int i = 0; i < Dk; ++i) e[i] = eb[ci + i] * kt[i];
+            /* r = Sbar^T e */
+            for (int j = 0; j < Dv; ++j) r[j] = 0.0;
+            for (int i = 0; i < Dk; ++i)
+                for (int j = 0; j < Dv; ++j) r[j] += S[(size_t)i * Dv + j] * e[i];
+            /* S = Sbar + k (z - r)^T with z = write gate (.) v */
+            for (int j = 0; j < Dv; ++j) r[j] = wb[vi + j] * vt[j] - r[j];
+            for (int i = 0; i < Dk; ++i)
+                for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] += kt[i] * r[j];
+            /* read-out after the update */
+            double *ot = out + (((size_t)bb * T + t) * Hv + hv) * Dv;
+            for (int j = 0; j < Dv; ++j) ot[j] = 0.0;
+            for (int i = 0; i < Dk; ++i)
+                for (int j = 0; j < Dv; ++j) ot[j] += S[(size_t)i * Dv + j] * qt[i];
+            for (int j = 0; j < Dv; ++j) ot[j] *= scale;
+        }
+        if (ST) memcpy(ST + (size_t)u * Dk * Dv, S, sizeof(double) * (size_t)Dk * Dv);
+        free(S);
+        free(e);
+        free(r);
+    }
+}
+
+/* Gated DeltaNet-2 forward from raw logits: oracle_gdn2_gates + core.
+ * a, erase : [B,T,Hv,Dk]; write : [B,T,Hv,Dv]; A_log : [Hv,Dk]. */
+void oracle_gdn2_fwd(int B, int T, int Hk, int Hv, int Dk, int Dv,
+                     const double *q, const double *k, const double *v,
+                     const double *a, const double *A_log, const double *erase,
+                     const double *write, double scale, const double *S0,
+                     double *out, double *ST) {
+    const size_t nk = (size_t)B * T * Hv * Dk, nv = (size_t)B * T * Hv * Dv;
+    double *g = (double *)malloc(sizeof(double) * (nk ? nk : 1));
+    double *eb = (double *)malloc(sizeof(double) * (nk ? nk : 1));
+    double *wb = (double *)malloc(sizeof(double) * (nv ? nv : 1));
+    oracle_gdn2_gates((long)B * T, Hv, Dk, Dv, a, A_log, erase, write, g, eb, wb);
+    oracle_gdn2_core(B, T, Hk, Hv, Dk, Dv, q, k, v, g, eb, wb, scale, S0, out, ST);
+    free(g);
+    free(eb);
+    free(wb);
+}
