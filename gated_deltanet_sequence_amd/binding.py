@@ -1,0 +1,215 @@
+"""Thin ctypes binding of libgdn.so (include/gdn.h) for torch tensors.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  Torch supplies device memory and the current
+stream.  If the library is missing this module raises at load time; there is
+no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+GDN_CHUNK_FWD_STAGES = 3
+STAGE_NAMES = ("gate_prep", "chunk_local", "state_scan")
+
+
+class gdn_dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hk", ctypes.c_int32),
+                ("Hv", ctypes.c_int32), ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}" if detail else name)
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gated_deltanet_sequence_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, fp, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
+    dims_p = ctypes.POINTER(gdn_dims)
+    L.gdn_chunk_fwd_workspace_bytes.restype = sz
+    L.gdn_chunk_fwd_workspace_bytes.argtypes = [dims_p]
+    L.gdn_chunk_fwd.restype = ctypes.c_int
+    L.gdn_chunk_fwd.argtypes = [dims_p, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, vp, sz, vp]
+    L.gdn_chunk_fwd_timed.restype = ctypes.c_int
+    L.gdn_chunk_fwd_timed.argtypes = [dims_p, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, vp, sz, vp,
+                                      ctypes.POINTER(ctypes.c_void_p)]
+    L.gdn_recurrent_step.restype = ctypes.c_int
+    L.gdn_recurrent_step.argtypes = [dims_p, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
+    L.gdn_status_str.restype = ctypes.c_char_p
+    L.gdn_status_str.argtypes = [ctypes.c_int]
+    L.gdn_last_error.restype = ctypes.c_char_p
+    L.gdn_last_error.argtypes = []
+    L.gdn_events_create.restype = ctypes.c_int
+    L.gdn_events_create.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]
+    L.gdn_events_destroy.restype = ctypes.c_int
+    L.gdn_events_destroy.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]
+    L.gdn_event_elapsed_ms.restype = ctypes.c_int
+    L.gdn_event_elapsed_ms.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_float)]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise GDNError(status, L.gdn_status_str(status).decode(), L.gdn_last_error().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return GDN_F32
+    if t == torch.bfloat16:
+        return GDN_BF16
+    raise TypeError(f"unsupported dtype {t}: float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _f32(t: Optional[torch.Tensor], name: str):
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return t
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def make_dims(B, T, Hk, Hv, Dk, Dv, dtype, scale=1.0, chunk=64) -> gdn_dims:
+    return gdn_dims(int(B), int(T), int(Hk), int(Hv), int(Dk), int(Dv), int(chunk),
+                    _dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype), float(scale))
+
+
+def gdn_chunk_fwd_workspace_bytes(dims: gdn_dims) -> int:
+    return int(lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def alloc_workspace(dims: gdn_dims, device="cuda") -> torch.Tensor:
+    """A device buffer of the required workspace size (torch's allocator aligns to 512 B)."""
+    n = gdn_chunk_fwd_workspace_bytes(dims)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def gdn_chunk_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, scale: float = 1.0,
+                  out=None, final_state=None, output_final_state: bool = True, workspace=None,
+                  stream=None, stage_events: Optional[Sequence[int]] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill.  q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv]; a, b [B,T,Hv] fp32;
+    A_log, dt_bias [Hv] fp32; initial_state [B,Hv,Dk,Dv] fp32 or None.
+    Returns (out [B,T,Hv,Dv], final_state [B,Hv,Dk,Dv] or None)."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dims = make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, scale)
+    for name, t in (("a", a), ("b", b), ("A_log", A_log), ("dt_bias", dt_bias),
+                    ("initial_state", initial_state), ("final_state", final_state)):
+        _f32(t, name)
+    if k.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k must share shape and q, k, v dtype")
+    if tuple(v.shape[:2]) != (B, T) or tuple(a.shape) != (B, T, Hv) or tuple(b.shape) != (B, T, Hv):
+        raise ValueError("shape mismatch among q, v, a, b")
+    if tuple(A_log.shape) != (Hv,) or tuple(dt_bias.shape) != (Hv,):
+        raise ValueError("A_log and dt_bias must be [Hv]")
+    if initial_state is not None and tuple(initial_state.shape) != (B, Hv, Dk, Dv):
+        raise ValueError("initial_state must be [B,Hv,Dk,Dv]")
+    if out is None:
+        out = torch.empty((B, T, Hv, Dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(dims, q.device)
+    ev = None
+    if stage_events is not None:
+        ev = (ctypes.c_void_p * (GDN_CHUNK_FWD_STAGES + 1))(*stage_events)
+    st = lib().gdn_chunk_fwd_timed(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+        _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream), ev)
+    _check(st)
+    return out, final_state
+
+
+def gdn_recurrent_step(q, k, v, a, b, A_log, dt_bias, state, *, scale: float = 1.0, out=None,
+                       stream=None) -> torch.Tensor:
+    """One decode step, state updated in place.  q, k [B,Hk,Dk]; v [B,Hv,Dv];
+    a, b [B,Hv] fp32; state [B,Hv,Dk,Dv] fp32.  Returns out [B,Hv,Dv]."""
+    B, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    dims = make_dims(B, 1, Hk, Hv, Dk, Dv, q.dtype, scale)
+    for name, t in (("a", a), ("b", b), ("A_log", A_log), ("dt_bias", dt_bias), ("state", state)):
+        _f32(t, name)
+    if tuple(state.shape) != (B, Hv, Dk, Dv):
+        raise ValueError("state must be [B,Hv,Dk,Dv]")
+    if out is None:
+        out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=q.device)
+    st = lib().gdn_recurrent_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                  _ptr(A_log), _ptr(dt_bias), _ptr(state), _ptr(out), _stream(stream))
+    _check(st)
+    return out
+
+
+class StageEvents:
+    """GDN_CHUNK_FWD_STAGES + 1 HIP events for gdn_chunk_fwd(..., stage_events=...)."""
+
+    def __init__(self):
+        self.n = GDN_CHUNK_FWD_STAGES + 1
+        self._arr = (ctypes.c_void_p * self.n)()
+        _check(lib().gdn_events_create(self.n, self._arr))
+
+    @property
+    def handles(self):
+        return [self._arr[i] for i in range(self.n)]
+
+    def stage_ms(self):
+        """Elapsed ms of each stage of the last recorded call (stream must be synchronised)."""
+        res = []
+        for i in range(self.n - 1):
+            ms = ctypes.c_float()
+            _check(lib().gdn_event_elapsed_ms(self._arr[i], self._arr[i + 1], ctypes.byref(ms)))
+            res.append(ms.value)
+        return res
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        _check(lib().gdn_event_elapsed_ms(self._arr[i], self._arr[j], ctypes.byref(ms)))
+        return ms.value
+
+    def close(self):
+        if self._arr is not None:
+            lib().gdn_events_destroy(self.n, self._arr)
+            self._arr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

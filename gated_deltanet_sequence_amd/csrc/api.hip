@@ -1,0 +1,237 @@
+// api.hip -- the C ABI of libgdn.so (declared in include/gdn.h): host-side
+// validation of every argument, then asynchronous launches on the caller's
+// stream.  Nothing is allocated and nothing is enqueued on a validation error.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local char g_err[320];
+
+gdn_status fail(gdn_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+gdn_status ok() {
+    g_err[0] = 0;
+    return GDN_OK;
+}
+
+struct Span {
+    const char *name;
+    const void *p;
+    size_t bytes;
+};
+
+bool overlap(const Span &x, const Span &y) {
+    if (!x.p || !y.p || !x.bytes || !y.bytes) return false;
+    const uintptr_t a0 = (uintptr_t)x.p, a1 = a0 + x.bytes;
+    const uintptr_t b0 = (uintptr_t)y.p, b1 = b0 + y.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+gdn_status need(const Span &s, size_t align) {
+    if (s.bytes == 0) return GDN_OK;  // empty tensor: pointer unused
+    if (!s.p) return fail(GDN_ERR_NULL, "%s is NULL", s.name);
+    if ((uintptr_t)s.p % align)
+        return fail(GDN_ERR_ALIGN, "%s is not %zu-byte aligned", s.name, align);
+    return GDN_OK;
+}
+
+gdn_status check_dims(const gdn_dims *d, bool prefill) {
+    if (!d) return fail(GDN_ERR_NULL, "dims is NULL");
+    if (d->B < 0) return fail(GDN_ERR_SHAPE, "B = %d < 0", d->B);
+    if (prefill && d->T < 0) return fail(GDN_ERR_SHAPE, "T = %d < 0", d->T);
+    if (d->Hk < 1 || d->Hv < 1) return fail(GDN_ERR_SHAPE, "Hk = %d, Hv = %d: need >= 1", d->Hk, d->Hv);
+    if (d->Hv % d->Hk) return fail(GDN_ERR_SHAPE, "Hv = %d is not a multiple of Hk = %d", d->Hv, d->Hk);
+    if (d->Dk != 64 && d->Dk != 128) return fail(GDN_ERR_UNSUPPORTED, "Dk = %d: supported 64, 128", d->Dk);
+    if (d->Dv != 64 && d->Dv != 128) return fail(GDN_ERR_UNSUPPORTED, "Dv = %d: supported 64, 128", d->Dv);
+    if (prefill && d->chunk != 64) return fail(GDN_ERR_UNSUPPORTED, "chunk = %d: supported 64", d->chunk);
+    if (d->dtype != GDN_F32 && d->dtype != GDN_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "dtype = %d: supported GDN_F32, GDN_BF16", d->dtype);
+    if (!isfinite(d->scale)) return fail(GDN_ERR_SHAPE, "scale is not finite");
+    // launch-grid limits
+    const long long units = (long long)d->B * d->Hv;
+    if (units > 0x7fffffffLL / 2) return fail(GDN_ERR_SHAPE, "B * Hv = %lld too large", units);
+    if (prefill) {
+        const long long nc = ((long long)d->T + 63) / 64;
+        if (d->Hk > 65535 || d->B > 65535)
+            return fail(GDN_ERR_SHAPE, "Hk = %d, B = %d: grid limit 65535", d->Hk, d->B);
+        if (units * nc > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "B * Hv * ceil(T/64) too large");
+    }
+    return GDN_OK;
+}
+
+size_t esize(const gdn_dims *d) { return d->dtype == GDN_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_str(int s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL: return "GDN_ERR_NULL";
+        case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+        case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+        case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP";
+        default: return "GDN_ERR_UNKNOWN";
+    }
+}
+
+const char *gdn_last_error(void) { return g_err; }
+
+size_t gdn_chunk_fwd_workspace_bytes(const gdn_dims *d) {
+    if (check_dims(d, true) != GDN_OK) return 0;
+    if (d->B == 0 || d->T == 0) return 0;
+    return gdn::prefill_workspace_layout(d->B, d->T, d->Hv, d->dtype == GDN_F32, nullptr, nullptr);
+}
+
+gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k, const void *v,
+                               const float *a, const float *b, const float *A_log,
+                               const float *dt_bias, const float *initial_state, void *out,
+                               float *final_state, void *workspace, size_t workspace_bytes,
+                               void *stream, void *const *stage_events) {
+    gdn_status st = check_dims(d, true);
+    if (st != GDN_OK) return st;
+    const size_t B = d->B, T = d->T, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv, es = esize(d);
+    const Span sq{"q", q, B * T * Hk * Dk * es}, sk{"k", k, B * T * Hk * Dk * es};
+    const Span sv{"v", v, B * T * Hv * Dv * es};
+    const Span sa{"a", a, B * T * Hv * 4}, sb{"b", b, B * T * Hv * 4};
+    const Span sal{"A_log", A_log, Hv * 4}, sdt{"dt_bias", dt_bias, Hv * 4};
+    const Span s0{"initial_state", initial_state, initial_state ? B * Hv * Dk * Dv * 4 : 0};
+    const Span so{"out", out, B * T * Hv * Dv * es};
+    const Span sf{"final_state", final_state, final_state ? B * Hv * Dk * Dv * 4 : 0};
+    const size_t wneed = gdn_chunk_fwd_workspace_bytes(d);
+    const Span sw{"workspace", workspace, wneed};
+    for (const Span *s : {&sq, &sk, &sv, &so, &s0, &sf})
+        if ((st = need(*s, 16)) != GDN_OK) return st;
+    for (const Span *s : {&sa, &sb, &sal, &sdt})
+        if ((st = need(*s, 4)) != GDN_OK) return st;
+    if (wneed) {
+        if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", wneed);
+        if (workspace_bytes < wneed)
+            return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, wneed);
+        if ((uintptr_t)workspace % 256) return fail(GDN_ERR_ALIGN, "workspace is not 256-byte aligned");
+    }
+    for (const Span *s : {&sq, &sk, &sv, &sa, &sb, &sal, &sdt, &s0, &sf, &sw})
+        if (overlap(so, *s)) return fail(GDN_ERR_ALIAS, "out overlaps %s", s->name);
+    for (const Span *s : {&sq, &sk, &sv, &sa, &sb, &sal, &sdt, &sw})
+        if (overlap(sf, *s)) return fail(GDN_ERR_ALIAS, "final_state overlaps %s", s->name);
+    if (overlap(sf, s0) && final_state != initial_state)
+        return fail(GDN_ERR_ALIAS, "final_state partly overlaps initial_state");
+    for (const Span *s : {&sq, &sk, &sv, &sa, &sb, &sal, &sdt, &s0})
+        if (overlap(sw, *s)) return fail(GDN_ERR_ALIAS, "workspace overlaps %s", s->name);
+    ok();
+    if (B == 0) return GDN_OK;
+
+    hipStream_t hs = (hipStream_t)stream;
+    gdn::PrefillArgs p;
+    p.B = d->B; p.T = d->T; p.Hk = d->Hk; p.Hv = d->Hv; p.Dk = d->Dk; p.Dv = d->Dv;
+    p.f32 = d->dtype == GDN_F32;
+    p.scale = d->scale;
+    p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.S0 = initial_state; p.out = out; p.ST = final_state;
+    hipEvent_t const *ev = (hipEvent_t const *)stage_events;
+    auto rec = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], hs) : hipSuccess; };
+    hipError_t e = hipSuccess;
+    if (T == 0) {
+        if (final_state && final_state != initial_state) e = gdn::launch_state_copy(p, hs);
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
+        return GDN_OK;
+    }
+    gdn::PrefillWorkspace ws;
+    gdn::prefill_workspace_layout(d->B, d->T, d->Hv, p.f32, workspace, &ws);
+    if (e == hipSuccess) e = rec(0);
+    if (e == hipSuccess) e = gdn::launch_gate_prep(p, ws, hs);
+    if (e == hipSuccess) e = rec(1);
+    if (e == hipSuccess) e = gdn::launch_chunk_local(p, ws, hs);
+    if (e == hipSuccess) e = rec(2);
+    if (e == hipSuccess) e = gdn::launch_state_scan(p, ws, hs);
+    if (e == hipSuccess) e = rec(3);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const void *v,
+                         const float *a, const float *b, const float *A_log, const float *dt_bias,
+                         const float *initial_state, void *out, float *final_state, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    return gdn_chunk_fwd_timed(d, q, k, v, a, b, A_log, dt_bias, initial_state, out, final_state,
+                               workspace, workspace_bytes, stream, nullptr);
+}
+
+gdn_status gdn_recurrent_step(const gdn_dims *d, const void *q, const void *k, const void *v,
+                              const float *a, const float *b, const float *A_log,
+                              const float *dt_bias, float *state, void *out, void *stream) {
+    gdn_status st = check_dims(d, false);
+    if (st != GDN_OK) return st;
+    const size_t B = d->B, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv, es = esize(d);
+    const Span sq{"q", q, B * Hk * Dk * es}, sk{"k", k, B * Hk * Dk * es};
+    const Span sv{"v", v, B * Hv * Dv * es};
+    const Span sa{"a", a, B * Hv * 4}, sb{"b", b, B * Hv * 4};
+    const Span sal{"A_log", A_log, Hv * 4}, sdt{"dt_bias", dt_bias, Hv * 4};
+    const Span ss{"state", state, B * Hv * Dk * Dv * 4};
+    const Span so{"out", out, B * Hv * Dv * es};
+    for (const Span *s : {&sq, &sk, &sv, &ss, &so})
+        if ((st = need(*s, 16)) != GDN_OK) return st;
+    for (const Span *s : {&sa, &sb, &sal, &sdt})
+        if ((st = need(*s, 4)) != GDN_OK) return st;
+    for (const Span *s : {&sq, &sk, &sv, &sa, &sb, &sal, &sdt, &ss})
+        if (overlap(so, *s)) return fail(GDN_ERR_ALIAS, "out overlaps %s", s->name);
+    for (const Span *s : {&sq, &sk, &sv, &sa, &sb, &sal, &sdt})
+        if (overlap(ss, *s)) return fail(GDN_ERR_ALIAS, "state overlaps %s", s->name);
+    ok();
+    if (B == 0) return GDN_OK;
+    gdn::DecodeArgs p;
+    p.B = d->B; p.Hk = d->Hk; p.Hv = d->Hv; p.Dk = d->Dk; p.Dv = d->Dv;
+    p.f32 = d->dtype == GDN_F32;
+    p.scale = d->scale;
+    p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.state = state; p.out = out;
+    const hipError_t e = gdn::launch_decode(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn_events_create(int n, void **events) {
+    if (n < 0) return fail(GDN_ERR_SHAPE, "n = %d < 0", n);
+    if (n && !events) return fail(GDN_ERR_NULL, "events is NULL");
+    for (int i = 0; i < n; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (int j = 0; j < i; ++j) (void)hipEventDestroy((hipEvent_t)events[j]);
+            return fail(GDN_ERR_HIP, "hipEventCreate failed");
+        }
+        events[i] = (void *)e;
+    }
+    return ok();
+}
+
+gdn_status gdn_events_destroy(int n, void *const *events) {
+    if (n && !events) return fail(GDN_ERR_NULL, "events is NULL");
+    for (int i = 0; i < n; ++i)
+        if (events[i]) (void)hipEventDestroy((hipEvent_t)events[i]);
+    return ok();
+}
+
+gdn_status gdn_event_elapsed_ms(void *start, void *stop, float *ms) {
+    if (!start || !stop || !ms) return fail(GDN_ERR_NULL, "NULL argument");
+    const hipError_t e = hipEventElapsedTime(ms, (hipEvent_t)start, (hipEvent_t)stop);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

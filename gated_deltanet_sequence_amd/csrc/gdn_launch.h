@@ -1,0 +1,51 @@
+// gdn_launch.h -- internal launchers shared by the C ABI (api.hip) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Workspace carve-up of the chunked prefill; every region is 256-byte aligned.
+struct PrefillWorkspace {
+    double *G;      // [B*Hv*NC*64] in-chunk cumulative log decay (float64)
+    float *beta;    // [B*Hv*NC*64] write strength (0 on padding)
+    float *tok;     // [B*Hv*NC*64][4]: beta, gamma = e^G, eta = e^(G_last - G), q.k
+    void *apair;    // [B*Hv*NC][6][64 lanes][8] strictly-lower (I+L)^{-1} operand fragments
+    void *qpair;    // [B*Hv*NC][6][64 lanes][8] strictly-lower gated Q K^T operand fragments
+    size_t bytes;   // total
+};
+
+size_t prefill_workspace_layout(int B, int T, int Hv, bool f32, void *base, PrefillWorkspace *ws);
+
+struct PrefillArgs {
+    int B, T, Hk, Hv, Dk, Dv;
+    bool f32;
+    float scale;
+    const void *q, *k, *v;
+    const float *a, *b, *A_log, *dt_bias;
+    const float *S0;
+    void *out;
+    float *ST;
+};
+
+hipError_t launch_gate_prep(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s);
+hipError_t launch_chunk_local(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s);
+hipError_t launch_state_scan(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s);
+hipError_t launch_state_copy(const PrefillArgs &p, hipStream_t s);  // T == 0: S_T = S_0 (or 0)
+
+struct DecodeArgs {
+    int B, Hk, Hv, Dk, Dv;
+    bool f32;
+    float scale;
+    const void *q, *k, *v;
+    const float *a, *b, *A_log, *dt_bias;
+    float *state;
+    void *out;
+};
+
+hipError_t launch_decode(const DecodeArgs &p, hipStream_t s);
+
+}  // namespace gdn

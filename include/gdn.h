@@ -1,0 +1,142 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet core library (libgdn.so).
+ *
+ * The operation: per (sequence b, value head h) a state S in R^{d_k x d_v}
+ * (float32, stored row-major as S[d_k][d_v]) follows the gated delta rule
+ *
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t                       (read-out after the write)
+ *
+ * with alpha_t = exp(g_t), g_t = -exp(A_log[h]) * softplus(a_t + dt_bias[h]),
+ * softplus(x) = log(1 + e^x) and beta_t = sigmoid(b_t).
+ * Sources: rainlin-net.pages.dev "Qwen3.5", section "GDN详解" (the rule, its
+ * five-step expansion and the [d_k][d_v] state indexing of its eager loop);
+ * dingfen.github.io "从 Full Attention 到 Gated DeltaNet", sections 9-10 (gate
+ * parametrisation, read-out S^T q); wanger-sjtu.github.io Qwen3.5 Gated
+ * DeltaNet architecture page, section "缓存与推理/训练分支" (a chunked path for a
+ * whole sequence and a recurrent path that updates a cached state).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no global mutable state.  Tensors are dense,
+ *    row-major, contiguous, and 16-byte aligned.
+ *  - Value head h reads key/query head h / (Hv / Hk) (consecutive groups).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream); the caller synchronises.
+ *  - Every argument is validated on the host before anything is enqueued; on
+ *    any error nothing is enqueued and no output is touched.  No exception or
+ *    abort crosses the ABI.  gdn_status_str() names a status code.
+ *  - GDN_BF16 inputs are multiplied on the matrix cores as float16 operands
+ *    with float32 accumulation: |q|, |k|, |v| entries and state entries must
+ *    stay below 6.0e4 (the float16 range).  GDN_F32 runs float32 end to end.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of q, k, v and out (and of the GDN-2 gate logits) */
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    GDN_ERR_SHAPE = -2,       /* negative, zero-where-forbidden or inconsistent dim */
+    GDN_ERR_UNSUPPORTED = -3, /* head size, chunk size or dtype not implemented    */
+    GDN_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned           */
+    GDN_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required           */
+    GDN_ERR_ALIAS = -6,       /* an output overlaps an input it may not alias      */
+    GDN_ERR_HIP = -7          /* the HIP runtime reported a launch error           */
+} gdn_status;
+
+/* Problem dimensions.
+ *   B      sequences (>= 0; 0 is a no-op)
+ *   T      tokens per sequence (>= 0; prefill only, ignored by the step)
+ *   Hk, Hv key/query heads and value heads (>= 1, Hv % Hk == 0)
+ *   Dk, Dv key and value head sizes: each 64 or 128
+ *   chunk  tokens per chunk of the chunked prefill: 64
+ *   dtype  gdn_dtype of q, k, v, out
+ *   scale  multiplies the read-out (1.0 = the pages' formula; 1/sqrt(Dk) is
+ *          the usual attention scaling) */
+typedef struct gdn_dims {
+    int32_t B, T, Hk, Hv, Dk, Dv;
+    int32_t chunk;
+    int32_t dtype;
+    float scale;
+} gdn_dims;
+
+/* Bytes of device workspace gdn_chunk_fwd needs for these dims (0 on invalid
+ * dims).  Grows linearly with B * Hv * ceil(T / chunk). */
+size_t gdn_chunk_fwd_workspace_bytes(const gdn_dims *d);
+
+/* Chunkwise-parallel prefill over whole sequences (wanger-sjtu page: the chunk
+ * branch for training and prefill; zhichai.net "Gated DeltaNet-2" digest,
+ * section "高效训练：WY 算法依然成立": the WY form with a triangular solve and
+ * dense products, here in its scalar-decay case).
+ *   q, k          [B,T,Hk,Dk] dtype
+ *   v             [B,T,Hv,Dv] dtype
+ *   a, b          [B,T,Hv] float32 raw gate logits (decay and write strength)
+ *   A_log, dt_bias[Hv] float32
+ *   initial_state [B,Hv,Dk,Dv] float32, or NULL for a zero state
+ *   out           [B,T,Hv,Dv] dtype (written)
+ *   final_state   [B,Hv,Dk,Dv] float32 (written), or NULL; may be exactly
+ *                 initial_state (in-place update) but must not partly overlap it
+ *   workspace     device scratch of at least gdn_chunk_fwd_workspace_bytes(d)
+ *                 bytes, 256-byte aligned; contents on entry are ignored.
+ * out must not overlap any input.  Results are deterministic (no atomics). */
+gdn_status gdn_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const void *v,
+                         const float *a, const float *b, const float *A_log,
+                         const float *dt_bias, const float *initial_state, void *out,
+                         float *final_state, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* gdn_chunk_fwd, plus timing events: stage_events is NULL or points to
+ * GDN_CHUNK_FWD_STAGES + 1 hipEvent_t handles (created by the caller, e.g. with
+ * gdn_events_create).  Event i is recorded on `stream` before stage i and the
+ * last one after the final stage, so the elapsed time between events i and
+ * i+1 is the duration of stage i: 0 gate preparation, 1 chunk-local WY
+ * auxiliaries, 2 inter-chunk state scan with output. */
+#define GDN_CHUNK_FWD_STAGES 3
+gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k,
+                               const void *v, const float *a, const float *b,
+                               const float *A_log, const float *dt_bias,
+                               const float *initial_state, void *out, float *final_state,
+                               void *workspace, size_t workspace_bytes, void *stream,
+                               void *const *stage_events);
+
+/* One-token recurrent decode step on a cached state, updated in place
+ * (wanger-sjtu page: the recurrent branch reads and updates the cached
+ * recurrent state; rainlin page, five-step form for one token).
+ *   q, k          [B,Hk,Dk] dtype
+ *   v             [B,Hv,Dv] dtype
+ *   a, b          [B,Hv] float32 raw gate logits
+ *   A_log, dt_bias[Hv] float32
+ *   state         [B,Hv,Dk,Dv] float32, read and overwritten with S_t
+ *   out           [B,Hv,Dv] dtype (written); must not overlap state or inputs.
+ * d->T and d->chunk are ignored. */
+gdn_status gdn_recurrent_step(const gdn_dims *d, const void *q, const void *k, const void *v,
+                              const float *a, const float *b, const float *A_log,
+                              const float *dt_bias, float *state, void *out, void *stream);
+
+/* Name of a status code (static string, never NULL). */
+const char *gdn_status_str(int status);
+
+/* Detail of the last validation failure on the calling thread (which argument
+ * and why), or "" -- a static thread-local string, valid until the next call. */
+const char *gdn_last_error(void);
+
+/* Timing-event helpers for gdn_chunk_fwd_timed (thin wrappers over HIP events). */
+gdn_status gdn_events_create(int n, void **events);
+gdn_status gdn_events_destroy(int n, void *const *events);
+gdn_status gdn_event_elapsed_ms(void *start, void *stop, float *ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "gdn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-GCC_CMD = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
+GCC_CMD = ["gcc", "-O3", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
            "-std=c11", "-Wall", "-Wextra", _SRC, "-o", _LIB, "-lm"]
 
 

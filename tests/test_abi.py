@@ -1,0 +1,230 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and its host-side validation rejects bad arguments before touching the GPU.
+
+Every call here fails validation (or is a B = 0 no-op), so no HIP work is ever
+enqueued; the pointers are host addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_sequence_amd as gdn
+from gated_deltanet_sequence_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_ALIAS = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ["gdn_chunk_fwd", "gdn_chunk_fwd_timed", "gdn_recurrent_step",
+                     "gdn_chunk_fwd_workspace_bytes", "gdn_status_str", "gdn_last_error"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(binding.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    L = gdn.lib()
+    for code, name in [(0, "GDN_OK"), (-1, "GDN_ERR_NULL"), (-2, "GDN_ERR_SHAPE"),
+                       (-3, "GDN_ERR_UNSUPPORTED"), (-4, "GDN_ERR_ALIGN"), (-5, "GDN_ERR_WORKSPACE"),
+                       (-6, "GDN_ERR_ALIAS"), (-7, "GDN_ERR_HIP")]:
+        assert L.gdn_status_str(code).decode() == name
+    assert L.gdn_status_str(99).decode() == "GDN_ERR_UNKNOWN"
+
+
+class Buf:
+    """Host buffers standing in for device pointers (validation only reads addresses)."""
+
+    def __init__(self):
+        self._keep = []
+
+    def __call__(self, nbytes, offset=0):
+        b = ctypes.create_string_buffer(nbytes + 512)
+        self._keep.append(b)
+        base = (ctypes.addressof(b) + 255) & ~255
+        return base + offset
+
+
+def dims(**kw):
+    d = dict(B=1, T=128, Hk=2, Hv=4, Dk=64, Dv=64, dtype=binding.GDN_BF16, scale=1.0, chunk=64)
+    d.update(kw)
+    return binding.make_dims(d["B"], d["T"], d["Hk"], d["Hv"], d["Dk"], d["Dv"], d["dtype"],
+                             d["scale"], d["chunk"])
+
+
+def prefill_args(buf, d, **override):
+    es = 4 if d.dtype == binding.GDN_F32 else 2
+    B, T, Hk, Hv, Dk, Dv = d.B, d.T, d.Hk, d.Hv, d.Dk, d.Dv
+    args = dict(
+        q=buf(B * T * Hk * Dk * es), k=buf(B * T * Hk * Dk * es), v=buf(B * T * Hv * Dv * es),
+        a=buf(B * T * Hv * 4), b=buf(B * T * Hv * 4), A_log=buf(Hv * 4), dt_bias=buf(Hv * 4),
+        S0=None, out=buf(B * T * Hv * Dv * es), ST=buf(B * Hv * Dk * Dv * 4))
+    ws = binding.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    args["ws"] = buf(ws)
+    args["ws_bytes"] = ws
+    args.update(override)
+    return args
+
+
+def call_prefill(d, a):
+    L = binding.lib()
+    return L.gdn_chunk_fwd(ctypes.byref(d), a["q"], a["k"], a["v"], a["a"], a["b"], a["A_log"],
+                           a["dt_bias"], a["S0"], a["out"], a["ST"], a["ws"], a["ws_bytes"], None)
+
+
+def last_error():
+    return binding.lib().gdn_last_error().decode()
+
+
+def test_workspace_bytes():
+    L = binding.lib()
+    d = dims(B=1, T=4096, Hk=16, Hv=64, Dk=128, Dv=128)
+    n = L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    units = 64 * 64
+    # per chunk unit: float64 + float32 gate vectors, 16 B token records, two 6 KB fragment sets
+    assert n >= units * (64 * 8 + 64 * 4 + 64 * 16 + 2 * 6 * 64 * 8 * 2)
+    assert n < units * 20000
+    d_bad = dims(Hv=3)
+    assert L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(d_bad)) == 0
+    assert L.gdn_chunk_fwd_workspace_bytes(None) == 0
+    assert L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(dims(T=0))) == 0
+    # float32 operands double the fragment storage
+    n32 = L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(dims(B=1, T=4096, Hk=16, Hv=64, Dk=128,
+                                                            Dv=128, dtype=binding.GDN_F32)))
+    assert n32 > n
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(Hv=3), ERR_SHAPE, "multiple"),
+    (dict(B=-1), ERR_SHAPE, "B"),
+    (dict(T=-5), ERR_SHAPE, "T"),
+    (dict(Hk=0), ERR_SHAPE, "Hk"),
+    (dict(Dk=96), ERR_UNSUPPORTED, "Dk"),
+    (dict(Dv=256), ERR_UNSUPPORTED, "Dv"),
+    (dict(chunk=32), ERR_UNSUPPORTED, "chunk"),
+    (dict(dtype=7), ERR_UNSUPPORTED, "dtype"),
+    (dict(scale=float("nan")), ERR_SHAPE, "scale"),
+])
+def test_prefill_rejects_bad_dims(kw, code, needle):
+    buf = Buf()
+    d = dims(**kw)
+    args = prefill_args(buf, dims())
+    assert call_prefill(d, args) == code
+    assert needle in last_error()
+
+
+def test_prefill_rejects_null_dims():
+    L = binding.lib()
+    assert L.gdn_chunk_fwd(None, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, None) == ERR_NULL
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "a", "b", "A_log", "dt_bias", "out"])
+def test_prefill_rejects_null_pointer(name):
+    buf = Buf()
+    d = dims()
+    args = prefill_args(buf, d, **{name: None})
+    assert call_prefill(d, args) == ERR_NULL
+    assert name in last_error()
+
+
+@pytest.mark.parametrize("name", ["q", "v", "out", "ST"])
+def test_prefill_rejects_misaligned(name):
+    buf = Buf()
+    d = dims()
+    args = prefill_args(buf, d)
+    args[name] = args[name] + 8
+    assert call_prefill(d, args) == ERR_ALIGN
+
+
+def test_prefill_workspace_checks():
+    buf = Buf()
+    d = dims()
+    args = prefill_args(buf, d, ws=None)
+    assert call_prefill(d, args) == ERR_WORKSPACE
+    args = prefill_args(buf, d)
+    args["ws_bytes"] -= 1
+    assert call_prefill(d, args) == ERR_WORKSPACE
+    args = prefill_args(buf, d)
+    args["ws"] += 16
+    assert call_prefill(d, args) == ERR_ALIGN
+
+
+def test_prefill_rejects_aliasing():
+    buf = Buf()
+    d = dims()
+    a = prefill_args(buf, d)
+    a["out"] = a["v"]
+    assert call_prefill(d, a) == ERR_ALIAS and "out overlaps v" in last_error()
+    a = prefill_args(buf, d)
+    a["ST"] = a["q"]
+    assert call_prefill(d, a) == ERR_ALIAS
+    # final_state may equal initial_state, but must not partly overlap it
+    a = prefill_args(buf, d)
+    s0 = buf(d.B * d.Hv * d.Dk * d.Dv * 4 + 64)
+    a["S0"] = s0
+    a["ST"] = s0 + 16
+    assert call_prefill(d, a) == ERR_ALIAS and "partly" in last_error()
+    a = prefill_args(buf, d)
+    a["ws"] = a["q"]
+    assert call_prefill(d, a) == ERR_ALIAS
+
+
+def test_prefill_zero_batch_is_a_noop():
+    buf = Buf()
+    d = dims(B=0)
+    a = prefill_args(buf, d, q=None, k=None, v=None, a=None, b=None, out=None, ST=None, ws=None)
+    assert call_prefill(d, a) == OK
+
+
+def step_args(buf, d, **override):
+    es = 4 if d.dtype == binding.GDN_F32 else 2
+    B, Hk, Hv, Dk, Dv = d.B, d.Hk, d.Hv, d.Dk, d.Dv
+    args = dict(q=buf(B * Hk * Dk * es), k=buf(B * Hk * Dk * es), v=buf(B * Hv * Dv * es),
+                a=buf(B * Hv * 4), b=buf(B * Hv * 4), A_log=buf(Hv * 4), dt_bias=buf(Hv * 4),
+                S=buf(B * Hv * Dk * Dv * 4), out=buf(B * Hv * Dv * es))
+    args.update(override)
+    return args
+
+
+def call_step(d, a):
+    return binding.lib().gdn_recurrent_step(ctypes.byref(d), a["q"], a["k"], a["v"], a["a"], a["b"],
+                                            a["A_log"], a["dt_bias"], a["S"], a["out"], None)
+
+
+def test_step_validation():
+    buf = Buf()
+    d = dims(B=4)
+    assert call_step(dims(B=4, Hv=5), step_args(buf, d)) == ERR_SHAPE
+    assert call_step(dims(B=4, Dk=32), step_args(buf, d)) == ERR_UNSUPPORTED
+    assert call_step(d, step_args(buf, d, S=None)) == ERR_NULL
+    a = step_args(buf, d)
+    a["out"] = a["S"]
+    assert call_step(d, a) == ERR_ALIAS
+    a = step_args(buf, d)
+    a["S"] += 4
+    assert call_step(d, a) == ERR_ALIGN
+    # chunk is ignored by the step: 32 is fine there (fails later only on Hv)
+    assert call_step(dims(B=4, chunk=32, Hv=5), step_args(buf, d)) == ERR_SHAPE
+    assert call_step(dims(B=0), step_args(buf, dims(B=0))) == OK
+
+
+def test_binding_rejects_missing_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
