@@ -17,8 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_F32, GDN_BF16 = 0, 1
-GDN_CHUNK_FWD_STAGES = 3
-STAGE_NAMES = ("gate_prep", "chunk_local", "state_scan")
+GDN_CHUNK_FWD_STAGES = 2
+STAGE_NAMES = ("chunk_local", "state_scan")
 
 
 class gdn_dims(ctypes.Structure):

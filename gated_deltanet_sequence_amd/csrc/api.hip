@@ -67,6 +67,12 @@ gdn_status check_dims(const gdn_dims *d, bool prefill) {
         if (d->Hk > 65535 || d->B > 65535)
             return fail(GDN_ERR_SHAPE, "Hk = %d, B = %d: grid limit 65535", d->Hk, d->B);
         if (units * nc > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "B * Hv * ceil(T/64) too large");
+        // one sequence of v / out is addressed with 32-bit byte offsets
+        const long long seq_bytes = (((long long)d->T + 63) / 64 * 64) * d->Hv * d->Dv *
+                                    (d->dtype == GDN_F32 ? 4 : 2);
+        if (seq_bytes > 0x7fffffffLL)
+            return fail(GDN_ERR_UNSUPPORTED, "T * Hv * Dv * element size = %lld bytes per sequence: limit 2^31",
+                        seq_bytes);
     }
     return GDN_OK;
 }
@@ -96,7 +102,8 @@ const char *gdn_last_error(void) { return g_err; }
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_dims *d) {
     if (check_dims(d, true) != GDN_OK) return 0;
     if (d->B == 0 || d->T == 0) return 0;
-    return gdn::prefill_workspace_layout(d->B, d->T, d->Hv, d->dtype == GDN_F32, nullptr, nullptr);
+    return gdn::prefill_workspace_layout(d->B, d->T, d->Hk, d->Hv, d->Dk, d->dtype == GDN_F32, nullptr,
+                                         nullptr);
 }
 
 gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k, const void *v,
@@ -153,14 +160,12 @@ gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k, 
         return GDN_OK;
     }
     gdn::PrefillWorkspace ws;
-    gdn::prefill_workspace_layout(d->B, d->T, d->Hv, p.f32, workspace, &ws);
+    gdn::prefill_workspace_layout(d->B, d->T, d->Hk, d->Hv, d->Dk, p.f32, workspace, &ws);
     if (e == hipSuccess) e = rec(0);
-    if (e == hipSuccess) e = gdn::launch_gate_prep(p, ws, hs);
-    if (e == hipSuccess) e = rec(1);
     if (e == hipSuccess) e = gdn::launch_chunk_local(p, ws, hs);
-    if (e == hipSuccess) e = rec(2);
+    if (e == hipSuccess) e = rec(1);
     if (e == hipSuccess) e = gdn::launch_state_scan(p, ws, hs);
-    if (e == hipSuccess) e = rec(3);
+    if (e == hipSuccess) e = rec(2);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
     return GDN_OK;
 }

@@ -1,0 +1,343 @@
+// chunk_local.hip -- gate preparation and the chunk-local WY auxiliaries of the
+// chunked prefill (method and notation in prefill_common.h).  Fully parallel
+// over chunks: one work-group of 4 waves per (sequence, key head, chunk).
+//
+//  1. Q and K rows of the chunk are converted to the operand type and staged in
+//     LDS as swizzled tile images; the images of Q, K and K^T are written to
+//     the workspace for the scan, which copies them into LDS byte for byte.
+//  2. K K^T and Q K^T (lower-triangular 16x16 tiles) on the matrix cores, once
+//     per key head: they are shared by its Hv/Hk value heads.
+//  3. Per value head (one wave each): gate preparation -- g = -exp(A_log)
+//     softplus(a + dt_bias) and beta = sigmoid(b) in float32 (dingfen.github.io
+//     page, sections 9-10) and the in-chunk inclusive prefix sum G of g in
+//     float64, so that e^{G_r - G_i} keeps float32 accuracy when |G| is in the
+//     hundreds; the decay ratios Gamma = e^{G_r - G_i} of the lower triangle
+//     (computed once, shared by L and A_qk); L = beta Gamma (.) K K^T; the
+//     blocked inverse A = (I + L)^{-1} (diagonal 16x16 blocks by forward
+//     substitution in registers, off-diagonal blocks on the matrix cores); and
+//     the operand fragments of A and A_qk plus the per-token records the scan
+//     needs.
+#include "prefill_common.h"
+
+namespace gdn {
+
+size_t prefill_workspace_layout(int B, int T, int Hk, int Hv, int Dk, bool f32, void *base,
+                                PrefillWorkspace *ws) {
+    const size_t NC = (size_t)(T + C - 1) / C;
+    const size_t vunits = (size_t)B * Hv * NC, kunits = (size_t)B * Hk * NC;
+    const size_t esz = f32 ? 4 : 2;
+    size_t off = 0;
+    const size_t oT = off;  off = align256(off + vunits * C * 4 * sizeof(float));
+    const size_t oA = off;  off = align256(off + vunits * NPAIR * 64 * 8 * esz);
+    const size_t oQ = off;  off = align256(off + vunits * NPAIR * 64 * 8 * esz);
+    const size_t oQi = off; off = align256(off + kunits * C * Dk * esz);
+    const size_t oKi = off; off = align256(off + kunits * C * Dk * esz);
+    const size_t oTi = off; off = align256(off + kunits * C * Dk * esz);
+    if (ws) {
+        char *p = (char *)base;
+        ws->tok = (float *)(p + oT);
+        ws->apair = p + oA;
+        ws->qpair = p + oQ;
+        ws->qimg = p + oQi;
+        ws->kimg = p + oKi;
+        ws->timg = p + oTi;
+        ws->bytes = off;
+    }
+    return off;
+}
+
+// Logical column of physical position p (inverse of perm_col).
+template <bool F32>
+__device__ __forceinline__ int unperm_col(int p) {
+    if constexpr (F32) return p;
+    return (p & ~31) | (((p & 7) >> 2) << 4) | (((p & 31) >> 3) << 2) | (p & 3);
+}
+
+// Off-diagonal blocks of X = (I + L)^{-1}, 16x16 blocks, diagonal blocks already
+// in Xw:  X[i][j] = -X[i][i] sum_{mb=j}^{i-1} L[i][mb] X[mb][j], one column block
+// at a time.  A column's finished blocks stay in accumulator layout, the B
+// operand of the next product.  Lf holds the A-operand fragments of L's
+// off-diagonal blocks; Xw is this wave's block-packed row-major copy of X.
+template <bool F32>
+__device__ __forceinline__ void inverse_offdiag(float *Xw, const f4 (&Lf)[10], int m, int g) {
+    typedef mma<F32> M;
+#pragma unroll
+    for (int jb = 0; jb < 3; ++jb) {
+        f4 Xc[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Xc[jb][s] = Xw[tri_index(jb, jb) * 256 + (4 * g + s) * 16 + m];
+#pragma unroll
+        for (int ib = jb + 1; ib < 4; ++ib) {
+            f4 Tacc = {0, 0, 0, 0};
+#pragma unroll
+            for (int mb = jb; mb < ib; ++mb)
+                Tacc = M::block(Tacc, M::from_f4(Lf[tri_index(ib, mb)]), M::from_f4(Xc[mb]));
+            const f4 dv = *reinterpret_cast<const f4 *>(Xw + tri_index(ib, ib) * 256 + m * 16 + 4 * g);
+            f4 Xn = {0, 0, 0, 0};
+            Xn = -M::block(Xn, M::from_f4(dv), M::from_f4(Tacc));
+            Xc[ib] = Xn;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xw[tri_index(ib, jb) * 256 + (4 * g + s) * 16 + m] = Xn[s];
+        }
+    }
+}
+
+template <bool F32, int DK>
+struct ChunkLocalCfg {
+    typedef typename mma<F32>::E E;
+    static constexpr size_t IMG = (size_t)C * DK;                  // elements per image
+    static constexpr size_t WAVE_FLOATS = 10 * 256 + 4 * 256 + 128 + 64;  // X blocks, L diag, G, beta
+    static constexpr size_t IMG_BYTES = 2 * IMG * sizeof(E);
+    static constexpr size_t WAVE_BYTES = 4 * WAVE_FLOATS * sizeof(float);
+    static constexpr size_t U_BYTES = IMG_BYTES > WAVE_BYTES ? IMG_BYTES : WAVE_BYTES;
+};
+
+template <bool F32, typename TIn, int DK>
+__global__ __launch_bounds__(256) void chunk_local_kernel(
+    int T, int Hk, int Hv, int NC, const TIn *__restrict__ q, const TIn *__restrict__ k,
+    const float *__restrict__ a, const float *__restrict__ b, const float *__restrict__ A_log,
+    const float *__restrict__ dt_bias, float *__restrict__ tok, typename mma<F32>::E *__restrict__ apair,
+    typename mma<F32>::E *__restrict__ qpair, typename mma<F32>::E *__restrict__ qimg,
+    typename mma<F32>::E *__restrict__ kimg, typename mma<F32>::E *__restrict__ timg) {
+    typedef ChunkLocalCfg<F32, DK> CF;
+    typedef typename mma<F32>::E E;
+    typedef typename mma<F32>::V4 V4;
+    constexpr int EPG = img_epg<F32>();
+    constexpr size_t IMG = CF::IMG;
+
+    // union: Q/K images (steps 1-2) | per-wave scratch (step 3)
+    __shared__ __attribute__((aligned(16))) char u_raw[CF::U_BYTES];
+    __shared__ __attribute__((aligned(16))) float KKt[10 * 256];
+    __shared__ __attribute__((aligned(16))) float QKt[10 * 256];
+    E *Qi = reinterpret_cast<E *>(u_raw);
+    E *Ki = Qi + IMG;
+
+    const int n = blockIdx.x, hk = blockIdx.y, bb = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
+    const int G = Hv / Hk;
+    const int t0 = n * C;
+    const size_t ku = ((size_t)bb * Hk + hk) * NC + n;
+
+    // gate logits of this wave's first value head, lane = token (loads issued first)
+    float a_pre = 0.f, b_pre = 0.f;
+    if (w < G && t0 + lane < T) {
+        const size_t ia = ((size_t)bb * T + t0 + lane) * Hv + hk * G + w;
+        a_pre = a[ia];
+        b_pre = b[ia];
+    }
+
+    // ---- 1. stage Q and K (zero past the end) as images: all loads, then all LDS stores
+    {
+        constexpr int NPC = C * (DK / 8) / 256;  // 8-element pieces per thread
+        f4 ql[NPC], qh[NPC], kl[NPC], kh[NPC];
+#pragma unroll
+        for (int it = 0; it < NPC; ++it) {
+            const int idx = tid + 256 * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+            ql[it] = qh[it] = kl[it] = kh[it] = f4{0, 0, 0, 0};
+            if (t0 + r < T) {
+                const size_t off = (((size_t)bb * T + t0 + r) * Hk + hk) * DK + c8;
+                ld8(q, off, ql[it], qh[it]);
+                ld8(k, off, kl[it], kh[it]);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NPC; ++it) {
+            const int idx = tid + 256 * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+            *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(ql[it]);
+            *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(qh[it]);
+            *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(kl[it]);
+            *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(kh[it]);
+        }
+    }
+    __syncthreads();
+
+    // ---- images to the workspace: Q and K verbatim, K^T transposed
+    {
+        typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+        const u4v *src = reinterpret_cast<const u4v *>(u_raw);
+        u4v *dq = reinterpret_cast<u4v *>(qimg + ku * IMG);
+        u4v *dk = reinterpret_cast<u4v *>(kimg + ku * IMG);
+        constexpr int UNITS = (int)(IMG * sizeof(E) / 16);
+        for (int i = tid; i < UNITS; i += 256) {
+            dq[i] = src[i];
+            dk[i] = src[UNITS + i];
+        }
+        E *dt = timg + ku * IMG;
+        constexpr int GPR = C / EPG;  // 16-byte groups per K^T row
+        for (int job = tid; job < DK * GPR; job += 256) {
+            const int R = job / GPR, gp = job % GPR;
+            const int pr = perm_col<F32>(R);
+            E vals[EPG];
+#pragma unroll
+            for (int j = 0; j < EPG; ++j) {
+                const int tk = unperm_col<F32>(gp * EPG + j);
+                vals[j] = Ki[img_index<F32>(tk, DK, pr)];
+            }
+            *reinterpret_cast<u4v *>(dt + img_index<F32>(R, C, gp * EPG)) = *reinterpret_cast<const u4v *>(vals);
+        }
+    }
+
+    // ---- 2. K K^T and Q K^T, lower-triangular 16x16 tiles (10 each), 5 per wave
+    for (int job = w; job < 20; job += 4) {
+        const E *X = job < 10 ? Ki : Qi;
+        float *Dst = job < 10 ? KKt : QKt;
+        const int p = job % 10;
+        const int rt = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+        const int ct = p - tri_index(rt, 0);
+        f4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int kq = 0; kq < DK / 32; ++kq) {
+            V4 a0, a1, b0, b1;
+            img_pair<F32>(X, DK, 16 * rt + m, kq, g, a0, a1);
+            img_pair<F32>(Ki, DK, 16 * ct + m, kq, g, b0, b1);
+            acc = mma<F32>::pair(acc, a0, a1, b0, b1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Dst[p * 256 + (4 * g + i) * 16 + m] = acc[i];
+    }
+    __syncthreads();  // the images in LDS are dead from here on
+
+    // ---- 3. per value head, one wave each
+    float *Xw = reinterpret_cast<float *>(u_raw) + w * CF::WAVE_FLOATS;
+    float *Ld = Xw + 10 * 256;
+    double *Gs = reinterpret_cast<double *>(Ld + 4 * 256);
+    float *Bs = reinterpret_cast<float *>(Gs + 64);
+    for (int j = w; j < G; j += 4) {
+        const int hv = hk * G + j;
+        const size_t vu = ((size_t)bb * Hv + hv) * NC + n;
+
+        // gates: lane = token
+        const int t = t0 + lane;
+        float gl = 0.f, be = 0.f;
+        if (t < T) {
+            float av = a_pre, bv = b_pre;
+            if (j != w) {
+                const size_t ia = ((size_t)bb * T + t) * Hv + hv;
+                av = a[ia];
+                bv = b[ia];
+            }
+            gl = -expf(A_log[hv]) * softplus_f32(av + dt_bias[hv]);
+            be = sigmoid_f32(bv);
+        }
+        double Gd = (double)gl;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double y = __shfl_up(Gd, off, 64);
+            if (lane >= off) Gd += y;
+        }
+        const double Glast = __shfl(Gd, 63, 64);
+        Gs[lane] = Gd;
+        Bs[lane] = be;
+        {
+            f4 rec;
+            rec[0] = be;
+            rec[1] = expf((float)Gd);
+            rec[2] = expf((float)(Glast - Gd));
+            rec[3] = QKt[tri_index(lane >> 4, lane >> 4) * 256 + (lane & 15) * 17];
+            *reinterpret_cast<f4 *>(tok + (vu * C + lane) * 4) = rec;
+        }
+        wave_lds_sync();
+
+        // decay ratios of the strictly-lower triangle in A-operand layout:
+        // lane (m, g) of block (rb, kb) holds rows 16rb+m, columns 16kb+4g+s
+        f4 Gm[10];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            const int row = 16 * rb + m;
+            const double Gr = Gs[row];
+#pragma unroll
+            for (int kb = 0; kb <= rb; ++kb)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int col = 16 * kb + 4 * g + s;
+                    Gm[tri_index(rb, kb)][s] = col < row ? expf((float)(Gr - Gs[col])) : 0.f;
+                }
+        }
+        // L: off-diagonal blocks as operand fragments, diagonal blocks row-major in Ld
+        f4 Lf[10];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            const float br = Bs[16 * rb + m];
+#pragma unroll
+            for (int kb = 0; kb <= rb; ++kb) {
+                const int ti = tri_index(rb, kb);
+                const f4 kk = *reinterpret_cast<const f4 *>(KKt + ti * 256 + m * 16 + 4 * g);
+                const f4 lv = br * Gm[ti] * kk;
+                if (kb < rb) Lf[ti] = lv;
+                else *reinterpret_cast<f4 *>(Ld + rb * 256 + m * 16 + 4 * g) = lv;
+            }
+        }
+        wave_lds_sync();
+
+        // diagonal blocks of X: lane (block bq, column c) by forward substitution
+        {
+            const int bq = lane >> 4, c = lane & 15;
+            const float *Lb = Ld + bq * 256;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float s = (r == c) ? 1.f : 0.f;
+#pragma unroll
+                for (int jj = 0; jj < r; ++jj) s -= Lb[r * 16 + jj] * x[jj];
+                x[r] = s;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Xw[tri_index(bq, bq) * 256 + r * 16 + c] = x[r];
+        }
+        wave_lds_sync();
+
+        inverse_offdiag<F32>(Xw, Lf, m, g);
+        wave_lds_sync();
+
+        // operand fragments of strictly-lower(A) and strictly-lower(A_qk)
+        E *ap = apair + vu * (NPAIR * 64 * 8) + lane * 8;
+        E *qp = qpair + vu * (NPAIR * 64 * 8) + lane * 8;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int qq = 0; qq <= r / 2; ++qq) {
+                f4 xv[2], av[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kb = 2 * qq + h;
+                    xv[h] = f4{0, 0, 0, 0};
+                    av[h] = f4{0, 0, 0, 0};
+                    if (kb <= r) {
+                        const int ti = tri_index(r, kb);
+                        f4 x4 = *reinterpret_cast<const f4 *>(Xw + ti * 256 + m * 16 + 4 * g);
+                        if (kb == r)
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) x4[s] = (4 * g + s < m) ? x4[s] : 0.f;
+                        xv[h] = x4;
+                        av[h] = Gm[ti] * *reinterpret_cast<const f4 *>(QKt + ti * 256 + m * 16 + 4 * g);
+                    }
+                }
+                const int p = pair_index(r, qq);
+                *reinterpret_cast<V4 *>(ap + p * 512) = mma<F32>::from_f4(xv[0]);
+                *reinterpret_cast<V4 *>(ap + p * 512 + 4) = mma<F32>::from_f4(xv[1]);
+                *reinterpret_cast<V4 *>(qp + p * 512) = mma<F32>::from_f4(av[0]);
+                *reinterpret_cast<V4 *>(qp + p * 512 + 4) = mma<F32>::from_f4(av[1]);
+            }
+        wave_lds_sync();
+    }
+}
+
+template <bool F32, typename TIn, int DK>
+static hipError_t launch_chunk_local_t(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s) {
+    typedef typename mma<F32>::E E;
+    const int NC = (p.T + C - 1) / C;
+    hipLaunchKernelGGL((chunk_local_kernel<F32, TIn, DK>), dim3(NC, p.Hk, p.B), dim3(256), 0, s, p.T,
+                       p.Hk, p.Hv, NC, (const TIn *)p.q, (const TIn *)p.k, p.a, p.b, p.A_log, p.dt_bias,
+                       ws.tok, (E *)ws.apair, (E *)ws.qpair, (E *)ws.qimg, (E *)ws.kimg, (E *)ws.timg);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_local(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s) {
+    if (p.f32) return p.Dk == 128 ? launch_chunk_local_t<true, float, 128>(p, ws, s)
+                                   : launch_chunk_local_t<true, float, 64>(p, ws, s);
+    return p.Dk == 128 ? launch_chunk_local_t<false, bf16_t, 128>(p, ws, s)
+                       : launch_chunk_local_t<false, bf16_t, 64>(p, ws, s);
+}
+
+}  // namespace gdn

@@ -33,6 +33,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Ordering of LDS accesses among the lanes of one wave (no work-group barrier):
+// complete this wave's outstanding LDS operations and keep the compiler from
+// moving LDS accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // Element-type traits of q/k/v/out.
 template <typename T> struct io;
 template <> struct io<float> {
@@ -97,13 +106,14 @@ __device__ __forceinline__ float sigmoid_f32(float x) { return 1.f / (1.f + expf
 __device__ __forceinline__ f4 mfma_f16_k32(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f4 mfma_f16_k16(h4 a, h4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f4 mfma_f32_k4(float a, float b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ h4 to_h4(f4 x) {
-    return h4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-}
+__device__ __forceinline__ h4 to_h4(f4 x) { return __builtin_convertvector(x, h4); }
 __device__ __forceinline__ h8 cat_h8(h4 a, h4 b) {
     return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
@@ -116,6 +126,8 @@ template <> struct mma<false> {
     typedef _Float16 E;
     typedef h4 V4;  // one k-block operand (4 values per lane)
     __device__ static __forceinline__ V4 from_f4(f4 x) { return to_h4(x); }
+    // acc += A(block) * B(block): one 16-deep k-block
+    __device__ static __forceinline__ f4 block(f4 acc, V4 a, V4 b) { return mfma_f16_k16(a, b, acc); }
     // acc += A(blocks kb0,kb1) * B(blocks kb0,kb1): two 16-deep k-blocks per instruction
     __device__ static __forceinline__ f4 pair(f4 acc, V4 a0, V4 a1, V4 b0, V4 b1) {
         return mfma_f16_k32(cat_h8(a0, a1), cat_h8(b0, b1), acc);

@@ -9,16 +9,19 @@
 namespace gdn {
 
 // Workspace carve-up of the chunked prefill; every region is 256-byte aligned.
+// E is the operand type (float16 for bf16 inputs, float32 for float32 inputs).
 struct PrefillWorkspace {
-    double *G;      // [B*Hv*NC*64] in-chunk cumulative log decay (float64)
-    float *beta;    // [B*Hv*NC*64] write strength (0 on padding)
     float *tok;     // [B*Hv*NC*64][4]: beta, gamma = e^G, eta = e^(G_last - G), q.k
-    void *apair;    // [B*Hv*NC][6][64 lanes][8] strictly-lower (I+L)^{-1} operand fragments
-    void *qpair;    // [B*Hv*NC][6][64 lanes][8] strictly-lower gated Q K^T operand fragments
+    void *apair;    // [B*Hv*NC][6][64 lanes][8] E: strictly-lower (I+L)^{-1} operand fragments
+    void *qpair;    // [B*Hv*NC][6][64 lanes][8] E: strictly-lower gated Q K^T operand fragments
+    void *qimg;     // [B*Hk*NC][64][Dk] E: Q tile images
+    void *kimg;     // [B*Hk*NC][64][Dk] E: K tile images
+    void *timg;     // [B*Hk*NC][Dk][64] E: K^T tile images
     size_t bytes;   // total
 };
 
-size_t prefill_workspace_layout(int B, int T, int Hv, bool f32, void *base, PrefillWorkspace *ws);
+size_t prefill_workspace_layout(int B, int T, int Hk, int Hv, int Dk, bool f32, void *base,
+                                PrefillWorkspace *ws);
 
 struct PrefillArgs {
     int B, T, Hk, Hv, Dk, Dv;
@@ -31,7 +34,6 @@ struct PrefillArgs {
     float *ST;
 };
 
-hipError_t launch_gate_prep(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s);
 hipError_t launch_chunk_local(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s);
 hipError_t launch_state_scan(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s);
 hipError_t launch_state_copy(const PrefillArgs &p, hipStream_t s);  // T == 0: S_T = S_0 (or 0)

@@ -1,0 +1,83 @@
+// prefill_common.h -- definitions shared by the chunked-prefill kernels.
+//
+// Method: the WY chunk form of zhichai.net's "Gated DeltaNet-2" digest
+// (section "高效训练：WY 算法依然成立") in its scalar-decay case (same page,
+// section "退化兼容性": D_t = alpha_t I and both gates equal beta_t), with the
+// state stored as S[d_k][d_v].  Inside a chunk of C = 64 tokens with in-chunk
+// cumulative log decay G_r (gamma_r = e^{G_r}) and chunk-start state S:
+//
+//   L     = strictly-lower( beta_r e^{G_r - G_i} k_r.k_i )          (C x C)
+//   A     = (I + L)^{-1}
+//   Delta = A (beta (.) V - beta gamma (.) K S)     (= U - W S of the page)
+//   O     = gamma (.) (Q S) + A_qk Delta,  A_qk = lower-incl-diag(e^{G_r-G_i} q_r.k_i)
+//   S'    = gamma_C S + K^T (eta (.) Delta),  eta_i = e^{G_C - G_i}
+//
+// Delta is formed as A times the residual instead of U - W S (W = A diag(beta
+// gamma) K, U = A diag(beta) V): the same numbers, one C x C x d_k product fewer.
+// Every decay factor is a difference of cumulative logs (all <= 1), never a
+// 1/gamma, so nothing overflows however strong the decay.
+#pragma once
+
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+static constexpr int C = 64;      // chunk length
+static constexpr int NPAIR = 6;   // operand fragments ("pairs") of a strictly-lower 64x64 matrix
+
+// Pair fragments of a strictly-lower 64x64 matrix M: row tile r (16 rows)
+// needs k-steps q = 0..r/2 (32 columns each); pair (r, q) holds, for lane
+// l = 16 g + m, the 8 values M[16r+m][32q + 4g + i] and M[16r+m][32q + 16 + 4g + i]
+// (i = 0..3), contiguous per lane.  pair_index numbers the pairs 0..5.
+__host__ __device__ constexpr int pair_base(int r) { return r == 0 ? 0 : r == 1 ? 1 : r == 2 ? 2 : 4; }
+__host__ __device__ constexpr int pair_index(int r, int q) { return pair_base(r) + q; }
+
+// Column permutation used when staging a row-major operand in LDS for the
+// float16 products: inside each 32-column block, logical column k goes to
+// position 8*((k%16)/4) + 4*(k/16) + k%4, so the 8 values a lane contributes to
+// one 16x16x32 step (k-blocks 4g..4g+3 and 16+4g..16+4g+3) are contiguous and
+// come in one 16-byte LDS read.  The float32 products read 4 values per k-block,
+// already contiguous: no permutation.
+template <bool F32>
+__host__ __device__ constexpr int perm_col(int k) {
+    return F32 ? k : (k & ~31) | (((k & 15) >> 2) << 3) | (((k & 31) >> 4) << 2) | (k & 3);
+}
+
+// Tile images.  Q and K of a chunk ([64 tokens][d_k]) and K^T ([d_k][64 tokens])
+// are kept as row-major tiles of the operand type, columns placed by perm_col
+// and each row's 16-byte groups XOR-swizzled with (row & 7): the 8 lanes that
+// read 16 consecutive-row operands in one instruction then hit 8 different
+// groups, i.e. all LDS banks, with no padding.  The chunk-local kernel writes
+// the images to the workspace in exactly this layout and the scan copies them
+// byte for byte into LDS.
+template <bool F32>
+__host__ __device__ constexpr int img_epg() { return F32 ? 4 : 8; }  // elements per 16-byte group
+
+template <bool F32>
+__device__ __forceinline__ int img_index(int row, int rowlen, int phys) {
+    constexpr int epg = img_epg<F32>();
+    return row * rowlen + (((phys / epg) ^ (row & 7)) * epg) + phys % epg;
+}
+
+// Operand pair (two 16-deep k-blocks, logical columns 32kq .. 32kq+31) of image
+// row R for lane group g.
+template <bool F32>
+__device__ __forceinline__ void img_pair(const typename mma<F32>::E *X, int rowlen, int R, int kq, int g,
+                                         typename mma<F32>::V4 &a0, typename mma<F32>::V4 &a1) {
+    if constexpr (F32) {
+        a0 = *reinterpret_cast<const f4 *>(X + R * rowlen + 4 * ((8 * kq + g) ^ (R & 7)));
+        a1 = *reinterpret_cast<const f4 *>(X + R * rowlen + 4 * ((8 * kq + 4 + g) ^ (R & 7)));
+    } else {
+        const h8 v = *reinterpret_cast<const h8 *>(X + R * rowlen + 8 * ((4 * kq + g) ^ (R & 7)));
+        a0 = h4{v[0], v[1], v[2], v[3]};
+        a1 = h4{v[4], v[5], v[6], v[7]};
+    }
+}
+
+// Lower-triangular 16x16 tiles (rt >= ct) of a 64x64 matrix, numbered 0..9.
+__host__ __device__ constexpr int tri_index(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace gdn

@@ -88,7 +88,9 @@ size_t gdn_chunk_fwd_workspace_bytes(const gdn_dims *d);
  *                 initial_state (in-place update) but must not partly overlap it
  *   workspace     device scratch of at least gdn_chunk_fwd_workspace_bytes(d)
  *                 bytes, 256-byte aligned; contents on entry are ignored.
- * out must not overlap any input.  Results are deterministic (no atomics). */
+ * out must not overlap any input.  Results are deterministic (no atomics).
+ * Limit: T * Hv * Dv * element size of one sequence below 2^31 bytes
+ * (GDN_ERR_UNSUPPORTED otherwise). */
 gdn_status gdn_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const void *v,
                          const float *a, const float *b, const float *A_log,
                          const float *dt_bias, const float *initial_state, void *out,
@@ -99,9 +101,9 @@ gdn_status gdn_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const 
  * GDN_CHUNK_FWD_STAGES + 1 hipEvent_t handles (created by the caller, e.g. with
  * gdn_events_create).  Event i is recorded on `stream` before stage i and the
  * last one after the final stage, so the elapsed time between events i and
- * i+1 is the duration of stage i: 0 gate preparation, 1 chunk-local WY
- * auxiliaries, 2 inter-chunk state scan with output. */
-#define GDN_CHUNK_FWD_STAGES 3
+ * i+1 is the duration of stage i: 0 gate preparation with the chunk-local WY
+ * auxiliaries (one kernel), 1 inter-chunk state scan with output. */
+#define GDN_CHUNK_FWD_STAGES 2
 gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k,
                                const void *v, const float *a, const float *b,
                                const float *A_log, const float *dt_bias,

@@ -32,6 +32,12 @@ def test_header_declares_the_entry_points():
         assert required in names
 
 
+def test_library_resolves_all_symbols_at_load():
+    # RTLD_NOW: every undefined symbol (e.g. a kernel launch stub the host pass
+    # failed to emit) must resolve when the library is loaded
+    ctypes.CDLL(binding.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(binding.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(L, n)]
@@ -95,10 +101,11 @@ def test_workspace_bytes():
     L = binding.lib()
     d = dims(B=1, T=4096, Hk=16, Hv=64, Dk=128, Dv=128)
     n = L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(d))
-    units = 64 * 64
-    # per chunk unit: float64 + float32 gate vectors, 16 B token records, two 6 KB fragment sets
-    assert n >= units * (64 * 8 + 64 * 4 + 64 * 16 + 2 * 6 * 64 * 8 * 2)
-    assert n < units * 20000
+    vunits, kunits = 64 * 64, 16 * 64
+    # per (value head, chunk): 16 B token records and two 6 KB operand-fragment sets;
+    # per (key head, chunk): Q, K and K^T tile images (64 x 128 float16 each)
+    need = vunits * (64 * 16 + 2 * 6 * 64 * 8 * 2) + kunits * 3 * 64 * 128 * 2
+    assert need <= n < need + 8 * 256
     d_bad = dims(Hv=3)
     assert L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(d_bad)) == 0
     assert L.gdn_chunk_fwd_workspace_bytes(None) == 0
