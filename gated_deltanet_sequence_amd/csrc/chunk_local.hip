@@ -5,6 +5,8 @@
 //  1. Q and K rows of the chunk are converted to the operand type and staged in
 //     LDS as swizzled tile images; the images of Q, K and K^T are written to
 //     the workspace for the scan, which copies them into LDS byte for byte.
+//     The read-out scale is folded into Q here, so Q S, A_qk and q.k (every
+//     term of the output) carry it and the scan applies none.
 //  2. K K^T and Q K^T (lower-triangular 16x16 tiles) on the matrix cores, once
 //     per key head: they are shared by its Hv/Hk value heads.
 //  3. Per value head (one wave each): gate preparation -- g = -exp(A_log)
@@ -94,7 +96,7 @@ struct ChunkLocalCfg {
 
 template <bool F32, typename TIn, int DK>
 __global__ __launch_bounds__(256) void chunk_local_kernel(
-    int T, int Hk, int Hv, int NC, const TIn *__restrict__ q, const TIn *__restrict__ k,
+    int T, int Hk, int Hv, int NC, float scale, const TIn *__restrict__ q, const TIn *__restrict__ k,
     const float *__restrict__ a, const float *__restrict__ b, const float *__restrict__ A_log,
     const float *__restrict__ dt_bias, float *__restrict__ tok, typename mma<F32>::E *__restrict__ apair,
     typename mma<F32>::E *__restrict__ qpair, typename mma<F32>::E *__restrict__ qimg,
@@ -144,8 +146,8 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 #pragma unroll
         for (int it = 0; it < NPC; ++it) {
             const int idx = tid + 256 * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-            *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(ql[it]);
-            *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(qh[it]);
+            *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(scale * ql[it]);
+            *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(scale * qh[it]);
             *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(kl[it]);
             *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(kh[it]);
         }
@@ -229,13 +231,12 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         const double Glast = __shfl(Gd, 63, 64);
         Gs[lane] = Gd;
         Bs[lane] = be;
-        {
-            f4 rec;
-            rec[0] = be;
-            rec[1] = expf((float)Gd);
-            rec[2] = expf((float)(Glast - Gd));
-            rec[3] = QKt[tri_index(lane >> 4, lane >> 4) * 256 + (lane & 15) * 17];
-            *reinterpret_cast<f4 *>(tok + (vu * C + lane) * 4) = rec;
+        {   // token records, one 64-float row per quantity: beta, gamma, eta, q.k
+            float *tr = tok + vu * C * 4 + lane;
+            tr[0] = be;
+            tr[64] = expf((float)Gd);
+            tr[128] = expf((float)(Glast - Gd));
+            tr[192] = QKt[tri_index(lane >> 4, lane >> 4) * 256 + (lane & 15) * 17];
         }
         wave_lds_sync();
 
@@ -328,7 +329,7 @@ static hipError_t launch_chunk_local_t(const PrefillArgs &p, const PrefillWorksp
     typedef typename mma<F32>::E E;
     const int NC = (p.T + C - 1) / C;
     hipLaunchKernelGGL((chunk_local_kernel<F32, TIn, DK>), dim3(NC, p.Hk, p.B), dim3(256), 0, s, p.T,
-                       p.Hk, p.Hv, NC, (const TIn *)p.q, (const TIn *)p.k, p.a, p.b, p.A_log, p.dt_bias,
+                       p.Hk, p.Hv, NC, p.scale, (const TIn *)p.q, (const TIn *)p.k, p.a, p.b, p.A_log, p.dt_bias,
                        ws.tok, (E *)ws.apair, (E *)ws.qpair, (E *)ws.qimg, (E *)ws.kimg, (E *)ws.timg);
     return hipGetLastError();
 }

@@ -11,7 +11,7 @@ namespace gdn {
 // Workspace carve-up of the chunked prefill; every region is 256-byte aligned.
 // E is the operand type (float16 for bf16 inputs, float32 for float32 inputs).
 struct PrefillWorkspace {
-    float *tok;     // [B*Hv*NC*64][4]: beta, gamma = e^G, eta = e^(G_last - G), q.k
+    float *tok;     // [B*Hv*NC][4][64]: rows beta, gamma = e^G, eta = e^(G_last - G), q.k
     void *apair;    // [B*Hv*NC][6][64 lanes][8] E: strictly-lower (I+L)^{-1} operand fragments
     void *qpair;    // [B*Hv*NC][6][64 lanes][8] E: strictly-lower gated Q K^T operand fragments
     void *qimg;     // [B*Hk*NC][64][Dk] E: Q tile images
