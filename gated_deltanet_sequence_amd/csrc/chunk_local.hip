@@ -3,10 +3,11 @@
 // over chunks: one work-group of 4 waves per (sequence, key head, chunk).
 //
 //  1. Q and K rows of the chunk are converted to the operand type and staged in
-//     LDS as swizzled tile images; the images of Q, K and K^T are written to
-//     the workspace for the scan, which copies them into LDS byte for byte.
-//     The read-out scale is folded into Q here, so Q S, A_qk and q.k (every
-//     term of the output) carry it and the scan applies none.
+//     LDS as swizzled tile images; the images of Q and K (and K^T for float32
+//     operands) are written to the workspace for the scan, which copies them
+//     into LDS byte for byte.
+//     The read-out scale is folded into Q here, so Q S and A_qk (every term of
+//     the output) carry it and the scan applies none.
 //  2. K K^T and Q K^T (lower-triangular 16x16 tiles) on the matrix cores, once
 //     per key head: they are shared by its Hv/Hk value heads.
 //  3. Per value head (one wave each): gate preparation -- g = -exp(A_log)
@@ -17,8 +18,9 @@
 //     (computed once, shared by L and A_qk); L = beta Gamma (.) K K^T; the
 //     blocked inverse A = (I + L)^{-1} (diagonal 16x16 blocks by forward
 //     substitution in registers, off-diagonal blocks on the matrix cores); and
-//     the operand fragments of A and A_qk plus the per-token records the scan
-//     needs.
+//     the operand fragments of the two matrices the scan applies to its
+//     residual (A and A_qk with the per-token factors folded in) plus the
+//     per-token decay record.
 #include "prefill_common.h"
 
 namespace gdn {
@@ -29,12 +31,14 @@ size_t prefill_workspace_layout(int B, int T, int Hk, int Hv, int Dk, bool f32, 
     const size_t vunits = (size_t)B * Hv * NC, kunits = (size_t)B * Hk * NC;
     const size_t esz = f32 ? 4 : 2;
     size_t off = 0;
-    const size_t oT = off;  off = align256(off + vunits * C * 4 * sizeof(float));
+    const size_t oT = off;  off = align256(off + vunits * C * 2 * sizeof(float));
     const size_t oA = off;  off = align256(off + vunits * NPAIR * 64 * 8 * esz);
     const size_t oQ = off;  off = align256(off + vunits * NPAIR * 64 * 8 * esz);
     const size_t oQi = off; off = align256(off + kunits * C * Dk * esz);
     const size_t oKi = off; off = align256(off + kunits * C * Dk * esz);
-    const size_t oTi = off; off = align256(off + kunits * C * Dk * esz);
+    // K^T images only for float32 operands: the float16 scan reads K^T operands
+    // from the K image with transposed LDS reads
+    const size_t oTi = off; off = align256(off + (f32 ? kunits * C * Dk * esz : 0));
     if (ws) {
         char *p = (char *)base;
         ws->tok = (float *)(p + oT);
@@ -42,7 +46,7 @@ size_t prefill_workspace_layout(int B, int T, int Hk, int Hv, int Dk, bool f32, 
         ws->qpair = p + oQ;
         ws->qimg = p + oQi;
         ws->kimg = p + oKi;
-        ws->timg = p + oTi;
+        ws->timg = f32 ? p + oTi : nullptr;
         ws->bytes = off;
     }
     return off;
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     }
     __syncthreads();
 
-    // ---- images to the workspace: Q and K verbatim, K^T transposed
+    // ---- images to the workspace: Q and K verbatim, K^T transposed (float32)
     {
         typedef uint32_t u4v __attribute__((ext_vector_type(4)));
         const u4v *src = reinterpret_cast<const u4v *>(u_raw);
@@ -165,18 +169,20 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
             dq[i] = src[i];
             dk[i] = src[UNITS + i];
         }
-        E *dt = timg + ku * IMG;
-        constexpr int GPR = C / EPG;  // 16-byte groups per K^T row
-        for (int job = tid; job < DK * GPR; job += 256) {
-            const int R = job / GPR, gp = job % GPR;
-            const int pr = perm_col<F32>(R);
-            E vals[EPG];
+        if constexpr (F32) {
+            E *dt = timg + ku * IMG;
+            constexpr int GPR = C / EPG;  // 16-byte groups per K^T row
+            for (int job = tid; job < DK * GPR; job += 256) {
+                const int R = job / GPR, gp = job % GPR;
+                const int pr = perm_col<F32>(R);
+                E vals[EPG];
 #pragma unroll
-            for (int j = 0; j < EPG; ++j) {
-                const int tk = unperm_col<F32>(gp * EPG + j);
-                vals[j] = Ki[img_index<F32>(tk, DK, pr)];
+                for (int j = 0; j < EPG; ++j) {
+                    const int tk = unperm_col<F32>(gp * EPG + j);
+                    vals[j] = Ki[img_index<F32>(tk, DK, pr)];
+                }
+                *reinterpret_cast<u4v *>(dt + img_index<F32>(R, C, gp * EPG)) = *reinterpret_cast<const u4v *>(vals);
             }
-            *reinterpret_cast<u4v *>(dt + img_index<F32>(R, C, gp * EPG)) = *reinterpret_cast<const u4v *>(vals);
         }
     }
 
@@ -231,12 +237,12 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         const double Glast = __shfl(Gd, 63, 64);
         Gs[lane] = Gd;
         Bs[lane] = be;
-        {   // token records, one 64-float row per quantity: beta, gamma, eta, q.k
-            float *tr = tok + vu * C * 4 + lane;
-            tr[0] = be;
-            tr[64] = expf((float)Gd);
-            tr[128] = expf((float)(Glast - Gd));
-            tr[192] = QKt[tri_index(lane >> 4, lane >> 4) * 256 + (lane & 15) * 17];
+        {   // token record: gamma = e^G in token order, then again with token
+            // 16r + m at position 4m + r
+            float *tr = tok + vu * C * 2;
+            const float gam = expf((float)Gd);
+            tr[lane] = gam;
+            tr[64 + 4 * (lane & 15) + (lane >> 4)] = gam;
         }
         wave_lds_sync();
 
@@ -291,35 +297,67 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         inverse_offdiag<F32>(Xw, Lf, m, g);
         wave_lds_sync();
 
-        // operand fragments of strictly-lower(A) and strictly-lower(A_qk)
+        // Operand fragments of the two per-chunk matrices the scan applies to the
+        // residual R' = V - gamma (.) (K S):
+        //   Ae = diag(eta) A diag(beta)         -> eta (.) Delta = Ae R'
+        //   Ao = A_qk A diag(beta)              -> A_qk Delta    = Ao R'
+        // with A = (I + L)^{-1} (unit diagonal; Xw) and A_qk = Gamma (.) Q K^T
+        // including its diagonal.  Both are lower triangular with diagonal.
+        // Ao's blocks come from the matrix cores as Ao^T = A^T A_qk^T, whose
+        // accumulator tile is exactly the A-operand layout of Ao.
+        f4 aq[10];  // A_qk blocks (rb, kb), A-operand layout (row 16rb+m, columns 16kb+4g+s)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int kb = 0; kb <= rb; ++kb) {
+                const int ti = tri_index(rb, kb);
+                f4 gm = Gm[ti];
+                if (kb == rb)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) gm[s] = (4 * g + s == m) ? 1.f : gm[s];
+                aq[ti] = gm * *reinterpret_cast<const f4 *>(QKt + ti * 256 + m * 16 + 4 * g);
+            }
+        f4 xt[10];  // A^T blocks (kb, mb) as A operands: lane holds A[16mb+4g+s][16kb+m]
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int kb = 0; kb <= mb; ++kb)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) xt[tri_index(mb, kb)][s] = Xw[tri_index(mb, kb) * 256 + (4 * g + s) * 16 + m];
+
         E *ap = apair + vu * (NPAIR * 64 * 8) + lane * 8;
         E *qp = qpair + vu * (NPAIR * 64 * 8) + lane * 8;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r) {
+            const float eta = expf((float)(Glast - Gs[16 * r + m]));
 #pragma unroll
             for (int qq = 0; qq <= r / 2; ++qq) {
-                f4 xv[2], av[2];
+                f4 ev[2], ov[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int kb = 2 * qq + h;
-                    xv[h] = f4{0, 0, 0, 0};
-                    av[h] = f4{0, 0, 0, 0};
+                    ev[h] = f4{0, 0, 0, 0};
+                    ov[h] = f4{0, 0, 0, 0};
                     if (kb <= r) {
                         const int ti = tri_index(r, kb);
-                        f4 x4 = *reinterpret_cast<const f4 *>(Xw + ti * 256 + m * 16 + 4 * g);
-                        if (kb == r)
+                        const f4 bcol = *reinterpret_cast<const f4 *>(Bs + 16 * kb + 4 * g);
+                        const f4 x4 = *reinterpret_cast<const f4 *>(Xw + ti * 256 + m * 16 + 4 * g);
+                        ev[h] = eta * x4 * bcol;
+                        f4 acc = {0, 0, 0, 0};
 #pragma unroll
-                            for (int s = 0; s < 4; ++s) x4[s] = (4 * g + s < m) ? x4[s] : 0.f;
-                        xv[h] = x4;
-                        av[h] = Gm[ti] * *reinterpret_cast<const f4 *>(QKt + ti * 256 + m * 16 + 4 * g);
+                        for (int mb = kb; mb <= r; ++mb)
+                            acc = mma<F32>::block(acc, mma<F32>::from_f4(xt[tri_index(mb, kb)]),
+                                                  mma<F32>::from_f4(aq[tri_index(r, mb)]));
+                        ov[h] = acc * bcol;
                     }
                 }
                 const int p = pair_index(r, qq);
-                *reinterpret_cast<V4 *>(ap + p * 512) = mma<F32>::from_f4(xv[0]);
-                *reinterpret_cast<V4 *>(ap + p * 512 + 4) = mma<F32>::from_f4(xv[1]);
-                *reinterpret_cast<V4 *>(qp + p * 512) = mma<F32>::from_f4(av[0]);
-                *reinterpret_cast<V4 *>(qp + p * 512 + 4) = mma<F32>::from_f4(av[1]);
+                *reinterpret_cast<V4 *>(ap + p * 512) = mma<F32>::from_f4(ev[0]);
+                *reinterpret_cast<V4 *>(ap + p * 512 + 4) = mma<F32>::from_f4(ev[1]);
+                *reinterpret_cast<V4 *>(qp + p * 512) = mma<F32>::from_f4(ov[0]);
+                *reinterpret_cast<V4 *>(qp + p * 512 + 4) = mma<F32>::from_f4(ov[1]);
             }
+        }
         wave_lds_sync();
     }
 }

@@ -11,12 +11,12 @@ namespace gdn {
 // Workspace carve-up of the chunked prefill; every region is 256-byte aligned.
 // E is the operand type (float16 for bf16 inputs, float32 for float32 inputs).
 struct PrefillWorkspace {
-    float *tok;     // [B*Hv*NC][4][64]: rows beta, gamma = e^G, eta = e^(G_last - G), q.k
-    void *apair;    // [B*Hv*NC][6][64 lanes][8] E: strictly-lower (I+L)^{-1} operand fragments
-    void *qpair;    // [B*Hv*NC][6][64 lanes][8] E: strictly-lower gated Q K^T operand fragments
+    float *tok;     // [B*Hv*NC][2][64]: gamma = e^G by token, then token 16r+m at 4m+r
+    void *apair;    // [B*Hv*NC][6][64 lanes][8] E: diag(eta) (I+L)^{-1} diag(beta) operand fragments
+    void *qpair;    // [B*Hv*NC][6][64 lanes][8] E: A_qk (I+L)^{-1} diag(beta) operand fragments
     void *qimg;     // [B*Hk*NC][64][Dk] E: Q tile images
     void *kimg;     // [B*Hk*NC][64][Dk] E: K tile images
-    void *timg;     // [B*Hk*NC][Dk][64] E: K^T tile images
+    void *timg;     // [B*Hk*NC][Dk][64] E: K^T tile images (float32 operands only)
     size_t bytes;   // total
 };
 

@@ -44,20 +44,36 @@ __host__ __device__ constexpr int perm_col(int k) {
     return F32 ? k : (k & ~31) | (((k & 15) >> 2) << 3) | (((k & 31) >> 4) << 2) | (k & 3);
 }
 
-// Tile images.  Q and K of a chunk ([64 tokens][d_k]) and K^T ([d_k][64 tokens])
-// are kept as row-major tiles of the operand type, columns placed by perm_col
-// and each row's 16-byte groups XOR-swizzled with (row & 7): the 8 lanes that
-// read 16 consecutive-row operands in one instruction then hit 8 different
-// groups, i.e. all LDS banks, with no padding.  The chunk-local kernel writes
-// the images to the workspace in exactly this layout and the scan copies them
-// byte for byte into LDS.
+// Tile images.  Q and K of a chunk ([64 tokens][d_k]) and, for float32
+// operands, K^T ([d_k][64 tokens]) are kept as row-major tiles of the operand
+// type, columns placed by perm_col
+// and each row's 16-byte groups XOR-swizzled by a function of the row
+// (img_swz): the 16 lanes that read the same group of 16 consecutive rows in
+// one instruction then cover all 64 LDS banks (256 bytes), with no padding.
+// The chunk-local kernel writes the images to the workspace in exactly this
+// layout and the scan copies them byte for byte into LDS.
 template <bool F32>
 __host__ __device__ constexpr int img_epg() { return F32 ? 4 : 8; }  // elements per 16-byte group
+
+// Group swizzle of image row `row` (LDS has 64 four-byte banks, 256 bytes).
+// 256-byte float16 rows (16 groups) XOR the group with the low 4 bits of the
+// row, rotated by two: ((row & 3) << 2) | ((row >> 2) & 3).  Being a bijection
+// of row & 15, it keeps the operand reads of 16 consecutive rows (one group
+// each) on 16 distinct groups; and the transposed reads of the state update
+// -- 4 consecutive rows (row & 3 = 0..3) times 4 consecutive groups (the low
+// two group bits) -- also land on 16 distinct groups, since the row's low
+// bits go to the high group bits.  128-byte float16 rows hold two rows per
+// 256 bytes: XOR with (row >> 1) & 7, the row parity picks the half.
+// Float32 rows XOR with row & 7.
+template <bool F32>
+__host__ __device__ constexpr int img_swz(int row, int rowlen) {
+    return F32 ? (row & 7) : rowlen >= 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((row >> 1) & 7);
+}
 
 template <bool F32>
 __device__ __forceinline__ int img_index(int row, int rowlen, int phys) {
     constexpr int epg = img_epg<F32>();
-    return row * rowlen + (((phys / epg) ^ (row & 7)) * epg) + phys % epg;
+    return row * rowlen + (((phys / epg) ^ img_swz<F32>(row, rowlen)) * epg) + phys % epg;
 }
 
 // Operand pair (two 16-deep k-blocks, logical columns 32kq .. 32kq+31) of image
@@ -69,7 +85,7 @@ __device__ __forceinline__ void img_pair(const typename mma<F32>::E *X, int rowl
         a0 = *reinterpret_cast<const f4 *>(X + R * rowlen + 4 * ((8 * kq + g) ^ (R & 7)));
         a1 = *reinterpret_cast<const f4 *>(X + R * rowlen + 4 * ((8 * kq + 4 + g) ^ (R & 7)));
     } else {
-        const h8 v = *reinterpret_cast<const h8 *>(X + R * rowlen + 8 * ((4 * kq + g) ^ (R & 7)));
+        const h8 v = *reinterpret_cast<const h8 *>(X + R * rowlen + 8 * ((4 * kq + g) ^ img_swz<false>(R, rowlen)));
         a0 = h4{v[0], v[1], v[2], v[3]};
         a1 = h4{v[4], v[5], v[6], v[7]};
     }

@@ -1,30 +1,21 @@
 // state_scan.hip -- inter-chunk state scan with fused output (method and
 // notation in prefill_common.h).
 //
-// One work-group per (sequence, value head, NW*16 state columns) with NW
-// compute waves and NL loader waves.  Each compute wave owns 16 columns of the
-// float32 state S[d_k][16], held in matrix-core accumulator tiles for the whole
-// sequence; the columns of S are independent recurrences given K, beta, gamma
-// and A.  Per chunk, each compute wave runs on the matrix cores:
-//   P = K S, Qa = Q S                    (64 x d_k x 16 each)
-//   Delta = R + strictly-lower(A) R,     R = beta (V - gamma P)
-//   O = gamma Qa + (q.k) Delta + strictly-lower(A_qk) Delta
-//   S = gamma_C S + K^T (eta Delta)      (d_k x 64 x 16)
-// The accumulator tiles of S, R and Delta are the B operands of the next
-// product directly (see gdn_device.h), so the state never leaves registers, and
-// compute waves issue no global-memory instruction inside the chunk loop: the
-// output tile goes to LDS.
+// Per chunk, with R' = V - gamma (.) (K S) the residual of the chunk-start
+// state S, the chunk-local kernel has prepared two 64 x 64 lower-triangular
+// matrices (operand fragments "pairs"):
+//   Ae = diag(eta) A diag(beta)   so that   eta (.) Delta = Ae R'
+//   Ao = A_qk A diag(beta)        so that   A_qk Delta    = Ao R'
+// and the scan runs, all on the matrix cores:
+//   P = K S,  R' = V - gamma (.) P
+//   O = gamma (.) (Q S) + Ao R'
+//   S = gamma_C S + K^T (Ae R')
+// The columns of S are independent recurrences, so work-groups split the
+// value dimension.  Accumulator tiles of S and R' feed the next product as B
+// operands directly (see gdn_device.h), so the state never leaves registers.
 //
-// The loader waves do all global-memory traffic: while the compute waves work
-// on chunk n, they copy chunk n+1 -- the Q, K and K^T tile images written by
-// the chunk-local kernel, the A / A_qk operand fragments, the token records and
-// this group's V columns -- into the other LDS buffer with direct-to-LDS buffer
-// loads (16 bytes per lane), and write chunk n-1's output rows from LDS with
-// 16-byte stores.  V and the output go through buffer resources bounded at the
-// sequence end, so the ragged last chunk reads zeros and drops its stores with
-// no branches.  One barrier per chunk.  Work-groups that share a key head are
-// numbered consecutively and mapped onto the same XCD, so their common image
-// reads hit one L2.
+// Two kernels: scan_split_kernel (float16 operands, bfloat16 inputs) and
+// state_scan_kernel (float32 operands, float32 inputs), described at each.
 #include "prefill_common.h"
 
 namespace gdn {
@@ -143,7 +134,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
         const __amdgpu_buffer_rsrc_t rt = rsrc(timg + ku0 * C * DK, (size_t)NC * CF::IMG_BYTES);
         const __amdgpu_buffer_rsrc_t ra = rsrc(apair + vu0 * (NPAIR * 64 * 8), (size_t)NC * CF::FRAG_BYTES);
         const __amdgpu_buffer_rsrc_t rf = rsrc(qpair + vu0 * (NPAIR * 64 * 8), (size_t)NC * CF::FRAG_BYTES);
-        const __amdgpu_buffer_rsrc_t rtk = rsrc(tok + vu0 * C * 4, (size_t)NC * C * 16);
+        const __amdgpu_buffer_rsrc_t rtk = rsrc(tok + vu0 * C * 2, (size_t)NC * C * 8);
         const int lane16 = lane * 16;
         // 16-byte slot of this lane in tile unit u: row, swizzled piece, element offset
         auto tile_slot = [&](int u, int &row, int &piece) {
@@ -178,8 +169,8 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void_t *)(base + CF::OFF_V + u * 1024), 16,
                                                          voff * (int)sizeof(TIn), 0, 0, 0);
             }
-            if (l == 0)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rtk, (lds_void_t *)(base + CF::OFF_TK), 16, lane16, n * C * 16, 0, 0);
+            if (l == 0 && lane < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rtk, (lds_void_t *)(base + CF::OFF_TK), 16, lane16, n * C * 8, 0, 0);
         };
         // write chunk n's output rows from LDS output tile (n & 1), 16 bytes per lane
         auto store_rows = [&](int n) {
@@ -247,7 +238,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
         const E *Ks = reinterpret_cast<const E *>(base + CF::OFF_K);
         const E *Kt = reinterpret_cast<const E *>(base + CF::OFF_T);
         const TIn *Vs = reinterpret_cast<const TIn *>(base + CF::OFF_V);
-        const float *Tq = reinterpret_cast<const float *>(base + CF::OFF_TK);  // [beta|gamma|eta|q.k][64]
+        const float *Tq = reinterpret_cast<const float *>(base + CF::OFF_TK);  // [gamma | gamma by lane][64]
         const E *Af = reinterpret_cast<const E *>(base + CF::OFF_AF) + lane * 8;
         const E *Qf = reinterpret_cast<const E *>(base + CF::OFF_QF) + lane * 8;
         TIn *Os = reinterpret_cast<TIn *>(smem + CF::OFF_O + (size_t)(n & 1) * CF::TILE_BYTES);
@@ -255,11 +246,10 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
         auto tokq = [&](int x, int r) { return *reinterpret_cast<const f4 *>(Tq + 64 * x + 16 * r + 4 * g); };
 
         // operands of the residual, read ahead of the products that need them
-        f4 be[4], ga[4], vv[4];
+        f4 ga[4], vv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            be[r] = tokq(0, r);
-            ga[r] = tokq(1, r);
+            ga[r] = tokq(0, r);
 #pragma unroll
             for (int i = 0; i < 4; ++i) vv[r][i] = lds_in(Vs + tile_index(16 * r + 4 * g + i));
         }
@@ -303,36 +293,23 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
             ld_pair<F32>(Af + p * 512, afr[p][0], afr[p][1]);
             ld_pair<F32>(Qf + p * 512, qfr[p][0], qfr[p][1]);
         }
-        f4 et[4], dq[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            et[r] = tokq(2, r);
-            dq[r] = tokq(3, r);
-        }
 
-        // ---- R = beta (V - gamma P)
-        f4 R[4];
+        // ---- R' = V - gamma P
         V4 Rb[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            R[r] = be[r] * (vv[r] - ga[r] * P[r]);
-            Rb[r] = mma<F32>::from_f4(R[r]);
-        }
+        for (int r = 0; r < 4; ++r) Rb[r] = mma<F32>::from_f4(vv[r] - ga[r] * P[r]);
 
-        // ---- Delta = R + strictly-lower(A) R
-        f4 D[4];
-        V4 Db[4], De[4];
+        // ---- eta Delta = Ae R'
+        V4 De[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            f4 acc = R[r];
+            f4 acc = {0, 0, 0, 0};
 #pragma unroll
             for (int qq = 0; qq <= r / 2; ++qq) {
                 const int p = pair_index(r, qq);
                 acc = mma<F32>::pair(acc, afr[p][0], afr[p][1], Rb[2 * qq], Rb[2 * qq + 1]);
             }
-            D[r] = acc;
-            Db[r] = mma<F32>::from_f4(acc);
-            De[r] = mma<F32>::from_f4(et[r] * acc);
+            De[r] = mma<F32>::from_f4(acc);
         }
 
         // K^T operands of the state update, read ahead of it
@@ -342,22 +319,22 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) img_pair<F32>(Kt, C, 16 * kb + m, qq, g, tf[kb][qq][0], tf[kb][qq][1]);
 
-        // ---- O = gamma Qa + (q.k) Delta + strictly-lower(A_qk) Delta, into the
-        //      LDS output tile (the read-out scale is already folded into Q)
+        // ---- O = gamma Qa + Ao R', into the LDS output tile (the read-out
+        //      scale is already folded into Q and Ao)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            f4 acc = ga[r] * Qa[r] + dq[r] * D[r];
+            f4 acc = ga[r] * Qa[r];
 #pragma unroll
             for (int qq = 0; qq <= r / 2; ++qq) {
                 const int p = pair_index(r, qq);
-                acc = mma<F32>::pair(acc, qfr[p][0], qfr[p][1], Db[2 * qq], Db[2 * qq + 1]);
+                acc = mma<F32>::pair(acc, qfr[p][0], qfr[p][1], Rb[2 * qq], Rb[2 * qq + 1]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) lds_out(Os + tile_index(16 * r + 4 * g + i), acc[i]);
         }
 
         // ---- S = gamma_C S + K^T (eta Delta)
-        const float gC = Tq[64 + C - 1];
+        const float gC = Tq[C - 1];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f4 acc = gC * S[kb];
@@ -379,6 +356,419 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Role-split scan (float16 operands, bfloat16 inputs and outputs).
+//
+// One work-group per (sequence, value head, 32 state columns), four waves with
+// distinct roles, one per SIMD:
+//   state wave: holds S[d_k][32] in accumulator tiles (two 16-column tiles that
+//     share every K, K^T and Ae operand read) and runs the recurrence
+//     P = K S, R' = V - gamma P, S = gamma_C S + K^T (Ae R'); per chunk it hands
+//     the float16 operand pairs of the chunk-start S and of R' to the output
+//     wave through LDS;
+//   output wave, one chunk behind: O^T = gamma (S^T Q^T) + R'^T Ao^T.  The
+//     transposed products take the very same operand registers, and their
+//     accumulators give each lane 4 consecutive output columns of one token,
+//     written with one 8-byte store;
+//   two loader waves: copy the next chunk's inputs into LDS with direct-to-LDS
+//     buffer loads -- K, K^T, V, Ae and gamma for the state wave, Q, Ao and
+//     gamma for the output wave.
+// Only the state wave is on the chunk-to-chunk critical path.  Inputs of both
+// consumers and the hand-over are double-buffered: one barrier per chunk.
+// ---------------------------------------------------------------------------
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+// Operand pair of image row R as one 8-value register group (float16 images).
+__device__ __forceinline__ h8 img_h8(const _Float16 *X, int rowlen, int R, int kq, int g) {
+    return *reinterpret_cast<const h8 *>(X + R * rowlen + 8 * ((4 * kq + g) ^ img_swz<false>(R, rowlen)));
+}
+
+template <typename TIn, int DK, int NL>
+struct SplitCfg {
+    static constexpr int NT = 2;                                   // 16-column tiles per work-group
+    static constexpr int NCOL = 16 * NT;
+    static constexpr int NKQ = DK / 32;                            // 32-deep contraction steps over d_k
+    static constexpr int IMG_BYTES = C * DK * 2;
+    static constexpr int FRAG_BYTES = NPAIR * 64 * 8 * 2;
+    static constexpr int TOK_BYTES = C * 8;                        // gamma twice (two orders)
+    static constexpr int TILE_BYTES = C * NCOL * (int)sizeof(TIn);  // V tile
+    static constexpr int VSPR = NCOL * (int)sizeof(TIn) / 16;       // 16-byte slots per V row
+    static constexpr int VEPS = 16 / (int)sizeof(TIn);              // elements per slot
+    // state-wave inputs of one chunk
+    static constexpr int S_K = 0, S_V = S_K + IMG_BYTES, S_A = S_V + TILE_BYTES,
+                         S_TK = S_A + FRAG_BYTES, S_BUF = S_TK + TOK_BYTES;
+    // output-wave inputs of one chunk
+    static constexpr int O_Q = 0, O_F = O_Q + IMG_BYTES, O_TK = O_F + FRAG_BYTES, O_BUF = O_TK + TOK_BYTES;
+    // hand-over: S (d_k x 16) and R' (64 x 16) of each column tile as operand pairs, 1 KB each
+    static constexpr int X_S = 0, X_R = NT * NKQ * 1024, X_BUF = X_R + NT * 2 * 1024;
+    static constexpr int OFF_S = 0, OFF_O = 2 * S_BUF, OFF_X = OFF_O + 2 * O_BUF, LDS = OFF_X + 2 * X_BUF;
+    static constexpr int IMG_UNITS = IMG_BYTES / 1024, FRAG_UNITS = FRAG_BYTES / 1024,
+                         TILE_UNITS = TILE_BYTES / 1024;
+    static_assert(IMG_UNITS % NL == 0 && FRAG_UNITS % NL == 0 && TILE_UNITS % NL == 0, "copy split");
+    static_assert(VSPR >= 4 && (VSPR & (VSPR - 1)) == 0, "V slots");
+    static_assert(S_BUF % 16 == 0 && O_BUF % 16 == 0, "alignment");
+    static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+// Loader-wave copies of one chunk's inputs into LDS: 16 bytes per lane per
+// instruction, straight from memory into LDS (no registers).
+template <typename TIn, int DK, int NL>
+struct SplitLoader {
+    typedef SplitCfg<TIn, DK, NL> CF;
+    __amdgpu_buffer_rsrc_t vres, rq, rk, ra, rf, rtk;
+    int l, lane;
+    unsigned vcol;  // element offset of this group's first V column in a token row
+    unsigned vrow;  // elements per token row of V (Hv * d_v)
+
+    __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t r, char *dst, int src_off) const {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, lane * 16, src_off, 0, 0);
+    }
+    // state-wave inputs: K image, Ae fragments, V columns, gamma
+    __device__ __forceinline__ void stage_state(char *smem, int n, int buf) const {
+        char *base = smem + CF::OFF_S + buf * CF::S_BUF;
+        const int io = n * CF::IMG_BYTES, fo = n * CF::FRAG_BYTES;
+#pragma unroll
+        for (int i = 0; i < CF::IMG_UNITS / NL; ++i) {
+            const int u = (l + NL * i) * 1024;
+            copy(rk, base + CF::S_K + u, io + u);
+        }
+#pragma unroll
+        for (int i = 0; i < CF::FRAG_UNITS / NL; ++i) {
+            const int u = (l + NL * i) * 1024;
+            copy(ra, base + CF::S_A + u, fo + u);
+        }
+#pragma unroll
+        for (int i = 0; i < CF::TILE_UNITS / NL; ++i) {
+            const int u = l + NL * i;
+            const int slot = u * 64 + lane;
+            const int row = slot / CF::VSPR;
+            const int piece = (slot % CF::VSPR) ^ ((row >> 2) & (CF::VSPR - 1));
+            const unsigned voff = ((unsigned)(n * C + row) * vrow + vcol + piece * CF::VEPS) * (unsigned)sizeof(TIn);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void_t *)(base + CF::S_V + u * 1024), 16, (int)voff, 0, 0, 0);
+        }
+        if (l == 0 && lane < CF::TOK_BYTES / 16) copy(rtk, base + CF::S_TK, n * CF::TOK_BYTES);
+    }
+    // output-wave inputs: Q image, Ao fragments, gamma
+    __device__ __forceinline__ void stage_out(char *smem, int n, int buf) const {
+        char *base = smem + CF::OFF_O + buf * CF::O_BUF;
+        const int io = n * CF::IMG_BYTES, fo = n * CF::FRAG_BYTES;
+#pragma unroll
+        for (int i = 0; i < CF::IMG_UNITS / NL; ++i) {
+            const int u = (l + NL * i) * 1024;
+            copy(rq, base + CF::O_Q + u, io + u);
+        }
+#pragma unroll
+        for (int i = 0; i < CF::FRAG_UNITS / NL; ++i) {
+            const int u = (l + NL * i) * 1024;
+            copy(rf, base + CF::O_F + u, fo + u);
+        }
+        if (l == NL - 1 && lane < CF::TOK_BYTES / 16) copy(rtk, base + CF::O_TK, n * CF::TOK_BYTES);
+    }
+};
+
+template <typename TIn, int DK, int DV, int NL>
+__global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
+    int T, int Hk, int Hv, int NC, const TIn *__restrict__ v, const float *__restrict__ tok,
+    const _Float16 *__restrict__ apair, const _Float16 *__restrict__ qpair,
+    const _Float16 *__restrict__ qimg, const _Float16 *__restrict__ kimg,
+    const float *__restrict__ S0, TIn *__restrict__ out, float *__restrict__ ST) {
+    static_assert(sizeof(TIn) == 2, "bfloat16 inputs");
+    typedef SplitCfg<TIn, DK, NL> CF;
+    typedef _Float16 E;
+    constexpr int NT = CF::NT, NCOL = CF::NCOL, NKB = DK / 16, NKQ = CF::NKQ, NCG = DV / NCOL;
+
+    __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
+
+    // XCD-aware numbering: work-groups are dealt round-robin to the 8 XCDs, so
+    // give each XCD a contiguous range of logical ids (same key head nearby).
+    const int nblk = gridDim.x;
+    int lid = blockIdx.x;
+    if ((nblk & 7) == 0) lid = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int cg = lid % NCG;
+    const int hv = (lid / NCG) % Hv;
+    const int bb = lid / (NCG * Hv);
+    const int hk = hv / (Hv / Hk);
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const size_t seq_elems = (size_t)T * Hv * DV;
+    auto rsrc = [](const void *p, size_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+    };
+
+    if (w >= 2) {
+        // ================= loader waves =================
+        const size_t ku0 = ((size_t)bb * Hk + hk) * NC, vu0 = ((size_t)bb * Hv + hv) * NC;
+        SplitLoader<TIn, DK, NL> ld;
+        ld.vres = rsrc(v + (size_t)bb * seq_elems, seq_elems * sizeof(TIn));
+        ld.rq = rsrc(qimg + ku0 * C * DK, (size_t)NC * CF::IMG_BYTES);
+        ld.rk = rsrc(kimg + ku0 * C * DK, (size_t)NC * CF::IMG_BYTES);
+        ld.ra = rsrc(apair + vu0 * (NPAIR * 64 * 8), (size_t)NC * CF::FRAG_BYTES);
+        ld.rf = rsrc(qpair + vu0 * (NPAIR * 64 * 8), (size_t)NC * CF::FRAG_BYTES);
+        ld.rtk = rsrc(tok + vu0 * C * 2, (size_t)NC * CF::TOK_BYTES);
+        ld.l = w - 2;
+        ld.lane = lane;
+        ld.vcol = (unsigned)(hv * DV + NCOL * cg);
+        ld.vrow = (unsigned)(Hv * DV);
+
+        ld.stage_state(smem, 0, 0);
+        wait_vmcnt<0>();
+        bare_barrier();
+        for (int n = 0; n < NC; ++n) {
+            if (n + 1 < NC) ld.stage_state(smem, n + 1, (n + 1) & 1);
+            ld.stage_out(smem, n, n & 1);
+            wait_vmcnt<0>();
+            bare_barrier();
+        }
+        return;
+    }
+
+    if (w == 1) {
+        // ================= output wave (one chunk behind) =================
+        const __amdgpu_buffer_rsrc_t ores = rsrc(out + (size_t)bb * seq_elems, seq_elems * sizeof(TIn));
+        const unsigned col = NCOL * cg + 4 * g;
+        auto emit = [&](int n) {
+            const char *ob = smem + CF::OFF_O + (n & 1) * CF::O_BUF;
+            const E *Qs = reinterpret_cast<const E *>(ob + CF::O_Q);
+            const E *Of = reinterpret_cast<const E *>(ob + CF::O_F) + lane * 8;
+            const float *Tq = reinterpret_cast<const float *>(ob + CF::O_TK);
+            const char *xb = smem + CF::OFF_X + (n & 1) * CF::X_BUF;
+            h8 Sp[NT][NKQ], Rp[NT][2];
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+#pragma unroll
+                for (int j = 0; j < NKQ; ++j)
+                    Sp[c][j] = *reinterpret_cast<const h8 *>(xb + CF::X_S + (c * NKQ + j) * 1024 + lane * 16);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    Rp[c][j] = *reinterpret_cast<const h8 *>(xb + CF::X_R + (c * 2 + j) * 1024 + lane * 16);
+            }
+            const f4 gam = *reinterpret_cast<const f4 *>(Tq + 64 + 4 * m);  // tokens m, 16+m, 32+m, 48+m
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                f4 sq[NT];
+#pragma unroll
+                for (int c = 0; c < NT; ++c) sq[c] = f4{0, 0, 0, 0};
+#pragma unroll
+                for (int kq = 0; kq < NKQ; ++kq) {
+                    const h8 qf = img_h8(Qs, DK, 16 * r + m, kq, g);
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) sq[c] = mfma_f16_k32(Sp[c][kq], qf, sq[c]);
+                }
+                f4 acc[NT];
+#pragma unroll
+                for (int c = 0; c < NT; ++c) acc[c] = gam[r] * sq[c];
+#pragma unroll
+                for (int qq = 0; qq <= r / 2; ++qq) {
+                    const h8 f = *reinterpret_cast<const h8 *>(Of + pair_index(r, qq) * 512);
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) acc[c] = mfma_f16_k32(Rp[c][qq], f, acc[c]);
+                }
+                // lane holds O[token 16r + m][col + 16c .. + 3]
+                typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+                typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+                const unsigned t = (unsigned)(n * C + 16 * r + m);
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+                    const bf4 hb = __builtin_convertvector(acc[c], bf4);
+                    u2v bits;
+                    __builtin_memcpy(&bits, &hb, 8);
+                    __builtin_amdgcn_raw_buffer_store_b64(bits, ores, (int)(((t * Hv + hv) * DV + col + 16 * c) * 2u), 0, 0);
+                }
+            }
+        };
+        bare_barrier();
+        for (int n = 0; n < NC; ++n) {
+            if (n > 0) emit(n - 1);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this chunk's LDS reads are done
+            bare_barrier();
+        }
+        if (NC > 0) emit(NC - 1);
+        return;
+    }
+
+    // ================= state wave =================
+    f4 S[NT][NKB];
+    const size_t sb = ((size_t)bb * Hv + hv) * DK * DV;
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[c][kb][i] = S0 ? S0[sb + (size_t)(16 * kb + 4 * g + i) * DV + NCOL * cg + 16 * c + m] : 0.f;
+
+    // Transposed reads (ds_read_b64_tr_b16): in each 16-lane group, lane 4i + q
+    // supplies the address of 4 consecutive 16-bit values -- columns 4q .. 4q+3
+    // of row i of a 4 x 16 block -- and lane j receives column j of the 4 rows.
+    //
+    // V: lane (g, m) points at row 16r + 4g + m/4, columns 16c + 4(m%4) .. +3 of
+    // the V tile and receives V[16r + 4g + i][16c + m], i = 0..3.
+    int vt_off[NT][4];
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * r + 4 * g + (m >> 2), cc = 16 * c + 4 * (m & 3);
+            const int piece = (cc / CF::VEPS) ^ ((row >> 2) & (CF::VSPR - 1));
+            vt_off[c][r] = (row * NCOL + piece * CF::VEPS + cc % CF::VEPS) * (int)sizeof(TIn);
+        }
+    // K^T operands of the state update from the K image: the A operand of pair
+    // (kb, qq) holds K[32qq + 16h + 4g + i][16kb + m] (h = 0, 1; i = 0..3), so lane
+    // (g, m) points at image row 32qq + 16h + 4g + m/4, logical columns
+    // 16kb + 4(m%4) .. +3 -- 4 values that perm_col keeps adjacent, at group
+    // 4(kb/2) + m%4, element 4(kb%2).  Rows differ between (qq, h) only by
+    // multiples of 16, which leave the swizzle unchanged: one address per kb,
+    // the row steps become immediate offsets.
+    int kt_off[NKB];
+    {
+        const int row = 4 * g + (m >> 2);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int grp = (4 * (kb >> 1) + (m & 3)) ^ img_swz<false>(row, DK);
+            kt_off[kb] = (row * DK + grp * 8 + 4 * (kb & 1)) * 2;
+        }
+    }
+
+    // Operands of P for chunk n (K, V, gamma, gamma_C), read one chunk ahead:
+    // right after the barrier that publishes chunk n, while chunk n-1's state
+    // update runs.
+    h8 kf[NKQ][4];
+    s4 vt[NT][4];
+    f4 ga[4];  // gamma of rows 16r + 4g + i
+    float gC;
+    auto read_p_operands = [&](int n) {
+        const char *base = smem + CF::OFF_S + (n & 1) * CF::S_BUF;
+        const E *Ks = reinterpret_cast<const E *>(base + CF::S_K);
+        const float *Tq = reinterpret_cast<const float *>(base + CF::S_TK);
+#pragma unroll
+        for (int kq = 0; kq < NKQ; ++kq)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) kf[kq][r] = img_h8(Ks, DK, 16 * r + m, kq, g);
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vt[c][r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + CF::S_V + vt_off[c][r]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ga[r] = *reinterpret_cast<const f4 *>(Tq + 16 * r + 4 * g);
+        gC = Tq[C - 1];
+    };
+
+    // A wave64 vector instruction takes 4 cycles, a 16x16x32 product 16 on its
+    // own unit: the vector work of each phase (operand conversions, the decay
+    // of S, the residual) is written next to independent products so the two
+    // overlap.
+    bare_barrier();  // chunk 0 staged
+    if (NC > 0) read_p_operands(0);
+    for (int n = 0; n < NC; ++n) {
+        const char *base = smem + CF::OFF_S + (n & 1) * CF::S_BUF;
+        const char *Ks8 = base + CF::S_K;
+        const E *Af = reinterpret_cast<const E *>(base + CF::S_A) + lane * 8;
+        char *xb = smem + CF::OFF_X + (n & 1) * CF::X_BUF;
+        // K^T operand pair (kb, qq): two transposed reads, rows 32qq and 32qq + 16 on
+        auto kt_pair = [&](int kb, int qq) {
+            const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(Ks8 + kt_off[kb] + 32 * qq * DK * 2));
+            const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(Ks8 + kt_off[kb] + (32 * qq + 16) * DK * 2));
+            return cat_h8(__builtin_bit_cast(h4, lo), __builtin_bit_cast(h4, hi));
+        };
+
+        // ---- P = K S.  Per contraction step kq: the float16 pairs of S rows
+        //      32kq .. 32kq + 31 (B operand here, and -- as S^T -- the output
+        //      wave's A operand, handed over), then those rows decay by gamma_C
+        //      (the state update accumulates onto them), and the K^T operands
+        //      of state-update rows 32kq .. 32kq + 31 are read into the
+        //      registers this step's K operands free.
+        f4 P[NT][4];
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) P[c][r] = f4{0, 0, 0, 0};
+        h8 tf[NKB][2];
+#pragma unroll
+        for (int kq = 0; kq < NKQ; ++kq) {
+            h8 Sp[NT];
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                Sp[c] = cat_h8(to_h4(S[c][2 * kq]), to_h4(S[c][2 * kq + 1]));
+                *reinterpret_cast<h8 *>(xb + CF::X_S + (c * NKQ + kq) * 1024 + lane * 16) = Sp[c];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < NT; ++c) P[c][r] = mfma_f16_k32(kf[kq][r], Sp[c], P[c][r]);
+#pragma unroll
+            for (int kb = 2 * kq; kb < 2 * kq + 2; ++kb)
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq) tf[kb][qq] = kt_pair(kb, qq);
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                S[c][2 * kq] *= gC;
+                S[c][2 * kq + 1] *= gC;
+            }
+        }
+        h8 afr[NPAIR];
+#pragma unroll
+        for (int p = 0; p < NPAIR; ++p) afr[p] = *reinterpret_cast<const h8 *>(Af + p * 512);
+
+        // ---- per column tile: R' = V - gamma P (handed over as operand pairs),
+        //      then eta Delta = Ae R'; one tile's products run under the other
+        //      tile's vector work
+        h4 De[NT][4];
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            h4 Rb[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                f4 vv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vv[i] = bf16_to_f32((uint16_t)vt[c][r][i]);
+                Rb[r] = to_h4(vv - ga[r] * P[c][r]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                *reinterpret_cast<h8 *>(xb + CF::X_R + (c * 2 + j) * 1024 + lane * 16) = cat_h8(Rb[2 * j], Rb[2 * j + 1]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                f4 acc = {0, 0, 0, 0};
+#pragma unroll
+                for (int qq = 0; qq <= r / 2; ++qq)
+                    acc = mfma_f16_k32(afr[pair_index(r, qq)], cat_h8(Rb[2 * qq], Rb[2 * qq + 1]), acc);
+                De[c][r] = to_h4(acc);
+            }
+        }
+
+        // every LDS access of this chunk is complete (its operands are in
+        // registers, the hand-over is written): publish, and let the loaders
+        // refill this buffer; then read the next chunk's P operands under the
+        // state update
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        bare_barrier();
+        if (n + 1 < NC) read_p_operands(n + 1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- S = gamma_C S + K^T (eta Delta)   (S already decayed above)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int c = 0; c < NT; ++c)
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq)
+                    S[c][kb] = mfma_f16_k32(tf[kb][qq], cat_h8(De[c][2 * qq], De[c][2 * qq + 1]), S[c][kb]);
+    }
+
+    if (ST) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    ST[sb + (size_t)(16 * kb + 4 * g + i) * DV + NCOL * cg + 16 * c + m] = S[c][kb][i];
+    }
+}
+
 // T == 0: the final state is the initial state (or zero).
 __global__ void state_copy_kernel(size_t n, const float *__restrict__ S0, float *__restrict__ ST) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -388,14 +778,25 @@ __global__ void state_copy_kernel(size_t n, const float *__restrict__ S0, float 
 template <bool F32, typename TIn, int DK, int DV>
 static hipError_t launch_scan_t(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s) {
     typedef typename mma<F32>::E E;
-    constexpr int NW = 2, NL = 2;
-    const int NC = (p.T + C - 1) / C;
-    const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / (16 * NW)));
-    hipLaunchKernelGGL((state_scan_kernel<F32, TIn, DK, DV, NW, NL>), dim3(blocks), dim3(64 * (NW + NL)), 0, s,
-                       p.T, p.Hk, p.Hv, NC, (const TIn *)p.v, ws.tok, (const E *)ws.apair,
-                       (const E *)ws.qpair, (const E *)ws.qimg, (const E *)ws.kimg, (const E *)ws.timg,
-                       p.S0, (TIn *)p.out, p.ST);
-    return hipGetLastError();
+    if constexpr (!F32) {
+        constexpr int NL = 2;
+        const int NC = (p.T + C - 1) / C;
+        const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<TIn, DK, NL>::NCOL));
+        hipLaunchKernelGGL((scan_split_kernel<TIn, DK, DV, NL>), dim3(blocks), dim3(64 * (2 + NL)), 0, s,
+                           p.T, p.Hk, p.Hv, NC, (const TIn *)p.v, ws.tok, (const E *)ws.apair,
+                           (const E *)ws.qpair, (const E *)ws.qimg, (const E *)ws.kimg,
+                           p.S0, (TIn *)p.out, p.ST);
+        return hipGetLastError();
+    } else {
+        constexpr int NW = 2, NL = 2;
+        const int NC = (p.T + C - 1) / C;
+        const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / (16 * NW)));
+        hipLaunchKernelGGL((state_scan_kernel<F32, TIn, DK, DV, NW, NL>), dim3(blocks), dim3(64 * (NW + NL)), 0, s,
+                           p.T, p.Hk, p.Hv, NC, (const TIn *)p.v, ws.tok, (const E *)ws.apair,
+                           (const E *)ws.qpair, (const E *)ws.qimg, (const E *)ws.kimg, (const E *)ws.timg,
+                           p.S0, (TIn *)p.out, p.ST);
+        return hipGetLastError();
+    }
 }
 
 template <bool F32, typename TIn>

@@ -102,9 +102,9 @@ def test_workspace_bytes():
     d = dims(B=1, T=4096, Hk=16, Hv=64, Dk=128, Dv=128)
     n = L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(d))
     vunits, kunits = 64 * 64, 16 * 64
-    # per (value head, chunk): 16 B token records and two 6 KB operand-fragment sets;
-    # per (key head, chunk): Q, K and K^T tile images (64 x 128 float16 each)
-    need = vunits * (64 * 16 + 2 * 6 * 64 * 8 * 2) + kunits * 3 * 64 * 128 * 2
+    # per (value head, chunk): 8 B token records and two 6 KB operand-fragment sets;
+    # per (key head, chunk): Q and K tile images (64 x 128 float16 each)
+    need = vunits * (64 * 8 + 2 * 6 * 64 * 8 * 2) + kunits * 2 * 64 * 128 * 2
     assert need <= n < need + 8 * 256
     d_bad = dims(Hv=3)
     assert L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(d_bad)) == 0
