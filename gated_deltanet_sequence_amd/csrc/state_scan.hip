@@ -598,12 +598,11 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
             for (int i = 0; i < 4; ++i)
                 S[c][kb][i] = S0 ? S0[sb + (size_t)(16 * kb + 4 * g + i) * DV + NCOL * cg + 16 * c + m] : 0.f;
 
-    // Transposed reads (ds_read_b64_tr_b16): in each 16-lane group, lane 4i + q
-    // supplies the address of 4 consecutive 16-bit values -- columns 4q .. 4q+3
-    // of row i of a 4 x 16 block -- and lane j receives column j of the 4 rows.
-    //
-    // V: lane (g, m) points at row 16r + 4g + m/4, columns 16c + 4(m%4) .. +3 of
-    // the V tile and receives V[16r + 4g + i][16c + m], i = 0..3.
+    // Transposed V reads (ds_read_b64_tr_b16): in each 16-lane group, lane
+    // 4i + q supplies the address of 4 consecutive 16-bit values -- columns
+    // 4q .. 4q+3 of row i of a 4 x 16 block -- and lane j receives column j of
+    // the 4 rows.  Lane (g, m) points at row 16r + 4g + m/4, columns
+    // 16c + 4(m%4) .. +3 of the V tile and receives V[16r + 4g + i][16c + m].
     int vt_off[NT][4];
 #pragma unroll
     for (int c = 0; c < NT; ++c)
@@ -613,13 +612,15 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
             const int piece = (cc / CF::VEPS) ^ ((row >> 2) & (CF::VSPR - 1));
             vt_off[c][r] = (row * NCOL + piece * CF::VEPS + cc % CF::VEPS) * (int)sizeof(TIn);
         }
-    // K^T operands of the state update from the K image: the A operand of pair
-    // (kb, qq) holds K[32qq + 16h + 4g + i][16kb + m] (h = 0, 1; i = 0..3), so lane
-    // (g, m) points at image row 32qq + 16h + 4g + m/4, logical columns
-    // 16kb + 4(m%4) .. +3 -- 4 values that perm_col keeps adjacent, at group
-    // 4(kb/2) + m%4, element 4(kb%2).  Rows differ between (qq, h) only by
-    // multiples of 16, which leave the swizzle unchanged: one address per kb,
-    // the row steps become immediate offsets.
+
+    // K^T operands of the state update from the K image, by transposed reads:
+    // the A operand of pair (kb, qq) holds K[32qq + 16h + 4g + i][16kb + m]
+    // (h = 0, 1; i = 0..3), so lane (g, m) points at image row
+    // 32qq + 16h + 4g + m/4, logical columns 16kb + 4(m%4) .. +3 -- 4 values
+    // that perm_col keeps adjacent, at group 4(kb/2) + m%4, element 4(kb%2).
+    // Rows differ between (qq, h) only by multiples of 16, which leave the
+    // swizzle unchanged: one address per kb, the row steps are immediate
+    // offsets.
     int kt_off[NKB];
     {
         const int row = 4 * g + (m >> 2);
@@ -630,17 +631,19 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
         }
     }
 
-    // Operands of P for chunk n (K, V, gamma, gamma_C), read one chunk ahead:
-    // right after the barrier that publishes chunk n, while chunk n-1's state
-    // update runs.
+    // Operands of chunk n (K, V, gamma, gamma_C, Ae), read one chunk ahead:
+    // right after the barrier that publishes chunk n, under chunk n-1's state
+    // update.
     h8 kf[NKQ][4];
     s4 vt[NT][4];
     f4 ga[4];  // gamma of rows 16r + 4g + i
     float gC;
-    auto read_p_operands = [&](int n) {
+    h8 afr[NPAIR];
+    auto read_operands = [&](int n) {
         const char *base = smem + CF::OFF_S + (n & 1) * CF::S_BUF;
         const E *Ks = reinterpret_cast<const E *>(base + CF::S_K);
         const float *Tq = reinterpret_cast<const float *>(base + CF::S_TK);
+        const E *Af = reinterpret_cast<const E *>(base + CF::S_A) + lane * 8;
 #pragma unroll
         for (int kq = 0; kq < NKQ; ++kq)
 #pragma unroll
@@ -653,18 +656,34 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) ga[r] = *reinterpret_cast<const f4 *>(Tq + 16 * r + 4 * g);
         gC = Tq[C - 1];
+#pragma unroll
+        for (int p = 0; p < NPAIR; ++p) afr[p] = *reinterpret_cast<const h8 *>(Af + p * 512);
     };
 
-    // A wave64 vector instruction takes 4 cycles, a 16x16x32 product 16 on its
-    // own unit: the vector work of each phase (operand conversions, the decay
-    // of S, the residual) is written next to independent products so the two
-    // overlap.
+    // Instruction schedule.  A wave64 vector instruction occupies the SIMD for
+    // 4 cycles, a 16x16x32 product the matrix unit for 16; the two overlap only
+    // if they are interleaved, and the compiler, left alone, groups them (and
+    // issues LDS reads just before their use).  So each phase below is a
+    // sequence of fenced steps: one product plus the independent vector / LDS
+    // work that fits under it.
+    //   A  P = K S for column tile 0 | S operand pairs, hand-over, K^T reads
+    //   B  P for tile 1               | K^T reads, R' = V - gamma P of tile 0
+    // (K^T comes from the K image by transposed reads rather than from a K^T
+    // image: the copy of a K^T image would add 16 KB per chunk to the loads,
+    // which already run near the CU's vector-memory rate)
+    //   C  Ae R' for tile 0           | R' of tile 1
+    //   D  Ae R' for tile 1           | float16 eta Delta of tile 0, decay of S rows 0..31
+    //   -- barrier: chunk n+1 is staged, this chunk's buffer is released
+    //   E  S += K^T (eta Delta)       | next chunk's operand reads, decay of the
+    //                                   next S rows, eta Delta of tile 1
+#define GDN_STEP() __builtin_amdgcn_sched_barrier(0)
+    constexpr int NSTEP = 4 * NKQ;     // products in phase A or B
+    constexpr int AE_R[6] = {0, 1, 2, 3, 2, 3}, AE_Q[6] = {0, 0, 0, 0, 1, 1};  // Ae R' order
+
     bare_barrier();  // chunk 0 staged
-    if (NC > 0) read_p_operands(0);
+    if (NC > 0) read_operands(0);
     for (int n = 0; n < NC; ++n) {
-        const char *base = smem + CF::OFF_S + (n & 1) * CF::S_BUF;
-        const char *Ks8 = base + CF::S_K;
-        const E *Af = reinterpret_cast<const E *>(base + CF::S_A) + lane * 8;
+        const char *Ks8 = smem + CF::OFF_S + (n & 1) * CF::S_BUF + CF::S_K;
         char *xb = smem + CF::OFF_X + (n & 1) * CF::X_BUF;
         // K^T operand pair (kb, qq): two transposed reads, rows 32qq and 32qq + 16 on
         auto kt_pair = [&](int kb, int qq) {
@@ -672,91 +691,118 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
             const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(Ks8 + kt_off[kb] + (32 * qq + 16) * DK * 2));
             return cat_h8(__builtin_bit_cast(h4, lo), __builtin_bit_cast(h4, hi));
         };
-
-        // ---- P = K S.  Per contraction step kq: the float16 pairs of S rows
-        //      32kq .. 32kq + 31 (B operand here, and -- as S^T -- the output
-        //      wave's A operand, handed over), then those rows decay by gamma_C
-        //      (the state update accumulates onto them), and the K^T operands
-        //      of state-update rows 32kq .. 32kq + 31 are read into the
-        //      registers this step's K operands free.
+        h8 Sp[NT][NKQ];
+        h8 tf[NKB][2];
         f4 P[NT][4];
+        h4 Rb[NT][4];
+        f4 Rx[4];
+        h4 De[NT][4];
+        f4 Ae[NT][4];
 #pragma unroll
         for (int c = 0; c < NT; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) P[c][r] = f4{0, 0, 0, 0};
-        h8 tf[NKB][2];
+            for (int r = 0; r < 4; ++r) P[c][r] = Ae[c][r] = f4{0, 0, 0, 0};
+        // residual of column tile c, row tile rr, in three steps
+        auto resid = [&](int c, int item) {
+            const int rr = item / 3, part = item % 3;
+            if (part == 0) {
 #pragma unroll
-        for (int kq = 0; kq < NKQ; ++kq) {
-            h8 Sp[NT];
-#pragma unroll
-            for (int c = 0; c < NT; ++c) {
-                Sp[c] = cat_h8(to_h4(S[c][2 * kq]), to_h4(S[c][2 * kq + 1]));
-                *reinterpret_cast<h8 *>(xb + CF::X_S + (c * NKQ + kq) * 1024 + lane * 16) = Sp[c];
+                for (int i = 0; i < 4; ++i) Rx[rr][i] = bf16_to_f32((uint16_t)vt[c][rr][i]);
+            } else if (part == 1) {
+                Rx[rr] = Rx[rr] - ga[rr] * P[c][rr];
+            } else {
+                Rb[c][rr] = to_h4(Rx[rr]);
+                if (rr & 1)
+                    *reinterpret_cast<h8 *>(xb + CF::X_R + (c * 2 + rr / 2) * 1024 + lane * 16) =
+                        cat_h8(Rb[c][rr - 1], Rb[c][rr]);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < NT; ++c) P[c][r] = mfma_f16_k32(kf[kq][r], Sp[c], P[c][r]);
-#pragma unroll
-            for (int kb = 2 * kq; kb < 2 * kq + 2; ++kb)
-#pragma unroll
-                for (int qq = 0; qq < 2; ++qq) tf[kb][qq] = kt_pair(kb, qq);
-#pragma unroll
-            for (int c = 0; c < NT; ++c) {
-                S[c][2 * kq] *= gC;
-                S[c][2 * kq + 1] *= gC;
-            }
-        }
-        h8 afr[NPAIR];
-#pragma unroll
-        for (int p = 0; p < NPAIR; ++p) afr[p] = *reinterpret_cast<const h8 *>(Af + p * 512);
+        };
+        auto sp_pair = [&](int c, int kq) { return cat_h8(to_h4(S[c][2 * kq]), to_h4(S[c][2 * kq + 1])); };
 
-        // ---- per column tile: R' = V - gamma P (handed over as operand pairs),
-        //      then eta Delta = Ae R'; one tile's products run under the other
-        //      tile's vector work
-        h4 De[NT][4];
+        // ---- A
+        Sp[0][0] = sp_pair(0, 0);
+        Sp[1][0] = sp_pair(1, 0);
+        GDN_STEP();
 #pragma unroll
-        for (int c = 0; c < NT; ++c) {
-            h4 Rb[4];
+        for (int j = 0; j < NSTEP; ++j) {
+            const int kq = j / 4, r = j % 4;
+            P[0][r] = mfma_f16_k32(kf[kq][r], Sp[0][kq], P[0][r]);
+            if (r == 0 && kq + 1 < NKQ) Sp[0][kq + 1] = sp_pair(0, kq + 1);
+            if (r == 1 && kq + 1 < NKQ) Sp[1][kq + 1] = sp_pair(1, kq + 1);
+            if (r == 2) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                f4 vv;
+                for (int c = 0; c < NT; ++c)
+                    *reinterpret_cast<h8 *>(xb + CF::X_S + (c * NKQ + kq) * 1024 + lane * 16) = Sp[c][kq];
+            }
+            if (r == 3) {
+                tf[2 * kq][0] = kt_pair(2 * kq, 0);
+                tf[2 * kq][1] = kt_pair(2 * kq, 1);
+            }
+            GDN_STEP();
+        }
+        // ---- B
 #pragma unroll
-                for (int i = 0; i < 4; ++i) vv[i] = bf16_to_f32((uint16_t)vt[c][r][i]);
-                Rb[r] = to_h4(vv - ga[r] * P[c][r]);
+        for (int j = 0; j < NSTEP; ++j) {
+            const int kq = j / 4, r = j % 4;
+            P[1][r] = mfma_f16_k32(kf[kq][r], Sp[1][kq], P[1][r]);
+            if (r == 0) {
+                tf[2 * kq + 1][0] = kt_pair(2 * kq + 1, 0);
+                tf[2 * kq + 1][1] = kt_pair(2 * kq + 1, 1);
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                *reinterpret_cast<h8 *>(xb + CF::X_R + (c * 2 + j) * 1024 + lane * 16) = cat_h8(Rb[2 * j], Rb[2 * j + 1]);
+            for (int it = 0; it < 12; ++it)
+                if (it * NSTEP / 12 == j) resid(0, it);
+            GDN_STEP();
+        }
+        // ---- C
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                f4 acc = {0, 0, 0, 0};
+        for (int st = 0; st < 6; ++st) {
+            const int r = AE_R[st], q = AE_Q[st];
+            Ae[0][r] = mfma_f16_k32(afr[pair_index(r, q)], cat_h8(Rb[0][2 * q], Rb[0][2 * q + 1]), Ae[0][r]);
 #pragma unroll
-                for (int qq = 0; qq <= r / 2; ++qq)
-                    acc = mfma_f16_k32(afr[pair_index(r, qq)], cat_h8(Rb[2 * qq], Rb[2 * qq + 1]), acc);
-                De[c][r] = to_h4(acc);
-            }
+            for (int it = 0; it < 12; ++it)
+                if (it / 2 == st) resid(1, it);
+            GDN_STEP();
+        }
+        // ---- D
+#pragma unroll
+        for (int st = 0; st < 6; ++st) {
+            const int r = AE_R[st], q = AE_Q[st];
+            Ae[1][r] = mfma_f16_k32(afr[pair_index(r, q)], cat_h8(Rb[1][2 * q], Rb[1][2 * q + 1]), Ae[1][r]);
+            if (st < 4) De[0][st] = to_h4(Ae[0][st]);
+            if (st >= 2) S[(st - 2) >> 1][(st - 2) & 1] *= gC;  // decay of S rows 0..31
+            GDN_STEP();
         }
 
         // every LDS access of this chunk is complete (its operands are in
         // registers, the hand-over is written): publish, and let the loaders
-        // refill this buffer; then read the next chunk's P operands under the
-        // state update
-        __builtin_amdgcn_sched_barrier(0);
+        // refill this buffer
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         bare_barrier();
-        if (n + 1 < NC) read_p_operands(n + 1);
-        __builtin_amdgcn_sched_barrier(0);
+        const float gCn = gC;
+        if (n + 1 < NC) read_operands(n + 1);
+        GDN_STEP();
 
-        // ---- S = gamma_C S + K^T (eta Delta)   (S already decayed above)
+        // ---- E: S = gamma_C S + K^T (eta Delta), 8 products per pair of
+        //      16-row blocks; rows of the next pair decay meanwhile
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int r = 0; r < 4; ++r) De[1][r] = to_h4(Ae[1][r]);
+        GDN_STEP();
 #pragma unroll
-            for (int c = 0; c < NT; ++c)
+        for (int kp = 0; kp < NKB / 2; ++kp) {
 #pragma unroll
-                for (int qq = 0; qq < 2; ++qq)
-                    S[c][kb] = mfma_f16_k32(tf[kb][qq], cat_h8(De[c][2 * qq], De[c][2 * qq + 1]), S[c][kb]);
+            for (int st = 0; st < 8; ++st) {
+                const int kb = 2 * kp + ((st >> 1) & 1), c = st & 1, qq = st >> 2;
+                S[c][kb] = mfma_f16_k32(tf[kb][qq], cat_h8(De[c][2 * qq], De[c][2 * qq + 1]), S[c][kb]);
+                if (kp + 1 < NKB / 2 && (st & 1)) {  // 4 of the 16 decays of the next pair
+                    const int u = st >> 1;                // 0..3
+                    S[u & 1][2 * kp + 2 + (u >> 1)] *= gCn;
+                }
+                GDN_STEP();
+            }
+        }
     }
+#undef GDN_STEP
 
     if (ST) {
 #pragma unroll
