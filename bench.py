@@ -15,13 +15,28 @@ per-kernel durations from HIP events recorded between the kernels on the
 launch stream, the roofline position of the dominant kernels, and the float64
 CPU oracle timed on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+HBM traffic of the dominant kernels comes from rocprofv3 counter runs
+(FETCH_SIZE and WRITE_SIZE, one pass each) summarised under profiles/ together
+with a hash of the kernel sources; it is reported only while the sources still
+match that hash.
+
+Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+  python bench.py --calibration-copy ...       (also run a 256 MiB device copy,
+                                                the counter calibration kernel)
+  python bench.py --summarize-stats DIR OUT CMD (rocprofv3 --stats CSVs -> profiles/OUT)
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR
+                                               (two counter passes -> traffic summaries)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -59,6 +74,137 @@ def decode_bytes(B, Hk, Hv, Dk, Dv, es):
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Counter-based HBM traffic (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE).
+# ---------------------------------------------------------------------------
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "gated_deltanet_sequence_amd", "csrc")
+COPY_MIB = 256                      # calibration copy: 256 MiB read + 256 MiB written
+TRAFFIC_FILES = {"scan_split_kernel": "scan_split_kernel_prefill_t4096_traffic.md",
+                 "decode_kernel": "decode_kernel_decode_b256_traffic.md"}
+
+
+def kernel_sources_sha256():
+    """Hash of every HIP source and header the kernels are built from."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))
+                   + glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel):
+    """Bytes per launch from the committed counter summary, or None if the
+    summary is missing or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, TRAFFIC_FILES.get(kernel, "-"))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)", text, re.M)
+    if not (m_sha and m_b) or m_sha.group(1) != kernel_sources_sha256():
+        return None
+    return int(m_b.group(1))
+
+
+def calibration_copy(torch):
+    """A plain streaming kernel of known traffic (reads and writes COPY_MIB MiB:
+    an elementwise multiply, which has a kernel of its own, unlike a device copy
+    that shares the runtime's blit kernel with the input uploads), profiled
+    beside the kernels so the counters can be scaled to bytes."""
+    n = COPY_MIB * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _read_counter_csv(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, counter, name_rx):
+    """Mean over dispatches of kernels matching name_rx of the counter (summed over dimensions)."""
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter or not re.search(name_rx, r["Kernel_Name"]):
+            continue
+        per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return (sum(per.values()) / len(per), len(per)) if per else (None, 0)
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Write profiles/<kernel>_..._traffic.md: FETCH_SIZE / WRITE_SIZE per
+    dispatch of the dominant kernels, scaled by the calibration copy, with the
+    source hash."""
+    f_rows, w_rows = _read_counter_csv(fetch_dir), _read_counter_csv(write_dir)
+    copy_rx = r"MulFunctor"
+    cf, ncf = _per_dispatch(f_rows, "FETCH_SIZE", copy_rx)
+    cw, ncw = _per_dispatch(w_rows, "WRITE_SIZE", copy_rx)
+    kib = COPY_MIB * 1024
+    f_scale, w_scale = kib / cf, kib / cw
+    sha = kernel_sources_sha256()
+    for kernel, fname in TRAFFIC_FILES.items():
+        kf, nkf = _per_dispatch(f_rows, "FETCH_SIZE", kernel)
+        kw, nkw = _per_dispatch(w_rows, "WRITE_SIZE", kernel)
+        if kf is None or kw is None:
+            continue
+        fetch_b = kf * f_scale * 1024
+        write_b = kw * w_scale * 1024
+        lines = [
+            f"# HBM traffic of {kernel} (rocprofv3 counters)", "",
+            "Two counter passes over the same bench command, one counter each:", "",
+            "```",
+            "cd /tmp && export TMPDIR=/tmp",
+            f"timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE -d <dir_fetch> -o pmc --output-format csv -- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibration-copy",
+            f"timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE -d <dir_write> -o pmc --output-format csv -- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibration-copy",
+            "python3 bench.py --summarize-pmc <dir_fetch> <dir_write>",
+            "```", "",
+            "| quantity | value |", "|---|---|",
+            f"| {kernel} FETCH_SIZE per dispatch (KiB, mean of {nkf}) | {kf:.0f} |",
+            f"| {kernel} WRITE_SIZE per dispatch (KiB, mean of {nkw}) | {kw:.0f} |",
+            f"| calibration: elementwise multiply, {COPY_MIB} MiB in + {COPY_MIB} MiB out, FETCH_SIZE per dispatch (KiB, mean of {ncf}) | {cf:.0f} |",
+            f"| calibration: same kernel, WRITE_SIZE per dispatch (KiB, mean of {ncw}) | {cw:.0f} |",
+            f"| scale factors (known KiB / counted KiB): fetch, write | {f_scale:.4f}, {w_scale:.4f} |",
+            f"| {kernel} HBM read bytes per launch | {fetch_b:.0f} |",
+            f"| {kernel} HBM write bytes per launch | {write_b:.0f} |", "",
+            f"traffic_bytes_per_launch: {int(round(fetch_b + write_b))}",
+            f"source_sha256: {sha}", ""]
+        path = os.path.join(PROFILES, fname)
+        open(path, "w").write("\n".join(lines))
+        print(f"wrote {path}")
+
+
+def summarize_stats(d, out_name, command):
+    """profiles/<out_name>: per-kernel durations from rocprofv3 --kernel-trace --stats."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(files[0])))
+    lines = [f"# Kernel durations (rocprofv3 --kernel-trace --stats)", "", "```", command, "```", "",
+             "| kernel | calls | total ms | average us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        short = re.sub(r"\(.*", "", name)[:90]
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    path = os.path.join(PROFILES, out_name)
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {path}")
 
 
 def bench_prefill(args, torch, gdn, synth):
@@ -103,13 +249,14 @@ def bench_prefill(args, torch, gdn, synth):
     scan_flop = scan_flop_per_token_head(spec.Dk, spec.Dv, spec.chunk) * units
     nbytes = prefill_bytes(spec.B, spec.T, spec.Hk, spec.Hv, spec.Dk, spec.Dv, 2, False)
     scan_ms = stage_ms[1]
+    scan_kernel = "scan_split_kernel" if spec.dtype == "bf16" else "state_scan_kernel"
     res = dict(
         spec=spec, ms=ms, tokens_per_s=toks / (ms * 1e-3), stage_ms=stage_ms,
         roofline=dict(
-            kernel="state_scan_kernel", bound="mfma",
+            kernel=scan_kernel, bound="mfma",
             achieved=round(scan_flop / (scan_ms * 1e-3) / 1e12, 2), peak=PEAK_MFMA_F16_TFLOPS,
             unit="TFLOP/s", frac=round(scan_flop / (scan_ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
-            traffic=None, flop_per_launch=scan_flop, avg_launch_ms=round(scan_ms, 5)),
+            traffic=stored_traffic(scan_kernel), flop_per_launch=scan_flop, avg_launch_ms=round(scan_ms, 5)),
         path=dict(flop=path_flop, bytes=nbytes,
                   tflops=round(path_flop / (ms * 1e-3) / 1e12, 2),
                   mfma_frac=round(path_flop / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
@@ -159,28 +306,33 @@ def bench_decode(args, torch, gdn, synth):
         config=dict(workload="decode_b256", B=spec.B, Hk=spec.Hk, Hv=spec.Hv, Dk=spec.Dk,
                     Dv=spec.Dv, input_dtype="bf16", state_dtype="f32", consecutive_steps=steps),
         roofline=dict(kernel="decode_kernel", bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS,
-                      unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None,
+                      unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4), traffic=stored_traffic("decode_kernel"),
                       bytes_per_launch=nbytes, avg_launch_ms=round(ms, 5)))
     del per_step, state
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(pre):
-    """The float64 oracle on this host's cores, over the whole prefill workload."""
+def cpu_baseline(pre, min_seconds=10.0):
+    """The float64 oracle on this host's cores: the whole prefill workload,
+    repeated until at least min_seconds of CPU time have passed."""
     import numpy as np
     import oracle
     spec, inp = pre["spec"], pre["inp"]
     x = {k: (None if v is None else oracle.f64(v)) for k, v in inp.items()}
     threads = oracle.num_threads()
-    t0 = time.perf_counter()
-    out, ST = oracle.gdn_fwd(x["q"], x["k"], x["v"], x["a"], x["b"], x["A_log"], x["dt_bias"], S0=x["S0"])
-    dt = time.perf_counter() - t0
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        out, ST = oracle.gdn_fwd(x["q"], x["k"], x["v"], x["a"], x["b"], x["A_log"], x["dt_bias"], S0=x["S0"])
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     assert np.isfinite(out).all()
-    return dict(value=round(spec.B * spec.T / dt, 1), unit="tokens/s", cores=threads, kind="oracle",
+    return dict(value=round(reps * spec.B * spec.T / dt, 1), unit="tokens/s", cores=threads, kind="oracle",
                 seconds=round(dt, 3),
-                sample=f"whole prefill workload once (B={spec.B}, T={spec.T}, {spec.Hv} value heads, "
-                       f"d={spec.Dk}), float64 token loop, OpenMP over (sequence, value head)")
+                sample=f"the whole prefill workload (B={spec.B}, T={spec.T}, {spec.Hv} value heads, "
+                       f"d={spec.Dk}) {reps} times, float64 token loop, OpenMP over (sequence, value head)")
 
 
 def main():
@@ -191,7 +343,17 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="buffer sets rotated in the timed region")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a 256 MiB device copy (counter calibration)")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("DIR", "OUT", "COMMAND"))
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
               f"sharding of the path is a design note, not implemented", file=sys.stderr)
@@ -206,6 +368,8 @@ def main():
 
     pre = bench_prefill(args, torch, gdn, synth)
     dec = None if args.no_decode else bench_decode(args, torch, gdn, synth)
+    if args.calibration_copy:
+        calibration_copy(torch)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre)
     spec = pre["spec"]
     line = {
