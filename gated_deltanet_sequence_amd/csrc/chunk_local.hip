@@ -92,7 +92,11 @@ template <bool F32, int DK>
 struct ChunkLocalCfg {
     typedef typename mma<F32>::E E;
     static constexpr size_t IMG = (size_t)C * DK;                  // elements per image
-    static constexpr size_t WAVE_FLOATS = 10 * 256 + 4 * 256 + 128 + 64;  // X blocks, L diag, G, beta
+    // per-wave scratch: the 10 lower 16x16 blocks of X = (I + L)^{-1}, then G
+    // (64 doubles) and beta; the diagonal blocks of L live in the off-diagonal
+    // X slots until the off-diagonal blocks of X are formed (LDS stays under
+    // 80 KB: two work-groups per CU)
+    static constexpr size_t WAVE_FLOATS = 10 * 256 + 128 + 64;
     static constexpr size_t IMG_BYTES = 2 * IMG * sizeof(E);
     static constexpr size_t WAVE_BYTES = 4 * WAVE_FLOATS * sizeof(float);
     static constexpr size_t U_BYTES = IMG_BYTES > WAVE_BYTES ? IMG_BYTES : WAVE_BYTES;
@@ -208,8 +212,9 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 
     // ---- 3. per value head, one wave each
     float *Xw = reinterpret_cast<float *>(u_raw) + w * CF::WAVE_FLOATS;
-    float *Ld = Xw + 10 * 256;
-    double *Gs = reinterpret_cast<double *>(Ld + 4 * 256);
+    double *Gs = reinterpret_cast<double *>(Xw + 10 * 256);
+    // diagonal block rb of L, in off-diagonal X slot (1,0), (2,0), (2,1) or (3,0)
+    auto Ld = [&](int rb) { return Xw + (rb == 0 ? 1 : rb == 1 ? 3 : rb == 2 ? 4 : 6) * 256; };
     float *Bs = reinterpret_cast<float *>(Gs + 64);
     for (int j = w; j < G; j += 4) {
         const int hv = hk * G + j;
@@ -228,19 +233,16 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
             gl = -expf(A_log[hv]) * softplus_f32(av + dt_bias[hv]);
             be = sigmoid_f32(bv);
         }
-        double Gd = (double)gl;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double y = __shfl_up(Gd, off, 64);
-            if (lane >= off) Gd += y;
-        }
-        const double Glast = __shfl(Gd, 63, 64);
+        const double Gd = wave_prefix_sum_f64((double)gl);
+        const double Glast = __longlong_as_double(
+            ((long long)__builtin_amdgcn_readlane((int)(__double_as_longlong(Gd) >> 32), 63) << 32) |
+            (unsigned)__builtin_amdgcn_readlane((int)__double_as_longlong(Gd), 63));
         Gs[lane] = Gd;
         Bs[lane] = be;
         {   // token record: gamma = e^G in token order, then again with token
             // 16r + m at position 4m + r
             float *tr = tok + vu * C * 2;
-            const float gam = expf((float)Gd);
+            const float gam = __expf((float)Gd);
             tr[lane] = gam;
             tr[64 + 4 * (lane & 15) + (lane >> 4)] = gam;
         }
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const int col = 16 * kb + 4 * g + s;
-                    Gm[tri_index(rb, kb)][s] = col < row ? expf((float)(Gr - Gs[col])) : 0.f;
+                    Gm[tri_index(rb, kb)][s] = col < row ? __expf((float)(Gr - Gs[col])) : 0.f;
                 }
         }
         // L: off-diagonal blocks as operand fragments, diagonal blocks row-major in Ld
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
                 const f4 kk = *reinterpret_cast<const f4 *>(KKt + ti * 256 + m * 16 + 4 * g);
                 const f4 lv = br * Gm[ti] * kk;
                 if (kb < rb) Lf[ti] = lv;
-                else *reinterpret_cast<f4 *>(Ld + rb * 256 + m * 16 + 4 * g) = lv;
+                else *reinterpret_cast<f4 *>(Ld(rb) + m * 16 + 4 * g) = lv;
             }
         }
         wave_lds_sync();
@@ -280,7 +282,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         // diagonal blocks of X: lane (block bq, column c) by forward substitution
         {
             const int bq = lane >> 4, c = lane & 15;
-            const float *Lb = Ld + bq * 256;
+            const float *Lb = Ld(bq);
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         E *qp = qpair + vu * (NPAIR * 64 * 8) + lane * 8;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float eta = expf((float)(Glast - Gs[16 * r + m]));
+            const float eta = __expf((float)(Glast - Gs[16 * r + m]));
 #pragma unroll
             for (int qq = 0; qq <= r / 2; ++qq) {
                 f4 ev[2], ov[2];

@@ -42,6 +42,27 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Inclusive prefix sum of a double over the 64 lanes of a wave, by DPP moves
+// of its two 32-bit halves (no LDS): shifts by 1, 2, 4, 8 inside each row of
+// 16 lanes, then lane 15 of each row into the next row and lane 31 into rows
+// 2 and 3.  Disabled or out-of-row sources read 0 (= +0.0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, ROW_MASK, 0xf, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROW_MASK, 0xf, true);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double wave_prefix_sum_f64(double x) {
+    x += dpp_f64<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_f64<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_f64<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_f64<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_f64<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
+    x += dpp_f64<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 // Element-type traits of q/k/v/out.
 template <typename T> struct io;
 template <> struct io<float> {
