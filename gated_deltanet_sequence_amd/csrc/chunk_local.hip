@@ -103,8 +103,8 @@ struct ChunkLocalCfg {
 };
 
 template <bool F32, typename TIn, int DK>
-__global__ __launch_bounds__(256) void chunk_local_kernel(
-    int T, int Hk, int Hv, int NC, float scale, const TIn *__restrict__ q, const TIn *__restrict__ k,
+__global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
+    int B, int T, int Hk, int Hv, int NC, float scale, const TIn *__restrict__ q, const TIn *__restrict__ k,
     const float *__restrict__ a, const float *__restrict__ b, const float *__restrict__ A_log,
     const float *__restrict__ dt_bias, float *__restrict__ tok, typename mma<F32>::E *__restrict__ apair,
     typename mma<F32>::E *__restrict__ qpair, typename mma<F32>::E *__restrict__ qimg,
@@ -122,25 +122,20 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     E *Qi = reinterpret_cast<E *>(u_raw);
     E *Ki = Qi + IMG;
 
-    const int n = blockIdx.x, hk = blockIdx.y, bb = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
     const int G = Hv / Hk;
-    const int t0 = n * C;
-    const size_t ku = ((size_t)bb * Hk + hk) * NC + n;
+    const int units = B * Hk * NC;
 
-    // gate logits of this wave's first value head, lane = token (loads issued first)
-    float a_pre = 0.f, b_pre = 0.f;
-    if (w < G && t0 + lane < T) {
-        const size_t ia = ((size_t)bb * T + t0 + lane) * Hv + hk * G + w;
-        a_pre = a[ia];
-        b_pre = b[ia];
-    }
-
-    // ---- 1. stage Q and K (zero past the end) as images: all loads, then all LDS stores
-    {
-        constexpr int NPC = C * (DK / 8) / 256;  // 8-element pieces per thread
-        f4 ql[NPC], qh[NPC], kl[NPC], kh[NPC];
+    // Persistent: the work-group walks units u = (b, key head, chunk), and the
+    // next unit's global loads (Q and K rows, gate logits and parameters of
+    // this wave's first value head) are in flight while this unit computes.
+    constexpr int NPC = C * (DK / 8) / 256;  // 8-element pieces of Q (and of K) per thread
+    f4 ql[NPC], qh[NPC], kl[NPC], kh[NPC];
+    float a_pre = 0.f, b_pre = 0.f, alog_pre = 0.f, dtb_pre = 0.f;
+    auto prefetch = [&](int u) {
+        const int n = u % NC, hk = (u / NC) % Hk, bb = u / (NC * Hk);
+        const int t0 = n * C;
 #pragma unroll
         for (int it = 0; it < NPC; ++it) {
             const int idx = tid + 256 * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
@@ -151,15 +146,37 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
                 ld8(k, off, kl[it], kh[it]);
             }
         }
-#pragma unroll
-        for (int it = 0; it < NPC; ++it) {
-            const int idx = tid + 256 * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-            *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(scale * ql[it]);
-            *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(scale * qh[it]);
-            *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(kl[it]);
-            *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(kh[it]);
+        a_pre = b_pre = 0.f;
+        if (w < G) {
+            const int hv = hk * G + w;
+            alog_pre = A_log[hv];
+            dtb_pre = dt_bias[hv];
+            if (t0 + lane < T) {
+                const size_t ia = ((size_t)bb * T + t0 + lane) * Hv + hv;
+                a_pre = a[ia];
+                b_pre = b[ia];
+            }
         }
+    };
+
+    if ((int)blockIdx.x >= units) return;
+    prefetch(blockIdx.x);
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int n = u % NC, hk = (u / NC) % Hk, bb = u / (NC * Hk);
+    const int t0 = n * C;
+    const size_t ku = (size_t)u;
+
+    // ---- 1. Q and K of this unit (zero past the end) into LDS as images
+#pragma unroll
+    for (int it = 0; it < NPC; ++it) {
+        const int idx = tid + 256 * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+        *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(scale * ql[it]);
+        *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(scale * qh[it]);
+        *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(kl[it]);
+        *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(kh[it]);
     }
+    const float a_cur = a_pre, b_cur = b_pre, alog_cur = alog_pre, dtb_cur = dtb_pre;
+    if (u + (int)gridDim.x < units) prefetch(u + gridDim.x);
     __syncthreads();
 
     // ---- images to the workspace: Q and K verbatim, K^T transposed (float32)
@@ -224,13 +241,15 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         const int t = t0 + lane;
         float gl = 0.f, be = 0.f;
         if (t < T) {
-            float av = a_pre, bv = b_pre;
+            float av = a_cur, bv = b_cur, alog = alog_cur, dtb = dtb_cur;
             if (j != w) {
                 const size_t ia = ((size_t)bb * T + t) * Hv + hv;
                 av = a[ia];
                 bv = b[ia];
+                alog = A_log[hv];
+                dtb = dt_bias[hv];
             }
-            gl = -expf(A_log[hv]) * softplus_f32(av + dt_bias[hv]);
+            gl = -expf(alog) * softplus_f32(av + dtb);
             be = sigmoid_f32(bv);
         }
         const double Gd = wave_prefix_sum_f64((double)gl);
@@ -362,13 +381,24 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         }
         wave_lds_sync();
     }
+    __syncthreads();  // every wave is done with this unit's LDS before the next unit's images
+    }
 }
 
 template <bool F32, typename TIn, int DK>
 static hipError_t launch_chunk_local_t(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s) {
     typedef typename mma<F32>::E E;
     const int NC = (p.T + C - 1) / C;
-    hipLaunchKernelGGL((chunk_local_kernel<F32, TIn, DK>), dim3(NC, p.Hk, p.B), dim3(256), 0, s, p.T,
+    const int units = p.B * p.Hk * NC;
+    // resident work-groups (persistent loop over units)
+    int dev = 0, cus = 0, per_cu = 0;
+    unsigned grid = (unsigned)units;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_local_kernel<F32, TIn, DK>, 256, 0) == hipSuccess &&
+        cus > 0 && per_cu > 0 && (long long)cus * per_cu < units)
+        grid = (unsigned)(cus * per_cu);
+    hipLaunchKernelGGL((chunk_local_kernel<F32, TIn, DK>), dim3(grid), dim3(256), 0, s, p.B, p.T,
                        p.Hk, p.Hv, NC, p.scale, (const TIn *)p.q, (const TIn *)p.k, p.a, p.b, p.A_log, p.dt_bias,
                        ws.tok, (E *)ws.apair, (E *)ws.qpair, (E *)ws.qimg, (E *)ws.kimg, (E *)ws.timg);
     return hipGetLastError();
