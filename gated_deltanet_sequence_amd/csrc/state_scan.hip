@@ -639,25 +639,29 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
     f4 ga[4];  // gamma of rows 16r + 4g + i
     float gC;
     h8 afr[NPAIR];
-    auto read_operands = [&](int n) {
+    // The reads one chunk ahead, as NRD separate items (so that they can be
+    // spread between the products of the state update): K operand pairs, V,
+    // gamma, gamma_C, Ae pairs.
+    constexpr int NRD = 4 * NKQ + 4 * NT + 4 + 1 + NPAIR;
+    auto read_item = [&](int n, int it) {
         const char *base = smem + CF::OFF_S + (n & 1) * CF::S_BUF;
-        const E *Ks = reinterpret_cast<const E *>(base + CF::S_K);
         const float *Tq = reinterpret_cast<const float *>(base + CF::S_TK);
-        const E *Af = reinterpret_cast<const E *>(base + CF::S_A) + lane * 8;
+        if (it < 4 * NKQ) {
+            kf[it / 4][it % 4] = img_h8(reinterpret_cast<const E *>(base + CF::S_K), DK, 16 * (it % 4) + m, it / 4, g);
+        } else if ((it -= 4 * NKQ) < 4 * NT) {
+            vt[it / 4][it % 4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + CF::S_V + vt_off[it / 4][it % 4]));
+        } else if ((it -= 4 * NT) < 4) {
+            ga[it] = *reinterpret_cast<const f4 *>(Tq + 16 * it + 4 * g);
+        } else if ((it -= 4) < 1) {
+            gC = Tq[C - 1];
+        } else {
+            it -= 1;
+            afr[it] = *reinterpret_cast<const h8 *>(reinterpret_cast<const E *>(base + CF::S_A) + lane * 8 + it * 512);
+        }
+    };
+    auto read_operands = [&](int n) {
 #pragma unroll
-        for (int kq = 0; kq < NKQ; ++kq)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) kf[kq][r] = img_h8(Ks, DK, 16 * r + m, kq, g);
-#pragma unroll
-        for (int c = 0; c < NT; ++c)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                vt[c][r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + CF::S_V + vt_off[c][r]));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ga[r] = *reinterpret_cast<const f4 *>(Tq + 16 * r + 4 * g);
-        gC = Tq[C - 1];
-#pragma unroll
-        for (int p = 0; p < NPAIR; ++p) afr[p] = *reinterpret_cast<const h8 *>(Af + p * 512);
+        for (int it = 0; it < NRD; ++it) read_item(n, it);
     };
 
     // Instruction schedule.  A wave64 vector instruction occupies the SIMD for
@@ -780,14 +784,14 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         bare_barrier();
         const float gCn = gC;
-        if (n + 1 < NC) read_operands(n + 1);
-        GDN_STEP();
 
         // ---- E: S = gamma_C S + K^T (eta Delta), 8 products per pair of
-        //      16-row blocks; rows of the next pair decay meanwhile
+        //      16-row blocks; rows of the next pair decay meanwhile, and the
+        //      next chunk's operand reads are spread between the products
 #pragma unroll
         for (int r = 0; r < 4; ++r) De[1][r] = to_h4(Ae[1][r]);
         GDN_STEP();
+        constexpr int NSTEP_E = 4 * NKB;
 #pragma unroll
         for (int kp = 0; kp < NKB / 2; ++kp) {
 #pragma unroll
@@ -798,6 +802,11 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
                     const int u = st >> 1;                // 0..3
                     S[u & 1][2 * kp + 2 + (u >> 1)] *= gCn;
                 }
+                // (after the last chunk these read a released buffer, in
+                // bounds, and the values go unused)
+#pragma unroll
+                for (int it = 0; it < NRD; ++it)
+                    if (it * NSTEP_E / NRD == 8 * kp + st) read_item(n + 1, it);
                 GDN_STEP();
             }
         }
