@@ -16,6 +16,8 @@
 //
 // Two kernels: scan_split_kernel (float16 operands, bfloat16 inputs) and
 // state_scan_kernel (float32 operands, float32 inputs), described at each.
+#include <type_traits>
+
 #include "prefill_common.h"
 
 namespace gdn {
@@ -359,22 +361,27 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
 // ---------------------------------------------------------------------------
 // Role-split scan (float16 operands, bfloat16 inputs and outputs).
 //
-// One work-group per (sequence, value head, 32 state columns), four waves with
-// distinct roles, one per SIMD:
-//   state wave: holds S[d_k][32] in accumulator tiles (two 16-column tiles that
-//     share every K, K^T and Ae operand read) and runs the recurrence
-//     P = K S, R' = V - gamma P, S = gamma_C S + K^T (Ae R'); per chunk it hands
-//     the float16 operand pairs of the chunk-start S and of R' to the output
-//     wave through LDS;
-//   output wave, one chunk behind: O^T = gamma (S^T Q^T) + R'^T Ao^T.  The
-//     transposed products take the very same operand registers, and their
-//     accumulators give each lane 4 consecutive output columns of one token,
-//     written with one 8-byte store;
-//   two loader waves: copy the next chunk's inputs into LDS with direct-to-LDS
-//     buffer loads -- K, K^T, V, Ae and gamma for the state wave, Q, Ao and
-//     gamma for the output wave.
-// Only the state wave is on the chunk-to-chunk critical path.  Inputs of both
-// consumers and the hand-over are double-buffered: one barrier per chunk.
+// One work-group per (sequence, value head, 32 state columns), six waves with
+// distinct roles.  Waves w and w + 4 share a SIMD; the two state waves get a
+// SIMD each, every other SIMD holds an output wave and a loader wave.
+//   two state waves (waves 2 and 3), one per 16-column tile: each holds its
+//     S[d_k][16] in accumulator tiles and runs the recurrence P = K S,
+//     R' = V - gamma P, S = gamma_C S + K^T (Ae R'); the two tiles are
+//     independent, so the chunk-to-chunk chain of each wave carries half the
+//     vector and matrix work of one 32-column wave (the K and K^T operand
+//     reads are not halved: both waves read them).  Per chunk each hands the
+//     float16 operand pairs of its chunk-start S and of R' to the output waves
+//     through LDS;
+//   two output waves (waves 0 and 1), one chunk behind, each for two of the
+//     four 16-token row tiles and both column tiles:
+//     O^T = gamma (S^T Q^T) + R'^T Ao^T.  The transposed products take the very
+//     same operand registers, and their accumulators give each lane 4
+//     consecutive output columns of one token, written with one 8-byte store;
+//   two loader waves: copy inputs into LDS with direct-to-LDS buffer loads --
+//     wave 5 K, V, Ae and gamma for the state waves, wave 4 Q, Ao and gamma
+//     for the output waves; the images two chunks ahead, the rest one ahead.
+// Only the state waves are on the chunk-to-chunk critical path.  One barrier
+// per chunk.
 // ---------------------------------------------------------------------------
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s4 lds_s4;
@@ -386,7 +393,7 @@ __device__ __forceinline__ h8 img_h8(const _Float16 *X, int rowlen, int R, int k
 
 template <typename TIn, int DK, int NL>
 struct SplitCfg {
-    static constexpr int NT = 2;                                   // 16-column tiles per work-group
+    static constexpr int NT = 2;                                   // 16-column tiles (state waves) per work-group
     static constexpr int NCOL = 16 * NT;
     static constexpr int NKQ = DK / 32;                            // 32-deep contraction steps over d_k
     static constexpr int IMG_BYTES = C * DK * 2;
@@ -395,85 +402,78 @@ struct SplitCfg {
     static constexpr int TILE_BYTES = C * NCOL * (int)sizeof(TIn);  // V tile
     static constexpr int VSPR = NCOL * (int)sizeof(TIn) / 16;       // 16-byte slots per V row
     static constexpr int VEPS = 16 / (int)sizeof(TIn);              // elements per slot
-    // state-wave inputs of one chunk
-    static constexpr int S_K = 0, S_V = S_K + IMG_BYTES, S_A = S_V + TILE_BYTES,
-                         S_TK = S_A + FRAG_BYTES, S_BUF = S_TK + TOK_BYTES;
-    // output-wave inputs of one chunk
-    static constexpr int O_Q = 0, O_F = O_Q + IMG_BYTES, O_TK = O_F + FRAG_BYTES, O_BUF = O_TK + TOK_BYTES;
+    // The K and Q images of a chunk are staged two chunks ahead (three
+    // buffers each), the rest of a chunk's inputs one chunk ahead (two
+    // buffers): the small per-chunk inputs of the state waves (V tile, Ae,
+    // gamma) and of the output waves (Ao, gamma).
+    static constexpr int S_V = 0, S_A = S_V + TILE_BYTES, S_TK = S_A + FRAG_BYTES, SR_BUF = S_TK + TOK_BYTES;
+    static constexpr int O_F = 0, O_TK = O_F + FRAG_BYTES, OR_BUF = O_TK + TOK_BYTES;
     // hand-over: S (d_k x 16) and R' (64 x 16) of each column tile as operand pairs, 1 KB each
     static constexpr int X_S = 0, X_R = NT * NKQ * 1024, X_BUF = X_R + NT * 2 * 1024;
-    static constexpr int OFF_S = 0, OFF_O = 2 * S_BUF, OFF_X = OFF_O + 2 * O_BUF, LDS = OFF_X + 2 * X_BUF;
+    static constexpr int NIB = 3;  // image buffers (K, and Q)
+    static constexpr int OFF_K = 0, OFF_SR = OFF_K + NIB * IMG_BYTES, OFF_Q = OFF_SR + 2 * SR_BUF,
+                         OFF_OR = OFF_Q + NIB * IMG_BYTES, OFF_X = OFF_OR + 2 * OR_BUF, LDS = OFF_X + 2 * X_BUF;
     static constexpr int IMG_UNITS = IMG_BYTES / 1024, FRAG_UNITS = FRAG_BYTES / 1024,
                          TILE_UNITS = TILE_BYTES / 1024;
-    static_assert(IMG_UNITS % NL == 0 && FRAG_UNITS % NL == 0 && TILE_UNITS % NL == 0, "copy split");
+    static_assert(IMG_UNITS < 64, "vmcnt");
     static_assert(VSPR >= 4 && (VSPR & (VSPR - 1)) == 0, "V slots");
-    static_assert(S_BUF % 16 == 0 && O_BUF % 16 == 0, "alignment");
+    static_assert(SR_BUF % 16 == 0 && OR_BUF % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
 // Loader-wave copies of one chunk's inputs into LDS: 16 bytes per lane per
-// instruction, straight from memory into LDS (no registers).
+// instruction, straight from memory into LDS (no registers).  One loader wave
+// stages the state-wave inputs, the other the output-wave inputs: each wave's
+// loads complete in issue order, so the two streams do not wait on each other.
 template <typename TIn, int DK, int NL>
 struct SplitLoader {
     typedef SplitCfg<TIn, DK, NL> CF;
     __amdgpu_buffer_rsrc_t vres, rq, rk, ra, rf, rtk;
-    int l, lane;
+    int lane;
     unsigned vcol;  // element offset of this group's first V column in a token row
     unsigned vrow;  // elements per token row of V (Hv * d_v)
 
     __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t r, char *dst, int src_off) const {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, lane * 16, src_off, 0, 0);
     }
-    // state-wave inputs: K image, Ae fragments, V columns, gamma
-    __device__ __forceinline__ void stage_state(char *smem, int n, int buf) const {
-        char *base = smem + CF::OFF_S + buf * CF::S_BUF;
-        const int io = n * CF::IMG_BYTES, fo = n * CF::FRAG_BYTES;
+    // an image (K or Q) of chunk n into image buffer ib: IMG_UNITS loads
+    __device__ __forceinline__ void stage_img(__amdgpu_buffer_rsrc_t r, char *dst, int n) const {
+        const int io = n * CF::IMG_BYTES;
 #pragma unroll
-        for (int i = 0; i < CF::IMG_UNITS / NL; ++i) {
-            const int u = (l + NL * i) * 1024;
-            copy(rk, base + CF::S_K + u, io + u);
-        }
+        for (int u = 0; u < CF::IMG_UNITS; ++u) copy(r, dst + u * 1024, io + u * 1024);
+    }
+    // the state waves' V columns, Ae fragments and gamma of chunk n
+    __device__ __forceinline__ void stage_state_rest(char *smem, int n, int buf) const {
+        char *base = smem + CF::OFF_SR + buf * CF::SR_BUF;
 #pragma unroll
-        for (int i = 0; i < CF::FRAG_UNITS / NL; ++i) {
-            const int u = (l + NL * i) * 1024;
-            copy(ra, base + CF::S_A + u, fo + u);
-        }
-#pragma unroll
-        for (int i = 0; i < CF::TILE_UNITS / NL; ++i) {
-            const int u = l + NL * i;
+        for (int u = 0; u < CF::TILE_UNITS; ++u) {
             const int slot = u * 64 + lane;
             const int row = slot / CF::VSPR;
             const int piece = (slot % CF::VSPR) ^ ((row >> 2) & (CF::VSPR - 1));
             const unsigned voff = ((unsigned)(n * C + row) * vrow + vcol + piece * CF::VEPS) * (unsigned)sizeof(TIn);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void_t *)(base + CF::S_V + u * 1024), 16, (int)voff, 0, 0, 0);
         }
-        if (l == 0 && lane < CF::TOK_BYTES / 16) copy(rtk, base + CF::S_TK, n * CF::TOK_BYTES);
+#pragma unroll
+        for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(ra, base + CF::S_A + u * 1024, n * CF::FRAG_BYTES + u * 1024);
+        if (lane < CF::TOK_BYTES / 16) copy(rtk, base + CF::S_TK, n * CF::TOK_BYTES);
     }
-    // output-wave inputs: Q image, Ao fragments, gamma
-    __device__ __forceinline__ void stage_out(char *smem, int n, int buf) const {
-        char *base = smem + CF::OFF_O + buf * CF::O_BUF;
-        const int io = n * CF::IMG_BYTES, fo = n * CF::FRAG_BYTES;
+    // the output waves' Ao fragments and gamma of chunk n
+    __device__ __forceinline__ void stage_out_rest(char *smem, int n, int buf) const {
+        char *base = smem + CF::OFF_OR + buf * CF::OR_BUF;
 #pragma unroll
-        for (int i = 0; i < CF::IMG_UNITS / NL; ++i) {
-            const int u = (l + NL * i) * 1024;
-            copy(rq, base + CF::O_Q + u, io + u);
-        }
-#pragma unroll
-        for (int i = 0; i < CF::FRAG_UNITS / NL; ++i) {
-            const int u = (l + NL * i) * 1024;
-            copy(rf, base + CF::O_F + u, fo + u);
-        }
-        if (l == NL - 1 && lane < CF::TOK_BYTES / 16) copy(rtk, base + CF::O_TK, n * CF::TOK_BYTES);
+        for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(rf, base + CF::O_F + u * 1024, n * CF::FRAG_BYTES + u * 1024);
+        if (lane < CF::TOK_BYTES / 16) copy(rtk, base + CF::O_TK, n * CF::TOK_BYTES);
     }
 };
 
 template <typename TIn, int DK, int DV, int NL>
-__global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
+__global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
     int T, int Hk, int Hv, int NC, const TIn *__restrict__ v, const float *__restrict__ tok,
     const _Float16 *__restrict__ apair, const _Float16 *__restrict__ qpair,
     const _Float16 *__restrict__ qimg, const _Float16 *__restrict__ kimg,
     const float *__restrict__ S0, TIn *__restrict__ out, float *__restrict__ ST) {
     static_assert(sizeof(TIn) == 2, "bfloat16 inputs");
+    static_assert(NL == 2, "waves 4 and 5 load");
     typedef SplitCfg<TIn, DK, NL> CF;
     typedef _Float16 E;
     constexpr int NT = CF::NT, NCOL = CF::NCOL, NKB = DK / 16, NKQ = CF::NKQ, NCG = DV / NCOL;
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
     };
 
-    if (w >= 2) {
+    if (w >= 4) {
         // ================= loader waves =================
         const size_t ku0 = ((size_t)bb * Hk + hk) * NC, vu0 = ((size_t)bb * Hv + hv) * NC;
         SplitLoader<TIn, DK, NL> ld;
@@ -506,30 +506,55 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
         ld.ra = rsrc(apair + vu0 * (NPAIR * 64 * 8), (size_t)NC * CF::FRAG_BYTES);
         ld.rf = rsrc(qpair + vu0 * (NPAIR * 64 * 8), (size_t)NC * CF::FRAG_BYTES);
         ld.rtk = rsrc(tok + vu0 * C * 2, (size_t)NC * CF::TOK_BYTES);
-        ld.l = w - 2;
         ld.lane = lane;
         ld.vcol = (unsigned)(hv * DV + NCOL * cg);
         ld.vrow = (unsigned)(Hv * DV);
 
-        ld.stage_state(smem, 0, 0);
-        wait_vmcnt<0>();
-        bare_barrier();
+        // Per chunk interval n (between the barriers that publish chunks n-1
+        // and n), each loader issues the small inputs of chunk n (state
+        // loader: of chunk n+1) and then the image of chunk n+1 (n+2), and
+        // waits until only that image's loads are in flight: loads complete in
+        // issue order, so the image gets a second interval.
+        const bool state = w == 5;
+        const __amdgpu_buffer_rsrc_t rimg = state ? ld.rk : ld.rq;
+        char *img = smem + (state ? CF::OFF_K : CF::OFF_Q);
+        ld.stage_img(rimg, img, 0);
+        if (state) {
+            ld.stage_state_rest(smem, 0, 0);
+            if (NC > 1) ld.stage_img(rimg, img + CF::IMG_BYTES, 1);
+            if (NC > 1) wait_vmcnt<CF::IMG_UNITS>();
+            else wait_vmcnt<0>();
+        }
+        bare_barrier();  // chunk 0 (state inputs) staged
+        const int lead = state ? 2 : 1;  // chunks the image runs ahead
+        int ib = lead;                   // image buffer of chunk n + lead
         for (int n = 0; n < NC; ++n) {
-            if (n + 1 < NC) ld.stage_state(smem, n + 1, (n + 1) & 1);
-            ld.stage_out(smem, n, n & 1);
-            wait_vmcnt<0>();
-            bare_barrier();
+            if (state) {
+                if (n + 1 < NC) ld.stage_state_rest(smem, n + 1, (n + 1) & 1);
+            } else {
+                ld.stage_out_rest(smem, n, n & 1);
+            }
+            if (n + lead < NC) {
+                ld.stage_img(rimg, img + ib * CF::IMG_BYTES, n + lead);
+                wait_vmcnt<CF::IMG_UNITS>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            ib = ib == CF::NIB - 1 ? 0 : ib + 1;
+            bare_barrier();  // chunk n+1 (state inputs) and chunk n (output inputs) staged
         }
         return;
     }
 
-    if (w == 1) {
-        // ================= output wave (one chunk behind) =================
+    if (w <= 1) {
+        // ================= output waves (one chunk behind) =================
+        // wave 0: token row tiles 0 and 3, wave 1: row tiles 1 and 2 (the same
+        // number of products each), both column tiles
         const __amdgpu_buffer_rsrc_t ores = rsrc(out + (size_t)bb * seq_elems, seq_elems * sizeof(TIn));
         const unsigned col = NCOL * cg + 4 * g;
-        auto emit = [&](int n) {
-            const char *ob = smem + CF::OFF_O + (n & 1) * CF::O_BUF;
-            const E *Qs = reinterpret_cast<const E *>(ob + CF::O_Q);
+        auto emit = [&](int n, int qb, auto RA, auto RB) {  // qb: image buffer of chunk n
+            const char *ob = smem + CF::OFF_OR + (n & 1) * CF::OR_BUF;
+            const E *Qs = reinterpret_cast<const E *>(smem + CF::OFF_Q + qb * CF::IMG_BYTES);
             const E *Of = reinterpret_cast<const E *>(ob + CF::O_F) + lane * 8;
             const float *Tq = reinterpret_cast<const float *>(ob + CF::O_TK);
             const char *xb = smem + CF::OFF_X + (n & 1) * CF::X_BUF;
@@ -544,8 +569,8 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
                     Rp[c][j] = *reinterpret_cast<const h8 *>(xb + CF::X_R + (c * 2 + j) * 1024 + lane * 16);
             }
             const f4 gam = *reinterpret_cast<const f4 *>(Tq + 64 + 4 * m);  // tokens m, 16+m, 32+m, 48+m
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            auto rows = [&](auto RR) {
+                constexpr int r = decltype(RR)::value;
                 f4 sq[NT];
 #pragma unroll
                 for (int c = 0; c < NT; ++c) sq[c] = f4{0, 0, 0, 0};
@@ -575,43 +600,48 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
                     __builtin_memcpy(&bits, &hb, 8);
                     __builtin_amdgcn_raw_buffer_store_b64(bits, ores, (int)(((t * Hv + hv) * DV + col + 16 * c) * 2u), 0, 0);
                 }
-            }
+            };
+            rows(RA);
+            rows(RB);
+        };
+        auto emit_mine = [&](int n, int qb) {
+            if (w == 0) emit(n, qb, std::integral_constant<int, 0>(), std::integral_constant<int, 3>());
+            else emit(n, qb, std::integral_constant<int, 1>(), std::integral_constant<int, 2>());
         };
         bare_barrier();
+        int qb = CF::NIB - 1;  // image buffer of chunk n - 1
         for (int n = 0; n < NC; ++n) {
-            if (n > 0) emit(n - 1);
+            if (n > 0) emit_mine(n - 1, qb);
+            qb = qb == CF::NIB - 1 ? 0 : qb + 1;
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this chunk's LDS reads are done
             bare_barrier();
         }
-        if (NC > 0) emit(NC - 1);
+        if (NC > 0) emit_mine(NC - 1, qb);
         return;
     }
 
-    // ================= state wave =================
-    f4 S[NT][NKB];
+    // ================= state waves: column tile c = w - 2 =================
+    const int c = w - 2;
+    f4 S[NKB];
     const size_t sb = ((size_t)bb * Hv + hv) * DK * DV;
+    const int scol = NCOL * cg + 16 * c + m;
 #pragma unroll
-    for (int c = 0; c < NT; ++c)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[c][kb][i] = S0 ? S0[sb + (size_t)(16 * kb + 4 * g + i) * DV + NCOL * cg + 16 * c + m] : 0.f;
+        for (int i = 0; i < 4; ++i) S[kb][i] = S0 ? S0[sb + (size_t)(16 * kb + 4 * g + i) * DV + scol] : 0.f;
 
     // Transposed V reads (ds_read_b64_tr_b16): in each 16-lane group, lane
     // 4i + q supplies the address of 4 consecutive 16-bit values -- columns
     // 4q .. 4q+3 of row i of a 4 x 16 block -- and lane j receives column j of
     // the 4 rows.  Lane (g, m) points at row 16r + 4g + m/4, columns
     // 16c + 4(m%4) .. +3 of the V tile and receives V[16r + 4g + i][16c + m].
-    int vt_off[NT][4];
+    int vt_off[4];
 #pragma unroll
-    for (int c = 0; c < NT; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * r + 4 * g + (m >> 2), cc = 16 * c + 4 * (m & 3);
-            const int piece = (cc / CF::VEPS) ^ ((row >> 2) & (CF::VSPR - 1));
-            vt_off[c][r] = (row * NCOL + piece * CF::VEPS + cc % CF::VEPS) * (int)sizeof(TIn);
-        }
+    for (int r = 0; r < 4; ++r) {
+        const int row = 16 * r + 4 * g + (m >> 2), cc = 16 * c + 4 * (m & 3);
+        const int piece = (cc / CF::VEPS) ^ ((row >> 2) & (CF::VSPR - 1));
+        vt_off[r] = (row * NCOL + piece * CF::VEPS + cc % CF::VEPS) * (int)sizeof(TIn);
+    }
 
     // K^T operands of the state update from the K image, by transposed reads:
     // the A operand of pair (kb, qq) holds K[32qq + 16h + 4g + i][16kb + m]
@@ -631,26 +661,24 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
         }
     }
 
-    // Operands of chunk n (K, V, gamma, gamma_C, Ae), read one chunk ahead:
-    // right after the barrier that publishes chunk n, under chunk n-1's state
-    // update.
+    // Operands of chunk n (K, V, gamma, gamma_C, Ae), read one chunk ahead,
+    // spread over chunk n-1's state update (after the barrier that publishes
+    // chunk n): NRD separate reads.
     h8 kf[NKQ][4];
-    s4 vt[NT][4];
+    s4 vt[4];
     f4 ga[4];  // gamma of rows 16r + 4g + i
     float gC;
     h8 afr[NPAIR];
-    // The reads one chunk ahead, as NRD separate items (so that they can be
-    // spread between the products of the state update): K operand pairs, V,
-    // gamma, gamma_C, Ae pairs.
-    constexpr int NRD = 4 * NKQ + 4 * NT + 4 + 1 + NPAIR;
-    auto read_item = [&](int n, int it) {
-        const char *base = smem + CF::OFF_S + (n & 1) * CF::S_BUF;
+    constexpr int NRD = 4 * NKQ + 4 + 4 + 1 + NPAIR;
+    auto read_item = [&](int kbi, int rbi, int it) {  // image buffer, small-input buffer of the chunk
+        const char *base = smem + CF::OFF_SR + rbi * CF::SR_BUF;
         const float *Tq = reinterpret_cast<const float *>(base + CF::S_TK);
         if (it < 4 * NKQ) {
-            kf[it / 4][it % 4] = img_h8(reinterpret_cast<const E *>(base + CF::S_K), DK, 16 * (it % 4) + m, it / 4, g);
-        } else if ((it -= 4 * NKQ) < 4 * NT) {
-            vt[it / 4][it % 4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + CF::S_V + vt_off[it / 4][it % 4]));
-        } else if ((it -= 4 * NT) < 4) {
+            kf[it / 4][it % 4] = img_h8(reinterpret_cast<const E *>(smem + CF::OFF_K + kbi * CF::IMG_BYTES), DK,
+                                        16 * (it % 4) + m, it / 4, g);
+        } else if ((it -= 4 * NKQ) < 4) {
+            vt[it] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + CF::S_V + vt_off[it]));
+        } else if ((it -= 4) < 4) {
             ga[it] = *reinterpret_cast<const f4 *>(Tq + 16 * it + 4 * g);
         } else if ((it -= 4) < 1) {
             gC = Tq[C - 1];
@@ -659,35 +687,32 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
             afr[it] = *reinterpret_cast<const h8 *>(reinterpret_cast<const E *>(base + CF::S_A) + lane * 8 + it * 512);
         }
     };
-    auto read_operands = [&](int n) {
-#pragma unroll
-        for (int it = 0; it < NRD; ++it) read_item(n, it);
-    };
 
-    // Instruction schedule.  A wave64 vector instruction occupies the SIMD for
-    // 4 cycles, a 16x16x32 product the matrix unit for 16; the two overlap only
-    // if they are interleaved, and the compiler, left alone, groups them (and
-    // issues LDS reads just before their use).  So each phase below is a
-    // sequence of fenced steps: one product plus the independent vector / LDS
-    // work that fits under it.
-    //   A  P = K S for column tile 0 | S operand pairs, hand-over, K^T reads
-    //   B  P for tile 1               | K^T reads, R' = V - gamma P of tile 0
-    // (K^T comes from the K image by transposed reads rather than from a K^T
-    // image: the copy of a K^T image would add 16 KB per chunk to the loads,
-    // which already run near the CU's vector-memory rate)
-    //   C  Ae R' for tile 0           | R' of tile 1
-    //   D  Ae R' for tile 1           | float16 eta Delta of tile 0, decay of S rows 0..31
+    // Instruction schedule.  Within one wave, LDS accesses and vector
+    // arithmetic hardly overlap each other, while a matrix product overlaps
+    // both if independent work is issued right behind it; the compiler, left
+    // alone, groups the products (and issues LDS reads just before their use).
+    // So each phase is a sequence of fenced steps: one product plus the
+    // independent vector / LDS work that fits under it.
+    //   A  P = K S (4 NKQ products)     | S operand pairs and their hand-over,
+    //                                     K^T reads
+    //   B  Ae R' (6 products)           | R' = V - gamma P and its hand-over,
+    //                                     decay of S
     //   -- barrier: chunk n+1 is staged, this chunk's buffer is released
-    //   E  S += K^T (eta Delta)       | next chunk's operand reads, decay of the
-    //                                   next S rows, eta Delta of tile 1
+    //   E  S += K^T (eta Delta)         | next chunk's operand reads
+    //      (4 NKQ products)
 #define GDN_STEP() __builtin_amdgcn_sched_barrier(0)
-    constexpr int NSTEP = 4 * NKQ;     // products in phase A or B
-    constexpr int AE_R[6] = {0, 1, 2, 3, 2, 3}, AE_Q[6] = {0, 0, 0, 0, 1, 1};  // Ae R' order
+    constexpr int NSTEP = 4 * NKQ;  // products in phase A (and in E)
 
     bare_barrier();  // chunk 0 staged
-    if (NC > 0) read_operands(0);
+    if (NC > 0) {
+#pragma unroll
+        for (int it = 0; it < NRD; ++it) read_item(0, 0, it);
+    }
+    int cur = 0;  // image buffer of chunk n
     for (int n = 0; n < NC; ++n) {
-        const char *Ks8 = smem + CF::OFF_S + (n & 1) * CF::S_BUF + CF::S_K;
+        const int nxt = cur == CF::NIB - 1 ? 0 : cur + 1;
+        const char *Ks8 = smem + CF::OFF_K + cur * CF::IMG_BYTES;
         char *xb = smem + CF::OFF_X + (n & 1) * CF::X_BUF;
         // K^T operand pair (kb, qq): two transposed reads, rows 32qq and 32qq + 16 on
         auto kt_pair = [&](int kb, int qq) {
@@ -695,132 +720,92 @@ __global__ __launch_bounds__(64 * (2 + NL)) void scan_split_kernel(
             const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(Ks8 + kt_off[kb] + (32 * qq + 16) * DK * 2));
             return cat_h8(__builtin_bit_cast(h4, lo), __builtin_bit_cast(h4, hi));
         };
-        h8 Sp[NT][NKQ];
+        auto sp_pair = [&](int kq) { return cat_h8(to_h4(S[2 * kq]), to_h4(S[2 * kq + 1])); };
+        h8 Sp[NKQ];
         h8 tf[NKB][2];
-        f4 P[NT][4];
-        h4 Rb[NT][4];
-        f4 Rx[4];
-        h4 De[NT][4];
-        f4 Ae[NT][4];
+        f4 P[4], Ae[4];
+        h4 Rb[4], De[4];
 #pragma unroll
-        for (int c = 0; c < NT; ++c)
+        for (int r = 0; r < 4; ++r) P[r] = Ae[r] = f4{0, 0, 0, 0};
+        // residual of row tile rr: R' = V - gamma P in float32, then float16
+        // (row tiles 2q, 2q+1 form operand pair q, handed over as one 1 KB block)
+        auto resid = [&](int rr) {
+            f4 x;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) P[c][r] = Ae[c][r] = f4{0, 0, 0, 0};
-        // residual of column tile c, row tile rr, in three steps
-        auto resid = [&](int c, int item) {
-            const int rr = item / 3, part = item % 3;
-            if (part == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Rx[rr][i] = bf16_to_f32((uint16_t)vt[c][rr][i]);
-            } else if (part == 1) {
-                Rx[rr] = Rx[rr] - ga[rr] * P[c][rr];
-            } else {
-                Rb[c][rr] = to_h4(Rx[rr]);
-                if (rr & 1)
-                    *reinterpret_cast<h8 *>(xb + CF::X_R + (c * 2 + rr / 2) * 1024 + lane * 16) =
-                        cat_h8(Rb[c][rr - 1], Rb[c][rr]);
-            }
+            for (int i = 0; i < 4; ++i) x[i] = bf16_to_f32((uint16_t)vt[rr][i]);
+            Rb[rr] = to_h4(x - ga[rr] * P[rr]);
+            if (rr & 1)
+                *reinterpret_cast<h8 *>(xb + CF::X_R + (c * 2 + rr / 2) * 1024 + lane * 16) = cat_h8(Rb[rr - 1], Rb[rr]);
         };
-        auto sp_pair = [&](int c, int kq) { return cat_h8(to_h4(S[c][2 * kq]), to_h4(S[c][2 * kq + 1])); };
 
         // ---- A
-        Sp[0][0] = sp_pair(0, 0);
-        Sp[1][0] = sp_pair(1, 0);
+        Sp[0] = sp_pair(0);
         GDN_STEP();
 #pragma unroll
         for (int j = 0; j < NSTEP; ++j) {
             const int kq = j / 4, r = j % 4;
-            P[0][r] = mfma_f16_k32(kf[kq][r], Sp[0][kq], P[0][r]);
-            if (r == 0 && kq + 1 < NKQ) Sp[0][kq + 1] = sp_pair(0, kq + 1);
-            if (r == 1 && kq + 1 < NKQ) Sp[1][kq + 1] = sp_pair(1, kq + 1);
-            if (r == 2) {
-#pragma unroll
-                for (int c = 0; c < NT; ++c)
-                    *reinterpret_cast<h8 *>(xb + CF::X_S + (c * NKQ + kq) * 1024 + lane * 16) = Sp[c][kq];
-            }
-            if (r == 3) {
-                tf[2 * kq][0] = kt_pair(2 * kq, 0);
-                tf[2 * kq][1] = kt_pair(2 * kq, 1);
-            }
+            P[r] = mfma_f16_k32(kf[kq][r], Sp[kq], P[r]);
+            if (r == 0 && kq + 1 < NKQ) Sp[kq + 1] = sp_pair(kq + 1);
+            if (r == 1) *reinterpret_cast<h8 *>(xb + CF::X_S + (c * NKQ + kq) * 1024 + lane * 16) = Sp[kq];
+            tf[j / 2][j % 2] = kt_pair(j / 2, j % 2);
             GDN_STEP();
         }
-        // ---- B
+        // ---- B: Ae R' in the order (r, q) = (0,0) (1,0) (2,0) (3,0) (2,1) (3,1)
+        resid(0);
+        resid(1);
+        GDN_STEP();
+        Ae[0] = mfma_f16_k32(afr[pair_index(0, 0)], cat_h8(Rb[0], Rb[1]), Ae[0]);
+        resid(2);
+        GDN_STEP();
+        Ae[1] = mfma_f16_k32(afr[pair_index(1, 0)], cat_h8(Rb[0], Rb[1]), Ae[1]);
+        resid(3);
+        GDN_STEP();
+        Ae[2] = mfma_f16_k32(afr[pair_index(2, 0)], cat_h8(Rb[0], Rb[1]), Ae[2]);
+        S[0] *= gC;
+        S[1] *= gC;
+        De[0] = to_h4(Ae[0]);
+        GDN_STEP();
+        Ae[3] = mfma_f16_k32(afr[pair_index(3, 0)], cat_h8(Rb[0], Rb[1]), Ae[3]);
+        S[2] *= gC;
+        S[3] *= gC;
+        De[1] = to_h4(Ae[1]);
+        GDN_STEP();
+        Ae[2] = mfma_f16_k32(afr[pair_index(2, 1)], cat_h8(Rb[2], Rb[3]), Ae[2]);
 #pragma unroll
-        for (int j = 0; j < NSTEP; ++j) {
-            const int kq = j / 4, r = j % 4;
-            P[1][r] = mfma_f16_k32(kf[kq][r], Sp[1][kq], P[1][r]);
-            if (r == 0) {
-                tf[2 * kq + 1][0] = kt_pair(2 * kq + 1, 0);
-                tf[2 * kq + 1][1] = kt_pair(2 * kq + 1, 1);
-            }
-#pragma unroll
-            for (int it = 0; it < 12; ++it)
-                if (it * NSTEP / 12 == j) resid(0, it);
-            GDN_STEP();
-        }
-        // ---- C
-#pragma unroll
-        for (int st = 0; st < 6; ++st) {
-            const int r = AE_R[st], q = AE_Q[st];
-            Ae[0][r] = mfma_f16_k32(afr[pair_index(r, q)], cat_h8(Rb[0][2 * q], Rb[0][2 * q + 1]), Ae[0][r]);
-#pragma unroll
-            for (int it = 0; it < 12; ++it)
-                if (it / 2 == st) resid(1, it);
-            GDN_STEP();
-        }
-        // ---- D
-#pragma unroll
-        for (int st = 0; st < 6; ++st) {
-            const int r = AE_R[st], q = AE_Q[st];
-            Ae[1][r] = mfma_f16_k32(afr[pair_index(r, q)], cat_h8(Rb[1][2 * q], Rb[1][2 * q + 1]), Ae[1][r]);
-            if (st < 4) De[0][st] = to_h4(Ae[0][st]);
-            if (st >= 2) S[(st - 2) >> 1][(st - 2) & 1] *= gC;  // decay of S rows 0..31
-            GDN_STEP();
-        }
+        for (int kb = 4; kb < NKB; ++kb) S[kb] *= gC;
+        GDN_STEP();
+        Ae[3] = mfma_f16_k32(afr[pair_index(3, 1)], cat_h8(Rb[2], Rb[3]), Ae[3]);
 
         // every LDS access of this chunk is complete (its operands are in
         // registers, the hand-over is written): publish, and let the loaders
         // refill this buffer
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         bare_barrier();
-        const float gCn = gC;
-
-        // ---- E: S = gamma_C S + K^T (eta Delta), 8 products per pair of
-        //      16-row blocks; rows of the next pair decay meanwhile, and the
-        //      next chunk's operand reads are spread between the products
-#pragma unroll
-        for (int r = 0; r < 4; ++r) De[1][r] = to_h4(Ae[1][r]);
+        De[2] = to_h4(Ae[2]);
+        De[3] = to_h4(Ae[3]);
         GDN_STEP();
-        constexpr int NSTEP_E = 4 * NKB;
+
+        // ---- E: S = gamma_C S + K^T (eta Delta); the next chunk's operand
+        //      reads are spread between the products (after the last chunk
+        //      they read a released buffer, in bounds, and go unused)
 #pragma unroll
-        for (int kp = 0; kp < NKB / 2; ++kp) {
+        for (int st = 0; st < NSTEP; ++st) {
+            const int kb = st / 2, qq = st % 2;
+            S[kb] = mfma_f16_k32(tf[kb][qq], cat_h8(De[2 * qq], De[2 * qq + 1]), S[kb]);
 #pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const int kb = 2 * kp + ((st >> 1) & 1), c = st & 1, qq = st >> 2;
-                S[c][kb] = mfma_f16_k32(tf[kb][qq], cat_h8(De[c][2 * qq], De[c][2 * qq + 1]), S[c][kb]);
-                if (kp + 1 < NKB / 2 && (st & 1)) {  // 4 of the 16 decays of the next pair
-                    const int u = st >> 1;                // 0..3
-                    S[u & 1][2 * kp + 2 + (u >> 1)] *= gCn;
-                }
-                // (after the last chunk these read a released buffer, in
-                // bounds, and the values go unused)
-#pragma unroll
-                for (int it = 0; it < NRD; ++it)
-                    if (it * NSTEP_E / NRD == 8 * kp + st) read_item(n + 1, it);
-                GDN_STEP();
-            }
+            for (int it = 0; it < NRD; ++it)
+                if (it * NSTEP / NRD == st) read_item(nxt, (n + 1) & 1, it);
+            GDN_STEP();
         }
+        cur = nxt;
     }
 #undef GDN_STEP
 
     if (ST) {
 #pragma unroll
-        for (int c = 0; c < NT; ++c)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    ST[sb + (size_t)(16 * kb + 4 * g + i) * DV + NCOL * cg + 16 * c + m] = S[c][kb][i];
+            for (int i = 0; i < 4; ++i) ST[sb + (size_t)(16 * kb + 4 * g + i) * DV + scol] = S[kb][i];
     }
 }
 
@@ -837,7 +822,7 @@ static hipError_t launch_scan_t(const PrefillArgs &p, const PrefillWorkspace &ws
         constexpr int NL = 2;
         const int NC = (p.T + C - 1) / C;
         const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<TIn, DK, NL>::NCOL));
-        hipLaunchKernelGGL((scan_split_kernel<TIn, DK, DV, NL>), dim3(blocks), dim3(64 * (2 + NL)), 0, s,
+        hipLaunchKernelGGL((scan_split_kernel<TIn, DK, DV, NL>), dim3(blocks), dim3(64 * (4 + NL)), 0, s,
                            p.T, p.Hk, p.Hv, NC, (const TIn *)p.v, ws.tok, (const E *)ws.apair,
                            (const E *)ws.qpair, (const E *)ws.qimg, (const E *)ws.kimg,
                            p.S0, (TIn *)p.out, p.ST);
