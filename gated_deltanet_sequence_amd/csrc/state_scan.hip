@@ -402,22 +402,24 @@ struct SplitCfg {
     static constexpr int TILE_BYTES = C * NCOL * (int)sizeof(TIn);  // V tile
     static constexpr int VSPR = NCOL * (int)sizeof(TIn) / 16;       // 16-byte slots per V row
     static constexpr int VEPS = 16 / (int)sizeof(TIn);              // elements per slot
-    // The K and Q images of a chunk are staged two chunks ahead (three
-    // buffers each), the rest of a chunk's inputs one chunk ahead (two
-    // buffers): the small per-chunk inputs of the state waves (V tile, Ae,
-    // gamma) and of the output waves (Ao, gamma).
-    static constexpr int S_V = 0, S_A = S_V + TILE_BYTES, S_TK = S_A + FRAG_BYTES, SR_BUF = S_TK + TOK_BYTES;
-    static constexpr int O_F = 0, O_TK = O_F + FRAG_BYTES, OR_BUF = O_TK + TOK_BYTES;
+    // Every input is staged two chunks ahead (three buffers per stream): the
+    // K image, V tile, Ae and gamma of the state waves, the Q image, Ao and
+    // gamma of the output waves.  The hand-over is single-buffered (two
+    // barriers per chunk).
+    static constexpr int S_K = 0, S_V = S_K + IMG_BYTES, S_A = S_V + TILE_BYTES, S_TK = S_A + FRAG_BYTES,
+                         S_BUF = S_TK + TOK_BYTES;
+    static constexpr int O_Q = 0, O_F = O_Q + IMG_BYTES, O_TK = O_F + FRAG_BYTES, O_BUF = O_TK + TOK_BYTES;
     // hand-over: S (d_k x 16) and R' (64 x 16) of each column tile as operand pairs, 1 KB each
     static constexpr int X_S = 0, X_R = NT * NKQ * 1024, X_BUF = X_R + NT * 2 * 1024;
-    static constexpr int NIB = 3;  // image buffers (K, and Q)
-    static constexpr int OFF_K = 0, OFF_SR = OFF_K + NIB * IMG_BYTES, OFF_Q = OFF_SR + 2 * SR_BUF,
-                         OFF_OR = OFF_Q + NIB * IMG_BYTES, OFF_X = OFF_OR + 2 * OR_BUF, LDS = OFF_X + 2 * X_BUF;
+    static constexpr int NB = 3;  // buffers per input stream
+    static constexpr int OFF_S = 0, OFF_O = OFF_S + NB * S_BUF, OFF_X = OFF_O + NB * O_BUF, LDS = OFF_X + X_BUF;
     static constexpr int IMG_UNITS = IMG_BYTES / 1024, FRAG_UNITS = FRAG_BYTES / 1024,
                          TILE_UNITS = TILE_BYTES / 1024;
-    static_assert(IMG_UNITS < 64, "vmcnt");
+    // loads per chunk of the state loader and of the output loader
+    static constexpr int STATE_LOADS = IMG_UNITS + TILE_UNITS + FRAG_UNITS + 1, OUT_LOADS = IMG_UNITS + FRAG_UNITS + 1;
+    static_assert(STATE_LOADS < 64 && OUT_LOADS < 64, "vmcnt");
     static_assert(VSPR >= 4 && (VSPR & (VSPR - 1)) == 0, "V slots");
-    static_assert(SR_BUF % 16 == 0 && OR_BUF % 16 == 0, "alignment");
+    static_assert(S_BUF % 16 == 0 && O_BUF % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -436,15 +438,12 @@ struct SplitLoader {
     __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t r, char *dst, int src_off) const {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, lane * 16, src_off, 0, 0);
     }
-    // an image (K or Q) of chunk n into image buffer ib: IMG_UNITS loads
-    __device__ __forceinline__ void stage_img(__amdgpu_buffer_rsrc_t r, char *dst, int n) const {
-        const int io = n * CF::IMG_BYTES;
+    // state-wave inputs of chunk n: K image, V columns, Ae fragments, gamma (STATE_LOADS loads)
+    __device__ __forceinline__ void stage_state(char *smem, int n, int buf) const {
+        char *base = smem + CF::OFF_S + buf * CF::S_BUF;
+        const int io = n * CF::IMG_BYTES, fo = n * CF::FRAG_BYTES;
 #pragma unroll
-        for (int u = 0; u < CF::IMG_UNITS; ++u) copy(r, dst + u * 1024, io + u * 1024);
-    }
-    // the state waves' V columns, Ae fragments and gamma of chunk n
-    __device__ __forceinline__ void stage_state_rest(char *smem, int n, int buf) const {
-        char *base = smem + CF::OFF_SR + buf * CF::SR_BUF;
+        for (int u = 0; u < CF::IMG_UNITS; ++u) copy(rk, base + CF::S_K + u * 1024, io + u * 1024);
 #pragma unroll
         for (int u = 0; u < CF::TILE_UNITS; ++u) {
             const int slot = u * 64 + lane;
@@ -454,14 +453,17 @@ struct SplitLoader {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void_t *)(base + CF::S_V + u * 1024), 16, (int)voff, 0, 0, 0);
         }
 #pragma unroll
-        for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(ra, base + CF::S_A + u * 1024, n * CF::FRAG_BYTES + u * 1024);
+        for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(ra, base + CF::S_A + u * 1024, fo + u * 1024);
         if (lane < CF::TOK_BYTES / 16) copy(rtk, base + CF::S_TK, n * CF::TOK_BYTES);
     }
-    // the output waves' Ao fragments and gamma of chunk n
-    __device__ __forceinline__ void stage_out_rest(char *smem, int n, int buf) const {
-        char *base = smem + CF::OFF_OR + buf * CF::OR_BUF;
+    // output-wave inputs of chunk n: Q image, Ao fragments, gamma (OUT_LOADS loads)
+    __device__ __forceinline__ void stage_out(char *smem, int n, int buf) const {
+        char *base = smem + CF::OFF_O + buf * CF::O_BUF;
+        const int io = n * CF::IMG_BYTES, fo = n * CF::FRAG_BYTES;
 #pragma unroll
-        for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(rf, base + CF::O_F + u * 1024, n * CF::FRAG_BYTES + u * 1024);
+        for (int u = 0; u < CF::IMG_UNITS; ++u) copy(rq, base + CF::O_Q + u * 1024, io + u * 1024);
+#pragma unroll
+        for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(rf, base + CF::O_F + u * 1024, fo + u * 1024);
         if (lane < CF::TOK_BYTES / 16) copy(rtk, base + CF::O_TK, n * CF::TOK_BYTES);
     }
 };
@@ -510,38 +512,56 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         ld.vcol = (unsigned)(hv * DV + NCOL * cg);
         ld.vrow = (unsigned)(Hv * DV);
 
-        // Per chunk interval n (between the barriers that publish chunks n-1
-        // and n), each loader issues the small inputs of chunk n (state
-        // loader: of chunk n+1) and then the image of chunk n+1 (n+2), and
-        // waits until only that image's loads are in flight: loads complete in
-        // issue order, so the image gets a second interval.
-        const bool state = w == 5;
-        const __amdgpu_buffer_rsrc_t rimg = state ? ld.rk : ld.rq;
-        char *img = smem + (state ? CF::OFF_K : CF::OFF_Q);
-        ld.stage_img(rimg, img, 0);
-        if (state) {
-            ld.stage_state_rest(smem, 0, 0);
-            if (NC > 1) ld.stage_img(rimg, img + CF::IMG_BYTES, 1);
-            if (NC > 1) wait_vmcnt<CF::IMG_UNITS>();
+        // Barriers, the same sequence in every wave: P(-1), then per chunk n
+        // P(n) -- chunk n+1's state-wave inputs, chunk n's output-wave inputs
+        // and chunk n's hand-over are in LDS -- and F(n) -- the output waves
+        // have read chunk n's hand-over.  Chunk m's inputs are issued right
+        // after F(m-3) (state) or F(m-2) (output), into the buffer its
+        // predecessor three chunks back has released, and waited for just
+        // before the barrier that publishes them: about two chunk intervals
+        // in flight.  Loads complete in issue order, so waiting until only
+        // the newest chunk's loads are outstanding suffices.
+        if (w == 5) {
+            // state-wave inputs: chunk m is needed from P(m-1) on
+            ld.stage_state(smem, 0, 0);
+            if (NC > 1) ld.stage_state(smem, 1, 1);
+            if (NC > 1) wait_vmcnt<CF::STATE_LOADS>();
             else wait_vmcnt<0>();
-        }
-        bare_barrier();  // chunk 0 (state inputs) staged
-        const int lead = state ? 2 : 1;  // chunks the image runs ahead
-        int ib = lead;                   // image buffer of chunk n + lead
-        for (int n = 0; n < NC; ++n) {
-            if (state) {
-                if (n + 1 < NC) ld.stage_state_rest(smem, n + 1, (n + 1) & 1);
-            } else {
-                ld.stage_out_rest(smem, n, n & 1);
+            bare_barrier();  // P(-1): chunk 0
+            if (NC > 2) ld.stage_state(smem, 2, 2);
+            if (NC > 2) wait_vmcnt<CF::STATE_LOADS>();
+            else wait_vmcnt<0>();
+            bare_barrier();  // P(0): chunk 1
+            int sb = 0;      // buffer of chunk n + 3
+            for (int n = 0; n < NC; ++n) {
+                bare_barrier();  // F(n)
+                if (n + 3 < NC) ld.stage_state(smem, n + 3, sb);
+                if (n + 1 < NC) {
+                    if (n + 3 < NC) wait_vmcnt<CF::STATE_LOADS>();
+                    else wait_vmcnt<0>();
+                    bare_barrier();  // P(n+1): chunk n+2
+                }
+                sb = sb == CF::NB - 1 ? 0 : sb + 1;
             }
-            if (n + lead < NC) {
-                ld.stage_img(rimg, img + ib * CF::IMG_BYTES, n + lead);
-                wait_vmcnt<CF::IMG_UNITS>();
-            } else {
-                wait_vmcnt<0>();
+        } else {
+            // output-wave inputs: chunk m is needed from P(m) on
+            ld.stage_out(smem, 0, 0);
+            if (NC > 1) ld.stage_out(smem, 1, 1);
+            bare_barrier();  // P(-1)
+            if (NC > 1) wait_vmcnt<CF::OUT_LOADS>();
+            else wait_vmcnt<0>();
+            bare_barrier();  // P(0): chunk 0
+            int ob = 2;      // buffer of chunk n + 2
+            for (int n = 0; n < NC; ++n) {
+                bare_barrier();  // F(n)
+                if (n + 2 < NC) ld.stage_out(smem, n + 2, ob);
+                if (n + 1 < NC) {
+                    if (n + 2 < NC) wait_vmcnt<CF::OUT_LOADS>();
+                    else wait_vmcnt<0>();
+                    bare_barrier();  // P(n+1): chunk n+1
+                }
+                ob = ob == CF::NB - 1 ? 0 : ob + 1;
             }
-            ib = ib == CF::NIB - 1 ? 0 : ib + 1;
-            bare_barrier();  // chunk n+1 (state inputs) and chunk n (output inputs) staged
         }
         return;
     }
@@ -552,12 +572,14 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         // number of products each), both column tiles
         const __amdgpu_buffer_rsrc_t ores = rsrc(out + (size_t)bb * seq_elems, seq_elems * sizeof(TIn));
         const unsigned col = NCOL * cg + 4 * g;
-        auto emit = [&](int n, int qb, auto RA, auto RB) {  // qb: image buffer of chunk n
-            const char *ob = smem + CF::OFF_OR + (n & 1) * CF::OR_BUF;
-            const E *Qs = reinterpret_cast<const E *>(smem + CF::OFF_Q + qb * CF::IMG_BYTES);
+        // chunk n from output buffer obi; the hand-over is read first, then
+        // F(n) releases it to the state waves
+        auto emit = [&](int n, int obi, auto RA, auto RB) {
+            const char *ob = smem + CF::OFF_O + obi * CF::O_BUF;
+            const E *Qs = reinterpret_cast<const E *>(ob + CF::O_Q);
             const E *Of = reinterpret_cast<const E *>(ob + CF::O_F) + lane * 8;
             const float *Tq = reinterpret_cast<const float *>(ob + CF::O_TK);
-            const char *xb = smem + CF::OFF_X + (n & 1) * CF::X_BUF;
+            const char *xb = smem + CF::OFF_X;
             h8 Sp[NT][NKQ], Rp[NT][2];
 #pragma unroll
             for (int c = 0; c < NT; ++c) {
@@ -568,6 +590,8 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
                 for (int j = 0; j < 2; ++j)
                     Rp[c][j] = *reinterpret_cast<const h8 *>(xb + CF::X_R + (c * 2 + j) * 1024 + lane * 16);
             }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the hand-over is in registers
+            bare_barrier();                      // F(n)
             const f4 gam = *reinterpret_cast<const f4 *>(Tq + 64 + 4 * m);  // tokens m, 16+m, 32+m, 48+m
             auto rows = [&](auto RR) {
                 constexpr int r = decltype(RR)::value;
@@ -604,19 +628,15 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
             rows(RA);
             rows(RB);
         };
-        auto emit_mine = [&](int n, int qb) {
-            if (w == 0) emit(n, qb, std::integral_constant<int, 0>(), std::integral_constant<int, 3>());
-            else emit(n, qb, std::integral_constant<int, 1>(), std::integral_constant<int, 2>());
-        };
-        bare_barrier();
-        int qb = CF::NIB - 1;  // image buffer of chunk n - 1
+        bare_barrier();  // P(-1)
+        int ob = 0;      // buffer of chunk n
         for (int n = 0; n < NC; ++n) {
-            if (n > 0) emit_mine(n - 1, qb);
-            qb = qb == CF::NIB - 1 ? 0 : qb + 1;
+            bare_barrier();  // P(n)
+            if (w == 0) emit(n, ob, std::integral_constant<int, 0>(), std::integral_constant<int, 3>());
+            else emit(n, ob, std::integral_constant<int, 1>(), std::integral_constant<int, 2>());
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this chunk's LDS reads are done
-            bare_barrier();
+            ob = ob == CF::NB - 1 ? 0 : ob + 1;
         }
-        if (NC > 0) emit_mine(NC - 1, qb);
         return;
     }
 
@@ -670,12 +690,11 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
     float gC;
     h8 afr[NPAIR];
     constexpr int NRD = 4 * NKQ + 4 + 4 + 1 + NPAIR;
-    auto read_item = [&](int kbi, int rbi, int it) {  // image buffer, small-input buffer of the chunk
-        const char *base = smem + CF::OFF_SR + rbi * CF::SR_BUF;
+    auto read_item = [&](int sbi, int it) {  // sbi: state buffer of the chunk
+        const char *base = smem + CF::OFF_S + sbi * CF::S_BUF;
         const float *Tq = reinterpret_cast<const float *>(base + CF::S_TK);
         if (it < 4 * NKQ) {
-            kf[it / 4][it % 4] = img_h8(reinterpret_cast<const E *>(smem + CF::OFF_K + kbi * CF::IMG_BYTES), DK,
-                                        16 * (it % 4) + m, it / 4, g);
+            kf[it / 4][it % 4] = img_h8(reinterpret_cast<const E *>(base + CF::S_K), DK, 16 * (it % 4) + m, it / 4, g);
         } else if ((it -= 4 * NKQ) < 4) {
             vt[it] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + CF::S_V + vt_off[it]));
         } else if ((it -= 4) < 4) {
@@ -704,16 +723,16 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
 #define GDN_STEP() __builtin_amdgcn_sched_barrier(0)
     constexpr int NSTEP = 4 * NKQ;  // products in phase A (and in E)
 
-    bare_barrier();  // chunk 0 staged
+    bare_barrier();  // P(-1): chunk 0 staged
     if (NC > 0) {
 #pragma unroll
-        for (int it = 0; it < NRD; ++it) read_item(0, 0, it);
+        for (int it = 0; it < NRD; ++it) read_item(0, it);
     }
-    int cur = 0;  // image buffer of chunk n
+    int cur = 0;  // state buffer of chunk n
     for (int n = 0; n < NC; ++n) {
-        const int nxt = cur == CF::NIB - 1 ? 0 : cur + 1;
-        const char *Ks8 = smem + CF::OFF_K + cur * CF::IMG_BYTES;
-        char *xb = smem + CF::OFF_X + (n & 1) * CF::X_BUF;
+        const int nxt = cur == CF::NB - 1 ? 0 : cur + 1;
+        const char *Ks8 = smem + CF::OFF_S + cur * CF::S_BUF + CF::S_K;
+        char *xb = smem + CF::OFF_X;
         // K^T operand pair (kb, qq): two transposed reads, rows 32qq and 32qq + 16 on
         auto kt_pair = [&](int kb, int qq) {
             const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(Ks8 + kt_off[kb] + 32 * qq * DK * 2));
@@ -794,9 +813,11 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
             S[kb] = mfma_f16_k32(tf[kb][qq], cat_h8(De[2 * qq], De[2 * qq + 1]), S[kb]);
 #pragma unroll
             for (int it = 0; it < NRD; ++it)
-                if (it * NSTEP / NRD == st) read_item(nxt, (n + 1) & 1, it);
+                if (it * NSTEP / NRD == st) read_item(nxt, it);
             GDN_STEP();
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        bare_barrier();  // F(n): the output waves have read the hand-over
         cur = nxt;
     }
 #undef GDN_STEP
