@@ -515,12 +515,13 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         // Barriers, the same sequence in every wave: P(-1), then per chunk n
         // P(n) -- chunk n+1's state-wave inputs, chunk n's output-wave inputs
         // and chunk n's hand-over are in LDS -- and F(n) -- the output waves
-        // have read chunk n's hand-over.  Chunk m's inputs are issued right
-        // after F(m-3) (state) or F(m-2) (output), into the buffer its
-        // predecessor three chunks back has released, and waited for just
-        // before the barrier that publishes them: about two chunk intervals
-        // in flight.  Loads complete in issue order, so waiting until only
-        // the newest chunk's loads are outstanding suffices.
+        // have read chunk n's hand-over.  After P(n) the state waves are done
+        // with chunk n's inputs and the output waves with chunk n-1's: chunk
+        // n+3's state inputs and chunk n+2's output inputs are issued into
+        // those buffers right then, and waited for just before the barrier
+        // that publishes them, more than two chunk intervals later.  Loads
+        // complete in issue order, so waiting until only the newest chunk's
+        // loads are outstanding suffices.
         if (w == 5) {
             // state-wave inputs: chunk m is needed from P(m-1) on
             ld.stage_state(smem, 0, 0);
@@ -534,8 +535,8 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
             bare_barrier();  // P(0): chunk 1
             int sb = 0;      // buffer of chunk n + 3
             for (int n = 0; n < NC; ++n) {
-                bare_barrier();  // F(n)
                 if (n + 3 < NC) ld.stage_state(smem, n + 3, sb);
+                bare_barrier();  // F(n)
                 if (n + 1 < NC) {
                     if (n + 3 < NC) wait_vmcnt<CF::STATE_LOADS>();
                     else wait_vmcnt<0>();
@@ -553,8 +554,8 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
             bare_barrier();  // P(0): chunk 0
             int ob = 2;      // buffer of chunk n + 2
             for (int n = 0; n < NC; ++n) {
-                bare_barrier();  // F(n)
                 if (n + 2 < NC) ld.stage_out(smem, n + 2, ob);
+                bare_barrier();  // F(n)
                 if (n + 1 < NC) {
                     if (n + 2 < NC) wait_vmcnt<CF::OUT_LOADS>();
                     else wait_vmcnt<0>();
@@ -795,9 +796,9 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         GDN_STEP();
         Ae[3] = mfma_f16_k32(afr[pair_index(3, 1)], cat_h8(Rb[2], Rb[3]), Ae[3]);
 
-        // every LDS access of this chunk is complete (its operands are in
-        // registers, the hand-over is written): publish, and let the loaders
-        // refill this buffer
+        // every LDS access to this chunk's inputs is complete (its operands are
+        // in registers) and the hand-over is written: P(n) publishes the
+        // hand-over and lets the loaders refill this chunk's buffer
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         bare_barrier();
         De[2] = to_h4(Ae[2]);
