@@ -249,8 +249,13 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
                 alog = A_log[hv];
                 dtb = dt_bias[hv];
             }
-            gl = -expf(alog) * softplus_f32(av + dtb);
-            be = sigmoid_f32(bv);
+            if constexpr (F32) {
+                gl = -expf(alog) * softplus_f32(av + dtb);
+                be = sigmoid_f32(bv);
+            } else {
+                gl = -exp_fast(alog) * softplus_fast(av + dtb);
+                be = sigmoid_fast(bv);
+            }
         }
         const double Gd = wave_prefix_sum_f64((double)gl);
         const double Glast = __longlong_as_double(

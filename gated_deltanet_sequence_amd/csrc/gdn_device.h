@@ -112,6 +112,15 @@ __device__ __forceinline__ float softplus_f32(float x) {
     return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
 }
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.f / (1.f + expf(-x)); }
+// The same gates from the hardware base-2 exponential and logarithm and the
+// hardware reciprocal (a few ulp): used where the operands are float16 and the
+// output bfloat16, whose rounding is orders of magnitude coarser.  softplus
+// keeps its absolute error near float32 rounding: max(x, 0) + log(1 + e^-|x|).
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float softplus_fast(float x) {
+    return fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + exp_fast(-fabsf(x))) * 0.6931471805599453f;
+}
+__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + exp_fast(-x)); }
 
 // ---------------------------------------------------------------------------
 // MFMA on 16x16 output tiles.  Layouts (checked on gfx950):
