@@ -64,14 +64,19 @@ __device__ __forceinline__ int unperm_col(int p) {
 // at a time.  A column's finished blocks stay in accumulator layout, the B
 // operand of the next product.  Lf holds the A-operand fragments of L's
 // off-diagonal blocks; Xw is this wave's block-packed row-major copy of X.
+// All ten blocks are also returned in accumulator layout (Xa: lane (m, g) holds
+// X[16i + 4g + s][16j + m]).
 template <bool F32>
-__device__ __forceinline__ void inverse_offdiag(float *Xw, const f4 (&Lf)[10], int m, int g) {
+__device__ __forceinline__ void inverse_offdiag(float *Xw, const f4 (&Lf)[10], int m, int g, f4 (&Xa)[10]) {
     typedef mma<F32> M;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Xa[tri_index(3, 3)][s] = Xw[tri_index(3, 3) * 256 + (4 * g + s) * 16 + m];
 #pragma unroll
     for (int jb = 0; jb < 3; ++jb) {
         f4 Xc[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) Xc[jb][s] = Xw[tri_index(jb, jb) * 256 + (4 * g + s) * 16 + m];
+        Xa[tri_index(jb, jb)] = Xc[jb];
 #pragma unroll
         for (int ib = jb + 1; ib < 4; ++ib) {
             f4 Tacc = {0, 0, 0, 0};
@@ -82,6 +87,7 @@ __device__ __forceinline__ void inverse_offdiag(float *Xw, const f4 (&Lf)[10], i
             f4 Xn = {0, 0, 0, 0};
             Xn = -M::block(Xn, M::from_f4(dv), M::from_f4(Tacc));
             Xc[ib] = Xn;
+            Xa[tri_index(ib, jb)] = Xn;
 #pragma unroll
             for (int s = 0; s < 4; ++s) Xw[tri_index(ib, jb) * 256 + (4 * g + s) * 16 + m] = Xn[s];
         }
@@ -207,23 +213,31 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
         }
     }
 
-    // ---- 2. K K^T and Q K^T, lower-triangular 16x16 tiles (10 each), 5 per wave
-    for (int job = w; job < 20; job += 4) {
-        const E *X = job < 10 ? Ki : Qi;
-        float *Dst = job < 10 ? KKt : QKt;
-        const int p = job % 10;
-        const int rt = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
-        const int ct = p - tri_index(rt, 0);
-        f4 acc = {0, 0, 0, 0};
+    // ---- 2. K K^T and Q K^T, lower-triangular 16x16 tiles (10 each): wave w
+    //      takes the row tiles {3, 0} (w < 2) or {2, 1} (5 tiles either way) of
+    //      K K^T (even w) or Q K^T (odd w), reading each row tile's operands
+    //      once.  Tile (rt, ct) of X K^T is formed as K_ct X_rt^T, whose
+    //      accumulator holds row 16rt + m, columns 16ct + 4g .. +3 -- the
+    //      operand layout its readers load, stored with one 16-byte write.
+    {
+        const E *X = (w & 1) ? Qi : Ki;
+        float *Dst = (w & 1) ? QKt : KKt;
+        for (int h = 0; h < 2; ++h) {
+            const int rt = w < 2 ? (h == 0 ? 3 : 0) : (h == 0 ? 2 : 1);
+            V4 xa[DK / 32][2];
 #pragma unroll
-        for (int kq = 0; kq < DK / 32; ++kq) {
-            V4 a0, a1, b0, b1;
-            img_pair<F32>(X, DK, 16 * rt + m, kq, g, a0, a1);
-            img_pair<F32>(Ki, DK, 16 * ct + m, kq, g, b0, b1);
-            acc = mma<F32>::pair(acc, a0, a1, b0, b1);
+            for (int kq = 0; kq < DK / 32; ++kq) img_pair<F32>(X, DK, 16 * rt + m, kq, g, xa[kq][0], xa[kq][1]);
+            for (int ct = 0; ct <= rt; ++ct) {
+                f4 acc = {0, 0, 0, 0};
+#pragma unroll
+                for (int kq = 0; kq < DK / 32; ++kq) {
+                    V4 b0, b1;
+                    img_pair<F32>(Ki, DK, 16 * ct + m, kq, g, b0, b1);
+                    acc = mma<F32>::pair(acc, b0, b1, xa[kq][0], xa[kq][1]);
+                }
+                *reinterpret_cast<f4 *>(Dst + tri_index(rt, ct) * 256 + m * 16 + 4 * g) = acc;
+            }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Dst[p * 256 + (4 * g + i) * 16 + m] = acc[i];
     }
     __syncthreads();  // the images in LDS are dead from here on
 
@@ -320,7 +334,8 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
         }
         wave_lds_sync();
 
-        inverse_offdiag<F32>(Xw, Lf, m, g);
+        f4 xt[10];  // A^T blocks (kb, mb) as A operands: lane holds A[16mb+4g+s][16kb+m]
+        inverse_offdiag<F32>(Xw, Lf, m, g, xt);
         wave_lds_sync();
 
         // Operand fragments of the two per-chunk matrices the scan applies to the
@@ -343,13 +358,6 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
                     for (int s = 0; s < 4; ++s) gm[s] = (4 * g + s == m) ? 1.f : gm[s];
                 aq[ti] = gm * *reinterpret_cast<const f4 *>(QKt + ti * 256 + m * 16 + 4 * g);
             }
-        f4 xt[10];  // A^T blocks (kb, mb) as A operands: lane holds A[16mb+4g+s][16kb+m]
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int kb = 0; kb <= mb; ++kb)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) xt[tri_index(mb, kb)][s] = Xw[tri_index(mb, kb) * 256 + (4 * g + s) * 16 + m];
 
         E *ap = apair + vu * (NPAIR * 64 * 8) + lane * 8;
         E *qp = qpair + vu * (NPAIR * 64 * 8) + lane * 8;
