@@ -134,6 +134,46 @@ def test_bf16_full_compare():
                        init_state=True))
 
 
+# The bfloat16 path runs a different scan (float16 operands, role-split work-group
+# with its own staging prologue for the first chunks): the same shape coverage.
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129, 200])
+def test_ragged_lengths_bf16(T):
+    """1, 2, 3 and 4 chunks (the scan stages its first chunks before the loop) and ragged tails."""
+    full_check(GDNSpec(B=1, T=T, Hk=1, Hv=2, Dk=128, Dv=128, dtype="bf16", seed=300 + T, init_state=True))
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 64), (64, 128), (128, 64)])
+def test_head_sizes_bf16(Dk, Dv):
+    full_check(GDNSpec(B=1, T=257, Hk=1, Hv=2, Dk=Dk, Dv=Dv, dtype="bf16", seed=310 + Dk + Dv,
+                       init_state=True))
+
+
+def test_batch_and_key_head_groups_bf16():
+    """B=3 distinct sequences; 2 key heads shared by 4 value heads each."""
+    full_check(GDNSpec(B=3, T=130, Hk=2, Hv=8, Dk=128, Dv=128, dtype="bf16", seed=330, init_state=True))
+
+
+def test_scale_bf16():
+    full_check(GDNSpec(B=1, T=100, Hk=1, Hv=2, Dk=128, Dv=128, dtype="bf16", seed=332),
+               scale=1 / math.sqrt(128))
+
+
+def test_in_place_final_state_bf16():
+    spec = GDNSpec(B=2, T=150, Hk=1, Hv=2, Dk=128, Dv=128, dtype="bf16", seed=340, init_state=True)
+    log(f"[prefill in-place] {spec}")
+    inp = synth.make_inputs(spec)
+    import gated_deltanet_sequence_amd as gdn
+    d = to_dev(inp)
+    S = d["S0"].clone()
+    out, ST = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], S,
+                                final_state=S)
+    torch.cuda.synchronize()
+    assert ST.data_ptr() == S.data_ptr()
+    o_ref, s_ref = oracle_prefill(inp)
+    assert_close("out", out.cpu(), o_ref, TOL["bf16"])
+    assert_close("final_state", S.cpu(), s_ref, TOL["bf16"])
+
+
 def test_bf16_slow_decay_reported():
     """Slow decay in bf16: the carried state dominates the output.  Gated at 2e-3 as well."""
     full_check(GDNSpec(B=1, T=512, Hk=2, Hv=4, Dk=128, Dv=128, dtype="bf16", seed=281,
