@@ -1,10 +1,12 @@
 """MI355X-native (gfx950) Gated DeltaNet core.
 
 The hot path (gate preparation, chunk-local WY auxiliaries, inter-chunk state
-scan, recurrent decode step) is hand-written HIP in ``csrc/`` behind the C ABI
+scan, recurrent decode step, and the Gated DeltaNet-2 chunked prefill) is
+hand-written HIP in ``csrc/`` behind the C ABI
 of ``include/gdn.h``; ``binding`` is its thin ctypes wrapper for torch tensors.
 """
 from .binding import (  # noqa: F401
     GDN_BF16, GDN_CHUNK_FWD_STAGES, GDN_F32, GDNError, STAGE_NAMES, StageEvents, alloc_workspace,
-    gdn_chunk_fwd, gdn_chunk_fwd_workspace_bytes, gdn_dims, gdn_recurrent_step, lib, make_dims,
+    gdn2_chunk_fwd, gdn_chunk_fwd, gdn_chunk_fwd_workspace_bytes, gdn_dims, gdn_recurrent_step, lib,
+    make_dims,
 )

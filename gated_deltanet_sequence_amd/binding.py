@@ -53,6 +53,10 @@ def lib():
     L.gdn_chunk_fwd_timed.restype = ctypes.c_int
     L.gdn_chunk_fwd_timed.argtypes = [dims_p, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, vp, sz, vp,
                                       ctypes.POINTER(ctypes.c_void_p)]
+    L.gdn2_chunk_fwd_workspace_bytes.restype = sz
+    L.gdn2_chunk_fwd_workspace_bytes.argtypes = [dims_p]
+    L.gdn2_chunk_fwd.restype = ctypes.c_int
+    L.gdn2_chunk_fwd.argtypes = [dims_p, vp, vp, vp, vp, fp, vp, vp, fp, vp, fp, vp, sz, vp]
     L.gdn_recurrent_step.restype = ctypes.c_int
     L.gdn_recurrent_step.argtypes = [dims_p, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
     L.gdn_status_str.restype = ctypes.c_char_p
@@ -154,6 +158,45 @@ def gdn_chunk_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, scale: f
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
         _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream), ev)
+    _check(st)
+    return out, final_state
+
+
+def gdn2_chunk_fwd(q, k, v, a, A_log, erase, write, initial_state=None, *, scale: float = 1.0,
+                   out=None, final_state=None, output_final_state: bool = True, workspace=None,
+                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated DeltaNet-2 chunked prefill (bfloat16).  q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv];
+    a, erase [B,T,Hv,Dk]; write [B,T,Hv,Dv]; A_log [Hv,Dk] fp32; initial_state
+    [B,Hv,Dk,Dv] fp32 or None.  Returns (out [B,T,Hv,Dv], final_state or None)."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dims = make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, scale)
+    for name, t in (("A_log", A_log), ("initial_state", initial_state), ("final_state", final_state)):
+        _f32(t, name)
+    for name, t in (("k", k), ("v", v), ("a", a), ("erase", erase), ("write", write)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must have the dtype of q")
+    if k.shape != q.shape or tuple(v.shape[:2]) != (B, T):
+        raise ValueError("shape mismatch among q, k, v")
+    if tuple(a.shape) != (B, T, Hv, Dk) or tuple(erase.shape) != (B, T, Hv, Dk):
+        raise ValueError("a and erase must be [B,T,Hv,Dk]")
+    if tuple(write.shape) != (B, T, Hv, Dv):
+        raise ValueError("write must be [B,T,Hv,Dv]")
+    if tuple(A_log.shape) != (Hv, Dk):
+        raise ValueError("A_log must be [Hv,Dk]")
+    if initial_state is not None and tuple(initial_state.shape) != (B, Hv, Dk, Dv):
+        raise ValueError("initial_state must be [B,Hv,Dk,Dv]")
+    if out is None:
+        out = torch.empty((B, T, Hv, Dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = int(lib().gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims)))
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    st = lib().gdn2_chunk_fwd(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log), _ptr(erase), _ptr(write),
+        _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st)
     return out, final_state
 

@@ -178,6 +178,72 @@ gdn_status gdn_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const 
                                workspace, workspace_bytes, stream, nullptr);
 }
 
+size_t gdn2_chunk_fwd_workspace_bytes(const gdn_dims *d) {
+    if (check_dims(d, true) != GDN_OK || d->dtype != GDN_BF16) return 0;
+    if (d->B == 0 || d->T == 0) return 0;
+    return gdn::gdn2_workspace_layout(d->B, d->T, d->Hv, d->Dk, d->Dv, nullptr, nullptr);
+}
+
+gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const void *v, const void *a,
+                          const float *A_log, const void *erase, const void *write,
+                          const float *initial_state, void *out, float *final_state, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    gdn_status st = check_dims(d, true);
+    if (st != GDN_OK) return st;
+    if (d->dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "gdn2_chunk_fwd: dtype must be GDN_BF16");
+    const size_t B = d->B, T = d->T, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv, es = 2;
+    const Span sq{"q", q, B * T * Hk * Dk * es}, sk{"k", k, B * T * Hk * Dk * es};
+    const Span sv{"v", v, B * T * Hv * Dv * es};
+    const Span sa{"a", a, B * T * Hv * Dk * es}, se{"erase", erase, B * T * Hv * Dk * es};
+    const Span swr{"write", write, B * T * Hv * Dv * es};
+    const Span sal{"A_log", A_log, Hv * Dk * 4};
+    const Span s0{"initial_state", initial_state, initial_state ? B * Hv * Dk * Dv * 4 : 0};
+    const Span so{"out", out, B * T * Hv * Dv * es};
+    const Span sf{"final_state", final_state, final_state ? B * Hv * Dk * Dv * 4 : 0};
+    const size_t wneed = gdn2_chunk_fwd_workspace_bytes(d);
+    const Span sw{"workspace", workspace, wneed};
+    for (const Span *s : {&sq, &sk, &sv, &sa, &se, &swr, &so, &s0, &sf})
+        if ((st = need(*s, 16)) != GDN_OK) return st;
+    if ((st = need(sal, 4)) != GDN_OK) return st;
+    if (wneed) {
+        if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", wneed);
+        if (workspace_bytes < wneed)
+            return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, wneed);
+        if ((uintptr_t)workspace % 256) return fail(GDN_ERR_ALIGN, "workspace is not 256-byte aligned");
+    }
+    for (const Span *s : {&sq, &sk, &sv, &sa, &se, &swr, &sal, &s0, &sf, &sw})
+        if (overlap(so, *s)) return fail(GDN_ERR_ALIAS, "out overlaps %s", s->name);
+    for (const Span *s : {&sq, &sk, &sv, &sa, &se, &swr, &sal, &sw})
+        if (overlap(sf, *s)) return fail(GDN_ERR_ALIAS, "final_state overlaps %s", s->name);
+    if (overlap(sf, s0) && final_state != initial_state)
+        return fail(GDN_ERR_ALIAS, "final_state partly overlaps initial_state");
+    for (const Span *s : {&sq, &sk, &sv, &sa, &se, &swr, &sal, &s0})
+        if (overlap(sw, *s)) return fail(GDN_ERR_ALIAS, "workspace overlaps %s", s->name);
+    ok();
+    if (B == 0) return GDN_OK;
+
+    hipStream_t hs = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (T == 0) {
+        gdn::PrefillArgs p{};
+        p.B = d->B; p.Hv = d->Hv; p.Dk = d->Dk; p.Dv = d->Dv; p.S0 = initial_state; p.ST = final_state;
+        if (final_state && final_state != initial_state) e = gdn::launch_state_copy(p, hs);
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
+        return GDN_OK;
+    }
+    gdn::Gdn2Args p;
+    p.B = d->B; p.T = d->T; p.Hk = d->Hk; p.Hv = d->Hv; p.Dk = d->Dk; p.Dv = d->Dv;
+    p.scale = d->scale;
+    p.q = q; p.k = k; p.v = v; p.a = a; p.erase = erase; p.write = write; p.A_log = A_log;
+    p.S0 = initial_state; p.out = out; p.ST = final_state;
+    gdn::Gdn2Workspace ws;
+    gdn::gdn2_workspace_layout(d->B, d->T, d->Hv, d->Dk, d->Dv, workspace, &ws);
+    e = gdn::launch_chunk_local2(p, ws, hs);
+    if (e == hipSuccess) e = gdn::launch_state_scan2(p, ws, hs);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 gdn_status gdn_recurrent_step(const gdn_dims *d, const void *q, const void *k, const void *v,
                               const float *a, const float *b, const float *A_log,
                               const float *dt_bias, float *state, void *out, void *stream) {

@@ -59,41 +59,6 @@ __device__ __forceinline__ int unperm_col(int p) {
     return (p & ~31) | (((p & 7) >> 2) << 4) | (((p & 31) >> 3) << 2) | (p & 3);
 }
 
-// Off-diagonal blocks of X = (I + L)^{-1}, 16x16 blocks, diagonal blocks already
-// in Xw:  X[i][j] = -X[i][i] sum_{mb=j}^{i-1} L[i][mb] X[mb][j], one column block
-// at a time.  A column's finished blocks stay in accumulator layout, the B
-// operand of the next product.  Lf holds the A-operand fragments of L's
-// off-diagonal blocks; Xw is this wave's block-packed row-major copy of X.
-// All ten blocks are also returned in accumulator layout (Xa: lane (m, g) holds
-// X[16i + 4g + s][16j + m]).
-template <bool F32>
-__device__ __forceinline__ void inverse_offdiag(float *Xw, const f4 (&Lf)[10], int m, int g, f4 (&Xa)[10]) {
-    typedef mma<F32> M;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) Xa[tri_index(3, 3)][s] = Xw[tri_index(3, 3) * 256 + (4 * g + s) * 16 + m];
-#pragma unroll
-    for (int jb = 0; jb < 3; ++jb) {
-        f4 Xc[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) Xc[jb][s] = Xw[tri_index(jb, jb) * 256 + (4 * g + s) * 16 + m];
-        Xa[tri_index(jb, jb)] = Xc[jb];
-#pragma unroll
-        for (int ib = jb + 1; ib < 4; ++ib) {
-            f4 Tacc = {0, 0, 0, 0};
-#pragma unroll
-            for (int mb = jb; mb < ib; ++mb)
-                Tacc = M::block(Tacc, M::from_f4(Lf[tri_index(ib, mb)]), M::from_f4(Xc[mb]));
-            const f4 dv = *reinterpret_cast<const f4 *>(Xw + tri_index(ib, ib) * 256 + m * 16 + 4 * g);
-            f4 Xn = {0, 0, 0, 0};
-            Xn = -M::block(Xn, M::from_f4(dv), M::from_f4(Tacc));
-            Xc[ib] = Xn;
-            Xa[tri_index(ib, jb)] = Xn;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Xw[tri_index(ib, jb) * 256 + (4 * g + s) * 16 + m] = Xn[s];
-        }
-    }
-}
-
 template <bool F32, int DK>
 struct ChunkLocalCfg {
     typedef typename mma<F32>::E E;

@@ -38,6 +38,35 @@ hipError_t launch_chunk_local(const PrefillArgs &p, const PrefillWorkspace &ws, 
 hipError_t launch_state_scan(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s);
 hipError_t launch_state_copy(const PrefillArgs &p, hipStream_t s);  // T == 0: S_T = S_0 (or 0)
 
+// Workspace of the Gated DeltaNet-2 chunked prefill (bfloat16 inputs, float16
+// operands), per (sequence, value head, chunk) unit; every region 256-byte
+// aligned.  G is the in-chunk inclusive prefix of the channel-wise log decay.
+struct Gdn2Workspace {
+    void *eimg;    // [B*Hv*NC][64][Dk] f16 image: (sigmoid(erase) . k) . e^{G}
+    void *khimg;   // [B*Hv*NC][64][Dk] f16 image: k . e^{G_C - G}
+    void *qimg;    // [B*Hv*NC][64][Dk] f16 image: scale q . e^{G}
+    void *apair;   // [B*Hv*NC][6][64 lanes][8] f16: A = (I + M)^{-1} operand fragments
+    void *qpair;   // [B*Hv*NC][6][64 lanes][8] f16: A_qk A operand fragments
+    float *gc;     // [B*Hv*NC][Dk] f32: e^{G_C} per key channel
+    void *z;       // [B,T,Hv,Dv] f16: sigmoid(write) . v
+    size_t bytes;  // total
+};
+
+size_t gdn2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, Gdn2Workspace *ws);
+
+struct Gdn2Args {
+    int B, T, Hk, Hv, Dk, Dv;
+    float scale;
+    const void *q, *k, *v, *a, *erase, *write;  // bfloat16
+    const float *A_log;                          // [Hv][Dk]
+    const float *S0;
+    void *out;
+    float *ST;
+};
+
+hipError_t launch_chunk_local2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s);
+hipError_t launch_state_scan2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s);
+
 struct DecodeArgs {
     int B, Hk, Hv, Dk, Dv;
     bool f32;

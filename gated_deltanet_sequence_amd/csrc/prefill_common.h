@@ -94,6 +94,41 @@ __device__ __forceinline__ void img_pair(const typename mma<F32>::E *X, int rowl
 // Lower-triangular 16x16 tiles (rt >= ct) of a 64x64 matrix, numbered 0..9.
 __host__ __device__ constexpr int tri_index(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }
 
+// Off-diagonal blocks of X = (I + L)^{-1}, 16x16 blocks, diagonal blocks already
+// in Xw:  X[i][j] = -X[i][i] sum_{mb=j}^{i-1} L[i][mb] X[mb][j], one column block
+// at a time.  A column's finished blocks stay in accumulator layout, the B
+// operand of the next product.  Lf holds the A-operand fragments of L's
+// off-diagonal blocks; Xw is this wave's block-packed row-major copy of X.
+// All ten blocks are also returned in accumulator layout (Xa: lane (m, g) holds
+// X[16i + 4g + s][16j + m]).
+template <bool F32>
+__device__ __forceinline__ void inverse_offdiag(float *Xw, const f4 (&Lf)[10], int m, int g, f4 (&Xa)[10]) {
+    typedef mma<F32> M;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) Xa[tri_index(3, 3)][s] = Xw[tri_index(3, 3) * 256 + (4 * g + s) * 16 + m];
+#pragma unroll
+    for (int jb = 0; jb < 3; ++jb) {
+        f4 Xc[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Xc[jb][s] = Xw[tri_index(jb, jb) * 256 + (4 * g + s) * 16 + m];
+        Xa[tri_index(jb, jb)] = Xc[jb];
+#pragma unroll
+        for (int ib = jb + 1; ib < 4; ++ib) {
+            f4 Tacc = {0, 0, 0, 0};
+#pragma unroll
+            for (int mb = jb; mb < ib; ++mb)
+                Tacc = M::block(Tacc, M::from_f4(Lf[tri_index(ib, mb)]), M::from_f4(Xc[mb]));
+            const f4 dv = *reinterpret_cast<const f4 *>(Xw + tri_index(ib, ib) * 256 + m * 16 + 4 * g);
+            f4 Xn = {0, 0, 0, 0};
+            Xn = -M::block(Xn, M::from_f4(dv), M::from_f4(Tacc));
+            Xc[ib] = Xn;
+            Xa[tri_index(ib, jb)] = Xn;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xw[tri_index(ib, jb) * 256 + (4 * g + s) * 16 + m] = Xn[s];
+        }
+    }
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace gdn

@@ -391,33 +391,40 @@ __device__ __forceinline__ h8 img_h8(const _Float16 *X, int rowlen, int R, int k
     return *reinterpret_cast<const h8 *>(X + R * rowlen + 8 * ((4 * kq + g) ^ img_swz<false>(R, rowlen)));
 }
 
-template <typename TIn, int DK, int NL>
+template <typename TIn, int DK, int NL, bool G2>
 struct SplitCfg {
     static constexpr int NT = 2;                                   // 16-column tiles (state waves) per work-group
     static constexpr int NCOL = 16 * NT;
     static constexpr int NKQ = DK / 32;                            // 32-deep contraction steps over d_k
     static constexpr int IMG_BYTES = C * DK * 2;
     static constexpr int FRAG_BYTES = NPAIR * 64 * 8 * 2;
-    static constexpr int TOK_BYTES = C * 8;                        // gamma twice (two orders)
-    static constexpr int TILE_BYTES = C * NCOL * (int)sizeof(TIn);  // V tile
-    static constexpr int VSPR = NCOL * (int)sizeof(TIn) / 16;       // 16-byte slots per V row
-    static constexpr int VEPS = 16 / (int)sizeof(TIn);              // elements per slot
-    // Every input is staged two chunks ahead (three buffers per stream): the
-    // K image, V tile, Ae and gamma of the state waves, the Q image, Ao and
-    // gamma of the output waves.  The hand-over is single-buffered (two
-    // barriers per chunk).
-    static constexpr int S_K = 0, S_V = S_K + IMG_BYTES, S_A = S_V + TILE_BYTES, S_TK = S_A + FRAG_BYTES,
-                         S_BUF = S_TK + TOK_BYTES;
-    static constexpr int O_Q = 0, O_F = O_Q + IMG_BYTES, O_TK = O_F + FRAG_BYTES, O_BUF = O_TK + TOK_BYTES;
+    // per-chunk record of the state waves: gamma twice (two token orders), or
+    // for the channel-wise decay e^{G_C} per key channel; the output waves'
+    // gamma record (none for the channel-wise decay, folded into its Q image)
+    static constexpr int STK_BYTES = G2 ? DK * 4 : C * 8, OTK_BYTES = G2 ? 0 : C * 8;
+    static constexpr int TILE_BYTES = C * NCOL * 2;                // V (or Z) tile, 16-bit elements
+    static constexpr int VSPR = NCOL * 2 / 16;                     // 16-byte slots per V row
+    static constexpr int VEPS = 8;                                 // elements per slot
+    // State-wave inputs: the image for P = K S (K; Et for the channel-wise
+    // decay), the image of the state update's K^T operands (the same K image;
+    // a separate Kh image for the channel-wise decay), V (Z), Ae, the record.
+    // Output-wave inputs: the Q image, Ao, gamma.  Every stream has NSB (NOB)
+    // LDS buffers, issued NSB-1 (NOB-1) chunks ahead: 3 for the scalar decay,
+    // 2 for the channel-wise decay (its two state images fill LDS).  The
+    // hand-over is single-buffered (two barriers per chunk).
+    static constexpr int S_K = 0, S_KH = G2 ? S_K + IMG_BYTES : S_K, S_V = S_KH + IMG_BYTES,
+                         S_A = S_V + TILE_BYTES, S_TK = S_A + FRAG_BYTES, S_BUF = S_TK + STK_BYTES;
+    static constexpr int O_Q = 0, O_F = O_Q + IMG_BYTES, O_TK = O_F + FRAG_BYTES, O_BUF = O_TK + OTK_BYTES;
     // hand-over: S (d_k x 16) and R' (64 x 16) of each column tile as operand pairs, 1 KB each
     static constexpr int X_S = 0, X_R = NT * NKQ * 1024, X_BUF = X_R + NT * 2 * 1024;
-    static constexpr int NB = 3;  // buffers per input stream
-    static constexpr int OFF_S = 0, OFF_O = OFF_S + NB * S_BUF, OFF_X = OFF_O + NB * O_BUF, LDS = OFF_X + X_BUF;
+    static constexpr int NSB = G2 ? 2 : 3, NOB = G2 ? 2 : 3;
+    static constexpr int OFF_S = 0, OFF_O = OFF_S + NSB * S_BUF, OFF_X = OFF_O + NOB * O_BUF, LDS = OFF_X + X_BUF;
     static constexpr int IMG_UNITS = IMG_BYTES / 1024, FRAG_UNITS = FRAG_BYTES / 1024,
                          TILE_UNITS = TILE_BYTES / 1024;
     // loads per chunk of the state loader and of the output loader
-    static constexpr int STATE_LOADS = IMG_UNITS + TILE_UNITS + FRAG_UNITS + 1, OUT_LOADS = IMG_UNITS + FRAG_UNITS + 1;
-    static_assert(STATE_LOADS < 64 && OUT_LOADS < 64, "vmcnt");
+    static constexpr int STATE_LOADS = IMG_UNITS * (G2 ? 2 : 1) + TILE_UNITS + FRAG_UNITS + 1,
+                         OUT_LOADS = IMG_UNITS + FRAG_UNITS + (G2 ? 0 : 1);
+    static_assert((NSB - 1) * STATE_LOADS < 64 && (NOB - 1) * OUT_LOADS < 64, "vmcnt");
     static_assert(VSPR >= 4 && (VSPR & (VSPR - 1)) == 0, "V slots");
     static_assert(S_BUF % 16 == 0 && O_BUF % 16 == 0, "alignment");
     static_assert(LDS <= 160 * 1024, "LDS");
@@ -427,10 +434,10 @@ struct SplitCfg {
 // instruction, straight from memory into LDS (no registers).  One loader wave
 // stages the state-wave inputs, the other the output-wave inputs: each wave's
 // loads complete in issue order, so the two streams do not wait on each other.
-template <typename TIn, int DK, int NL>
+template <typename TIn, int DK, int NL, bool G2>
 struct SplitLoader {
-    typedef SplitCfg<TIn, DK, NL> CF;
-    __amdgpu_buffer_rsrc_t vres, rq, rk, ra, rf, rtk;
+    typedef SplitCfg<TIn, DK, NL, G2> CF;
+    __amdgpu_buffer_rsrc_t vres, rq, rk, rkh, ra, rf, rtk, rgc;
     int lane;
     unsigned vcol;  // element offset of this group's first V column in a token row
     unsigned vrow;  // elements per token row of V (Hv * d_v)
@@ -438,12 +445,16 @@ struct SplitLoader {
     __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t r, char *dst, int src_off) const {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, lane * 16, src_off, 0, 0);
     }
-    // state-wave inputs of chunk n: K image, V columns, Ae fragments, gamma (STATE_LOADS loads)
+    // state-wave inputs of chunk n: image(s), V columns, Ae fragments, record (STATE_LOADS loads)
     __device__ __forceinline__ void stage_state(char *smem, int n, int buf) const {
         char *base = smem + CF::OFF_S + buf * CF::S_BUF;
         const int io = n * CF::IMG_BYTES, fo = n * CF::FRAG_BYTES;
 #pragma unroll
         for (int u = 0; u < CF::IMG_UNITS; ++u) copy(rk, base + CF::S_K + u * 1024, io + u * 1024);
+        if constexpr (G2) {
+#pragma unroll
+            for (int u = 0; u < CF::IMG_UNITS; ++u) copy(rkh, base + CF::S_KH + u * 1024, io + u * 1024);
+        }
 #pragma unroll
         for (int u = 0; u < CF::TILE_UNITS; ++u) {
             const int slot = u * 64 + lane;
@@ -454,7 +465,7 @@ struct SplitLoader {
         }
 #pragma unroll
         for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(ra, base + CF::S_A + u * 1024, fo + u * 1024);
-        if (lane < CF::TOK_BYTES / 16) copy(rtk, base + CF::S_TK, n * CF::TOK_BYTES);
+        if (lane < CF::STK_BYTES / 16) copy(G2 ? rgc : rtk, base + CF::S_TK, n * CF::STK_BYTES);
     }
     // output-wave inputs of chunk n: Q image, Ao fragments, gamma (OUT_LOADS loads)
     __device__ __forceinline__ void stage_out(char *smem, int n, int buf) const {
@@ -464,19 +475,21 @@ struct SplitLoader {
         for (int u = 0; u < CF::IMG_UNITS; ++u) copy(rq, base + CF::O_Q + u * 1024, io + u * 1024);
 #pragma unroll
         for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(rf, base + CF::O_F + u * 1024, fo + u * 1024);
-        if (lane < CF::TOK_BYTES / 16) copy(rtk, base + CF::O_TK, n * CF::TOK_BYTES);
+        if constexpr (!G2)
+            if (lane < CF::OTK_BYTES / 16) copy(rtk, base + CF::O_TK, n * CF::OTK_BYTES);
     }
 };
 
-template <typename TIn, int DK, int DV, int NL>
+template <typename TIn, int DK, int DV, int NL, bool G2>
 __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
-    int T, int Hk, int Hv, int NC, const TIn *__restrict__ v, const float *__restrict__ tok,
+    int T, int Hk, int Hv, int NC, const void *__restrict__ v, const float *__restrict__ tok,
     const _Float16 *__restrict__ apair, const _Float16 *__restrict__ qpair,
     const _Float16 *__restrict__ qimg, const _Float16 *__restrict__ kimg,
+    const _Float16 *__restrict__ khimg, const float *__restrict__ gcrec,
     const float *__restrict__ S0, TIn *__restrict__ out, float *__restrict__ ST) {
     static_assert(sizeof(TIn) == 2, "bfloat16 inputs");
     static_assert(NL == 2, "waves 4 and 5 load");
-    typedef SplitCfg<TIn, DK, NL> CF;
+    typedef SplitCfg<TIn, DK, NL, G2> CF;
     typedef _Float16 E;
     constexpr int NT = CF::NT, NCOL = CF::NCOL, NKB = DK / 16, NKQ = CF::NKQ, NCG = DV / NCOL;
 
@@ -501,13 +514,16 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
     if (w >= 4) {
         // ================= loader waves =================
         const size_t ku0 = ((size_t)bb * Hk + hk) * NC, vu0 = ((size_t)bb * Hv + hv) * NC;
-        SplitLoader<TIn, DK, NL> ld;
-        ld.vres = rsrc(v + (size_t)bb * seq_elems, seq_elems * sizeof(TIn));
-        ld.rq = rsrc(qimg + ku0 * C * DK, (size_t)NC * CF::IMG_BYTES);
-        ld.rk = rsrc(kimg + ku0 * C * DK, (size_t)NC * CF::IMG_BYTES);
+        const size_t iu0 = G2 ? vu0 : ku0;  // images per value head (channel-wise decay) or per key head
+        SplitLoader<TIn, DK, NL, G2> ld;
+        ld.vres = rsrc((const char *)v + (size_t)bb * seq_elems * 2, seq_elems * 2);
+        ld.rq = rsrc(qimg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
+        ld.rk = rsrc(kimg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
+        if constexpr (G2) ld.rkh = rsrc(khimg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
         ld.ra = rsrc(apair + vu0 * (NPAIR * 64 * 8), (size_t)NC * CF::FRAG_BYTES);
         ld.rf = rsrc(qpair + vu0 * (NPAIR * 64 * 8), (size_t)NC * CF::FRAG_BYTES);
-        ld.rtk = rsrc(tok + vu0 * C * 2, (size_t)NC * CF::TOK_BYTES);
+        if constexpr (G2) ld.rgc = rsrc(gcrec + vu0 * DK, (size_t)NC * CF::STK_BYTES);
+        else ld.rtk = rsrc(tok + vu0 * C * 2, (size_t)NC * CF::STK_BYTES);
         ld.lane = lane;
         ld.vcol = (unsigned)(hv * DV + NCOL * cg);
         ld.vrow = (unsigned)(Hv * DV);
@@ -522,46 +538,56 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         // that publishes them, more than two chunk intervals later.  Loads
         // complete in issue order, so waiting until only the newest chunk's
         // loads are outstanding suffices.
+        // wait until at most k chunks' loads of this stream are in flight
+        // (at most K chunks ahead: K = buffers - 1 <= 2)
+        auto wait_chunks = [](int k, auto LOADS, auto KMAX) {
+            constexpr int L = decltype(LOADS)::value, K = decltype(KMAX)::value;
+            if (k <= 0) wait_vmcnt<0>();
+            else if (K < 2 || k == 1) wait_vmcnt<L>();
+            else wait_vmcnt<(K < 2 ? 0 : 2 * L)>();
+        };
         if (w == 5) {
-            // state-wave inputs: chunk m is needed from P(m-1) on
-            ld.stage_state(smem, 0, 0);
-            if (NC > 1) ld.stage_state(smem, 1, 1);
-            if (NC > 1) wait_vmcnt<CF::STATE_LOADS>();
-            else wait_vmcnt<0>();
+            // state-wave inputs: chunk m is read from P(m-1) to P(m), buffer
+            // m % NSB; chunk n+NSB is issued after P(n)
+            const std::integral_constant<int, CF::STATE_LOADS> SL;
+            const std::integral_constant<int, CF::NSB - 1> SK;
+            const int npre = NC < CF::NSB ? NC : CF::NSB;
+            for (int j = 0; j < npre; ++j) ld.stage_state(smem, j, j);
+            wait_chunks(npre - 1, SL, SK);
             bare_barrier();  // P(-1): chunk 0
-            if (NC > 2) ld.stage_state(smem, 2, 2);
-            if (NC > 2) wait_vmcnt<CF::STATE_LOADS>();
-            else wait_vmcnt<0>();
+            wait_chunks(npre - 2, SL, SK);
             bare_barrier();  // P(0): chunk 1
-            int sb = 0;      // buffer of chunk n + 3
+            int sb = 0;      // buffer of chunk n (and of chunk n + NSB)
             for (int n = 0; n < NC; ++n) {
-                if (n + 3 < NC) ld.stage_state(smem, n + 3, sb);
+                if (n + CF::NSB < NC) ld.stage_state(smem, n + CF::NSB, sb);
                 bare_barrier();  // F(n)
                 if (n + 1 < NC) {
-                    if (n + 3 < NC) wait_vmcnt<CF::STATE_LOADS>();
-                    else wait_vmcnt<0>();
+                    const int last = n + CF::NSB < NC - 1 ? n + CF::NSB : NC - 1;  // newest chunk issued
+                    wait_chunks(last - n - 2, SL, SK);
                     bare_barrier();  // P(n+1): chunk n+2
                 }
-                sb = sb == CF::NB - 1 ? 0 : sb + 1;
+                sb = sb == CF::NSB - 1 ? 0 : sb + 1;
             }
         } else {
-            // output-wave inputs: chunk m is needed from P(m) on
-            ld.stage_out(smem, 0, 0);
-            if (NC > 1) ld.stage_out(smem, 1, 1);
+            // output-wave inputs: chunk m is read from P(m) to P(m+1), buffer
+            // m % NOB; chunk n+NOB-1 is issued after P(n)
+            const std::integral_constant<int, CF::OUT_LOADS> OL;
+            const std::integral_constant<int, CF::NOB - 1> OK;
+            const int npre = NC < CF::NOB - 1 ? NC : CF::NOB - 1;
+            for (int j = 0; j < npre; ++j) ld.stage_out(smem, j, j);
             bare_barrier();  // P(-1)
-            if (NC > 1) wait_vmcnt<CF::OUT_LOADS>();
-            else wait_vmcnt<0>();
+            wait_chunks(npre - 1, OL, OK);
             bare_barrier();  // P(0): chunk 0
-            int ob = 2;      // buffer of chunk n + 2
+            int ob = CF::NOB - 1;  // buffer of chunk n + NOB - 1
             for (int n = 0; n < NC; ++n) {
-                if (n + 2 < NC) ld.stage_out(smem, n + 2, ob);
+                if (n + CF::NOB - 1 < NC) ld.stage_out(smem, n + CF::NOB - 1, ob);
                 bare_barrier();  // F(n)
                 if (n + 1 < NC) {
-                    if (n + 2 < NC) wait_vmcnt<CF::OUT_LOADS>();
-                    else wait_vmcnt<0>();
+                    const int last = n + CF::NOB - 1 < NC - 1 ? n + CF::NOB - 1 : NC - 1;
+                    wait_chunks(last - n - 1, OL, OK);
                     bare_barrier();  // P(n+1): chunk n+1
                 }
-                ob = ob == CF::NB - 1 ? 0 : ob + 1;
+                ob = ob == CF::NOB - 1 ? 0 : ob + 1;
             }
         }
         return;
@@ -593,7 +619,8 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the hand-over is in registers
             bare_barrier();                      // F(n)
-            const f4 gam = *reinterpret_cast<const f4 *>(Tq + 64 + 4 * m);  // tokens m, 16+m, 32+m, 48+m
+            f4 gam = {1.f, 1.f, 1.f, 1.f};  // the channel-wise decay has it folded into Q
+            if constexpr (!G2) gam = *reinterpret_cast<const f4 *>(Tq + 64 + 4 * m);  // tokens m, 16+m, 32+m, 48+m
             auto rows = [&](auto RR) {
                 constexpr int r = decltype(RR)::value;
                 f4 sq[NT];
@@ -607,7 +634,7 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
                 }
                 f4 acc[NT];
 #pragma unroll
-                for (int c = 0; c < NT; ++c) acc[c] = gam[r] * sq[c];
+                for (int c = 0; c < NT; ++c) acc[c] = G2 ? sq[c] : gam[r] * sq[c];
 #pragma unroll
                 for (int qq = 0; qq <= r / 2; ++qq) {
                     const h8 f = *reinterpret_cast<const h8 *>(Of + pair_index(r, qq) * 512);
@@ -636,7 +663,7 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
             if (w == 0) emit(n, ob, std::integral_constant<int, 0>(), std::integral_constant<int, 3>());
             else emit(n, ob, std::integral_constant<int, 1>(), std::integral_constant<int, 2>());
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this chunk's LDS reads are done
-            ob = ob == CF::NB - 1 ? 0 : ob + 1;
+            ob = ob == CF::NOB - 1 ? 0 : ob + 1;
         }
         return;
     }
@@ -682,15 +709,16 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         }
     }
 
-    // Operands of chunk n (K, V, gamma, gamma_C, Ae), read one chunk ahead,
-    // spread over chunk n-1's state update (after the barrier that publishes
-    // chunk n): NRD separate reads.
+    // Operands of chunk n (K, V, gamma, gamma_C, Ae; for the channel-wise decay
+    // Et, Z, A), read one chunk ahead, spread over chunk n-1's state update
+    // (after the barrier that publishes chunk n): NRD separate reads.  (The
+    // channel-wise e^{G_C} per state row is read in phase B, where it is used.)
     h8 kf[NKQ][4];
     s4 vt[4];
-    f4 ga[4];  // gamma of rows 16r + 4g + i
-    float gC;
+    f4 ga[4];  // gamma of rows 16r + 4g + i (scalar decay)
+    float gC;  // gamma_C (scalar decay)
     h8 afr[NPAIR];
-    constexpr int NRD = 4 * NKQ + 4 + 4 + 1 + NPAIR;
+    constexpr int NRD = 4 * NKQ + 4 + (G2 ? 0 : 4 + 1) + NPAIR;
     auto read_item = [&](int sbi, int it) {  // sbi: state buffer of the chunk
         const char *base = smem + CF::OFF_S + sbi * CF::S_BUF;
         const float *Tq = reinterpret_cast<const float *>(base + CF::S_TK);
@@ -698,6 +726,9 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
             kf[it / 4][it % 4] = img_h8(reinterpret_cast<const E *>(base + CF::S_K), DK, 16 * (it % 4) + m, it / 4, g);
         } else if ((it -= 4 * NKQ) < 4) {
             vt[it] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + CF::S_V + vt_off[it]));
+        } else if (G2) {
+            it -= 4;
+            afr[it] = *reinterpret_cast<const h8 *>(reinterpret_cast<const E *>(base + CF::S_A) + lane * 8 + it * 512);
         } else if ((it -= 4) < 4) {
             ga[it] = *reinterpret_cast<const f4 *>(Tq + 16 * it + 4 * g);
         } else if ((it -= 4) < 1) {
@@ -731,8 +762,8 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
     }
     int cur = 0;  // state buffer of chunk n
     for (int n = 0; n < NC; ++n) {
-        const int nxt = cur == CF::NB - 1 ? 0 : cur + 1;
-        const char *Ks8 = smem + CF::OFF_S + cur * CF::S_BUF + CF::S_K;
+        const int nxt = cur == CF::NSB - 1 ? 0 : cur + 1;
+        const char *Ks8 = smem + CF::OFF_S + cur * CF::S_BUF + CF::S_KH;  // K^T operands (Kh for the channel-wise decay)
         char *xb = smem + CF::OFF_X;
         // K^T operand pair (kb, qq): two transposed reads, rows 32qq and 32qq + 16 on
         auto kt_pair = [&](int kb, int qq) {
@@ -741,6 +772,18 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
             return cat_h8(__builtin_bit_cast(h4, lo), __builtin_bit_cast(h4, hi));
         };
         auto sp_pair = [&](int kq) { return cat_h8(to_h4(S[2 * kq]), to_h4(S[2 * kq + 1])); };
+        // S rows 16kb .. 16kb+15 decay to the chunk end: by gamma_C, or per
+        // key channel by e^{G_C} (state rows 16kb + 4g + i)
+        f4 gcv[NKB];
+        if constexpr (G2) {
+            const float *Tq = reinterpret_cast<const float *>(smem + CF::OFF_S + cur * CF::S_BUF + CF::S_TK);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) gcv[kb] = *reinterpret_cast<const f4 *>(Tq + 16 * kb + 4 * g);
+        }
+        auto decay = [&](int kb) {
+            if constexpr (G2) S[kb] = S[kb] * gcv[kb];
+            else S[kb] *= gC;
+        };
         h8 Sp[NKQ];
         h8 tf[NKB][2];
         f4 P[4], Ae[4];
@@ -751,9 +794,14 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         // (row tiles 2q, 2q+1 form operand pair q, handed over as one 1 KB block)
         auto resid = [&](int rr) {
             f4 x;
+            if constexpr (G2) {  // Z (float16) - Et S; the whole 4-vector is reinterpreted
+                x = __builtin_convertvector(__builtin_bit_cast(h4, vt[rr]), f4);
+                Rb[rr] = to_h4(x - P[rr]);
+            } else {  // V (bfloat16) - gamma K S
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = bf16_to_f32((uint16_t)vt[rr][i]);
-            Rb[rr] = to_h4(x - ga[rr] * P[rr]);
+                for (int i = 0; i < 4; ++i) x[i] = bf16_to_f32((uint16_t)vt[rr][i]);
+                Rb[rr] = to_h4(x - ga[rr] * P[rr]);
+            }
             if (rr & 1)
                 *reinterpret_cast<h8 *>(xb + CF::X_R + (c * 2 + rr / 2) * 1024 + lane * 16) = cat_h8(Rb[rr - 1], Rb[rr]);
         };
@@ -781,18 +829,18 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         resid(3);
         GDN_STEP();
         Ae[2] = mfma_f16_k32(afr[pair_index(2, 0)], cat_h8(Rb[0], Rb[1]), Ae[2]);
-        S[0] *= gC;
-        S[1] *= gC;
+        decay(0);
+        decay(1);
         De[0] = to_h4(Ae[0]);
         GDN_STEP();
         Ae[3] = mfma_f16_k32(afr[pair_index(3, 0)], cat_h8(Rb[0], Rb[1]), Ae[3]);
-        S[2] *= gC;
-        S[3] *= gC;
+        decay(2);
+        decay(3);
         De[1] = to_h4(Ae[1]);
         GDN_STEP();
         Ae[2] = mfma_f16_k32(afr[pair_index(2, 1)], cat_h8(Rb[2], Rb[3]), Ae[2]);
 #pragma unroll
-        for (int kb = 4; kb < NKB; ++kb) S[kb] *= gC;
+        for (int kb = 4; kb < NKB; ++kb) decay(kb);
         GDN_STEP();
         Ae[3] = mfma_f16_k32(afr[pair_index(3, 1)], cat_h8(Rb[2], Rb[3]), Ae[3]);
 
@@ -843,11 +891,11 @@ static hipError_t launch_scan_t(const PrefillArgs &p, const PrefillWorkspace &ws
     if constexpr (!F32) {
         constexpr int NL = 2;
         const int NC = (p.T + C - 1) / C;
-        const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<TIn, DK, NL>::NCOL));
-        hipLaunchKernelGGL((scan_split_kernel<TIn, DK, DV, NL>), dim3(blocks), dim3(64 * (4 + NL)), 0, s,
-                           p.T, p.Hk, p.Hv, NC, (const TIn *)p.v, ws.tok, (const E *)ws.apair,
-                           (const E *)ws.qpair, (const E *)ws.qimg, (const E *)ws.kimg,
-                           p.S0, (TIn *)p.out, p.ST);
+        const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<TIn, DK, NL, false>::NCOL));
+        hipLaunchKernelGGL((scan_split_kernel<TIn, DK, DV, NL, false>), dim3(blocks), dim3(64 * (4 + NL)), 0, s,
+                           p.T, p.Hk, p.Hv, NC, p.v, ws.tok, (const E *)ws.apair,
+                           (const E *)ws.qpair, (const E *)ws.qimg, (const E *)ws.kimg, (const E *)nullptr,
+                           (const float *)nullptr, p.S0, (TIn *)p.out, p.ST);
         return hipGetLastError();
     } else {
         constexpr int NW = 2, NL = 2;
@@ -872,6 +920,28 @@ static hipError_t launch_scan_dt(const PrefillArgs &p, const PrefillWorkspace &w
 
 hipError_t launch_state_scan(const PrefillArgs &p, const PrefillWorkspace &ws, hipStream_t s) {
     return p.f32 ? launch_scan_dt<true, float>(p, ws, s) : launch_scan_dt<false, bf16_t>(p, ws, s);
+}
+
+// Gated DeltaNet-2 (channel-wise decay, bfloat16 inputs): the same work-group
+// with Et for P, Kh for the state update, Z for V, e^{G_C} per state row.
+template <int DK, int DV>
+static hipError_t launch_scan2_t(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s) {
+    constexpr int NL = 2;
+    const int NC = (p.T + C - 1) / C;
+    const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<bf16_t, DK, NL, true>::NCOL));
+    hipLaunchKernelGGL((scan_split_kernel<bf16_t, DK, DV, NL, true>), dim3(blocks), dim3(64 * (4 + NL)), 0, s,
+                       p.T, p.Hk, p.Hv, NC, (const void *)ws.z, (const float *)nullptr,
+                       (const _Float16 *)ws.apair, (const _Float16 *)ws.qpair, (const _Float16 *)ws.qimg,
+                       (const _Float16 *)ws.eimg, (const _Float16 *)ws.khimg, ws.gc, p.S0, (bf16_t *)p.out, p.ST);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_scan2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s) {
+    if (p.Dk == 128 && p.Dv == 128) return launch_scan2_t<128, 128>(p, ws, s);
+    if (p.Dk == 128 && p.Dv == 64) return launch_scan2_t<128, 64>(p, ws, s);
+    if (p.Dk == 64 && p.Dv == 128) return launch_scan2_t<64, 128>(p, ws, s);
+    if (p.Dk == 64 && p.Dv == 64) return launch_scan2_t<64, 64>(p, ws, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_state_copy(const PrefillArgs &p, hipStream_t s) {

@@ -111,6 +111,33 @@ gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k,
                                void *workspace, size_t workspace_bytes, void *stream,
                                void *const *stage_events);
 
+/* Gated DeltaNet-2 chunked prefill (zhichai.net "Gated DeltaNet-2" digest:
+ * the decoupled update S <- diag(D_t) S + k_t (z_t - (diag(D_t) S)^T e_t)^T with
+ * a channel-wise decay D_t, erase gate b_t and write gate w_t, e_t = b_t . k_t,
+ * z_t = w_t . v_t, read-out o_t = scale S_t^T q_t; section "高效训练：WY 算法依然成立"
+ * for its chunked WY form).  Gates from raw logits, per (b, t, value head,
+ * channel): D = exp(-exp(A_log[h][c]) * softplus(a)), b = sigmoid(erase),
+ * w = sigmoid(write).  With D_t = alpha_t I and both gates equal to beta_t it
+ * is the rule of gdn_chunk_fwd.
+ *   q, k          [B,T,Hk,Dk] bfloat16
+ *   v             [B,T,Hv,Dv] bfloat16
+ *   a, erase      [B,T,Hv,Dk] bfloat16 decay and erase-gate logits
+ *   write         [B,T,Hv,Dv] bfloat16 write-gate logits
+ *   A_log         [Hv,Dk] float32
+ *   initial_state [B,Hv,Dk,Dv] float32, or NULL for a zero state
+ *   out           [B,T,Hv,Dv] bfloat16 (written)
+ *   final_state   [B,Hv,Dk,Dv] float32 (written), or NULL; may be exactly
+ *                 initial_state
+ *   workspace     device scratch of at least gdn2_chunk_fwd_workspace_bytes(d)
+ *                 bytes, 256-byte aligned.
+ * d->dtype must be GDN_BF16 (GDN_ERR_UNSUPPORTED otherwise).  Same aliasing
+ * rules and limits as gdn_chunk_fwd. */
+size_t gdn2_chunk_fwd_workspace_bytes(const gdn_dims *d);
+gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const void *v,
+                          const void *a, const float *A_log, const void *erase, const void *write,
+                          const float *initial_state, void *out, float *final_state, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* One-token recurrent decode step on a cached state, updated in place
  * (wanger-sjtu page: the recurrent branch reads and updates the cached
  * recurrent state; rainlin page, five-step form for one token).

@@ -235,3 +235,106 @@ def test_binding_rejects_missing_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         binding.lib()
+
+
+# ---- Gated DeltaNet-2 prefill (gdn2_chunk_fwd) ----
+
+def gdn2_args(buf, d, **override):
+    B, T, Hk, Hv, Dk, Dv = d.B, d.T, d.Hk, d.Hv, d.Dk, d.Dv
+    args = dict(
+        q=buf(B * T * Hk * Dk * 2), k=buf(B * T * Hk * Dk * 2), v=buf(B * T * Hv * Dv * 2),
+        a=buf(B * T * Hv * Dk * 2), A_log=buf(Hv * Dk * 4), erase=buf(B * T * Hv * Dk * 2),
+        write=buf(B * T * Hv * Dv * 2), S0=None, out=buf(B * T * Hv * Dv * 2),
+        ST=buf(B * Hv * Dk * Dv * 4))
+    ws = binding.lib().gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    args["ws"] = buf(ws)
+    args["ws_bytes"] = ws
+    args.update(override)
+    return args
+
+
+def call_gdn2(d, a):
+    return binding.lib().gdn2_chunk_fwd(ctypes.byref(d), a["q"], a["k"], a["v"], a["a"], a["A_log"],
+                                        a["erase"], a["write"], a["S0"], a["out"], a["ST"], a["ws"],
+                                        a["ws_bytes"], None)
+
+
+def test_gdn2_declared():
+    assert {"gdn2_chunk_fwd", "gdn2_chunk_fwd_workspace_bytes"} <= set(declared_functions())
+
+
+def test_gdn2_workspace_bytes():
+    L = binding.lib()
+    d = dims(B=1, T=8192, Hk=16, Hv=64, Dk=128, Dv=128)
+    n = L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    units = 64 * 128  # (value head, chunk) pairs
+    # per unit: three 64 x 128 float16 images (Et, Kh, Q~), two 6 KB fragment sets and the
+    # chunk-end decay per key channel; plus Z [B,T,Hv,Dv] float16
+    need = units * (3 * 64 * 128 * 2 + 2 * 6 * 64 * 8 * 2 + 128 * 4) + 8192 * 64 * 128 * 2
+    assert need <= n < need + 8 * 256
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims(dtype=binding.GDN_F32))) == 0
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims(Hv=3))) == 0
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims(T=0))) == 0
+    assert L.gdn2_chunk_fwd_workspace_bytes(None) == 0
+
+
+def test_gdn2_rejects_float32():
+    buf = Buf()
+    d = dims()
+    a = gdn2_args(buf, d)
+    assert call_gdn2(dims(dtype=binding.GDN_F32), a) == ERR_UNSUPPORTED
+    assert "BF16" in last_error()
+
+
+@pytest.mark.parametrize("kw,code", [(dict(Hv=3), ERR_SHAPE), (dict(Dk=96), ERR_UNSUPPORTED),
+                                     (dict(chunk=32), ERR_UNSUPPORTED), (dict(T=-1), ERR_SHAPE)])
+def test_gdn2_rejects_bad_dims(kw, code):
+    buf = Buf()
+    assert call_gdn2(dims(**kw), gdn2_args(buf, dims())) == code
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "a", "A_log", "erase", "write", "out"])
+def test_gdn2_rejects_null_pointer(name):
+    buf = Buf()
+    d = dims()
+    assert call_gdn2(d, gdn2_args(buf, d, **{name: None})) == ERR_NULL
+    assert name in last_error()
+
+
+@pytest.mark.parametrize("name", ["a", "erase", "write", "ST"])
+def test_gdn2_rejects_misaligned(name):
+    buf = Buf()
+    d = dims()
+    a = gdn2_args(buf, d)
+    a[name] += 8
+    assert call_gdn2(d, a) == ERR_ALIGN
+
+
+def test_gdn2_workspace_and_alias_checks():
+    buf = Buf()
+    d = dims()
+    assert call_gdn2(d, gdn2_args(buf, d, ws=None)) == ERR_WORKSPACE
+    a = gdn2_args(buf, d)
+    a["ws_bytes"] -= 1
+    assert call_gdn2(d, a) == ERR_WORKSPACE
+    a = gdn2_args(buf, d)
+    a["out"] = a["write"]
+    assert call_gdn2(d, a) == ERR_ALIAS and "out overlaps write" in last_error()
+    a = gdn2_args(buf, d)
+    a["ST"] = a["erase"]
+    assert call_gdn2(d, a) == ERR_ALIAS
+    a = gdn2_args(buf, d)
+    s0 = buf(d.B * d.Hv * d.Dk * d.Dv * 4 + 64)
+    a["S0"], a["ST"] = s0, s0 + 16
+    assert call_gdn2(d, a) == ERR_ALIAS and "partly" in last_error()
+    a = gdn2_args(buf, d)
+    a["ws"] = a["a"]
+    assert call_gdn2(d, a) == ERR_ALIAS
+
+
+def test_gdn2_zero_batch_is_a_noop():
+    buf = Buf()
+    d = dims(B=0)
+    a = gdn2_args(buf, d, q=None, k=None, v=None, a=None, erase=None, write=None, out=None, ST=None,
+                  ws=None)
+    assert call_gdn2(d, a) == OK
