@@ -59,6 +59,17 @@ def scan_flop_per_token_head(dk, dv, C):
     return 2 * (3 * dk * dv + C * dv // 2 + C * dv // 2)
 
 
+# Gated DeltaNet-2 (channel-wise decay): the chunk-local products are per value head.
+#   whole prefill:  3 dk dv + C (dk + dv)   MAC  (M and A_qk: C dk / 2 each; A R', A_qk A R': C dv / 2 each)
+#   state scan:     3 dk dv + C dv          MAC
+def gdn2_flop_per_token_head(dk, dv, C):
+    return 2 * (3 * dk * dv + C * (dk + dv))
+
+
+def gdn2_scan_flop_per_token_head(dk, dv, C):
+    return 2 * (3 * dk * dv + C * dv)
+
+
 def prefill_bytes(B, T, Hk, Hv, Dk, Dv, es, init_state):
     qk = 2 * B * T * Hk * Dk * es
     vo = 2 * B * T * Hv * Dv * es
@@ -82,8 +93,15 @@ def log(msg):
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "gated_deltanet_sequence_amd", "csrc")
 COPY_MIB = 256                      # calibration copy: 256 MiB read + 256 MiB written
-TRAFFIC_FILES = {"scan_split_kernel": "scan_split_kernel_prefill_t4096_traffic.md",
-                 "decode_kernel": "decode_kernel_decode_b256_traffic.md"}
+# kernel key -> (regex on the demangled kernel name, summary file)
+TRAFFIC_FILES = {
+    # (names with float16 template arguments come out mangled: Lb0E / Lb1E is the bool)
+    "scan_split_kernel": (r"scan_split_kernel(<[^>]*false>|I.*Lb0E)", "scan_split_kernel_prefill_t4096_traffic.md"),
+    "chunk_local_kernel": (r"chunk_local_kernel", "chunk_local_kernel_prefill_t4096_traffic.md"),
+    "decode_kernel": (r"decode_kernel", "decode_kernel_decode_b256_traffic.md"),
+    "scan_split_kernel_gdn2": (r"scan_split_kernel(<[^>]*true>|I.*Lb1E)", "scan_split_kernel_gdn2_t8192_traffic.md"),
+    "chunk_local2_kernel": (r"chunk_local2_kernel", "chunk_local2_kernel_gdn2_t8192_traffic.md"),
+}
 
 
 def kernel_sources_sha256():
@@ -100,7 +118,7 @@ def kernel_sources_sha256():
 def stored_traffic(kernel):
     """Bytes per launch from the committed counter summary, or None if the
     summary is missing or the kernel sources changed since it was taken."""
-    path = os.path.join(PROFILES, TRAFFIC_FILES.get(kernel, "-"))
+    path = os.path.join(PROFILES, TRAFFIC_FILES.get(kernel, ("", "-"))[1])
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -157,15 +175,15 @@ def summarize_pmc(fetch_dir, write_dir):
     kib = COPY_MIB * 1024
     f_scale, w_scale = kib / cf, kib / cw
     sha = kernel_sources_sha256()
-    for kernel, fname in TRAFFIC_FILES.items():
-        kf, nkf = _per_dispatch(f_rows, "FETCH_SIZE", kernel)
-        kw, nkw = _per_dispatch(w_rows, "WRITE_SIZE", kernel)
+    for kernel, (rx, fname) in TRAFFIC_FILES.items():
+        kf, nkf = _per_dispatch(f_rows, "FETCH_SIZE", rx)
+        kw, nkw = _per_dispatch(w_rows, "WRITE_SIZE", rx)
         if kf is None or kw is None:
             continue
         fetch_b = kf * f_scale * 1024
         write_b = kw * w_scale * 1024
         lines = [
-            f"# HBM traffic of {kernel} (rocprofv3 counters)", "",
+            f"# HBM traffic of {kernel} (rocprofv3 counters; kernel names matching `{rx}`)", "",
             "Two counter passes over the same bench command, one counter each:", "",
             "```",
             "cd /tmp && export TMPDIR=/tmp",
@@ -322,6 +340,51 @@ def bench_decode(args, torch, gdn, synth):
     return res
 
 
+def bench_gdn2(args, torch, gdn, synth):
+    """The Gated DeltaNet-2 prefill (B=1, T=8192, 16/64 heads, d=128, bf16): K steps of
+    gdn2_chunk_fwd over rotated buffer sets, nothing else in the timed region."""
+    spec = synth.WORKLOADS["gdn2_t8192"]
+    log(f"[bench] gdn2 workload {spec}")
+    inp = synth.make_inputs(spec)
+    sets = []
+    for _ in range(args.rotate):
+        d = {k: (None if v is None else v.cuda().contiguous()) for k, v in inp.items()}
+        d["out"] = torch.empty((spec.B, spec.T, spec.Hv, spec.Dv), dtype=spec.torch_dtype, device="cuda")
+        d["ST"] = torch.empty((spec.B, spec.Hv, spec.Dk, spec.Dv), dtype=torch.float32, device="cuda")
+        d["ws"] = gdn.alloc_workspace_gdn2(
+            gdn.make_dims(spec.B, spec.T, spec.Hk, spec.Hv, spec.Dk, spec.Dv, spec.torch_dtype))
+        sets.append(d)
+    del inp
+
+    def step(d):
+        gdn.gdn2_chunk_fwd(d["q"], d["k"], d["v"], d["a"], d["A_log"], d["erase"], d["write"], d["S0"],
+                           out=d["out"], final_state=d["ST"], workspace=d["ws"])
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    units = spec.B * spec.T * spec.Hv
+    flop = gdn2_flop_per_token_head(spec.Dk, spec.Dv, spec.chunk) * units
+    tf = flop / (ms * 1e-3) / 1e12
+    log(f"[bench] gdn2 {ms * 1e3:.1f} us/step")
+    del sets
+    torch.cuda.empty_cache()
+    return dict(value=round(spec.B * spec.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
+                config=dict(workload="gdn2_t8192", B=spec.B, T=spec.T, Hk=spec.Hk, Hv=spec.Hv, Dk=spec.Dk,
+                            Dv=spec.Dv, chunk=spec.chunk, input_dtype="bf16", state_dtype="f32",
+                            matrix_operands="f16", accumulate="f32"),
+                path=dict(flop=flop, tflops=round(tf, 2), mfma_frac=round(tf / PEAK_MFMA_F16_TFLOPS, 4)),
+                scan_traffic=stored_traffic("scan_split_kernel_gdn2"))
+
+
 def cpu_baseline(pre, min_seconds=10.0):
     """The float64 oracle on this host's cores: the whole prefill workload,
     repeated until at least min_seconds of CPU time have passed."""
@@ -351,6 +414,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=3, help="buffer sets rotated in the timed region")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gdn2", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration)")
@@ -377,6 +441,7 @@ def main():
 
     pre = bench_prefill(args, torch, gdn, synth)
     dec = None if args.no_decode else bench_decode(args, torch, gdn, synth)
+    g2 = None if args.no_gdn2 else bench_gdn2(args, torch, gdn, synth)
     if args.calibration_copy:
         calibration_copy(torch)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre)
@@ -402,6 +467,7 @@ def main():
         "stages_us": {n: round(s * 1e3, 2) for n, s in zip(gdn.STAGE_NAMES, pre["stage_ms"])},
         "path": pre["path"],
         "decode": dec,
+        "gdn2": g2,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -124,6 +124,16 @@ def alloc_workspace(dims: gdn_dims, device="cuda") -> torch.Tensor:
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
+def gdn2_chunk_fwd_workspace_bytes(dims: gdn_dims) -> int:
+    return int(lib().gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def alloc_workspace_gdn2(dims: gdn_dims, device="cuda") -> torch.Tensor:
+    """A device buffer of the workspace size gdn2_chunk_fwd needs."""
+    n = gdn2_chunk_fwd_workspace_bytes(dims)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
 def gdn_chunk_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, scale: float = 1.0,
                   out=None, final_state=None, output_final_state: bool = True, workspace=None,
                   stream=None, stage_events: Optional[Sequence[int]] = None
@@ -191,8 +201,7 @@ def gdn2_chunk_fwd(q, k, v, a, A_log, erase, write, initial_state=None, *, scale
     if final_state is None and output_final_state:
         final_state = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
     if workspace is None:
-        nbytes = int(lib().gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims)))
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+        workspace = alloc_workspace_gdn2(dims, device=q.device)
     st = lib().gdn2_chunk_fwd(
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log), _ptr(erase), _ptr(write),
         _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace),
