@@ -22,10 +22,14 @@
 // reference token between the row and the column:
 //   - a 16x16 tile below the diagonal (rows I > columns J): reference 16I, one
 //     float16 matrix-core product of (k e^{G_ref - G}) and (e e^{G - G_ref});
-//   - a diagonal tile: three products with references at 4-token steps, each
-//     taking the columns of one 4-token sub-block and every later row;
-//   - entries inside a 4-token diagonal sub-block: elementwise in float32.
-// One work-group of 4 waves per (sequence, value head, chunk).
+//   - a diagonal tile: four dyadic levels (blocks of 16, 8, 4, 2 tokens); a
+//     pair i < t belongs to the level whose block has i in its first and t in
+//     its second half, with the first token of that half as reference: one
+//     product per level, each lane a row or a column of it;
+//   - the diagonal of A_qk carries no decay: q_t . k_t.
+// G is kept in log2 units so that every decay factor is one exp2.  One
+// work-group of 4 waves per (sequence, value head, chunk), 80 KB of LDS (two
+// work-groups per compute unit).
 #include "prefill_common.h"
 
 namespace gdn {
@@ -57,38 +61,65 @@ size_t gdn2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, G
 
 template <int DK>
 struct Cl2Cfg {
-    static constexpr int GS = DK + 4;  // float row stride of G in LDS (16-byte pad: rows land on distinct banks)
-    static constexpr int HS = DK + 8;  // half row stride of e, k, q in LDS
+    static constexpr int NKQ = DK / 32;                // 32-deep contraction steps over the key channels
     static constexpr int NP = 256 / DK, LEN = C / NP;  // prefix-sum parts per channel, tokens per part
+    // LDS: G (float) and e, k, q (float16) as [C][DK] row-major with the
+    // 16-byte pieces of each row XOR-swizzled by the row (no padding): 80 KB
+    // at DK = 128, so two work-groups share a compute unit.
+    static constexpr int LDS = C * DK * 4 + 3 * C * DK * 2;
+    static_assert(3 * C * DK * 2 >= 2 * 10 * 256 * 4, "M and A_qk tiles reuse the e/k/q space");
+    static_assert(C * DK * 4 >= 10 * 256 * 4, "the inverse's blocks reuse the G space");
 };
 
-__device__ __forceinline__ void ld8h(const _Float16 *p, float (&x)[8]) {
-    const h8 v = *reinterpret_cast<const h8 *>(p);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = (float)v[j];
+// element (r, c) of a swizzled [C][DK] float / float16 array
+template <int DK> __device__ __forceinline__ int gsw(int r, int c) {
+    return r * DK + ((((c >> 2) ^ r) & (DK / 4 - 1)) << 2) + (c & 3);
 }
-__device__ __forceinline__ void ld8f(const float *p, float (&x)[8]) {
-    const f4 a = *reinterpret_cast<const f4 *>(p), b = *reinterpret_cast<const f4 *>(p + 4);
+template <int DK> __device__ __forceinline__ int hsw(int r, int c) {
+    return r * DK + ((((c >> 3) ^ r) & (DK / 8 - 1)) << 3) + (c & 7);
+}
+// 8 consecutive channels c .. c+7 (c a multiple of 8) of row r
+template <int DK> __device__ __forceinline__ void ldg8(const float *G, int r, int c, float (&x)[8]) {
+    const f4 a = *reinterpret_cast<const f4 *>(G + gsw<DK>(r, c)), b = *reinterpret_cast<const f4 *>(G + gsw<DK>(r, c + 4));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         x[j] = a[j];
         x[4 + j] = b[j];
     }
 }
+template <int DK> __device__ __forceinline__ h8 ldh8(const _Float16 *X, int r, int c) {
+    return *reinterpret_cast<const h8 *>(X + hsw<DK>(r, c));
+}
+
+// x (float16) times f (float32) as a float16 operand.  Written as an fma with a
+// zero addend, which the compiler maps to v_fma_mix (the float16 input is
+// converted inside the instruction); kept out of inline assembly, whose
+// results the compiler's hazard checks do not see (a matrix-core product still
+// reading an accumulator register it would overwrite).
+__device__ __forceinline__ h8 mul_mix(h8 x, const float (&f)[8]) {
+    h8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (_Float16)__builtin_fmaf((float)x[j], f[j], 0.f);
+    return r;
+}
+// value of lane (4 (lane / 4) + P[lane % 4]) of x (a DPP quad permutation)
+template <int CTRL> __device__ __forceinline__ float quad_perm(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void chunk_local2_kernel(
+__global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
     int T, int Hk, int Hv, int NC, float scale, const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ v, const bf16_t *__restrict__ a, const bf16_t *__restrict__ erase,
     const bf16_t *__restrict__ write, const float *__restrict__ A_log, _Float16 *__restrict__ eimg,
     _Float16 *__restrict__ khimg, _Float16 *__restrict__ qimg, _Float16 *__restrict__ apair,
     _Float16 *__restrict__ qpair, float *__restrict__ gc, _Float16 *__restrict__ z) {
     typedef Cl2Cfg<DK> CF;
-    constexpr int GS = CF::GS, HS = CF::HS;
-    __shared__ __attribute__((aligned(16))) float Gl[C * GS];  // g, then G; the inverse's scratch at the end
-    __shared__ __attribute__((aligned(16))) _Float16 El[C * HS], Kl[C * HS], Ql[C * HS];
-    __shared__ __attribute__((aligned(16))) float Ms[10 * 256], Qs[10 * 256];  // lower 16x16 tiles of M, A_qk
-    __shared__ float tot[CF::NP][DK];
+    constexpr int NKQ = CF::NKQ;
+    __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
+    float *Gl = reinterpret_cast<float *>(smem);  // G in log2 units; later the inverse's blocks
+    _Float16 *El = reinterpret_cast<_Float16 *>(smem + C * DK * 4), *Kl = El + C * DK, *Ql = Kl + C * DK;
+    float *Ms = reinterpret_cast<float *>(El), *Qs = Ms + 10 * 256;  // lower 16x16 tiles of M, A_qk (after the tiles)
 
     const int u = blockIdx.x;
     const int n = u % NC, hv = (u / NC) % Hv, bb = u / (NC * Hv), hk = hv / (Hv / Hk);
@@ -96,72 +127,93 @@ __global__ __launch_bounds__(256) void chunk_local2_kernel(
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t vu = ((size_t)bb * Hv + hv) * NC + n;
+    constexpr float LOG2E = 1.4426950408889634f;
 
     // ---- 1. gates and key-side operands of the chunk into LDS (zero past T);
-    //         z = sigmoid(write) v to the workspace
+    //         z = sigmoid(write) v to the workspace.  Every load of the phase
+    //         is issued before any arithmetic; a thread sees the same 8
+    //         channels in each of its rows (256 is a multiple of DK / 8 and
+    //         DV / 8), so their decay rates exp(A_log) are loaded once.  g is
+    //         kept in log2 units (g log2 e) so that every decay is one exp2.
     constexpr int PK = C * (DK / 8) / 256, PV = C * (DV / 8) / 256;
+    const int c8k = (tid % (DK / 8)) * 8, c8v = (tid % (DV / 8)) * 8;
+    u16x8 rq[PK], rk[PK], ra[PK], re[PK], rv[PV], rw[PV];
+    f4 Alo, Ahi;
+    ld8(A_log, (size_t)hv * DK + c8k, Alo, Ahi);
 #pragma unroll
     for (int it = 0; it < PK; ++it) {
-        const int idx = tid + 256 * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8, t = t0 + r;
-        f4 q0 = {0, 0, 0, 0}, q1 = q0, k0 = q0, k1 = q0, a0 = q0, a1 = q0, e0 = q0, e1 = q0;
+        const int t = t0 + (tid + 256 * it) / (DK / 8);
+        rq[it] = rk[it] = ra[it] = re[it] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
         if (t < T) {
-            const size_t kq = (((size_t)bb * T + t) * Hk + hk) * DK + c8;
-            const size_t ka = (((size_t)bb * T + t) * Hv + hv) * DK + c8;
-            ld8(q, kq, q0, q1);
-            ld8(k, kq, k0, k1);
-            ld8(a, ka, a0, a1);
-            ld8(erase, ka, e0, e1);
+            const size_t kq = (((size_t)bb * T + t) * Hk + hk) * DK + c8k;
+            const size_t ka = (((size_t)bb * T + t) * Hv + hv) * DK + c8k;
+            rq[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(q) + kq);
+            rk[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(k) + kq);
+            ra[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(a) + ka);
+            re[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(erase) + ka);
         }
+    }
+#pragma unroll
+    for (int it = 0; it < PV; ++it) {
+        const int t = t0 + (tid + 256 * it) / (DV / 8);
+        rv[it] = rw[it] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (t < T) {
+            const size_t kv = (((size_t)bb * T + t) * Hv + hv) * DV + c8v;
+            rv[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(v) + kv);
+            rw[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(write) + kv);
+        }
+    }
+    float rate[8];  // exp(A_log) log2 e
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rate[j] = exp_fast(j < 4 ? Alo[j] : Ahi[j - 4]) * LOG2E;
+#pragma unroll
+    for (int it = 0; it < PK; ++it) {
+        const int r = (tid + 256 * it) / (DK / 8), t = t0 + r;
         float gv[8];
         h8 eh, kh, qh;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float av = j < 4 ? a0[j] : a1[j - 4], ev = j < 4 ? e0[j] : e1[j - 4];
-            const float kv = j < 4 ? k0[j] : k1[j - 4], qv = j < 4 ? q0[j] : q1[j - 4];
-            gv[j] = t < T ? -exp_fast(A_log[(size_t)hv * DK + c8 + j]) * softplus_fast(av) : 0.f;
-            eh[j] = (_Float16)(sigmoid_fast(ev) * kv);
+            const float kv = bf16_to_f32(rk[it][j]);
+            gv[j] = t < T ? -rate[j] * softplus_fast(bf16_to_f32(ra[it][j])) : 0.f;
+            eh[j] = (_Float16)(sigmoid_fast(bf16_to_f32(re[it][j])) * kv);
             kh[j] = (_Float16)kv;
-            qh[j] = (_Float16)(scale * qv);
+            qh[j] = (_Float16)(scale * bf16_to_f32(rq[it][j]));
         }
-        *reinterpret_cast<f4 *>(Gl + r * GS + c8) = f4{gv[0], gv[1], gv[2], gv[3]};
-        *reinterpret_cast<f4 *>(Gl + r * GS + c8 + 4) = f4{gv[4], gv[5], gv[6], gv[7]};
-        *reinterpret_cast<h8 *>(El + r * HS + c8) = eh;
-        *reinterpret_cast<h8 *>(Kl + r * HS + c8) = kh;
-        *reinterpret_cast<h8 *>(Ql + r * HS + c8) = qh;
+        *reinterpret_cast<f4 *>(Gl + gsw<DK>(r, c8k)) = f4{gv[0], gv[1], gv[2], gv[3]};
+        *reinterpret_cast<f4 *>(Gl + gsw<DK>(r, c8k + 4)) = f4{gv[4], gv[5], gv[6], gv[7]};
+        *reinterpret_cast<h8 *>(El + hsw<DK>(r, c8k)) = eh;
+        *reinterpret_cast<h8 *>(Kl + hsw<DK>(r, c8k)) = kh;
+        *reinterpret_cast<h8 *>(Ql + hsw<DK>(r, c8k)) = qh;
     }
 #pragma unroll
     for (int it = 0; it < PV; ++it) {
-        const int idx = tid + 256 * it, r = idx / (DV / 8), c8 = (idx % (DV / 8)) * 8, t = t0 + r;
+        const int t = t0 + (tid + 256 * it) / (DV / 8);
         if (t < T) {
-            const size_t kv = (((size_t)bb * T + t) * Hv + hv) * DV + c8;
-            f4 v0, v1, w0, w1;
-            ld8(v, kv, v0, v1);
-            ld8(write, kv, w0, w1);
             h8 zh;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                zh[j] = (_Float16)(sigmoid_fast(w0[j]) * v0[j]);
-                zh[4 + j] = (_Float16)(sigmoid_fast(w1[j]) * v1[j]);
-            }
-            *reinterpret_cast<h8 *>(z + kv) = zh;
+            for (int j = 0; j < 8; ++j) zh[j] = (_Float16)(sigmoid_fast(bf16_to_f32(rw[it][j])) * bf16_to_f32(rv[it][j]));
+            *reinterpret_cast<h8 *>(z + (((size_t)bb * T + t) * Hv + hv) * DV + c8v) = zh;
         }
     }
     __syncthreads();
 
-    // ---- 2. G: inclusive prefix of g over the chunk's tokens, per channel
+    // ---- 2. G: inclusive prefix of g over the chunk's tokens, per channel, in
+    //         NP parts of LEN tokens; a part adds the local totals of the parts
+    //         before it (read from their last rows between two barriers)
     {
         const int c = tid % DK, part = tid / DK;
         float x[CF::LEN];
 #pragma unroll
-        for (int j = 0; j < CF::LEN; ++j) x[j] = Gl[(part * CF::LEN + j) * GS + c];
+        for (int j = 0; j < CF::LEN; ++j) x[j] = Gl[gsw<DK>(part * CF::LEN + j, c)];
 #pragma unroll
         for (int j = 1; j < CF::LEN; ++j) x[j] += x[j - 1];
-        tot[part][c] = x[CF::LEN - 1];
+        Gl[gsw<DK>(part * CF::LEN + CF::LEN - 1, c)] = x[CF::LEN - 1];
         __syncthreads();
         float off = 0.f;
-        for (int p = 0; p < part; ++p) off += tot[p][c];
+        for (int p = 0; p < part; ++p) off += Gl[gsw<DK>(p * CF::LEN + CF::LEN - 1, c)];
+        __syncthreads();
 #pragma unroll
-        for (int j = 0; j < CF::LEN; ++j) Gl[(part * CF::LEN + j) * GS + c] = x[j] + off;
+        for (int j = 0; j < CF::LEN; ++j) Gl[gsw<DK>(part * CF::LEN + j, c)] = x[j] + off;
     }
     __syncthreads();
 
@@ -176,14 +228,18 @@ __global__ __launch_bounds__(256) void chunk_local2_kernel(
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int c = lc + 16 * hh;
-            const f4 gt = *reinterpret_cast<const f4 *>(Gl + r * GS + c);
-            const f4 gC = *reinterpret_cast<const f4 *>(Gl + (C - 1) * GS + c);
+            const f4 gt = *reinterpret_cast<const f4 *>(Gl + gsw<DK>(r, c));
+            const f4 gC = *reinterpret_cast<const f4 *>(Gl + gsw<DK>(C - 1, c));
+            typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+            const h4v ev = *reinterpret_cast<const h4v *>(El + hsw<DK>(r, c));
+            const h4v kv = *reinterpret_cast<const h4v *>(Kl + hsw<DK>(r, c));
+            const h4v qv = *reinterpret_cast<const h4v *>(Ql + hsw<DK>(r, c));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float fe = exp_fast(gt[j]), fk = exp_fast(gC[j] - gt[j]);
-                eo[4 * hh + j] = (_Float16)((float)El[r * HS + c + j] * fe);
-                qo[4 * hh + j] = (_Float16)((float)Ql[r * HS + c + j] * fe);
-                ko[4 * hh + j] = (_Float16)((float)Kl[r * HS + c + j] * fk);
+                const float fe = __builtin_amdgcn_exp2f(gt[j]), fk = __builtin_amdgcn_exp2f(gC[j] - gt[j]);
+                eo[4 * hh + j] = (_Float16)((float)ev[j] * fe);
+                qo[4 * hh + j] = (_Float16)((float)qv[j] * fe);
+                ko[4 * hh + j] = (_Float16)((float)kv[j] * fk);
             }
         }
         const size_t o = vu * C * DK + img_index<false>(r, DK, P * 8);
@@ -191,119 +247,113 @@ __global__ __launch_bounds__(256) void chunk_local2_kernel(
         *reinterpret_cast<h8 *>(khimg + o) = ko;
         *reinterpret_cast<h8 *>(qimg + o) = qo;
     }
-    if (tid < DK) gc[vu * DK + tid] = exp_fast(Gl[(C - 1) * GS + tid]);
+    if (tid < DK) gc[vu * DK + tid] = __builtin_amdgcn_exp2f(Gl[gsw<DK>(C - 1, tid)]);
 
     // ---- 4. tiles of M and A_qk below the diagonal (rows 16I, columns 16J,
     //         I > J): reference token 16I.  A = k e^{G_ref - G} (column rows),
     //         B = e e^{G - G_ref} or q e^{G - G_ref} (row rows): the accumulator
-    //         holds row 16I + m, columns 16J + 4g .. +3 (the operand layout the
-    //         inverse reads)
-    {
-        constexpr int TI[6] = {1, 2, 2, 3, 3, 3}, TJ[6] = {0, 0, 1, 0, 1, 2};
-        for (int p = w; p < 6; p += 4) {
-            const int I = TI[p], J = TJ[p], ref = 16 * I, tr = 16 * I + m, ir = 16 * J + m;
-            f4 accM = {0, 0, 0, 0}, accQ = accM;
+    //         holds row 16I + m, columns 16J + 4g .. +3.  Wave w takes tiles w
+    //         and w + 4; the results stay in registers until the e/k/q space is
+    //         free.
+    constexpr int TI[6] = {1, 2, 2, 3, 3, 3}, TJ[6] = {0, 0, 1, 0, 1, 2};
+    f4 oM[2], oQ[2];
 #pragma unroll
-            for (int kq = 0; kq < DK / 32; ++kq) {
+    for (int h = 0; h < 2; ++h) {
+        oM[h] = oQ[h] = f4{0, 0, 0, 0};
+        const int p = w + 4 * h;
+        if (p < 6) {
+            const int I = TI[p], J = TJ[p], ref = 16 * I, tr = 16 * I + m, ir = 16 * J + m;
+#pragma unroll
+            for (int kq = 0; kq < NKQ; ++kq) {
                 const int c = 32 * kq + 8 * g;
-                float gt[8], gr[8], gi[8], et[8], qt[8], ki[8];
-                ld8f(Gl + tr * GS + c, gt);
-                ld8f(Gl + ref * GS + c, gr);
-                ld8f(Gl + ir * GS + c, gi);
-                ld8h(El + tr * HS + c, et);
-                ld8h(Ql + tr * HS + c, qt);
-                ld8h(Kl + ir * HS + c, ki);
-                h8 le, lq, rk;
+                float gt[8], gr[8], gi[8], fl[8], fr[8];
+                ldg8<DK>(Gl, tr, c, gt);
+                ldg8<DK>(Gl, ref, c, gr);
+                ldg8<DK>(Gl, ir, c, gi);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float fl = exp_fast(gt[j] - gr[j]), fr = exp_fast(gr[j] - gi[j]);
-                    le[j] = (_Float16)(et[j] * fl);
-                    lq[j] = (_Float16)(qt[j] * fl);
-                    rk[j] = (_Float16)(ki[j] * fr);
+                    fl[j] = __builtin_amdgcn_exp2f(gt[j] - gr[j]);
+                    fr[j] = __builtin_amdgcn_exp2f(gr[j] - gi[j]);
                 }
-                accM = mfma_f16_k32(rk, le, accM);
-                accQ = mfma_f16_k32(rk, lq, accQ);
+                const h8 rk8 = mul_mix(ldh8<DK>(Kl, ir, c), fr);
+                oM[h] = mfma_f16_k32(rk8, mul_mix(ldh8<DK>(El, tr, c), fl), oM[h]);
+                oQ[h] = mfma_f16_k32(rk8, mul_mix(ldh8<DK>(Ql, tr, c), fl), oQ[h]);
             }
-            *reinterpret_cast<f4 *>(Ms + tri_index(I, J) * 256 + m * 16 + 4 * g) = accM;
-            *reinterpret_cast<f4 *>(Qs + tri_index(I, J) * 256 + m * 16 + 4 * g) = accQ;
         }
     }
 
-    // ---- 5. diagonal tile I = w
+    // ---- 5. diagonal tile I = w, token r0 + m in lane (g, m).  Every pair
+    //         i < t of the tile is split at the coarsest of four dyadic levels
+    //         where i and t fall into the two halves of one block (block sizes
+    //         16, 8, 4, 2): at that level the reference is the first token of
+    //         the block's second half, every lane is a column (first half,
+    //         factor e^{G_ref - G_i}) or a row (second half, e^{G_t - G_ref}),
+    //         both e^{-|G - G_ref|}, one exp2 per lane and channel and level.
+    //         One product per level and matrix; each level's accumulator keeps
+    //         only its own pairs.  The diagonal of A_qk (no decay) is q.k.
+    f4 dM = {0, 0, 0, 0}, dQ = {0, 0, 0, 0};
     {
-        const int I = w, r0 = 16 * I, t = r0 + m;
-        f4 accM = {0, 0, 0, 0}, accQ = accM;
-        // (a) columns in an earlier 4-token sub-block than the row: reference
-        //     token r0 + 4s takes the columns of sub-block s-1 and rows >= r0 + 4s
-        for (int s = 1; s < 4; ++s) {
-            const int ref = r0 + 4 * s;
-            const bool lrow = m >= 4 * s, rrow = m >= 4 * s - 4 && m < 4 * s;
+        const int r0 = 16 * w, t = r0 + m;
+        f4 aM[4], aQ[4];
 #pragma unroll
-            for (int kq = 0; kq < DK / 32; ++kq) {
-                const int c = 32 * kq + 8 * g;
-                float gt[8], gr[8], et[8], qt[8], kt[8];
-                ld8f(Gl + t * GS + c, gt);
-                ld8f(Gl + ref * GS + c, gr);
-                ld8h(El + t * HS + c, et);
-                ld8h(Ql + t * HS + c, qt);
-                ld8h(Kl + t * HS + c, kt);
-                h8 le, lq, rk;
+        for (int l = 0; l < 4; ++l) aM[l] = aQ[l] = f4{0, 0, 0, 0};
+        float dq = 0.f;
+#pragma unroll
+        for (int kq = 0; kq < NKQ; ++kq) {
+            const int c = 32 * kq + 8 * g;
+            float gt[8], g0[8], g1[8];
+            ldg8<DK>(Gl, t, c, gt);
+            ldg8<DK>(Gl, r0 + 8, c, g0);             // level 0: reference 8
+            ldg8<DK>(Gl, r0 + (m & 8) + 4, c, g1);   // level 1: reference 4 or 12
+            const h8 et = ldh8<DK>(El, t, c), qt = ldh8<DK>(Ql, t, c), kt = ldh8<DK>(Kl, t, c);
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+                dq = __builtin_amdgcn_fdot2(h2v{qt[j], qt[j + 1]}, h2v{kt[j], kt[j + 1]}, dq, false);
+            }
+#pragma unroll
+            for (int l = 0; l < 4; ++l) {
+                float f[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    // each factor is taken only where its exponent is <= 0
-                    const float fl = exp_fast(fminf(gt[j] - gr[j], 0.f)), fr = exp_fast(fminf(gr[j] - gt[j], 0.f));
-                    le[j] = lrow ? (_Float16)(et[j] * fl) : (_Float16)0.f;
-                    lq[j] = lrow ? (_Float16)(qt[j] * fl) : (_Float16)0.f;
-                    rk[j] = rrow ? (_Float16)(kt[j] * fr) : (_Float16)0.f;
+                    // level 2: reference lane 2 of the quad; level 3: lane 1 or 3
+                    const float gr = l == 0 ? g0[j] : l == 1 ? g1[j] : l == 2 ? quad_perm<0xAA>(gt[j]) : quad_perm<0xF5>(gt[j]);
+                    f[j] = __builtin_amdgcn_exp2f(-fabsf(gt[j] - gr));
                 }
-                accM = mfma_f16_k32(rk, le, accM);
-                accQ = mfma_f16_k32(rk, lq, accQ);
+                const h8 A = mul_mix(kt, f);
+                aM[l] = mfma_f16_k32(A, mul_mix(et, f), aM[l]);
+                aQ[l] = mfma_f16_k32(A, mul_mix(qt, f), aQ[l]);
             }
         }
-        // (b) columns in the row's own 4-token sub-block, elementwise in
-        //     float32: lane group g sums a quarter of the channels, then the
-        //     four groups are added across lanes
-        const int base = r0 + 4 * (m / 4);
-        float pm[4] = {0, 0, 0, 0}, pq[4] = {0, 0, 0, 0};
-        constexpr int NCH = DK / 4;
-        for (int cc = 0; cc < NCH; cc += 8) {
-            const int c = g * NCH + cc;
-            float gt[8], et[8], qt[8];
-            ld8f(Gl + t * GS + c, gt);
-            ld8h(El + t * HS + c, et);
-            ld8h(Ql + t * HS + c, qt);
+        // lane holds pairs (i = 4g + s, t = m)
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            const int b = 16 >> l, hb = b >> 1;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int i = base + s;
-                float gi[8], ki[8];
-                ld8f(Gl + i * GS + c, gi);
-                ld8h(Kl + i * HS + c, ki);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float f = exp_fast(fminf(gt[j] - gi[j], 0.f)) * ki[j];  // columns past the row are dropped below
-                    pm[s] += et[j] * f;
-                    pq[s] += qt[j] * f;
-                }
+                const int i = 4 * g + s;
+                const bool mine = (i / b == m / b) && (i % b < hb) && (m % b >= hb);
+                dM[s] += mine ? aM[l][s] : 0.f;
+                dQ[s] += mine ? aQ[l][s] : 0.f;
             }
         }
+        dq += __shfl_xor(dq, 16, 64);
+        dq += __shfl_xor(dq, 32, 64);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            pm[s] += __shfl_xor(pm[s], 16, 64);
-            pm[s] += __shfl_xor(pm[s], 32, 64);
-            pq[s] += __shfl_xor(pq[s], 16, 64);
-            pq[s] += __shfl_xor(pq[s], 32, 64);
-        }
-        if (g == m / 4) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int i = base + s;
-                accM[s] += i < t ? pm[s] : 0.f;
-                accQ[s] += i <= t ? pq[s] : 0.f;
-            }
-        }
-        *reinterpret_cast<f4 *>(Ms + tri_index(I, I) * 256 + m * 16 + 4 * g) = accM;
-        *reinterpret_cast<f4 *>(Qs + tri_index(I, I) * 256 + m * 16 + 4 * g) = accQ;
+        for (int s = 0; s < 4; ++s)
+            if (4 * g + s == m) dQ[s] += dq;
     }
+    __syncthreads();  // G, e, k, q are dead: the tiles take their space
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int p = w + 4 * h;
+        if (p < 6) {
+            *reinterpret_cast<f4 *>(Ms + tri_index(TI[p], TJ[p]) * 256 + m * 16 + 4 * g) = oM[h];
+            *reinterpret_cast<f4 *>(Qs + tri_index(TI[p], TJ[p]) * 256 + m * 16 + 4 * g) = oQ[h];
+        }
+    }
+    *reinterpret_cast<f4 *>(Ms + tri_index(w, w) * 256 + m * 16 + 4 * g) = dM;
+    *reinterpret_cast<f4 *>(Qs + tri_index(w, w) * 256 + m * 16 + 4 * g) = dQ;
     __syncthreads();
     if (w != 0) return;
 
