@@ -59,15 +59,17 @@ def scan_flop_per_token_head(dk, dv, C):
     return 2 * (3 * dk * dv + C * dv // 2 + C * dv // 2)
 
 
-# Gated DeltaNet-2 (channel-wise decay): the chunk-local products are per value head.
-#   whole prefill:  3 dk dv + C (dk + dv)   MAC  (M and A_qk: C dk / 2 each; A R', A_qk A R': C dv / 2 each)
-#   state scan:     3 dk dv + C dv          MAC
+# Gated DeltaNet-2 (channel-wise decay): no sharing of the chunk-local products
+# across value heads: 3 dk dv + C (dk + (dk+dv)/2 + dv/2) MAC per (token, value head)
+# (= 139,264 flop at d = 128, C = 64).  Its minimum traffic: q, k, v, the three
+# gate-logit tensors and the output once each, plus the state(s).
 def gdn2_flop_per_token_head(dk, dv, C):
-    return 2 * (3 * dk * dv + C * (dk + dv))
+    return 2 * (3 * dk * dv + C * (dk + (dk + dv) // 2 + dv // 2))
 
 
-def gdn2_scan_flop_per_token_head(dk, dv, C):
-    return 2 * (3 * dk * dv + C * dv)
+def gdn2_bytes(B, T, Hk, Hv, Dk, Dv, es, init_state):
+    return (2 * B * T * Hk * Dk * es + 2 * B * T * Hv * Dv * es + 2 * B * T * Hv * Dk * es
+            + B * T * Hv * Dv * es + Hv * Dk * 4 + (2 if init_state else 1) * B * Hv * Dk * Dv * 4)
 
 
 def prefill_bytes(B, T, Hk, Hv, Dk, Dv, es, init_state):
@@ -373,7 +375,9 @@ def bench_gdn2(args, torch, gdn, synth):
     ms = start.elapsed_time(stop) / args.steps
     units = spec.B * spec.T * spec.Hv
     flop = gdn2_flop_per_token_head(spec.Dk, spec.Dv, spec.chunk) * units
+    nbytes = gdn2_bytes(spec.B, spec.T, spec.Hk, spec.Hv, spec.Dk, spec.Dv, 2, spec.init_state)
     tf = flop / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] gdn2 {ms * 1e3:.1f} us/step")
     del sets
     torch.cuda.empty_cache()
@@ -381,8 +385,13 @@ def bench_gdn2(args, torch, gdn, synth):
                 config=dict(workload="gdn2_t8192", B=spec.B, T=spec.T, Hk=spec.Hk, Hv=spec.Hv, Dk=spec.Dk,
                             Dv=spec.Dv, chunk=spec.chunk, input_dtype="bf16", state_dtype="f32",
                             matrix_operands="f16", accumulate="f32"),
-                path=dict(flop=flop, tflops=round(tf, 2), mfma_frac=round(tf / PEAK_MFMA_F16_TFLOPS, 4)),
-                scan_traffic=stored_traffic("scan_split_kernel_gdn2"))
+                roofline=dict(kernel="whole step (chunk_local2_kernel + scan_split_kernel<G2>)", bound="hbm",
+                              achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(gbs / PEAK_HBM_GBS, 4), bytes_per_step=nbytes,
+                              traffic=(None if stored_traffic("chunk_local2_kernel") is None
+                                       or stored_traffic("scan_split_kernel_gdn2") is None else
+                                       stored_traffic("chunk_local2_kernel") + stored_traffic("scan_split_kernel_gdn2"))),
+                path=dict(flop=flop, tflops=round(tf, 2), mfma_frac=round(tf / PEAK_MFMA_F16_TFLOPS, 4)))
 
 
 def cpu_baseline(pre, min_seconds=10.0):

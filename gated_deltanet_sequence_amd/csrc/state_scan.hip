@@ -467,6 +467,35 @@ struct SplitLoader {
         for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(ra, base + CF::S_A + u * 1024, fo + u * 1024);
         if (lane < CF::STK_BYTES / 16) copy(G2 ? rgc : rtk, base + CF::S_TK, n * CF::STK_BYTES);
     }
+    // the channel-wise decay's state-wave inputs in two portions by the time
+    // the state waves read them: "early" (the Et image, Z, A; read one chunk
+    // ahead, during the previous chunk's state update) and "late" (the Kh
+    // image and e^{G_C}; read during the chunk's own phases A and B)
+    static constexpr int EARLY_LOADS = CF::IMG_UNITS + CF::TILE_UNITS + CF::FRAG_UNITS,
+                         LATE_LOADS = CF::IMG_UNITS + 1;
+    __device__ __forceinline__ void stage_early(char *smem, int n, int buf) const {
+        char *base = smem + CF::OFF_S + buf * CF::S_BUF;
+        const int io = n * CF::IMG_BYTES, fo = n * CF::FRAG_BYTES;
+#pragma unroll
+        for (int u = 0; u < CF::IMG_UNITS; ++u) copy(rk, base + CF::S_K + u * 1024, io + u * 1024);
+#pragma unroll
+        for (int u = 0; u < CF::TILE_UNITS; ++u) {
+            const int slot = u * 64 + lane;
+            const int row = slot / CF::VSPR;
+            const int piece = (slot % CF::VSPR) ^ ((row >> 2) & (CF::VSPR - 1));
+            const unsigned voff = ((unsigned)(n * C + row) * vrow + vcol + piece * CF::VEPS) * (unsigned)sizeof(TIn);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void_t *)(base + CF::S_V + u * 1024), 16, (int)voff, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(ra, base + CF::S_A + u * 1024, fo + u * 1024);
+    }
+    __device__ __forceinline__ void stage_late(char *smem, int n, int buf) const {
+        char *base = smem + CF::OFF_S + buf * CF::S_BUF;
+        const int io = n * CF::IMG_BYTES;
+#pragma unroll
+        for (int u = 0; u < CF::IMG_UNITS; ++u) copy(rkh, base + CF::S_KH + u * 1024, io + u * 1024);
+        if (lane < CF::STK_BYTES / 16) copy(rgc, base + CF::S_TK, n * CF::STK_BYTES);
+    }
     // output-wave inputs of chunk n: Q image, Ao fragments, gamma (OUT_LOADS loads)
     __device__ __forceinline__ void stage_out(char *smem, int n, int buf) const {
         char *base = smem + CF::OFF_O + buf * CF::O_BUF;
@@ -546,7 +575,49 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
             else if (K < 2 || k == 1) wait_vmcnt<L>();
             else wait_vmcnt<(K < 2 ? 0 : 2 * L)>();
         };
-        if (w == 5) {
+        if (G2 && w == 5) {
+            // Channel-wise decay, two state buffers: chunk m lives in buffer
+            // m % 2.  Its early portion is read during E(m-1) (from P(m-1) to
+            // F(m-1)), its late portion during A(m) and B(m) (from F(m-1) to
+            // P(m)).  So the early portion of chunk n+3 is issued after F(n),
+            // the late portion of chunk n+2 after P(n), each more than one
+            // chunk interval before it is needed.  Waits count loads issued
+            // after the awaited ones (in-order completion).
+            constexpr int EL = decltype(ld)::EARLY_LOADS, LL = decltype(ld)::LATE_LOADS;
+            auto wait_for = [](bool a_early, bool a_late) {  // loads issued after the awaited ones
+                if (a_early && a_late) wait_vmcnt<EL + LL>();
+                else if (a_early) wait_vmcnt<EL>();
+                else if (a_late) wait_vmcnt<LL>();
+                else wait_vmcnt<0>();
+            };
+            // at most 63 loads in flight (the width of the wave's counter):
+            // before issuing L more, wait until at most 63 - L are outstanding
+            auto early = [&](int m, int buf) { wait_vmcnt<63 - EL>(); ld.stage_early(smem, m, buf); };
+            auto late = [&](int m, int buf) { wait_vmcnt<63 - LL>(); ld.stage_late(smem, m, buf); };
+            if (NC > 0) {
+                early(0, 0);
+                late(0, 0);
+            }
+            if (NC > 1) {
+                early(1, 1);
+                late(1, 1);
+            }
+            wait_for(NC > 1, NC > 1);
+            bare_barrier();  // P(-1): chunk 0
+            wait_for(false, NC > 1);
+            bare_barrier();  // P(0): early portion of chunk 1
+            if (NC > 2) early(2, 0);  // chunk 0's early portion was read before P(0)
+            for (int n = 0; n < NC; ++n) {
+                if (n + 2 < NC) late(n + 2, n & 1);
+                if (n + 1 < NC) wait_for(n + 2 < NC, n + 2 < NC);  // late portion of chunk n+1
+                bare_barrier();  // F(n)
+                if (n + 3 < NC) early(n + 3, (n + 1) & 1);
+                if (n + 1 < NC) {
+                    wait_for(n + 3 < NC, n + 2 < NC);  // early portion of chunk n+2
+                    bare_barrier();  // P(n+1)
+                }
+            }
+        } else if (w == 5) {
             // state-wave inputs: chunk m is read from P(m-1) to P(m), buffer
             // m % NSB; chunk n+NSB is issued after P(n)
             const std::integral_constant<int, CF::STATE_LOADS> SL;
