@@ -85,6 +85,11 @@ def decode_bytes(B, Hk, Hv, Dk, Dv, es):
             + 2 * B * Hv * 4 + 2 * Hv * 4)
 
 
+def decode_gdn2_bytes(B, Hk, Hv, Dk, Dv, es):
+    return (2 * B * Hv * Dk * Dv * 4 + 2 * B * Hk * Dk * es + 3 * B * Hv * Dv * es
+            + 2 * B * Hv * Dk * es + Hv * Dk * 4)
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -342,6 +347,49 @@ def bench_decode(args, torch, gdn, synth):
     return res
 
 
+def bench_decode_gdn2(args, torch, gdn, synth):
+    """Gated DeltaNet-2 decode: B=256, 16/64 heads, d=128, bf16, 1 GiB state updated in place;
+    the 16 distinct seeded tokens are fed 4 times over (64 steps in the timed region)."""
+    spec = synth.WORKLOADS["decode_gdn2_b256"]
+    log(f"[bench] gdn2 decode workload {spec}")
+    inp = synth.make_inputs(spec)
+    per_step = [{k: inp[k][:, t].contiguous().cuda() for k in ("q", "k", "v", "a", "erase", "write")}
+                for t in range(spec.T)]
+    A_log = inp["A_log"].cuda()
+    state = inp["S0"].cuda()
+    del inp
+    out = torch.empty((spec.B, spec.Hv, spec.Dv), dtype=spec.torch_dtype, device="cuda")
+
+    def step(t):
+        x = per_step[t % spec.T]
+        gdn.gdn2_recurrent_step(x["q"], x["k"], x["v"], x["a"], A_log, x["erase"], x["write"], state, out=out)
+
+    for t in range(min(args.warmup, 8)):
+        step(t)
+    steps = 64
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for t in range(steps):
+        step(t)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    nbytes = decode_gdn2_bytes(spec.B, spec.Hk, spec.Hv, spec.Dk, spec.Dv, 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] gdn2 decode {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+    del per_step, state
+    torch.cuda.empty_cache()
+    return dict(value=round(gbs, 1), unit="GB/s", ms_per_step=round(ms, 5), steps=steps,
+                tokens_per_s=round(spec.B / (ms * 1e-3), 1),
+                config=dict(workload="decode_gdn2_b256", B=spec.B, Hk=spec.Hk, Hv=spec.Hv, Dk=spec.Dk,
+                            Dv=spec.Dv, input_dtype="bf16", state_dtype="f32", distinct_tokens=spec.T),
+                roofline=dict(kernel="decode_kernel<G2>", bound="hbm", achieved=round(gbs, 1),
+                              peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                              bytes_per_launch=nbytes, avg_launch_ms=round(ms, 5)))
+
+
 def bench_gdn2(args, torch, gdn, synth):
     """The Gated DeltaNet-2 prefill (B=1, T=8192, 16/64 heads, d=128, bf16): K steps of
     gdn2_chunk_fwd over rotated buffer sets, nothing else in the timed region."""
@@ -451,6 +499,7 @@ def main():
     pre = bench_prefill(args, torch, gdn, synth)
     dec = None if args.no_decode else bench_decode(args, torch, gdn, synth)
     g2 = None if args.no_gdn2 else bench_gdn2(args, torch, gdn, synth)
+    g2d = None if args.no_gdn2 or args.no_decode else bench_decode_gdn2(args, torch, gdn, synth)
     if args.calibration_copy:
         calibration_copy(torch)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre)
@@ -477,6 +526,7 @@ def main():
         "path": pre["path"],
         "decode": dec,
         "gdn2": g2,
+        "gdn2_decode": g2d,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

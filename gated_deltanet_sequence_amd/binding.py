@@ -59,6 +59,8 @@ def lib():
     L.gdn2_chunk_fwd.argtypes = [dims_p, vp, vp, vp, vp, fp, vp, vp, fp, vp, fp, vp, sz, vp]
     L.gdn_recurrent_step.restype = ctypes.c_int
     L.gdn_recurrent_step.argtypes = [dims_p, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
+    L.gdn2_recurrent_step.restype = ctypes.c_int
+    L.gdn2_recurrent_step.argtypes = [dims_p, vp, vp, vp, vp, fp, vp, vp, fp, vp, vp]
     L.gdn_status_str.restype = ctypes.c_char_p
     L.gdn_status_str.argtypes = [ctypes.c_int]
     L.gdn_last_error.restype = ctypes.c_char_p
@@ -225,6 +227,35 @@ def gdn_recurrent_step(q, k, v, a, b, A_log, dt_bias, state, *, scale: float = 1
         out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=q.device)
     st = lib().gdn_recurrent_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
                                   _ptr(A_log), _ptr(dt_bias), _ptr(state), _ptr(out), _stream(stream))
+    _check(st)
+    return out
+
+
+def gdn2_recurrent_step(q, k, v, a, A_log, erase, write, state, *, scale: float = 1.0, out=None,
+                        stream=None) -> torch.Tensor:
+    """One Gated DeltaNet-2 decode step, state updated in place.  q, k [B,Hk,Dk];
+    v [B,Hv,Dv]; a, erase [B,Hv,Dk] and write [B,Hv,Dv] in the dtype of q; A_log
+    [Hv,Dk] fp32; state [B,Hv,Dk,Dv] fp32.  Returns out [B,Hv,Dv]."""
+    B, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    dims = make_dims(B, 1, Hk, Hv, Dk, Dv, q.dtype, scale)
+    for name, t in (("A_log", A_log), ("state", state)):
+        _f32(t, name)
+    for name, t in (("k", k), ("v", v), ("a", a), ("erase", erase), ("write", write)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must have the dtype of q")
+    if tuple(a.shape) != (B, Hv, Dk) or tuple(erase.shape) != (B, Hv, Dk):
+        raise ValueError("a and erase must be [B,Hv,Dk]")
+    if tuple(write.shape) != (B, Hv, Dv):
+        raise ValueError("write must be [B,Hv,Dv]")
+    if tuple(A_log.shape) != (Hv, Dk):
+        raise ValueError("A_log must be [Hv,Dk]")
+    if tuple(state.shape) != (B, Hv, Dk, Dv):
+        raise ValueError("state must be [B,Hv,Dk,Dv]")
+    if out is None:
+        out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=q.device)
+    st = lib().gdn2_recurrent_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log),
+                                   _ptr(erase), _ptr(write), _ptr(state), _ptr(out), _stream(stream))
     _check(st)
     return out
 

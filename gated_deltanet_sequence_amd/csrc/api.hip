@@ -269,8 +269,43 @@ gdn_status gdn_recurrent_step(const gdn_dims *d, const void *q, const void *k, c
     gdn::DecodeArgs p;
     p.B = d->B; p.Hk = d->Hk; p.Hv = d->Hv; p.Dk = d->Dk; p.Dv = d->Dv;
     p.f32 = d->dtype == GDN_F32;
+    p.gdn2 = false;
     p.scale = d->scale;
-    p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.q = q; p.k = k; p.v = v; p.a = a; p.b = b; p.write = nullptr; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.state = state; p.out = out;
+    const hipError_t e = gdn::launch_decode(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn2_recurrent_step(const gdn_dims *d, const void *q, const void *k, const void *v,
+                               const void *a, const float *A_log, const void *erase, const void *write,
+                               float *state, void *out, void *stream) {
+    gdn_status st = check_dims(d, false);
+    if (st != GDN_OK) return st;
+    const size_t B = d->B, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv, es = esize(d);
+    const Span sq{"q", q, B * Hk * Dk * es}, sk{"k", k, B * Hk * Dk * es};
+    const Span sv{"v", v, B * Hv * Dv * es};
+    const Span sa{"a", a, B * Hv * Dk * es}, se{"erase", erase, B * Hv * Dk * es};
+    const Span swr{"write", write, B * Hv * Dv * es};
+    const Span sal{"A_log", A_log, Hv * Dk * 4};
+    const Span ss{"state", state, B * Hv * Dk * Dv * 4};
+    const Span so{"out", out, B * Hv * Dv * es};
+    for (const Span *s : {&sq, &sk, &sv, &sa, &se, &swr, &ss, &so})
+        if ((st = need(*s, 16)) != GDN_OK) return st;
+    if ((st = need(sal, 4)) != GDN_OK) return st;
+    for (const Span *s : {&sq, &sk, &sv, &sa, &se, &swr, &sal, &ss})
+        if (overlap(so, *s)) return fail(GDN_ERR_ALIAS, "out overlaps %s", s->name);
+    for (const Span *s : {&sq, &sk, &sv, &sa, &se, &swr, &sal})
+        if (overlap(ss, *s)) return fail(GDN_ERR_ALIAS, "state overlaps %s", s->name);
+    ok();
+    if (B == 0) return GDN_OK;
+    gdn::DecodeArgs p;
+    p.B = d->B; p.Hk = d->Hk; p.Hv = d->Hv; p.Dk = d->Dk; p.Dv = d->Dv;
+    p.f32 = d->dtype == GDN_F32;
+    p.gdn2 = true;
+    p.scale = d->scale;
+    p.q = q; p.k = k; p.v = v; p.a = a; p.b = erase; p.write = write; p.A_log = A_log; p.dt_bias = nullptr;
     p.state = state; p.out = out;
     const hipError_t e = gdn::launch_decode(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));

@@ -67,12 +67,16 @@ struct Gdn2Args {
 hipError_t launch_chunk_local2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s);
 hipError_t launch_state_scan2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s);
 
+// One recurrent step.  The scalar decay (gdn2 = false): a, b [B,H_v] float32,
+// A_log, dt_bias [H_v].  The channel-wise decay (gdn2 = true): a, b = erase
+// [B,H_v,d_k] and write [B,H_v,d_v] in the input type, A_log [H_v,d_k].
 struct DecodeArgs {
     int B, Hk, Hv, Dk, Dv;
-    bool f32;
+    bool f32, gdn2;
     float scale;
     const void *q, *k, *v;
-    const float *a, *b, *A_log, *dt_bias;
+    const void *a, *b, *write;
+    const float *A_log, *dt_bias;
     float *state;
     void *out;
 };

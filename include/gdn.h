@@ -152,6 +152,24 @@ gdn_status gdn_recurrent_step(const gdn_dims *d, const void *q, const void *k, c
                               const float *a, const float *b, const float *A_log,
                               const float *dt_bias, float *state, void *out, void *stream);
 
+/* One-token Gated DeltaNet-2 step on a cached state, updated in place
+ * (zhichai.net "Gated DeltaNet-2" digest, section "Gated Delta Rule-2": with
+ * D = exp(-exp(A_log[h]) * softplus(a)) per key channel, e = sigmoid(erase) . k,
+ * z = sigmoid(write) . v:  S <- diag(D) S + k (z - (diag(D) S)^T e)^T,
+ * out = scale S^T q after the update).  Equal erase and write logits per head
+ * give the KDA rule (channel-wise decay, one write strength).
+ *   q, k          [B,Hk,Dk] dtype
+ *   v             [B,Hv,Dv] dtype
+ *   a, erase      [B,Hv,Dk] dtype decay and erase-gate logits
+ *   write         [B,Hv,Dv] dtype write-gate logits
+ *   A_log         [Hv,Dk] float32
+ *   state         [B,Hv,Dk,Dv] float32, read and overwritten
+ *   out           [B,Hv,Dv] dtype (written); must not overlap state or inputs.
+ * d->T and d->chunk are ignored; dtype GDN_BF16 or GDN_F32. */
+gdn_status gdn2_recurrent_step(const gdn_dims *d, const void *q, const void *k, const void *v,
+                               const void *a, const float *A_log, const void *erase,
+                               const void *write, float *state, void *out, void *stream);
+
 /* Name of a status code (static string, never NULL). */
 const char *gdn_status_str(int status);
 

@@ -78,6 +78,9 @@ WORKLOADS: Dict[str, GDNSpec] = {
     # Gated DeltaNet-2 prefill, T=8192
     "gdn2_t8192": GDNSpec(B=1, T=8192, Hk=16, Hv=64, Dk=128, Dv=128, dtype="bf16", seed=104,
                           variant="gdn2"),
+    # Gated DeltaNet-2 decode: 256 sequences, 16 distinct one-token steps, state N(0, 0.02^2)
+    "decode_gdn2_b256": GDNSpec(B=256, T=16, Hk=16, Hv=64, Dk=128, Dv=128, dtype="bf16", seed=105,
+                                init_state=True, variant="gdn2"),
 }
 
 # Stress variants: slow decay keeps the carried state alive across chunks.

@@ -338,3 +338,52 @@ def test_gdn2_zero_batch_is_a_noop():
     a = gdn2_args(buf, d, q=None, k=None, v=None, a=None, erase=None, write=None, out=None, ST=None,
                   ws=None)
     assert call_gdn2(d, a) == OK
+
+
+# ---- Gated DeltaNet-2 decode step (gdn2_recurrent_step) ----
+
+def step2_args(buf, d, **override):
+    es = 4 if d.dtype == binding.GDN_F32 else 2
+    B, Hk, Hv, Dk, Dv = d.B, d.Hk, d.Hv, d.Dk, d.Dv
+    args = dict(q=buf(B * Hk * Dk * es), k=buf(B * Hk * Dk * es), v=buf(B * Hv * Dv * es),
+                a=buf(B * Hv * Dk * es), A_log=buf(Hv * Dk * 4), erase=buf(B * Hv * Dk * es),
+                write=buf(B * Hv * Dv * es), S=buf(B * Hv * Dk * Dv * 4), out=buf(B * Hv * Dv * es))
+    args.update(override)
+    return args
+
+
+def call_step2(d, a):
+    return binding.lib().gdn2_recurrent_step(ctypes.byref(d), a["q"], a["k"], a["v"], a["a"], a["A_log"],
+                                             a["erase"], a["write"], a["S"], a["out"], None)
+
+
+def test_gdn2_step_declared():
+    assert "gdn2_recurrent_step" in declared_functions()
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "a", "A_log", "erase", "write", "S", "out"])
+def test_gdn2_step_rejects_null(name):
+    buf = Buf()
+    d = dims(B=4)
+    assert call_step2(d, step2_args(buf, d, **{name: None})) == ERR_NULL
+
+
+def test_gdn2_step_validation():
+    buf = Buf()
+    d = dims(B=4)
+    assert call_step2(dims(B=4, Hv=5), step2_args(buf, d)) == ERR_SHAPE
+    assert call_step2(dims(B=4, Dv=32), step2_args(buf, d)) == ERR_UNSUPPORTED
+    for name in ("write", "erase", "S"):
+        a = step2_args(buf, d)
+        a[name] += 8
+        assert call_step2(d, a) == ERR_ALIGN, name
+    a = step2_args(buf, d)
+    a["out"] = a["write"]
+    assert call_step2(d, a) == ERR_ALIAS and "out overlaps write" in last_error()
+    a = step2_args(buf, d)
+    a["S"] = a["a"]
+    assert call_step2(d, a) == ERR_ALIAS
+    # fp32 is accepted by the step (validation passes up to the B = 0 no-op)
+    d32 = dims(B=0, dtype=binding.GDN_F32)
+    assert call_step2(d32, step2_args(buf, d32)) == OK
+    assert call_step2(dims(B=0), step2_args(buf, dims(B=0))) == OK
