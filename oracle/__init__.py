@@ -54,6 +54,7 @@ def _load():
     lib.oracle_gdn2_gates.argtypes = [ctypes.c_long, i, i, i, D, D, D, D, D, D, D]
     lib.oracle_gdn2_core.argtypes = [i] * 6 + [D] * 6 + [ctypes.c_double, D, D, D]
     lib.oracle_gdn2_fwd.argtypes = [i] * 6 + [D] * 7 + [ctypes.c_double, D, D, D]
+    lib.oracle_gated_rmsnorm.argtypes = [ctypes.c_long, i, D, D, D, ctypes.c_double, i, D]
     _lib = lib
     return lib
 
@@ -176,6 +177,21 @@ def gdn2_fwd(q, k, v, a, A_log, erase, write, S0=None, scale: float = 1.0):
     _load().oracle_gdn2_fwd(B, T, Hk, Hv, Dk, Dv, _p(q), _p(k), _p(v), _p(a), _p(A_log),
                             _p(erase), _p(write), float(scale), _p(S0), _p(out), _p(ST))
     return out, ST
+
+
+GATE_SILU, GATE_SIGMOID = 0, 1
+
+
+def gated_rmsnorm(x, z, weight, eps: float, gate: int = GATE_SILU):
+    """Gated RMS normalisation over the last axis: x / rms(x) * weight * act(z),
+    act = SiLU (GATE_SILU) or sigmoid (GATE_SIGMOID).  Returns float64."""
+    x, z, weight = f64(x), f64(z), f64(weight)
+    d = x.shape[-1]
+    if z.shape != x.shape or weight.shape != (d,):
+        raise ValueError("shape mismatch")
+    y = np.empty_like(x)
+    _load().oracle_gated_rmsnorm(x.size // d, d, _p(x), _p(z), _p(weight), float(eps), int(gate), _p(y))
+    return y
 
 
 def rel_l2(x, ref) -> float:

@@ -231,3 +231,29 @@ void oracle_gdn2_fwd(int B, int T, int Hk, int Hv, int Dk, int Dv,
     free(eb);
     free(wb);
 }
+
+/* Gated RMS normalisation of the core's output (rainlin-net.pages.dev
+ * "Qwen3.5", section "GDN详解": the module passes the read-out through a gated
+ * RMSNorm with the output gate z before the output projection; wanger-sjtu
+ * page, section "输出门控与 RMSNorm": the gate works like SwiGLU's; 10100.com
+ * pseudocode: a sigmoid output gate multiplied elementwise).  The pages give
+ * no formula; the reading taken here: per row (one token of one value head,
+ * d values)
+ *     y_c = x_c / sqrt(mean_c(x_c^2) + eps) * w_c * act(z_c)
+ * with act = SiLU (gate 0: z * sigmoid(z), the SwiGLU gate) or sigmoid
+ * (gate 1).  rows x d row-major in x, z, y; w has d entries. */
+void oracle_gated_rmsnorm(long rows, int d, const double *x, const double *z, const double *w,
+                          double eps, int gate, double *y) {
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        const double *xr = x + r * d, *zr = z + r * d;
+        double ss = 0.0;
+        for (int c = 0; c < d; ++c) ss += xr[c] * xr[c];
+        const double inv = 1.0 / sqrt(ss / d + eps);
+        for (int c = 0; c < d; ++c) {
+            const double s = oracle_sigmoid(zr[c]);
+            const double act = gate == 0 ? zr[c] * s : s;
+            y[r * d + c] = xr[c] * inv * w[c] * act;
+        }
+    }
+}

@@ -398,3 +398,44 @@ def test_pins_catch_planted_mistakes(oracle_lib):
     for kind in ["decay_after_erase", "sign", "readout_before_write"]:
         o, s = variant(kind)
         assert not np.allclose(o, o_bf, rtol=1e-6, atol=1e-9), kind
+
+
+# ---------------------------------------------------------------- gated RMSNorm epilogue
+
+def test_hand_worked_gated_rmsnorm(oracle_lib):
+    fx = json.load(open(os.path.join(GOLDEN, "hand_worked_gated_rmsnorm.json")))
+    i = fx["inputs"]
+    x, z, w = (np.array(i[n], dtype=np.float64) for n in ("x", "z", "w"))
+    for name, gate in (("sigmoid", oracle.GATE_SIGMOID), ("silu", oracle.GATE_SILU)):
+        y = oracle.gated_rmsnorm(x, z, w, i["eps"], gate)
+        np.testing.assert_allclose(y, np.array(fx["expected"][name]), rtol=0, atol=fx["tolerance_abs"])
+
+
+def test_gated_rmsnorm_against_library_rms_norm(oracle_lib):
+    """With the sigmoid gate saturated at 1 (z = 60) the epilogue is a plain RMSNorm:
+    torch.nn.functional.rms_norm in float64, with eps."""
+    import torch
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((37, 128)) * 3.0
+    w = rng.uniform(0.5, 1.5, size=128)
+    for eps in (1e-6, 0.3):
+        y = oracle.gated_rmsnorm(x, np.full_like(x, 60.0), w, eps, oracle.GATE_SIGMOID)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (128,), torch.from_numpy(w), eps).numpy()
+        np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_gated_rmsnorm_gate_and_scale_identities(oracle_lib):
+    """SiLU(z) = z sigmoid(z) relates the two gates; with eps = 0 the result does not depend
+    on the scale of x; a constant row normalises to its sign."""
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((9, 64))
+    z = rng.standard_normal((9, 64)) * 2
+    w = rng.uniform(-1, 1, size=64)
+    y_sig = oracle.gated_rmsnorm(x, z, w, 0.0, oracle.GATE_SIGMOID)
+    y_silu = oracle.gated_rmsnorm(x, z, w, 0.0, oracle.GATE_SILU)
+    np.testing.assert_allclose(y_silu, y_sig * z, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(37.5 * x, z, w, 0.0, oracle.GATE_SILU), y_silu,
+                               rtol=1e-13, atol=1e-14)
+    c = np.full((2, 64), -2.5)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(c, z[:2], w, 0.0, oracle.GATE_SIGMOID),
+                               -w * expit(z[:2]), rtol=1e-14, atol=1e-15)
