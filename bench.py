@@ -390,6 +390,42 @@ def bench_decode_gdn2(args, torch, gdn, synth):
                               bytes_per_launch=nbytes, avg_launch_ms=round(ms, 5)))
 
 
+def bench_epilogue(args, torch, gdn, synth):
+    """The gated RMS normalisation on the prefill output's shape (B=1, T=4096, 64 value heads,
+    d=128, bf16): read x and z, write y, over rotated buffer sets."""
+    shape = (1, 4096, 64, 128)
+    log(f"[bench] gated rmsnorm workload {shape} bf16")
+    x, z, w = synth.make_norm_inputs(shape, "bf16", seed=620)
+    sets = [dict(x=x.cuda(), z=z.cuda(), y=torch.empty(shape, dtype=torch.bfloat16, device="cuda"))
+            for _ in range(args.rotate)]
+    w = w.cuda()
+
+    def step(d):
+        gdn.gdn_gated_rmsnorm(d["x"], d["z"], w, eps=1e-6, gate="silu", out=d["y"])
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = 3 * x.numel() * 2 + 128 * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] gated rmsnorm {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+    del sets
+    torch.cuda.empty_cache()
+    return dict(value=round(gbs, 1), unit="GB/s", ms_per_step=round(ms, 5),
+                config=dict(workload="gated_rmsnorm_t4096", rows=4096 * 64, d=128, dtype="bf16", gate="silu"),
+                roofline=dict(kernel="gated_rmsnorm_kernel", bound="hbm", achieved=round(gbs, 1),
+                              peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                              bytes_per_launch=nbytes, avg_launch_ms=round(ms, 5)))
+
+
 def bench_gdn2(args, torch, gdn, synth):
     """The Gated DeltaNet-2 prefill (B=1, T=8192, 16/64 heads, d=128, bf16): K steps of
     gdn2_chunk_fwd over rotated buffer sets, nothing else in the timed region."""
@@ -500,6 +536,7 @@ def main():
     dec = None if args.no_decode else bench_decode(args, torch, gdn, synth)
     g2 = None if args.no_gdn2 else bench_gdn2(args, torch, gdn, synth)
     g2d = None if args.no_gdn2 or args.no_decode else bench_decode_gdn2(args, torch, gdn, synth)
+    epi = bench_epilogue(args, torch, gdn, synth)
     if args.calibration_copy:
         calibration_copy(torch)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre)
@@ -527,6 +564,7 @@ def main():
         "decode": dec,
         "gdn2": g2,
         "gdn2_decode": g2d,
+        "gated_rmsnorm": epi,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -61,6 +61,9 @@ def lib():
     L.gdn_recurrent_step.argtypes = [dims_p, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
     L.gdn2_recurrent_step.restype = ctypes.c_int
     L.gdn2_recurrent_step.argtypes = [dims_p, vp, vp, vp, vp, fp, vp, vp, fp, vp, vp]
+    L.gdn_gated_rmsnorm.restype = ctypes.c_int
+    L.gdn_gated_rmsnorm.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, fp,
+                                    ctypes.c_float, ctypes.c_int32, vp, vp]
     L.gdn_status_str.restype = ctypes.c_char_p
     L.gdn_status_str.argtypes = [ctypes.c_int]
     L.gdn_last_error.restype = ctypes.c_char_p
@@ -256,6 +259,33 @@ def gdn2_recurrent_step(q, k, v, a, A_log, erase, write, state, *, scale: float 
         out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=q.device)
     st = lib().gdn2_recurrent_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log),
                                    _ptr(erase), _ptr(write), _ptr(state), _ptr(out), _stream(stream))
+    _check(st)
+    return out
+
+
+GDN_GATE_SILU, GDN_GATE_SIGMOID = 0, 1
+
+
+def gdn_gated_rmsnorm(x, z, weight, *, eps: float = 1e-6, gate: str = "silu", out=None,
+                      stream=None) -> torch.Tensor:
+    """Gated RMS normalisation over the last axis (d = 64 or 128): x / rms(x) * weight *
+    act(z), act = SiLU ("silu") or sigmoid ("sigmoid").  x and z of one shape and dtype
+    (bf16 or fp32); weight [d] fp32.  out may be x (in place)."""
+    if z.shape != x.shape or z.dtype != x.dtype:
+        raise ValueError("z must have the shape and dtype of x")
+    d = x.shape[-1]
+    _f32(weight, "weight")
+    if tuple(weight.shape) != (d,):
+        raise ValueError("weight must be [d]")
+    gates = {"silu": GDN_GATE_SILU, "sigmoid": GDN_GATE_SIGMOID}
+    if gate not in gates:
+        raise ValueError(f"gate must be one of {sorted(gates)}")
+    if out is None:
+        out = torch.empty_like(x)
+    rows = x.numel() // d if d else 0
+    dt = GDN_F32 if x.dtype == torch.float32 else GDN_BF16 if x.dtype == torch.bfloat16 else -1
+    st = lib().gdn_gated_rmsnorm(rows, d, dt, _ptr(x), _ptr(z), _ptr(weight), float(eps), gates[gate],
+                                 _ptr(out), _stream(stream))
     _check(st)
     return out
 

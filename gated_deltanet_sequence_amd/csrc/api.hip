@@ -1,6 +1,7 @@
 // api.hip -- the C ABI of libgdn.so (declared in include/gdn.h): host-side
 // validation of every argument, then asynchronous launches on the caller's
 // stream.  Nothing is allocated and nothing is enqueued on a validation error.
+#include <cmath>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -308,6 +309,33 @@ gdn_status gdn2_recurrent_step(const gdn_dims *d, const void *q, const void *k, 
     p.q = q; p.k = k; p.v = v; p.a = a; p.b = erase; p.write = write; p.A_log = A_log; p.dt_bias = nullptr;
     p.state = state; p.out = out;
     const hipError_t e = gdn::launch_decode(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t d, int32_t dtype, const void *x, const void *z,
+                             const float *weight, float eps, int32_t gate, void *out, void *stream) {
+    if (rows < 0) return fail(GDN_ERR_SHAPE, "rows = %lld < 0", (long long)rows);
+    if (rows > gdn::gated_rmsnorm_max_rows()) return fail(GDN_ERR_UNSUPPORTED, "rows = %lld: too many", (long long)rows);
+    if (d != 64 && d != 128) return fail(GDN_ERR_UNSUPPORTED, "d = %d: supported 64, 128", d);
+    if (dtype != GDN_F32 && dtype != GDN_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "dtype = %d: supported GDN_F32, GDN_BF16", dtype);
+    if (gate != GDN_GATE_SILU && gate != GDN_GATE_SIGMOID)
+        return fail(GDN_ERR_UNSUPPORTED, "gate = %d: supported GDN_GATE_SILU, GDN_GATE_SIGMOID", gate);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(GDN_ERR_SHAPE, "eps must be finite and >= 0");
+    const size_t es = dtype == GDN_F32 ? 4 : 2, bytes = (size_t)rows * d * es;
+    const Span sx{"x", x, bytes}, sz{"z", z, bytes}, so{"out", out, bytes}, sw{"weight", weight, rows ? (size_t)d * 4 : 0};
+    gdn_status st;
+    for (const Span *s : {&sx, &sz, &so, &sw})
+        if ((st = need(*s, 16)) != GDN_OK) return st;
+    if (overlap(so, sx) && out != x) return fail(GDN_ERR_ALIAS, "out partly overlaps x");
+    for (const Span *s : {&sz, &sw})
+        if (overlap(so, *s)) return fail(GDN_ERR_ALIAS, "out overlaps %s", s->name);
+    ok();
+    gdn::NormArgs p;
+    p.rows = rows; p.d = d; p.f32 = dtype == GDN_F32; p.silu = gate == GDN_GATE_SILU; p.eps = eps;
+    p.x = x; p.z = z; p.w = weight; p.out = out;
+    const hipError_t e = gdn::launch_gated_rmsnorm(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
     return GDN_OK;
 }

@@ -83,4 +83,17 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t s);
 
+// Gated RMS normalisation of rows x d values (d = 64 or 128).
+struct NormArgs {
+    long long rows;
+    int d;
+    bool f32, silu;
+    float eps;
+    const void *x, *z;
+    const float *w;
+    void *out;
+};
+hipError_t launch_gated_rmsnorm(const NormArgs &p, hipStream_t s);
+long long gated_rmsnorm_max_rows();
+
 }  // namespace gdn

@@ -170,6 +170,23 @@ gdn_status gdn2_recurrent_step(const gdn_dims *d, const void *q, const void *k, 
                                const void *a, const float *A_log, const void *erase,
                                const void *write, float *state, void *out, void *stream);
 
+/* Gated RMS normalisation of the core's output, the step before the output
+ * projection (rainlin-net.pages.dev "Qwen3.5", section "GDN详解": the read-out
+ * passes through a gated RMSNorm with the output gate z; wanger-sjtu Qwen3.5
+ * GDN page, section "输出门控与 RMSNorm": the gate works like SwiGLU's;
+ * 10100.com pseudocode: a sigmoid output gate).  The pages give no formula;
+ * per row of d values (one token of one value head):
+ *     out = x / sqrt(mean(x^2) + eps) * weight * act(z),
+ * act = SiLU (z sigmoid(z), GDN_GATE_SILU) or sigmoid (GDN_GATE_SIGMOID).
+ *   x, z, out  [rows, d] dtype (e.g. the core output [B,T,Hv,Dv] viewed as
+ *              rows = B*T*Hv, d = Dv; z in the same layout)
+ *   weight     [d] float32
+ * d is 64 or 128; eps finite and >= 0.  out may be exactly x (in place) and
+ * must not overlap z or weight otherwise.  rows = 0 is a no-op. */
+typedef enum gdn_gate { GDN_GATE_SILU = 0, GDN_GATE_SIGMOID = 1 } gdn_gate;
+gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t d, int32_t dtype, const void *x, const void *z,
+                             const float *weight, float eps, int32_t gate, void *out, void *stream);
+
 /* Name of a status code (static string, never NULL). */
 const char *gdn_status_str(int status);
 

@@ -32,6 +32,7 @@ import torch
 
 # tensor ids of the per-tensor random streams
 TID_A_LOG, TID_DT_BIAS, TID_Q, TID_K, TID_V, TID_A, TID_B, TID_S0, TID_ERASE, TID_WRITE = range(10)
+TID_NORM_X, TID_NORM_Z, TID_NORM_W = 10, 11, 12
 
 _SLAB = 1 << 22  # values drawn per slab (bounds the float64 working set)
 
@@ -176,3 +177,15 @@ def head_slice(inp: Dict[str, Optional[torch.Tensor]], spec: GDNSpec, b: int, hv
         o["A_log"] = inp["A_log"][hv:hv + 1]
     o["S0"] = None if inp["S0"] is None else inp["S0"][b:b + 1, hv:hv + 1]
     return o
+
+
+def make_norm_inputs(shape, dtype: str, seed: int, x_sigma: float = 1.0):
+    """Inputs of the gated RMS normalisation: x ~ N(0, x_sigma^2) and the gate z ~ N(0, 1)
+    of ``shape`` (last axis = d) in ``dtype`` ("f32" or "bf16"), weight [d] ~ U(0.5, 1.5)
+    float32."""
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    x = _normal_rows(_rng(seed, TID_NORM_X), tuple(shape), False)
+    x *= np.float32(x_sigma)
+    z = _normal_rows(_rng(seed, TID_NORM_Z), tuple(shape), False)
+    w = _rng(seed, TID_NORM_W).uniform(0.5, 1.5, size=(shape[-1],)).astype(np.float32)
+    return _to_torch(x, dt), _to_torch(z, dt), torch.from_numpy(w)

@@ -387,3 +387,29 @@ def test_gdn2_step_validation():
     d32 = dims(B=0, dtype=binding.GDN_F32)
     assert call_step2(d32, step2_args(buf, d32)) == OK
     assert call_step2(dims(B=0), step2_args(buf, dims(B=0))) == OK
+
+
+# ---- gated RMS normalisation (gdn_gated_rmsnorm) ----
+
+def call_norm(rows, d, dtype, x, z, w, eps=1e-6, gate=0, out=None):
+    return binding.lib().gdn_gated_rmsnorm(rows, d, dtype, x, z, w, eps, gate, out, None)
+
+
+def test_gated_rmsnorm_validation():
+    buf = Buf()
+    rows, d = 10, 128
+    x, z, w, o = buf(rows * d * 2), buf(rows * d * 2), buf(d * 4), buf(rows * d * 2)
+    bf = binding.GDN_BF16
+    assert "gdn_gated_rmsnorm" in declared_functions()
+    assert call_norm(-1, d, bf, x, z, w, out=o) == ERR_SHAPE
+    assert call_norm(rows, 96, bf, x, z, w, out=o) == ERR_UNSUPPORTED
+    assert call_norm(rows, d, 5, x, z, w, out=o) == ERR_UNSUPPORTED
+    assert call_norm(rows, d, bf, x, z, w, gate=2, out=o) == ERR_UNSUPPORTED
+    assert call_norm(rows, d, bf, x, z, w, eps=-1.0, out=o) == ERR_SHAPE
+    assert call_norm(rows, d, bf, x, z, w, eps=float("inf"), out=o) == ERR_SHAPE
+    assert call_norm(rows, d, bf, None, z, w, out=o) == ERR_NULL
+    assert call_norm(rows, d, bf, x, z, None, out=o) == ERR_NULL
+    assert call_norm(rows, d, bf, x + 8, z, w, out=o) == ERR_ALIGN
+    assert call_norm(rows, d, bf, x, z, w, out=z) == ERR_ALIAS
+    assert call_norm(rows, d, bf, x, z, w, out=x + 16) == ERR_ALIAS and "partly" in last_error()
+    assert call_norm(0, d, bf, None, None, None, out=None) == OK
