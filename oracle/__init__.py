@@ -55,6 +55,7 @@ def _load():
     lib.oracle_gdn2_core.argtypes = [i] * 6 + [D] * 6 + [ctypes.c_double, D, D, D]
     lib.oracle_gdn2_fwd.argtypes = [i] * 6 + [D] * 7 + [ctypes.c_double, D, D, D]
     lib.oracle_gated_rmsnorm.argtypes = [ctypes.c_long, i, D, D, D, ctypes.c_double, i, D]
+    lib.oracle_causal_conv1d.argtypes = [i, i, i, i, D, D, D, D, i, D, D]
     _lib = lib
     return lib
 
@@ -192,6 +193,21 @@ def gated_rmsnorm(x, z, weight, eps: float, gate: int = GATE_SILU):
     y = np.empty_like(x)
     _load().oracle_gated_rmsnorm(x.size // d, d, _p(x), _p(z), _p(weight), float(eps), int(gate), _p(y))
     return y
+
+
+def causal_conv1d(x, weight, bias=None, state=None, silu: bool = True):
+    """Depthwise causal convolution over time (+ SiLU).  x [B,T,C]; weight [C,K]; bias [C]
+    or None; state [B,K-1,C] (the inputs before token 0) or None.  Returns (y [B,T,C],
+    state_out [B,K-1,C]) in float64."""
+    x, weight = f64(x), f64(weight)
+    bias, state = f64(bias), f64(state)
+    B, T, C = x.shape
+    K = weight.shape[1]
+    y = np.empty((B, T, C))
+    st = np.empty((B, K - 1, C))
+    _load().oracle_causal_conv1d(B, T, C, K, _p(x), _p(weight), _p(bias), _p(state), int(bool(silu)),
+                                 _p(y), _p(st))
+    return y, st
 
 
 def rel_l2(x, ref) -> float:

@@ -257,3 +257,44 @@ void oracle_gated_rmsnorm(long rows, int d, const double *x, const double *z, co
         }
     }
 }
+
+/* Depthwise causal convolution over time with an optional SiLU, the prologue
+ * that turns the mixed q|k|v projection into q, k, v (dingfen.github.io,
+ * section 10: x -> Linear -> CausalConv1D -> SiLU -> (q, k, v); 10100.com:
+ * kernel size 4; wanger-sjtu page: a depthwise causal conv over the mixed QKV
+ * channels, with the conv inputs cached for decode).  Per sequence b, channel
+ * c and token t (inputs before token 0 come from the cached state, or are 0):
+ *     y[b,t,c] = act(bias[c] + sum_{j<K} w[c][j] x[b, t-K+1+j, c])
+ * x, y [B][T][C]; w [C][K]; bias [C] or NULL; state [B][K-1][C] (the K-1
+ * inputs before token 0, oldest first) or NULL; state_out [B][K-1][C] (the
+ * last K-1 inputs, including older state when T < K-1) or NULL.
+ * silu: act(x) = x sigmoid(x), else the identity. */
+void oracle_causal_conv1d(int B, int T, int C, int K, const double *x, const double *w,
+                          const double *bias, const double *state, int silu, double *y,
+                          double *state_out) {
+#pragma omp parallel for schedule(static)
+    for (int b = 0; b < B; ++b) {
+        for (int c = 0; c < C; ++c) {
+            for (int t = 0; t < T; ++t) {
+                double acc = bias ? bias[c] : 0.0;
+                for (int j = 0; j < K; ++j) {
+                    const int s = t - K + 1 + j;  /* input token; s < 0 reads the state */
+                    double xv = 0.0;
+                    if (s >= 0) xv = x[((size_t)b * T + s) * C + c];
+                    else if (state) xv = state[((size_t)b * (K - 1) + (K - 1 + s)) * C + c];
+                    acc += w[(size_t)c * K + j] * xv;
+                }
+                y[((size_t)b * T + t) * C + c] = silu ? acc * oracle_sigmoid(acc) : acc;
+            }
+            if (state_out) {
+                for (int i = 0; i < K - 1; ++i) {
+                    const int s = T - (K - 1) + i;  /* token of state slot i */
+                    double xv = 0.0;
+                    if (s >= 0) xv = x[((size_t)b * T + s) * C + c];
+                    else if (state) xv = state[((size_t)b * (K - 1) + (K - 1 + s)) * C + c];
+                    state_out[((size_t)b * (K - 1) + i) * C + c] = xv;
+                }
+            }
+        }
+    }
+}

@@ -439,3 +439,53 @@ def test_gated_rmsnorm_gate_and_scale_identities(oracle_lib):
     c = np.full((2, 64), -2.5)
     np.testing.assert_allclose(oracle.gated_rmsnorm(c, z[:2], w, 0.0, oracle.GATE_SIGMOID),
                                -w * expit(z[:2]), rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- causal conv1d prologue
+
+def test_hand_worked_causal_conv1d(oracle_lib):
+    fx = json.load(open(os.path.join(GOLDEN, "hand_worked_causal_conv1d.json")))
+    i = {k: np.array(v, dtype=np.float64) for k, v in fx["inputs"].items()}
+    y, st = oracle.causal_conv1d(i["x"], i["w"], state=i["state"], silu=False)
+    tol = fx["tolerance_abs"]
+    np.testing.assert_allclose(y, np.array(fx["expected"]["y"]), rtol=0, atol=tol)
+    np.testing.assert_allclose(st, np.array(fx["expected"]["state_out"]), rtol=0, atol=tol)
+    y, _ = oracle.causal_conv1d(i["x"], i["w"], state=i["state"], silu=True)
+    assert abs(y[0, 0, 0] - fx["expected"]["y0_silu"]) <= tol
+
+
+def test_causal_conv1d_against_library_conv(oracle_lib):
+    """A zero state is torch's depthwise conv1d (groups = channels) with K-1 zeros of left
+    padding, then SiLU; a bias adds per channel."""
+    import torch
+    rng = np.random.default_rng(51)
+    B, T, C, K = 2, 37, 24, 4
+    x = rng.standard_normal((B, T, C))
+    w = rng.standard_normal((C, K))
+    bias = rng.standard_normal(C)
+    y, st = oracle.causal_conv1d(x, w, bias=bias, silu=True)
+    xt = torch.from_numpy(x).transpose(1, 2)                      # [B, C, T]
+    ref = torch.nn.functional.conv1d(xt, torch.from_numpy(w)[:, None, :], torch.from_numpy(bias),
+                                     padding=K - 1, groups=C)[..., :T]
+    ref = torch.nn.functional.silu(ref).transpose(1, 2).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(st, x[:, T - (K - 1):], rtol=0, atol=0)
+
+
+def test_causal_conv1d_split_invariance(oracle_lib):
+    """Running T tokens in pieces, each starting from the previous piece's state (including
+    pieces shorter than K-1 and single-token steps), equals one pass."""
+    rng = np.random.default_rng(52)
+    B, T, C, K = 2, 23, 16, 4
+    x = rng.standard_normal((B, T, C))
+    w = rng.standard_normal((C, K))
+    s0 = rng.standard_normal((B, K - 1, C))
+    y_all, st_all = oracle.causal_conv1d(x, w, state=s0)
+    st, ys, t = s0, [], 0
+    for n in (1, 2, 1, 7, 1, 1, 10):
+        y, st = oracle.causal_conv1d(x[:, t:t + n], w, state=st)
+        ys.append(y)
+        t += n
+    assert t == T
+    np.testing.assert_allclose(np.concatenate(ys, axis=1), y_all, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(st, st_all, rtol=0, atol=0)
