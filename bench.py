@@ -426,6 +426,46 @@ def bench_epilogue(args, torch, gdn, synth):
                               bytes_per_launch=nbytes, avg_launch_ms=round(ms, 5)))
 
 
+def bench_prologue(args, torch, gdn, synth):
+    """The causal conv1d + SiLU prologue on the prefill's shape: x [1, 4096, 12288] bf16
+    (q | k | v channels of 16/64 heads, d=128) -> q, k, v, plus the new conv state."""
+    B, T, Hk, Hv, D = 1, 4096, 16, 64, 128
+    C = 2 * Hk * D + Hv * D
+    log(f"[bench] causal conv1d workload B={B} T={T} C={C} bf16")
+    x, w, b, s0 = synth.make_conv_inputs(B, T, C, "bf16", seed=630)
+    w, b = w.cuda(), b.cuda()
+    mk = lambda H: torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    sets = [dict(x=x.cuda(), s=s0.cuda(), so=torch.empty_like(s0, device="cuda"), q=mk(Hk), k=mk(Hk), v=mk(Hv))
+            for _ in range(args.rotate)]
+
+    def step(d):
+        gdn.gdn_causal_conv1d(d["x"], w, b, d["s"], Hk=Hk, Hv=Hv, Dk=D, Dv=D, conv_state_out=d["so"],
+                              q=d["q"], k=d["k"], v=d["v"])
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = 2 * B * T * C * 2 + 2 * B * 3 * C * 2 + C * 5 * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] causal conv1d {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+    del sets
+    torch.cuda.empty_cache()
+    return dict(value=round(gbs, 1), unit="GB/s", ms_per_step=round(ms, 5),
+                config=dict(workload="causal_conv1d_t4096", B=B, T=T, C=C, kernel_size=4, dtype="bf16",
+                            activation="silu"),
+                roofline=dict(kernel="causal_conv1d_kernel", bound="hbm", achieved=round(gbs, 1),
+                              peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                              bytes_per_launch=nbytes, avg_launch_ms=round(ms, 5)))
+
+
 def bench_gdn2(args, torch, gdn, synth):
     """The Gated DeltaNet-2 prefill (B=1, T=8192, 16/64 heads, d=128, bf16): K steps of
     gdn2_chunk_fwd over rotated buffer sets, nothing else in the timed region."""
@@ -537,6 +577,7 @@ def main():
     g2 = None if args.no_gdn2 else bench_gdn2(args, torch, gdn, synth)
     g2d = None if args.no_gdn2 or args.no_decode else bench_decode_gdn2(args, torch, gdn, synth)
     epi = bench_epilogue(args, torch, gdn, synth)
+    pro = bench_prologue(args, torch, gdn, synth)
     if args.calibration_copy:
         calibration_copy(torch)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pre)
@@ -565,6 +606,7 @@ def main():
         "gdn2": g2,
         "gdn2_decode": g2d,
         "gated_rmsnorm": epi,
+        "causal_conv1d": pro,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

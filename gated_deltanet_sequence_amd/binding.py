@@ -64,6 +64,8 @@ def lib():
     L.gdn_gated_rmsnorm.restype = ctypes.c_int
     L.gdn_gated_rmsnorm.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp, fp,
                                     ctypes.c_float, ctypes.c_int32, vp, vp]
+    L.gdn_causal_conv1d.restype = ctypes.c_int
+    L.gdn_causal_conv1d.argtypes = [dims_p, ctypes.c_int32, vp, fp, fp, vp, vp, ctypes.c_int32, vp, vp, vp, vp]
     L.gdn_status_str.restype = ctypes.c_char_p
     L.gdn_status_str.argtypes = [ctypes.c_int]
     L.gdn_last_error.restype = ctypes.c_char_p
@@ -288,6 +290,44 @@ def gdn_gated_rmsnorm(x, z, weight, *, eps: float = 1e-6, gate: str = "silu", ou
                                  _ptr(out), _stream(stream))
     _check(st)
     return out
+
+
+GDN_ACT_NONE, GDN_ACT_SILU = 0, 1
+
+
+def gdn_causal_conv1d(x, weight, bias=None, conv_state=None, *, Hk: int, Hv: int, Dk: int, Dv: int,
+                      activation: str = "silu", conv_state_out=None, output_conv_state: bool = True,
+                      q=None, k=None, v=None, stream=None):
+    """Depthwise causal conv1d (kernel 4) + SiLU over the mixed projection x [B,T,C]
+    (C = 2 Hk Dk + Hv Dv, channels q | k | v), split into q, k [B,T,Hk,Dk] and v [B,T,Hv,Dv].
+    weight [C,4] fp32, bias [C] fp32 or None, conv_state [B,3,C] (x dtype) or None.
+    Returns (q, k, v, conv_state_out or None); conv_state_out may be conv_state."""
+    B, T, C = x.shape
+    K = weight.shape[1] if weight.dim() == 2 else 0
+    if C != 2 * Hk * Dk + Hv * Dv:
+        raise ValueError("x's last axis must be 2 Hk Dk + Hv Dv")
+    _f32(weight, "weight")
+    _f32(bias, "bias")
+    if tuple(weight.shape) != (C, K) or (bias is not None and tuple(bias.shape) != (C,)):
+        raise ValueError("weight must be [C, K] and bias [C]")
+    for name, t in (("conv_state", conv_state), ("conv_state_out", conv_state_out)):
+        if t is not None and (tuple(t.shape) != (B, K - 1, C) or t.dtype != x.dtype):
+            raise ValueError(f"{name} must be [B, K-1, C] in the dtype of x")
+    acts = {"silu": GDN_ACT_SILU, "none": GDN_ACT_NONE}
+    if activation not in acts:
+        raise ValueError(f"activation must be one of {sorted(acts)}")
+    dims = make_dims(B, T, Hk, Hv, Dk, Dv, x.dtype)
+    mk = lambda H, D: torch.empty((B, T, H, D), dtype=x.dtype, device=x.device)
+    q = mk(Hk, Dk) if q is None else q
+    k = mk(Hk, Dk) if k is None else k
+    v = mk(Hv, Dv) if v is None else v
+    if conv_state_out is None and output_conv_state:
+        conv_state_out = torch.empty((B, K - 1, C), dtype=x.dtype, device=x.device)
+    st = lib().gdn_causal_conv1d(ctypes.byref(dims), K, _ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state),
+                                 _ptr(conv_state_out), acts[activation], _ptr(q), _ptr(k), _ptr(v),
+                                 _stream(stream))
+    _check(st)
+    return q, k, v, conv_state_out
 
 
 class StageEvents:

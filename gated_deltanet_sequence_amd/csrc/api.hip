@@ -340,6 +340,50 @@ gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t d, int32_t dtype, const void 
     return GDN_OK;
 }
 
+gdn_status gdn_causal_conv1d(const gdn_dims *d, int32_t kernel_size, const void *x, const float *weight,
+                             const float *bias, const void *conv_state, void *conv_state_out,
+                             int32_t activation, void *q, void *k, void *v, void *stream) {
+    gdn_status st = check_dims(d, false);
+    if (st != GDN_OK) return st;
+    if (d->T < 0) return fail(GDN_ERR_SHAPE, "T = %d < 0", d->T);
+    if (kernel_size != 4) return fail(GDN_ERR_UNSUPPORTED, "kernel_size = %d: supported 4", kernel_size);
+    if (activation != GDN_ACT_NONE && activation != GDN_ACT_SILU)
+        return fail(GDN_ERR_UNSUPPORTED, "activation = %d: supported GDN_ACT_NONE, GDN_ACT_SILU", activation);
+    if (d->B > 65535 || (long long)d->T > 65535LL * gdn::conv_tokens_per_thread())
+        return fail(GDN_ERR_UNSUPPORTED, "B = %d, T = %d: at most 65535 sequences and %lld tokens", d->B, d->T,
+                    65535LL * gdn::conv_tokens_per_thread());
+    const size_t B = d->B, T = d->T, K = kernel_size, es = esize(d);
+    const size_t qk = (size_t)d->Hk * d->Dk, vw = (size_t)d->Hv * d->Dv, C = 2 * qk + vw;
+    const Span sx{"x", x, B * T * C * es}, sw{"weight", weight, C * K * 4}, sb{"bias", bias, bias ? C * 4 : 0};
+    const Span ss{"conv_state", conv_state, conv_state ? B * (K - 1) * C * es : 0};
+    const Span so{"conv_state_out", conv_state_out, conv_state_out ? B * (K - 1) * C * es : 0};
+    const Span sq{"q", q, B * T * qk * es}, sk{"k", k, B * T * qk * es}, sv{"v", v, B * T * vw * es};
+    for (const Span *s : {&sx, &sq, &sk, &sv, &ss, &so, &sb})
+        if ((st = need(*s, 16)) != GDN_OK) return st;
+    if (B && (st = need(sw, 16)) != GDN_OK) return st;
+    const Span *outs[] = {&sq, &sk, &sv, &so};
+    for (const Span *o : outs) {
+        for (const Span *s : {&sx, &sw, &sb})
+            if (overlap(*o, *s)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", o->name, s->name);
+        for (const Span *o2 : outs)
+            if (o2 != o && overlap(*o, *o2)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", o->name, o2->name);
+    }
+    for (const Span *o : {&sq, &sk, &sv})
+        if (overlap(*o, ss)) return fail(GDN_ERR_ALIAS, "%s overlaps conv_state", o->name);
+    if (overlap(so, ss) && conv_state_out != conv_state)
+        return fail(GDN_ERR_ALIAS, "conv_state_out partly overlaps conv_state");
+    ok();
+    if (B == 0) return GDN_OK;
+    gdn::ConvArgs p;
+    p.B = d->B; p.T = d->T; p.C = (int)C; p.qk = (int)qk; p.K = kernel_size;
+    p.f32 = d->dtype == GDN_F32; p.silu = activation == GDN_ACT_SILU;
+    p.x = x; p.w = weight; p.bias = bias; p.state = conv_state; p.state_out = conv_state_out;
+    p.q = q; p.k = k; p.v = v;
+    const hipError_t e = gdn::launch_causal_conv1d(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 gdn_status gdn_events_create(int n, void **events) {
     if (n < 0) return fail(GDN_ERR_SHAPE, "n = %d < 0", n);
     if (n && !events) return fail(GDN_ERR_NULL, "events is NULL");

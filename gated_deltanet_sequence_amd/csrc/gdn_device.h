@@ -23,15 +23,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// float32 -> bfloat16 with round-to-nearest-even: add half an ulp of the
-// bfloat16 result, minus one when the kept part is even (so ties go to even),
-// then truncate.  NaN inputs stay NaN (quiet bit forced).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+// float32 -> bfloat16, round-to-nearest-even, NaN kept a NaN: the hardware
+// converter (v_cvt_pk_bf16_f32 on gfx950; a software rounding with a NaN test
+// cost several instructions and a branch per element)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Ordering of LDS accesses among the lanes of one wave (no work-group barrier):
 // complete this wave's outstanding LDS operations and keep the compiler from

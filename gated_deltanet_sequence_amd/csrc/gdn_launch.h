@@ -94,6 +94,20 @@ struct NormArgs {
     void *out;
 };
 hipError_t launch_gated_rmsnorm(const NormArgs &p, hipStream_t s);
+
+// Depthwise causal conv1d (+ SiLU) over x [B,T,C] (C = 2 qk + v channels),
+// split into q, k [B,T,qk] and v [B,T,C - 2 qk]; state / state_out [B][K-1][C]
+// or null (state_out may be state).
+struct ConvArgs {
+    int B, T, C, qk, K;
+    bool f32, silu;
+    const void *x;
+    const float *w, *bias;
+    const void *state;
+    void *state_out, *q, *k, *v;
+};
+hipError_t launch_causal_conv1d(const ConvArgs &p, hipStream_t s);
+int conv_tokens_per_thread();
 long long gated_rmsnorm_max_rows();
 
 }  // namespace gdn

@@ -187,6 +187,29 @@ typedef enum gdn_gate { GDN_GATE_SILU = 0, GDN_GATE_SIGMOID = 1 } gdn_gate;
 gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t d, int32_t dtype, const void *x, const void *z,
                              const float *weight, float eps, int32_t gate, void *out, void *stream);
 
+/* Depthwise causal convolution over time + SiLU on the mixed q|k|v projection,
+ * written as the separate q, k, v tensors the core takes (dingfen.github.io,
+ * section 10: x -> Linear -> CausalConv1D -> SiLU -> q, k, v; 10100.com: kernel
+ * size 4; wanger-sjtu Qwen3.5 GDN page: a depthwise causal conv over the mixed
+ * QKV channels, its inputs cached for decode).  Per sequence b, channel c and
+ * token t, with C = 2 Hk Dk + Hv Dv channels ordered q | k | v:
+ *     y[b,t,c] = act(bias[c] + sum_{j<K} weight[c][j] x[b, t-K+1+j, c]),
+ * inputs before token 0 taken from conv_state (zero if NULL).
+ *   d             B, T (>= 0; 1 for a decode step), Hk, Hv, Dk, Dv, dtype (chunk ignored)
+ *   kernel_size   K: 4
+ *   x             [B,T,C] dtype (the projection output, token-major)
+ *   weight        [C][K] float32; bias [C] float32 or NULL
+ *   conv_state    [B][K-1][C] dtype, the K-1 inputs before token 0 (oldest first), or NULL
+ *   conv_state_out[B][K-1][C] dtype, written with the last K-1 inputs (older cached inputs
+ *                 when T < K-1), or NULL; may be exactly conv_state (in-place update)
+ *   activation    GDN_ACT_SILU or GDN_ACT_NONE
+ *   q, k          [B,T,Hk,Dk] dtype; v [B,T,Hv,Dv] dtype (written)
+ * Outputs overlap no input and no other output.  Limits: B <= 65535, T <= 1,048,560. */
+typedef enum gdn_act { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_act;
+gdn_status gdn_causal_conv1d(const gdn_dims *d, int32_t kernel_size, const void *x, const float *weight,
+                             const float *bias, const void *conv_state, void *conv_state_out,
+                             int32_t activation, void *q, void *k, void *v, void *stream);
+
 /* Name of a status code (static string, never NULL). */
 const char *gdn_status_str(int status);
 

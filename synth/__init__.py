@@ -33,6 +33,7 @@ import torch
 # tensor ids of the per-tensor random streams
 TID_A_LOG, TID_DT_BIAS, TID_Q, TID_K, TID_V, TID_A, TID_B, TID_S0, TID_ERASE, TID_WRITE = range(10)
 TID_NORM_X, TID_NORM_Z, TID_NORM_W = 10, 11, 12
+TID_CONV_X, TID_CONV_W, TID_CONV_B, TID_CONV_S = 13, 14, 15, 16
 
 _SLAB = 1 << 22  # values drawn per slab (bounds the float64 working set)
 
@@ -189,3 +190,17 @@ def make_norm_inputs(shape, dtype: str, seed: int, x_sigma: float = 1.0):
     z = _normal_rows(_rng(seed, TID_NORM_Z), tuple(shape), False)
     w = _rng(seed, TID_NORM_W).uniform(0.5, 1.5, size=(shape[-1],)).astype(np.float32)
     return _to_torch(x, dt), _to_torch(z, dt), torch.from_numpy(w)
+
+
+def make_conv_inputs(B: int, T: int, C: int, dtype: str, seed: int, K: int = 4, bias: bool = True,
+                     state: bool = True):
+    """Inputs of the causal conv1d prologue: the mixed projection x [B,T,C] ~ N(0,1) and the
+    cached inputs state [B,K-1,C] ~ N(0,1) in ``dtype``; weight [C,K] and bias [C] ~
+    U(-1/sqrt(K), 1/sqrt(K)) float32 (the usual fan-in bound of a depthwise kernel)."""
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    lim = 1.0 / math.sqrt(K)
+    x = _to_torch(_normal_rows(_rng(seed, TID_CONV_X), (B, T, C), False), dt)
+    w = torch.from_numpy(_rng(seed, TID_CONV_W).uniform(-lim, lim, size=(C, K)).astype(np.float32))
+    b = torch.from_numpy(_rng(seed, TID_CONV_B).uniform(-lim, lim, size=(C,)).astype(np.float32)) if bias else None
+    s = _to_torch(_normal_rows(_rng(seed, TID_CONV_S), (B, K - 1, C), False), dt) if state else None
+    return x, w, b, s

@@ -413,3 +413,52 @@ def test_gated_rmsnorm_validation():
     assert call_norm(rows, d, bf, x, z, w, out=z) == ERR_ALIAS
     assert call_norm(rows, d, bf, x, z, w, out=x + 16) == ERR_ALIAS and "partly" in last_error()
     assert call_norm(0, d, bf, None, None, None, out=None) == OK
+
+
+# ---- causal conv1d prologue (gdn_causal_conv1d) ----
+
+def conv_args(buf, d, K=4):
+    es = 4 if d.dtype == binding.GDN_F32 else 2
+    qk, vw = d.Hk * d.Dk, d.Hv * d.Dv
+    C = 2 * qk + vw
+    return dict(x=buf(d.B * d.T * C * es), w=buf(C * K * 4), b=buf(C * 4), s=buf(d.B * (K - 1) * C * es),
+                so=buf(d.B * (K - 1) * C * es), q=buf(d.B * d.T * qk * es), k=buf(d.B * d.T * qk * es),
+                v=buf(d.B * d.T * vw * es))
+
+
+def call_conv(d, a, K=4, act=1):
+    return binding.lib().gdn_causal_conv1d(ctypes.byref(d), K, a["x"], a["w"], a["b"], a["s"], a["so"], act,
+                                           a["q"], a["k"], a["v"], None)
+
+
+def test_causal_conv1d_validation():
+    buf = Buf()
+    d = dims(B=2, T=20)
+    assert "gdn_causal_conv1d" in declared_functions()
+    assert call_conv(d, conv_args(buf, d), K=3) == ERR_UNSUPPORTED
+    assert call_conv(d, conv_args(buf, d), act=7) == ERR_UNSUPPORTED
+    assert call_conv(dims(B=2, T=-1), conv_args(buf, d)) == ERR_SHAPE
+    assert call_conv(dims(B=70000, T=1), conv_args(buf, dims(B=1, T=1))) == ERR_UNSUPPORTED
+    for name in ("x", "w", "q", "k", "v"):
+        a = conv_args(buf, d)
+        a[name] = None
+        assert call_conv(d, a) == ERR_NULL, name
+    a = conv_args(buf, d)
+    a["x"] += 8
+    assert call_conv(d, a) == ERR_ALIGN
+    a = conv_args(buf, d)
+    a["q"] = a["x"]
+    assert call_conv(d, a) == ERR_ALIAS
+    a = conv_args(buf, d)
+    a["v"] = a["k"]
+    assert call_conv(d, a) == ERR_ALIAS and "overlaps" in last_error()
+    a = conv_args(buf, d)
+    a["so"] = a["s"] + 16
+    assert call_conv(d, a) == ERR_ALIAS and "partly" in last_error()
+    a = conv_args(buf, d)
+    a["so"] = a["s"]  # in place: allowed (B = 0 keeps the call host-only)
+    d0 = dims(B=0, T=20)
+    assert call_conv(d0, conv_args(buf, d0)) == OK
+    a0 = conv_args(buf, d0)
+    a0["b"] = a0["s"] = a0["so"] = None
+    assert call_conv(d0, a0) == OK
