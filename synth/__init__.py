@@ -65,7 +65,7 @@ class GDNSpec:
         return {"f32": torch.float32, "bf16": torch.bfloat16}[self.dtype]
 
 
-# Named workloads (sizes as stated for each; see the design doc for the list).
+# Named workloads (sizes as stated for each).
 WORKLOADS: Dict[str, GDNSpec] = {
     # tiny fp32 forward: parity at 1e-5
     "tiny_f32": GDNSpec(B=1, T=256, Hk=2, Hv=2, Dk=64, Dv=64, dtype="f32", seed=100),

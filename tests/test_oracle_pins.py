@@ -7,7 +7,7 @@ least one of them.  The pins:
 
 * gate closed forms (dingfen page, sections 9-10) against NumPy/SciPy routines;
 * hand-worked examples from the five-step form (tests/golden/*.json);
-* alpha = 1, beta = 0 leaves the state unchanged (north-star check 1);
+* alpha = 1, beta = 0 leaves the state unchanged (the identity transition);
 * alpha = beta = 1 with a unit key writes v exactly at address k, and the
   interpolation identity of the dingfen page, section 7, for any beta;
 * orthonormal keys reduce the delta rule to linear attention, whose outputs
