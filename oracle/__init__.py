@@ -54,6 +54,7 @@ def _load():
     lib.oracle_gdn2_gates.argtypes = [ctypes.c_long, i, i, i, D, D, D, D, D, D, D]
     lib.oracle_gdn2_core.argtypes = [i] * 6 + [D] * 6 + [ctypes.c_double, D, D, D]
     lib.oracle_gdn2_fwd.argtypes = [i] * 6 + [D] * 7 + [ctypes.c_double, D, D, D]
+    lib.oracle_gdn2_bwd.argtypes = [i] * 6 + [D] * 7 + [ctypes.c_double] + [D] * 11
     lib.oracle_gated_rmsnorm.argtypes = [ctypes.c_long, i, D, D, D, ctypes.c_double, i, D]
     lib.oracle_causal_conv1d.argtypes = [i, i, i, i, D, D, D, D, i, D, D]
     _lib = lib
@@ -178,6 +179,26 @@ def gdn2_fwd(q, k, v, a, A_log, erase, write, S0=None, scale: float = 1.0):
     _load().oracle_gdn2_fwd(B, T, Hk, Hv, Dk, Dv, _p(q), _p(k), _p(v), _p(a), _p(A_log),
                             _p(erase), _p(write), float(scale), _p(S0), _p(out), _p(ST))
     return out, ST
+
+
+def gdn2_bwd(q, k, v, a, A_log, erase, write, d_out, S0=None, d_ST=None, scale: float = 1.0):
+    """Gradient of gdn2_fwd: the vector-Jacobian products of (out, S_T) with (d_out, d_ST)
+    (d_ST None = 0), by reverse-mode differentiation of the token loop.  Returns a dict of
+    float64 arrays: dq, dk [B,T,Hk,Dk]; dv, d_write [B,T,Hv,Dv]; da, d_erase [B,T,Hv,Dk];
+    dA_log [Hv,Dk]; dS0 [B,Hv,Dk,Dv]."""
+    q, k, v, a, A_log, erase, write, d_out, S0, d_ST = (
+        f64(t) for t in (q, k, v, a, A_log, erase, write, d_out, S0, d_ST))
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    r = {"dq": np.empty((B, T, Hk, Dk)), "dk": np.empty((B, T, Hk, Dk)),
+         "dv": np.empty((B, T, Hv, Dv)), "da": np.empty((B, T, Hv, Dk)),
+         "d_erase": np.empty((B, T, Hv, Dk)), "d_write": np.empty((B, T, Hv, Dv)),
+         "dA_log": np.empty((Hv, Dk)), "dS0": np.empty((B, Hv, Dk, Dv))}
+    _load().oracle_gdn2_bwd(B, T, Hk, Hv, Dk, Dv, _p(q), _p(k), _p(v), _p(a), _p(A_log),
+                            _p(erase), _p(write), float(scale), _p(S0), _p(d_out), _p(d_ST),
+                            _p(r["dq"]), _p(r["dk"]), _p(r["dv"]), _p(r["da"]), _p(r["d_erase"]),
+                            _p(r["d_write"]), _p(r["dA_log"]), _p(r["dS0"]))
+    return r
 
 
 GATE_SILU, GATE_SIGMOID = 0, 1

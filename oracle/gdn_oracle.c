@@ -298,3 +298,197 @@ void oracle_causal_conv1d(int B, int T, int C, int K, const double *x, const dou
         }
     }
 }
+
+/* One Gated Delta Rule-2 token step on a d_k x d_v state (zhichai page, the
+ * expanded form): S = diag(D) S;  r = S^T e;  S += k (z - r)^T.  r is scratch
+ * of d_v entries. */
+static void g2_step(int Dk, int Dv, double *S, const double *D, const double *e,
+                    const double *k, const double *z, double *r) {
+    for (int i = 0; i < Dk; ++i)
+        for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] *= D[i];
+    for (int j = 0; j < Dv; ++j) r[j] = 0.0;
+    for (int i = 0; i < Dk; ++i)
+        for (int j = 0; j < Dv; ++j) r[j] += S[(size_t)i * Dv + j] * e[i];
+    for (int j = 0; j < Dv; ++j) r[j] = z[j] - r[j];
+    for (int i = 0; i < Dk; ++i)
+        for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] += k[i] * r[j];
+}
+
+/* Gradient of the Gated DeltaNet-2 forward (oracle_gdn2_fwd) by reverse-mode
+ * differentiation of the token loop (zhichai page, sections "Gated Delta
+ * Rule-2" for the recurrence and "Gate-aware 反向传播" for the requirement that
+ * the gate factors stay at each token instead of being pulled out of the
+ * accumulation).  The scalar being differentiated is
+ *     L = sum(d_out * out) + sum(d_ST * S_T),
+ * so the results are the vector-Jacobian products of the forward with the
+ * given output and final-state gradients (d_ST NULL = 0).
+ *
+ * Per token, with D = exp(g), e = eb (.) k, z = wb (.) v, the forward step is
+ * Sbar = diag(D) S_prev, r = Sbar^T e, S = Sbar + k (z - r)^T, o = scale S^T q;
+ * its adjoint, given dS (the gradient of S after the step), is
+ *     dS += scale q do^T;          dq = scale S do
+ *     dk += dS (z - r);            dz = dS^T k;        dr = -dz
+ *     dSbar = dS + e dr^T;         de = Sbar dr
+ *     dD_i = sum_j dSbar_ij S_prev_ij;   dS_prev = diag(D) dSbar
+ * and through the gates g = -exp(A_log) softplus(a), eb = sigmoid(erase),
+ * wb = sigmoid(write):
+ *     dg = dD D;  da = -dg exp(A_log) sigmoid(a);  dA_log += dg g
+ *     dk += de eb;  d_erase = de k eb (1 - eb);  dv = dz wb;
+ *     d_write = dz v wb (1 - wb).
+ * The states before each token are needed in reverse order; they are kept
+ * every SEG tokens and recomputed inside each stretch of SEG tokens with the
+ * same forward step, which reproduces them exactly.
+ * Layouts: dq, dk [B,T,Hk,Dk] (summed over the value heads of a key head);
+ * dv, d_write [B,T,Hv,Dv]; da, d_erase [B,T,Hv,Dk]; dA_log [Hv,Dk]; dS0
+ * [B,Hv,Dk,Dv] (the gradient of the initial state, S0 NULL = 0). */
+#define G2_SEG 64
+void oracle_gdn2_bwd(int B, int T, int Hk, int Hv, int Dk, int Dv,
+                     const double *q, const double *k, const double *v,
+                     const double *a, const double *A_log, const double *erase,
+                     const double *write, double scale, const double *S0,
+                     const double *dout, const double *dST, double *dq, double *dk,
+                     double *dv, double *da, double *derase, double *dwrite,
+                     double *dA_log, double *dS0) {
+    const int grp = Hv / Hk;
+    const size_t nk = (size_t)B * T * Hv * Dk, nv = (size_t)B * T * Hv * Dv, SS = (size_t)Dk * Dv;
+    double *g = (double *)malloc(sizeof(double) * (nk ? nk : 1));
+    double *eb = (double *)malloc(sizeof(double) * (nk ? nk : 1));
+    double *wb = (double *)malloc(sizeof(double) * (nv ? nv : 1));
+    /* per value head gradients of q and k, summed over each key head's group below */
+    double *dqh = (double *)calloc(nk ? nk : 1, sizeof(double));
+    double *dkh = (double *)calloc(nk ? nk : 1, sizeof(double));
+    double *dal = (double *)calloc((size_t)B * Hv * Dk, sizeof(double));
+    oracle_gdn2_gates((long)B * T, Hv, Dk, Dv, a, A_log, erase, write, g, eb, wb);
+    const int nseg = (T + G2_SEG - 1) / G2_SEG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int u = 0; u < B * Hv; ++u) {
+        const int bb = u / Hv, hv = u % Hv, hk = hv / grp;
+        double *cp = (double *)malloc(sizeof(double) * SS * (nseg ? nseg : 1));
+        double *st = (double *)malloc(sizeof(double) * SS * G2_SEG);
+        double *S = (double *)malloc(sizeof(double) * SS);
+        double *Sb = (double *)malloc(sizeof(double) * SS);
+        double *dS = (double *)malloc(sizeof(double) * SS);
+        double *D = (double *)malloc(sizeof(double) * Dk);
+        double *e = (double *)malloc(sizeof(double) * Dk);
+        double *de = (double *)malloc(sizeof(double) * Dk);
+        double *z = (double *)malloc(sizeof(double) * Dv);
+        double *dl = (double *)malloc(sizeof(double) * Dv);
+        double *dz = (double *)malloc(sizeof(double) * Dv);
+        double *r = (double *)malloc(sizeof(double) * Dv);
+#define TOK_GATES(t)                                                                  \
+        const size_t ci = (((size_t)bb * T + (t)) * Hv + hv) * Dk;                    \
+        const size_t vi = (((size_t)bb * T + (t)) * Hv + hv) * Dv;                    \
+        const double *kt = k + (((size_t)bb * T + (t)) * Hk + hk) * Dk;               \
+        const double *vt = v + vi;                                                    \
+        for (int i = 0; i < Dk; ++i) { D[i] = exp(g[ci + i]); e[i] = eb[ci + i] * kt[i]; } \
+        for (int j = 0; j < Dv; ++j) z[j] = wb[vi + j] * vt[j];
+        /* forward pass keeping the state before every SEG-th token */
+        if (S0) memcpy(S, S0 + (size_t)u * SS, sizeof(double) * SS);
+        else memset(S, 0, sizeof(double) * SS);
+        for (int t = 0; t < T; ++t) {
+            if (t % G2_SEG == 0) memcpy(cp + (size_t)(t / G2_SEG) * SS, S, sizeof(double) * SS);
+            TOK_GATES(t)
+            g2_step(Dk, Dv, S, D, e, kt, z, r);
+        }
+        if (dST) memcpy(dS, dST + (size_t)u * SS, sizeof(double) * SS);
+        else memset(dS, 0, sizeof(double) * SS);
+        for (int s = nseg - 1; s >= 0; --s) {
+            const int t0 = s * G2_SEG, len = (T - t0 < G2_SEG) ? T - t0 : G2_SEG;
+            /* st[j] = state before token t0 + j */
+            memcpy(S, cp + (size_t)s * SS, sizeof(double) * SS);
+            for (int j = 0; j < len; ++j) {
+                memcpy(st + (size_t)j * SS, S, sizeof(double) * SS);
+                if (j + 1 < len) {
+                    TOK_GATES(t0 + j)
+                    g2_step(Dk, Dv, S, D, e, kt, z, r);
+                }
+            }
+            for (int j = len - 1; j >= 0; --j) {
+                const int t = t0 + j;
+                TOK_GATES(t)
+                const double *Sp = st + (size_t)j * SS;
+                const double *qt = q + (((size_t)bb * T + t) * Hk + hk) * Dk;
+                const double *dot = dout + vi;
+                /* recompute Sbar, r, delta = z - r and S after the step */
+                for (int i = 0; i < Dk; ++i)
+                    for (int jj = 0; jj < Dv; ++jj) Sb[(size_t)i * Dv + jj] = Sp[(size_t)i * Dv + jj] * D[i];
+                for (int jj = 0; jj < Dv; ++jj) r[jj] = 0.0;
+                for (int i = 0; i < Dk; ++i)
+                    for (int jj = 0; jj < Dv; ++jj) r[jj] += Sb[(size_t)i * Dv + jj] * e[i];
+                for (int jj = 0; jj < Dv; ++jj) dl[jj] = z[jj] - r[jj];
+                for (int i = 0; i < Dk; ++i)
+                    for (int jj = 0; jj < Dv; ++jj)
+                        S[(size_t)i * Dv + jj] = Sb[(size_t)i * Dv + jj] + kt[i] * dl[jj];
+                /* read-out: o = scale S^T q */
+                double *dqt = dqh + ci, *dkt = dkh + ci;
+                for (int i = 0; i < Dk; ++i) {
+                    double acc = 0.0;
+                    for (int jj = 0; jj < Dv; ++jj) acc += S[(size_t)i * Dv + jj] * dot[jj];
+                    dqt[i] += scale * acc;
+                }
+                for (int i = 0; i < Dk; ++i)
+                    for (int jj = 0; jj < Dv; ++jj) dS[(size_t)i * Dv + jj] += scale * qt[i] * dot[jj];
+                /* S = Sbar + k delta^T */
+                for (int i = 0; i < Dk; ++i) {
+                    double acc = 0.0;
+                    for (int jj = 0; jj < Dv; ++jj) acc += dS[(size_t)i * Dv + jj] * dl[jj];
+                    dkt[i] += acc;
+                }
+                for (int jj = 0; jj < Dv; ++jj) dz[jj] = 0.0;
+                for (int i = 0; i < Dk; ++i)
+                    for (int jj = 0; jj < Dv; ++jj) dz[jj] += dS[(size_t)i * Dv + jj] * kt[i];
+                /* r = Sbar^T e, dr = -dz: dSbar = dS - e dz^T, de = -Sbar dz */
+                for (int i = 0; i < Dk; ++i) {
+                    double acc = 0.0;
+                    for (int jj = 0; jj < Dv; ++jj) acc += Sb[(size_t)i * Dv + jj] * dz[jj];
+                    de[i] = -acc;
+                }
+                for (int i = 0; i < Dk; ++i)
+                    for (int jj = 0; jj < Dv; ++jj) dS[(size_t)i * Dv + jj] -= e[i] * dz[jj];
+                /* Sbar = diag(D) S_prev */
+                for (int i = 0; i < Dk; ++i) {
+                    double dD = 0.0;
+                    for (int jj = 0; jj < Dv; ++jj) dD += dS[(size_t)i * Dv + jj] * Sp[(size_t)i * Dv + jj];
+                    for (int jj = 0; jj < Dv; ++jj) dS[(size_t)i * Dv + jj] *= D[i];
+                    const double dg = dD * D[i];
+                    const double Ai = A_log[(size_t)hv * Dk + i];
+                    da[ci + i] = -dg * exp(Ai) * oracle_sigmoid(a[ci + i]);
+                    dal[(size_t)u * Dk + i] += dg * g[ci + i];
+                    /* e = eb (.) k */
+                    dkt[i] += de[i] * eb[ci + i];
+                    derase[ci + i] = de[i] * kt[i] * eb[ci + i] * (1.0 - eb[ci + i]);
+                }
+                /* z = wb (.) v */
+                for (int jj = 0; jj < Dv; ++jj) {
+                    dv[vi + jj] = dz[jj] * wb[vi + jj];
+                    dwrite[vi + jj] = dz[jj] * vt[jj] * wb[vi + jj] * (1.0 - wb[vi + jj]);
+                }
+            }
+        }
+#undef TOK_GATES
+        memcpy(dS0 + (size_t)u * SS, dS, sizeof(double) * SS);
+        free(cp); free(st); free(S); free(Sb); free(dS);
+        free(D); free(e); free(de); free(z); free(dl); free(dz); free(r);
+    }
+    /* sums over the value heads of each key head, and over sequences for A_log */
+    for (int bb = 0; bb < B; ++bb)
+        for (int t = 0; t < T; ++t)
+            for (int hk = 0; hk < Hk; ++hk)
+                for (int i = 0; i < Dk; ++i) {
+                    double sq = 0.0, sk = 0.0;
+                    for (int x = 0; x < grp; ++x) {
+                        const size_t ci = (((size_t)bb * T + t) * Hv + hk * grp + x) * Dk + i;
+                        sq += dqh[ci];
+                        sk += dkh[ci];
+                    }
+                    dq[(((size_t)bb * T + t) * Hk + hk) * Dk + i] = sq;
+                    dk[(((size_t)bb * T + t) * Hk + hk) * Dk + i] = sk;
+                }
+    for (int hv = 0; hv < Hv; ++hv)
+        for (int i = 0; i < Dk; ++i) {
+            double s = 0.0;
+            for (int bb = 0; bb < B; ++bb) s += dal[((size_t)bb * Hv + hv) * Dk + i];
+            dA_log[(size_t)hv * Dk + i] = s;
+        }
+    free(g); free(eb); free(wb); free(dqh); free(dkh); free(dal);
+}
