@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tokens/s at T=4096 (16k/64v heads, d=128) + decode-step HBM GB/s"
 PEAK_MFMA_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+PEAK_MFMA_F32_TFLOPS = 157.3    # MI355X dense fp32 matrix (and packed fp32 vector) peak
 
 # Algorithmic work per (token, value head) at d_k = d_v = 128, chunk C = 64, G = 4
 # value heads per key head (flop = 2 x multiply-accumulate):
@@ -65,6 +66,25 @@ def scan_flop_per_token_head(dk, dv, C):
 # gate-logit tensors and the output once each, plus the state(s).
 def gdn2_flop_per_token_head(dk, dv, C):
     return 2 * (3 * dk * dv + C * (dk + (dk + dv) // 2 + dv // 2))
+
+
+# Algorithmic work of the Gated DeltaNet-2 backward per (token, value head) and launch
+# (flop = 2 x multiply-accumulate; triangular products counted as triangles):
+#   g2b_prep      M and A_qk over the channels, (C + 1)/2 pairs each; A = (I + M)^{-1}: C^2/6
+#   g2b_fwd_scan  R = Z - Et S, S update (dk dv each); U = A R (C dv / 2)
+#   g2b_bwd_scan  Kh dS, Qt^T dO, Et^T dR (dk dv each); A_qk^T dO, A^T dU (C dv / 2 each)
+#   g2b_products  dEt, dQt, dKh (dk dv each); tril(dO U^T) (C dv / 2); dU R^T (C dv);
+#                 A^T dA and X A^T (C^2 / 2 each)
+#   g2b_local     the three pairwise decay sums over (C + 1)/2 partners per channel
+def bwd2_flop_per_token_head(dk, dv, C):
+    return {
+        "g2b_prep": 2 * (C + 1) * dk + C * C // 3,
+        "g2b_fwd_scan": 2 * (2 * dk * dv + C * dv // 2),
+        "g2b_bwd_scan": 2 * (3 * dk * dv + C * dv),
+        "g2b_products": 2 * (3 * dk * dv + 3 * C * dv // 2 + C * C),
+        "g2b_local": 3 * (C + 1) * dk,
+        "g2b_reduce": 0,
+    }
 
 
 def gdn2_bytes(B, T, Hk, Hv, Dk, Dv, es, init_state):
@@ -518,6 +538,69 @@ def bench_gdn2(args, torch, gdn, synth):
                 path=dict(flop=flop, tflops=round(tf, 2), mfma_frac=round(tf / PEAK_MFMA_F16_TFLOPS, 4)))
 
 
+def bench_gdn2_bwd(args, torch, gdn, synth):
+    """The Gated DeltaNet-2 backward on the same workload (B=1, T=8192, 16/64 heads, d=128):
+    K calls of gdn2_chunk_bwd (output and final-state gradients given), each launch
+    bracketed by HIP events on the call's stream."""
+    spec = synth.WORKLOADS["gdn2_t8192"]
+    log(f"[bench] gdn2 backward workload {spec}")
+    inp = synth.make_inputs(spec)
+    inp.update(synth.make_grad_inputs(spec))
+    nsets = 2
+    sets = []
+    for _ in range(nsets):
+        d = {k: (None if v is None else v.cuda().contiguous()) for k, v in inp.items()}
+        d["ws"] = torch.empty(gdn.gdn2_chunk_bwd_workspace_bytes(
+            gdn.make_dims(spec.B, spec.T, spec.Hk, spec.Hv, spec.Dk, spec.Dv, spec.torch_dtype)),
+            dtype=torch.uint8, device="cuda")
+        d["g"] = None
+        sets.append(d)
+    del inp
+    stream = torch.cuda.current_stream()
+    events = [gdn.StageEvents(gdn.GDN2_CHUNK_BWD_STAGES) for _ in range(args.steps)]
+
+    def step(d, ev=None):
+        d["g"] = gdn.gdn2_chunk_bwd(d["q"], d["k"], d["v"], d["a"], d["A_log"], d["erase"], d["write"],
+                                    d["S0"], d["d_out"], d["d_ST"], workspace=d["ws"], grads=d["g"],
+                                    stream=stream, stage_events=ev)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(sets[i % nsets], events[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    stage = [sum(e.stage_ms()[j] for e in events) / args.steps for j in range(gdn.GDN2_CHUNK_BWD_STAGES)]
+    for e in events:
+        e.close()
+    units = spec.B * spec.T * spec.Hv
+    fl = bwd2_flop_per_token_head(spec.Dk, spec.Dv, spec.chunk)
+    names = gdn.BWD2_STAGE_NAMES
+    dom = max(range(len(names)), key=lambda j: stage[j])
+    dflop = fl[names[dom]] * units
+    tf = dflop / (stage[dom] * 1e-3) / 1e12
+    total_flop = sum(fl.values()) * units
+    log(f"[bench] gdn2 backward {ms * 1e3:.1f} us/step; "
+        + ", ".join(f"{n} {t * 1e3:.1f} us" for n, t in zip(names, stage)))
+    del sets
+    torch.cuda.empty_cache()
+    return dict(value=round(spec.B * spec.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
+                config=dict(workload="gdn2_t8192_backward", B=spec.B, T=spec.T, Hk=spec.Hk, Hv=spec.Hv,
+                            Dk=spec.Dk, Dv=spec.Dv, chunk=spec.chunk, input_dtype="bf16",
+                            grad_dtype="f32", arithmetic="f32"),
+                stages_us={n: round(t * 1e3, 2) for n, t in zip(names, stage)},
+                roofline=dict(kernel=names[dom], bound="mfma", achieved=round(tf, 2), peak=PEAK_MFMA_F32_TFLOPS,
+                              unit="TFLOP/s", frac=round(tf / PEAK_MFMA_F32_TFLOPS, 4), flop_per_launch=dflop,
+                              avg_launch_ms=round(stage[dom], 5), traffic=None),
+                path=dict(flop=total_flop, tflops=round(total_flop / (ms * 1e-3) / 1e12, 2),
+                          f32_frac=round(total_flop / (ms * 1e-3) / 1e12 / PEAK_MFMA_F32_TFLOPS, 4)))
+
+
 def cpu_baseline(pre, min_seconds=10.0):
     """The float64 oracle on this host's cores: the whole prefill workload,
     repeated until at least min_seconds of CPU time have passed."""
@@ -548,6 +631,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=3, help="buffer sets rotated in the timed region")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gdn2", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the Gated DeltaNet-2 backward leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration)")
@@ -576,6 +660,7 @@ def main():
     dec = None if args.no_decode else bench_decode(args, torch, gdn, synth)
     g2 = None if args.no_gdn2 else bench_gdn2(args, torch, gdn, synth)
     g2d = None if args.no_gdn2 or args.no_decode else bench_decode_gdn2(args, torch, gdn, synth)
+    g2b = None if args.no_gdn2 or args.no_bwd else bench_gdn2_bwd(args, torch, gdn, synth)
     epi = bench_epilogue(args, torch, gdn, synth)
     pro = bench_prologue(args, torch, gdn, synth)
     if args.calibration_copy:
@@ -605,6 +690,7 @@ def main():
         "decode": dec,
         "gdn2": g2,
         "gdn2_decode": g2d,
+        "gdn2_backward": g2b,
         "gated_rmsnorm": epi,
         "causal_conv1d": pro,
         "cpu_baseline": cpu,

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 GDN_CHUNK_FWD_STAGES = 2
 STAGE_NAMES = ("chunk_local", "state_scan")
+GDN2_CHUNK_BWD_STAGES = 6
+BWD2_STAGE_NAMES = ("g2b_prep", "g2b_fwd_scan", "g2b_bwd_scan", "g2b_products", "g2b_local", "g2b_reduce")
 
 
 class gdn_dims(ctypes.Structure):
@@ -57,6 +59,13 @@ def lib():
     L.gdn2_chunk_fwd_workspace_bytes.argtypes = [dims_p]
     L.gdn2_chunk_fwd.restype = ctypes.c_int
     L.gdn2_chunk_fwd.argtypes = [dims_p, vp, vp, vp, vp, fp, vp, vp, fp, vp, fp, vp, sz, vp]
+    L.gdn2_chunk_bwd_workspace_bytes.restype = sz
+    L.gdn2_chunk_bwd_workspace_bytes.argtypes = [dims_p]
+    L.gdn2_chunk_bwd.restype = ctypes.c_int
+    L.gdn2_chunk_bwd.argtypes = [dims_p, vp, vp, vp, vp, fp, vp, vp, fp, vp, fp,
+                                 fp, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
+    L.gdn2_chunk_bwd_timed.restype = ctypes.c_int
+    L.gdn2_chunk_bwd_timed.argtypes = L.gdn2_chunk_bwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
     L.gdn_recurrent_step.restype = ctypes.c_int
     L.gdn_recurrent_step.argtypes = [dims_p, vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
     L.gdn2_recurrent_step.restype = ctypes.c_int
@@ -217,6 +226,60 @@ def gdn2_chunk_fwd(q, k, v, a, A_log, erase, write, initial_state=None, *, scale
     return out, final_state
 
 
+def gdn2_chunk_bwd_workspace_bytes(dims: gdn_dims) -> int:
+    return int(lib().gdn2_chunk_bwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def gdn2_chunk_bwd(q, k, v, a, A_log, erase, write, initial_state, d_out, d_final_state=None, *,
+                   scale: float = 1.0, output_d_initial_state: bool = True, workspace=None,
+                   stream=None, grads=None, stage_events=None) -> dict:
+    """Gradient of gdn2_chunk_fwd: the vector-Jacobian products of (out, final_state) with
+    (d_out [B,T,Hv,Dv] bfloat16, d_final_state [B,Hv,Dk,Dv] fp32 or None).  Same inputs as
+    gdn2_chunk_fwd.  Returns a dict of float32 tensors: dq, dk [B,T,Hk,Dk]; dv, d_write
+    [B,T,Hv,Dv]; da, d_erase [B,T,Hv,Dk]; dA_log [Hv,Dk]; d_initial_state [B,Hv,Dk,Dv]
+    (or None when output_d_initial_state is False).  grads: an earlier result to write
+    into instead; stage_events: a StageEvents(GDN2_CHUNK_BWD_STAGES) to time each launch."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dims = make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, scale)
+    for name, t in (("A_log", A_log), ("initial_state", initial_state), ("d_final_state", d_final_state)):
+        _f32(t, name)
+    for name, t in (("k", k), ("v", v), ("a", a), ("erase", erase), ("write", write), ("d_out", d_out)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must have the dtype of q")
+    if k.shape != q.shape or tuple(v.shape[:2]) != (B, T) or tuple(d_out.shape) != tuple(v.shape):
+        raise ValueError("shape mismatch among q, k, v, d_out")
+    if tuple(a.shape) != (B, T, Hv, Dk) or tuple(erase.shape) != (B, T, Hv, Dk):
+        raise ValueError("a and erase must be [B,T,Hv,Dk]")
+    if tuple(write.shape) != (B, T, Hv, Dv):
+        raise ValueError("write must be [B,T,Hv,Dv]")
+    if tuple(A_log.shape) != (Hv, Dk):
+        raise ValueError("A_log must be [Hv,Dk]")
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None and tuple(t.shape) != (B, Hv, Dk, Dv):
+            raise ValueError(f"{name} must be [B,Hv,Dk,Dv]")
+    dev, f32 = q.device, torch.float32
+    g = grads if grads is not None else {"dq": torch.empty((B, T, Hk, Dk), dtype=f32, device=dev),
+         "dk": torch.empty((B, T, Hk, Dk), dtype=f32, device=dev),
+         "dv": torch.empty((B, T, Hv, Dv), dtype=f32, device=dev),
+         "da": torch.empty((B, T, Hv, Dk), dtype=f32, device=dev),
+         "d_erase": torch.empty((B, T, Hv, Dk), dtype=f32, device=dev),
+         "d_write": torch.empty((B, T, Hv, Dv), dtype=f32, device=dev),
+         "dA_log": torch.empty((Hv, Dk), dtype=f32, device=dev),
+         "d_initial_state": (torch.empty((B, Hv, Dk, Dv), dtype=f32, device=dev)
+                             if output_d_initial_state else None)}
+    if workspace is None:
+        workspace = torch.empty(max(gdn2_chunk_bwd_workspace_bytes(dims), 1), dtype=torch.uint8, device=dev)
+    st = lib().gdn2_chunk_bwd_timed(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log), _ptr(erase), _ptr(write),
+        _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), _ptr(g["dq"]), _ptr(g["dk"]),
+        _ptr(g["dv"]), _ptr(g["da"]), _ptr(g["d_erase"]), _ptr(g["d_write"]), _ptr(g["dA_log"]),
+        _ptr(g["d_initial_state"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream), None if stage_events is None else stage_events._arr)
+    _check(st)
+    return g
+
+
 def gdn_recurrent_step(q, k, v, a, b, A_log, dt_bias, state, *, scale: float = 1.0, out=None,
                        stream=None) -> torch.Tensor:
     """One decode step, state updated in place.  q, k [B,Hk,Dk]; v [B,Hv,Dv];
@@ -331,10 +394,10 @@ def gdn_causal_conv1d(x, weight, bias=None, conv_state=None, *, Hk: int, Hv: int
 
 
 class StageEvents:
-    """GDN_CHUNK_FWD_STAGES + 1 HIP events for gdn_chunk_fwd(..., stage_events=...)."""
+    """stages + 1 HIP events (default GDN_CHUNK_FWD_STAGES) for the timed entry points."""
 
-    def __init__(self):
-        self.n = GDN_CHUNK_FWD_STAGES + 1
+    def __init__(self, stages: int = None):
+        self.n = (GDN_CHUNK_FWD_STAGES if stages is None else int(stages)) + 1
         self._arr = (ctypes.c_void_p * self.n)()
         _check(lib().gdn_events_create(self.n, self._arr))
 

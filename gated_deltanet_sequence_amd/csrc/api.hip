@@ -245,6 +245,84 @@ gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const
     return GDN_OK;
 }
 
+size_t gdn2_chunk_bwd_workspace_bytes(const gdn_dims *d) {
+    if (check_dims(d, true) != GDN_OK || d->dtype != GDN_BF16) return 0;
+    if (d->B == 0 || d->T == 0) return 0;
+    return gdn::bwd2_workspace_layout(d->B, d->T, d->Hv, d->Dk, d->Dv, nullptr, nullptr);
+}
+
+gdn_status gdn2_chunk_bwd_timed(const gdn_dims *d, const void *q, const void *k, const void *v,
+                                const void *a, const float *A_log, const void *erase, const void *write,
+                                const float *initial_state, const void *d_out, const float *d_final_state,
+                                float *dq, float *dk, float *dv, float *da, float *d_erase, float *d_write,
+                                float *dA_log, float *d_initial_state, void *workspace,
+                                size_t workspace_bytes, void *stream, void *const *stage_events) {
+    gdn_status st = check_dims(d, true);
+    if (st != GDN_OK) return st;
+    if (d->dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "gdn2_chunk_bwd: dtype must be GDN_BF16");
+    const size_t B = d->B, T = d->T, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv, es = 2;
+    const Span sq{"q", q, B * T * Hk * Dk * es}, sk{"k", k, B * T * Hk * Dk * es};
+    const Span sv{"v", v, B * T * Hv * Dv * es};
+    const Span sa{"a", a, B * T * Hv * Dk * es}, se{"erase", erase, B * T * Hv * Dk * es};
+    const Span swr{"write", write, B * T * Hv * Dv * es};
+    const Span sal{"A_log", A_log, Hv * Dk * 4};
+    const Span s0{"initial_state", initial_state, initial_state ? B * Hv * Dk * Dv * 4 : 0};
+    const Span sdo{"d_out", d_out, B * T * Hv * Dv * es};
+    const Span sdf{"d_final_state", d_final_state, d_final_state ? B * Hv * Dk * Dv * 4 : 0};
+    const Span gq{"dq", dq, B * T * Hk * Dk * 4}, gk{"dk", dk, B * T * Hk * Dk * 4};
+    const Span gv{"dv", dv, B * T * Hv * Dv * 4}, gw{"d_write", d_write, B * T * Hv * Dv * 4};
+    const Span ga{"da", da, B * T * Hv * Dk * 4}, ge{"d_erase", d_erase, B * T * Hv * Dk * 4};
+    const Span gal{"dA_log", dA_log, Hv * Dk * 4};
+    const Span g0{"d_initial_state", d_initial_state, d_initial_state ? B * Hv * Dk * Dv * 4 : 0};
+    const size_t wneed = gdn2_chunk_bwd_workspace_bytes(d);
+    const Span sw{"workspace", workspace, wneed};
+    for (const Span *s : {&sq, &sk, &sv, &sa, &se, &swr, &s0, &sdo, &sdf, &gq, &gk, &gv, &gw, &ga, &ge, &g0})
+        if ((st = need(*s, 16)) != GDN_OK) return st;
+    for (const Span *s : {&sal, &gal})
+        if ((st = need(*s, 4)) != GDN_OK) return st;
+    if (wneed) {
+        if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", wneed);
+        if (workspace_bytes < wneed)
+            return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, wneed);
+        if ((uintptr_t)workspace % 256) return fail(GDN_ERR_ALIGN, "workspace is not 256-byte aligned");
+    }
+    const Span *ins[] = {&sq, &sk, &sv, &sa, &se, &swr, &sal, &s0, &sdo, &sdf};
+    const Span *outs[] = {&gq, &gk, &gv, &gw, &ga, &ge, &gal, &g0, &sw};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Span *s : ins)
+            if (overlap(*outs[i], *s)) return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[i]->name, s->name);
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlap(*outs[i], *outs[j]))
+                return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[i]->name, outs[j]->name);
+    }
+    ok();
+    if (B == 0) return GDN_OK;
+    gdn::Bwd2Args p{};
+    p.B = d->B; p.T = d->T; p.Hk = d->Hk; p.Hv = d->Hv; p.Dk = d->Dk; p.Dv = d->Dv;
+    p.NC = (d->T + 63) / 64; p.scale = d->scale;
+    p.q = q; p.k = k; p.v = v; p.a = a; p.erase = erase; p.write = write; p.A_log = A_log;
+    p.S0 = initial_state; p.dout = d_out; p.dST = d_final_state;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.da = da; p.derase = d_erase; p.dwrite = d_write;
+    p.dA_log = dA_log; p.dS0 = d_initial_state;
+    gdn::Bwd2Workspace ws{};
+    if (T) gdn::bwd2_workspace_layout(d->B, d->T, d->Hv, d->Dk, d->Dv, workspace, &ws);
+    const hipEvent_t *ev = (p.T > 0) ? (const hipEvent_t *)stage_events : nullptr;
+    const hipError_t e = gdn::launch_bwd2(p, ws, (hipStream_t)stream, ev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+gdn_status gdn2_chunk_bwd(const gdn_dims *d, const void *q, const void *k, const void *v, const void *a,
+                          const float *A_log, const void *erase, const void *write,
+                          const float *initial_state, const void *d_out, const float *d_final_state,
+                          float *dq, float *dk, float *dv, float *da, float *d_erase, float *d_write,
+                          float *dA_log, float *d_initial_state, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+    return gdn2_chunk_bwd_timed(d, q, k, v, a, A_log, erase, write, initial_state, d_out, d_final_state, dq,
+                                dk, dv, da, d_erase, d_write, dA_log, d_initial_state, workspace,
+                                workspace_bytes, stream, nullptr);
+}
+
 gdn_status gdn_recurrent_step(const gdn_dims *d, const void *q, const void *k, const void *v,
                               const float *a, const float *b, const float *A_log,
                               const float *dt_bias, float *state, void *out, void *stream) {

@@ -1,0 +1,874 @@
+// bwd2.hip -- gradient of the Gated DeltaNet-2 chunked forward (zhichai.net,
+// "Gated DeltaNet-2": sections "WY 形式" for the chunk form that is
+// differentiated, "Gate-aware 反向传播" for the backward's requirement that the
+// gate factors stay at the accumulation points: dA += dU Z^T, dA += dY Ebar^T).
+//
+// Per chunk of C = 64 tokens (n), value head and sequence, with G the in-chunk
+// inclusive prefix of the channel-wise log decay, gamma = e^G, e = sigmoid(erase) k,
+// z = sigmoid(write) v, qs = scale q:
+//   Et = gamma . e, Qt = gamma . qs, Kh = (gamma_C / gamma) . k      (rows)
+//   M[t][i]  = sum_c e_t k_i e^{G_t - G_i}  (i < t),   A = (I + M)^{-1}
+//   Aq[t][i] = sum_c qs_t k_i e^{G_t - G_i} (i <= t)
+//   R = Z - Et S_n,  U = A R,  O = Qt S_n + Aq U,  S_{n+1} = gamma_C . S_n + Kh^T U.
+// Its adjoint, given dO and dS_{n+1}:
+//   dU = Aq^T dO + Kh dS_{n+1};  dR = dZ = A^T dU
+//   dS_n = gamma_C . dS_{n+1} + Qt^T dO - Et^T dR          (the reverse state scan)
+//   dEt = -dR S_n^T,  dQt = dO S_n^T,  dKh = U dS_{n+1}^T,  dgamma_C = rowsum(dS_{n+1} . S_n)
+//   dAq = tril(dO U^T),  dA = dU R^T = dU Z^T + dY Et^T (dY = -dU S_n^T),
+//   dM = -strict_tril(A^T dA A^T)
+// and through the pairwise decay: with E = e^{G_t - G_i},
+//   de_t += sum_i dM_ti k_i E,  dqs_t += sum_i dAq_ti k_i E,
+//   dk_i += sum_t (dM_ti e_t + dAq_ti qs_t) E,
+//   dG_t += e_t de^M_t + qs_t dqs^A_t - k_t dk^P_t  (+ the image terms),
+// then dg = reverse in-chunk prefix of dG, and the gates' own derivatives.
+//
+// Every quantity is float32.  The work is split over six launches:
+//   g2b_prep       per chunk: gates, images, M and Aq, A = (I + M)^{-1}
+//   g2b_fwd_scan   per (sequence, head, 32 value columns): S_n, R, U over the chunks
+//   g2b_bwd_scan   the same slices in reverse: dS_{n+1}, dU, dR; dS_0
+//   g2b_products   per chunk: dEt, dQt, dKh, dgamma_C, dAq, dM
+//   g2b_local      per (chunk, 64 key channels): pairwise decay sums, gate chain
+//   g2b_reduce     dq, dk over the value heads of a key head; dA_log over chunks
+// Decay factors never exceed 1: a product e^{G_t - G_i} over a 16-token block
+// pair below the diagonal is split at the block's first row r (i < r <= t) into
+// e^{G_t - G_r} e^{G_r - G_i}; inside a diagonal block it is either taken
+// directly or split at dyadic sub-blocks (first token of the second half).
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int C = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// acc += A(16 x K) B(K x 16), A(m, k) = a0[m * AM + k * AK], B(k, n) = b0[k * BK + n * BN]
+// (K a multiple of 4; float32 MFMA, lane l supplies A[l%16][l/16], B[l/16][l%16]).
+template <int AM, int AK, int BK, int BN>
+__device__ __forceinline__ void mma(f4 &acc, const float *a0, const float *b0, int K) {
+    const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+    const float *pa = a0 + r * AM + g * AK, *pb = b0 + g * BK + r * BN;
+    for (int k = 0; k < K; k += 4) acc = mfma_f32_k4(pa[k * AK], pb[k * BK], acc);
+}
+
+// rows x COLS float32 block (row-major, contiguous) into LDS rows of stride LS, times f
+template <int COLS, int LS>
+__device__ __forceinline__ void lds_load(float *dst, const float *__restrict__ src, int rows, float f = 1.f) {
+    for (int i = threadIdx.x; i < rows * (COLS / 4); i += blockDim.x) {
+        const int r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
+        const f4 x = *reinterpret_cast<const f4 *>(src + (size_t)r * COLS + c) * f;
+        *reinterpret_cast<f4 *>(dst + r * LS + c) = x;
+    }
+}
+
+__device__ __forceinline__ size_t unit_of(int bb, int hv, int n, int Hv, int NC) {
+    return ((size_t)bb * Hv + hv) * NC + n;
+}
+
+// ---------------------------------------------------------------------------
+// g2b_prep: one work-group of 4 waves per (sequence, value head, chunk)
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
+    constexpr int LS = DK + 4;  // conflict-free for lanes (row = l%16, col = l/16)
+    __shared__ __attribute__((aligned(16))) float sm[4 * C * LS + C];
+    float *Gs = sm, *Es = Gs + C * LS, *Qs = Es + C * LS, *Ks = Qs + C * LS, *dd = Ks + C * LS;
+    float *Ms = Es, *As = Qs, *Xt = Ks;  // after the tiles: M, A (stride 68), 4 x [16][48] scratch
+
+    const int u = blockIdx.x, NC = p.NC;
+    const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv), hk = hv / (p.Hv / p.Hk);
+    const int t0 = n * C, L = min(C, p.T - t0);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4;
+    const uint16_t *q = reinterpret_cast<const uint16_t *>(p.q), *k = reinterpret_cast<const uint16_t *>(p.k);
+    const uint16_t *a = reinterpret_cast<const uint16_t *>(p.a), *er = reinterpret_cast<const uint16_t *>(p.erase);
+    const uint16_t *v = reinterpret_cast<const uint16_t *>(p.v), *wr = reinterpret_cast<const uint16_t *>(p.write);
+
+    // 1. gates: G (log2 units, 0 past T), e = sigmoid(erase) k, qs = scale q, k; z to the workspace
+    for (int i = tid; i < C * DK / 4; i += 256) {
+        const int t = i / (DK / 4), c = (i % (DK / 4)) * 4;
+        f4 gv = {0, 0, 0, 0}, ev = gv, qv = gv, kv = gv;
+        if (t < L) {
+            const size_t kq = (((size_t)bb * p.T + t0 + t) * p.Hk + hk) * DK + c;
+            const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float kk = bf16_to_f32(k[kq + j]);
+                gv[j] = -expf(p.A_log[(size_t)hv * DK + c + j]) * softplus_f32(bf16_to_f32(a[ka + j])) * LOG2E;
+                ev[j] = sigmoid_f32(bf16_to_f32(er[ka + j])) * kk;
+                qv[j] = p.scale * bf16_to_f32(q[kq + j]);
+                kv[j] = kk;
+            }
+        }
+        *reinterpret_cast<f4 *>(Gs + t * LS + c) = gv;
+        *reinterpret_cast<f4 *>(Es + t * LS + c) = ev;
+        *reinterpret_cast<f4 *>(Qs + t * LS + c) = qv;
+        *reinterpret_cast<f4 *>(Ks + t * LS + c) = kv;
+    }
+    float *Zu = ws.Z + (size_t)u * C * DV;
+    for (int i = tid; i < C * DV / 4; i += 256) {
+        const int t = i / (DV / 4), j = (i % (DV / 4)) * 4;
+        f4 zv = {0, 0, 0, 0};
+        if (t < L) {
+            const size_t kv = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DV + j;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) zv[x] = sigmoid_f32(bf16_to_f32(wr[kv + x])) * bf16_to_f32(v[kv + x]);
+        }
+        *reinterpret_cast<f4 *>(Zu + t * DV + j) = zv;
+    }
+    __syncthreads();
+    // 2. in-chunk inclusive prefix per channel
+    for (int c = tid; c < DK; c += 256) {
+        float s = 0.f;
+        for (int t = 0; t < C; ++t) {
+            s += Gs[t * LS + c];
+            Gs[t * LS + c] = s;
+        }
+    }
+    __syncthreads();
+    // 3. images, gamma_C and the diagonal of Aq (q_t . k_t, no decay)
+    {
+        const size_t ub = (size_t)u * C * DK;
+        for (int i = tid; i < C * DK / 4; i += 256) {
+            const int t = i / (DK / 4), c = (i % (DK / 4)) * 4;
+            const f4 G = *reinterpret_cast<const f4 *>(Gs + t * LS + c);
+            const f4 GC = *reinterpret_cast<const f4 *>(Gs + (C - 1) * LS + c);
+            f4 eg, kg;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                eg[j] = exp2f(G[j]);
+                kg[j] = exp2f(GC[j] - G[j]);
+            }
+            *reinterpret_cast<f4 *>(ws.Et + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Es + t * LS + c) * eg;
+            *reinterpret_cast<f4 *>(ws.Qt + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Qs + t * LS + c) * eg;
+            *reinterpret_cast<f4 *>(ws.Kh + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Ks + t * LS + c) * kg;
+        }
+        for (int c = tid; c < DK; c += 256) ws.gC[(size_t)u * DK + c] = exp2f(Gs[(C - 1) * LS + c]);
+        if (tid < C) {
+            float s = 0.f;
+            for (int c = 0; c < DK; ++c) s += Qs[tid * LS + c] * Ks[tid * LS + c];
+            dd[tid] = s;
+        }
+    }
+    __syncthreads();
+    // 4. M and Aq.  Tiles below the diagonal (bt > bi), reference row r = 16 bt:
+    //    sum_c [e_t e^{G_t - G_r}] [k_i e^{G_r - G_i}].  Wave w takes tiles w, w + 4.
+    constexpr int OBT[6] = {1, 2, 2, 3, 3, 3}, OBI[6] = {0, 0, 1, 0, 1, 2};
+    f4 mO[2], qO[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        mO[x] = qO[x] = f4{0, 0, 0, 0};
+        const int ti = w + 4 * x;
+        if (ti < 6) {
+            const int bt = OBT[ti], bi = OBI[ti], r = 16 * bt, t = 16 * bt + rr, i = 16 * bi + rr;
+            for (int c0 = 0; c0 < DK; c0 += 4) {
+                const int c = c0 + gg;
+                const float Gr = Gs[r * LS + c];
+                const float ft = exp2f(Gs[t * LS + c] - Gr), b = Ks[i * LS + c] * exp2f(Gr - Gs[i * LS + c]);
+                mO[x] = mfma_f32_k4(Es[t * LS + c] * ft, b, mO[x]);
+                qO[x] = mfma_f32_k4(Qs[t * LS + c] * ft, b, qO[x]);
+            }
+        }
+    }
+    //    Diagonal tile w: dyadic levels (half sizes 8, 4, 2, 1); a pair (t > i) of
+    //    the tile belongs to the level whose 2h-block holds both with i in the
+    //    first and t in the second half; reference = first token of that half.
+    f4 mD = {0, 0, 0, 0}, qD = {0, 0, 0, 0};
+    {
+        const int base = 16 * w, t = base + rr, i = base + rr;
+#pragma unroll
+        for (int h = 8; h >= 1; h >>= 1) {
+            const bool tsec = (rr & h) != 0;
+            const int rt = base + (rr & ~(h - 1)), ri = base + ((rr | h) & ~(h - 1));
+            f4 aM = {0, 0, 0, 0}, aQ = {0, 0, 0, 0};
+            for (int c0 = 0; c0 < DK; c0 += 4) {
+                const int c = c0 + gg;
+                float ae = 0.f, aq = 0.f, b = 0.f;
+                if (tsec) {
+                    const float ft = exp2f(Gs[t * LS + c] - Gs[rt * LS + c]);
+                    ae = Es[t * LS + c] * ft;
+                    aq = Qs[t * LS + c] * ft;
+                } else {
+                    b = Ks[i * LS + c] * exp2f(Gs[ri * LS + c] - Gs[i * LS + c]);
+                }
+                aM = mfma_f32_k4(ae, b, aM);
+                aQ = mfma_f32_k4(aq, b, aQ);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int tl = 4 * gg + s;
+                if (((tl ^ rr) & ~(2 * h - 1)) == 0 && (tl & h) && !(rr & h)) {
+                    mD[s] += aM[s];
+                    qD[s] += aQ[s];
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            if (4 * gg + s == rr) qD[s] += dd[base + rr];
+    }
+    __syncthreads();  // Es, Qs, Ks are reused below
+    // Aq to the workspace (zero above the diagonal); M into LDS (zero on and above)
+    {
+        float *Aqu = ws.Aq + (size_t)u * C * C;
+        for (int i = tid; i < C * 68; i += 256) Ms[i] = 0.f;
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int ti = w + 4 * x;
+            if (ti < 6) {
+                const int bt = OBT[ti], bi = OBI[ti];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int t = 16 * bt + 4 * gg + s, i = 16 * bi + rr;
+                    Ms[t * 68 + i] = mO[x][s];
+                    Aqu[t * C + i] = qO[x][s];
+                    Aqu[i * C + t] = 0.f;  // the mirrored tile above the diagonal
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int t = 16 * w + 4 * gg + s, i = 16 * w + rr;
+            Ms[t * 68 + i] = mD[s];
+            Aqu[t * C + i] = qD[s];
+        }
+    }
+    __syncthreads();
+    // 5. A = (I + M)^{-1}: diagonal 16 x 16 blocks by forward substitution (wave w,
+    //    lane j < 16 owns column j of block w), then block rows 1..3:
+    //    A_bj = -A_bb sum_{m=j}^{b-1} M_bm A_mj.
+    if (lane < 16) {
+        const int base = 16 * w, j = lane;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float s = (t == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < t; ++i) s -= Ms[(base + t) * 68 + base + i] * x[i];
+            x[t] = s;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) As[(base + t) * 68 + base + j] = x[t];
+    }
+    // zero the blocks above the diagonal of A
+    for (int i = tid; i < C * C; i += 256) {
+        const int t = i / C, c = i % C;
+        if ((c >> 4) > (t >> 4)) As[t * 68 + c] = 0.f;
+    }
+    __syncthreads();
+    for (int b = 1; b < 4; ++b) {
+        if (w < b) {
+            f4 X = {0, 0, 0, 0};
+            for (int m = w; m < b; ++m) mma<68, 1, 68, 1>(X, Ms + 16 * b * 68 + 16 * m, As + 16 * m * 68 + 16 * w, 16);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Xt[w * 16 * 48 + (4 * gg + s) * 48 + rr] = X[s];
+        }
+        __syncthreads();
+        if (w < b) {
+            f4 Y = {0, 0, 0, 0};
+            mma<68, 1, 48, 1>(Y, As + 16 * b * 68 + 16 * b, Xt + w * 16 * 48, 16);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) As[(16 * b + 4 * gg + s) * 68 + 16 * w + rr] = -Y[s];
+        }
+        __syncthreads();
+    }
+    float *Au = ws.A + (size_t)u * C * C;
+    for (int i = tid; i < C * C / 4; i += 256) {
+        const int t = i / (C / 4), c = (i % (C / 4)) * 4;
+        *reinterpret_cast<f4 *>(Au + t * C + c) = *reinterpret_cast<const f4 *>(As + t * 68 + c);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// g2b_fwd_scan: one work-group per (sequence, value head, 32 value columns);
+// wave w holds the state tiles (c-blocks 2w', j-blocks) as MFMA accumulators.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws) {
+    constexpr int LE = DK + 4, LK = DK + 16, LA = 68, LB = 48, NS = DV / 32, NT = DK / 32;
+    __shared__ __attribute__((aligned(16))) float Ets[C * LE], Khs[C * LK], As[C * LA], Ss[DK * LB], Rs[C * LB],
+        Us[C * LB];
+    const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
+    f4 S[NT];
+#pragma unroll
+    for (int x = 0; x < NT; ++x) {
+        const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c = 16 * cb + 4 * gg + s, j = 16 * jb + rr;
+            S[x][s] = p.S0 ? p.S0[(((size_t)bb * p.Hv + hv) * DK + c) * DV + j0 + j] : 0.f;
+            Ss[c * LB + j] = S[x][s];
+        }
+    }
+    for (int n = 0; n < NC; ++n) {
+        const size_t u = unit_of(bb, hv, n, p.Hv, NC);
+        float *Snu = ws.Sn + u * DK * DV;
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Snu[(16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = S[x][s];
+        }
+        lds_load<DK, LE>(Ets, ws.Et + u * C * DK, C);
+        lds_load<DK, LK>(Khs, ws.Kh + u * C * DK, C);
+        lds_load<C, LA>(As, ws.A + u * C * C, C);
+        __syncthreads();
+        // R = Z - Et S (rows of block w)
+        const float *Zu = ws.Z + u * C * DV;
+        float *Ru = ws.R + u * C * DV, *Uu = ws.U + u * C * DV;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            f4 acc = {0, 0, 0, 0};
+            mma<LE, 1, LB, 1>(acc, Ets + 16 * w * LE, Ss + 16 * jb, DK);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
+                const float rv = Zu[t * DV + j0 + j] - acc[s];
+                Rs[t * LB + j] = rv;
+                Ru[t * DV + j0 + j] = rv;
+            }
+        }
+        __syncthreads();
+        // U = A R (A lower triangular: columns up to the block's last row)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            f4 acc = {0, 0, 0, 0};
+            mma<LA, 1, LB, 1>(acc, As + 16 * w * LA, Rs + 16 * jb, 16 * (w + 1));
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
+                Us[t * LB + j] = acc[s];
+                Uu[t * DV + j0 + j] = acc[s];
+            }
+        }
+        __syncthreads();
+        // S = gamma_C . S + Kh^T U
+        const float *gCu = ws.gC + u * DK;
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) S[x][s] *= gCu[16 * cb + 4 * gg + s];
+            mma<1, LK, LB, 1>(S[x], Khs + 16 * cb, Us + 16 * jb, C);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Ss[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = S[x][s];
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// g2b_bwd_scan: the same slices, chunks in reverse; dS in MFMA accumulators.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws) {
+    constexpr int LQ = 80, LKA = DK + 4, LKB = DK + 16, LB = 48, NS = DV / 32, NT = DK / 32;
+    __shared__ __attribute__((aligned(16))) float bA[C * LQ], bK[C * LKB], Os[C * LB], dSs[DK * LB], dUs[C * LB],
+        dRs[C * LB];
+    const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
+    const uint16_t *dout = reinterpret_cast<const uint16_t *>(p.dout);
+    f4 dS[NT];
+#pragma unroll
+    for (int x = 0; x < NT; ++x) {
+        const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c = 16 * cb + 4 * gg + s, j = 16 * jb + rr;
+            dS[x][s] = p.dST ? p.dST[(((size_t)bb * p.Hv + hv) * DK + c) * DV + j0 + j] : 0.f;
+            dSs[c * LB + j] = dS[x][s];
+        }
+    }
+    for (int n = NC - 1; n >= 0; --n) {
+        const size_t u = unit_of(bb, hv, n, p.Hv, NC);
+        const int t0 = n * C, L = min(C, p.T - t0);
+        float *dS1u = ws.dS1 + u * DK * DV;
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) dS1u[(16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = dS[x][s];
+        }
+        lds_load<C, LQ>(bA, ws.Aq + u * C * C, C);
+        lds_load<DK, LKA>(bK, ws.Kh + u * C * DK, C);
+        for (int i = tid; i < C * 32; i += 256) {
+            const int t = i >> 5, j = i & 31;
+            Os[t * LB + j] = t < L ? bf16_to_f32(dout[(((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DV + j0 + j]) : 0.f;
+        }
+        __syncthreads();
+        // dU = Aq^T dO + Kh dS  (Aq[i][t] vanishes for i < t)
+        float *dUu = ws.dU + u * C * DV, *dRu = ws.dR + u * C * DV;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            f4 acc = {0, 0, 0, 0};
+            mma<1, LQ, LB, 1>(acc, bA + 16 * w * LQ + 16 * w, Os + 16 * w * LB + 16 * jb, C - 16 * w);
+            mma<LKA, 1, LB, 1>(acc, bK + 16 * w * LKA, dSs + 16 * jb, DK);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
+                dUs[t * LB + j] = acc[s];
+                dUu[t * DV + j0 + j] = acc[s];
+            }
+        }
+        __syncthreads();
+        lds_load<C, LQ>(bA, ws.A + u * C * C, C);
+        lds_load<DK, LKB>(bK, ws.Qt + u * C * DK, C);
+        __syncthreads();
+        // dR = A^T dU;  dS = gamma_C . dS + Qt^T dO
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            f4 acc = {0, 0, 0, 0};
+            mma<1, LQ, LB, 1>(acc, bA + 16 * w * LQ + 16 * w, dUs + 16 * w * LB + 16 * jb, C - 16 * w);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
+                dRs[t * LB + j] = acc[s];
+                dRu[t * DV + j0 + j] = acc[s];
+            }
+        }
+        const float *gCu = ws.gC + u * DK;
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) dS[x][s] *= gCu[16 * cb + 4 * gg + s];
+            mma<1, LKB, LB, 1>(dS[x], bK + 16 * cb, Os + 16 * jb, C);
+        }
+        __syncthreads();
+        lds_load<DK, LKB>(bK, ws.Et + u * C * DK, C, -1.f);
+        __syncthreads();
+        // dS -= Et^T dR
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+            mma<1, LKB, LB, 1>(dS[x], bK + 16 * cb, dRs + 16 * jb, C);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) dSs[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = dS[x][s];
+        }
+        __syncthreads();
+    }
+    if (p.dS0) {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                p.dS0[(((size_t)bb * p.Hv + hv) * DK + 16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = dS[x][s];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// g2b_products: one work-group per chunk.  Wave w owns the rows of block w.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws) {
+    constexpr int LV = DV + 4, R1 = (DK * LV > 2 * C * 80) ? DK * LV : 2 * C * 80;
+    __shared__ __attribute__((aligned(16))) float r1[R1], b1[C * LV], b2[C * LV];
+    const int u = blockIdx.x, NC = p.NC;
+    const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv);
+    const int t0 = n * C, L = min(C, p.T - t0);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4;
+    const size_t uC = (size_t)u * C;
+    const uint16_t *dout = reinterpret_cast<const uint16_t *>(p.dout);
+
+    // phase 1: dEt = -dR Sn^T, dQt = dO Sn^T, dgamma_C = rowsum(dS1 . Sn)
+    lds_load<DV, LV>(r1, ws.Sn + (size_t)u * DK * DV, DK);
+    lds_load<DV, LV>(b1, ws.dR + uC * DV, C, -1.f);
+    for (int i = tid; i < C * DV; i += 256) {
+        const int t = i / DV, j = i % DV;
+        b2[t * LV + j] = t < L ? bf16_to_f32(dout[(((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DV + j]) : 0.f;
+    }
+    __syncthreads();
+    for (int cb = 0; cb < DK / 16; ++cb) {
+        f4 e = {0, 0, 0, 0}, q = {0, 0, 0, 0};
+        mma<LV, 1, 1, LV>(e, b1 + 16 * w * LV, r1 + 16 * cb * LV, DV);
+        mma<LV, 1, 1, LV>(q, b2 + 16 * w * LV, r1 + 16 * cb * LV, DV);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const size_t o = (uC + 16 * w + 4 * gg + s) * DK + 16 * cb + rr;
+            ws.dEt[o] = e[s];
+            ws.dQt[o] = q[s];
+        }
+    }
+    if (tid < 2 * DK) {
+        const int c = tid >> 1, h = tid & 1;
+        const float *d1 = ws.dS1 + ((size_t)u * DK + c) * DV;
+        float s = 0.f;
+        for (int j = h * (DV / 2); j < (h + 1) * (DV / 2); ++j) s += d1[j] * r1[c * LV + j];
+        s += __shfl_xor(s, 1);
+        if (!h) ws.dgC[(size_t)u * DK + c] = s;
+    }
+    __syncthreads();
+    // phase 2: dKh = U dS1^T, dAq = tril(dO U^T)
+    lds_load<DV, LV>(r1, ws.dS1 + (size_t)u * DK * DV, DK);
+    lds_load<DV, LV>(b1, ws.U + uC * DV, C);
+    __syncthreads();
+    for (int cb = 0; cb < DK / 16; ++cb) {
+        f4 acc = {0, 0, 0, 0};
+        mma<LV, 1, 1, LV>(acc, b1 + 16 * w * LV, r1 + 16 * cb * LV, DV);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ws.dKh[(uC + 16 * w + 4 * gg + s) * DK + 16 * cb + rr] = acc[s];
+    }
+    float *dAqu = ws.dAq + uC * C;
+    for (int ib = 0; ib < 4; ++ib) {
+        f4 acc = {0, 0, 0, 0};
+        if (ib <= w) mma<LV, 1, 1, LV>(acc, b2 + 16 * w * LV, b1 + 16 * ib * LV, DV);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int t = 16 * w + 4 * gg + s, i = 16 * ib + rr;
+            dAqu[t * C + i] = i <= t ? acc[s] : 0.f;
+        }
+    }
+    __syncthreads();
+    // phase 3: dA = dU R^T; X = A^T dA; dM = -strict_tril(X A^T)
+    float *dAs = r1, *A80 = r1 + C * 80, *A68 = b1, *Xs = b2;
+    lds_load<DV, LV>(b1, ws.R + uC * DV, C);
+    lds_load<DV, LV>(b2, ws.dU + uC * DV, C);
+    lds_load<C, 80>(A80, ws.A + uC * C, C);
+    __syncthreads();
+    f4 dA[4];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+        dA[ib] = f4{0, 0, 0, 0};
+        mma<LV, 1, 1, LV>(dA[ib], b2 + 16 * w * LV, b1 + 16 * ib * LV, DV);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) dAs[(16 * w + 4 * gg + s) * 80 + 16 * ib + rr] = dA[ib][s];
+    lds_load<C, 68>(A68, ws.A + uC * C, C);
+    __syncthreads();
+    // X[i][s] = sum_{t >= i} A[t][i] dA[t][s]: rows i of block w
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+        f4 acc = {0, 0, 0, 0};
+        mma<1, 80, 80, 1>(acc, A80 + 16 * w * 80 + 16 * w, dAs + 16 * w * 80 + 16 * sb, C - 16 * w);
+        dA[sb] = acc;  // reuse the registers for X
+    }
+    __syncthreads();  // Xs aliases b2, read by nobody now; A68 stays
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Xs[(16 * w + 4 * gg + s) * 68 + 16 * sb + rr] = dA[sb][s];
+    __syncthreads();
+    // dM[i][q] = -sum_{s <= q} X[i][s] A[q][s], strictly lower
+    float *dMu = ws.dM + uC * C;
+    for (int qb = 0; qb < 4; ++qb) {
+        f4 acc = {0, 0, 0, 0};
+        if (qb <= w) mma<68, 1, 1, 68>(acc, Xs + 16 * w * 68, A68 + 16 * qb * 68, 16 * (qb + 1));
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int i = 16 * w + 4 * gg + s, qq = 16 * qb + rr;
+            dMu[i * C + qq] = qq < i ? -acc[s] : 0.f;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// g2b_local: one work-group per (chunk, 64 key channels); lane = channel.
+// Waves 0/1: sums over i for rows t of blocks {0,3}/{1,2} (de, dqs);
+// waves 2/3: sums over t for rows i of blocks {0,3}/{1,2} (dk).  Then each wave
+// applies the chain rule to the rows of its block.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
+    constexpr int CG = DK / 64;
+    __shared__ __attribute__((aligned(16))) float Gs[C * 64], Ks[C * 64], Es[C * 64], Qs[C * 64], dMs[C * C],
+        dAqs[C * C], Te[C * 64], Tq[C * 64], Ik[C * 64], blk[4 * 64], gcp[4 * 64], alp[4 * 64];
+    const int cg = blockIdx.x % CG, u = blockIdx.x / CG, NC = p.NC;
+    const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv), hk = hv / (p.Hv / p.Hk);
+    const int t0 = n * C, L = min(C, p.T - t0);
+    const int tid = threadIdx.x, w = tid >> 6, cl = tid & 63, c = 64 * cg + cl;
+    const uint16_t *q = reinterpret_cast<const uint16_t *>(p.q), *k = reinterpret_cast<const uint16_t *>(p.k);
+    const uint16_t *a = reinterpret_cast<const uint16_t *>(p.a), *er = reinterpret_cast<const uint16_t *>(p.erase);
+    const float Al = p.A_log[(size_t)hv * DK + c], rate = expf(Al);
+
+    for (int tt = 0; tt < 16; ++tt) {
+        const int t = 16 * w + tt;
+        float gv = 0.f, ev = 0.f, qv = 0.f, kv = 0.f;
+        if (t < L) {
+            const size_t kq = (((size_t)bb * p.T + t0 + t) * p.Hk + hk) * DK + c;
+            const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
+            kv = bf16_to_f32(k[kq]);
+            gv = -rate * softplus_f32(bf16_to_f32(a[ka])) * LOG2E;
+            ev = sigmoid_f32(bf16_to_f32(er[ka])) * kv;
+            qv = p.scale * bf16_to_f32(q[kq]);
+        }
+        Gs[t * 64 + cl] = gv;
+        Ks[t * 64 + cl] = kv;
+        Es[t * 64 + cl] = ev;
+        Qs[t * 64 + cl] = qv;
+    }
+    lds_load<C, C>(dMs, ws.dM + (size_t)u * C * C, C);
+    lds_load<C, C>(dAqs, ws.dAq + (size_t)u * C * C, C);
+    __syncthreads();
+    if (w == 0) {
+        float s = 0.f;
+        for (int t = 0; t < C; ++t) {
+            s += Gs[t * 64 + cl];
+            Gs[t * 64 + cl] = s;
+        }
+    }
+    __syncthreads();
+
+    if (w < 2) {
+        // sums over i for the rows t of block bt
+        for (int pass = 0; pass < 2; ++pass) {
+            const int bt = w == 0 ? (pass ? 3 : 0) : (pass ? 2 : 1);
+            float de[16], dq[16];
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) de[tt] = dq[tt] = 0.f;
+            if (bt > 0) {
+                const int r = 16 * bt;
+                const float Gr = Gs[r * 64 + cl];
+                for (int i = 0; i < r; ++i) {
+                    const float kt = Ks[i * 64 + cl] * exp2f(Gr - Gs[i * 64 + cl]);
+#pragma unroll
+                    for (int tt = 0; tt < 16; ++tt) {
+                        de[tt] += dMs[(r + tt) * C + i] * kt;
+                        dq[tt] += dAqs[(r + tt) * C + i] * kt;
+                    }
+                }
+#pragma unroll
+                for (int tt = 0; tt < 16; ++tt) {
+                    const float F = exp2f(Gs[(r + tt) * 64 + cl] - Gr);
+                    de[tt] *= F;
+                    dq[tt] *= F;
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) {
+                const int t = 16 * bt + tt;
+                const float Gt = Gs[t * 64 + cl];
+#pragma unroll
+                for (int ii = 0; ii <= tt; ++ii) {
+                    const int i = 16 * bt + ii;
+                    const float kE = Ks[i * 64 + cl] * exp2f(Gt - Gs[i * 64 + cl]);
+                    if (ii < tt) de[tt] += dMs[t * C + i] * kE;
+                    dq[tt] += dAqs[t * C + i] * kE;
+                }
+                Te[t * 64 + cl] = de[tt];
+                Tq[t * 64 + cl] = dq[tt];
+            }
+        }
+    } else {
+        // sums over t for the rows i of block bi
+        for (int pass = 0; pass < 2; ++pass) {
+            const int bi = w == 2 ? (pass ? 3 : 0) : (pass ? 2 : 1);
+            float dk[16];
+#pragma unroll
+            for (int ii = 0; ii < 16; ++ii) dk[ii] = 0.f;
+            for (int bt = bi + 1; bt < 4; ++bt) {
+                const int r = 16 * bt;
+                const float Gr = Gs[r * 64 + cl];
+                float tmp[16];
+#pragma unroll
+                for (int ii = 0; ii < 16; ++ii) tmp[ii] = 0.f;
+                for (int tt = 0; tt < 16; ++tt) {
+                    const int t = r + tt;
+                    const float F = exp2f(Gs[t * 64 + cl] - Gr);
+                    const float et = Es[t * 64 + cl] * F, qt = Qs[t * 64 + cl] * F;
+#pragma unroll
+                    for (int ii = 0; ii < 16; ++ii)
+                        tmp[ii] += dMs[t * C + 16 * bi + ii] * et + dAqs[t * C + 16 * bi + ii] * qt;
+                }
+#pragma unroll
+                for (int ii = 0; ii < 16; ++ii) dk[ii] += exp2f(Gr - Gs[(16 * bi + ii) * 64 + cl]) * tmp[ii];
+            }
+#pragma unroll
+            for (int ii = 0; ii < 16; ++ii) {
+                const int i = 16 * bi + ii;
+                const float Gi = Gs[i * 64 + cl];
+#pragma unroll
+                for (int tt = ii; tt < 16; ++tt) {
+                    const int t = 16 * bi + tt;
+                    const float E = exp2f(Gs[t * 64 + cl] - Gi);
+                    float x = dAqs[t * C + i] * Qs[t * 64 + cl];
+                    if (tt > ii) x += dMs[t * C + i] * Es[t * 64 + cl];
+                    dk[ii] += x * E;
+                }
+                Ik[i * 64 + cl] = dk[ii];
+            }
+        }
+    }
+    __syncthreads();
+
+    // chain rule for the rows of block w
+    const size_t ub = (size_t)u * C * DK;
+    const float GC = Gs[(C - 1) * 64 + cl];
+    float dG[16], de[16], dq[16], dk[16], sKK = 0.f, bsum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+        const int t = 16 * w + tt;
+        const float G = Gs[t * 64 + cl], eg = exp2f(G), kg = exp2f(GC - G);
+        const float dEt = ws.dEt[ub + t * DK + c], dQt = ws.dQt[ub + t * DK + c], dKh = ws.dKh[ub + t * DK + c];
+        const float e = Es[t * 64 + cl], qs = Qs[t * 64 + cl], kk = Ks[t * 64 + cl];
+        const float te = Te[t * 64 + cl], tq = Tq[t * 64 + cl], ik = Ik[t * 64 + cl];
+        de[tt] = eg * dEt + te;
+        dq[tt] = eg * dQt + tq;
+        dk[tt] = kg * dKh + ik;
+        const float khv = kk * kg;
+        dG[tt] = dEt * (e * eg) + dQt * (qs * eg) - dKh * khv + e * te + qs * tq - kk * ik;
+        sKK += dKh * khv;
+        bsum += dG[tt];
+    }
+    blk[w * 64 + cl] = bsum;
+    gcp[w * 64 + cl] = sKK;
+    __syncthreads();
+    float carry = gcp[cl] + gcp[64 + cl] + gcp[128 + cl] + gcp[192 + cl] + ws.dgC[(size_t)u * DK + c] * exp2f(GC);
+    for (int x = w + 1; x < 4; ++x) carry += blk[x * 64 + cl];
+    float alsum = 0.f;
+#pragma unroll
+    for (int tt = 15; tt >= 0; --tt) {
+        carry += dG[tt];
+        const int t = 16 * w + tt;
+        if (t < L) {
+            const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
+            const float av = bf16_to_f32(a[ka]), beta = sigmoid_f32(bf16_to_f32(er[ka]));
+            const float kk = Ks[t * 64 + cl];
+            const float dg = carry;  // natural-log units
+            p.da[ka] = -dg * rate * sigmoid_f32(av);
+            alsum += dg * (-rate * softplus_f32(av));
+            p.derase[ka] = de[tt] * kk * beta * (1.f - beta);
+            ws.dqh[ka] = p.scale * dq[tt];
+            ws.dkh[ka] = dk[tt] + de[tt] * beta;
+        }
+    }
+    alp[w * 64 + cl] = alsum;
+    __syncthreads();
+    if (w == 0) ws.dAl[(size_t)u * DK + c] = alp[cl] + alp[64 + cl] + alp[128 + cl] + alp[192 + cl];
+    // dz = dR -> dv, d_write (the first channel group of each chunk)
+    if (cg == 0) {
+        const uint16_t *v = reinterpret_cast<const uint16_t *>(p.v), *wr = reinterpret_cast<const uint16_t *>(p.write);
+        const float *dRu = ws.dR + (size_t)u * C * DV;
+        for (int i = tid; i < L * DV; i += 256) {
+            const int t = i / DV, j = i % DV;
+            const size_t kv = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DV + j;
+            const float dz = dRu[t * DV + j], om = sigmoid_f32(bf16_to_f32(wr[kv])), vv = bf16_to_f32(v[kv]);
+            p.dv[kv] = dz * om;
+            p.dwrite[kv] = dz * vv * om * (1.f - om);
+        }
+    }
+}
+
+// dq, dk: sums over the value heads of each key head; dA_log: sums over chunks.
+template <int DK>
+__global__ __launch_bounds__(256) void g2b_reduce(Bwd2Args p, Bwd2Workspace ws) {
+    const int grp = p.Hv / p.Hk;
+    const size_t nq = (size_t)p.B * p.T * p.Hk * DK;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nq; i += (size_t)gridDim.x * 256) {
+        const int c = i % DK;
+        const size_t row = i / DK;  // (b, t, hk)
+        const int hk = row % p.Hk;
+        const size_t bt = row / p.Hk;
+        float sq = 0.f, sk = 0.f;
+        for (int x = 0; x < grp; ++x) {
+            const size_t o = (bt * p.Hv + (size_t)hk * grp + x) * DK + c;
+            sq += ws.dqh[o];
+            sk += ws.dkh[o];
+        }
+        p.dq[i] = sq;
+        p.dk[i] = sk;
+    }
+    const size_t na = (size_t)p.Hv * DK;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < na; i += (size_t)gridDim.x * 256) {
+        const int hv = i / DK, c = i % DK;
+        float s = 0.f;
+        for (int bb = 0; bb < p.B; ++bb)
+            for (int n = 0; n < p.NC; ++n) s += ws.dAl[unit_of(bb, hv, n, p.Hv, p.NC) * DK + c];
+        p.dA_log[i] = s;
+    }
+}
+
+// T = 0: dS0 = dS_T (or 0), dA_log = 0
+__global__ void g2b_empty(float *dS0, const float *dST, size_t ns, float *dA_log, size_t na) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < ns + na; i += (size_t)gridDim.x * blockDim.x) {
+        if (i < ns) {
+            if (dS0) dS0[i] = dST ? dST[i] : 0.f;
+        } else {
+            dA_log[i - ns] = 0.f;
+        }
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t s, const hipEvent_t *ev) {
+    const unsigned units = (unsigned)(p.B * p.Hv * p.NC), slices = (unsigned)(p.B * p.Hv * (DV / 32));
+    hipError_t e = hipSuccess;
+    auto rec = [&](int i) {
+        if (ev && e == hipSuccess) e = hipEventRecord(ev[i], s);
+    };
+    rec(0);
+    hipLaunchKernelGGL((g2b_prep<DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
+    rec(1);
+    hipLaunchKernelGGL((g2b_fwd_scan<DK, DV>), dim3(slices), dim3(256), 0, s, p, ws);
+    rec(2);
+    hipLaunchKernelGGL((g2b_bwd_scan<DK, DV>), dim3(slices), dim3(256), 0, s, p, ws);
+    rec(3);
+    hipLaunchKernelGGL((g2b_products<DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
+    rec(4);
+    hipLaunchKernelGGL((g2b_local<DK, DV>), dim3(units * (DK / 64)), dim3(256), 0, s, p, ws);
+    rec(5);
+    const size_t nq = (size_t)p.B * p.T * p.Hk * DK / 256 + 1;
+    hipLaunchKernelGGL((g2b_reduce<DK>), dim3((unsigned)(nq < 65536 ? nq : 65536)), dim3(256), 0, s, p, ws);
+    rec(6);
+    const hipError_t le = hipGetLastError();
+    return le != hipSuccess ? le : e;
+}
+
+}  // namespace
+
+size_t bwd2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, Bwd2Workspace *ws) {
+    const size_t NC = ((size_t)T + C - 1) / C, U = (size_t)B * Hv * NC;
+    size_t off = 0;
+    auto take = [&](float **dst, size_t elems) {
+        if (dst) *dst = base ? reinterpret_cast<float *>(static_cast<char *>(base) + off) : nullptr;
+        off += (elems * 4 + 255) / 256 * 256;
+    };
+    Bwd2Workspace w{};
+    take(&w.A, U * C * C);
+    take(&w.Aq, U * C * C);
+    take(&w.Et, U * C * Dk);
+    take(&w.Qt, U * C * Dk);
+    take(&w.Kh, U * C * Dk);
+    take(&w.gC, U * Dk);
+    take(&w.Z, U * C * Dv);
+    take(&w.U, U * C * Dv);
+    take(&w.R, U * C * Dv);
+    take(&w.dU, U * C * Dv);
+    take(&w.dR, U * C * Dv);
+    take(&w.Sn, U * Dk * Dv);
+    take(&w.dS1, U * Dk * Dv);
+    take(&w.dEt, U * C * Dk);
+    take(&w.dQt, U * C * Dk);
+    take(&w.dKh, U * C * Dk);
+    take(&w.dgC, U * Dk);
+    take(&w.dM, U * C * C);
+    take(&w.dAq, U * C * C);
+    take(&w.dqh, (size_t)B * T * Hv * Dk);
+    take(&w.dkh, (size_t)B * T * Hv * Dk);
+    take(&w.dAl, U * Dk);
+    w.bytes = off;
+    if (ws) *ws = w;
+    return off;
+}
+
+hipError_t launch_bwd2(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t s, const hipEvent_t *ev) {
+    if (p.B == 0) return hipSuccess;
+    if (p.T == 0) {
+        const size_t ns = (size_t)p.B * p.Hv * p.Dk * p.Dv, na = (size_t)p.Hv * p.Dk;
+        hipLaunchKernelGGL(g2b_empty, dim3((unsigned)((ns + na) / 256 + 1 < 65536 ? (ns + na) / 256 + 1 : 65536)),
+                           dim3(256), 0, s, p.dS0, p.dST, ns, p.dA_log, na);
+        return hipGetLastError();
+    }
+    if (p.Dk == 128 && p.Dv == 128) return launch_bwd2_t<128, 128>(p, ws, s, ev);
+    if (p.Dk == 128 && p.Dv == 64) return launch_bwd2_t<128, 64>(p, ws, s, ev);
+    if (p.Dk == 64 && p.Dv == 128) return launch_bwd2_t<64, 128>(p, ws, s, ev);
+    if (p.Dk == 64 && p.Dv == 64) return launch_bwd2_t<64, 64>(p, ws, s, ev);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -67,6 +67,37 @@ struct Gdn2Args {
 hipError_t launch_chunk_local2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s);
 hipError_t launch_state_scan2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s);
 
+// Gradient of the Gated DeltaNet-2 chunked forward (bwd2.hip).  Float32
+// workspace, per (sequence, value head, chunk) unit u unless noted.
+struct Bwd2Workspace {
+    float *A, *Aq;                 // [U][64][64]: (I + M)^{-1}; A_qk (scale folded into q)
+    float *Et, *Qt, *Kh;           // [U][64][Dk]: e^{G} e, e^{G} scale q, e^{G_C - G} k
+    float *gC;                     // [U][Dk]: e^{G_C}
+    float *Z, *U, *R, *dU, *dR;    // [U][64][Dv]
+    float *Sn, *dS1;               // [U][Dk][Dv]: state before the chunk; its gradient after
+    float *dEt, *dQt, *dKh;        // [U][64][Dk]
+    float *dgC;                    // [U][Dk]
+    float *dM, *dAq;               // [U][64][64]
+    float *dqh, *dkh;              // [B][T][Hv][Dk]: per value head, summed per key head later
+    float *dAl;                    // [U][Dk]: per-chunk part of dA_log
+    size_t bytes;
+};
+
+size_t bwd2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, Bwd2Workspace *ws);
+
+struct Bwd2Args {
+    int B, T, Hk, Hv, Dk, Dv, NC;
+    float scale;
+    const void *q, *k, *v, *a, *erase, *write;  // bfloat16
+    const float *A_log, *S0;
+    const void *dout;                            // bfloat16 [B,T,Hv,Dv]
+    const float *dST;                            // [B,Hv,Dk,Dv] or null
+    float *dq, *dk, *dv, *da, *derase, *dwrite, *dA_log, *dS0;
+};
+
+// ev: null, or 7 events recorded before each of the six launches and after the last
+hipError_t launch_bwd2(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t s, const hipEvent_t *ev);
+
 // One recurrent step.  The scalar decay (gdn2 = false): a, b [B,H_v] float32,
 // A_log, dt_bias [H_v].  The channel-wise decay (gdn2 = true): a, b = erase
 // [B,H_v,d_k] and write [B,H_v,d_v] in the input type, A_log [H_v,d_k].

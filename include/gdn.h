@@ -138,6 +138,53 @@ gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const
                           const float *initial_state, void *out, float *final_state, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* Gradient of gdn2_chunk_fwd (zhichai.net "Gated DeltaNet-2" digest, section
+ * "Gate-aware 反向传播": the backward of the chunked WY form, with the erase and
+ * write gates kept at each token where the products accumulate, i.e. the
+ * gradient of A = (I + tril(Ebar Kbar^T, -1))^{-1} collects dU Z^T and dY Ebar^T).
+ * Computes the vector-Jacobian products of (out, final_state) with
+ * (d_out, d_final_state) for the same inputs as gdn2_chunk_fwd:
+ *   d_out           [B,T,Hv,Dv] bfloat16 gradient of out
+ *   d_final_state   [B,Hv,Dk,Dv] float32 gradient of final_state, or NULL (zero)
+ *   dq, dk          [B,T,Hk,Dk] float32 (written): summed over the Hv/Hk value
+ *                   heads that share a key head
+ *   dv, d_write     [B,T,Hv,Dv] float32 (written)
+ *   da, d_erase     [B,T,Hv,Dk] float32 (written)
+ *   dA_log          [Hv,Dk] float32 (written): summed over sequences and tokens
+ *   d_initial_state [B,Hv,Dk,Dv] float32 (written), or NULL to skip it
+ *   workspace       device scratch of at least gdn2_chunk_bwd_workspace_bytes(d)
+ *                   bytes, 256-byte aligned (about 0.6 MB per (sequence, value
+ *                   head, 64 tokens) at Dk = Dv = 128: the forward is recomputed
+ *                   in float32 and its per-chunk states are kept).
+ * All arithmetic is float32.  d->dtype must be GDN_BF16.  No output may overlap
+ * any input, the workspace or another output (GDN_ERR_ALIAS).  Deterministic
+ * (no atomics).  Asynchronous on `stream`; nothing is enqueued on an error. */
+size_t gdn2_chunk_bwd_workspace_bytes(const gdn_dims *d);
+gdn_status gdn2_chunk_bwd(const gdn_dims *d, const void *q, const void *k, const void *v,
+                          const void *a, const float *A_log, const void *erase,
+                          const void *write, const float *initial_state, const void *d_out,
+                          const float *d_final_state, float *dq, float *dk, float *dv,
+                          float *da, float *d_erase, float *d_write, float *dA_log,
+                          float *d_initial_state, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* gdn2_chunk_bwd, plus timing events: stage_events is NULL or points to
+ * GDN2_CHUNK_BWD_STAGES + 1 hipEvent_t handles; event i is recorded on `stream`
+ * before stage i and the last after the final stage (none are recorded when
+ * T = 0).  Stages: 0 gates, decay images, M, A_qk and A = (I + M)^{-1};
+ * 1 float32 forward state scan keeping each chunk's state; 2 reverse state
+ * scan of the state gradient; 3 per-chunk products (dEt, dQt, dKh, dA_qk, dM);
+ * 4 pairwise decay sums and the gate chain rule; 5 sums over value heads
+ * (dq, dk) and chunks (dA_log). */
+#define GDN2_CHUNK_BWD_STAGES 6
+gdn_status gdn2_chunk_bwd_timed(const gdn_dims *d, const void *q, const void *k, const void *v,
+                                const void *a, const float *A_log, const void *erase,
+                                const void *write, const float *initial_state, const void *d_out,
+                                const float *d_final_state, float *dq, float *dk, float *dv,
+                                float *da, float *d_erase, float *d_write, float *dA_log,
+                                float *d_initial_state, void *workspace, size_t workspace_bytes,
+                                void *stream, void *const *stage_events);
+
 /* One-token recurrent decode step on a cached state, updated in place
  * (wanger-sjtu page: the recurrent branch reads and updates the cached
  * recurrent state; rainlin page, five-step form for one token).

@@ -34,6 +34,7 @@ import torch
 TID_A_LOG, TID_DT_BIAS, TID_Q, TID_K, TID_V, TID_A, TID_B, TID_S0, TID_ERASE, TID_WRITE = range(10)
 TID_NORM_X, TID_NORM_Z, TID_NORM_W = 10, 11, 12
 TID_CONV_X, TID_CONV_W, TID_CONV_B, TID_CONV_S = 13, 14, 15, 16
+TID_DOUT, TID_DST = 17, 18
 
 _SLAB = 1 << 22  # values drawn per slab (bounds the float64 working set)
 
@@ -153,6 +154,20 @@ def make_inputs(spec: GDNSpec) -> Dict[str, Optional[torch.Tensor]]:
     else:
         out["S0"] = None
     return out
+
+
+def make_grad_inputs(spec: GDNSpec, d_state: bool = True, d_state_sigma: float = 1.0):
+    """Seeded gradients of the forward's outputs: d_out [B,T,Hv,Dv] N(0,1) in the input
+    dtype and d_ST [B,Hv,Dk,Dv] float32 N(0, d_state_sigma) (None when d_state is False)."""
+    s = spec
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    d_out = _to_torch(_normal_rows(_rng(s.seed, TID_DOUT), (s.B, s.T, s.Hv, s.Dv), False), dt)
+    d_ST = None
+    if d_state:
+        x = _normal_rows(_rng(s.seed, TID_DST), (s.B, s.Hv, s.Dk, s.Dv), False)
+        x *= np.float32(d_state_sigma)
+        d_ST = torch.from_numpy(x)
+    return {"d_out": d_out, "d_ST": d_ST}
 
 
 def head_slice(inp: Dict[str, Optional[torch.Tensor]], spec: GDNSpec, b: int, hv: int):

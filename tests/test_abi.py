@@ -340,6 +340,82 @@ def test_gdn2_zero_batch_is_a_noop():
     assert call_gdn2(d, a) == OK
 
 
+# ---- Gated DeltaNet-2 backward (gdn2_chunk_bwd) ----
+
+def bwd2_args(buf, d, **override):
+    B, T, Hk, Hv, Dk, Dv = d.B, d.T, d.Hk, d.Hv, d.Dk, d.Dv
+    args = dict(
+        q=buf(B * T * Hk * Dk * 2), k=buf(B * T * Hk * Dk * 2), v=buf(B * T * Hv * Dv * 2),
+        a=buf(B * T * Hv * Dk * 2), A_log=buf(Hv * Dk * 4), erase=buf(B * T * Hv * Dk * 2),
+        write=buf(B * T * Hv * Dv * 2), S0=None, dout=buf(B * T * Hv * Dv * 2), dST=None,
+        dq=buf(B * T * Hk * Dk * 4), dk=buf(B * T * Hk * Dk * 4), dv=buf(B * T * Hv * Dv * 4),
+        da=buf(B * T * Hv * Dk * 4), derase=buf(B * T * Hv * Dk * 4), dwrite=buf(B * T * Hv * Dv * 4),
+        dAl=buf(Hv * Dk * 4), dS0=buf(B * Hv * Dk * Dv * 4))
+    ws = binding.lib().gdn2_chunk_bwd_workspace_bytes(ctypes.byref(d))
+    args["ws"] = buf(ws)
+    args["ws_bytes"] = ws
+    args.update(override)
+    return args
+
+
+def call_bwd2(d, a):
+    return binding.lib().gdn2_chunk_bwd(
+        ctypes.byref(d), a["q"], a["k"], a["v"], a["a"], a["A_log"], a["erase"], a["write"], a["S0"],
+        a["dout"], a["dST"], a["dq"], a["dk"], a["dv"], a["da"], a["derase"], a["dwrite"], a["dAl"],
+        a["dS0"], a["ws"], a["ws_bytes"], None)
+
+
+def test_bwd2_declared():
+    assert {"gdn2_chunk_bwd", "gdn2_chunk_bwd_timed", "gdn2_chunk_bwd_workspace_bytes"} <= set(declared_functions())
+
+
+def test_bwd2_workspace_bytes():
+    L = binding.lib()
+    n = L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(dims(B=1, T=8192, Hk=16, Hv=64, Dk=128, Dv=128)))
+    units = 64 * 128
+    # per unit, float32: A, A_qk, dM, dA_qk (64 x 64); Et, Qt, Kh, dEt, dQt, dKh (64 x Dk);
+    # Z, U, R, dU, dR (64 x Dv); S_n, dS_{n+1} (Dk x Dv); e^{G_C}, its gradient and the
+    # dA_log part (Dk); plus per value head dq and dk [B,T,Hv,Dk]
+    need = units * 4 * (4 * 64 * 64 + 6 * 64 * 128 + 5 * 64 * 128 + 2 * 128 * 128 + 3 * 128) \
+        + 2 * 8192 * 64 * 128 * 4
+    assert need <= n < need + 24 * 256
+    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(dims(dtype=binding.GDN_F32))) == 0
+    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(dims(T=0))) == 0
+    assert L.gdn2_chunk_bwd_workspace_bytes(None) == 0
+
+
+def test_bwd2_validation():
+    buf = Buf()
+    d = dims()
+    assert call_bwd2(dims(dtype=binding.GDN_F32), bwd2_args(buf, d)) == ERR_UNSUPPORTED
+    assert call_bwd2(dims(Hv=3), bwd2_args(buf, d)) == ERR_SHAPE
+    assert call_bwd2(dims(Dk=96), bwd2_args(buf, d)) == ERR_UNSUPPORTED
+    for name in ["q", "k", "v", "a", "A_log", "erase", "write", "dout", "dq", "dk", "dv", "da", "derase",
+                 "dwrite", "dAl"]:
+        assert call_bwd2(d, bwd2_args(buf, d, **{name: None})) == ERR_NULL, name
+    for name in ["dq", "da", "dwrite", "dS0"]:
+        a = bwd2_args(buf, d)
+        a[name] += 8
+        assert call_bwd2(d, a) == ERR_ALIGN, name
+    assert call_bwd2(d, bwd2_args(buf, d, ws=None)) == ERR_WORKSPACE
+    a = bwd2_args(buf, d)
+    a["ws_bytes"] -= 1
+    assert call_bwd2(d, a) == ERR_WORKSPACE
+    a = bwd2_args(buf, d)
+    a["dv"] = a["v"]
+    assert call_bwd2(d, a) == ERR_ALIAS and "dv overlaps v" in last_error()
+    a = bwd2_args(buf, d)
+    a["da"] = a["derase"]
+    assert call_bwd2(d, a) == ERR_ALIAS
+    a = bwd2_args(buf, d)
+    a["dS0"] = a["ws"]
+    assert call_bwd2(d, a) == ERR_ALIAS
+    d0 = dims(B=0)
+    assert call_bwd2(d0, bwd2_args(buf, d0, q=None, k=None, v=None, a=None, erase=None, write=None,
+                                   dout=None, dq=None, dk=None, dv=None, da=None, derase=None,
+                                   dwrite=None, dS0=None, ws=None)) == OK
+
+
 # ---- Gated DeltaNet-2 decode step (gdn2_recurrent_step) ----
 
 def step2_args(buf, d, **override):

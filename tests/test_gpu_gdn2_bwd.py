@@ -1,0 +1,172 @@
+"""GPU parity of the Gated DeltaNet-2 backward (gdn2_chunk_bwd) against the float64
+oracle's reverse-mode gradient of the token loop (oracle.gdn2_bwd).
+
+bfloat16 inputs and output gradient, float32 arithmetic and gradients: every gradient
+tensor is compared on its own by relative L2 against TOL_BWD (see the module constant).
+Every case prints its name and shape first.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import GDNSpec, SLOW_DECAY, WORKLOADS
+from tests.gpu_util import assert_close, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# The path computes in float32 from exactly widened bfloat16 inputs, so its error is
+# float32 rounding amplified by the chunk algebra ((I + M)^{-1}, products over 64-token
+# chunks, the state chain).  Measured: at most 9e-6 relative L2 on the per-token
+# gradients and the initial-state gradient, so 1e-4 leaves a 10x margin and stays 20x
+# below the bfloat16 bound of 2e-3.  dA_log is a sum over every token of dg * g with
+# both signs: its relative error is that of dg times the cancellation ratio
+# sum|dg g| / |sum dg g| (measured up to 5.6e-5), hence its own bound of 5e-4.
+TOL_BWD = 1e-4
+TOL_SUM = 5e-4
+NAMES = ["dq", "dk", "dv", "da", "d_erase", "d_write", "dA_log", "dS0"]
+
+
+def tol(name: str) -> float:
+    return TOL_SUM if name == "dA_log" else TOL_BWD
+
+
+def gpu_bwd(inp, grads, scale: float = 1.0, **kw):
+    import gated_deltanet_sequence_amd as gdn
+    d = to_dev(inp)
+    g = to_dev(grads)
+    r = gdn.gdn2_chunk_bwd(d["q"], d["k"], d["v"], d["a"], d["A_log"], d["erase"], d["write"],
+                           d["S0"], g["d_out"], g["d_ST"], scale=scale, **kw)
+    torch.cuda.synchronize()
+    r = {k: (None if v is None else v.cpu()) for k, v in r.items()}
+    r["dS0"] = r.pop("d_initial_state")
+    return r
+
+
+def oracle_bwd(inp, grads, scale: float = 1.0):
+    return oracle.gdn2_bwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["A_log"], inp["erase"],
+                           inp["write"], grads["d_out"], S0=inp["S0"], d_ST=grads["d_ST"], scale=scale)
+
+
+def full_check(spec: GDNSpec, scale: float = 1.0, d_state: bool = True):
+    log(f"[gdn2 bwd] {spec} d_state={d_state}")
+    inp = synth.make_inputs(spec)
+    grads = synth.make_grad_inputs(spec, d_state=d_state)
+    got = gpu_bwd(inp, grads, scale=scale)
+    ref = oracle_bwd(inp, grads, scale=scale)
+    for n in NAMES:
+        assert_close(n, got[n], ref[n], tol(n))
+    return inp, grads, got
+
+
+def g2(**kw) -> GDNSpec:
+    return GDNSpec(variant="gdn2", dtype="bf16", **kw)
+
+
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 130, 200])
+def test_ragged_lengths(T):
+    """One to four chunks, ragged tails, a single token."""
+    full_check(g2(B=1, T=T, Hk=1, Hv=2, Dk=128, Dv=128, seed=500 + T, init_state=True))
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 64), (64, 128), (128, 64)])
+def test_head_sizes(Dk, Dv):
+    full_check(g2(B=1, T=150, Hk=1, Hv=2, Dk=Dk, Dv=Dv, seed=510 + Dk + Dv, init_state=True))
+
+
+def test_batch_and_key_head_groups():
+    """B=2 sequences; 2 key heads shared by 3 value heads each (dq, dk summed per group)."""
+    full_check(g2(B=2, T=130, Hk=2, Hv=6, Dk=128, Dv=128, seed=520, init_state=True))
+
+
+def test_no_initial_state_no_final_gradient():
+    full_check(g2(B=1, T=140, Hk=1, Hv=2, Dk=128, Dv=128, seed=521), d_state=False)
+
+
+def test_scale():
+    full_check(g2(B=1, T=100, Hk=1, Hv=2, Dk=128, Dv=128, seed=522, init_state=True),
+               scale=1 / math.sqrt(128))
+
+
+def test_slow_and_wide_decay():
+    """exp(A_log) over 1e-3 .. 30: channels that keep their state across all chunks next to
+    channels that forget it within a token."""
+    full_check(g2(B=1, T=260, Hk=1, Hv=2, Dk=128, Dv=128, seed=523, init_state=True,
+                  state_sigma=0.3, a_log_lo=math.log(1e-3), a_log_hi=math.log(30.0)))
+
+
+def test_slow_decay():
+    full_check(g2(B=1, T=256, Hk=1, Hv=2, Dk=128, Dv=128, seed=524, init_state=True, **SLOW_DECAY))
+
+
+def test_skip_initial_state_gradient():
+    spec = g2(B=1, T=70, Hk=1, Hv=2, Dk=64, Dv=64, seed=525, init_state=True)
+    log(f"[gdn2 bwd no dS0] {spec}")
+    inp = synth.make_inputs(spec)
+    grads = synth.make_grad_inputs(spec)
+    got = gpu_bwd(inp, grads, output_d_initial_state=False)
+    ref = oracle_bwd(inp, grads)
+    assert got["dS0"] is None
+    for n in NAMES[:-1]:
+        assert_close(n, got[n], ref[n], tol(n))
+
+
+def test_zero_length():
+    spec = g2(B=2, T=0, Hk=1, Hv=2, Dk=128, Dv=128, seed=526, init_state=True)
+    log(f"[gdn2 bwd T=0] {spec}")
+    inp = synth.make_inputs(spec)
+    grads = synth.make_grad_inputs(spec)
+    got = gpu_bwd(inp, grads)
+    assert got["dq"].numel() == 0 and got["dv"].numel() == 0
+    assert torch.equal(got["dS0"], grads["d_ST"])
+    assert torch.count_nonzero(got["dA_log"]) == 0
+
+
+def test_deterministic():
+    spec = g2(B=1, T=200, Hk=1, Hv=4, Dk=128, Dv=128, seed=527, init_state=True)
+    log(f"[gdn2 bwd determinism] {spec}")
+    inp = synth.make_inputs(spec)
+    grads = synth.make_grad_inputs(spec)
+    r1 = gpu_bwd(inp, grads)
+    r2 = gpu_bwd(inp, grads)
+    for n in NAMES:
+        assert torch.equal(r1[n], r2[n]), n
+
+
+def test_gdn2_t8192_sampled_key_heads():
+    """B=1, T=8192, 16 key / 64 value heads, d=128: the workload the bench times.  The
+    oracle runs on 2 sampled key heads with their 4 value heads each, over all 8192 tokens
+    (dq, dk are sums over a key head's value heads, so whole groups are compared)."""
+    spec = WORKLOADS["gdn2_t8192"]
+    log(f"[gdn2 bwd] {spec}")
+    inp = synth.make_inputs(spec)
+    grads = synth.make_grad_inputs(spec)
+    got = gpu_bwd(inp, grads)
+    grp = spec.Hv // spec.Hk
+    rng = np.random.default_rng(3)
+    for hk in sorted(rng.choice(spec.Hk, 2, replace=False)):
+        hv0 = hk * grp
+        sl = {k: None if v is None else v for k, v in inp.items()}
+        sub = {"q": sl["q"][:, :, hk:hk + 1], "k": sl["k"][:, :, hk:hk + 1],
+               "v": sl["v"][:, :, hv0:hv0 + grp], "a": sl["a"][:, :, hv0:hv0 + grp],
+               "erase": sl["erase"][:, :, hv0:hv0 + grp], "write": sl["write"][:, :, hv0:hv0 + grp],
+               "A_log": sl["A_log"][hv0:hv0 + grp],
+               "S0": None if sl["S0"] is None else sl["S0"][:, hv0:hv0 + grp]}
+        gsub = {"d_out": grads["d_out"][:, :, hv0:hv0 + grp],
+                "d_ST": None if grads["d_ST"] is None else grads["d_ST"][:, hv0:hv0 + grp]}
+        ref = oracle_bwd(sub, gsub)
+        log(f"  key head {hk} (value heads {hv0}..{hv0 + grp - 1})")
+        assert_close("dq", got["dq"][:, :, hk:hk + 1], ref["dq"], TOL_BWD)
+        assert_close("dk", got["dk"][:, :, hk:hk + 1], ref["dk"], TOL_BWD)
+        for n, sl_ in (("dv", (slice(None), slice(None), slice(hv0, hv0 + grp))),
+                       ("da", (slice(None), slice(None), slice(hv0, hv0 + grp))),
+                       ("d_erase", (slice(None), slice(None), slice(hv0, hv0 + grp))),
+                       ("d_write", (slice(None), slice(None), slice(hv0, hv0 + grp))),
+                       ("dA_log", (slice(hv0, hv0 + grp),)),
+                       ("dS0", (slice(None), slice(hv0, hv0 + grp)))):
+            assert_close(n, got[n][sl_], ref[n], tol(n))
+    for n in NAMES:
+        assert torch.isfinite(got[n]).all(), n
