@@ -44,20 +44,42 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 // acc += A(16 x K) B(K x 16), A(m, k) = a0[m * AM + k * AK], B(k, n) = b0[k * BK + n * BN]
 // (K a multiple of 4; float32 MFMA, lane l supplies A[l%16][l/16], B[l/16][l%16]).
-template <int AM, int AK, int BK, int BN>
-__device__ __forceinline__ void mma(f4 &acc, const float *a0, const float *b0, int K) {
+// Fully unrolled so that the operand reads are issued ahead of the MFMAs.
+template <int K, int AM, int AK, int BK, int BN>
+__device__ __forceinline__ void mma(f4 &acc, const float *a0, const float *b0) {
     const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
     const float *pa = a0 + r * AM + g * AK, *pb = b0 + g * BK + r * BN;
+#pragma unroll
     for (int k = 0; k < K; k += 4) acc = mfma_f32_k4(pa[k * AK], pb[k * BK], acc);
 }
 
-// rows x COLS float32 block (row-major, contiguous) into LDS rows of stride LS, times f
-template <int COLS, int LS>
-__device__ __forceinline__ void lds_load(float *dst, const float *__restrict__ src, int rows, float f = 1.f) {
-    for (int i = threadIdx.x; i < rows * (COLS / 4); i += blockDim.x) {
-        const int r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
-        const f4 x = *reinterpret_cast<const f4 *>(src + (size_t)r * COLS + c) * f;
-        *reinterpret_cast<f4 *>(dst + r * LS + c) = x;
+// ROWS x COLS float32 block (row-major, contiguous) into LDS rows of stride LS,
+// times f.  Compile-time trip counts: each thread issues its loads in batches of
+// 8 before storing them, so the global latency is paid once per batch.
+template <int ROWS, int COLS, int LS>
+__device__ __forceinline__ void lds_load(float *dst, const float *__restrict__ src, float f = 1.f) {
+    constexpr int N = ROWS * COLS / 4, PER = N / 256, BT = PER < 8 ? PER : 8;
+    static_assert(N % 256 == 0 && PER % BT == 0, "block size");
+#pragma unroll
+    for (int b0 = 0; b0 < PER; b0 += BT) {
+        f4 x[BT];
+#pragma unroll
+        for (int j = 0; j < BT; ++j)
+            x[j] = *reinterpret_cast<const f4 *>(src + (size_t)(threadIdx.x + (b0 + j) * 256) * 4);
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            const int i = threadIdx.x + (b0 + j) * 256, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
+            *reinterpret_cast<f4 *>(dst + r * LS + c) = x[j] * f;
+        }
+    }
+}
+
+// 8 bfloat16 values to float32
+__device__ __forceinline__ void bf8_to_f32(const u16x8 x, f4 &lo, f4 &hi) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        lo[j] = bf16_to_f32(x[j]);
+        hi[j] = bf16_to_f32(x[j + 4]);
     }
 }
 
@@ -79,25 +101,27 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv), hk = hv / (p.Hv / p.Hk);
     const int t0 = n * C, L = min(C, p.T - t0);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4;
-    const uint16_t *q = reinterpret_cast<const uint16_t *>(p.q), *k = reinterpret_cast<const uint16_t *>(p.k);
-    const uint16_t *a = reinterpret_cast<const uint16_t *>(p.a), *er = reinterpret_cast<const uint16_t *>(p.erase);
     const uint16_t *v = reinterpret_cast<const uint16_t *>(p.v), *wr = reinterpret_cast<const uint16_t *>(p.write);
 
-    // 1. gates: G (log2 units, 0 past T), e = sigmoid(erase) k, qs = scale q, k; z to the workspace
-    for (int i = tid; i < C * DK / 4; i += 256) {
-        const int t = i / (DK / 4), c = (i % (DK / 4)) * 4;
-        f4 gv = {0, 0, 0, 0}, ev = gv, qv = gv, kv = gv;
-        if (t < L) {
-            const size_t kq = (((size_t)bb * p.T + t0 + t) * p.Hk + hk) * DK + c;
-            const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
+    // 1. gates: G (log2 units, 0 past T), e = sigmoid(erase) k, qs = scale q, k; z to the workspace.
+    //    Rows past T read the last token (L >= 1) and are zeroed, so every load is unconditional.
+    const bf16_t *qb = reinterpret_cast<const bf16_t *>(p.q), *kb = reinterpret_cast<const bf16_t *>(p.k);
+    const bf16_t *ab = reinterpret_cast<const bf16_t *>(p.a), *eb = reinterpret_cast<const bf16_t *>(p.erase);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float kk = bf16_to_f32(k[kq + j]);
-                gv[j] = -expf(p.A_log[(size_t)hv * DK + c + j]) * softplus_f32(bf16_to_f32(a[ka + j])) * LOG2E;
-                ev[j] = sigmoid_f32(bf16_to_f32(er[ka + j])) * kk;
-                qv[j] = p.scale * bf16_to_f32(q[kq + j]);
-                kv[j] = kk;
-            }
+    for (int it = 0; it < C * DK / 4 / 256; ++it) {
+        const int i = tid + 256 * it, t = i / (DK / 4), c = (i % (DK / 4)) * 4, tl = min(t, L - 1);
+        const size_t kq = (((size_t)bb * p.T + t0 + tl) * p.Hk + hk) * DK + c;
+        const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
+        const f4 kk = ld4(kb, kq), qq = ld4(qb, kq), aa = ld4(ab, ka), ee = ld4(eb, ka);
+        const f4 al = *reinterpret_cast<const f4 *>(p.A_log + (size_t)hv * DK + c);
+        const float on = t < L ? 1.f : 0.f;
+        f4 gv, ev, qv, kv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gv[j] = -expf(al[j]) * softplus_f32(aa[j]) * LOG2E * on;
+            ev[j] = sigmoid_f32(ee[j]) * kk[j] * on;
+            qv[j] = p.scale * qq[j] * on;
+            kv[j] = kk[j] * on;
         }
         *reinterpret_cast<f4 *>(Gs + t * LS + c) = gv;
         *reinterpret_cast<f4 *>(Es + t * LS + c) = ev;
@@ -105,15 +129,21 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
         *reinterpret_cast<f4 *>(Ks + t * LS + c) = kv;
     }
     float *Zu = ws.Z + (size_t)u * C * DV;
-    for (int i = tid; i < C * DV / 4; i += 256) {
-        const int t = i / (DV / 4), j = (i % (DV / 4)) * 4;
-        f4 zv = {0, 0, 0, 0};
-        if (t < L) {
-            const size_t kv = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DV + j;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) zv[x] = sigmoid_f32(bf16_to_f32(wr[kv + x])) * bf16_to_f32(v[kv + x]);
+    for (int it = 0; it < C * DV / 8 / 256; ++it) {
+        const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
+        const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
+        f4 vl, vh, wl, wh;
+        bf8_to_f32(*reinterpret_cast<const u16x8 *>(v + kv), vl, vh);
+        bf8_to_f32(*reinterpret_cast<const u16x8 *>(wr + kv), wl, wh);
+        const float on = t < L ? 1.f : 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            vl[x] = sigmoid_f32(wl[x]) * vl[x] * on;
+            vh[x] = sigmoid_f32(wh[x]) * vh[x] * on;
         }
-        *reinterpret_cast<f4 *>(Zu + t * DV + j) = zv;
+        *reinterpret_cast<f4 *>(Zu + t * DV + j) = vl;
+        *reinterpret_cast<f4 *>(Zu + t * DV + j + 4) = vh;
     }
     __syncthreads();
     // 2. in-chunk inclusive prefix per channel
@@ -160,6 +190,7 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
         const int ti = w + 4 * x;
         if (ti < 6) {
             const int bt = OBT[ti], bi = OBI[ti], r = 16 * bt, t = 16 * bt + rr, i = 16 * bi + rr;
+#pragma unroll 8
             for (int c0 = 0; c0 < DK; c0 += 4) {
                 const int c = c0 + gg;
                 const float Gr = Gs[r * LS + c];
@@ -180,6 +211,7 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
             const bool tsec = (rr & h) != 0;
             const int rt = base + (rr & ~(h - 1)), ri = base + ((rr | h) & ~(h - 1));
             f4 aM = {0, 0, 0, 0}, aQ = {0, 0, 0, 0};
+#pragma unroll 8
             for (int c0 = 0; c0 < DK; c0 += 4) {
                 const int c = c0 + gg;
                 float ae = 0.f, aq = 0.f, b = 0.f;
@@ -259,14 +291,14 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     for (int b = 1; b < 4; ++b) {
         if (w < b) {
             f4 X = {0, 0, 0, 0};
-            for (int m = w; m < b; ++m) mma<68, 1, 68, 1>(X, Ms + 16 * b * 68 + 16 * m, As + 16 * m * 68 + 16 * w, 16);
+            for (int m = w; m < b; ++m) mma<16, 68, 1, 68, 1>(X, Ms + 16 * b * 68 + 16 * m, As + 16 * m * 68 + 16 * w);
 #pragma unroll
             for (int s = 0; s < 4; ++s) Xt[w * 16 * 48 + (4 * gg + s) * 48 + rr] = X[s];
         }
         __syncthreads();
         if (w < b) {
             f4 Y = {0, 0, 0, 0};
-            mma<68, 1, 48, 1>(Y, As + 16 * b * 68 + 16 * b, Xt + w * 16 * 48, 16);
+            mma<16, 68, 1, 48, 1>(Y, As + 16 * b * 68 + 16 * b, Xt + w * 16 * 48);
 #pragma unroll
             for (int s = 0; s < 4; ++s) As[(16 * b + 4 * gg + s) * 68 + 16 * w + rr] = -Y[s];
         }
@@ -310,21 +342,31 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
 #pragma unroll
             for (int s = 0; s < 4; ++s) Snu[(16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = S[x][s];
         }
-        lds_load<DK, LE>(Ets, ws.Et + u * C * DK, C);
-        lds_load<DK, LK>(Khs, ws.Kh + u * C * DK, C);
-        lds_load<C, LA>(As, ws.A + u * C * C, C);
+        // this lane's Z elements and decay factors, loaded ahead of the staging
+        const float *Zu = ws.Z + u * C * DV, *gCu = ws.gC + u * DK;
+        float zr[2][4], gcr[NT][4];
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) zr[jb][s] = Zu[(16 * w + 4 * gg + s) * DV + j0 + 16 * jb + rr];
+#pragma unroll
+        for (int x = 0; x < NT; ++x)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) gcr[x][s] = gCu[16 * ((w * NT + x) >> 1) + 4 * gg + s];
+        lds_load<C, DK, LE>(Ets, ws.Et + u * C * DK);
+        lds_load<C, DK, LK>(Khs, ws.Kh + u * C * DK);
+        lds_load<C, C, LA>(As, ws.A + u * C * C);
         __syncthreads();
         // R = Z - Et S (rows of block w)
-        const float *Zu = ws.Z + u * C * DV;
         float *Ru = ws.R + u * C * DV, *Uu = ws.U + u * C * DV;
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
             f4 acc = {0, 0, 0, 0};
-            mma<LE, 1, LB, 1>(acc, Ets + 16 * w * LE, Ss + 16 * jb, DK);
+            mma<DK, LE, 1, LB, 1>(acc, Ets + 16 * w * LE, Ss + 16 * jb);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
-                const float rv = Zu[t * DV + j0 + j] - acc[s];
+                const float rv = zr[jb][s] - acc[s];
                 Rs[t * LB + j] = rv;
                 Ru[t * DV + j0 + j] = rv;
             }
@@ -334,7 +376,7 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
             f4 acc = {0, 0, 0, 0};
-            mma<LA, 1, LB, 1>(acc, As + 16 * w * LA, Rs + 16 * jb, 16 * (w + 1));
+            mma<C, LA, 1, LB, 1>(acc, As + 16 * w * LA, Rs + 16 * jb);  // A is zero above the diagonal
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
@@ -344,13 +386,12 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
         }
         __syncthreads();
         // S = gamma_C . S + Kh^T U
-        const float *gCu = ws.gC + u * DK;
 #pragma unroll
         for (int x = 0; x < NT; ++x) {
             const int id = w * NT + x, cb = id >> 1, jb = id & 1;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) S[x][s] *= gCu[16 * cb + 4 * gg + s];
-            mma<1, LK, LB, 1>(S[x], Khs + 16 * cb, Us + 16 * jb, C);
+            for (int s = 0; s < 4; ++s) S[x][s] *= gcr[x][s];
+            mma<C, 1, LK, LB, 1>(S[x], Khs + 16 * cb, Us + 16 * jb);
 #pragma unroll
             for (int s = 0; s < 4; ++s) Ss[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = S[x][s];
         }
@@ -390,20 +431,32 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
 #pragma unroll
             for (int s = 0; s < 4; ++s) dS1u[(16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = dS[x][s];
         }
-        lds_load<C, LQ>(bA, ws.Aq + u * C * C, C);
-        lds_load<DK, LKA>(bK, ws.Kh + u * C * DK, C);
-        for (int i = tid; i < C * 32; i += 256) {
-            const int t = i >> 5, j = i & 31;
-            Os[t * LB + j] = t < L ? bf16_to_f32(dout[(((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DV + j0 + j]) : 0.f;
+        float gcr[NT][4];
+#pragma unroll
+        for (int x = 0; x < NT; ++x)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) gcr[x][s] = ws.gC[u * DK + 16 * ((w * NT + x) >> 1) + 4 * gg + s];
+        {
+            // dO slice: 64 rows x 32 columns, 8 per thread (rows past T read the last token, zeroed)
+            const int t = tid >> 2, j = (tid & 3) * 8, tl = min(t, L - 1);
+            const u16x8 x = *reinterpret_cast<const u16x8 *>(
+                dout + (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j0 + j);
+            f4 lo, hi;
+            bf8_to_f32(x, lo, hi);
+            const float on = t < L ? 1.f : 0.f;
+            lds_load<C, C, LQ>(bA, ws.Aq + u * C * C);
+            lds_load<C, DK, LKA>(bK, ws.Kh + u * C * DK);
+            *reinterpret_cast<f4 *>(Os + t * LB + j) = lo * on;
+            *reinterpret_cast<f4 *>(Os + t * LB + j + 4) = hi * on;
         }
         __syncthreads();
-        // dU = Aq^T dO + Kh dS  (Aq[i][t] vanishes for i < t)
+        // dU = Aq^T dO + Kh dS  (Aq is zero above the diagonal)
         float *dUu = ws.dU + u * C * DV, *dRu = ws.dR + u * C * DV;
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
             f4 acc = {0, 0, 0, 0};
-            mma<1, LQ, LB, 1>(acc, bA + 16 * w * LQ + 16 * w, Os + 16 * w * LB + 16 * jb, C - 16 * w);
-            mma<LKA, 1, LB, 1>(acc, bK + 16 * w * LKA, dSs + 16 * jb, DK);
+            mma<C, 1, LQ, LB, 1>(acc, bA + 16 * w, Os + 16 * jb);
+            mma<DK, LKA, 1, LB, 1>(acc, bK + 16 * w * LKA, dSs + 16 * jb);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
@@ -412,14 +465,14 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
             }
         }
         __syncthreads();
-        lds_load<C, LQ>(bA, ws.A + u * C * C, C);
-        lds_load<DK, LKB>(bK, ws.Qt + u * C * DK, C);
+        lds_load<C, C, LQ>(bA, ws.A + u * C * C);
+        lds_load<C, DK, LKB>(bK, ws.Qt + u * C * DK);
         __syncthreads();
         // dR = A^T dU;  dS = gamma_C . dS + Qt^T dO
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
             f4 acc = {0, 0, 0, 0};
-            mma<1, LQ, LB, 1>(acc, bA + 16 * w * LQ + 16 * w, dUs + 16 * w * LB + 16 * jb, C - 16 * w);
+            mma<C, 1, LQ, LB, 1>(acc, bA + 16 * w, dUs + 16 * jb);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
@@ -427,22 +480,21 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
                 dRu[t * DV + j0 + j] = acc[s];
             }
         }
-        const float *gCu = ws.gC + u * DK;
 #pragma unroll
         for (int x = 0; x < NT; ++x) {
             const int id = w * NT + x, cb = id >> 1, jb = id & 1;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) dS[x][s] *= gCu[16 * cb + 4 * gg + s];
-            mma<1, LKB, LB, 1>(dS[x], bK + 16 * cb, Os + 16 * jb, C);
+            for (int s = 0; s < 4; ++s) dS[x][s] *= gcr[x][s];
+            mma<C, 1, LKB, LB, 1>(dS[x], bK + 16 * cb, Os + 16 * jb);
         }
         __syncthreads();
-        lds_load<DK, LKB>(bK, ws.Et + u * C * DK, C, -1.f);
+        lds_load<C, DK, LKB>(bK, ws.Et + u * C * DK, -1.f);
         __syncthreads();
         // dS -= Et^T dR
 #pragma unroll
         for (int x = 0; x < NT; ++x) {
             const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-            mma<1, LKB, LB, 1>(dS[x], bK + 16 * cb, dRs + 16 * jb, C);
+            mma<C, 1, LKB, LB, 1>(dS[x], bK + 16 * cb, dRs + 16 * jb);
 #pragma unroll
             for (int s = 0; s < 4; ++s) dSs[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = dS[x][s];
         }
@@ -474,17 +526,31 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     const uint16_t *dout = reinterpret_cast<const uint16_t *>(p.dout);
 
     // phase 1: dEt = -dR Sn^T, dQt = dO Sn^T, dgamma_C = rowsum(dS1 . Sn)
-    lds_load<DV, LV>(r1, ws.Sn + (size_t)u * DK * DV, DK);
-    lds_load<DV, LV>(b1, ws.dR + uC * DV, C, -1.f);
-    for (int i = tid; i < C * DV; i += 256) {
-        const int t = i / DV, j = i % DV;
-        b2[t * LV + j] = t < L ? bf16_to_f32(dout[(((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DV + j]) : 0.f;
+    {
+        // dO: 8 values per load (rows past T read the last token, zeroed)
+        u16x8 xo[C * DV / 8 / 256];
+#pragma unroll
+        for (int it = 0; it < C * DV / 8 / 256; ++it) {
+            const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
+            xo[it] = *reinterpret_cast<const u16x8 *>(dout + (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j);
+        }
+        lds_load<DK, DV, LV>(r1, ws.Sn + (size_t)u * DK * DV);
+        lds_load<C, DV, LV>(b1, ws.dR + uC * DV, -1.f);
+#pragma unroll
+        for (int it = 0; it < C * DV / 8 / 256; ++it) {
+            const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8;
+            f4 lo, hi;
+            bf8_to_f32(xo[it], lo, hi);
+            const float on = t < L ? 1.f : 0.f;
+            *reinterpret_cast<f4 *>(b2 + t * LV + j) = lo * on;
+            *reinterpret_cast<f4 *>(b2 + t * LV + j + 4) = hi * on;
+        }
     }
     __syncthreads();
     for (int cb = 0; cb < DK / 16; ++cb) {
         f4 e = {0, 0, 0, 0}, q = {0, 0, 0, 0};
-        mma<LV, 1, 1, LV>(e, b1 + 16 * w * LV, r1 + 16 * cb * LV, DV);
-        mma<LV, 1, 1, LV>(q, b2 + 16 * w * LV, r1 + 16 * cb * LV, DV);
+        mma<DV, LV, 1, 1, LV>(e, b1 + 16 * w * LV, r1 + 16 * cb * LV);
+        mma<DV, LV, 1, 1, LV>(q, b2 + 16 * w * LV, r1 + 16 * cb * LV);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const size_t o = (uC + 16 * w + 4 * gg + s) * DK + 16 * cb + rr;
@@ -494,27 +560,31 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     }
     if (tid < 2 * DK) {
         const int c = tid >> 1, h = tid & 1;
-        const float *d1 = ws.dS1 + ((size_t)u * DK + c) * DV;
+        const float *d1 = ws.dS1 + ((size_t)u * DK + c) * DV + h * (DV / 2);
         float s = 0.f;
-        for (int j = h * (DV / 2); j < (h + 1) * (DV / 2); ++j) s += d1[j] * r1[c * LV + j];
+#pragma unroll
+        for (int j = 0; j < DV / 2; j += 4) {
+            const f4 x = *reinterpret_cast<const f4 *>(d1 + j), y = *reinterpret_cast<const f4 *>(r1 + c * LV + h * (DV / 2) + j);
+            s += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+        }
         s += __shfl_xor(s, 1);
         if (!h) ws.dgC[(size_t)u * DK + c] = s;
     }
     __syncthreads();
     // phase 2: dKh = U dS1^T, dAq = tril(dO U^T)
-    lds_load<DV, LV>(r1, ws.dS1 + (size_t)u * DK * DV, DK);
-    lds_load<DV, LV>(b1, ws.U + uC * DV, C);
+    lds_load<DK, DV, LV>(r1, ws.dS1 + (size_t)u * DK * DV);
+    lds_load<C, DV, LV>(b1, ws.U + uC * DV);
     __syncthreads();
     for (int cb = 0; cb < DK / 16; ++cb) {
         f4 acc = {0, 0, 0, 0};
-        mma<LV, 1, 1, LV>(acc, b1 + 16 * w * LV, r1 + 16 * cb * LV, DV);
+        mma<DV, LV, 1, 1, LV>(acc, b1 + 16 * w * LV, r1 + 16 * cb * LV);
 #pragma unroll
         for (int s = 0; s < 4; ++s) ws.dKh[(uC + 16 * w + 4 * gg + s) * DK + 16 * cb + rr] = acc[s];
     }
     float *dAqu = ws.dAq + uC * C;
     for (int ib = 0; ib < 4; ++ib) {
         f4 acc = {0, 0, 0, 0};
-        if (ib <= w) mma<LV, 1, 1, LV>(acc, b2 + 16 * w * LV, b1 + 16 * ib * LV, DV);
+        if (ib <= w) mma<DV, LV, 1, 1, LV>(acc, b2 + 16 * w * LV, b1 + 16 * ib * LV);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int t = 16 * w + 4 * gg + s, i = 16 * ib + rr;
@@ -524,28 +594,28 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     __syncthreads();
     // phase 3: dA = dU R^T; X = A^T dA; dM = -strict_tril(X A^T)
     float *dAs = r1, *A80 = r1 + C * 80, *A68 = b1, *Xs = b2;
-    lds_load<DV, LV>(b1, ws.R + uC * DV, C);
-    lds_load<DV, LV>(b2, ws.dU + uC * DV, C);
-    lds_load<C, 80>(A80, ws.A + uC * C, C);
+    lds_load<C, DV, LV>(b1, ws.R + uC * DV);
+    lds_load<C, DV, LV>(b2, ws.dU + uC * DV);
+    lds_load<C, C, 80>(A80, ws.A + uC * C);
     __syncthreads();
     f4 dA[4];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
         dA[ib] = f4{0, 0, 0, 0};
-        mma<LV, 1, 1, LV>(dA[ib], b2 + 16 * w * LV, b1 + 16 * ib * LV, DV);
+        mma<DV, LV, 1, 1, LV>(dA[ib], b2 + 16 * w * LV, b1 + 16 * ib * LV);
     }
     __syncthreads();
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
         for (int s = 0; s < 4; ++s) dAs[(16 * w + 4 * gg + s) * 80 + 16 * ib + rr] = dA[ib][s];
-    lds_load<C, 68>(A68, ws.A + uC * C, C);
+    lds_load<C, C, 68>(A68, ws.A + uC * C);
     __syncthreads();
-    // X[i][s] = sum_{t >= i} A[t][i] dA[t][s]: rows i of block w
+    // X[i][s] = sum_t A[t][i] dA[t][s] (A[t][i] = 0 for t < i): rows i of block w
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
         f4 acc = {0, 0, 0, 0};
-        mma<1, 80, 80, 1>(acc, A80 + 16 * w * 80 + 16 * w, dAs + 16 * w * 80 + 16 * sb, C - 16 * w);
+        mma<C, 1, 80, 80, 1>(acc, A80 + 16 * w, dAs + 16 * sb);
         dA[sb] = acc;  // reuse the registers for X
     }
     __syncthreads();  // Xs aliases b2, read by nobody now; A68 stays
@@ -554,11 +624,11 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
 #pragma unroll
         for (int s = 0; s < 4; ++s) Xs[(16 * w + 4 * gg + s) * 68 + 16 * sb + rr] = dA[sb][s];
     __syncthreads();
-    // dM[i][q] = -sum_{s <= q} X[i][s] A[q][s], strictly lower
+    // dM[i][q] = -sum_s X[i][s] A[q][s] (A[q][s] = 0 for s > q), strictly lower
     float *dMu = ws.dM + uC * C;
     for (int qb = 0; qb < 4; ++qb) {
         f4 acc = {0, 0, 0, 0};
-        if (qb <= w) mma<68, 1, 1, 68>(acc, Xs + 16 * w * 68, A68 + 16 * qb * 68, 16 * (qb + 1));
+        if (qb <= w) mma<C, 68, 1, 1, 68>(acc, Xs + 16 * w * 68, A68 + 16 * qb * 68);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int i = 16 * w + 4 * gg + s, qq = 16 * qb + rr;
@@ -568,10 +638,11 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
 }
 
 // ---------------------------------------------------------------------------
-// g2b_local: one work-group per (chunk, 64 key channels); lane = channel.
-// Waves 0/1: sums over i for rows t of blocks {0,3}/{1,2} (de, dqs);
-// waves 2/3: sums over t for rows i of blocks {0,3}/{1,2} (dk).  Then each wave
-// applies the chain rule to the rows of its block.
+// g2b_local: one work-group per (chunk, 64 key channels).  Wave w owns the
+// rows of 16-token block w: first the block pairs below the diagonal on the
+// matrix cores (rows t of block w against every earlier block, rows i of block
+// w against every later block), then the pairs inside block w on the vector
+// unit (lane = channel), then the chain rule for its rows.
 // ---------------------------------------------------------------------------
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
@@ -581,29 +652,28 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
     const int cg = blockIdx.x % CG, u = blockIdx.x / CG, NC = p.NC;
     const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv), hk = hv / (p.Hv / p.Hk);
     const int t0 = n * C, L = min(C, p.T - t0);
-    const int tid = threadIdx.x, w = tid >> 6, cl = tid & 63, c = 64 * cg + cl;
+    const int tid = threadIdx.x, w = tid >> 6, cl = tid & 63, c = 64 * cg + cl, rr = cl & 15, gg = cl >> 4;
     const uint16_t *q = reinterpret_cast<const uint16_t *>(p.q), *k = reinterpret_cast<const uint16_t *>(p.k);
     const uint16_t *a = reinterpret_cast<const uint16_t *>(p.a), *er = reinterpret_cast<const uint16_t *>(p.erase);
     const float Al = p.A_log[(size_t)hv * DK + c], rate = expf(Al);
 
+#pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
-        const int t = 16 * w + tt;
-        float gv = 0.f, ev = 0.f, qv = 0.f, kv = 0.f;
-        if (t < L) {
-            const size_t kq = (((size_t)bb * p.T + t0 + t) * p.Hk + hk) * DK + c;
-            const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
-            kv = bf16_to_f32(k[kq]);
-            gv = -rate * softplus_f32(bf16_to_f32(a[ka])) * LOG2E;
-            ev = sigmoid_f32(bf16_to_f32(er[ka])) * kv;
-            qv = p.scale * bf16_to_f32(q[kq]);
-        }
+        const int t = 16 * w + tt, tl = min(t, L - 1);
+        const size_t kq = (((size_t)bb * p.T + t0 + tl) * p.Hk + hk) * DK + c;
+        const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
+        const float on = t < L ? 1.f : 0.f;
+        const float kv = bf16_to_f32(k[kq]) * on;
+        const float gv = -rate * softplus_f32(bf16_to_f32(a[ka])) * LOG2E * on;
+        const float ev = sigmoid_f32(bf16_to_f32(er[ka])) * kv;
+        const float qv = p.scale * bf16_to_f32(q[kq]) * on;
         Gs[t * 64 + cl] = gv;
         Ks[t * 64 + cl] = kv;
         Es[t * 64 + cl] = ev;
         Qs[t * 64 + cl] = qv;
     }
-    lds_load<C, C>(dMs, ws.dM + (size_t)u * C * C, C);
-    lds_load<C, C>(dAqs, ws.dAq + (size_t)u * C * C, C);
+    lds_load<C, C, C>(dMs, ws.dM + (size_t)u * C * C);
+    lds_load<C, C, C>(dAqs, ws.dAq + (size_t)u * C * C);
     __syncthreads();
     if (w == 0) {
         float s = 0.f;
@@ -614,87 +684,80 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
     }
     __syncthreads();
 
-    if (w < 2) {
-        // sums over i for the rows t of block bt
-        for (int pass = 0; pass < 2; ++pass) {
-            const int bt = w == 0 ? (pass ? 3 : 0) : (pass ? 2 : 1);
-            float de[16], dq[16];
-#pragma unroll
-            for (int tt = 0; tt < 16; ++tt) de[tt] = dq[tt] = 0.f;
-            if (bt > 0) {
-                const int r = 16 * bt;
-                const float Gr = Gs[r * 64 + cl];
-                for (int i = 0; i < r; ++i) {
-                    const float kt = Ks[i * 64 + cl] * exp2f(Gr - Gs[i * 64 + cl]);
-#pragma unroll
-                    for (int tt = 0; tt < 16; ++tt) {
-                        de[tt] += dMs[(r + tt) * C + i] * kt;
-                        dq[tt] += dAqs[(r + tt) * C + i] * kt;
-                    }
-                }
-#pragma unroll
-                for (int tt = 0; tt < 16; ++tt) {
-                    const float F = exp2f(Gs[(r + tt) * 64 + cl] - Gr);
-                    de[tt] *= F;
-                    dq[tt] *= F;
-                }
-            }
-#pragma unroll
-            for (int tt = 0; tt < 16; ++tt) {
-                const int t = 16 * bt + tt;
-                const float Gt = Gs[t * 64 + cl];
-#pragma unroll
-                for (int ii = 0; ii <= tt; ++ii) {
-                    const int i = 16 * bt + ii;
-                    const float kE = Ks[i * 64 + cl] * exp2f(Gt - Gs[i * 64 + cl]);
-                    if (ii < tt) de[tt] += dMs[t * C + i] * kE;
-                    dq[tt] += dAqs[t * C + i] * kE;
-                }
-                Te[t * 64 + cl] = de[tt];
-                Tq[t * 64 + cl] = dq[tt];
+    // block pairs below the diagonal, 16 channels at a time (MFMA: lane supplies
+    // A[rr][gg], B[gg][rr]; accumulator element s is row 4 gg + s, channel rr).
+    //   rows t of block w, reference r = 16 w (i < r <= t):
+    //     de_t  = e^{G_t - G_r} sum_{i < r} dM_ti  k_i e^{G_r - G_i}, dqs_t likewise with dAq
+    //   rows i of block w, each later block b with reference r = 16 b:
+    //     dk_i += e^{G_r - G_i} sum_{t in b} dM_ti e_t e^{G_t - G_r} + dAq_ti qs_t e^{G_t - G_r}
+    for (int ct = 0; ct < 4; ++ct) {
+        const int cc = 16 * ct + rr;
+        f4 aE = {0, 0, 0, 0}, aQ = {0, 0, 0, 0}, aK = {0, 0, 0, 0};
+        if (w > 0) {
+            const int r = 16 * w;
+            const float Gr = Gs[r * 64 + cc];
+#pragma unroll 4
+            for (int i0 = 0; i0 < r; i0 += 4) {
+                const int i = i0 + gg;
+                const float b = Ks[i * 64 + cc] * exp2f(Gr - Gs[i * 64 + cc]);
+                aE = mfma_f32_k4(dMs[(r + rr) * C + i], b, aE);
+                aQ = mfma_f32_k4(dAqs[(r + rr) * C + i], b, aQ);
             }
         }
-    } else {
-        // sums over t for the rows i of block bi
-        for (int pass = 0; pass < 2; ++pass) {
-            const int bi = w == 2 ? (pass ? 3 : 0) : (pass ? 2 : 1);
-            float dk[16];
+        for (int b2 = w + 1; b2 < 4; ++b2) {
+            const int r = 16 * b2;
+            const float Gr = Gs[r * 64 + cc];
+            f4 acc = {0, 0, 0, 0};
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii) dk[ii] = 0.f;
-            for (int bt = bi + 1; bt < 4; ++bt) {
-                const int r = 16 * bt;
-                const float Gr = Gs[r * 64 + cl];
-                float tmp[16];
-#pragma unroll
-                for (int ii = 0; ii < 16; ++ii) tmp[ii] = 0.f;
-                for (int tt = 0; tt < 16; ++tt) {
-                    const int t = r + tt;
-                    const float F = exp2f(Gs[t * 64 + cl] - Gr);
-                    const float et = Es[t * 64 + cl] * F, qt = Qs[t * 64 + cl] * F;
-#pragma unroll
-                    for (int ii = 0; ii < 16; ++ii)
-                        tmp[ii] += dMs[t * C + 16 * bi + ii] * et + dAqs[t * C + 16 * bi + ii] * qt;
-                }
-#pragma unroll
-                for (int ii = 0; ii < 16; ++ii) dk[ii] += exp2f(Gr - Gs[(16 * bi + ii) * 64 + cl]) * tmp[ii];
+            for (int k0 = 0; k0 < 16; k0 += 4) {
+                const int t = r + k0 + gg;
+                const float f = exp2f(Gs[t * 64 + cc] - Gr);
+                acc = mfma_f32_k4(dMs[t * C + 16 * w + rr], Es[t * 64 + cc] * f, acc);
+                acc = mfma_f32_k4(dAqs[t * C + 16 * w + rr], Qs[t * 64 + cc] * f, acc);
             }
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii) {
-                const int i = 16 * bi + ii;
-                const float Gi = Gs[i * 64 + cl];
-#pragma unroll
-                for (int tt = ii; tt < 16; ++tt) {
-                    const int t = 16 * bi + tt;
-                    const float E = exp2f(Gs[t * 64 + cl] - Gi);
-                    float x = dAqs[t * C + i] * Qs[t * 64 + cl];
-                    if (tt > ii) x += dMs[t * C + i] * Es[t * 64 + cl];
-                    dk[ii] += x * E;
-                }
-                Ik[i * 64 + cl] = dk[ii];
+            for (int s = 0; s < 4; ++s) {
+                const int i = 16 * w + 4 * gg + s;
+                aK[s] += acc[s] * exp2f(Gs[r * 64 + 16 * ct + rr] - Gs[i * 64 + 16 * ct + rr]);
             }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int t = 16 * w + 4 * gg + s, ch = 16 * ct + rr;
+            const float F = w > 0 ? exp2f(Gs[t * 64 + ch] - Gs[16 * w * 64 + ch]) : 0.f;
+            Te[t * 64 + ch] = aE[s] * F;
+            Tq[t * 64 + ch] = aQ[s] * F;
+            Ik[t * 64 + ch] = aK[s];
         }
     }
     __syncthreads();
+
+    // pairs inside block w, lane = channel: E = e^{G_t - G_i}, i <= t
+    float sde[16], sdq[16], sdk[16];
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+        const int t = 16 * w + tt;
+        sde[tt] = Te[t * 64 + cl];
+        sdq[tt] = Tq[t * 64 + cl];
+        sdk[tt] = Ik[t * 64 + cl];
+    }
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+        const int t = 16 * w + tt;
+        const float Gt = Gs[t * 64 + cl], et = Es[t * 64 + cl], qt = Qs[t * 64 + cl];
+#pragma unroll
+        for (int ii = 0; ii <= tt; ++ii) {
+            const int i = 16 * w + ii;
+            const float E = exp2f(Gt - Gs[i * 64 + cl]), ki = Ks[i * 64 + cl];
+            const float m = dMs[t * C + i], aq = dAqs[t * C + i];
+            if (ii < tt) {
+                sde[tt] += m * ki * E;
+                sdk[ii] += m * et * E;
+            }
+            sdq[tt] += aq * ki * E;
+            sdk[ii] += aq * qt * E;
+        }
+    }
 
     // chain rule for the rows of block w
     const size_t ub = (size_t)u * C * DK;
@@ -706,7 +769,7 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
         const float G = Gs[t * 64 + cl], eg = exp2f(G), kg = exp2f(GC - G);
         const float dEt = ws.dEt[ub + t * DK + c], dQt = ws.dQt[ub + t * DK + c], dKh = ws.dKh[ub + t * DK + c];
         const float e = Es[t * 64 + cl], qs = Qs[t * 64 + cl], kk = Ks[t * 64 + cl];
-        const float te = Te[t * 64 + cl], tq = Tq[t * 64 + cl], ik = Ik[t * 64 + cl];
+        const float te = sde[tt], tq = sdq[tt], ik = sdk[tt];
         de[tt] = eg * dEt + te;
         dq[tt] = eg * dQt + tq;
         dk[tt] = kg * dKh + ik;
@@ -744,12 +807,28 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
     if (cg == 0) {
         const uint16_t *v = reinterpret_cast<const uint16_t *>(p.v), *wr = reinterpret_cast<const uint16_t *>(p.write);
         const float *dRu = ws.dR + (size_t)u * C * DV;
-        for (int i = tid; i < L * DV; i += 256) {
-            const int t = i / DV, j = i % DV;
-            const size_t kv = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DV + j;
-            const float dz = dRu[t * DV + j], om = sigmoid_f32(bf16_to_f32(wr[kv])), vv = bf16_to_f32(v[kv]);
-            p.dv[kv] = dz * om;
-            p.dwrite[kv] = dz * vv * om * (1.f - om);
+#pragma unroll
+        for (int it = 0; it < C * DV / 8 / 256; ++it) {
+            const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
+            const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
+            f4 vv[2], om[2];
+            bf8_to_f32(*reinterpret_cast<const u16x8 *>(v + kv), vv[0], vv[1]);
+            bf8_to_f32(*reinterpret_cast<const u16x8 *>(wr + kv), om[0], om[1]);
+            f4 dz[2] = {*reinterpret_cast<const f4 *>(dRu + t * DV + j), *reinterpret_cast<const f4 *>(dRu + t * DV + j + 4)};
+            if (t < L) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    f4 o1, o2;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const float sg = sigmoid_f32(om[hh][x]);
+                        o1[x] = dz[hh][x] * sg;
+                        o2[x] = dz[hh][x] * vv[hh][x] * sg * (1.f - sg);
+                    }
+                    *reinterpret_cast<f4 *>(p.dv + kv + 4 * hh) = o1;
+                    *reinterpret_cast<f4 *>(p.dwrite + kv + 4 * hh) = o2;
+                }
+            }
         }
     }
 }
