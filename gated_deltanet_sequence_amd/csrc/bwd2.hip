@@ -83,6 +83,9 @@ __device__ __forceinline__ void bf8_to_f32(const u16x8 x, f4 &lo, f4 &hi) {
     }
 }
 
+// 2^x on the hardware unit (arguments here are <= 0: every decay factor is at most 1)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ size_t unit_of(int bb, int hv, int n, int Hv, int NC) {
     return ((size_t)bb * Hv + hv) * NC + n;
 }
@@ -104,29 +107,47 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     const uint16_t *v = reinterpret_cast<const uint16_t *>(p.v), *wr = reinterpret_cast<const uint16_t *>(p.write);
 
     // 1. gates: G (log2 units, 0 past T), e = sigmoid(erase) k, qs = scale q, k; z to the workspace.
-    //    Rows past T read the last token (L >= 1) and are zeroed, so every load is unconditional.
-    const bf16_t *qb = reinterpret_cast<const bf16_t *>(p.q), *kb = reinterpret_cast<const bf16_t *>(p.k);
-    const bf16_t *ab = reinterpret_cast<const bf16_t *>(p.a), *eb = reinterpret_cast<const bf16_t *>(p.erase);
-#pragma unroll
-    for (int it = 0; it < C * DK / 4 / 256; ++it) {
-        const int i = tid + 256 * it, t = i / (DK / 4), c = (i % (DK / 4)) * 4, tl = min(t, L - 1);
-        const size_t kq = (((size_t)bb * p.T + t0 + tl) * p.Hk + hk) * DK + c;
-        const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
-        const f4 kk = ld4(kb, kq), qq = ld4(qb, kq), aa = ld4(ab, ka), ee = ld4(eb, ka);
+    //    Thread = (4 channels, a group of RPT consecutive rows); rows past T read the last
+    //    token (L >= 1) and are zeroed, so every load is unconditional.  The in-chunk prefix
+    //    of g is taken over the thread's rows, then the totals of the earlier row groups
+    //    are added.
+    constexpr int NQ = DK / 4, NRG = 256 / NQ, RPT = C / NRG;
+    __shared__ float tot[NRG * DK];
+    {
+        const bf16_t *qb = reinterpret_cast<const bf16_t *>(p.q), *kb = reinterpret_cast<const bf16_t *>(p.k);
+        const bf16_t *ab = reinterpret_cast<const bf16_t *>(p.a), *eb = reinterpret_cast<const bf16_t *>(p.erase);
+        const int c = (tid % NQ) * 4, rg = tid / NQ;
         const f4 al = *reinterpret_cast<const f4 *>(p.A_log + (size_t)hv * DK + c);
-        const float on = t < L ? 1.f : 0.f;
-        f4 gv, ev, qv, kv;
+        f4 rate;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            gv[j] = -expf(al[j]) * softplus_f32(aa[j]) * LOG2E * on;
-            ev[j] = sigmoid_f32(ee[j]) * kk[j] * on;
-            qv[j] = p.scale * qq[j] * on;
-            kv[j] = kk[j] * on;
+        for (int j = 0; j < 4; ++j) rate[j] = -exp_fast(al[j]) * LOG2E;
+        f4 run = {0, 0, 0, 0}, gr[RPT];
+#pragma unroll
+        for (int x = 0; x < RPT; ++x) {
+            const int t = rg * RPT + x, tl = min(t, L - 1);
+            const size_t kq = (((size_t)bb * p.T + t0 + tl) * p.Hk + hk) * DK + c;
+            const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
+            const f4 kk = ld4(kb, kq), qq = ld4(qb, kq), aa = ld4(ab, ka), ee = ld4(eb, ka);
+            const float on = t < L ? 1.f : 0.f;
+            f4 ev, qv, kv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                run[j] += rate[j] * softplus_fast(aa[j]) * on;
+                ev[j] = sigmoid_fast(ee[j]) * kk[j] * on;
+                qv[j] = p.scale * qq[j] * on;
+                kv[j] = kk[j] * on;
+            }
+            gr[x] = run;
+            *reinterpret_cast<f4 *>(Es + t * LS + c) = ev;
+            *reinterpret_cast<f4 *>(Qs + t * LS + c) = qv;
+            *reinterpret_cast<f4 *>(Ks + t * LS + c) = kv;
         }
-        *reinterpret_cast<f4 *>(Gs + t * LS + c) = gv;
-        *reinterpret_cast<f4 *>(Es + t * LS + c) = ev;
-        *reinterpret_cast<f4 *>(Qs + t * LS + c) = qv;
-        *reinterpret_cast<f4 *>(Ks + t * LS + c) = kv;
+        *reinterpret_cast<f4 *>(tot + rg * DK + c) = run;
+        __syncthreads();
+        f4 off = {0, 0, 0, 0};
+        for (int x = 0; x < rg; ++x) off += *reinterpret_cast<const f4 *>(tot + x * DK + c);
+#pragma unroll
+        for (int x = 0; x < RPT; ++x) *reinterpret_cast<f4 *>(Gs + (rg * RPT + x) * LS + c) = gr[x] + off;
     }
     float *Zu = ws.Z + (size_t)u * C * DV;
 #pragma unroll
@@ -139,20 +160,11 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
         const float on = t < L ? 1.f : 0.f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            vl[x] = sigmoid_f32(wl[x]) * vl[x] * on;
-            vh[x] = sigmoid_f32(wh[x]) * vh[x] * on;
+            vl[x] = sigmoid_fast(wl[x]) * vl[x] * on;
+            vh[x] = sigmoid_fast(wh[x]) * vh[x] * on;
         }
         *reinterpret_cast<f4 *>(Zu + t * DV + j) = vl;
         *reinterpret_cast<f4 *>(Zu + t * DV + j + 4) = vh;
-    }
-    __syncthreads();
-    // 2. in-chunk inclusive prefix per channel
-    for (int c = tid; c < DK; c += 256) {
-        float s = 0.f;
-        for (int t = 0; t < C; ++t) {
-            s += Gs[t * LS + c];
-            Gs[t * LS + c] = s;
-        }
     }
     __syncthreads();
     // 3. images, gamma_C and the diagonal of Aq (q_t . k_t, no decay)
@@ -165,14 +177,14 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
             f4 eg, kg;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                eg[j] = exp2f(G[j]);
-                kg[j] = exp2f(GC[j] - G[j]);
+                eg[j] = ex2(G[j]);
+                kg[j] = ex2(GC[j] - G[j]);
             }
             *reinterpret_cast<f4 *>(ws.Et + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Es + t * LS + c) * eg;
             *reinterpret_cast<f4 *>(ws.Qt + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Qs + t * LS + c) * eg;
             *reinterpret_cast<f4 *>(ws.Kh + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Ks + t * LS + c) * kg;
         }
-        for (int c = tid; c < DK; c += 256) ws.gC[(size_t)u * DK + c] = exp2f(Gs[(C - 1) * LS + c]);
+        for (int c = tid; c < DK; c += 256) ws.gC[(size_t)u * DK + c] = ex2(Gs[(C - 1) * LS + c]);
         if (tid < C) {
             float s = 0.f;
             for (int c = 0; c < DK; ++c) s += Qs[tid * LS + c] * Ks[tid * LS + c];
@@ -194,7 +206,7 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
             for (int c0 = 0; c0 < DK; c0 += 4) {
                 const int c = c0 + gg;
                 const float Gr = Gs[r * LS + c];
-                const float ft = exp2f(Gs[t * LS + c] - Gr), b = Ks[i * LS + c] * exp2f(Gr - Gs[i * LS + c]);
+                const float ft = ex2(Gs[t * LS + c] - Gr), b = Ks[i * LS + c] * ex2(Gr - Gs[i * LS + c]);
                 mO[x] = mfma_f32_k4(Es[t * LS + c] * ft, b, mO[x]);
                 qO[x] = mfma_f32_k4(Qs[t * LS + c] * ft, b, qO[x]);
             }
@@ -216,11 +228,11 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
                 const int c = c0 + gg;
                 float ae = 0.f, aq = 0.f, b = 0.f;
                 if (tsec) {
-                    const float ft = exp2f(Gs[t * LS + c] - Gs[rt * LS + c]);
+                    const float ft = ex2(Gs[t * LS + c] - Gs[rt * LS + c]);
                     ae = Es[t * LS + c] * ft;
                     aq = Qs[t * LS + c] * ft;
                 } else {
-                    b = Ks[i * LS + c] * exp2f(Gs[ri * LS + c] - Gs[i * LS + c]);
+                    b = Ks[i * LS + c] * ex2(Gs[ri * LS + c] - Gs[i * LS + c]);
                 }
                 aM = mfma_f32_k4(ae, b, aM);
                 aQ = mfma_f32_k4(aq, b, aQ);
@@ -655,8 +667,11 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
     const int tid = threadIdx.x, w = tid >> 6, cl = tid & 63, c = 64 * cg + cl, rr = cl & 15, gg = cl >> 4;
     const uint16_t *q = reinterpret_cast<const uint16_t *>(p.q), *k = reinterpret_cast<const uint16_t *>(p.k);
     const uint16_t *a = reinterpret_cast<const uint16_t *>(p.a), *er = reinterpret_cast<const uint16_t *>(p.erase);
-    const float Al = p.A_log[(size_t)hv * DK + c], rate = expf(Al);
+    const float Al = p.A_log[(size_t)hv * DK + c], rate = exp_fast(Al);
 
+    // gates of the rows of block w; the in-chunk prefix of g runs over the block's rows,
+    // then the totals of the earlier blocks are added
+    float grun = 0.f, gpre[16];
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
         const int t = 16 * w + tt, tl = min(t, L - 1);
@@ -664,23 +679,23 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
         const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
         const float on = t < L ? 1.f : 0.f;
         const float kv = bf16_to_f32(k[kq]) * on;
-        const float gv = -rate * softplus_f32(bf16_to_f32(a[ka])) * LOG2E * on;
-        const float ev = sigmoid_f32(bf16_to_f32(er[ka])) * kv;
+        grun += -rate * softplus_fast(bf16_to_f32(a[ka])) * LOG2E * on;
+        const float ev = sigmoid_fast(bf16_to_f32(er[ka])) * kv;
         const float qv = p.scale * bf16_to_f32(q[kq]) * on;
-        Gs[t * 64 + cl] = gv;
+        gpre[tt] = grun;
         Ks[t * 64 + cl] = kv;
         Es[t * 64 + cl] = ev;
         Qs[t * 64 + cl] = qv;
     }
+    blk[w * 64 + cl] = grun;
     lds_load<C, C, C>(dMs, ws.dM + (size_t)u * C * C);
     lds_load<C, C, C>(dAqs, ws.dAq + (size_t)u * C * C);
     __syncthreads();
-    if (w == 0) {
-        float s = 0.f;
-        for (int t = 0; t < C; ++t) {
-            s += Gs[t * 64 + cl];
-            Gs[t * 64 + cl] = s;
-        }
+    {
+        float off = 0.f;
+        for (int x = 0; x < w; ++x) off += blk[x * 64 + cl];
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) Gs[(16 * w + tt) * 64 + cl] = gpre[tt] + off;
     }
     __syncthreads();
 
@@ -699,7 +714,7 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
 #pragma unroll 4
             for (int i0 = 0; i0 < r; i0 += 4) {
                 const int i = i0 + gg;
-                const float b = Ks[i * 64 + cc] * exp2f(Gr - Gs[i * 64 + cc]);
+                const float b = Ks[i * 64 + cc] * ex2(Gr - Gs[i * 64 + cc]);
                 aE = mfma_f32_k4(dMs[(r + rr) * C + i], b, aE);
                 aQ = mfma_f32_k4(dAqs[(r + rr) * C + i], b, aQ);
             }
@@ -711,20 +726,20 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
 #pragma unroll
             for (int k0 = 0; k0 < 16; k0 += 4) {
                 const int t = r + k0 + gg;
-                const float f = exp2f(Gs[t * 64 + cc] - Gr);
+                const float f = ex2(Gs[t * 64 + cc] - Gr);
                 acc = mfma_f32_k4(dMs[t * C + 16 * w + rr], Es[t * 64 + cc] * f, acc);
                 acc = mfma_f32_k4(dAqs[t * C + 16 * w + rr], Qs[t * 64 + cc] * f, acc);
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int i = 16 * w + 4 * gg + s;
-                aK[s] += acc[s] * exp2f(Gs[r * 64 + 16 * ct + rr] - Gs[i * 64 + 16 * ct + rr]);
+                aK[s] += acc[s] * ex2(Gs[r * 64 + 16 * ct + rr] - Gs[i * 64 + 16 * ct + rr]);
             }
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int t = 16 * w + 4 * gg + s, ch = 16 * ct + rr;
-            const float F = w > 0 ? exp2f(Gs[t * 64 + ch] - Gs[16 * w * 64 + ch]) : 0.f;
+            const float F = w > 0 ? ex2(Gs[t * 64 + ch] - Gs[16 * w * 64 + ch]) : 0.f;
             Te[t * 64 + ch] = aE[s] * F;
             Tq[t * 64 + ch] = aQ[s] * F;
             Ik[t * 64 + ch] = aK[s];
@@ -748,7 +763,7 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
 #pragma unroll
         for (int ii = 0; ii <= tt; ++ii) {
             const int i = 16 * w + ii;
-            const float E = exp2f(Gt - Gs[i * 64 + cl]), ki = Ks[i * 64 + cl];
+            const float E = ex2(Gt - Gs[i * 64 + cl]), ki = Ks[i * 64 + cl];
             const float m = dMs[t * C + i], aq = dAqs[t * C + i];
             if (ii < tt) {
                 sde[tt] += m * ki * E;
@@ -766,7 +781,7 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
         const int t = 16 * w + tt;
-        const float G = Gs[t * 64 + cl], eg = exp2f(G), kg = exp2f(GC - G);
+        const float G = Gs[t * 64 + cl], eg = ex2(G), kg = ex2(GC - G);
         const float dEt = ws.dEt[ub + t * DK + c], dQt = ws.dQt[ub + t * DK + c], dKh = ws.dKh[ub + t * DK + c];
         const float e = Es[t * 64 + cl], qs = Qs[t * 64 + cl], kk = Ks[t * 64 + cl];
         const float te = sde[tt], tq = sdq[tt], ik = sdk[tt];
@@ -781,7 +796,7 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
     blk[w * 64 + cl] = bsum;
     gcp[w * 64 + cl] = sKK;
     __syncthreads();
-    float carry = gcp[cl] + gcp[64 + cl] + gcp[128 + cl] + gcp[192 + cl] + ws.dgC[(size_t)u * DK + c] * exp2f(GC);
+    float carry = gcp[cl] + gcp[64 + cl] + gcp[128 + cl] + gcp[192 + cl] + ws.dgC[(size_t)u * DK + c] * ex2(GC);
     for (int x = w + 1; x < 4; ++x) carry += blk[x * 64 + cl];
     float alsum = 0.f;
 #pragma unroll
@@ -790,11 +805,11 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
         const int t = 16 * w + tt;
         if (t < L) {
             const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
-            const float av = bf16_to_f32(a[ka]), beta = sigmoid_f32(bf16_to_f32(er[ka]));
+            const float av = bf16_to_f32(a[ka]), beta = sigmoid_fast(bf16_to_f32(er[ka]));
             const float kk = Ks[t * 64 + cl];
             const float dg = carry;  // natural-log units
-            p.da[ka] = -dg * rate * sigmoid_f32(av);
-            alsum += dg * (-rate * softplus_f32(av));
+            p.da[ka] = -dg * rate * sigmoid_fast(av);
+            alsum += dg * (-rate * softplus_fast(av));
             p.derase[ka] = de[tt] * kk * beta * (1.f - beta);
             ws.dqh[ka] = p.scale * dq[tt];
             ws.dkh[ka] = dk[tt] + de[tt] * beta;
@@ -821,7 +836,7 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
                     f4 o1, o2;
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
-                        const float sg = sigmoid_f32(om[hh][x]);
+                        const float sg = sigmoid_fast(om[hh][x]);
                         o1[x] = dz[hh][x] * sg;
                         o2[x] = dz[hh][x] * vv[hh][x] * sg * (1.f - sg);
                     }

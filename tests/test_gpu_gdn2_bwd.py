@@ -20,11 +20,11 @@ pytestmark = pytest.mark.gpu
 
 # The path computes in float32 from exactly widened bfloat16 inputs, so its error is
 # float32 rounding amplified by the chunk algebra ((I + M)^{-1}, products over 64-token
-# chunks, the state chain).  Measured: at most 9e-6 relative L2 on the per-token
-# gradients and the initial-state gradient, so 1e-4 leaves a 10x margin and stays 20x
+# chunks, the state chain).  Measured: at most 1.1e-5 relative L2 on the per-token
+# gradients and the initial-state gradient, so 1e-4 leaves a 9x margin and stays 20x
 # below the bfloat16 bound of 2e-3.  dA_log is a sum over every token of dg * g with
 # both signs: its relative error is that of dg times the cancellation ratio
-# sum|dg g| / |sum dg g| (measured up to 5.6e-5), hence its own bound of 5e-4.
+# sum|dg g| / |sum dg g| (measured up to 6.4e-5), hence its own bound of 5e-4.
 TOL_BWD = 1e-4
 TOL_SUM = 5e-4
 NAMES = ["dq", "dk", "dv", "da", "d_erase", "d_write", "dA_log", "dS0"]
