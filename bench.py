@@ -46,7 +46,8 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN prefill tokens/s at T=4096 (16k/64v heads, d=128) + decode-step HBM GB/s"
 PEAK_MFMA_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
-PEAK_MFMA_F32_TFLOPS = 157.3    # MI355X dense fp32 matrix (and packed fp32 vector) peak
+PEAK_MFMA_F32_TFLOPS = 157.3    # MI355X fp32 matrix peak, equal to the packed fp32 vector peak:
+                                # 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
 
 # Algorithmic work per (token, value head) at d_k = d_v = 128, chunk C = 64, G = 4
 # value heads per key head (flop = 2 x multiply-accumulate):
@@ -594,7 +595,8 @@ def bench_gdn2_bwd(args, torch, gdn, synth):
                             Dk=spec.Dk, Dv=spec.Dv, chunk=spec.chunk, input_dtype="bf16",
                             grad_dtype="f32", arithmetic="f32"),
                 stages_us={n: round(t * 1e3, 2) for n, t in zip(names, stage)},
-                roofline=dict(kernel=names[dom], bound="mfma", achieved=round(tf, 2), peak=PEAK_MFMA_F32_TFLOPS,
+                roofline=dict(kernel=names[dom], bound=("alu" if names[dom] in ("g2b_local", "g2b_prep") else "mfma"),
+                              achieved=round(tf, 2), peak=PEAK_MFMA_F32_TFLOPS,
                               unit="TFLOP/s", frac=round(tf / PEAK_MFMA_F32_TFLOPS, 4), flop_per_launch=dflop,
                               avg_launch_ms=round(stage[dom], 5), traffic=None),
                 path=dict(flop=total_flop, tflops=round(total_flop / (ms * 1e-3) / 1e12, 2),
