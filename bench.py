@@ -126,9 +126,12 @@ TRAFFIC_FILES = {
     # (names with float16 template arguments come out mangled: Lb0E / Lb1E is the bool)
     "scan_split_kernel": (r"scan_split_kernel(<[^>]*false>|I.*Lb0E)", "scan_split_kernel_prefill_t4096_traffic.md"),
     "chunk_local_kernel": (r"chunk_local_kernel", "chunk_local_kernel_prefill_t4096_traffic.md"),
-    "decode_kernel": (r"decode_kernel", "decode_kernel_decode_b256_traffic.md"),
+    "decode_kernel": (r"decode_kernel<[^>]*false>", "decode_kernel_decode_b256_traffic.md"),
     "scan_split_kernel_gdn2": (r"scan_split_kernel(<[^>]*true>|I.*Lb1E)", "scan_split_kernel_gdn2_t8192_traffic.md"),
     "chunk_local2_kernel": (r"chunk_local2_kernel", "chunk_local2_kernel_gdn2_t8192_traffic.md"),
+    "g2b_local": (r"g2b_local", "g2b_local_gdn2_bwd_t8192_traffic.md"),
+    "gated_rmsnorm_kernel": (r"gated_rmsnorm_kernel", "gated_rmsnorm_kernel_t4096_traffic.md"),
+    "causal_conv1d_kernel": (r"causal_conv1d_kernel", "causal_conv1d_kernel_t4096_traffic.md"),
 }
 
 
@@ -244,7 +247,7 @@ def summarize_stats(d, out_name, command):
              "| kernel | calls | total ms | average us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
-        short = re.sub(r"\(.*", "", name)[:90]
+        short = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", ""))[:90]
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
@@ -444,6 +447,7 @@ def bench_epilogue(args, torch, gdn, synth):
                 config=dict(workload="gated_rmsnorm_t4096", rows=4096 * 64, d=128, dtype="bf16", gate="silu"),
                 roofline=dict(kernel="gated_rmsnorm_kernel", bound="hbm", achieved=round(gbs, 1),
                               peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                              traffic=stored_traffic("gated_rmsnorm_kernel"),
                               bytes_per_launch=nbytes, avg_launch_ms=round(ms, 5)))
 
 
@@ -484,6 +488,7 @@ def bench_prologue(args, torch, gdn, synth):
                             activation="silu"),
                 roofline=dict(kernel="causal_conv1d_kernel", bound="hbm", achieved=round(gbs, 1),
                               peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                              traffic=stored_traffic("causal_conv1d_kernel"),
                               bytes_per_launch=nbytes, avg_launch_ms=round(ms, 5)))
 
 
@@ -598,7 +603,7 @@ def bench_gdn2_bwd(args, torch, gdn, synth):
                 roofline=dict(kernel=names[dom], bound=("alu" if names[dom] in ("g2b_local", "g2b_prep") else "mfma"),
                               achieved=round(tf, 2), peak=PEAK_MFMA_F32_TFLOPS,
                               unit="TFLOP/s", frac=round(tf / PEAK_MFMA_F32_TFLOPS, 4), flop_per_launch=dflop,
-                              avg_launch_ms=round(stage[dom], 5), traffic=None),
+                              avg_launch_ms=round(stage[dom], 5), traffic=stored_traffic(names[dom])),
                 path=dict(flop=total_flop, tflops=round(total_flop / (ms * 1e-3) / 1e12, 2),
                           f32_frac=round(total_flop / (ms * 1e-3) / 1e12 / PEAK_MFMA_F32_TFLOPS, 4)))
 
