@@ -652,7 +652,7 @@ def main():
         summarize_pmc(*args.summarize_pmc)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
+        print(f"bench.py: runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
               f"sharding of the path is a design note, not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
