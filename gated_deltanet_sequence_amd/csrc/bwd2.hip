@@ -56,19 +56,19 @@ __device__ __forceinline__ void mma(f4 &acc, const float *a0, const float *b0) {
 // ROWS x COLS float32 block (row-major, contiguous) into LDS rows of stride LS,
 // times f.  Compile-time trip counts: each thread issues its loads in batches of
 // 8 before storing them, so the global latency is paid once per batch.
-template <int ROWS, int COLS, int LS>
+template <int ROWS, int COLS, int LS, int NT = 256>
 __device__ __forceinline__ void lds_load(float *dst, const float *__restrict__ src, float f = 1.f) {
-    constexpr int N = ROWS * COLS / 4, PER = N / 256, BT = PER < 8 ? PER : 8;
-    static_assert(N % 256 == 0 && PER % BT == 0, "block size");
+    constexpr int N = ROWS * COLS / 4, PER = N / NT, BT = PER < 8 ? PER : 8;
+    static_assert(N % NT == 0 && PER % BT == 0, "block size");
 #pragma unroll
     for (int b0 = 0; b0 < PER; b0 += BT) {
         f4 x[BT];
 #pragma unroll
         for (int j = 0; j < BT; ++j)
-            x[j] = *reinterpret_cast<const f4 *>(src + (size_t)(threadIdx.x + (b0 + j) * 256) * 4);
+            x[j] = *reinterpret_cast<const f4 *>(src + (size_t)(threadIdx.x + (b0 + j) * NT) * 4);
 #pragma unroll
         for (int j = 0; j < BT; ++j) {
-            const int i = threadIdx.x + (b0 + j) * 256, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
+            const int i = threadIdx.x + (b0 + j) * NT, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
             *reinterpret_cast<f4 *>(dst + r * LS + c) = x[j] * f;
         }
     }
@@ -650,31 +650,47 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
 }
 
 // ---------------------------------------------------------------------------
-// g2b_local: one work-group per (chunk, 64 key channels).  Wave w owns the
-// rows of 16-token block w: first the block pairs below the diagonal on the
-// matrix cores (rows t of block w against every earlier block, rows i of block
-// w against every later block), then the pairs inside block w on the vector
-// unit (lane = channel), then the chain rule for its rows.
+// g2b_local: one work-group of 8 waves per (chunk, 64 key channels).  Wave w
+// owns rows 8w .. 8w+7, half of 16-token block b = w/2: first the block pairs
+// below the diagonal on the matrix cores for block b and two of its four
+// 16-channel tiles (rows t of block b against every earlier block, rows i of
+// block b against every later block), then the pairs inside block b that its
+// own rows take part in, on the vector unit (lane = channel), then the chain
+// rule for its rows.
 // ---------------------------------------------------------------------------
+constexpr int LOCAL_NT = 512;
+
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
-    constexpr int CG = DK / 64;
+__global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
+    constexpr int CG = DK / 64, NW = LOCAL_NT / 64;
     __shared__ __attribute__((aligned(16))) float Gs[C * 64], Ks[C * 64], Es[C * 64], Qs[C * 64], dMs[C * C],
-        dAqs[C * C], Te[C * 64], Tq[C * 64], Ik[C * 64], blk[4 * 64], gcp[4 * 64], alp[4 * 64];
+        dAqs[C * C], Te[C * 64], Tq[C * 64], Ik[C * 64], blk[NW * 64], gcp[NW * 64], alp[NW * 64];
     const int cg = blockIdx.x % CG, u = blockIdx.x / CG, NC = p.NC;
     const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv), hk = hv / (p.Hv / p.Hk);
     const int t0 = n * C, L = min(C, p.T - t0);
     const int tid = threadIdx.x, w = tid >> 6, cl = tid & 63, c = 64 * cg + cl, rr = cl & 15, gg = cl >> 4;
+    const int b = w >> 1, half = w & 1, r0 = 8 * w;  // block, half of it, first own row
     const uint16_t *q = reinterpret_cast<const uint16_t *>(p.q), *k = reinterpret_cast<const uint16_t *>(p.k);
     const uint16_t *a = reinterpret_cast<const uint16_t *>(p.a), *er = reinterpret_cast<const uint16_t *>(p.erase);
     const float Al = p.A_log[(size_t)hv * DK + c], rate = exp_fast(Al);
 
-    // gates of the rows of block w; the in-chunk prefix of g runs over the block's rows,
-    // then the totals of the earlier blocks are added
-    float grun = 0.f, gpre[16];
+    // inputs of the chain rule, loaded first so that their latency overlaps the pair sums
+    const size_t ub = (size_t)u * C * DK;
+    float pdE[8], pdQ[8], pdK[8];
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-        const int t = 16 * w + tt, tl = min(t, L - 1);
+    for (int x = 0; x < 8; ++x) {
+        pdE[x] = ws.dEt[ub + (r0 + x) * DK + c];
+        pdQ[x] = ws.dQt[ub + (r0 + x) * DK + c];
+        pdK[x] = ws.dKh[ub + (r0 + x) * DK + c];
+    }
+    const float pgC = ws.dgC[(size_t)u * DK + c];
+
+    // gates of the wave's rows; the in-chunk prefix of g runs over them, then the
+    // totals of the earlier row groups are added
+    float grun = 0.f, gpre[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        const int t = r0 + x, tl = min(t, L - 1);
         const size_t kq = (((size_t)bb * p.T + t0 + tl) * p.Hk + hk) * DK + c;
         const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
         const float on = t < L ? 1.f : 0.f;
@@ -682,44 +698,44 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
         grun += -rate * softplus_fast(bf16_to_f32(a[ka])) * LOG2E * on;
         const float ev = sigmoid_fast(bf16_to_f32(er[ka])) * kv;
         const float qv = p.scale * bf16_to_f32(q[kq]) * on;
-        gpre[tt] = grun;
+        gpre[x] = grun;
         Ks[t * 64 + cl] = kv;
         Es[t * 64 + cl] = ev;
         Qs[t * 64 + cl] = qv;
     }
     blk[w * 64 + cl] = grun;
-    lds_load<C, C, C>(dMs, ws.dM + (size_t)u * C * C);
-    lds_load<C, C, C>(dAqs, ws.dAq + (size_t)u * C * C);
+    lds_load<C, C, C, LOCAL_NT>(dMs, ws.dM + (size_t)u * C * C);
+    lds_load<C, C, C, LOCAL_NT>(dAqs, ws.dAq + (size_t)u * C * C);
     __syncthreads();
     {
         float off = 0.f;
         for (int x = 0; x < w; ++x) off += blk[x * 64 + cl];
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) Gs[(16 * w + tt) * 64 + cl] = gpre[tt] + off;
+        for (int x = 0; x < 8; ++x) Gs[(r0 + x) * 64 + cl] = gpre[x] + off;
     }
     __syncthreads();
 
     // block pairs below the diagonal, 16 channels at a time (MFMA: lane supplies
     // A[rr][gg], B[gg][rr]; accumulator element s is row 4 gg + s, channel rr).
-    //   rows t of block w, reference r = 16 w (i < r <= t):
+    //   rows t of block b, reference r = 16 b (i < r <= t):
     //     de_t  = e^{G_t - G_r} sum_{i < r} dM_ti  k_i e^{G_r - G_i}, dqs_t likewise with dAq
-    //   rows i of block w, each later block b with reference r = 16 b:
-    //     dk_i += e^{G_r - G_i} sum_{t in b} dM_ti e_t e^{G_t - G_r} + dAq_ti qs_t e^{G_t - G_r}
-    for (int ct = 0; ct < 4; ++ct) {
+    //   rows i of block b, each later block b2 with reference r = 16 b2:
+    //     dk_i += e^{G_r - G_i} sum_{t in b2} dM_ti e_t e^{G_t - G_r} + dAq_ti qs_t e^{G_t - G_r}
+    for (int ct = 2 * half; ct < 2 * half + 2; ++ct) {
         const int cc = 16 * ct + rr;
         f4 aE = {0, 0, 0, 0}, aQ = {0, 0, 0, 0}, aK = {0, 0, 0, 0};
-        if (w > 0) {
-            const int r = 16 * w;
+        if (b > 0) {
+            const int r = 16 * b;
             const float Gr = Gs[r * 64 + cc];
 #pragma unroll 4
             for (int i0 = 0; i0 < r; i0 += 4) {
                 const int i = i0 + gg;
-                const float b = Ks[i * 64 + cc] * ex2(Gr - Gs[i * 64 + cc]);
-                aE = mfma_f32_k4(dMs[(r + rr) * C + i], b, aE);
-                aQ = mfma_f32_k4(dAqs[(r + rr) * C + i], b, aQ);
+                const float bv = Ks[i * 64 + cc] * ex2(Gr - Gs[i * 64 + cc]);
+                aE = mfma_f32_k4(dMs[(r + rr) * C + i], bv, aE);
+                aQ = mfma_f32_k4(dAqs[(r + rr) * C + i], bv, aQ);
             }
         }
-        for (int b2 = w + 1; b2 < 4; ++b2) {
+        for (int b2 = b + 1; b2 < 4; ++b2) {
             const int r = 16 * b2;
             const float Gr = Gs[r * 64 + cc];
             f4 acc = {0, 0, 0, 0};
@@ -727,19 +743,19 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
             for (int k0 = 0; k0 < 16; k0 += 4) {
                 const int t = r + k0 + gg;
                 const float f = ex2(Gs[t * 64 + cc] - Gr);
-                acc = mfma_f32_k4(dMs[t * C + 16 * w + rr], Es[t * 64 + cc] * f, acc);
-                acc = mfma_f32_k4(dAqs[t * C + 16 * w + rr], Qs[t * 64 + cc] * f, acc);
+                acc = mfma_f32_k4(dMs[t * C + 16 * b + rr], Es[t * 64 + cc] * f, acc);
+                acc = mfma_f32_k4(dAqs[t * C + 16 * b + rr], Qs[t * 64 + cc] * f, acc);
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int i = 16 * w + 4 * gg + s;
+                const int i = 16 * b + 4 * gg + s;
                 aK[s] += acc[s] * ex2(Gs[r * 64 + 16 * ct + rr] - Gs[i * 64 + 16 * ct + rr]);
             }
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int t = 16 * w + 4 * gg + s, ch = 16 * ct + rr;
-            const float F = w > 0 ? ex2(Gs[t * 64 + ch] - Gs[16 * w * 64 + ch]) : 0.f;
+            const int t = 16 * b + 4 * gg + s, ch = 16 * ct + rr;
+            const float F = b > 0 ? ex2(Gs[t * 64 + ch] - Gs[16 * b * 64 + ch]) : 0.f;
             Te[t * 64 + ch] = aE[s] * F;
             Tq[t * 64 + ch] = aQ[s] * F;
             Ik[t * 64 + ch] = aK[s];
@@ -747,62 +763,70 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
     }
     __syncthreads();
 
-    // pairs inside block w, lane = channel: E = e^{G_t - G_i}, i <= t
-    float sde[16], sdq[16], sdk[16];
+    // pairs inside block b that the wave's rows take part in, lane = channel:
+    // E = e^{G_t - G_i}, i <= t; as t the rows r0.., as i the same rows
+    float sde[8], sdq[8], sdk[8];
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-        const int t = 16 * w + tt;
-        sde[tt] = Te[t * 64 + cl];
-        sdq[tt] = Tq[t * 64 + cl];
-        sdk[tt] = Ik[t * 64 + cl];
+    for (int x = 0; x < 8; ++x) {
+        const int t = r0 + x;
+        sde[x] = Te[t * 64 + cl];
+        sdq[x] = Tq[t * 64 + cl];
+        sdk[x] = Ik[t * 64 + cl];
     }
+    const int base = 16 * b;
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-        const int t = 16 * w + tt;
-        const float Gt = Gs[t * 64 + cl], et = Es[t * 64 + cl], qt = Qs[t * 64 + cl];
+    for (int x = 0; x < 8; ++x) {
+        const int tl = 8 * half + x, t = base + tl;
+        const float Gt = Gs[t * 64 + cl];
 #pragma unroll
-        for (int ii = 0; ii <= tt; ++ii) {
-            const int i = 16 * w + ii;
-            const float E = ex2(Gt - Gs[i * 64 + cl]), ki = Ks[i * 64 + cl];
-            const float m = dMs[t * C + i], aq = dAqs[t * C + i];
-            if (ii < tt) {
-                sde[tt] += m * ki * E;
-                sdk[ii] += m * et * E;
+        for (int j = 0; j < 16; ++j) {
+            const int o = base + j;
+            const float Go = Gs[o * 64 + cl];
+            if (j <= tl) {  // o = i <= t: row t's sums
+                const float E = ex2(Gt - Go), ko = Ks[o * 64 + cl];
+                if (j < tl) sde[x] += dMs[t * C + o] * ko * E;
+                sdq[x] += dAqs[t * C + o] * ko * E;
             }
-            sdq[tt] += aq * ki * E;
-            sdk[ii] += aq * qt * E;
+            if (j >= tl) {  // o = t >= i with i = this row: row i's sum
+                const float E = ex2(Go - Gt);
+                float y = dAqs[o * C + t] * Qs[o * 64 + cl];
+                if (j > tl) y += dMs[o * C + t] * Es[o * 64 + cl];
+                sdk[x] += y * E;
+            }
         }
     }
 
-    // chain rule for the rows of block w
-    const size_t ub = (size_t)u * C * DK;
+    // chain rule for the wave's rows
     const float GC = Gs[(C - 1) * 64 + cl];
-    float dG[16], de[16], dq[16], dk[16], sKK = 0.f, bsum = 0.f;
+    float dG[8], de[8], dq[8], dk[8], sKK = 0.f, bsum = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-        const int t = 16 * w + tt;
+    for (int x = 0; x < 8; ++x) {
+        const int t = r0 + x;
         const float G = Gs[t * 64 + cl], eg = ex2(G), kg = ex2(GC - G);
-        const float dEt = ws.dEt[ub + t * DK + c], dQt = ws.dQt[ub + t * DK + c], dKh = ws.dKh[ub + t * DK + c];
+        const float dEt = pdE[x], dQt = pdQ[x], dKh = pdK[x];
         const float e = Es[t * 64 + cl], qs = Qs[t * 64 + cl], kk = Ks[t * 64 + cl];
-        const float te = sde[tt], tq = sdq[tt], ik = sdk[tt];
-        de[tt] = eg * dEt + te;
-        dq[tt] = eg * dQt + tq;
-        dk[tt] = kg * dKh + ik;
+        const float te = sde[x], tq = sdq[x], ik = sdk[x];
+        de[x] = eg * dEt + te;
+        dq[x] = eg * dQt + tq;
+        dk[x] = kg * dKh + ik;
         const float khv = kk * kg;
-        dG[tt] = dEt * (e * eg) + dQt * (qs * eg) - dKh * khv + e * te + qs * tq - kk * ik;
+        dG[x] = dEt * (e * eg) + dQt * (qs * eg) - dKh * khv + e * te + qs * tq - kk * ik;
         sKK += dKh * khv;
-        bsum += dG[tt];
+        bsum += dG[x];
     }
     blk[w * 64 + cl] = bsum;
     gcp[w * 64 + cl] = sKK;
     __syncthreads();
-    float carry = gcp[cl] + gcp[64 + cl] + gcp[128 + cl] + gcp[192 + cl] + ws.dgC[(size_t)u * DK + c] * ex2(GC);
-    for (int x = w + 1; x < 4; ++x) carry += blk[x * 64 + cl];
+    // dg_t = sum_{r >= t} dG_r; G_C (the last row) also enters through K-hat and gamma_C
+    float carry = pgC * ex2(GC);
+#pragma unroll
+    for (int x = 0; x < NW; ++x) carry += gcp[x * 64 + cl];
+    for (int x = w + 1; x < NW; ++x) carry += blk[x * 64 + cl];
     float alsum = 0.f;
 #pragma unroll
-    for (int tt = 15; tt >= 0; --tt) {
-        carry += dG[tt];
-        const int t = 16 * w + tt;
+    for (int x = 7; x >= 0; --x) {
+        carry += dG[x];
+        const int t = r0 + x;
         if (t < L) {
             const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
             const float av = bf16_to_f32(a[ka]), beta = sigmoid_fast(bf16_to_f32(er[ka]));
@@ -810,21 +834,26 @@ __global__ __launch_bounds__(256) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
             const float dg = carry;  // natural-log units
             p.da[ka] = -dg * rate * sigmoid_fast(av);
             alsum += dg * (-rate * softplus_fast(av));
-            p.derase[ka] = de[tt] * kk * beta * (1.f - beta);
-            ws.dqh[ka] = p.scale * dq[tt];
-            ws.dkh[ka] = dk[tt] + de[tt] * beta;
+            p.derase[ka] = de[x] * kk * beta * (1.f - beta);
+            ws.dqh[ka] = p.scale * dq[x];
+            ws.dkh[ka] = dk[x] + de[x] * beta;
         }
     }
     alp[w * 64 + cl] = alsum;
     __syncthreads();
-    if (w == 0) ws.dAl[(size_t)u * DK + c] = alp[cl] + alp[64 + cl] + alp[128 + cl] + alp[192 + cl];
+    if (w == 0) {
+        float sa = 0.f;
+#pragma unroll
+        for (int x = 0; x < NW; ++x) sa += alp[x * 64 + cl];
+        ws.dAl[(size_t)u * DK + c] = sa;
+    }
     // dz = dR -> dv, d_write (the first channel group of each chunk)
     if (cg == 0) {
         const uint16_t *v = reinterpret_cast<const uint16_t *>(p.v), *wr = reinterpret_cast<const uint16_t *>(p.write);
         const float *dRu = ws.dR + (size_t)u * C * DV;
 #pragma unroll
-        for (int it = 0; it < C * DV / 8 / 256; ++it) {
-            const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
+        for (int it = 0; it < C * DV / 8 / LOCAL_NT; ++it) {
+            const int i = tid + LOCAL_NT * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
             const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
             f4 vv[2], om[2];
             bf8_to_f32(*reinterpret_cast<const u16x8 *>(v + kv), vv[0], vv[1]);
@@ -904,7 +933,7 @@ hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t
     rec(3);
     hipLaunchKernelGGL((g2b_products<DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
     rec(4);
-    hipLaunchKernelGGL((g2b_local<DK, DV>), dim3(units * (DK / 64)), dim3(256), 0, s, p, ws);
+    hipLaunchKernelGGL((g2b_local<DK, DV>), dim3(units * (DK / 64)), dim3(LOCAL_NT), 0, s, p, ws);
     rec(5);
     const size_t nq = (size_t)p.B * p.T * p.Hk * DK / 256 + 1;
     hipLaunchKernelGGL((g2b_reduce<DK>), dim3((unsigned)(nq < 65536 ? nq : 65536)), dim3(256), 0, s, p, ws);
