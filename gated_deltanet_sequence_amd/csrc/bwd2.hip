@@ -83,6 +83,26 @@ __device__ __forceinline__ void bf8_to_f32(const u16x8 x, f4 &lo, f4 &hi) {
     }
 }
 
+// A ROWS x COLS float32 tile (row-major, contiguous) held in registers between
+// its global load and its LDS store: the scans load the next chunk's operands
+// while computing the current one.
+template <int ROWS, int COLS, int NT = 256> struct RegTile {
+    static constexpr int PER = ROWS * COLS / 4 / NT;
+    static_assert(ROWS * COLS / 4 % NT == 0, "tile size");
+    f4 x[PER];
+    __device__ __forceinline__ void load(const float *__restrict__ src) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) x[j] = *reinterpret_cast<const f4 *>(src + (size_t)(threadIdx.x + j * NT) * 4);
+    }
+    template <int LS> __device__ __forceinline__ void store(float *dst, float f = 1.f) const {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int i = threadIdx.x + j * NT, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
+            *reinterpret_cast<f4 *>(dst + r * LS + c) = x[j] * f;
+        }
+    }
+};
+
 // 2^x on the hardware unit (arguments here are <= 0: every decay factor is at most 1)
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -417,8 +437,9 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws) {
     constexpr int LQ = 80, LKA = DK + 4, LKB = DK + 16, LB = 48, NS = DV / 32, NT = DK / 32;
-    __shared__ __attribute__((aligned(16))) float bA[C * LQ], bK[C * LKB], Os[C * LB], dSs[DK * LB], dUs[C * LB],
-        dRs[C * LB];
+    // bA: A_qk, then A; bK1: Kh (stride LKA), then -Et (stride LKB); bK2: Qt
+    __shared__ __attribute__((aligned(16))) float bA[C * LQ], bK1[C * LKB], bK2[C * LKB], Os[C * LB],
+        dSs[DK * LB], dUs[C * LB], dRs[C * LB];
     const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
     const uint16_t *dout = reinterpret_cast<const uint16_t *>(p.dout);
@@ -433,9 +454,36 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
             dSs[c * LB + j] = dS[x][s];
         }
     }
+    // dO slice of chunk n: 64 rows x 32 columns, 8 per thread (rows past T read the last
+    // token and are zeroed when stored)
+    const int ot = tid >> 2, oj = (tid & 3) * 8;
+    auto load_do = [&](int n) {
+        const int L = min(C, p.T - n * C), tl = min(ot, L - 1);
+        return *reinterpret_cast<const u16x8 *>(dout + (((size_t)bb * p.T + n * C + tl) * p.Hv + hv) * DV + j0 + oj);
+    };
+    auto store_do = [&](const u16x8 x, int n) {
+        const int L = min(C, p.T - n * C);
+        f4 lo, hi;
+        bf8_to_f32(x, lo, hi);
+        const float on = ot < L ? 1.f : 0.f;
+        *reinterpret_cast<f4 *>(Os + ot * LB + oj) = lo * on;
+        *reinterpret_cast<f4 *>(Os + ot * LB + oj + 4) = hi * on;
+    };
+    // staged for the chunk about to run: A_qk in bA, Kh in bK1, dO in Os
+    RegTile<C, C> rAq, rA;
+    RegTile<C, DK> rKh, rQ, rE;
+    u16x8 rdo;
+    {
+        const size_t u = unit_of(bb, hv, NC - 1, p.Hv, NC);
+        rAq.load(ws.Aq + u * C * C);
+        rKh.load(ws.Kh + u * C * DK);
+        rdo = load_do(NC - 1);
+        rAq.template store<LQ>(bA);
+        rKh.template store<LKA>(bK1);
+        store_do(rdo, NC - 1);
+    }
     for (int n = NC - 1; n >= 0; --n) {
         const size_t u = unit_of(bb, hv, n, p.Hv, NC);
-        const int t0 = n * C, L = min(C, p.T - t0);
         float *dS1u = ws.dS1 + u * DK * DV;
 #pragma unroll
         for (int x = 0; x < NT; ++x) {
@@ -448,27 +496,18 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
         for (int x = 0; x < NT; ++x)
 #pragma unroll
             for (int s = 0; s < 4; ++s) gcr[x][s] = ws.gC[u * DK + 16 * ((w * NT + x) >> 1) + 4 * gg + s];
-        {
-            // dO slice: 64 rows x 32 columns, 8 per thread (rows past T read the last token, zeroed)
-            const int t = tid >> 2, j = (tid & 3) * 8, tl = min(t, L - 1);
-            const u16x8 x = *reinterpret_cast<const u16x8 *>(
-                dout + (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j0 + j);
-            f4 lo, hi;
-            bf8_to_f32(x, lo, hi);
-            const float on = t < L ? 1.f : 0.f;
-            lds_load<C, C, LQ>(bA, ws.Aq + u * C * C);
-            lds_load<C, DK, LKA>(bK, ws.Kh + u * C * DK);
-            *reinterpret_cast<f4 *>(Os + t * LB + j) = lo * on;
-            *reinterpret_cast<f4 *>(Os + t * LB + j + 4) = hi * on;
-        }
         __syncthreads();
+        // this chunk's A, Qt, Et in flight while dU is computed
+        rA.load(ws.A + u * C * C);
+        rQ.load(ws.Qt + u * C * DK);
+        rE.load(ws.Et + u * C * DK);
         // dU = Aq^T dO + Kh dS  (Aq is zero above the diagonal)
         float *dUu = ws.dU + u * C * DV, *dRu = ws.dR + u * C * DV;
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
             f4 acc = {0, 0, 0, 0};
             mma<C, 1, LQ, LB, 1>(acc, bA + 16 * w, Os + 16 * jb);
-            mma<DK, LKA, 1, LB, 1>(acc, bK + 16 * w * LKA, dSs + 16 * jb);
+            mma<DK, LKA, 1, LB, 1>(acc, bK1 + 16 * w * LKA, dSs + 16 * jb);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
@@ -477,8 +516,16 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
             }
         }
         __syncthreads();
-        lds_load<C, C, LQ>(bA, ws.A + u * C * C);
-        lds_load<C, DK, LKB>(bK, ws.Qt + u * C * DK);
+        rA.template store<LQ>(bA);
+        rQ.template store<LKB>(bK2);
+        rE.template store<LKB>(bK1, -1.f);
+        // the next chunk's A_qk, Kh and dO in flight while this one finishes
+        if (n > 0) {
+            const size_t un = u - 1;
+            rAq.load(ws.Aq + un * C * C);
+            rKh.load(ws.Kh + un * C * DK);
+            rdo = load_do(n - 1);
+        }
         __syncthreads();
         // dR = A^T dU;  dS = gamma_C . dS + Qt^T dO
 #pragma unroll
@@ -497,20 +544,23 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
             const int id = w * NT + x, cb = id >> 1, jb = id & 1;
 #pragma unroll
             for (int s = 0; s < 4; ++s) dS[x][s] *= gcr[x][s];
-            mma<C, 1, LKB, LB, 1>(dS[x], bK + 16 * cb, Os + 16 * jb);
+            mma<C, 1, LKB, LB, 1>(dS[x], bK2 + 16 * cb, Os + 16 * jb);
         }
         __syncthreads();
-        lds_load<C, DK, LKB>(bK, ws.Et + u * C * DK, -1.f);
-        __syncthreads();
-        // dS -= Et^T dR
+        // dS -= Et^T dR  (bK1 holds -Et)
 #pragma unroll
         for (int x = 0; x < NT; ++x) {
             const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-            mma<C, 1, LKB, LB, 1>(dS[x], bK + 16 * cb, dRs + 16 * jb);
+            mma<C, 1, LKB, LB, 1>(dS[x], bK1 + 16 * cb, dRs + 16 * jb);
 #pragma unroll
             for (int s = 0; s < 4; ++s) dSs[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = dS[x][s];
         }
         __syncthreads();
+        if (n > 0) {
+            rAq.template store<LQ>(bA);
+            rKh.template store<LKA>(bK1);
+            store_do(rdo, n - 1);
+        }
     }
     if (p.dS0) {
 #pragma unroll
