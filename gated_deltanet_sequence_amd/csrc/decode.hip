@@ -10,12 +10,14 @@
 //   out = scale (qs + (k.q) delta)          (= S_new^T q, read from the old S)
 //   S_new = alpha S + k delta^T
 // so each 64 KB state (d = 128) is read once and written once: the kernel is
-// bound by HBM bandwidth.  A 256-thread work-group handles one (sequence, value
+// bound by HBM bandwidth.  A 512-thread work-group handles one (sequence, value
 // head) at a time; thread (row group rg, column quad cq) keeps Dk/RG rows x 4
-// columns of the state in registers between the two reductions and the
-// write-back.  The work-groups are persistent (as many as fit on the device)
-// and load the next head's state while they reduce and write back the
-// current one, so reads and writes stream concurrently.
+// columns of the state in registers (8 rows at d = 128) between the two
+// reductions and the write-back.  The work-groups are persistent (as many as
+// fit on the device: with one state per work-group the registers allow 16
+// waves per CU), so the loads of some work-groups stream while others reduce
+// and write back; measured faster than a double-buffered 256-thread form,
+// which needs twice the registers per thread and so holds half the waves.
 // Loads and stores are 16 bytes per lane and whole rows per wave, and marked
 // non-temporal: each state byte is touched exactly once per step.
 //
@@ -41,17 +43,19 @@ template <typename T, bool G2> struct DecodeGates {
     const float *A_log, *dt_bias;
 };
 
+constexpr int DECODE_NT = 512;  // threads per work-group
+
 template <typename T, int DK, int DV, bool G2>
-__global__ __launch_bounds__(256) void decode_kernel(int units, int Hk, int Hv, const T *__restrict__ q,
+__global__ __launch_bounds__(DECODE_NT) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(int units, int Hk, int Hv, const T *__restrict__ q,
                                                      const T *__restrict__ k,
                                                      const T *__restrict__ v,
                                                      DecodeGates<T, G2> gates,
                                                      float scale, float *__restrict__ state,
                                                      T *__restrict__ out) {
     constexpr int CQ = DV / 4;      // float4 columns of a state row
-    constexpr int RG = 256 / CQ;    // row groups
+    constexpr int RG = DECODE_NT / CQ;  // row groups
     constexpr int RPT = DK / RG;    // rows held per thread
-    static_assert(RG * CQ == 256 && RPT * RG == DK, "tile");
+    static_assert(RG * CQ == DECODE_NT && RPT * RG == DK, "tile");
 
     // per state row: the read weights (k and q; D e and D q for the
     // channel-wise decay), and for the channel-wise decay the written key k,
@@ -106,8 +110,8 @@ __global__ __launch_bounds__(256) void decode_kernel(int units, int Hk, int Hv, 
         float alpha = 1.f, beta = 1.f;  // scalar decay and write strength (scalar decay only)
         if constexpr (G2) {
             if (tid < DK) {  // row tid: D, e = sigmoid(erase) k, weights D e and D q
-                const float D = expf(-expf(sm.al) * softplus_f32(sm.a));
-                ks[tid] = D * sigmoid_f32(sm.b) * sm.k;
+                const float D = exp_fast(-exp_fast(sm.al) * softplus_fast(sm.a));
+                ks[tid] = D * sigmoid_fast(sm.b) * sm.k;
                 qs[tid] = D * sm.q;
                 kw[tid] = sm.k;
                 dd[tid] = D;
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_kernel(int units, int Hk, int Hv, 
             if constexpr (G2) {  // u = sigmoid(write) v - S^T (D e)
                 const f4 wl = ld4(static_cast<const T *>(gates.write), (size_t)unit * DV + 4 * tid);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) d[j] = sigmoid_f32(wl[j]) * vv[j] - sk[j];
+                for (int j = 0; j < 4; ++j) d[j] = sigmoid_fast(wl[j]) * vv[j] - sk[j];
             } else {
                 d = beta * (vv - alpha * sk);
             }
@@ -178,30 +182,12 @@ __global__ __launch_bounds__(256) void decode_kernel(int units, int Hk, int Hv, 
         }
     };
 
-    // Persistent loop over heads, two state buffers: the next head's state
-    // is in flight while this one is reduced and written back.
-    const int stride = gridDim.x;
-    int u = blockIdx.x;
-    if (u >= units) return;
-    f4 s0[RPT], s1[RPT];
-    load_state(s0, u);
-    Small m0 = load_small(u), m1 = m0;
-    while (true) {
-        const int u1 = u + stride;
-        if (u1 < units) {
-            load_state(s1, u1);
-            m1 = load_small(u1);
-        }
-        step(s0, m0, u);
-        if (u1 >= units) break;
-        const int u2 = u1 + stride;
-        if (u2 < units) {
-            load_state(s0, u2);
-            m0 = load_small(u2);
-        }
-        step(s1, m1, u1);
-        if (u2 >= units) break;
-        u = u2;
+    // Persistent loop over heads.
+    f4 st[RPT];
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        load_state(st, u);
+        const Small sm = load_small(u);
+        step(st, sm, u);
     }
 }
 
@@ -212,7 +198,7 @@ static unsigned decode_grid(int units) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<T, DK, DV, G2>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<T, DK, DV, G2>, DECODE_NT, 0) != hipSuccess ||
         cus <= 0 || per_cu <= 0)
         return (unsigned)units;
     const long long resident = (long long)cus * per_cu;
@@ -223,7 +209,7 @@ template <typename T, int DK, int DV, bool G2>
 static hipError_t launch_decode_t(const DecodeArgs &p, hipStream_t s) {
     const int units = p.B * p.Hv;
     const DecodeGates<T, G2> gates{p.a, p.b, p.write, p.A_log, p.dt_bias};
-    hipLaunchKernelGGL((decode_kernel<T, DK, DV, G2>), dim3(decode_grid<T, DK, DV, G2>(units)), dim3(256), 0, s,
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV, G2>), dim3(decode_grid<T, DK, DV, G2>(units)), dim3(DECODE_NT), 0, s,
                        units, p.Hk, p.Hv, (const T *)p.q, (const T *)p.k, (const T *)p.v, gates, p.scale,
                        p.state, (T *)p.out);
     return hipGetLastError();
