@@ -328,6 +328,71 @@ def bench_prefill(args, torch, gdn, synth):
     return res
 
 
+def bench_prefill_long(args, torch, gdn, synth):
+    """The long-context prefill (B=2, T=65536, 16/64 heads, d=128, bf16, initial state ~ N(0, 0.02)):
+    the same call and protocol as the headline leg, on fewer steps (each call is ~1 ms)."""
+    spec = synth.WORKLOADS["prefill_long"]
+    log(f"[bench] long-context prefill workload {spec}")
+    inp = synth.make_inputs(spec)
+    dims = gdn.make_dims(spec.B, spec.T, spec.Hk, spec.Hv, spec.Dk, spec.Dv, spec.torch_dtype)
+    sets = []
+    for _ in range(args.rotate):
+        d = {k: (None if v is None else v.cuda().contiguous()) for k, v in inp.items()}
+        d["out"] = torch.empty((spec.B, spec.T, spec.Hv, spec.Dv), dtype=spec.torch_dtype, device="cuda")
+        d["ST"] = torch.empty((spec.B, spec.Hv, spec.Dk, spec.Dv), dtype=torch.float32, device="cuda")
+        d["ws"] = gdn.alloc_workspace(dims)
+        sets.append(d)
+    del inp
+    steps, warmup = max(1, min(args.steps, 5)), max(1, min(args.warmup, 2))
+
+    def step(d, ev=None):
+        gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], d["S0"],
+                          out=d["out"], final_state=d["ST"], workspace=d["ws"], stage_events=ev)
+
+    for i in range(warmup):
+        step(sets[i % len(sets)])
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(sets[i % len(sets)])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    evs = [gdn.StageEvents() for _ in range(steps)]
+    for i in range(steps):
+        step(sets[i % len(sets)], evs[i].handles)
+    torch.cuda.synchronize()
+    stage_ms = [sum(e.stage_ms()[j] for e in evs) / steps for j in range(gdn.GDN_CHUNK_FWD_STAGES)]
+    for e in evs:
+        e.close()
+    G = spec.Hv // spec.Hk
+    units = spec.B * spec.T * spec.Hv
+    path_flop = prefill_flop_per_token_head(spec.Dk, spec.Dv, spec.chunk, G) * units
+    scan_flop = scan_flop_per_token_head(spec.Dk, spec.Dv, spec.chunk) * units
+    nbytes = prefill_bytes(spec.B, spec.T, spec.Hk, spec.Hv, spec.Dk, spec.Dv, 2, True)
+    scan_tf = scan_flop / (stage_ms[1] * 1e-3) / 1e12
+    path_tf = path_flop / (ms * 1e-3) / 1e12
+    log(f"[bench] long-context prefill {ms * 1e3:.1f} us/step, stages (us) "
+        + ", ".join(f"{n}={t * 1e3:.1f}" for n, t in zip(gdn.STAGE_NAMES, stage_ms)))
+    del sets
+    torch.cuda.empty_cache()
+    return dict(value=round(spec.B * spec.T / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
+                steps=steps, warmup=warmup,
+                config=dict(workload="prefill_long", B=spec.B, T=spec.T, Hk=spec.Hk, Hv=spec.Hv, Dk=spec.Dk,
+                            Dv=spec.Dv, chunk=spec.chunk, input_dtype="bf16", state_dtype="f32",
+                            initial_state=True, rotated_buffer_sets=args.rotate),
+                stages_us={n: round(t * 1e3, 2) for n, t in zip(gdn.STAGE_NAMES, stage_ms)},
+                roofline=dict(kernel="scan_split_kernel", bound="mfma", achieved=round(scan_tf, 2),
+                              peak=PEAK_MFMA_F16_TFLOPS, unit="TFLOP/s", frac=round(scan_tf / PEAK_MFMA_F16_TFLOPS, 4),
+                              flop_per_launch=scan_flop, avg_launch_ms=round(stage_ms[1], 5)),
+                path=dict(flop=path_flop, bytes=nbytes, tflops=round(path_tf, 2),
+                          mfma_frac=round(path_tf / PEAK_MFMA_F16_TFLOPS, 4),
+                          hbm_gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)))
+
+
 def bench_decode(args, torch, gdn, synth):
     spec = synth.WORKLOADS["decode_b256"]
     log(f"[bench] decode workload {spec}")
@@ -639,6 +704,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gdn2", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the Gated DeltaNet-2 backward leg")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context prefill leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a 256 MiB device copy (counter calibration)")
@@ -664,6 +730,7 @@ def main():
     gdn.lib()
 
     pre = bench_prefill(args, torch, gdn, synth)
+    lng = None if args.no_long else bench_prefill_long(args, torch, gdn, synth)
     dec = None if args.no_decode else bench_decode(args, torch, gdn, synth)
     g2 = None if args.no_gdn2 else bench_gdn2(args, torch, gdn, synth)
     g2d = None if args.no_gdn2 or args.no_decode else bench_decode_gdn2(args, torch, gdn, synth)
@@ -694,6 +761,7 @@ def main():
         "roofline": pre["roofline"],
         "stages_us": {n: round(s * 1e3, 2) for n, s in zip(gdn.STAGE_NAMES, pre["stage_ms"])},
         "path": pre["path"],
+        "prefill_long": lng,
         "decode": dec,
         "gdn2": g2,
         "gdn2_decode": g2d,
