@@ -218,8 +218,8 @@ def summarize_pmc(fetch_dir, write_dir):
             "Two counter passes over the same bench command, one counter each:", "",
             "```",
             "cd /tmp && export TMPDIR=/tmp",
-            f"timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE -d <dir_fetch> -o pmc --output-format csv -- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibration-copy",
-            f"timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE -d <dir_write> -o pmc --output-format csv -- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibration-copy",
+            f"timeout -s KILL 200 rocprofv3 --pmc FETCH_SIZE -d <dir_fetch> -o pmc --output-format csv -- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-long --calibration-copy",
+            f"timeout -s KILL 200 rocprofv3 --pmc WRITE_SIZE -d <dir_write> -o pmc --output-format csv -- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-long --calibration-copy",
             "python3 bench.py --summarize-pmc <dir_fetch> <dir_write>",
             "```", "",
             "| quantity | value |", "|---|---|",
