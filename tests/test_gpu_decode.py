@@ -84,3 +84,17 @@ def test_decode_b256_64_steps():
     assert_close("out (32 heads x 64 steps)", o_gpu, np.stack(o_ref), TOL["bf16"])
     assert_close("state (32 heads)", s_gpu, np.stack(s_ref), TOL["bf16"])
     assert torch.isfinite(S).all()
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [("f32", 128, 128), ("bf16", 128, 128), ("bf16", 64, 128)])
+def test_ragged_persistent_tail(dtype, Dk, Dv):
+    """B*Hv = 1072 heads: more than any resident grid (at most 4 work-groups on each of
+    256 CUs) and not a multiple of 256, so the persistent loop walks several heads per
+    work-group and ends on a partial sweep."""
+    spec = GDNSpec(B=67, T=3, Hk=4, Hv=16, Dk=Dk, Dv=Dv, dtype=dtype, seed=320 + Dk, init_state=True)
+    log(f"[decode ragged] {spec}")
+    inp = synth.make_inputs(spec)
+    out, S = run_steps(spec, inp)
+    o_ref, s_ref = oracle_prefill(inp)
+    assert_close("out", out, o_ref, TOL[dtype])
+    assert_close("state", S, s_ref, TOL[dtype])

@@ -142,3 +142,11 @@ def test_decode_gdn2_b256():
         s_ref.append(st[0, 0])
     assert_close("out (16 heads)", o_gpu, np.stack(o_ref), TOL["bf16"])
     assert_close("state (16 heads)", s_gpu, np.stack(s_ref), TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [("f32", 128, 128), ("bf16", 128, 128), ("bf16", 64, 128)])
+def test_ragged_persistent_tail(dtype, Dk, Dv):
+    """B*Hv = 1072 heads: more than any resident grid (at most 4 work-groups on each of
+    256 CUs) and not a multiple of 256, so the persistent loop walks several heads per
+    work-group and ends on a partial sweep."""
+    check(g2(B=67, T=3, Hk=4, Hv=16, Dk=Dk, Dv=Dv, dtype=dtype, seed=520 + Dk, init_state=True))
