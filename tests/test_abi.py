@@ -126,6 +126,12 @@ def test_workspace_bytes():
     (dict(chunk=32), ERR_UNSUPPORTED, "chunk"),
     (dict(dtype=7), ERR_UNSUPPORTED, "dtype"),
     (dict(scale=float("nan")), ERR_SHAPE, "scale"),
+    # launch-grid and addressing limits
+    (dict(B=70000), ERR_SHAPE, "grid limit"),
+    (dict(Hk=70000, Hv=70000), ERR_SHAPE, "grid limit"),
+    (dict(B=65535, Hk=16, Hv=65520), ERR_SHAPE, "too large"),
+    (dict(B=1000, Hk=16, Hv=64, T=64 * 40000), ERR_SHAPE, "too large"),
+    (dict(Hk=16, Hv=64, Dk=128, Dv=128, T=131072), ERR_UNSUPPORTED, "limit 2^31"),
 ])
 def test_prefill_rejects_bad_dims(kw, code, needle):
     buf = Buf()
@@ -133,6 +139,19 @@ def test_prefill_rejects_bad_dims(kw, code, needle):
     args = prefill_args(buf, dims())
     assert call_prefill(d, args) == code
     assert needle in last_error()
+
+
+def test_prefill_size_limits_are_exact():
+    """The longest bfloat16 sequence at 64 value heads of d_v = 128 that one launch addresses
+    with 32-bit byte offsets is accepted (a workspace size comes back); one chunk more is not."""
+    L = binding.lib()
+    big = dict(B=1, Hk=16, Hv=64, Dk=128, Dv=128)
+    ok = L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(dims(T=131072 - 64, **big)))
+    assert ok > 0
+    assert L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(dims(T=131072 - 63, **big))) == 0
+    # float32 inputs halve the token limit
+    assert L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(dims(T=65536 - 64, dtype=binding.GDN_F32, **big))) > 0
+    assert L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(dims(T=65536 - 63, dtype=binding.GDN_F32, **big))) == 0
 
 
 def test_prefill_rejects_null_dims():
