@@ -89,8 +89,9 @@ size_t gdn_chunk_fwd_workspace_bytes(const gdn_dims *d);
  *   workspace     device scratch of at least gdn_chunk_fwd_workspace_bytes(d)
  *                 bytes, 256-byte aligned; contents on entry are ignored.
  * out must not overlap any input.  Results are deterministic (no atomics).
- * Limit: T * Hv * Dv * element size of one sequence below 2^31 bytes
- * (GDN_ERR_UNSUPPORTED otherwise). */
+ * Limits: with T rounded up to a multiple of 64, T * Hv * Dv * element size
+ * of one sequence below 2^31 bytes (GDN_ERR_UNSUPPORTED otherwise); B and Hk
+ * at most 65535 and B * Hv * ceil(T/64) below 2^31 (GDN_ERR_SHAPE). */
 gdn_status gdn_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const void *v,
                          const float *a, const float *b, const float *A_log,
                          const float *dt_bias, const float *initial_state, void *out,
