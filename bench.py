@@ -127,6 +127,7 @@ TRAFFIC_FILES = {
     "scan_split_kernel": (r"scan_split_kernel(<[^>]*false>|I.*Lb0E)", "scan_split_kernel_prefill_t4096_traffic.md"),
     "chunk_local_kernel": (r"chunk_local_kernel", "chunk_local_kernel_prefill_t4096_traffic.md"),
     "decode_kernel": (r"decode_kernel<[^>]*false>", "decode_kernel_decode_b256_traffic.md"),
+    "decode_kernel_gdn2": (r"decode_kernel<[^>]*true>", "decode_kernel_gdn2_decode_b256_traffic.md"),
     "scan_split_kernel_gdn2": (r"scan_split_kernel(<[^>]*true>|I.*Lb1E)", "scan_split_kernel_gdn2_t8192_traffic.md"),
     "chunk_local2_kernel": (r"chunk_local2_kernel", "chunk_local2_kernel_gdn2_t8192_traffic.md"),
     "g2b_local": (r"g2b_local", "g2b_local_gdn2_bwd_t8192_traffic.md"),
@@ -476,6 +477,7 @@ def bench_decode_gdn2(args, torch, gdn, synth):
                             Dv=spec.Dv, input_dtype="bf16", state_dtype="f32", distinct_tokens=spec.T),
                 roofline=dict(kernel="decode_kernel<G2>", bound="hbm", achieved=round(gbs, 1),
                               peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                              traffic=stored_traffic("decode_kernel_gdn2"),
                               bytes_per_launch=nbytes, avg_launch_ms=round(ms, 5)))
 
 
