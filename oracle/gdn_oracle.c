@@ -16,11 +16,11 @@
  *    softplus(x) = log(1 + e^x), write strength beta = sigmoid(b), read-out
  *    y_t = S_t^T q_t.
  *  - rainlin-net.pages.dev "Qwen3.5", section "GDN详解": the gated delta rule
- *    S_t = alpha_t S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T, expanded
- *    into five steps: decay, read at address k, scaled difference, rank-one
- *    write, read-out with q.  The state is stored here as S[d_k][d_v] (the
- *    indexing of that page's eager loop: read S^T k, write k delta^T, output
- *    S^T q), i.e. the transpose of the d_v x d_k matrix in the formula.
+ *    S_t = alpha_t S_{t-1}(I - beta_t k_t k_t^T) + beta_t v_t k_t^T with the
+ *    read-out o_t = S_t q_t taken after the update.  The state is stored here
+ *    as S[d_k][d_v], the transpose of that d_v x d_k matrix, so the rule reads
+ *    S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T and the
+ *    read-out o_t = S_t^T q_t.
  *  - zhichai.net "Gated DeltaNet-2", sections "Gated Delta Rule-2" and
  *    "退化兼容性": decoupled erase gate b_t (per key channel) and write gate
  *    w_t (per value channel), channel-wise decay D_t:
@@ -69,12 +69,16 @@ void oracle_gdn_gates(long n, int Hv, const double *a, const double *b,
         }
 }
 
-/* The gated delta rule, token by token (rainlin page, five-step form).
+/* The gated delta rule, token by token (rainlin page, section "GDN详解").
  *   q, k : [B,T,Hk,Dk]   v, out : [B,T,Hv,Dv]   g, beta : [B,T,Hv]
  *   S0, ST : [B,Hv,Dk,Dv] (S0 may be NULL: zero initial state; ST may be NULL)
- * Value head hv reads key/query head hv / (Hv/Hk).  For every token:
- *   S <- alpha S;  kv = S^T k;  delta = beta (v - kv);  S <- S + k delta^T;
- *   out = scale * S^T q. */
+ * Value head hv reads key/query head hv / (Hv/Hk).  Each token applies the
+ * transition P_t = alpha_t (I - beta_t k_t k_t^T) to the state and adds the
+ * write beta_t k_t v_t^T.  P_t S is evaluated by distributing the product,
+ *   P_t S = alpha_t S - alpha_t beta_t k_t (S^T k_t)^T,
+ * which is the same matrix without forming the d_k x d_k factor; so
+ *   S_t = alpha_t S_{t-1} + k_t (beta_t v_t - alpha_t beta_t S_{t-1}^T k_t)^T,
+ * and o_t = scale * S_t^T q_t. */
 void oracle_gdn_core(int B, int T, int Hk, int Hv, int Dk, int Dv,
                      const double *q, const double *k, const double *v,
                      const double *g, const double *beta, double scale,
@@ -84,8 +88,8 @@ void oracle_gdn_core(int B, int T, int Hk, int Hv, int Dk, int Dv,
     for (int u = 0; u < B * Hv; ++u) {
         const int bb = u / Hv, hv = u % Hv, hk = hv / grp;
         double *S = (double *)malloc(sizeof(double) * (size_t)Dk * Dv);
-        double *kv = (double *)malloc(sizeof(double) * (size_t)Dv);
-        double *d = (double *)malloc(sizeof(double) * (size_t)Dv);
+        double *sk = (double *)malloc(sizeof(double) * (size_t)Dv);  /* S_{t-1}^T k_t */
+        double *w = (double *)malloc(sizeof(double) * (size_t)Dv);   /* column factor of the rank-one term */
         if (S0) memcpy(S, S0 + (size_t)u * Dk * Dv, sizeof(double) * (size_t)Dk * Dv);
         else memset(S, 0, sizeof(double) * (size_t)Dk * Dv);
         for (int t = 0; t < T; ++t) {
@@ -95,19 +99,13 @@ void oracle_gdn_core(int B, int T, int Hk, int Hv, int Dk, int Dv,
             const size_t gi = ((size_t)bb * T + t) * Hv + hv;
             const double alpha = exp(g[gi]);
             const double be = beta[gi];
-            /* 1. decay the old state */
+            for (int j = 0; j < Dv; ++j) sk[j] = 0.0;
             for (int i = 0; i < Dk; ++i)
-                for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] *= alpha;
-            /* 2. read what the memory holds at address k */
-            for (int j = 0; j < Dv; ++j) kv[j] = 0.0;
+                for (int j = 0; j < Dv; ++j) sk[j] += S[(size_t)i * Dv + j] * kt[i];
+            for (int j = 0; j < Dv; ++j) w[j] = be * vt[j] - alpha * be * sk[j];
             for (int i = 0; i < Dk; ++i)
-                for (int j = 0; j < Dv; ++j) kv[j] += S[(size_t)i * Dv + j] * kt[i];
-            /* 3. scaled difference to the target */
-            for (int j = 0; j < Dv; ++j) d[j] = be * (vt[j] - kv[j]);
-            /* 4. rank-one write at address k */
-            for (int i = 0; i < Dk; ++i)
-                for (int j = 0; j < Dv; ++j) S[(size_t)i * Dv + j] += kt[i] * d[j];
-            /* 5. read-out with the query, after the write */
+                for (int j = 0; j < Dv; ++j)
+                    S[(size_t)i * Dv + j] = alpha * S[(size_t)i * Dv + j] + kt[i] * w[j];
             double *ot = out + (((size_t)bb * T + t) * Hv + hv) * Dv;
             for (int j = 0; j < Dv; ++j) ot[j] = 0.0;
             for (int i = 0; i < Dk; ++i)
@@ -116,8 +114,8 @@ void oracle_gdn_core(int B, int T, int Hk, int Hv, int Dk, int Dv,
         }
         if (ST) memcpy(ST + (size_t)u * Dk * Dv, S, sizeof(double) * (size_t)Dk * Dv);
         free(S);
-        free(kv);
-        free(d);
+        free(sk);
+        free(w);
     }
 }
 

@@ -6,7 +6,8 @@ a wrong head map, read-out before the write, decay after the erase) fails at
 least one of them.  The pins:
 
 * gate closed forms (dingfen page, sections 9-10) against NumPy/SciPy routines;
-* hand-worked examples from the five-step form (tests/golden/*.json);
+* hand-worked examples worked from the rule by exact arithmetic (tests/golden/*.json),
+  among them a Gated DeltaNet-2 example entered through the raw gate logits;
 * alpha = 1, beta = 0 leaves the state unchanged (the identity transition);
 * alpha = beta = 1 with a unit key writes v exactly at address k, and the
   interpolation identity of the dingfen page, section 7, for any beta;
@@ -17,7 +18,8 @@ least one of them.  The pins:
   matrices (rainlin page, gated delta rule formula);
 * the pages' chunkwise WY form (zhichai page) reproduces the token loop;
 * GDN-2 with b = w = beta 1 and D = alpha I reduces to GDN (zhichai page,
-  section "退化兼容性").
+  section "退化兼容性"), both through explicit gates and through the raw logits
+  (channel-constant logits against the GDN gates with dt_bias = 0).
 """
 import json
 import math
@@ -107,6 +109,18 @@ def test_hand_worked_gdn2_example(oracle_lib):
     fx = json.load(open(os.path.join(GOLDEN, "hand_worked_gdn2.json")))
     i = {k: np.array(v, dtype=np.float64) for k, v in fx["inputs"].items()}
     out, ST = oracle.gdn2_core(i["q"], i["k"], i["v"], i["g"], i["eb"], i["wb"], S0=i["S0"])
+    tol = fx["tolerance_abs"]
+    np.testing.assert_allclose(out, np.array(fx["expected"]["out"]), rtol=0, atol=tol)
+    np.testing.assert_allclose(ST, np.array(fx["expected"]["final_state"]), rtol=0, atol=tol)
+
+
+def test_hand_worked_gdn2_raw_logit_example(oracle_lib):
+    """The GDN-2 forward from raw logits (decay logit a with A_log per key channel, erase and
+    write logits): gates and recurrence together, against values worked by hand."""
+    fx = json.load(open(os.path.join(GOLDEN, "hand_worked_gdn2_logits.json")))
+    i = {k: np.array(v, dtype=np.float64) for k, v in fx["inputs"].items()}
+    out, ST = oracle.gdn2_fwd(i["q"], i["k"], i["v"], i["a"], i["A_log"], i["erase"], i["write"],
+                              S0=i["S0"])
     tol = fx["tolerance_abs"]
     np.testing.assert_allclose(out, np.array(fx["expected"]["out"]), rtol=0, atol=tol)
     np.testing.assert_allclose(ST, np.array(fx["expected"]["final_state"]), rtol=0, atol=tol)
@@ -316,6 +330,34 @@ def test_gdn2_reduces_to_gdn(oracle_lib):
     o2, s2 = oracle.gdn2_core(q, k, v, g2, eb, wb, S0=S0)
     np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(s2, s1, rtol=1e-12, atol=1e-13)
+
+
+def test_gdn2_raw_logits_reduce_to_gdn(oracle_lib):
+    """Channel-constant raw logits: a[t,h,c] = a[t,h], A_log[h,c] = A_log[h] and erase = write
+    logits = b[t,h] make the GDN-2 gates D = alpha 1, b = w = beta 1, so gdn2_fwd must equal
+    gdn_fwd (whose gates are pinned by closed forms) with dt_bias = 0."""
+    rng = np.random.default_rng(19)
+    B, T, Hk, Hv, Dk, Dv = 2, 11, 1, 3, 4, 5
+    q = rng.standard_normal((B, T, Hk, Dk))
+    k = rng.standard_normal((B, T, Hk, Dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, Hv, Dv))
+    a = rng.standard_normal((B, T, Hv)) * 2
+    b = rng.standard_normal((B, T, Hv)) * 2
+    A_log = rng.uniform(-1.0, math.log(16.0), size=Hv)
+    S0 = rng.standard_normal((B, Hv, Dk, Dv))
+    o1, s1 = oracle.gdn_fwd(q, k, v, a, b, A_log, np.zeros(Hv), S0=S0, scale=0.7)
+    o2, s2 = oracle.gdn2_fwd(q, k, v, np.repeat(a[..., None], Dk, -1), np.repeat(A_log[:, None], Dk, -1),
+                             np.repeat(b[..., None], Dk, -1), np.repeat(b[..., None], Dv, -1),
+                             S0=S0, scale=0.7)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s2, s1, rtol=1e-12, atol=1e-13)
+    # a channel-varying decay must not reduce (the pin would catch a gate that ignores c)
+    A2 = np.repeat(A_log[:, None], Dk, -1).copy()
+    A2[:, 0] += 1.0
+    o3, _ = oracle.gdn2_fwd(q, k, v, np.repeat(a[..., None], Dk, -1), A2, np.repeat(b[..., None], Dk, -1),
+                            np.repeat(b[..., None], Dv, -1), S0=S0, scale=0.7)
+    assert oracle.rel_l2(o3, o1) > 1e-3
 
 
 def test_gdn2_brute_force(oracle_lib):
