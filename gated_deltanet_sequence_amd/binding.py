@@ -111,10 +111,39 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr() if t.numel() else None
 
 
-def _f32(t: Optional[torch.Tensor], name: str):
-    if t is not None and t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32")
-    return t
+def _validate(dev, specs):
+    """Check every (name, tensor, shape, dtype) of specs: a torch tensor of that shape and
+    dtype (None: any), contiguous, on the GPU device dev.  A spec whose tensor is None is an
+    omitted optional argument and is skipped.  Shapes and dtypes of all tensors are checked
+    before any device, so a wrong size is reported as such whatever the device; a host tensor
+    (whose address a kernel would fault on) is rejected before anything is enqueued."""
+    for name, t, shape, dtype in specs:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (isinstance(dev, torch.device) and dev.type == "cuda"):
+        raise ValueError(f"inputs must be GPU tensors (got {dev})")
+    for name, t, _, _ in specs:
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _workspace_spec(workspace, need: int):
+    """The workspace must hold at least `need` bytes (also checked by the library)."""
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor):
+            raise TypeError("workspace must be a torch.Tensor")
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                             f"{need} needed")
+    return ("workspace", workspace, None, None)
 
 
 def _stream(stream) -> Optional[int]:
@@ -160,17 +189,13 @@ def gdn_chunk_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, scale: f
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     dims = make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, scale)
-    for name, t in (("a", a), ("b", b), ("A_log", A_log), ("dt_bias", dt_bias),
-                    ("initial_state", initial_state), ("final_state", final_state)):
-        _f32(t, name)
-    if k.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k must share shape and q, k, v dtype")
-    if tuple(v.shape[:2]) != (B, T) or tuple(a.shape) != (B, T, Hv) or tuple(b.shape) != (B, T, Hv):
-        raise ValueError("shape mismatch among q, v, a, b")
-    if tuple(A_log.shape) != (Hv,) or tuple(dt_bias.shape) != (Hv,):
-        raise ValueError("A_log and dt_bias must be [Hv]")
-    if initial_state is not None and tuple(initial_state.shape) != (B, Hv, Dk, Dv):
-        raise ValueError("initial_state must be [B,Hv,Dk,Dv]")
+    f32, dt = torch.float32, q.dtype
+    _validate(q.device, [
+        ("q", q, None, None), ("k", k, q.shape, dt), ("v", v, (B, T, Hv, Dv), dt),
+        ("a", a, (B, T, Hv), f32), ("b", b, (B, T, Hv), f32), ("A_log", A_log, (Hv,), f32),
+        ("dt_bias", dt_bias, (Hv,), f32), ("initial_state", initial_state, (B, Hv, Dk, Dv), f32),
+        ("out", out, (B, T, Hv, Dv), dt), ("final_state", final_state, (B, Hv, Dk, Dv), f32),
+        _workspace_spec(workspace, gdn_chunk_fwd_workspace_bytes(dims))])
     if out is None:
         out = torch.empty((B, T, Hv, Dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
@@ -197,21 +222,14 @@ def gdn2_chunk_fwd(q, k, v, a, A_log, erase, write, initial_state=None, *, scale
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     dims = make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, scale)
-    for name, t in (("A_log", A_log), ("initial_state", initial_state), ("final_state", final_state)):
-        _f32(t, name)
-    for name, t in (("k", k), ("v", v), ("a", a), ("erase", erase), ("write", write)):
-        if t.dtype != q.dtype:
-            raise ValueError(f"{name} must have the dtype of q")
-    if k.shape != q.shape or tuple(v.shape[:2]) != (B, T):
-        raise ValueError("shape mismatch among q, k, v")
-    if tuple(a.shape) != (B, T, Hv, Dk) or tuple(erase.shape) != (B, T, Hv, Dk):
-        raise ValueError("a and erase must be [B,T,Hv,Dk]")
-    if tuple(write.shape) != (B, T, Hv, Dv):
-        raise ValueError("write must be [B,T,Hv,Dv]")
-    if tuple(A_log.shape) != (Hv, Dk):
-        raise ValueError("A_log must be [Hv,Dk]")
-    if initial_state is not None and tuple(initial_state.shape) != (B, Hv, Dk, Dv):
-        raise ValueError("initial_state must be [B,Hv,Dk,Dv]")
+    f32, dt = torch.float32, q.dtype
+    _validate(q.device, [
+        ("q", q, None, None), ("k", k, q.shape, dt), ("v", v, (B, T, Hv, Dv), dt),
+        ("a", a, (B, T, Hv, Dk), dt), ("erase", erase, (B, T, Hv, Dk), dt),
+        ("write", write, (B, T, Hv, Dv), dt), ("A_log", A_log, (Hv, Dk), f32),
+        ("initial_state", initial_state, (B, Hv, Dk, Dv), f32), ("out", out, (B, T, Hv, Dv), dt),
+        ("final_state", final_state, (B, Hv, Dk, Dv), f32),
+        _workspace_spec(workspace, gdn2_chunk_fwd_workspace_bytes(dims))])
     if out is None:
         out = torch.empty((B, T, Hv, Dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
@@ -242,32 +260,29 @@ def gdn2_chunk_bwd(q, k, v, a, A_log, erase, write, initial_state, d_out, d_fina
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     dims = make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, scale)
-    for name, t in (("A_log", A_log), ("initial_state", initial_state), ("d_final_state", d_final_state)):
-        _f32(t, name)
-    for name, t in (("k", k), ("v", v), ("a", a), ("erase", erase), ("write", write), ("d_out", d_out)):
-        if t.dtype != q.dtype:
-            raise ValueError(f"{name} must have the dtype of q")
-    if k.shape != q.shape or tuple(v.shape[:2]) != (B, T) or tuple(d_out.shape) != tuple(v.shape):
-        raise ValueError("shape mismatch among q, k, v, d_out")
-    if tuple(a.shape) != (B, T, Hv, Dk) or tuple(erase.shape) != (B, T, Hv, Dk):
-        raise ValueError("a and erase must be [B,T,Hv,Dk]")
-    if tuple(write.shape) != (B, T, Hv, Dv):
-        raise ValueError("write must be [B,T,Hv,Dv]")
-    if tuple(A_log.shape) != (Hv, Dk):
-        raise ValueError("A_log must be [Hv,Dk]")
-    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
-        if t is not None and tuple(t.shape) != (B, Hv, Dk, Dv):
-            raise ValueError(f"{name} must be [B,Hv,Dk,Dv]")
-    dev, f32 = q.device, torch.float32
-    g = grads if grads is not None else {"dq": torch.empty((B, T, Hk, Dk), dtype=f32, device=dev),
-         "dk": torch.empty((B, T, Hk, Dk), dtype=f32, device=dev),
-         "dv": torch.empty((B, T, Hv, Dv), dtype=f32, device=dev),
-         "da": torch.empty((B, T, Hv, Dk), dtype=f32, device=dev),
-         "d_erase": torch.empty((B, T, Hv, Dk), dtype=f32, device=dev),
-         "d_write": torch.empty((B, T, Hv, Dv), dtype=f32, device=dev),
-         "dA_log": torch.empty((Hv, Dk), dtype=f32, device=dev),
-         "d_initial_state": (torch.empty((B, Hv, Dk, Dv), dtype=f32, device=dev)
-                             if output_d_initial_state else None)}
+    f32, dt = torch.float32, q.dtype
+    gshapes = {"dq": (B, T, Hk, Dk), "dk": (B, T, Hk, Dk), "dv": (B, T, Hv, Dv), "da": (B, T, Hv, Dk),
+               "d_erase": (B, T, Hv, Dk), "d_write": (B, T, Hv, Dv), "dA_log": (Hv, Dk),
+               "d_initial_state": (B, Hv, Dk, Dv)}
+    if grads is not None:
+        if not isinstance(grads, dict):
+            raise TypeError("grads must be a dict of tensors")
+        missing = [n for n in gshapes if n not in grads or (grads[n] is None and n != "d_initial_state")]
+        if missing:
+            raise ValueError(f"grads is missing {missing}")
+    _validate(q.device, [
+        ("q", q, None, None), ("k", k, q.shape, dt), ("v", v, (B, T, Hv, Dv), dt),
+        ("a", a, (B, T, Hv, Dk), dt), ("erase", erase, (B, T, Hv, Dk), dt),
+        ("write", write, (B, T, Hv, Dv), dt), ("A_log", A_log, (Hv, Dk), f32),
+        ("initial_state", initial_state, (B, Hv, Dk, Dv), f32), ("d_out", d_out, (B, T, Hv, Dv), dt),
+        ("d_final_state", d_final_state, (B, Hv, Dk, Dv), f32),
+        *([(f"grads['{n}']", grads[n], shp, f32) for n, shp in gshapes.items()] if grads is not None else []),
+        _workspace_spec(workspace, gdn2_chunk_bwd_workspace_bytes(dims))])
+    dev = q.device
+    g = grads if grads is not None else {n: torch.empty(shp, dtype=f32, device=dev)
+                                         for n, shp in gshapes.items()
+                                         if n != "d_initial_state" or output_d_initial_state}
+    g.setdefault("d_initial_state", None)
     if workspace is None:
         workspace = torch.empty(max(gdn2_chunk_bwd_workspace_bytes(dims), 1), dtype=torch.uint8, device=dev)
     st = lib().gdn2_chunk_bwd_timed(
@@ -287,10 +302,13 @@ def gdn_recurrent_step(q, k, v, a, b, A_log, dt_bias, state, *, scale: float = 1
     B, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
     dims = make_dims(B, 1, Hk, Hv, Dk, Dv, q.dtype, scale)
-    for name, t in (("a", a), ("b", b), ("A_log", A_log), ("dt_bias", dt_bias), ("state", state)):
-        _f32(t, name)
-    if tuple(state.shape) != (B, Hv, Dk, Dv):
-        raise ValueError("state must be [B,Hv,Dk,Dv]")
+    f32, dt = torch.float32, q.dtype
+    _validate(q.device, [
+        ("q", q, None, None), ("k", k, q.shape, dt), ("v", v, (B, Hv, Dv), dt), ("a", a, (B, Hv), f32),
+        ("b", b, (B, Hv), f32), ("A_log", A_log, (Hv,), f32), ("dt_bias", dt_bias, (Hv,), f32),
+        ("state", state, (B, Hv, Dk, Dv), f32), ("out", out, (B, Hv, Dv), dt)])
+    if state is None:
+        raise ValueError("state is required")
     if out is None:
         out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=q.device)
     st = lib().gdn_recurrent_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
@@ -307,19 +325,13 @@ def gdn2_recurrent_step(q, k, v, a, A_log, erase, write, state, *, scale: float 
     B, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
     dims = make_dims(B, 1, Hk, Hv, Dk, Dv, q.dtype, scale)
-    for name, t in (("A_log", A_log), ("state", state)):
-        _f32(t, name)
-    for name, t in (("k", k), ("v", v), ("a", a), ("erase", erase), ("write", write)):
-        if t.dtype != q.dtype:
-            raise ValueError(f"{name} must have the dtype of q")
-    if tuple(a.shape) != (B, Hv, Dk) or tuple(erase.shape) != (B, Hv, Dk):
-        raise ValueError("a and erase must be [B,Hv,Dk]")
-    if tuple(write.shape) != (B, Hv, Dv):
-        raise ValueError("write must be [B,Hv,Dv]")
-    if tuple(A_log.shape) != (Hv, Dk):
-        raise ValueError("A_log must be [Hv,Dk]")
-    if tuple(state.shape) != (B, Hv, Dk, Dv):
-        raise ValueError("state must be [B,Hv,Dk,Dv]")
+    f32, dt = torch.float32, q.dtype
+    _validate(q.device, [
+        ("q", q, None, None), ("k", k, q.shape, dt), ("v", v, (B, Hv, Dv), dt), ("a", a, (B, Hv, Dk), dt),
+        ("erase", erase, (B, Hv, Dk), dt), ("write", write, (B, Hv, Dv), dt), ("A_log", A_log, (Hv, Dk), f32),
+        ("state", state, (B, Hv, Dk, Dv), f32), ("out", out, (B, Hv, Dv), dt)])
+    if state is None:
+        raise ValueError("state is required")
     if out is None:
         out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=q.device)
     st = lib().gdn2_recurrent_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(A_log),
@@ -336,15 +348,12 @@ def gdn_gated_rmsnorm(x, z, weight, *, eps: float = 1e-6, gate: str = "silu", ou
     """Gated RMS normalisation over the last axis (d = 64 or 128): x / rms(x) * weight *
     act(z), act = SiLU ("silu") or sigmoid ("sigmoid").  x and z of one shape and dtype
     (bf16 or fp32); weight [d] fp32.  out may be x (in place)."""
-    if z.shape != x.shape or z.dtype != x.dtype:
-        raise ValueError("z must have the shape and dtype of x")
     d = x.shape[-1]
-    _f32(weight, "weight")
-    if tuple(weight.shape) != (d,):
-        raise ValueError("weight must be [d]")
     gates = {"silu": GDN_GATE_SILU, "sigmoid": GDN_GATE_SIGMOID}
     if gate not in gates:
         raise ValueError(f"gate must be one of {sorted(gates)}")
+    _validate(x.device, [("x", x, None, None), ("z", z, x.shape, x.dtype),
+                         ("weight", weight, (d,), torch.float32), ("out", out, x.shape, x.dtype)])
     if out is None:
         out = torch.empty_like(x)
     rows = x.numel() // d if d else 0
@@ -369,16 +378,14 @@ def gdn_causal_conv1d(x, weight, bias=None, conv_state=None, *, Hk: int, Hv: int
     K = weight.shape[1] if weight.dim() == 2 else 0
     if C != 2 * Hk * Dk + Hv * Dv:
         raise ValueError("x's last axis must be 2 Hk Dk + Hv Dv")
-    _f32(weight, "weight")
-    _f32(bias, "bias")
-    if tuple(weight.shape) != (C, K) or (bias is not None and tuple(bias.shape) != (C,)):
-        raise ValueError("weight must be [C, K] and bias [C]")
-    for name, t in (("conv_state", conv_state), ("conv_state_out", conv_state_out)):
-        if t is not None and (tuple(t.shape) != (B, K - 1, C) or t.dtype != x.dtype):
-            raise ValueError(f"{name} must be [B, K-1, C] in the dtype of x")
     acts = {"silu": GDN_ACT_SILU, "none": GDN_ACT_NONE}
     if activation not in acts:
         raise ValueError(f"activation must be one of {sorted(acts)}")
+    f32, dt = torch.float32, x.dtype
+    _validate(x.device, [
+        ("x", x, None, None), ("weight", weight, (C, K), f32), ("bias", bias, (C,), f32),
+        ("conv_state", conv_state, (B, K - 1, C), dt), ("conv_state_out", conv_state_out, (B, K - 1, C), dt),
+        ("q", q, (B, T, Hk, Dk), dt), ("k", k, (B, T, Hk, Dk), dt), ("v", v, (B, T, Hv, Dv), dt)])
     dims = make_dims(B, T, Hk, Hv, Dk, Dv, x.dtype)
     mk = lambda H, D: torch.empty((B, T, H, D), dtype=x.dtype, device=x.device)
     q = mk(Hk, Dk) if q is None else q
