@@ -296,7 +296,6 @@ gdn_status gdn2_chunk_bwd_timed(const gdn_dims *d, const void *q, const void *k,
                 return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[i]->name, outs[j]->name);
     }
     ok();
-    if (B == 0) return GDN_OK;
     gdn::Bwd2Args p{};
     p.B = d->B; p.T = d->T; p.Hk = d->Hk; p.Hv = d->Hv; p.Dk = d->Dk; p.Dv = d->Dv;
     p.NC = (d->T + 63) / 64; p.scale = d->scale;

@@ -956,7 +956,7 @@ __global__ __launch_bounds__(256) void g2b_reduce(Bwd2Args p, Bwd2Workspace ws) 
     }
 }
 
-// T = 0: dS0 = dS_T (or 0), dA_log = 0
+// T = 0: dS0 = dS_T (or 0), dA_log = 0; B = 0 (ns = 0): dA_log = 0
 __global__ void g2b_empty(float *dS0, const float *dST, size_t ns, float *dA_log, size_t na) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < ns + na; i += (size_t)gridDim.x * blockDim.x) {
         if (i < ns) {
@@ -1030,8 +1030,7 @@ size_t bwd2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, B
 }
 
 hipError_t launch_bwd2(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t s, const hipEvent_t *ev) {
-    if (p.B == 0) return hipSuccess;
-    if (p.T == 0) {
+    if (p.B == 0 || p.T == 0) {  // no tokens: dA_log (a sum over none) is zero
         const size_t ns = (size_t)p.B * p.Hv * p.Dk * p.Dv, na = (size_t)p.Hv * p.Dk;
         hipLaunchKernelGGL(g2b_empty, dim3((unsigned)((ns + na) / 256 + 1 < 65536 ? (ns + na) / 256 + 1 : 65536)),
                            dim3(256), 0, s, p.dS0, p.dST, ns, p.dA_log, na);

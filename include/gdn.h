@@ -9,8 +9,8 @@
  *
  * with alpha_t = exp(g_t), g_t = -exp(A_log[h]) * softplus(a_t + dt_bias[h]),
  * softplus(x) = log(1 + e^x) and beta_t = sigmoid(b_t).
- * Sources: rainlin-net.pages.dev "Qwen3.5", section "GDN详解" (the rule, its
- * five-step expansion and the [d_k][d_v] state indexing of its eager loop);
+ * Sources: rainlin-net.pages.dev "Qwen3.5", section "GDN详解" (the rule and
+ * the [d_k][d_v] state layout used there);
  * dingfen.github.io "从 Full Attention 到 Gated DeltaNet", sections 9-10 (gate
  * parametrisation, read-out S^T q); wanger-sjtu.github.io Qwen3.5 Gated
  * DeltaNet architecture page, section "缓存与推理/训练分支" (a chunked path for a
@@ -27,8 +27,17 @@
  *    any error nothing is enqueued and no output is touched.  No exception or
  *    abort crosses the ABI.  gdn_status_str() names a status code.
  *  - GDN_BF16 inputs are multiplied on the matrix cores as float16 operands
- *    with float32 accumulation: |q|, |k|, |v| entries and state entries must
- *    stay below 6.0e4 (the float16 range).  GDN_F32 runs float32 end to end.
+ *    with float32 accumulation (the chunked paths; the decode steps are
+ *    float32).  Besides q and k, the value-sized operands -- v, the state and
+ *    the residuals derived from them -- are rounded to float16, whose normal
+ *    range is [6.1e-5, 6.5e4].  The accuracy stated for bf16 inputs (relative
+ *    L2 <= 2e-3 on outputs and final state) holds while the root mean square
+ *    of v's entries and of the initial state's entries lies in
+ *    [2^-10, 2^10] (tested at both ends, with L2-normalised q and k); the rule
+ *    is linear in (v, S0), so a caller outside that range can rescale both by a
+ *    power of two and scale the results back exactly.  Below it the float16
+ *    operands lose relative precision (subnormals), above it they can
+ *    overflow.  GDN_F32 runs float32 end to end.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -151,7 +160,8 @@ gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const
  *                   heads that share a key head
  *   dv, d_write     [B,T,Hv,Dv] float32 (written)
  *   da, d_erase     [B,T,Hv,Dk] float32 (written)
- *   dA_log          [Hv,Dk] float32 (written): summed over sequences and tokens
+ *   dA_log          [Hv,Dk] float32 (written): summed over sequences and tokens,
+ *                   so zero when B == 0 or T == 0 (it is written then too)
  *   d_initial_state [B,Hv,Dk,Dv] float32 (written), or NULL to skip it
  *   workspace       device scratch of at least gdn2_chunk_bwd_workspace_bytes(d)
  *                   bytes, 256-byte aligned (about 0.6 MB per (sequence, value

@@ -429,10 +429,12 @@ def test_bwd2_validation():
     a = bwd2_args(buf, d)
     a["dS0"] = a["ws"]
     assert call_bwd2(d, a) == ERR_ALIAS
+    # B = 0: the per-token tensors are empty (their pointers unused), but dA_log [Hv,Dk] is
+    # still written (zeros), so it must be given; the zeroing itself is a GPU test
     d0 = dims(B=0)
     assert call_bwd2(d0, bwd2_args(buf, d0, q=None, k=None, v=None, a=None, erase=None, write=None,
                                    dout=None, dq=None, dk=None, dv=None, da=None, derase=None,
-                                   dwrite=None, dS0=None, ws=None)) == OK
+                                   dwrite=None, dS0=None, ws=None, dAl=None)) == ERR_NULL
 
 
 # ---- Gated DeltaNet-2 decode step (gdn2_recurrent_step) ----

@@ -125,6 +125,24 @@ def test_zero_length():
     assert torch.count_nonzero(got["dA_log"]) == 0
 
 
+def test_zero_batch_zeroes_dA_log():
+    """B = 0: no sequence contributes, so dA_log (a sum over sequences and tokens) is zero;
+    it is written even though every per-token tensor is empty."""
+    import gated_deltanet_sequence_amd as gdn
+    spec = g2(B=1, T=4, Hk=1, Hv=2, Dk=128, Dv=128, seed=528)
+    log(f"[gdn2 bwd B=0] {spec}")
+    inp = to_dev(synth.make_inputs(spec))
+    e = lambda t: t[:0].contiguous()
+    got = gdn.gdn2_chunk_bwd(e(inp["q"]), e(inp["k"]), e(inp["v"]), e(inp["a"]), inp["A_log"],
+                             e(inp["erase"]), e(inp["write"]), None, e(inp["v"]))
+    g0 = got["dA_log"]
+    g0.fill_(float("nan"))
+    got = gdn.gdn2_chunk_bwd(e(inp["q"]), e(inp["k"]), e(inp["v"]), e(inp["a"]), inp["A_log"],
+                             e(inp["erase"]), e(inp["write"]), None, e(inp["v"]), grads=got)
+    torch.cuda.synchronize()
+    assert got["dA_log"].shape == (2, 128) and torch.count_nonzero(got["dA_log"]) == 0
+
+
 def test_deterministic():
     spec = g2(B=1, T=200, Hk=1, Hv=4, Dk=128, Dv=128, seed=527, init_state=True)
     log(f"[gdn2 bwd determinism] {spec}")
