@@ -195,6 +195,31 @@ def head_slice(inp: Dict[str, Optional[torch.Tensor]], spec: GDNSpec, b: int, hv
     return o
 
 
+def key_head_slice(inp: Dict[str, Optional[torch.Tensor]], spec: GDNSpec, b0: int, b1: int,
+                   hk0: int, hk1: int):
+    """Inputs of sequences b0..b1-1 and key heads hk0..hk1-1 together with the value heads
+    that read them (value heads hk0*G .. hk1*G-1, G = Hv // Hk), as a smaller problem.
+
+    Pure indexing, like head_slice."""
+    G = spec.Hv // spec.Hk
+    v0, v1 = hk0 * G, hk1 * G
+    o = {
+        "q": inp["q"][b0:b1, :, hk0:hk1],
+        "k": inp["k"][b0:b1, :, hk0:hk1],
+        "v": inp["v"][b0:b1, :, v0:v1],
+        "a": inp["a"][b0:b1, :, v0:v1],
+        "A_log": inp["A_log"][v0:v1],
+    }
+    if spec.variant == "gdn":
+        o["b"] = inp["b"][b0:b1, :, v0:v1]
+        o["dt_bias"] = inp["dt_bias"][v0:v1]
+    else:
+        o["erase"] = inp["erase"][b0:b1, :, v0:v1]
+        o["write"] = inp["write"][b0:b1, :, v0:v1]
+    o["S0"] = None if inp["S0"] is None else inp["S0"][b0:b1, v0:v1]
+    return o
+
+
 def make_norm_inputs(shape, dtype: str, seed: int, x_sigma: float = 1.0):
     """Inputs of the gated RMS normalisation: x ~ N(0, x_sigma^2) and the gate z ~ N(0, 1)
     of ``shape`` (last axis = d) in ``dtype`` ("f32" or "bf16"), weight [d] ~ U(0.5, 1.5)
