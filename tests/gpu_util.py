@@ -179,3 +179,7 @@ def check_stats(name: str, st: Stats, tol: float, head_tol: Optional[float] = No
 # and the kernel's own error, against the oracle rounded to bf16, at 1.2e-3.
 BF16_BOUNDS = dict(tol=2e-3, head_tol=2e-3, chunk_tol=4e-3)
 BF16_ROUNDED_TOL = 1.2e-3
+# The decode workloads give each head only 16 or 64 tokens (2048 or 8192 outputs): the bf16
+# rounding of the output alone spreads more per head (measured up to 1.96e-3 while the
+# step's own error against the rounded oracle is 1.8e-5), so their heads are gated at 2.5e-3.
+BF16_DECODE_BOUNDS = dict(tol=2e-3, head_tol=2.5e-3, chunk_tol=4e-3)

@@ -6,7 +6,7 @@ import torch
 import oracle
 import synth
 from synth import GDNSpec, WORKLOADS
-from tests.gpu_util import (BF16_BOUNDS, BF16_ROUNDED_TOL, TOL, Stats, accumulate_out, accumulate_state,
+from tests.gpu_util import (BF16_DECODE_BOUNDS, BF16_ROUNDED_TOL, TOL, Stats, accumulate_out, accumulate_state,
                             assert_close, check_stats, log, oracle_prefill, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -78,7 +78,7 @@ def test_decode_b256_64_steps():
         o_ref, s_ref = oracle_prefill(sl)
         accumulate_out(so, out[b0:b0 + 32], o_ref, b0=b0, bf16=True)
         accumulate_state(ss, S[b0:b0 + 32], s_ref, b0=b0)
-    check_stats("out (16384 heads x 64 steps)", so, **BF16_BOUNDS, rounded_tol=BF16_ROUNDED_TOL)
+    check_stats("out (16384 heads x 64 steps)", so, **BF16_DECODE_BOUNDS, rounded_tol=BF16_ROUNDED_TOL)
     check_stats("state (16384 heads)", ss, TOL["bf16"], head_tol=TOL["bf16"])
 
 

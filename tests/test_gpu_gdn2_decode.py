@@ -11,7 +11,7 @@ import torch
 import oracle
 import synth
 from synth import GDNSpec, SLOW_DECAY, WORKLOADS
-from tests.gpu_util import (BF16_BOUNDS, BF16_ROUNDED_TOL, TOL, Stats, accumulate_out, accumulate_state,
+from tests.gpu_util import (BF16_DECODE_BOUNDS, BF16_ROUNDED_TOL, TOL, Stats, accumulate_out, accumulate_state,
                             assert_close, check_stats, log, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -139,7 +139,7 @@ def test_decode_gdn2_b256():
                                        sl["write"], S0=sl["S0"])
         accumulate_out(so, out[b0:b0 + 32], o_ref, b0=b0, bf16=True)
         accumulate_state(ss, S[b0:b0 + 32], s_ref, b0=b0)
-    check_stats("out (16384 heads x 16 steps)", so, **BF16_BOUNDS, rounded_tol=BF16_ROUNDED_TOL)
+    check_stats("out (16384 heads x 16 steps)", so, **BF16_DECODE_BOUNDS, rounded_tol=BF16_ROUNDED_TOL)
     check_stats("state (16384 heads)", ss, TOL["bf16"], head_tol=TOL["bf16"])
 
 
