@@ -55,6 +55,8 @@ def lib():
     L.gdn_chunk_fwd_timed.restype = ctypes.c_int
     L.gdn_chunk_fwd_timed.argtypes = [dims_p, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, vp, sz, vp,
                                       ctypes.POINTER(ctypes.c_void_p)]
+    L.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
+    L.gdn_chunk_fwd_noalloc.argtypes = [dims_p, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, vp]
     L.gdn2_chunk_fwd_workspace_bytes.restype = sz
     L.gdn2_chunk_fwd_workspace_bytes.argtypes = [dims_p]
     L.gdn2_chunk_fwd.restype = ctypes.c_int
@@ -209,6 +211,35 @@ def gdn_chunk_fwd(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, scale: f
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
         _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream), ev)
+    _check(st)
+    return out, final_state
+
+
+NOALLOC_MAX_WORKSPACE_BYTES = 128 << 20  # GDN_NOALLOC_MAX_WORKSPACE_BYTES
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, scale: float = 1.0,
+                          out=None, final_state=None, output_final_state: bool = True, stream=None
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """gdn_chunk_fwd without a workspace: the library's own device scratch is used (see
+    gdn_chunk_fwd_noalloc in include/gdn.h: bounded size, one per GPU, shared by all calls
+    on that GPU).  Pass out (and final_state) to allocate nothing at all."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dims = make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, scale)
+    f32, dt = torch.float32, q.dtype
+    _validate(q.device, [
+        ("q", q, None, None), ("k", k, q.shape, dt), ("v", v, (B, T, Hv, Dv), dt),
+        ("a", a, (B, T, Hv), f32), ("b", b, (B, T, Hv), f32), ("A_log", A_log, (Hv,), f32),
+        ("dt_bias", dt_bias, (Hv,), f32), ("initial_state", initial_state, (B, Hv, Dk, Dv), f32),
+        ("out", out, (B, T, Hv, Dv), dt), ("final_state", final_state, (B, Hv, Dk, Dv), f32)])
+    if out is None:
+        out = torch.empty((B, T, Hv, Dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=q.device)
+    st = lib().gdn_chunk_fwd_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+        _ptr(initial_state), _ptr(out), _ptr(final_state), _stream(stream))
     _check(st)
     return out, final_state
 

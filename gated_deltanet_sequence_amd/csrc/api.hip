@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gdn.h"
 #include "gdn_launch.h"
 
@@ -107,13 +109,75 @@ size_t gdn_chunk_fwd_workspace_bytes(const gdn_dims *d) {
                                          nullptr);
 }
 
-gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k, const void *v,
-                               const float *a, const float *b, const float *A_log,
-                               const float *dt_bias, const float *initial_state, void *out,
-                               float *final_state, void *workspace, size_t workspace_bytes,
-                               void *stream, void *const *stage_events) {
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Device scratch of gdn_chunk_fwd_noalloc: the prefill workspace in a
+// file-scope device array instead of caller memory.  Each GPU the library runs
+// on holds its own copy (allocated with the code object, kept until the
+// process ends).  In host code `scratch` names a host-side stand-in, not a
+// device address: its address on a device is resolved once per device with
+// hipGetSymbolAddress (with that device current) and only that pointer is
+// ever handed to a kernel.  Calls on one GPU share the array; the prefill
+// kernels write every workspace byte they read, so nothing is cleared.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_MAX_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (nullptr: not resolved yet)
+
+// Device address of `scratch` on the device that runs `stream`.
+gdn_status scratch_on(hipStream_t stream, void **ptr) {
+    int cur = -1, dev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    dev = cur;
+    if (stream) {
+        hipDevice_t sd;
+        e = hipStreamGetDevice(stream, &sd);
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        dev = (int)sd;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(GDN_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess && e2 != hipSuccess) e = e2;
+        }
+        if (e != hipSuccess || !p)
+            return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return GDN_OK;
+}
+
+// The chunked prefill: validation, then the launches.  With noalloc the
+// workspace arguments are ignored and the device scratch is used (the size
+// limit is checked with the other arguments, before any HIP call).
+gdn_status prefill(const gdn_dims *d, const void *q, const void *k, const void *v, const float *a,
+                   const float *b, const float *A_log, const float *dt_bias, const float *initial_state,
+                   void *out, float *final_state, void *workspace, size_t workspace_bytes, void *stream,
+                   void *const *stage_events, bool noalloc) {
     gdn_status st = check_dims(d, true);
     if (st != GDN_OK) return st;
+    if (noalloc) {
+        const size_t wneed = gdn_chunk_fwd_workspace_bytes(d);
+        if (wneed > GDN_NOALLOC_MAX_WORKSPACE_BYTES)
+            return fail(GDN_ERR_WORKSPACE,
+                        "these dims need %zu bytes of scratch, more than the %zu bytes gdn_chunk_fwd_noalloc "
+                        "holds: call gdn_chunk_fwd with a workspace",
+                        wneed, (size_t)GDN_NOALLOC_MAX_WORKSPACE_BYTES);
+        workspace = nullptr;
+        workspace_bytes = 0;
+    }
     const size_t B = d->B, T = d->T, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv, es = esize(d);
     const Span sq{"q", q, B * T * Hk * Dk * es}, sk{"k", k, B * T * Hk * Dk * es};
     const Span sv{"v", v, B * T * Hv * Dv * es};
@@ -128,7 +192,7 @@ gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k, 
         if ((st = need(*s, 16)) != GDN_OK) return st;
     for (const Span *s : {&sa, &sb, &sal, &sdt})
         if ((st = need(*s, 4)) != GDN_OK) return st;
-    if (wneed) {
+    if (wneed && !noalloc) {
         if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", wneed);
         if (workspace_bytes < wneed)
             return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, wneed);
@@ -160,6 +224,7 @@ gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k, 
         if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));
         return GDN_OK;
     }
+    if (noalloc && (st = scratch_on(hs, &workspace)) != GDN_OK) return st;
     gdn::PrefillWorkspace ws;
     gdn::prefill_workspace_layout(d->B, d->T, d->Hk, d->Hv, d->Dk, p.f32, workspace, &ws);
     if (e == hipSuccess) e = rec(0);
@@ -171,12 +236,33 @@ gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k, 
     return GDN_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k, const void *v,
+                               const float *a, const float *b, const float *A_log,
+                               const float *dt_bias, const float *initial_state, void *out,
+                               float *final_state, void *workspace, size_t workspace_bytes,
+                               void *stream, void *const *stage_events) {
+    return prefill(d, q, k, v, a, b, A_log, dt_bias, initial_state, out, final_state, workspace,
+                   workspace_bytes, stream, stage_events, false);
+}
+
 gdn_status gdn_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const void *v,
                          const float *a, const float *b, const float *A_log, const float *dt_bias,
                          const float *initial_state, void *out, float *final_state, void *workspace,
                          size_t workspace_bytes, void *stream) {
-    return gdn_chunk_fwd_timed(d, q, k, v, a, b, A_log, dt_bias, initial_state, out, final_state,
-                               workspace, workspace_bytes, stream, nullptr);
+    return prefill(d, q, k, v, a, b, A_log, dt_bias, initial_state, out, final_state, workspace,
+                   workspace_bytes, stream, nullptr, false);
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const gdn_dims *d, const void *q, const void *k, const void *v,
+                                 const float *a, const float *b, const float *A_log,
+                                 const float *dt_bias, const float *initial_state, void *out,
+                                 float *final_state, void *stream) {
+    return prefill(d, q, k, v, a, b, A_log, dt_bias, initial_state, out, final_state, nullptr, 0, stream,
+                   nullptr, true);
 }
 
 size_t gdn2_chunk_fwd_workspace_bytes(const gdn_dims *d) {

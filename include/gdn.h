@@ -18,7 +18,8 @@
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing and keeps no global mutable state.  Tensors are dense,
+ *    allocates nothing and keeps no global mutable state (except the device
+ *    scratch of gdn_chunk_fwd_noalloc, described there).  Tensors are dense,
  *    row-major, contiguous, and 16-byte aligned.
  *  - Value head h reads key/query head h / (Hv / Hk) (consecutive groups).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
@@ -120,6 +121,27 @@ gdn_status gdn_chunk_fwd_timed(const gdn_dims *d, const void *q, const void *k,
                                const float *initial_state, void *out, float *final_state,
                                void *workspace, size_t workspace_bytes, void *stream,
                                void *const *stage_events);
+
+/* gdn_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and kernels as gdn_chunk_fwd, without the workspace:
+ * the scratch lives in a device array of GDN_NOALLOC_MAX_WORKSPACE_BYTES
+ * inside the library (one per GPU, allocated with the code object and held
+ * until the process ends).  Dims whose gdn_chunk_fwd_workspace_bytes exceeds
+ * that size are rejected with GDN_ERR_WORKSPACE before anything runs (at
+ * Hk = 16, Hv = 64, Dk = Dv = 128 that allows B * ceil(T / 64) <= 99 chunks,
+ * about 6300 tokens).  The call
+ * allocates nothing and makes no allocating library call; the first call on a
+ * device resolves that device's array address once (the device running
+ * `stream`).  All calls on one GPU share the array: calls that overlap in time
+ * on one GPU (different streams, or concurrent host threads) race and give
+ * wrong results; serialise them. */
+#define GDN_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)128 << 20)
+gdn_status gdn_chunk_fwd_noalloc(const gdn_dims *d, const void *q, const void *k,
+                                 const void *v, const float *a, const float *b,
+                                 const float *A_log, const float *dt_bias,
+                                 const float *initial_state, void *out, float *final_state,
+                                 void *stream);
 
 /* Gated DeltaNet-2 chunked prefill (zhichai.net "Gated DeltaNet-2" digest:
  * the decoupled update S <- diag(D_t) S + k_t (z_t - (diag(D_t) S)^T e_t)^T with

@@ -217,6 +217,32 @@ def test_prefill_zero_batch_is_a_noop():
     assert call_prefill(d, a) == OK
 
 
+def test_noalloc_rejects_dims_beyond_its_scratch():
+    """gdn_chunk_fwd_noalloc checks the workspace its dims need against its fixed device scratch
+    before any HIP call: beyond it, GDN_ERR_WORKSPACE with a message naming both sizes."""
+    L = binding.lib()
+    buf = Buf()
+    limit = binding.NOALLOC_MAX_WORKSPACE_BYTES
+    d = dims(B=1, T=8192, Hk=16, Hv=64, Dk=128, Dv=128)
+    need = L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    assert need > limit
+    a = prefill_args(buf, dims())  # pointers are never dereferenced: the size check comes first
+    st = L.gdn_chunk_fwd_noalloc(ctypes.byref(d), a["q"], a["k"], a["v"], a["a"], a["b"], a["A_log"],
+                                 a["dt_bias"], a["S0"], a["out"], a["ST"], None)
+    assert st == ERR_WORKSPACE
+    assert str(need) in last_error() and str(limit) in last_error()
+    # the limit stated in include/gdn.h: 99 chunks of one sequence fit at this head configuration,
+    # 100 do not
+    d100 = dims(B=1, T=6400, Hk=16, Hv=64, Dk=128, Dv=128)
+    assert L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(d100)) > limit
+    d99 = dims(B=1, T=6336, Hk=16, Hv=64, Dk=128, Dv=128)
+    assert L.gdn_chunk_fwd_workspace_bytes(ctypes.byref(d99)) <= limit
+    # invalid dims are reported as such first
+    st = L.gdn_chunk_fwd_noalloc(ctypes.byref(dims(Dk=96)), a["q"], a["k"], a["v"], a["a"], a["b"],
+                                 a["A_log"], a["dt_bias"], a["S0"], a["out"], a["ST"], None)
+    assert st == ERR_UNSUPPORTED
+
+
 def step_args(buf, d, **override):
     es = 4 if d.dtype == binding.GDN_F32 else 2
     B, Hk, Hv, Dk, Dv = d.B, d.Hk, d.Hv, d.Dk, d.Dv
