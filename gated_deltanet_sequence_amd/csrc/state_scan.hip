@@ -391,9 +391,9 @@ __device__ __forceinline__ h8 img_h8(const _Float16 *X, int rowlen, int R, int k
     return *reinterpret_cast<const h8 *>(X + R * rowlen + 8 * ((4 * kq + g) ^ img_swz<false>(R, rowlen)));
 }
 
-template <typename TIn, int DK, int NL, bool G2>
+template <typename TIn, int DK, int NL, bool G2, int NT_ = 2>
 struct SplitCfg {
-    static constexpr int NT = 2;                                   // 16-column tiles (state waves) per work-group
+    static constexpr int NT = NT_;                                 // 16-column tiles (state waves) per work-group
     static constexpr int NCOL = 16 * NT;
     static constexpr int NKQ = DK / 32;                            // 32-deep contraction steps over d_k
     static constexpr int IMG_BYTES = C * DK * 2;
@@ -417,7 +417,10 @@ struct SplitCfg {
     static constexpr int O_Q = 0, O_F = O_Q + IMG_BYTES, O_TK = O_F + FRAG_BYTES, O_BUF = O_TK + OTK_BYTES;
     // hand-over: S (d_k x 16) and R' (64 x 16) of each column tile as operand pairs, 1 KB each
     static constexpr int X_S = 0, X_R = NT * NKQ * 1024, X_BUF = X_R + NT * 2 * 1024;
-    static constexpr int NSB = G2 ? 2 : 3, NOB = G2 ? 2 : 3;
+    // buffer depths: three each where they fit in LDS (two chunks of lead), else
+    // the state stream keeps three if it can; the channel-wise decay two each
+    static constexpr int NSB = G2 ? 2 : (3 * S_BUF + 2 * O_BUF + X_BUF <= 160 * 1024) ? 3 : 2;
+    static constexpr int NOB = G2 ? 2 : (NSB * S_BUF + 3 * O_BUF + X_BUF <= 160 * 1024) ? 3 : 2;
     static constexpr int OFF_S = 0, OFF_O = OFF_S + NSB * S_BUF, OFF_X = OFF_O + NOB * O_BUF, LDS = OFF_X + X_BUF;
     static constexpr int IMG_UNITS = IMG_BYTES / 1024, FRAG_UNITS = FRAG_BYTES / 1024,
                          TILE_UNITS = TILE_BYTES / 1024;
@@ -434,9 +437,9 @@ struct SplitCfg {
 // instruction, straight from memory into LDS (no registers).  One loader wave
 // stages the state-wave inputs, the other the output-wave inputs: each wave's
 // loads complete in issue order, so the two streams do not wait on each other.
-template <typename TIn, int DK, int NL, bool G2>
+template <typename TIn, int DK, int NL, bool G2, int NT>
 struct SplitLoader {
-    typedef SplitCfg<TIn, DK, NL, G2> CF;
+    typedef SplitCfg<TIn, DK, NL, G2, NT> CF;
     __amdgpu_buffer_rsrc_t vres, rq, rk, rkh, ra, rf, rtk, rgc;
     int lane;
     unsigned vcol;  // element offset of this group's first V column in a token row
@@ -509,18 +512,24 @@ struct SplitLoader {
     }
 };
 
-template <typename TIn, int DK, int DV, int NL, bool G2>
-__global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
+template <typename TIn, int DK, int DV, int NL, bool G2, int NT_>
+__global__ __launch_bounds__(64 * (NT_ + 2 + NL)) void scan_split_kernel(
     int T, int Hk, int Hv, int NC, const void *__restrict__ v, const float *__restrict__ tok,
     const _Float16 *__restrict__ apair, const _Float16 *__restrict__ qpair,
     const _Float16 *__restrict__ qimg, const _Float16 *__restrict__ kimg,
     const _Float16 *__restrict__ khimg, const float *__restrict__ gcrec,
     const float *__restrict__ S0, TIn *__restrict__ out, float *__restrict__ ST) {
     static_assert(sizeof(TIn) == 2, "bfloat16 inputs");
-    static_assert(NL == 2, "waves 4 and 5 load");
-    typedef SplitCfg<TIn, DK, NL, G2> CF;
+    static_assert(NL == 2, "two loader waves");
+    static_assert(NT_ == 2 || (NT_ == 4 && !G2), "2 or 4 column tiles (4: scalar decay)");
+    typedef SplitCfg<TIn, DK, NL, G2, NT_> CF;
     typedef _Float16 E;
     constexpr int NT = CF::NT, NCOL = CF::NCOL, NKB = DK / 16, NKQ = CF::NKQ, NCG = DV / NCOL;
+    // Wave roles.  Waves w and w + 4 share a SIMD.  Two column tiles: output
+    // waves 0, 1, state waves 2, 3, loaders 4, 5 (each state wave alone on its
+    // SIMD).  Four column tiles: state waves 0..3 (one per SIMD), output
+    // waves 4, 5 and loaders 6, 7 beside them.
+    constexpr int W_STATE = NT == 2 ? 2 : 0, W_OUT = NT == 2 ? 0 : 4, W_LOAD = NT == 2 ? 4 : 6;
 
     __shared__ __attribute__((aligned(1024))) char smem[CF::LDS];
 
@@ -540,11 +549,11 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
     };
 
-    if (w >= 4) {
+    if (w >= W_LOAD) {
         // ================= loader waves =================
         const size_t ku0 = ((size_t)bb * Hk + hk) * NC, vu0 = ((size_t)bb * Hv + hv) * NC;
         const size_t iu0 = G2 ? vu0 : ku0;  // images per value head (channel-wise decay) or per key head
-        SplitLoader<TIn, DK, NL, G2> ld;
+        SplitLoader<TIn, DK, NL, G2, NT> ld;
         ld.vres = rsrc((const char *)v + (size_t)bb * seq_elems * 2, seq_elems * 2);
         ld.rq = rsrc(qimg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
         ld.rk = rsrc(kimg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
@@ -575,7 +584,7 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
             else if (K < 2 || k == 1) wait_vmcnt<L>();
             else wait_vmcnt<(K < 2 ? 0 : 2 * L)>();
         };
-        if (G2 && w == 5) {
+        if (G2 && w == W_LOAD + 1) {
             // Channel-wise decay, two state buffers: chunk m lives in buffer
             // m % 2.  Its early portion is read during E(m-1) (from P(m-1) to
             // F(m-1)), its late portion during A(m) and B(m) (from F(m-1) to
@@ -617,7 +626,7 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
                     bare_barrier();  // P(n+1)
                 }
             }
-        } else if (w == 5) {
+        } else if (w == W_LOAD + 1) {
             // state-wave inputs: chunk m is read from P(m-1) to P(m), buffer
             // m % NSB; chunk n+NSB is issued after P(n)
             const std::integral_constant<int, CF::STATE_LOADS> SL;
@@ -664,7 +673,7 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         return;
     }
 
-    if (w <= 1) {
+    if (w >= W_OUT && w < W_OUT + 2) {
         // ================= output waves (one chunk behind) =================
         // wave 0: token row tiles 0 and 3, wave 1: row tiles 1 and 2 (the same
         // number of products each), both column tiles
@@ -731,7 +740,7 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         int ob = 0;      // buffer of chunk n
         for (int n = 0; n < NC; ++n) {
             bare_barrier();  // P(n)
-            if (w == 0) emit(n, ob, std::integral_constant<int, 0>(), std::integral_constant<int, 3>());
+            if (w == W_OUT) emit(n, ob, std::integral_constant<int, 0>(), std::integral_constant<int, 3>());
             else emit(n, ob, std::integral_constant<int, 1>(), std::integral_constant<int, 2>());
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this chunk's LDS reads are done
             ob = ob == CF::NOB - 1 ? 0 : ob + 1;
@@ -739,8 +748,8 @@ __global__ __launch_bounds__(64 * (4 + NL)) void scan_split_kernel(
         return;
     }
 
-    // ================= state waves: column tile c = w - 2 =================
-    const int c = w - 2;
+    // ================= state waves: column tile c = w - W_STATE =================
+    const int c = w - W_STATE;
     f4 S[NKB];
     const size_t sb = ((size_t)bb * Hv + hv) * DK * DV;
     const int scol = NCOL * cg + 16 * c + m;
@@ -962,11 +971,33 @@ static hipError_t launch_scan_t(const PrefillArgs &p, const PrefillWorkspace &ws
     if constexpr (!F32) {
         constexpr int NL = 2;
         const int NC = (p.T + C - 1) / C;
-        const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<TIn, DK, NL, false>::NCOL));
-        hipLaunchKernelGGL((scan_split_kernel<TIn, DK, DV, NL, false>), dim3(blocks), dim3(64 * (4 + NL)), 0, s,
-                           p.T, p.Hk, p.Hv, NC, p.v, ws.tok, (const E *)ws.apair,
-                           (const E *)ws.qpair, (const E *)ws.qimg, (const E *)ws.kimg, (const E *)nullptr,
-                           (const float *)nullptr, p.S0, (TIn *)p.out, p.ST);
+        // 32 columns per work-group while that gives at most two work-groups per
+        // CU; beyond, 64 columns (four state waves, one per SIMD), so that all
+        // chains run in one round instead of two
+        static int cus = 0;
+        if (cus == 0) {
+            int dev = 0, n = 0;
+            if (hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+                cus = n;
+            else
+                cus = 256;
+        }
+        const long long units32 = (long long)p.B * p.Hv * (DV / 32);
+        if (units32 > cus) {
+            typedef SplitCfg<TIn, DK, NL, false, 4> CF4;
+            const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / CF4::NCOL));
+            hipLaunchKernelGGL((scan_split_kernel<TIn, DK, DV, NL, false, 4>), dim3(blocks), dim3(64 * (4 + 2 + NL)),
+                               0, s, p.T, p.Hk, p.Hv, NC, p.v, ws.tok, (const E *)ws.apair, (const E *)ws.qpair,
+                               (const E *)ws.qimg, (const E *)ws.kimg, (const E *)nullptr, (const float *)nullptr,
+                               p.S0, (TIn *)p.out, p.ST);
+        } else {
+            const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<TIn, DK, NL, false, 2>::NCOL));
+            hipLaunchKernelGGL((scan_split_kernel<TIn, DK, DV, NL, false, 2>), dim3(blocks), dim3(64 * (2 + 2 + NL)),
+                               0, s, p.T, p.Hk, p.Hv, NC, p.v, ws.tok, (const E *)ws.apair, (const E *)ws.qpair,
+                               (const E *)ws.qimg, (const E *)ws.kimg, (const E *)nullptr, (const float *)nullptr,
+                               p.S0, (TIn *)p.out, p.ST);
+        }
         return hipGetLastError();
     } else {
         constexpr int NW = 2, NL = 2;
@@ -999,8 +1030,8 @@ template <int DK, int DV>
 static hipError_t launch_scan2_t(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s) {
     constexpr int NL = 2;
     const int NC = (p.T + C - 1) / C;
-    const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<bf16_t, DK, NL, true>::NCOL));
-    hipLaunchKernelGGL((scan_split_kernel<bf16_t, DK, DV, NL, true>), dim3(blocks), dim3(64 * (4 + NL)), 0, s,
+    const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<bf16_t, DK, NL, true, 2>::NCOL));
+    hipLaunchKernelGGL((scan_split_kernel<bf16_t, DK, DV, NL, true, 2>), dim3(blocks), dim3(64 * (2 + 2 + NL)), 0, s,
                        p.T, p.Hk, p.Hv, NC, (const void *)ws.z, (const float *)nullptr,
                        (const _Float16 *)ws.apair, (const _Float16 *)ws.qpair, (const _Float16 *)ws.qimg,
                        (const _Float16 *)ws.eimg, (const _Float16 *)ws.khimg, ws.gc, p.S0, (bf16_t *)p.out, p.ST);

@@ -180,6 +180,22 @@ def test_bf16_slow_decay_reported():
                        init_state=True, **SLOW_DECAY))
 
 
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_many_heads_four_column_tiles(Dk, Dv):
+    """More (sequence, value head, 32-column) units than CUs: the scan then gives each
+    work-group 64 state columns (four state waves).  Ragged T, initial state, every head."""
+    spec = GDNSpec(B=3, T=130, Hk=4, Hv=64, Dk=Dk, Dv=Dv, dtype="bf16", seed=360 + Dk + Dv, init_state=True)
+    log(f"[prefill 64-column work-groups] {spec}")
+    inp = synth.make_inputs(spec)
+    out, ST = gpu_prefill(spec, inp)
+    o_ref, s_ref = oracle_prefill(inp)
+    so, ss = Stats(), Stats()
+    accumulate_out(so, out, o_ref, bf16=True)
+    accumulate_state(ss, ST, s_ref)
+    check_stats("out", so, **BF16_BOUNDS, rounded_tol=BF16_ROUNDED_TOL)
+    check_stats("final_state", ss, TOL["bf16"], head_tol=TOL["bf16"])
+
+
 def test_qwen_shaped_prefill_t4096():
     """B=1, T=4096, 16 key / 64 value heads, d=128, bf16, zero state: the timed workload.
     The oracle over every head and token; whole-tensor, per-head and per-chunk errors."""
