@@ -21,6 +21,8 @@
 //     the operand fragments of the two matrices the scan applies to its
 //     residual (A and A_qk with the per-token factors folded in) plus the
 //     per-token decay record.
+#include <utility>
+
 #include "prefill_common.h"
 
 namespace gdn {
@@ -50,6 +52,23 @@ size_t prefill_workspace_layout(int B, int T, int Hk, int Hv, int Dk, bool f32, 
         ws->bytes = off;
     }
     return off;
+}
+
+// One step j of the column-oriented forward substitution in a 16-lane row:
+// x[r] += (-L[r][j]) x[j] for r > j, where lane j of the row holds -L[r][j] in
+// nl[r] (DPP row_newbcast:j broadcasts it to the whole row).
+template <int J>
+__device__ __forceinline__ void subst_step(const float (&nl)[16], float (&x)[16]) {
+#pragma unroll
+    for (int r = J + 1; r < 16; ++r) {
+        const float lrj = __builtin_bit_cast(
+            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, nl[r]), 0x150 + J, 0xf, 0xf, true));
+        x[r] = fmaf(lrj, x[J], x[r]);
+    }
+}
+template <int... J>
+__device__ __forceinline__ void subst_steps(const float (&nl)[16], float (&x)[16], std::integer_sequence<int, J...>) {
+    (subst_step<J>(nl, x), ...);
 }
 
 // Logical column of physical position p (inverse of perm_col).
@@ -282,18 +301,22 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
         }
         wave_lds_sync();
 
-        // diagonal blocks of X: lane (block bq, column c) by forward substitution
+        // diagonal blocks of X: lane (block bq, column c) by forward substitution,
+        // column-oriented: with x = column c of X (x[r] = delta_rc to start),
+        // for j = 0..14, x[r] -= L[r][j] x[j] for r > j.  Each lane keeps column
+        // c of -L in registers; L[r][j] comes from lane j of the same 16-lane
+        // row (the block) by a DPP row broadcast, so the inner step is a vector
+        // multiply-add with no LDS access.
         {
             const int bq = lane >> 4, c = lane & 15;
             const float *Lb = Ld(bq);
-            float x[16];
+            float nl[16], x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float s = (r == c) ? 1.f : 0.f;
-#pragma unroll
-                for (int jj = 0; jj < r; ++jj) s -= Lb[r * 16 + jj] * x[jj];
-                x[r] = s;
+                nl[r] = -Lb[r * 16 + c];
+                x[r] = (r == c) ? 1.f : 0.f;
             }
+            subst_steps(nl, x, std::make_integer_sequence<int, 15>());
 #pragma unroll
             for (int r = 0; r < 16; ++r) Xw[tri_index(bq, bq) * 256 + r * 16 + c] = x[r];
         }
