@@ -247,9 +247,10 @@ def gdn_chunk_fwd_noalloc(q, k, v, a, b, A_log, dt_bias, initial_state=None, *, 
 def gdn2_chunk_fwd(q, k, v, a, A_log, erase, write, initial_state=None, *, scale: float = 1.0,
                    out=None, final_state=None, output_final_state: bool = True, workspace=None,
                    stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Gated DeltaNet-2 chunked prefill (bfloat16).  q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv];
-    a, erase [B,T,Hv,Dk]; write [B,T,Hv,Dv]; A_log [Hv,Dk] fp32; initial_state
-    [B,Hv,Dk,Dv] fp32 or None.  Returns (out [B,T,Hv,Dv], final_state or None)."""
+    """Gated DeltaNet-2 chunked prefill, bfloat16 or float32 (q's dtype).  q, k [B,T,Hk,Dk];
+    v [B,T,Hv,Dv]; a, erase [B,T,Hv,Dk]; write [B,T,Hv,Dv] (all in q's dtype); A_log
+    [Hv,Dk] fp32; initial_state [B,Hv,Dk,Dv] fp32 or None.  Returns (out [B,T,Hv,Dv] in
+    q's dtype, final_state or None)."""
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     dims = make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, scale)

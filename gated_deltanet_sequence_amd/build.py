@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["api.hip", "decode.hip", "chunk_local.hip", "chunk_local2.hip", "state_scan.hip", "epilogue.hip", "prologue.hip", "bwd2.hip"]
+SOURCES = ["api.hip", "decode.hip", "chunk_local.hip", "chunk_local2.hip", "chunk_local2_f32.hip", "state_scan.hip", "epilogue.hip", "prologue.hip", "bwd2.hip"]
 ARCH = "gfx950"
 
 

@@ -266,9 +266,9 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_dims *d, const void *q, const void *k
 }
 
 size_t gdn2_chunk_fwd_workspace_bytes(const gdn_dims *d) {
-    if (check_dims(d, true) != GDN_OK || d->dtype != GDN_BF16) return 0;
+    if (check_dims(d, true) != GDN_OK) return 0;
     if (d->B == 0 || d->T == 0) return 0;
-    return gdn::gdn2_workspace_layout(d->B, d->T, d->Hv, d->Dk, d->Dv, nullptr, nullptr);
+    return gdn::gdn2_workspace_layout(d->B, d->T, d->Hv, d->Dk, d->Dv, d->dtype == GDN_F32, nullptr, nullptr);
 }
 
 gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const void *v, const void *a,
@@ -277,8 +277,7 @@ gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const
                           size_t workspace_bytes, void *stream) {
     gdn_status st = check_dims(d, true);
     if (st != GDN_OK) return st;
-    if (d->dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "gdn2_chunk_fwd: dtype must be GDN_BF16");
-    const size_t B = d->B, T = d->T, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv, es = 2;
+    const size_t B = d->B, T = d->T, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv, es = esize(d);
     const Span sq{"q", q, B * T * Hk * Dk * es}, sk{"k", k, B * T * Hk * Dk * es};
     const Span sv{"v", v, B * T * Hv * Dv * es};
     const Span sa{"a", a, B * T * Hv * Dk * es}, se{"erase", erase, B * T * Hv * Dk * es};
@@ -320,11 +319,12 @@ gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const
     }
     gdn::Gdn2Args p;
     p.B = d->B; p.T = d->T; p.Hk = d->Hk; p.Hv = d->Hv; p.Dk = d->Dk; p.Dv = d->Dv;
+    p.f32 = d->dtype == GDN_F32;
     p.scale = d->scale;
     p.q = q; p.k = k; p.v = v; p.a = a; p.erase = erase; p.write = write; p.A_log = A_log;
     p.S0 = initial_state; p.out = out; p.ST = final_state;
     gdn::Gdn2Workspace ws;
-    gdn::gdn2_workspace_layout(d->B, d->T, d->Hv, d->Dk, d->Dv, workspace, &ws);
+    gdn::gdn2_workspace_layout(d->B, d->T, d->Hv, d->Dk, d->Dv, p.f32, workspace, &ws);
     e = gdn::launch_chunk_local2(p, ws, hs);
     if (e == hipSuccess) e = gdn::launch_state_scan2(p, ws, hs);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch: %s", hipGetErrorString(e));

@@ -54,23 +54,6 @@ size_t prefill_workspace_layout(int B, int T, int Hk, int Hv, int Dk, bool f32, 
     return off;
 }
 
-// One step j of the column-oriented forward substitution in a 16-lane row:
-// x[r] += (-L[r][j]) x[j] for r > j, where lane j of the row holds -L[r][j] in
-// nl[r] (DPP row_newbcast:j broadcasts it to the whole row).
-template <int J>
-__device__ __forceinline__ void subst_step(const float (&nl)[16], float (&x)[16]) {
-#pragma unroll
-    for (int r = J + 1; r < 16; ++r) {
-        const float lrj = __builtin_bit_cast(
-            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, nl[r]), 0x150 + J, 0xf, 0xf, true));
-        x[r] = fmaf(lrj, x[J], x[r]);
-    }
-}
-template <int... J>
-__device__ __forceinline__ void subst_steps(const float (&nl)[16], float (&x)[16], std::integer_sequence<int, J...>) {
-    (subst_step<J>(nl, x), ...);
-}
-
 // Logical column of physical position p (inverse of perm_col).
 template <bool F32>
 __device__ __forceinline__ int unperm_col(int p) {

@@ -34,22 +34,25 @@
 
 namespace gdn {
 
-size_t gdn2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, Gdn2Workspace *ws) {
+size_t gdn2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, bool f32, void *base, Gdn2Workspace *ws) {
     const size_t NC = (size_t)(T + C - 1) / C;
     const size_t vunits = (size_t)B * Hv * NC;
+    const size_t esz = f32 ? 4 : 2;
     size_t off = 0;
-    const size_t oE = off;  off = align256(off + vunits * C * Dk * 2);
-    const size_t oKh = off; off = align256(off + vunits * C * Dk * 2);
-    const size_t oQ = off;  off = align256(off + vunits * C * Dk * 2);
-    const size_t oA = off;  off = align256(off + vunits * NPAIR * 64 * 8 * 2);
-    const size_t oAq = off; off = align256(off + vunits * NPAIR * 64 * 8 * 2);
+    const size_t oE = off;  off = align256(off + vunits * C * Dk * esz);
+    const size_t oKh = off; off = align256(off + vunits * C * Dk * esz);
+    const size_t oQ = off;  off = align256(off + vunits * C * Dk * esz);
+    const size_t oKt = off; off = align256(off + (f32 ? vunits * C * Dk * esz : 0));
+    const size_t oA = off;  off = align256(off + vunits * NPAIR * 64 * 8 * esz);
+    const size_t oAq = off; off = align256(off + vunits * NPAIR * 64 * 8 * esz);
     const size_t oG = off;  off = align256(off + vunits * Dk * 4);
-    const size_t oZ = off;  off = align256(off + (size_t)B * T * Hv * Dv * 2);
+    const size_t oZ = off;  off = align256(off + (size_t)B * T * Hv * Dv * esz);
     if (ws) {
         char *p = (char *)base;
         ws->eimg = p + oE;
         ws->khimg = p + oKh;
         ws->qimg = p + oQ;
+        ws->khtimg = f32 ? p + oKt : nullptr;
         ws->apair = p + oA;
         ws->qpair = p + oAq;
         ws->gc = (float *)(p + oG);
@@ -434,6 +437,7 @@ static hipError_t launch_cl2_t(const Gdn2Args &p, const Gdn2Workspace &ws, hipSt
 }
 
 hipError_t launch_chunk_local2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s) {
+    if (p.f32) return launch_chunk_local2_f32(p, ws, s);
     if (p.Dk == 128 && p.Dv == 128) return launch_cl2_t<128, 128>(p, ws, s);
     if (p.Dk == 128 && p.Dv == 64) return launch_cl2_t<128, 64>(p, ws, s);
     if (p.Dk == 64 && p.Dv == 128) return launch_cl2_t<64, 128>(p, ws, s);

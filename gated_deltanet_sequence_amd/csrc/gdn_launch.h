@@ -41,23 +41,27 @@ hipError_t launch_state_copy(const PrefillArgs &p, hipStream_t s);  // T == 0: S
 // Workspace of the Gated DeltaNet-2 chunked prefill (bfloat16 inputs, float16
 // operands), per (sequence, value head, chunk) unit; every region 256-byte
 // aligned.  G is the in-chunk inclusive prefix of the channel-wise log decay.
+// Element type E: float16 for bfloat16 inputs, float32 for float32 inputs.
 struct Gdn2Workspace {
-    void *eimg;    // [B*Hv*NC][64][Dk] f16 image: (sigmoid(erase) . k) . e^{G}
-    void *khimg;   // [B*Hv*NC][64][Dk] f16 image: k . e^{G_C - G}
-    void *qimg;    // [B*Hv*NC][64][Dk] f16 image: scale q . e^{G}
-    void *apair;   // [B*Hv*NC][6][64 lanes][8] f16: A = (I + M)^{-1} operand fragments
-    void *qpair;   // [B*Hv*NC][6][64 lanes][8] f16: A_qk A operand fragments
+    void *eimg;    // [B*Hv*NC][64][Dk] E image: (sigmoid(erase) . k) . e^{G}
+    void *khimg;   // [B*Hv*NC][64][Dk] E image: k . e^{G_C - G}
+    void *qimg;    // [B*Hv*NC][64][Dk] E image: scale q . e^{G}
+    void *khtimg;  // [B*Hv*NC][Dk][64] f32 image of Kh^T (float32 only; the float16
+                   // scan reads Kh^T operands from the Kh image with transposed LDS reads)
+    void *apair;   // [B*Hv*NC][6][64 lanes][8] E: A = (I + M)^{-1} operand fragments
+    void *qpair;   // [B*Hv*NC][6][64 lanes][8] E: A_qk A operand fragments
     float *gc;     // [B*Hv*NC][Dk] f32: e^{G_C} per key channel
-    void *z;       // [B,T,Hv,Dv] f16: sigmoid(write) . v
+    void *z;       // [B,T,Hv,Dv] E: sigmoid(write) . v
     size_t bytes;  // total
 };
 
-size_t gdn2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, Gdn2Workspace *ws);
+size_t gdn2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, bool f32, void *base, Gdn2Workspace *ws);
 
 struct Gdn2Args {
     int B, T, Hk, Hv, Dk, Dv;
+    bool f32;
     float scale;
-    const void *q, *k, *v, *a, *erase, *write;  // bfloat16
+    const void *q, *k, *v, *a, *erase, *write;  // bfloat16 or float32
     const float *A_log;                          // [Hv][Dk]
     const float *S0;
     void *out;
@@ -65,6 +69,7 @@ struct Gdn2Args {
 };
 
 hipError_t launch_chunk_local2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s);
+hipError_t launch_chunk_local2_f32(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s);
 hipError_t launch_state_scan2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s);
 
 // Gradient of the Gated DeltaNet-2 chunked forward (bwd2.hip).  Float32

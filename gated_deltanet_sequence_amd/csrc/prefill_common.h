@@ -18,6 +18,8 @@
 // 1/gamma, so nothing overflows however strong the decay.
 #pragma once
 
+#include <utility>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -93,6 +95,23 @@ __device__ __forceinline__ void img_pair(const typename mma<F32>::E *X, int rowl
 
 // Lower-triangular 16x16 tiles (rt >= ct) of a 64x64 matrix, numbered 0..9.
 __host__ __device__ constexpr int tri_index(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }
+
+// One step j of the column-oriented forward substitution in a 16-lane row:
+// x[r] += (-L[r][j]) x[j] for r > j, where lane j of the row holds -L[r][j] in
+// nl[r] (DPP row_newbcast:j broadcasts it to the whole row).
+template <int J>
+__device__ __forceinline__ void subst_step(const float (&nl)[16], float (&x)[16]) {
+#pragma unroll
+    for (int r = J + 1; r < 16; ++r) {
+        const float lrj = __builtin_bit_cast(
+            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, nl[r]), 0x150 + J, 0xf, 0xf, true));
+        x[r] = fmaf(lrj, x[J], x[r]);
+    }
+}
+template <int... J>
+__device__ __forceinline__ void subst_steps(const float (&nl)[16], float (&x)[16], std::integer_sequence<int, J...>) {
+    (subst_step<J>(nl, x), ...);
+}
 
 // Off-diagonal blocks of X = (I + L)^{-1}, 16x16 blocks, diagonal blocks already
 // in Xw:  X[i][j] = -X[i][i] sum_{mb=j}^{i-1} L[i][mb] X[mb][j], one column block

@@ -91,7 +91,11 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <bool F32, typename TIn, int DK, int DV, int NW, int NL>
+// G2: the channel-wise decay (Gated DeltaNet-2, float32): the images are the
+// per-value-head Qt, Et and Kh^T, V is Z, the fragments are A and Aq A, and
+// the per-chunk record is e^{G_C} per key channel: R' = Z - Et S,
+// O = Qt S + (Aq A) R', S = diag(e^{G_C}) S + Kh^T (A R').
+template <bool F32, typename TIn, int DK, int DV, int NW, int NL, bool G2 = false>
 __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
     int T, int Hk, int Hv, int NC, const TIn *__restrict__ v,
     const float *__restrict__ tok, const typename mma<F32>::E *__restrict__ apair,
@@ -101,7 +105,10 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
     typedef ScanCfg<F32, TIn, DK, NW, NL> CF;
     typedef typename mma<F32>::E E;
     typedef typename mma<F32>::V4 V4;
+    static_assert(!G2 || F32, "the channel-wise decay runs here in float32 only");
     constexpr int NCOL = CF::NCOL;
+    constexpr int TKB = G2 ? DK * 4 : C * 8;  // per-chunk record bytes
+    static_assert(TKB <= C * 16 && TKB % 16 == 0, "record slot");
     constexpr int NKB = DK / 16;
     constexpr int NCG = DV / NCOL;
 
@@ -131,12 +138,13 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
         const __amdgpu_buffer_rsrc_t vres = rsrc(v + (size_t)bb * seq_elems, seq_elems * sizeof(TIn));
         const __amdgpu_buffer_rsrc_t ores = rsrc(out + (size_t)bb * seq_elems, seq_elems * sizeof(TIn));
         const size_t ku0 = ((size_t)bb * Hk + hk) * NC, vu0 = ((size_t)bb * Hv + hv) * NC;
-        const __amdgpu_buffer_rsrc_t rq = rsrc(qimg + ku0 * C * DK, (size_t)NC * CF::IMG_BYTES);
-        const __amdgpu_buffer_rsrc_t rk = rsrc(kimg + ku0 * C * DK, (size_t)NC * CF::IMG_BYTES);
-        const __amdgpu_buffer_rsrc_t rt = rsrc(timg + ku0 * C * DK, (size_t)NC * CF::IMG_BYTES);
+        const size_t iu0 = G2 ? vu0 : ku0;  // images per value head (channel-wise decay) or per key head
+        const __amdgpu_buffer_rsrc_t rq = rsrc(qimg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
+        const __amdgpu_buffer_rsrc_t rk = rsrc(kimg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
+        const __amdgpu_buffer_rsrc_t rt = rsrc(timg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
         const __amdgpu_buffer_rsrc_t ra = rsrc(apair + vu0 * (NPAIR * 64 * 8), (size_t)NC * CF::FRAG_BYTES);
         const __amdgpu_buffer_rsrc_t rf = rsrc(qpair + vu0 * (NPAIR * 64 * 8), (size_t)NC * CF::FRAG_BYTES);
-        const __amdgpu_buffer_rsrc_t rtk = rsrc(tok + vu0 * C * 2, (size_t)NC * C * 8);
+        const __amdgpu_buffer_rsrc_t rtk = rsrc(tok + vu0 * (TKB / 4), (size_t)NC * TKB);
         const int lane16 = lane * 16;
         // 16-byte slot of this lane in tile unit u: row, swizzled piece, element offset
         auto tile_slot = [&](int u, int &row, int &piece) {
@@ -171,8 +179,8 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void_t *)(base + CF::OFF_V + u * 1024), 16,
                                                          voff * (int)sizeof(TIn), 0, 0, 0);
             }
-            if (l == 0 && lane < 32)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rtk, (lds_void_t *)(base + CF::OFF_TK), 16, lane16, n * C * 8, 0, 0);
+            if (l == 0 && lane < TKB / 16)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rtk, (lds_void_t *)(base + CF::OFF_TK), 16, lane16, n * TKB, 0, 0);
         };
         // write chunk n's output rows from LDS output tile (n & 1), 16 bytes per lane
         auto store_rows = [&](int n) {
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
         f4 ga[4], vv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            ga[r] = tokq(0, r);
+            ga[r] = G2 ? f4{1, 1, 1, 1} : tokq(0, r);
 #pragma unroll
             for (int i = 0; i < 4; ++i) vv[r][i] = lds_in(Vs + tile_index(16 * r + 4 * g + i));
         }
@@ -296,10 +304,10 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
             ld_pair<F32>(Qf + p * 512, qfr[p][0], qfr[p][1]);
         }
 
-        // ---- R' = V - gamma P
+        // ---- R' = V - gamma P  (channel-wise decay: Z - Et S, the decay is in the image)
         V4 Rb[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Rb[r] = mma<F32>::from_f4(vv[r] - ga[r] * P[r]);
+        for (int r = 0; r < 4; ++r) Rb[r] = mma<F32>::from_f4(G2 ? vv[r] - P[r] : vv[r] - ga[r] * P[r]);
 
         // ---- eta Delta = Ae R'
         V4 De[4];
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
         //      scale is already folded into Q and Ao)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            f4 acc = ga[r] * Qa[r];
+            f4 acc = G2 ? Qa[r] : ga[r] * Qa[r];
 #pragma unroll
             for (int qq = 0; qq <= r / 2; ++qq) {
                 const int p = pair_index(r, qq);
@@ -335,11 +343,11 @@ __global__ __launch_bounds__(64 * (NW + NL)) void state_scan_kernel(
             for (int i = 0; i < 4; ++i) lds_out(Os + tile_index(16 * r + 4 * g + i), acc[i]);
         }
 
-        // ---- S = gamma_C S + K^T (eta Delta)
+        // ---- S = gamma_C S + K^T (eta Delta)  (channel-wise: e^{G_C} of row 16 kb + 4 g + i)
         const float gC = Tq[C - 1];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            f4 acc = gC * S[kb];
+            f4 acc = G2 ? *reinterpret_cast<const f4 *>(Tq + 16 * kb + 4 * g) * S[kb] : gC * S[kb];
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) acc = mma<F32>::pair(acc, tf[kb][qq][0], tf[kb][qq][1], De[2 * qq], De[2 * qq + 1]);
             S[kb] = acc;
@@ -1038,7 +1046,27 @@ static hipError_t launch_scan2_t(const Gdn2Args &p, const Gdn2Workspace &ws, hip
     return hipGetLastError();
 }
 
+// float32 inputs: the float32 scan with the channel-wise decay
+template <int DK, int DV>
+static hipError_t launch_scan2_f32_t(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s) {
+    constexpr int NW = 2, NL = 2;
+    const int NC = (p.T + C - 1) / C;
+    const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / (16 * NW)));
+    hipLaunchKernelGGL((state_scan_kernel<true, float, DK, DV, NW, NL, true>), dim3(blocks), dim3(64 * (NW + NL)), 0, s,
+                       p.T, p.Hk, p.Hv, NC, (const float *)ws.z, ws.gc, (const float *)ws.apair,
+                       (const float *)ws.qpair, (const float *)ws.qimg, (const float *)ws.eimg,
+                       (const float *)ws.khtimg, p.S0, (float *)p.out, p.ST);
+    return hipGetLastError();
+}
+
 hipError_t launch_state_scan2(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s) {
+    if (p.f32) {
+        if (p.Dk == 128 && p.Dv == 128) return launch_scan2_f32_t<128, 128>(p, ws, s);
+        if (p.Dk == 128 && p.Dv == 64) return launch_scan2_f32_t<128, 64>(p, ws, s);
+        if (p.Dk == 64 && p.Dv == 128) return launch_scan2_f32_t<64, 128>(p, ws, s);
+        if (p.Dk == 64 && p.Dv == 64) return launch_scan2_f32_t<64, 64>(p, ws, s);
+        return hipErrorInvalidValue;
+    }
     if (p.Dk == 128 && p.Dv == 128) return launch_scan2_t<128, 128>(p, ws, s);
     if (p.Dk == 128 && p.Dv == 64) return launch_scan2_t<128, 64>(p, ws, s);
     if (p.Dk == 64 && p.Dv == 128) return launch_scan2_t<64, 128>(p, ws, s);

@@ -151,19 +151,21 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_dims *d, const void *q, const void *k
  * channel): D = exp(-exp(A_log[h][c]) * softplus(a)), b = sigmoid(erase),
  * w = sigmoid(write).  With D_t = alpha_t I and both gates equal to beta_t it
  * is the rule of gdn_chunk_fwd.
- *   q, k          [B,T,Hk,Dk] bfloat16
- *   v             [B,T,Hv,Dv] bfloat16
- *   a, erase      [B,T,Hv,Dk] bfloat16 decay and erase-gate logits
- *   write         [B,T,Hv,Dv] bfloat16 write-gate logits
+ *   q, k          [B,T,Hk,Dk] in d->dtype
+ *   v             [B,T,Hv,Dv] in d->dtype
+ *   a, erase      [B,T,Hv,Dk] in d->dtype: decay and erase-gate logits
+ *   write         [B,T,Hv,Dv] in d->dtype: write-gate logits
  *   A_log         [Hv,Dk] float32
  *   initial_state [B,Hv,Dk,Dv] float32, or NULL for a zero state
- *   out           [B,T,Hv,Dv] bfloat16 (written)
+ *   out           [B,T,Hv,Dv] in d->dtype (written)
  *   final_state   [B,Hv,Dk,Dv] float32 (written), or NULL; may be exactly
  *                 initial_state
  *   workspace     device scratch of at least gdn2_chunk_fwd_workspace_bytes(d)
  *                 bytes, 256-byte aligned.
- * d->dtype must be GDN_BF16 (GDN_ERR_UNSUPPORTED otherwise).  Same aliasing
- * rules and limits as gdn_chunk_fwd. */
+ * d->dtype GDN_BF16: float16 matrix-core operands, float32 state and
+ * accumulation (the input-scale domain of gdn_chunk_fwd applies).  GDN_F32:
+ * float32 throughout, each in-chunk decay ratio from a float64 prefix.  Same
+ * aliasing rules and limits as gdn_chunk_fwd. */
 size_t gdn2_chunk_fwd_workspace_bytes(const gdn_dims *d);
 gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const void *v,
                           const void *a, const float *A_log, const void *erase, const void *write,

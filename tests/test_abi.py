@@ -317,18 +317,26 @@ def test_gdn2_workspace_bytes():
     # chunk-end decay per key channel; plus Z [B,T,Hv,Dv] float16
     need = units * (3 * 64 * 128 * 2 + 2 * 6 * 64 * 8 * 2 + 128 * 4) + 8192 * 64 * 128 * 2
     assert need <= n < need + 8 * 256
-    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims(dtype=binding.GDN_F32))) == 0
+    # float32: the same arrays in float32, plus the 128 x 64 float32 image of Kh^T per unit
+    n32 = L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims(B=1, T=8192, Hk=16, Hv=64, Dk=128, Dv=128,
+                                                             dtype=binding.GDN_F32)))
+    need32 = units * (4 * 64 * 128 * 4 + 2 * 6 * 64 * 8 * 4 + 128 * 4) + 8192 * 64 * 128 * 4
+    assert need32 <= n32 < need32 + 9 * 256
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims(Hv=3))) == 0
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims(T=0))) == 0
     assert L.gdn2_chunk_fwd_workspace_bytes(None) == 0
 
 
-def test_gdn2_rejects_float32():
+def test_gdn2_float32_checks_its_own_workspace_size():
+    """A float32 call needs the float32 workspace: the bfloat16 size is refused before
+    anything is enqueued."""
     buf = Buf()
-    d = dims()
-    a = gdn2_args(buf, d)
-    assert call_gdn2(dims(dtype=binding.GDN_F32), a) == ERR_UNSUPPORTED
-    assert "BF16" in last_error()
+    a = gdn2_args(buf, dims())
+    d32 = dims(dtype=binding.GDN_F32)
+    need32 = binding.lib().gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d32))
+    assert need32 > a["ws_bytes"]
+    assert call_gdn2(d32, a) == ERR_WORKSPACE
+    assert "needed" in last_error()
 
 
 @pytest.mark.parametrize("kw,code", [(dict(Hv=3), ERR_SHAPE), (dict(Dk=96), ERR_UNSUPPORTED),
