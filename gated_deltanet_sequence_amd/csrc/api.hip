@@ -332,7 +332,7 @@ gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const
 }
 
 size_t gdn2_chunk_bwd_workspace_bytes(const gdn_dims *d) {
-    if (check_dims(d, true) != GDN_OK || d->dtype != GDN_BF16) return 0;
+    if (check_dims(d, true) != GDN_OK) return 0;
     if (d->B == 0 || d->T == 0) return 0;
     return gdn::bwd2_workspace_layout(d->B, d->T, d->Hv, d->Dk, d->Dv, nullptr, nullptr);
 }
@@ -345,8 +345,7 @@ gdn_status gdn2_chunk_bwd_timed(const gdn_dims *d, const void *q, const void *k,
                                 size_t workspace_bytes, void *stream, void *const *stage_events) {
     gdn_status st = check_dims(d, true);
     if (st != GDN_OK) return st;
-    if (d->dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "gdn2_chunk_bwd: dtype must be GDN_BF16");
-    const size_t B = d->B, T = d->T, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv, es = 2;
+    const size_t B = d->B, T = d->T, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv, es = esize(d);
     const Span sq{"q", q, B * T * Hk * Dk * es}, sk{"k", k, B * T * Hk * Dk * es};
     const Span sv{"v", v, B * T * Hv * Dv * es};
     const Span sa{"a", a, B * T * Hv * Dk * es}, se{"erase", erase, B * T * Hv * Dk * es};
@@ -384,7 +383,7 @@ gdn_status gdn2_chunk_bwd_timed(const gdn_dims *d, const void *q, const void *k,
     ok();
     gdn::Bwd2Args p{};
     p.B = d->B; p.T = d->T; p.Hk = d->Hk; p.Hv = d->Hv; p.Dk = d->Dk; p.Dv = d->Dv;
-    p.NC = (d->T + 63) / 64; p.scale = d->scale;
+    p.NC = (d->T + 63) / 64; p.scale = d->scale; p.f32 = d->dtype == GDN_F32;
     p.q = q; p.k = k; p.v = v; p.a = a; p.erase = erase; p.write = write; p.A_log = A_log;
     p.S0 = initial_state; p.dout = d_out; p.dST = d_final_state;
     p.dq = dq; p.dk = dk; p.dv = dv; p.da = da; p.derase = d_erase; p.dwrite = d_write;

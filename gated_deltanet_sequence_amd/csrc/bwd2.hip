@@ -22,7 +22,8 @@
 //   dG_t += e_t de^M_t + qs_t dqs^A_t - k_t dk^P_t  (+ the image terms),
 // then dg = reverse in-chunk prefix of dG, and the gates' own derivatives.
 //
-// Every quantity is float32.  The work is split over six launches:
+// Every quantity is float32 (the inputs are bfloat16 or float32).  The work is
+// split over six launches:
 //   g2b_prep       per chunk: gates, images, M and Aq, A = (I + M)^{-1}
 //   g2b_fwd_scan   per (sequence, head, 32 value columns): S_n, R, U over the chunks
 //   g2b_bwd_scan   the same slices in reverse: dS_{n+1}, dU, dR; dS_0
@@ -83,6 +84,28 @@ __device__ __forceinline__ void bf8_to_f32(const u16x8 x, f4 &lo, f4 &hi) {
     }
 }
 
+// 8 consecutive input elements (bfloat16 or float32) held in registers between
+// their load and their conversion to float32.
+template <typename TIn> struct In8;
+template <> struct In8<bf16_t> {
+    u16x8 x;
+    __device__ __forceinline__ void load(const bf16_t *p, size_t i) {
+        x = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(p) + i);
+    }
+    __device__ __forceinline__ void get(f4 &lo, f4 &hi) const { bf8_to_f32(x, lo, hi); }
+};
+template <> struct In8<float> {
+    f4 lo_, hi_;
+    __device__ __forceinline__ void load(const float *p, size_t i) {
+        lo_ = *reinterpret_cast<const f4 *>(p + i);
+        hi_ = *reinterpret_cast<const f4 *>(p + i + 4);
+    }
+    __device__ __forceinline__ void get(f4 &lo, f4 &hi) const {
+        lo = lo_;
+        hi = hi_;
+    }
+};
+
 // A ROWS x COLS float32 tile (row-major, contiguous) held in registers between
 // its global load and its LDS store: the scans load the next chunk's operands
 // while computing the current one.
@@ -113,7 +136,7 @@ __device__ __forceinline__ size_t unit_of(int bb, int hv, int n, int Hv, int NC)
 // ---------------------------------------------------------------------------
 // g2b_prep: one work-group of 4 waves per (sequence, value head, chunk)
 // ---------------------------------------------------------------------------
-template <int DK, int DV>
+template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     constexpr int LS = DK + 4;  // conflict-free for lanes (row = l%16, col = l/16)
     __shared__ __attribute__((aligned(16))) float sm[4 * C * LS + C];
@@ -124,7 +147,7 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv), hk = hv / (p.Hv / p.Hk);
     const int t0 = n * C, L = min(C, p.T - t0);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4;
-    const uint16_t *v = reinterpret_cast<const uint16_t *>(p.v), *wr = reinterpret_cast<const uint16_t *>(p.write);
+    const TIn *v = static_cast<const TIn *>(p.v), *wr = static_cast<const TIn *>(p.write);
 
     // 1. gates: G (log2 units, 0 past T), e = sigmoid(erase) k, qs = scale q, k; z to the workspace.
     //    Thread = (4 channels, a group of RPT consecutive rows); rows past T read the last
@@ -134,8 +157,8 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     constexpr int NQ = DK / 4, NRG = 256 / NQ, RPT = C / NRG;
     __shared__ float tot[NRG * DK];
     {
-        const bf16_t *qb = reinterpret_cast<const bf16_t *>(p.q), *kb = reinterpret_cast<const bf16_t *>(p.k);
-        const bf16_t *ab = reinterpret_cast<const bf16_t *>(p.a), *eb = reinterpret_cast<const bf16_t *>(p.erase);
+        const TIn *qb = static_cast<const TIn *>(p.q), *kb = static_cast<const TIn *>(p.k);
+        const TIn *ab = static_cast<const TIn *>(p.a), *eb = static_cast<const TIn *>(p.erase);
         const int c = (tid % NQ) * 4, rg = tid / NQ;
         const f4 al = *reinterpret_cast<const f4 *>(p.A_log + (size_t)hv * DK + c);
         f4 rate;
@@ -175,8 +198,11 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
         const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
         const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
         f4 vl, vh, wl, wh;
-        bf8_to_f32(*reinterpret_cast<const u16x8 *>(v + kv), vl, vh);
-        bf8_to_f32(*reinterpret_cast<const u16x8 *>(wr + kv), wl, wh);
+        In8<TIn> xv, xw;
+        xv.load(v, kv);
+        xw.load(wr, kv);
+        xv.get(vl, vh);
+        xw.get(wl, wh);
         const float on = t < L ? 1.f : 0.f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -434,7 +460,7 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
 // ---------------------------------------------------------------------------
 // g2b_bwd_scan: the same slices, chunks in reverse; dS in MFMA accumulators.
 // ---------------------------------------------------------------------------
-template <int DK, int DV>
+template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws) {
     constexpr int LQ = 80, LKA = DK + 4, LKB = DK + 16, LB = 48, NS = DV / 32, NT = DK / 32;
     // bA: A_qk, then A; bK1: Kh (stride LKA), then -Et (stride LKB); bK2: Qt
@@ -442,7 +468,7 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
         dSs[DK * LB], dUs[C * LB], dRs[C * LB];
     const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
-    const uint16_t *dout = reinterpret_cast<const uint16_t *>(p.dout);
+    const TIn *dout = static_cast<const TIn *>(p.dout);
     f4 dS[NT];
 #pragma unroll
     for (int x = 0; x < NT; ++x) {
@@ -459,12 +485,14 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
     const int ot = tid >> 2, oj = (tid & 3) * 8;
     auto load_do = [&](int n) {
         const int L = min(C, p.T - n * C), tl = min(ot, L - 1);
-        return *reinterpret_cast<const u16x8 *>(dout + (((size_t)bb * p.T + n * C + tl) * p.Hv + hv) * DV + j0 + oj);
+        In8<TIn> x;
+        x.load(dout, (((size_t)bb * p.T + n * C + tl) * p.Hv + hv) * DV + j0 + oj);
+        return x;
     };
-    auto store_do = [&](const u16x8 x, int n) {
+    auto store_do = [&](const In8<TIn> &x, int n) {
         const int L = min(C, p.T - n * C);
         f4 lo, hi;
-        bf8_to_f32(x, lo, hi);
+        x.get(lo, hi);
         const float on = ot < L ? 1.f : 0.f;
         *reinterpret_cast<f4 *>(Os + ot * LB + oj) = lo * on;
         *reinterpret_cast<f4 *>(Os + ot * LB + oj + 4) = hi * on;
@@ -472,7 +500,7 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
     // staged for the chunk about to run: A_qk in bA, Kh in bK1, dO in Os
     RegTile<C, C> rAq, rA;
     RegTile<C, DK> rKh, rQ, rE;
-    u16x8 rdo;
+    In8<TIn> rdo;
     {
         const size_t u = unit_of(bb, hv, NC - 1, p.Hv, NC);
         rAq.load(ws.Aq + u * C * C);
@@ -576,7 +604,7 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
 // ---------------------------------------------------------------------------
 // g2b_products: one work-group per chunk.  Wave w owns the rows of block w.
 // ---------------------------------------------------------------------------
-template <int DK, int DV>
+template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws) {
     constexpr int LV = DV + 4, R1 = (DK * LV > 2 * C * 80) ? DK * LV : 2 * C * 80;
     __shared__ __attribute__((aligned(16))) float r1[R1], b1[C * LV], b2[C * LV];
@@ -585,16 +613,16 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     const int t0 = n * C, L = min(C, p.T - t0);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4;
     const size_t uC = (size_t)u * C;
-    const uint16_t *dout = reinterpret_cast<const uint16_t *>(p.dout);
+    const TIn *dout = static_cast<const TIn *>(p.dout);
 
     // phase 1: dEt = -dR Sn^T, dQt = dO Sn^T, dgamma_C = rowsum(dS1 . Sn)
     {
         // dO: 8 values per load (rows past T read the last token, zeroed)
-        u16x8 xo[C * DV / 8 / 256];
+        In8<TIn> xo[C * DV / 8 / 256];
 #pragma unroll
         for (int it = 0; it < C * DV / 8 / 256; ++it) {
             const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
-            xo[it] = *reinterpret_cast<const u16x8 *>(dout + (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j);
+            xo[it].load(dout, (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j);
         }
         lds_load<DK, DV, LV>(r1, ws.Sn + (size_t)u * DK * DV);
         lds_load<C, DV, LV>(b1, ws.dR + uC * DV, -1.f);
@@ -602,7 +630,7 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
         for (int it = 0; it < C * DV / 8 / 256; ++it) {
             const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8;
             f4 lo, hi;
-            bf8_to_f32(xo[it], lo, hi);
+            xo[it].get(lo, hi);
             const float on = t < L ? 1.f : 0.f;
             *reinterpret_cast<f4 *>(b2 + t * LV + j) = lo * on;
             *reinterpret_cast<f4 *>(b2 + t * LV + j + 4) = hi * on;
@@ -710,7 +738,7 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
 // ---------------------------------------------------------------------------
 constexpr int LOCAL_NT = 512;
 
-template <int DK, int DV>
+template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
     constexpr int CG = DK / 64, NW = LOCAL_NT / 64;
     __shared__ __attribute__((aligned(16))) float Gs[C * 64], Ks[C * 64], Es[C * 64], Qs[C * 64], dMs[C * C],
@@ -720,8 +748,8 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
     const int t0 = n * C, L = min(C, p.T - t0);
     const int tid = threadIdx.x, w = tid >> 6, cl = tid & 63, c = 64 * cg + cl, rr = cl & 15, gg = cl >> 4;
     const int b = w >> 1, half = w & 1, r0 = 8 * w;  // block, half of it, first own row
-    const uint16_t *q = reinterpret_cast<const uint16_t *>(p.q), *k = reinterpret_cast<const uint16_t *>(p.k);
-    const uint16_t *a = reinterpret_cast<const uint16_t *>(p.a), *er = reinterpret_cast<const uint16_t *>(p.erase);
+    const TIn *q = static_cast<const TIn *>(p.q), *k = static_cast<const TIn *>(p.k);
+    const TIn *a = static_cast<const TIn *>(p.a), *er = static_cast<const TIn *>(p.erase);
     const float Al = p.A_log[(size_t)hv * DK + c], rate = exp_fast(Al);
 
     // inputs of the chain rule, loaded first so that their latency overlaps the pair sums
@@ -744,10 +772,10 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
         const size_t kq = (((size_t)bb * p.T + t0 + tl) * p.Hk + hk) * DK + c;
         const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
         const float on = t < L ? 1.f : 0.f;
-        const float kv = bf16_to_f32(k[kq]) * on;
-        grun += -rate * softplus_fast(bf16_to_f32(a[ka])) * LOG2E * on;
-        const float ev = sigmoid_fast(bf16_to_f32(er[ka])) * kv;
-        const float qv = p.scale * bf16_to_f32(q[kq]) * on;
+        const float kv = io<TIn>::ld(k, kq) * on;
+        grun += -rate * softplus_fast(io<TIn>::ld(a, ka)) * LOG2E * on;
+        const float ev = sigmoid_fast(io<TIn>::ld(er, ka)) * kv;
+        const float qv = p.scale * io<TIn>::ld(q, kq) * on;
         gpre[x] = grun;
         Ks[t * 64 + cl] = kv;
         Es[t * 64 + cl] = ev;
@@ -879,7 +907,7 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
         const int t = r0 + x;
         if (t < L) {
             const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
-            const float av = bf16_to_f32(a[ka]), beta = sigmoid_fast(bf16_to_f32(er[ka]));
+            const float av = io<TIn>::ld(a, ka), beta = sigmoid_fast(io<TIn>::ld(er, ka));
             const float kk = Ks[t * 64 + cl];
             const float dg = carry;  // natural-log units
             p.da[ka] = -dg * rate * sigmoid_fast(av);
@@ -899,15 +927,18 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
     }
     // dz = dR -> dv, d_write (the first channel group of each chunk)
     if (cg == 0) {
-        const uint16_t *v = reinterpret_cast<const uint16_t *>(p.v), *wr = reinterpret_cast<const uint16_t *>(p.write);
+        const TIn *v = static_cast<const TIn *>(p.v), *wr = static_cast<const TIn *>(p.write);
         const float *dRu = ws.dR + (size_t)u * C * DV;
 #pragma unroll
         for (int it = 0; it < C * DV / 8 / LOCAL_NT; ++it) {
             const int i = tid + LOCAL_NT * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
             const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
             f4 vv[2], om[2];
-            bf8_to_f32(*reinterpret_cast<const u16x8 *>(v + kv), vv[0], vv[1]);
-            bf8_to_f32(*reinterpret_cast<const u16x8 *>(wr + kv), om[0], om[1]);
+            In8<TIn> xv, xw;
+            xv.load(v, kv);
+            xw.load(wr, kv);
+            xv.get(vv[0], vv[1]);
+            xw.get(om[0], om[1]);
             f4 dz[2] = {*reinterpret_cast<const f4 *>(dRu + t * DV + j), *reinterpret_cast<const f4 *>(dRu + t * DV + j + 4)};
             if (t < L) {
 #pragma unroll
@@ -967,7 +998,7 @@ __global__ void g2b_empty(float *dS0, const float *dST, size_t ns, float *dA_log
     }
 }
 
-template <int DK, int DV>
+template <typename TIn, int DK, int DV>
 hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t s, const hipEvent_t *ev) {
     const unsigned units = (unsigned)(p.B * p.Hv * p.NC), slices = (unsigned)(p.B * p.Hv * (DV / 32));
     hipError_t e = hipSuccess;
@@ -975,15 +1006,15 @@ hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t
         if (ev && e == hipSuccess) e = hipEventRecord(ev[i], s);
     };
     rec(0);
-    hipLaunchKernelGGL((g2b_prep<DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
+    hipLaunchKernelGGL((g2b_prep<TIn, DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
     rec(1);
     hipLaunchKernelGGL((g2b_fwd_scan<DK, DV>), dim3(slices), dim3(256), 0, s, p, ws);
     rec(2);
-    hipLaunchKernelGGL((g2b_bwd_scan<DK, DV>), dim3(slices), dim3(256), 0, s, p, ws);
+    hipLaunchKernelGGL((g2b_bwd_scan<TIn, DK, DV>), dim3(slices), dim3(256), 0, s, p, ws);
     rec(3);
-    hipLaunchKernelGGL((g2b_products<DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
+    hipLaunchKernelGGL((g2b_products<TIn, DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
     rec(4);
-    hipLaunchKernelGGL((g2b_local<DK, DV>), dim3(units * (DK / 64)), dim3(LOCAL_NT), 0, s, p, ws);
+    hipLaunchKernelGGL((g2b_local<TIn, DK, DV>), dim3(units * (DK / 64)), dim3(LOCAL_NT), 0, s, p, ws);
     rec(5);
     const size_t nq = (size_t)p.B * p.T * p.Hk * DK / 256 + 1;
     hipLaunchKernelGGL((g2b_reduce<DK>), dim3((unsigned)(nq < 65536 ? nq : 65536)), dim3(256), 0, s, p, ws);
@@ -1036,10 +1067,17 @@ hipError_t launch_bwd2(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t s
                            dim3(256), 0, s, p.dS0, p.dST, ns, p.dA_log, na);
         return hipGetLastError();
     }
-    if (p.Dk == 128 && p.Dv == 128) return launch_bwd2_t<128, 128>(p, ws, s, ev);
-    if (p.Dk == 128 && p.Dv == 64) return launch_bwd2_t<128, 64>(p, ws, s, ev);
-    if (p.Dk == 64 && p.Dv == 128) return launch_bwd2_t<64, 128>(p, ws, s, ev);
-    if (p.Dk == 64 && p.Dv == 64) return launch_bwd2_t<64, 64>(p, ws, s, ev);
+    if (p.f32) {
+        if (p.Dk == 128 && p.Dv == 128) return launch_bwd2_t<float, 128, 128>(p, ws, s, ev);
+        if (p.Dk == 128 && p.Dv == 64) return launch_bwd2_t<float, 128, 64>(p, ws, s, ev);
+        if (p.Dk == 64 && p.Dv == 128) return launch_bwd2_t<float, 64, 128>(p, ws, s, ev);
+        if (p.Dk == 64 && p.Dv == 64) return launch_bwd2_t<float, 64, 64>(p, ws, s, ev);
+        return hipErrorInvalidValue;
+    }
+    if (p.Dk == 128 && p.Dv == 128) return launch_bwd2_t<bf16_t, 128, 128>(p, ws, s, ev);
+    if (p.Dk == 128 && p.Dv == 64) return launch_bwd2_t<bf16_t, 128, 64>(p, ws, s, ev);
+    if (p.Dk == 64 && p.Dv == 128) return launch_bwd2_t<bf16_t, 64, 128>(p, ws, s, ev);
+    if (p.Dk == 64 && p.Dv == 64) return launch_bwd2_t<bf16_t, 64, 64>(p, ws, s, ev);
     return hipErrorInvalidValue;
 }
 

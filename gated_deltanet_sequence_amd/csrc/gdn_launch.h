@@ -92,10 +92,11 @@ size_t bwd2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, B
 
 struct Bwd2Args {
     int B, T, Hk, Hv, Dk, Dv, NC;
+    bool f32;                                    // float32 inputs (else bfloat16)
     float scale;
-    const void *q, *k, *v, *a, *erase, *write;  // bfloat16
+    const void *q, *k, *v, *a, *erase, *write;  // input type
     const float *A_log, *S0;
-    const void *dout;                            // bfloat16 [B,T,Hv,Dv]
+    const void *dout;                            // input type, [B,T,Hv,Dv]
     const float *dST;                            // [B,Hv,Dk,Dv] or null
     float *dq, *dk, *dv, *da, *derase, *dwrite, *dA_log, *dS0;
 };

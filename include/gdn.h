@@ -178,7 +178,7 @@ gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const
  * gradient of A = (I + tril(Ebar Kbar^T, -1))^{-1} collects dU Z^T and dY Ebar^T).
  * Computes the vector-Jacobian products of (out, final_state) with
  * (d_out, d_final_state) for the same inputs as gdn2_chunk_fwd:
- *   d_out           [B,T,Hv,Dv] bfloat16 gradient of out
+ *   d_out           [B,T,Hv,Dv] gradient of out, in d->dtype
  *   d_final_state   [B,Hv,Dk,Dv] float32 gradient of final_state, or NULL (zero)
  *   dq, dk          [B,T,Hk,Dk] float32 (written): summed over the Hv/Hk value
  *                   heads that share a key head
@@ -191,7 +191,8 @@ gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const
  *                   bytes, 256-byte aligned (about 0.6 MB per (sequence, value
  *                   head, 64 tokens) at Dk = Dv = 128: the forward is recomputed
  *                   in float32 and its per-chunk states are kept).
- * All arithmetic is float32.  d->dtype must be GDN_BF16.  No output may overlap
+ * All arithmetic is float32; the inputs and d_out are bfloat16 or float32
+ * (d->dtype), the gradients float32 either way.  No output may overlap
  * any input, the workspace or another output (GDN_ERR_ALIAS).  Deterministic
  * (no atomics).  Asynchronous on `stream`; nothing is enqueued on an error. */
 size_t gdn2_chunk_bwd_workspace_bytes(const gdn_dims *d);

@@ -432,7 +432,9 @@ def test_bwd2_workspace_bytes():
     need = units * 4 * (4 * 64 * 64 + 6 * 64 * 128 + 5 * 64 * 128 + 2 * 128 * 128 + 3 * 128) \
         + 2 * 8192 * 64 * 128 * 4
     assert need <= n < need + 24 * 256
-    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(dims(dtype=binding.GDN_F32))) == 0
+    # float32 inputs: the same float32 workspace
+    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(dims(dtype=binding.GDN_F32))) == \
+        L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(dims()))
     assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(dims(T=0))) == 0
     assert L.gdn2_chunk_bwd_workspace_bytes(None) == 0
 
@@ -440,7 +442,6 @@ def test_bwd2_workspace_bytes():
 def test_bwd2_validation():
     buf = Buf()
     d = dims()
-    assert call_bwd2(dims(dtype=binding.GDN_F32), bwd2_args(buf, d)) == ERR_UNSUPPORTED
     assert call_bwd2(dims(Hv=3), bwd2_args(buf, d)) == ERR_SHAPE
     assert call_bwd2(dims(Dk=96), bwd2_args(buf, d)) == ERR_UNSUPPORTED
     for name in ["q", "k", "v", "a", "A_log", "erase", "write", "dout", "dq", "dk", "dv", "da", "derase",

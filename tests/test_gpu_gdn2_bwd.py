@@ -188,3 +188,16 @@ def test_gdn2_t8192_sampled_key_heads():
             assert_close(n, got[n][sl_], ref[n], tol(n))
     for n in NAMES:
         assert torch.isfinite(got[n]).all(), n
+
+
+@pytest.mark.parametrize("T,Dk,Dv", [(1, 128, 128), (65, 128, 128), (200, 128, 128), (150, 64, 64),
+                                     (130, 64, 128)])
+def test_float32_inputs(T, Dk, Dv):
+    """float32 inputs and output gradient: the same float32 arithmetic, the same bounds."""
+    full_check(GDNSpec(variant="gdn2", dtype="f32", B=1, T=T, Hk=1, Hv=2, Dk=Dk, Dv=Dv, seed=530 + T + Dk,
+                       init_state=True))
+
+
+def test_float32_batch_and_key_head_groups():
+    full_check(GDNSpec(variant="gdn2", dtype="f32", B=2, T=130, Hk=2, Hv=4, Dk=128, Dv=128, seed=540,
+                       init_state=True))
