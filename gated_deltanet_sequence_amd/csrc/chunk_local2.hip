@@ -255,32 +255,38 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
     // ---- 4. tiles of M and A_qk below the diagonal (rows 16I, columns 16J,
     //         I > J): reference token 16I.  A = k e^{G_ref - G} (column rows),
     //         B = e e^{G - G_ref} or q e^{G - G_ref} (row rows): the accumulator
-    //         holds row 16I + m, columns 16J + 4g .. +3.  Wave w takes tiles w
-    //         and w + 4; the results stay in registers until the e/k/q space is
-    //         free.
-    constexpr int TI[6] = {1, 2, 2, 3, 3, 3}, TJ[6] = {0, 0, 1, 0, 1, 2};
+    //         holds row 16I + m, columns 16J + 4g .. +3.  A wave takes whole row
+    //         tiles, so the row side (its factors and both B operands) is formed
+    //         once for its tiles: wave 0 (1,0) (it alone runs the inverse
+    //         afterwards), wave 1 (2,0) (2,1), wave 2 (3,0) (3,1), wave 3 (3,2).
+    //         The results stay in registers until the e/k/q space is free.
+    const int oI = w == 0 ? 1 : w == 1 ? 2 : 3, oJ0 = w == 3 ? 2 : 0, onj = (w == 1 || w == 2) ? 2 : 1;
     f4 oM[2], oQ[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        oM[h] = oQ[h] = f4{0, 0, 0, 0};
-        const int p = w + 4 * h;
-        if (p < 6) {
-            const int I = TI[p], J = TJ[p], ref = 16 * I, tr = 16 * I + m, ir = 16 * J + m;
+    for (int h = 0; h < 2; ++h) oM[h] = oQ[h] = f4{0, 0, 0, 0};
+    {
+        const int ref = 16 * oI, tr = 16 * oI + m;
 #pragma unroll
-            for (int kq = 0; kq < NKQ; ++kq) {
-                const int c = 32 * kq + 8 * g;
-                float gt[8], gr[8], gi[8], fl[8], fr[8];
-                ldg8<DK>(Gl, tr, c, gt);
-                ldg8<DK>(Gl, ref, c, gr);
-                ldg8<DK>(Gl, ir, c, gi);
+        for (int kq = 0; kq < NKQ; ++kq) {
+            const int c = 32 * kq + 8 * g;
+            float gt[8], gr[8], fl[8];
+            ldg8<DK>(Gl, tr, c, gt);
+            ldg8<DK>(Gl, ref, c, gr);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    fl[j] = __builtin_amdgcn_exp2f(gt[j] - gr[j]);
-                    fr[j] = __builtin_amdgcn_exp2f(gr[j] - gi[j]);
+            for (int j = 0; j < 8; ++j) fl[j] = __builtin_amdgcn_exp2f(gt[j] - gr[j]);
+            const h8 be = mul_mix(ldh8<DK>(El, tr, c), fl), bq = mul_mix(ldh8<DK>(Ql, tr, c), fl);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (h < onj) {
+                    const int ir = 16 * (oJ0 + h) + m;
+                    float gi[8], fr[8];
+                    ldg8<DK>(Gl, ir, c, gi);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) fr[j] = __builtin_amdgcn_exp2f(gr[j] - gi[j]);
+                    const h8 rk8 = mul_mix(ldh8<DK>(Kl, ir, c), fr);
+                    oM[h] = mfma_f16_k32(rk8, be, oM[h]);
+                    oQ[h] = mfma_f16_k32(rk8, bq, oQ[h]);
                 }
-                const h8 rk8 = mul_mix(ldh8<DK>(Kl, ir, c), fr);
-                oM[h] = mfma_f16_k32(rk8, mul_mix(ldh8<DK>(El, tr, c), fl), oM[h]);
-                oQ[h] = mfma_f16_k32(rk8, mul_mix(ldh8<DK>(Ql, tr, c), fl), oQ[h]);
             }
         }
     }
@@ -349,10 +355,9 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
     __syncthreads();  // G, e, k, q are dead: the tiles take their space
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int p = w + 4 * h;
-        if (p < 6) {
-            *reinterpret_cast<f4 *>(Ms + tri_index(TI[p], TJ[p]) * 256 + m * 16 + 4 * g) = oM[h];
-            *reinterpret_cast<f4 *>(Qs + tri_index(TI[p], TJ[p]) * 256 + m * 16 + 4 * g) = oQ[h];
+        if (h < onj) {
+            *reinterpret_cast<f4 *>(Ms + tri_index(oI, oJ0 + h) * 256 + m * 16 + 4 * g) = oM[h];
+            *reinterpret_cast<f4 *>(Qs + tri_index(oI, oJ0 + h) * 256 + m * 16 + 4 * g) = oQ[h];
         }
     }
     *reinterpret_cast<f4 *>(Ms + tri_index(w, w) * 256 + m * 16 + 4 * g) = dM;
@@ -369,17 +374,17 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
 #pragma unroll
         for (int kb = 0; kb < rb; ++kb)
             Lf[tri_index(rb, kb)] = *reinterpret_cast<const f4 *>(Ms + tri_index(rb, kb) * 256 + m * 16 + 4 * g);
-    {
+    {   // lane (block bq, column c): column c of the block's inverse, x[r] = delta_rc to
+        // start; L[r][j] from lane j of the same 16-lane row by a DPP row broadcast
         const int bq = lane >> 4, c = lane & 15;
         const float *Lb = Ms + tri_index(bq, bq) * 256;
-        float x[16];
+        float nl[16], x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float s = (r == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int jj = 0; jj < r; ++jj) s -= Lb[r * 16 + jj] * x[jj];
-            x[r] = s;
+            nl[r] = -Lb[r * 16 + c];
+            x[r] = (r == c) ? 1.f : 0.f;
         }
+        subst_steps(nl, x, std::make_integer_sequence<int, 15>());
 #pragma unroll
         for (int r = 0; r < 16; ++r) Xw[tri_index(bq, bq) * 256 + r * 16 + c] = x[r];
     }
