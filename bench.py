@@ -121,27 +121,43 @@ def log(msg):
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "gated_deltanet_sequence_amd", "csrc")
 COPY_MIB = 256                      # calibration copy: 256 MiB read + 256 MiB written
-# kernel key -> (regex on the demangled kernel name, summary file)
+# kernel key -> (regex on the demangled kernel name, summary file, source file)
 TRAFFIC_FILES = {
     # (names with float16 template arguments come out mangled: Lb0E / Lb1E is the bool)
-    "scan_split_kernel": (r"scan_split_kernel(<[^>]*false>|I.*Lb0E)", "scan_split_kernel_prefill_t4096_traffic.md"),
-    "chunk_local_kernel": (r"chunk_local_kernel", "chunk_local_kernel_prefill_t4096_traffic.md"),
-    "decode_kernel": (r"decode_kernel<[^>]*false>", "decode_kernel_decode_b256_traffic.md"),
-    "decode_kernel_gdn2": (r"decode_kernel<[^>]*true>", "decode_kernel_gdn2_decode_b256_traffic.md"),
-    "scan_split_kernel_gdn2": (r"scan_split_kernel(<[^>]*true>|I.*Lb1E)", "scan_split_kernel_gdn2_t8192_traffic.md"),
-    "chunk_local2_kernel": (r"chunk_local2_kernel", "chunk_local2_kernel_gdn2_t8192_traffic.md"),
-    "g2b_local": (r"g2b_local", "g2b_local_gdn2_bwd_t8192_traffic.md"),
-    "gated_rmsnorm_kernel": (r"gated_rmsnorm_kernel", "gated_rmsnorm_kernel_t4096_traffic.md"),
-    "causal_conv1d_kernel": (r"causal_conv1d_kernel", "causal_conv1d_kernel_t4096_traffic.md"),
+    "scan_split_kernel": (r"scan_split_kernel(<[^>]*false>|I.*Lb0E)", "scan_split_kernel_prefill_t4096_traffic.md",
+                          "state_scan.hip"),
+    "chunk_local_kernel": (r"chunk_local_kernel", "chunk_local_kernel_prefill_t4096_traffic.md", "chunk_local.hip"),
+    "decode_kernel": (r"decode_kernel<[^>]*false>", "decode_kernel_decode_b256_traffic.md", "decode.hip"),
+    "decode_kernel_gdn2": (r"decode_kernel<[^>]*true>", "decode_kernel_gdn2_decode_b256_traffic.md", "decode.hip"),
+    "scan_split_kernel_gdn2": (r"scan_split_kernel(<[^>]*true>|I.*Lb1E)", "scan_split_kernel_gdn2_t8192_traffic.md",
+                               "state_scan.hip"),
+    "chunk_local2_kernel": (r"chunk_local2_kernel", "chunk_local2_kernel_gdn2_t8192_traffic.md", "chunk_local2.hip"),
+    "g2b_local": (r"g2b_local", "g2b_local_gdn2_bwd_t8192_traffic.md", "bwd2.hip"),
+    "gated_rmsnorm_kernel": (r"gated_rmsnorm_kernel", "gated_rmsnorm_kernel_t4096_traffic.md", "epilogue.hip"),
+    "causal_conv1d_kernel": (r"causal_conv1d_kernel", "causal_conv1d_kernel_t4096_traffic.md", "prologue.hip"),
 }
 
 
-def kernel_sources_sha256():
-    """Hash of every HIP source and header the kernels are built from."""
+def _source_closure(src):
+    """The HIP source and the local headers it includes, transitively."""
+    seen, todo = set(), [os.path.join(CSRC, src)]
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(f):
+            continue
+        seen.add(f)
+        for inc in re.findall(r'^#include\s+"([^"]+)"', open(f).read(), re.M):
+            for d in (os.path.dirname(f), CSRC, os.path.join(ROOT, "include")):
+                if os.path.exists(os.path.join(d, inc)):
+                    todo.append(os.path.join(d, inc))
+                    break
+    return sorted(seen)
+
+
+def kernel_sources_sha256(kernel):
+    """Hash of the source file a kernel is built from and the headers it includes."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))
-                   + glob.glob(os.path.join(ROOT, "include", "*.h")))
-    for f in files:
+    for f in _source_closure(TRAFFIC_FILES[kernel][2]):
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()
@@ -149,14 +165,14 @@ def kernel_sources_sha256():
 
 def stored_traffic(kernel):
     """Bytes per launch from the committed counter summary, or None if the
-    summary is missing or the kernel sources changed since it was taken."""
-    path = os.path.join(PROFILES, TRAFFIC_FILES.get(kernel, ("", "-"))[1])
+    summary is missing or the kernel's sources changed since it was taken."""
+    path = os.path.join(PROFILES, TRAFFIC_FILES.get(kernel, ("", "-", ""))[1])
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_sha = re.search(r"^source_sha256:\s*([0-9a-f]{64})", text, re.M)
     m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)", text, re.M)
-    if not (m_sha and m_b) or m_sha.group(1) != kernel_sources_sha256():
+    if not (m_sha and m_b) or m_sha.group(1) != kernel_sources_sha256(kernel):
         return None
     return int(m_b.group(1))
 
@@ -206,8 +222,8 @@ def summarize_pmc(fetch_dir, write_dir):
     cw, ncw = _per_dispatch(w_rows, "WRITE_SIZE", copy_rx)
     kib = COPY_MIB * 1024
     f_scale, w_scale = kib / cf, kib / cw
-    sha = kernel_sources_sha256()
-    for kernel, (rx, fname) in TRAFFIC_FILES.items():
+    for kernel, (rx, fname, _src) in TRAFFIC_FILES.items():
+        sha = kernel_sources_sha256(kernel)
         kf, nkf = _per_dispatch(f_rows, "FETCH_SIZE", rx)
         kw, nkw = _per_dispatch(w_rows, "WRITE_SIZE", rx)
         if kf is None or kw is None:
@@ -232,6 +248,7 @@ def summarize_pmc(fetch_dir, write_dir):
             f"| {kernel} HBM read bytes per launch | {fetch_b:.0f} |",
             f"| {kernel} HBM write bytes per launch | {write_b:.0f} |", "",
             f"traffic_bytes_per_launch: {int(round(fetch_b + write_b))}",
+            f"sources: {', '.join(os.path.basename(f) for f in _source_closure(_src))}",
             f"source_sha256: {sha}", ""]
         path = os.path.join(PROFILES, fname)
         open(path, "w").write("\n".join(lines))
