@@ -511,9 +511,9 @@ gdn_status gdn_causal_conv1d(const gdn_dims *d, int32_t kernel_size, const void 
     if (kernel_size != 4) return fail(GDN_ERR_UNSUPPORTED, "kernel_size = %d: supported 4", kernel_size);
     if (activation != GDN_ACT_NONE && activation != GDN_ACT_SILU)
         return fail(GDN_ERR_UNSUPPORTED, "activation = %d: supported GDN_ACT_NONE, GDN_ACT_SILU", activation);
-    if (d->B > 65535 || (long long)d->T > 65535LL * gdn::conv_tokens_per_thread())
+    if (d->B > 65535 || (long long)d->T > 65535LL * gdn::conv_tokens_per_block())
         return fail(GDN_ERR_UNSUPPORTED, "B = %d, T = %d: at most 65535 sequences and %lld tokens", d->B, d->T,
-                    65535LL * gdn::conv_tokens_per_thread());
+                    65535LL * gdn::conv_tokens_per_block());
     const size_t B = d->B, T = d->T, K = kernel_size, es = esize(d);
     const size_t qk = (size_t)d->Hk * d->Dk, vw = (size_t)d->Hv * d->Dv, C = 2 * qk + vw;
     const Span sx{"x", x, B * T * C * es}, sw{"weight", weight, C * K * 4}, sb{"bias", bias, bias ? C * 4 : 0};

@@ -144,7 +144,7 @@ struct ConvArgs {
     void *state_out, *q, *k, *v;
 };
 hipError_t launch_causal_conv1d(const ConvArgs &p, hipStream_t s);
-int conv_tokens_per_thread();
+int conv_tokens_per_block();
 long long gated_rmsnorm_max_rows();
 
 }  // namespace gdn

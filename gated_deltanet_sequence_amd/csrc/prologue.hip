@@ -6,23 +6,28 @@
 // for decode).  Per sequence b, channel c, token t:
 //     y[b,t,c] = act(bias[c] + sum_{j<K} w[c][j] x[b, t-K+1+j, c]),
 // inputs before token 0 from the cached state [B][K-1][C] (or zero).
-// A streaming kernel (about a dozen flops per 4 bytes moved): a thread owns
-// 4 channels (8-byte accesses for bfloat16, 16-byte for float32, non-temporal
-// stores) of CONV_TT consecutive tokens, issues all CONV_TT + K - 1 row loads
-// (its outputs plus the K-1 halo) before any arithmetic and keeps the window in
-// registers.  Four channels rather than eight keep a thread at ~72 registers, so
-// seven waves share a SIMD and one wave's arithmetic overlaps the others'
-// loads; at eight channels (~140 registers, three waves) the SiLU's issue time
-// showed through.  The new state (the last K-1 inputs) is written by the first
-// token block's threads, which are also the only readers of the old state:
-// in-place state update is race-free.
+// A streaming kernel (about a dozen flops per 4 bytes moved).  A work-group of
+// eight waves covers 256 channels of 64 consecutive tokens: a thread owns 4
+// channels (8-byte accesses for bfloat16, 16-byte for float32, non-temporal
+// stores) of one wave's 8 tokens and keeps its window (its 8 rows plus the K-1
+// rows before them) in registers, issuing all its row loads before any
+// arithmetic.  Each wave hands its last K-1 rows to the next wave through LDS,
+// so only the work-group's first wave loads a halo: the input is read 67/64
+// times (with a halo per 16-token thread block it was 19/16, 1.10x the minimum
+// traffic).  Four channels per thread keep a thread near 70 registers, so six
+// waves share a SIMD and one wave's arithmetic overlaps the others' loads.  The new state (the last K-1 inputs) is written
+// by the first wave of the first token block, which is also the only reader of
+// the old state: in-place state update is race-free.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
-constexpr int CONV_TT = 16;  // tokens per thread
-constexpr int CONV_CH = 4;   // channels per thread
+constexpr int CONV_TT = 8;                       // tokens per thread (one wave's block)
+constexpr int CONV_CH = 4;                       // channels per thread
+constexpr int CONV_WAVES = 8;                    // consecutive token blocks per work-group
+constexpr int CONV_BT = CONV_TT * CONV_WAVES;    // tokens per work-group
+constexpr int CONV_BC = 64 * CONV_CH;            // channels per work-group
 
 template <typename T> struct Row4;
 template <> struct Row4<bf16_t> {
@@ -55,40 +60,53 @@ template <> struct Row4<float> {
 };
 
 template <typename E, int K, bool SILU>
-__global__ __launch_bounds__(256) void causal_conv1d_kernel(ConvArgs p) {
+__global__ __launch_bounds__(64 * CONV_WAVES) void causal_conv1d_kernel(ConvArgs p) {
     typedef Row4<E> R4;
+    typedef typename R4::raw raw;
     constexpr int W = CONV_TT + K - 1;  // rows in the window
     // bfloat16 SiLU with log2 e folded into the weights and bias: a = x log2 e
     // and x sigmoid(x) = a / (log2 e (1 + 2^-a)), one exp2, one fma, one
     // reciprocal, one multiply.  float32 keeps the exact-exponential sigmoid.
     constexpr bool FOLD = SILU && sizeof(E) == 2;
     constexpr float L2E = 1.4426950408889634f, WS = FOLD ? L2E : 1.f;
-    const int cg = blockIdx.x * 256 + threadIdx.x;
-    if (cg * CONV_CH >= p.C) return;  // no barriers below
-    const int c0 = cg * CONV_CH, b = blockIdx.z, t0 = blockIdx.y * CONV_TT, T = p.T, C = p.C;
+    __shared__ raw hand[CONV_WAVES - 1][K - 1][64];  // wave w's last K-1 rows, for wave w + 1
+
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c0 = blockIdx.x * CONV_BC + lane * CONV_CH;
+    const bool valid = c0 < p.C;  // no early exit: every thread reaches the barrier
+    const int b = blockIdx.z, T = p.T, C = p.C;
+    const int t0 = blockIdx.y * CONV_BT + wv * CONV_TT;  // this wave's first token
     const void *state = p.state;
-    // interior token blocks (the window inside [0, T), all outputs < T) take
-    // straight-line loads and stores from one base offset; a per-row test with
-    // the cached-state fallback put several scalar branches in front of every
-    // load and cut the bytes in flight
-    const bool interior = t0 >= K - 1 && t0 + CONV_TT <= T;
-    typename R4::raw win[W];
-    if (interior) {
-        const size_t base = ((size_t)b * T + (t0 - (K - 1))) * C + c0;
+
+    // own rows t0 .. t0+15 into win[K-1 ..]: full blocks take straight-line
+    // loads from one base offset (a per-row bound test put scalar branches in
+    // front of every load and cut the bytes in flight)
+    raw win[W];
 #pragma unroll
-        for (int i = 0; i < W; ++i) win[i] = R4::ld(p.x, base + (size_t)i * C);
-    } else {
+    for (int i = 0; i < W; ++i) win[i] = R4::zero();
+    if (valid) {
+        const size_t base = ((size_t)b * T + t0) * C + c0;
+        if (t0 + CONV_TT <= T) {
 #pragma unroll
-        for (int i = 0; i < W; ++i) {
-            const int s = t0 - (K - 1) + i;  // input token of window row i
-            win[i] = R4::zero();
-            if (s >= 0 && s < T) win[i] = R4::ld(p.x, ((size_t)b * T + s) * C + c0);
-            else if (s < 0 && state) win[i] = R4::ld(state, ((size_t)b * (K - 1) + (K - 1 + s)) * C + c0);
+            for (int i = 0; i < CONV_TT; ++i) win[K - 1 + i] = R4::ld(p.x, base + (size_t)i * C);
+        } else {
+#pragma unroll
+            for (int i = 0; i < CONV_TT; ++i)
+                if (t0 + i < T) win[K - 1 + i] = R4::ld(p.x, base + (size_t)i * C);
+        }
+        if (wv == 0) {  // the work-group's halo: earlier inputs, the cached state, or zeros
+#pragma unroll
+            for (int i = 0; i < K - 1; ++i) {
+                const int s = t0 - (K - 1) + i;
+                if (s >= 0 && s < T) win[i] = R4::ld(p.x, ((size_t)b * T + s) * C + c0);
+                else if (s < 0 && state) win[i] = R4::ld(state, ((size_t)b * (K - 1) + (K - 1 + s)) * C + c0);
+            }
         }
     }
     // weights and bias after the window, with no branch around a load: a
     // guarded load's wait would also wait for every window row issued before it
-    const f4 *wp = reinterpret_cast<const f4 *>(p.w + (size_t)c0 * K);
+    const int cw = valid ? c0 : 0;
+    const f4 *wp = reinterpret_cast<const f4 *>(p.w + (size_t)cw * K);
     const float *bp = p.bias ? p.bias : p.w;  // any valid address when there is no bias
     const bool has_bias = p.bias != nullptr;
     float w[CONV_CH][K], bias[CONV_CH];
@@ -98,9 +116,20 @@ __global__ __launch_bounds__(256) void causal_conv1d_kernel(ConvArgs p) {
         const f4 wj = wp[j];
 #pragma unroll
         for (int k = 0; k < K; ++k) w[j][k] = wj[k] * WS;
-        const float bj = bp[c0 + j];
+        const float bj = bp[cw + j];
         bias[j] = has_bias ? bj * WS : 0.f;
     }
+    // hand-over: the last K-1 own rows go to the next wave, whose halo they are
+    if (wv < CONV_WAVES - 1) {
+#pragma unroll
+        for (int i = 0; i < K - 1; ++i) hand[wv][i][lane] = win[CONV_TT + i];
+    }
+    __syncthreads();
+    if (wv > 0) {
+#pragma unroll
+        for (int i = 0; i < K - 1; ++i) win[i] = hand[wv - 1][i][lane];
+    }
+
     // destination: the q, k or v tensor that holds these channels
     void *dst;
     int cd, dw;  // channel offset within the destination row, destination row width
@@ -112,7 +141,7 @@ __global__ __launch_bounds__(256) void causal_conv1d_kernel(ConvArgs p) {
         dst = p.v; cd = c0 - 2 * p.qk; dw = C - 2 * p.qk;
     }
     const size_t obase = ((size_t)b * T + t0) * dw + cd;
-    const int nout = T - t0 < CONV_TT ? T - t0 : CONV_TT;  // outputs of this block (uniform)
+    const int nout = valid ? (T - t0 < CONV_TT ? T - t0 : CONV_TT) : 0;  // outputs of this thread
     // a guarded body, not an early exit: the loop must unroll fully so that the
     // window stays in registers (a runtime exit left it in scratch memory)
 #pragma unroll
@@ -131,12 +160,12 @@ __global__ __launch_bounds__(256) void causal_conv1d_kernel(ConvArgs p) {
             R4::st_f(dst, obase + (size_t)i * dw, y);
         }
     }
-    if (blockIdx.y == 0 && p.state_out) {
+    if (blockIdx.y == 0 && wv == 0 && valid && p.state_out) {
         // the last K-1 inputs; older cached inputs when T < K-1
 #pragma unroll
         for (int i = 0; i < K - 1; ++i) {
             const int s = T - (K - 1) + i;
-            typename R4::raw r = R4::zero();
+            raw r = R4::zero();
             if (s >= 0) r = R4::ld(p.x, ((size_t)b * T + s) * C + c0);
             // cached slot K-1+s = T+i >= i: not yet overwritten when the state is updated in place
             else if (state) r = R4::ld(state, ((size_t)b * (K - 1) + (K - 1 + s)) * C + c0);
@@ -147,9 +176,9 @@ __global__ __launch_bounds__(256) void causal_conv1d_kernel(ConvArgs p) {
 
 template <typename T, bool SILU>
 static hipError_t launch_conv_t(const ConvArgs &p, hipStream_t s) {
-    const dim3 grid((unsigned)((p.C / CONV_CH + 255) / 256),
-                    (unsigned)(p.T > 0 ? (p.T + CONV_TT - 1) / CONV_TT : 1), (unsigned)p.B);
-    hipLaunchKernelGGL((causal_conv1d_kernel<T, 4, SILU>), grid, dim3(256), 0, s, p);
+    const dim3 grid((unsigned)((p.C + CONV_BC - 1) / CONV_BC),
+                    (unsigned)(p.T > 0 ? (p.T + CONV_BT - 1) / CONV_BT : 1), (unsigned)p.B);
+    hipLaunchKernelGGL((causal_conv1d_kernel<T, 4, SILU>), grid, dim3(64 * CONV_WAVES), 0, s, p);
     return hipGetLastError();
 }
 
@@ -160,6 +189,6 @@ hipError_t launch_causal_conv1d(const ConvArgs &p, hipStream_t s) {
     return p.silu ? launch_conv_t<bf16_t, true>(p, s) : launch_conv_t<bf16_t, false>(p, s);
 }
 
-int conv_tokens_per_thread() { return CONV_TT; }
+int conv_tokens_per_block() { return CONV_BT; }
 
 }  // namespace gdn

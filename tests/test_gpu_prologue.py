@@ -35,12 +35,19 @@ def check(B, T, Hk, Hv, Dk, Dv, dtype, seed, bias=True, state=True, act="silu"):
     assert torch.equal(so.cpu().double(), torch.from_numpy(s_ref)), "conv state"
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 15, 16, 17, 100])
+@pytest.mark.parametrize("T", [1, 2, 3, 15, 16, 17, 63, 64, 65, 100, 130])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_lengths(T, dtype):
-    """Token blocks of 16: a partial first block, exact blocks, a ragged tail; T < 3 takes part
-    of the new state from the old one."""
+    """Waves of 8 tokens handing their last rows to the next wave, work-groups of 64 tokens
+    loading their own halo: a partial first block, exact blocks and work-groups, ragged tails
+    inside and across work-groups; T < 3 takes part of the new state from the old one."""
     check(2, T, 2, 4, 64, 64, dtype, seed=700 + T)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_channels_not_a_multiple_of_the_work_group(dtype):
+    """C = 192: a work-group covers 256 channels, so a quarter of its lanes hold none."""
+    check(2, 70, 1, 1, 64, 64, dtype, seed=730)
 
 
 @pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 128), (128, 64)])
