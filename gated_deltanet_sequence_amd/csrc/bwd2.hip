@@ -1025,36 +1025,38 @@ hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t
 
 }  // namespace
 
+// Buffers whose lives do not overlap share memory.  Lives (W = written, R = read):
+//   A: prep W, fwd/bwd scans and products R;  Aq, Et, Qt, Kh, gC: prep W, scans R;
+//   Z: prep W, forward scan R;  Sn, R, U: forward scan W, products R;
+//   dS1, dU: reverse scan W, products R;  dR: reverse scan W, products and local R;
+//   dEt, dQt, dKh, dgC, dAq, dM: products W, local R;  dqh, dkh, dAl: local W, reduce R.
+// So products writes into the space of buffers last read by the scans (dEt into Et, dQt
+// into Qt, dKh into Kh, dgC into gC, dAq into Aq, dM into Z), and local into the space of
+// buffers last read by products (dqh into Sn, dkh into dS1, dAl into U).  No kernel reads
+// a buffer whose space it writes through another name.
 size_t bwd2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, Bwd2Workspace *ws) {
     const size_t NC = ((size_t)T + C - 1) / C, U = (size_t)B * Hv * NC;
     size_t off = 0;
-    auto take = [&](float **dst, size_t elems) {
-        if (dst) *dst = base ? reinterpret_cast<float *>(static_cast<char *>(base) + off) : nullptr;
+    auto take = [&](size_t elems) {
+        float *p = base ? reinterpret_cast<float *>(static_cast<char *>(base) + off) : nullptr;
         off += (elems * 4 + 255) / 256 * 256;
+        return p;
     };
     Bwd2Workspace w{};
-    take(&w.A, U * C * C);
-    take(&w.Aq, U * C * C);
-    take(&w.Et, U * C * Dk);
-    take(&w.Qt, U * C * Dk);
-    take(&w.Kh, U * C * Dk);
-    take(&w.gC, U * Dk);
-    take(&w.Z, U * C * Dv);
-    take(&w.U, U * C * Dv);
-    take(&w.R, U * C * Dv);
-    take(&w.dU, U * C * Dv);
-    take(&w.dR, U * C * Dv);
-    take(&w.Sn, U * Dk * Dv);
-    take(&w.dS1, U * Dk * Dv);
-    take(&w.dEt, U * C * Dk);
-    take(&w.dQt, U * C * Dk);
-    take(&w.dKh, U * C * Dk);
-    take(&w.dgC, U * Dk);
-    take(&w.dM, U * C * C);
-    take(&w.dAq, U * C * C);
-    take(&w.dqh, (size_t)B * T * Hv * Dk);
-    take(&w.dkh, (size_t)B * T * Hv * Dk);
-    take(&w.dAl, U * Dk);
+    w.A = take(U * C * C);
+    w.Aq = w.dAq = take(U * C * C);
+    w.Et = w.dEt = take(U * C * Dk);
+    w.Qt = w.dQt = take(U * C * Dk);
+    w.Kh = w.dKh = take(U * C * Dk);
+    w.gC = w.dgC = take(U * Dk);
+    w.Z = w.dM = take(U * C * Dv);    // dM: C x C per unit, within C x Dv (Dv >= 64 = C)
+    w.R = take(U * C * Dv);
+    w.U = w.dAl = take(U * C * Dv);   // dAl: Dk per unit
+    w.dU = take(U * C * Dv);
+    w.dR = take(U * C * Dv);
+    // dqh / dkh hold [B][T][Hv][Dk]: at most U * C * Dk floats, within S_n / dS_{n+1} (Dv >= 64 = C)
+    w.Sn = w.dqh = take(U * Dk * Dv);
+    w.dS1 = w.dkh = take(U * Dk * Dv);
     w.bytes = off;
     if (ws) *ws = w;
     return off;
