@@ -103,20 +103,31 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
     // Persistent: the work-group walks units u = (b, key head, chunk), and the
     // next unit's global loads (Q and K rows, gate logits and parameters of
     // this wave's first value head) are in flight while this unit computes.
+    // The rows stay raw 16-byte pieces until the next unit's images are
+    // written, and they are loaded without a branch: a row past the sequence
+    // end loads the tensor's first piece and is zeroed at conversion (rmask).
+    // Converting inside a bounds branch made the compiler wait for every
+    // piece right where it was loaded, one memory round trip after another.
     constexpr int NPC = C * (DK / 8) / 256;  // 8-element pieces of Q (and of K) per thread
-    f4 ql[NPC], qh[NPC], kl[NPC], kh[NPC];
+    constexpr int LPP = (int)sizeof(TIn) / 2;  // 16-byte loads per 8-element piece
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    u4v qr[NPC][LPP], kr[NPC][LPP];
+    unsigned rmask = 0;  // bit it: piece it lies in a row before the sequence end
     float a_pre = 0.f, b_pre = 0.f, alog_pre = 0.f, dtb_pre = 0.f;
     auto prefetch = [&](int u) {
         const int n = u % NC, hk = (u / NC) % Hk, bb = u / (NC * Hk);
         const int t0 = n * C;
+        rmask = 0;
 #pragma unroll
         for (int it = 0; it < NPC; ++it) {
             const int idx = tid + 256 * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-            ql[it] = qh[it] = kl[it] = kh[it] = f4{0, 0, 0, 0};
-            if (t0 + r < T) {
-                const size_t off = (((size_t)bb * T + t0 + r) * Hk + hk) * DK + c8;
-                ld8(q, off, ql[it], qh[it]);
-                ld8(k, off, kl[it], kh[it]);
+            const bool ok = t0 + r < T;
+            rmask |= ok ? 1u << it : 0u;
+            const size_t off = ok ? (((size_t)bb * T + t0 + r) * Hk + hk) * DK + c8 : 0;
+#pragma unroll
+            for (int l = 0; l < LPP; ++l) {
+                qr[it][l] = *reinterpret_cast<const u4v *>(q + off + 4 * l);
+                kr[it][l] = *reinterpret_cast<const u4v *>(k + off + 4 * l);
             }
         }
         a_pre = b_pre = 0.f;
@@ -128,6 +139,22 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
                 const size_t ia = ((size_t)bb * T + t0 + lane) * Hv + hv;
                 a_pre = a[ia];
                 b_pre = b[ia];
+            }
+        }
+    };
+    // raw piece -> 8 values (zero when the row lies past the sequence end)
+    auto unpack = [&](const u4v (&r)[LPP], bool ok, f4 &lo, f4 &hi) {
+        if constexpr (LPP == 2) {
+            lo = ok ? __builtin_bit_cast(f4, r[0]) : f4{0, 0, 0, 0};
+            hi = ok ? __builtin_bit_cast(f4, r[1]) : f4{0, 0, 0, 0};
+        } else {
+            const u4v z = ok ? r[0] : u4v{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                lo[2 * j] = __uint_as_float(z[j] << 16);
+                lo[2 * j + 1] = __uint_as_float(z[j] & 0xffff0000u);
+                hi[2 * j] = __uint_as_float(z[2 + j] << 16);
+                hi[2 * j + 1] = __uint_as_float(z[2 + j] & 0xffff0000u);
             }
         }
     };
@@ -143,10 +170,14 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
 #pragma unroll
     for (int it = 0; it < NPC; ++it) {
         const int idx = tid + 256 * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-        *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(scale * ql[it]);
-        *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(scale * qh[it]);
-        *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(kl[it]);
-        *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(kh[it]);
+        const bool ok = (rmask >> it) & 1u;
+        f4 ql, qh, kl, kh;
+        unpack(qr[it], ok, ql, qh);
+        unpack(kr[it], ok, kl, kh);
+        *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(scale * ql);
+        *reinterpret_cast<V4 *>(Qi + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(scale * qh);
+        *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8))) = mma<F32>::from_f4(kl);
+        *reinterpret_cast<V4 *>(Ki + img_index<F32>(r, DK, perm_col<F32>(c8 + 4))) = mma<F32>::from_f4(kh);
     }
     const float a_cur = a_pre, b_cur = b_pre, alog_cur = alog_pre, dtb_cur = dtb_pre;
     if (u + (int)gridDim.x < units) prefetch(u + gridDim.x);
@@ -159,7 +190,10 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
         u4v *dq = reinterpret_cast<u4v *>(qimg + ku * IMG);
         u4v *dk = reinterpret_cast<u4v *>(kimg + ku * IMG);
         constexpr int UNITS = (int)(IMG * sizeof(E) / 16);
-        for (int i = tid; i < UNITS; i += 256) {
+        static_assert(UNITS % 256 == 0, "whole 16-byte pieces per thread");
+#pragma unroll
+        for (int it = 0; it < UNITS / 256; ++it) {  // a fixed count: the compiler counts these stores
+            const int i = tid + 256 * it;
             dq[i] = src[i];
             dk[i] = src[UNITS + i];
         }
@@ -287,19 +321,19 @@ __global__ __launch_bounds__(256, F32 ? 1 : 2) void chunk_local_kernel(
         // diagonal blocks of X: lane (block bq, column c) by forward substitution,
         // column-oriented: with x = column c of X (x[r] = delta_rc to start),
         // for j = 0..14, x[r] -= L[r][j] x[j] for r > j.  Each lane keeps column
-        // c of -L in registers; L[r][j] comes from lane j of the same 16-lane
-        // row (the block) by a DPP row broadcast, so the inner step is a vector
-        // multiply-add with no LDS access.
+        // c of L in registers; L[r][j] comes from lane j of the same 16-lane
+        // row (the block) by a DPP row broadcast inside the multiply-add, so
+        // the inner step is one vector instruction with no LDS access.
         {
             const int bq = lane >> 4, c = lane & 15;
             const float *Lb = Ld(bq);
-            float nl[16], x[16];
+            float lv[16], x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                nl[r] = -Lb[r * 16 + c];
+                lv[r] = Lb[r * 16 + c];
                 x[r] = (r == c) ? 1.f : 0.f;
             }
-            subst_steps(nl, x, std::make_integer_sequence<int, 15>());
+            subst_steps(lv, x, std::make_integer_sequence<int, 15>());
 #pragma unroll
             for (int r = 0; r < 16; ++r) Xw[tri_index(bq, bq) * 256 + r * 16 + c] = x[r];
         }

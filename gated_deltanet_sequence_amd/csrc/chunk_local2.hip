@@ -378,13 +378,13 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
         // start; L[r][j] from lane j of the same 16-lane row by a DPP row broadcast
         const int bq = lane >> 4, c = lane & 15;
         const float *Lb = Ms + tri_index(bq, bq) * 256;
-        float nl[16], x[16];
+        float lv[16], x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            nl[r] = -Lb[r * 16 + c];
+            lv[r] = Lb[r * 16 + c];
             x[r] = (r == c) ? 1.f : 0.f;
         }
-        subst_steps(nl, x, std::make_integer_sequence<int, 15>());
+        subst_steps(lv, x, std::make_integer_sequence<int, 15>());
 #pragma unroll
         for (int r = 0; r < 16; ++r) Xw[tri_index(bq, bq) * 256 + r * 16 + c] = x[r];
     }

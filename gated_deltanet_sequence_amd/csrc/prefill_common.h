@@ -97,20 +97,24 @@ __device__ __forceinline__ void img_pair(const typename mma<F32>::E *X, int rowl
 __host__ __device__ constexpr int tri_index(int rt, int ct) { return rt * (rt + 1) / 2 + ct; }
 
 // One step j of the column-oriented forward substitution in a 16-lane row:
-// x[r] += (-L[r][j]) x[j] for r > j, where lane j of the row holds -L[r][j] in
-// nl[r] (DPP row_newbcast:j broadcasts it to the whole row).
+// x[r] -= L[r][j] x[j] for r > j, where lane j of the row holds L[r][j] in
+// lv[r].  One v_fmac_f32_dpp per update: its first source is taken from lane j
+// of the row (DPP row_newbcast:j) and negated by the source modifier.  The
+// compiler does not fuse a separate DPP move into the multiply-add, which
+// doubled the instruction count.  lv must come straight from LDS loads: a DPP
+// source written by a vector instruction needs two wait states that the
+// compiler cannot see inside the assembly.
 template <int J>
-__device__ __forceinline__ void subst_step(const float (&nl)[16], float (&x)[16]) {
+__device__ __forceinline__ void subst_step(const float (&lv)[16], float (&x)[16]) {
 #pragma unroll
-    for (int r = J + 1; r < 16; ++r) {
-        const float lrj = __builtin_bit_cast(
-            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, nl[r]), 0x150 + J, 0xf, 0xf, true));
-        x[r] = fmaf(lrj, x[J], x[r]);
-    }
+    for (int r = J + 1; r < 16; ++r)
+        asm("v_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+            : "+v"(x[r])
+            : "v"(lv[r]), "v"(x[J]), "i"(J));
 }
 template <int... J>
-__device__ __forceinline__ void subst_steps(const float (&nl)[16], float (&x)[16], std::integer_sequence<int, J...>) {
-    (subst_step<J>(nl, x), ...);
+__device__ __forceinline__ void subst_steps(const float (&lv)[16], float (&x)[16], std::integer_sequence<int, J...>) {
+    (subst_step<J>(lv, x), ...);
 }
 
 // Off-diagonal blocks of X = (I + L)^{-1}, 16x16 blocks, diagonal blocks already
