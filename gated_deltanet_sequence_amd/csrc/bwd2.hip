@@ -380,16 +380,25 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
         Us[C * LB];
     const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
+    // initial state: every load issued before any is used (one wait, not one per element)
     f4 S[NT];
+    if (p.S0) {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                S[x][s] = p.S0[(((size_t)bb * p.Hv + hv) * DK + 16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr];
+        }
+    } else {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) S[x] = f4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int x = 0; x < NT; ++x) {
         const int id = w * NT + x, cb = id >> 1, jb = id & 1;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int c = 16 * cb + 4 * gg + s, j = 16 * jb + rr;
-            S[x][s] = p.S0 ? p.S0[(((size_t)bb * p.Hv + hv) * DK + c) * DV + j0 + j] : 0.f;
-            Ss[c * LB + j] = S[x][s];
-        }
+        for (int s = 0; s < 4; ++s) Ss[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = S[x][s];
     }
     for (int n = 0; n < NC; ++n) {
         const size_t u = unit_of(bb, hv, n, p.Hv, NC);
@@ -469,16 +478,25 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
     const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
     const TIn *dout = static_cast<const TIn *>(p.dout);
+    // gradient of the final state: every load issued before any is used
     f4 dS[NT];
+    if (p.dST) {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                dS[x][s] = p.dST[(((size_t)bb * p.Hv + hv) * DK + 16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr];
+        }
+    } else {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) dS[x] = f4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int x = 0; x < NT; ++x) {
         const int id = w * NT + x, cb = id >> 1, jb = id & 1;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int c = 16 * cb + 4 * gg + s, j = 16 * jb + rr;
-            dS[x][s] = p.dST ? p.dST[(((size_t)bb * p.Hv + hv) * DK + c) * DV + j0 + j] : 0.f;
-            dSs[c * LB + j] = dS[x][s];
-        }
+        for (int s = 0; s < 4; ++s) dSs[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = dS[x][s];
     }
     // dO slice of chunk n: 64 rows x 32 columns, 8 per thread (rows past T read the last
     // token and are zeroed when stored)
