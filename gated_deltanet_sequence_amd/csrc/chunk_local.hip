@@ -408,13 +408,20 @@ static hipError_t launch_chunk_local_t(const PrefillArgs &p, const PrefillWorksp
     typedef typename mma<F32>::E E;
     const int NC = (p.T + C - 1) / C;
     const int units = p.B * p.Hk * NC;
-    // resident work-groups (persistent loop over units)
+    // Resident work-groups walking the units (persistent), while that gives each
+    // at most four units; beyond, one work-group per unit.  A persistent unit
+    // waits at its end for its own workspace stores (loads and stores share one
+    // counter, and the value-head loop's runtime trip count leaves the compiler
+    // only the image stores to count), which the prefetch pays for at two units
+    // per work-group (30.5 against 33.5 us at T = 4096) and stops paying for by
+    // eight (107.8 against 103.5 us at T = 16384; 813 against 757 us at two
+    // sequences of 65536 tokens).
     int dev = 0, cus = 0, per_cu = 0;
     unsigned grid = (unsigned)units;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chunk_local_kernel<F32, TIn, DK>, 256, 0) == hipSuccess &&
-        cus > 0 && per_cu > 0 && (long long)cus * per_cu < units)
+        cus > 0 && per_cu > 0 && (long long)cus * per_cu < units && units <= 4LL * cus * per_cu)
         grid = (unsigned)(cus * per_cu);
     hipLaunchKernelGGL((chunk_local_kernel<F32, TIn, DK>), dim3(grid), dim3(256), 0, s, p.B, p.T,
                        p.Hk, p.Hv, NC, p.scale, (const TIn *)p.q, (const TIn *)p.k, p.a, p.b, p.A_log, p.dt_bias,
