@@ -409,13 +409,13 @@ static hipError_t launch_chunk_local_t(const PrefillArgs &p, const PrefillWorksp
     const int NC = (p.T + C - 1) / C;
     const int units = p.B * p.Hk * NC;
     // Resident work-groups walking the units (persistent), while that gives each
-    // at most four units; beyond, one work-group per unit.  A persistent unit
-    // waits at its end for its own workspace stores (loads and stores share one
-    // counter, and the value-head loop's runtime trip count leaves the compiler
-    // only the image stores to count), which the prefetch pays for at two units
-    // per work-group (30.5 against 33.5 us at T = 4096) and stops paying for by
-    // eight (107.8 against 103.5 us at T = 16384; 813 against 757 us at two
-    // sequences of 65536 tokens).
+    // at most four units; beyond, one work-group per unit.  Measured: persistent
+    // is faster at two units per work-group (30.5 against 33.5 us at T = 4096)
+    // and slower from eight (107.8 against 103.5 us at T = 16384; 813 against
+    // 757 us at two sequences of 65536 tokens).  The persistent loop's wait for
+    // its own workspace stores (loads and stores share one counter) is not the
+    // reason: an instance with a static value-head count, whose loop waits for
+    // the loads alone, measured the same.
     int dev = 0, cus = 0, per_cu = 0;
     unsigned grid = (unsigned)units;
     if (hipGetDevice(&dev) == hipSuccess &&
