@@ -134,6 +134,23 @@ def test_bf16_full_compare():
                        init_state=True))
 
 
+def test_bf16_persistent_units_with_ragged_tail():
+    """1024 chunk-local units (2 x 16 key heads x 32 chunks) on a device holding 512 work-groups:
+    each work-group walks two units and prefetches the second while computing the first, and
+    some second units are the ragged last chunk (T = 2000 = 31 x 64 + 16), whose rows past the
+    end are loaded from a clamped address and zeroed at conversion."""
+    full_check(GDNSpec(B=2, T=2000, Hk=16, Hv=64, Dk=128, Dv=128, dtype="bf16", seed=285,
+                       init_state=True))
+
+
+def test_f32_persistent_units_with_ragged_tail():
+    """fp32, d_k = 128: 512 chunk-local units (2 x 16 key heads x 16 chunks) where the kernel's
+    registers allow one work-group per CU, so each walks two units; T = 1000 leaves a ragged
+    last chunk of 40 tokens."""
+    full_check(GDNSpec(B=2, T=1000, Hk=16, Hv=32, Dk=128, Dv=64, dtype="f32", seed=286,
+                       init_state=True))
+
+
 # The bfloat16 path runs a different scan (float16 operands, role-split work-group
 # with its own staging prologue for the first chunks): the same shape coverage.
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 129, 200])
