@@ -783,7 +783,9 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
 
     // gates of the wave's rows; the in-chunk prefix of g runs over them, then the
     // totals of the earlier row groups are added
-    float grun = 0.f, gpre[8];
+    // (the logits a and the erase gate stay in registers for the chain rule: reloading
+    // them there, inside its row-bounds branch, waited for each row's loads in turn)
+    float grun = 0.f, gpre[8], a_row[8], beta_row[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
         const int t = r0 + x, tl = min(t, L - 1);
@@ -791,8 +793,10 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
         const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
         const float on = t < L ? 1.f : 0.f;
         const float kv = io<TIn>::ld(k, kq) * on;
-        grun += -rate * softplus_fast(io<TIn>::ld(a, ka)) * LOG2E * on;
-        const float ev = sigmoid_fast(io<TIn>::ld(er, ka)) * kv;
+        a_row[x] = io<TIn>::ld(a, ka);
+        beta_row[x] = sigmoid_fast(io<TIn>::ld(er, ka));
+        grun += -rate * softplus_fast(a_row[x]) * LOG2E * on;
+        const float ev = beta_row[x] * kv;
         const float qv = p.scale * io<TIn>::ld(q, kq) * on;
         gpre[x] = grun;
         Ks[t * 64 + cl] = kv;
@@ -925,7 +929,7 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
         const int t = r0 + x;
         if (t < L) {
             const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
-            const float av = io<TIn>::ld(a, ka), beta = sigmoid_fast(io<TIn>::ld(er, ka));
+            const float av = a_row[x], beta = beta_row[x];
             const float kk = Ks[t * 64 + cl];
             const float dg = carry;  // natural-log units
             p.da[ka] = -dg * rate * sigmoid_fast(av);
