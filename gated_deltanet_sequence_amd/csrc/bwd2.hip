@@ -106,6 +106,24 @@ template <> struct In8<float> {
     }
 };
 
+// 4 consecutive input elements held raw in registers between their load and
+// their conversion to float32 (so that a phase can issue all its loads first).
+template <typename TIn> struct In4;
+template <> struct In4<bf16_t> {
+    u16x4 x;
+    __device__ __forceinline__ void load(const bf16_t *p, size_t i) {
+        x = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const uint16_t *>(p) + i);
+    }
+    __device__ __forceinline__ f4 get() const {
+        return f4{bf16_to_f32(x[0]), bf16_to_f32(x[1]), bf16_to_f32(x[2]), bf16_to_f32(x[3])};
+    }
+};
+template <> struct In4<float> {
+    f4 x;
+    __device__ __forceinline__ void load(const float *p, size_t i) { x = *reinterpret_cast<const f4 *>(p + i); }
+    __device__ __forceinline__ f4 get() const { return x; }
+};
+
 // A ROWS x COLS float32 tile (row-major, contiguous) held in registers between
 // its global load and its LDS store: the scans load the next chunk's operands
 // while computing the current one.
@@ -165,12 +183,23 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) rate[j] = -exp_fast(al[j]) * LOG2E;
         f4 run = {0, 0, 0, 0}, gr[RPT];
+        // every row's loads issued before any is used (converted in the loop below):
+        // interleaved with the arithmetic, only a few were in flight at a time
+        In4<TIn> rk[RPT], rq[RPT], ra[RPT], re[RPT];
 #pragma unroll
         for (int x = 0; x < RPT; ++x) {
-            const int t = rg * RPT + x, tl = min(t, L - 1);
+            const int tl = min(rg * RPT + x, L - 1);
             const size_t kq = (((size_t)bb * p.T + t0 + tl) * p.Hk + hk) * DK + c;
             const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
-            const f4 kk = ld4(kb, kq), qq = ld4(qb, kq), aa = ld4(ab, ka), ee = ld4(eb, ka);
+            rk[x].load(kb, kq);
+            rq[x].load(qb, kq);
+            ra[x].load(ab, ka);
+            re[x].load(eb, ka);
+        }
+#pragma unroll
+        for (int x = 0; x < RPT; ++x) {
+            const int t = rg * RPT + x;
+            const f4 kk = rk[x].get(), qq = rq[x].get(), aa = ra[x].get(), ee = re[x].get();
             const float on = t < L ? 1.f : 0.f;
             f4 ev, qv, kv;
 #pragma unroll
@@ -193,16 +222,23 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
         for (int x = 0; x < RPT; ++x) *reinterpret_cast<f4 *>(Gs + (rg * RPT + x) * LS + c) = gr[x] + off;
     }
     float *Zu = ws.Z + (size_t)u * C * DV;
+    // v and the write logits: all loads before the first store to Z (the compiler
+    // cannot move a load above a store that might alias it)
+    constexpr int ZIT = C * DV / 8 / 256;
+    In8<TIn> zv[ZIT], zw[ZIT];
 #pragma unroll
-    for (int it = 0; it < C * DV / 8 / 256; ++it) {
+    for (int it = 0; it < ZIT; ++it) {
         const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
         const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
+        zv[it].load(v, kv);
+        zw[it].load(wr, kv);
+    }
+#pragma unroll
+    for (int it = 0; it < ZIT; ++it) {
+        const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8;
         f4 vl, vh, wl, wh;
-        In8<TIn> xv, xw;
-        xv.load(v, kv);
-        xw.load(wr, kv);
-        xv.get(vl, vh);
-        xw.get(wl, wh);
+        zv[it].get(vl, vh);
+        zw[it].get(wl, wh);
         const float on = t < L ? 1.f : 0.f;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -240,14 +276,17 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     __syncthreads();
     // 4. M and Aq.  Tiles below the diagonal (bt > bi), reference row r = 16 bt:
     //    sum_c [e_t e^{G_t - G_r}] [k_i e^{G_r - G_i}].  Wave w takes tiles w, w + 4.
-    constexpr int OBT[6] = {1, 2, 2, 3, 3, 3}, OBI[6] = {0, 0, 1, 0, 1, 2};
+    // tile ti = 0..5 below the diagonal, row by row: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    // (computed: a constexpr table was placed in global memory and loaded per use)
+    auto obt = [](int ti) { return ti < 1 ? 1 : ti < 3 ? 2 : 3; };
+    auto obi = [&](int ti) { const int bt = obt(ti); return ti - bt * (bt - 1) / 2; };
     f4 mO[2], qO[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
         mO[x] = qO[x] = f4{0, 0, 0, 0};
         const int ti = w + 4 * x;
         if (ti < 6) {
-            const int bt = OBT[ti], bi = OBI[ti], r = 16 * bt, t = 16 * bt + rr, i = 16 * bi + rr;
+            const int bt = obt(ti), bi = obi(ti), r = 16 * bt, t = 16 * bt + rr, i = 16 * bi + rr;
 #pragma unroll 8
             for (int c0 = 0; c0 < DK; c0 += 4) {
                 const int c = c0 + gg;
@@ -306,7 +345,7 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
         for (int x = 0; x < 2; ++x) {
             const int ti = w + 4 * x;
             if (ti < 6) {
-                const int bt = OBT[ti], bi = OBI[ti];
+                const int bt = obt(ti), bi = obi(ti);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const int t = 16 * bt + 4 * gg + s, i = 16 * bi + rr;
