@@ -693,6 +693,12 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
             *reinterpret_cast<f4 *>(b2 + t * LV + j + 4) = hi * on;
         }
     }
+    // phase 2's inputs, in flight during phase 1's products (one work-group per CU:
+    // nothing else would hide a phase's loads)
+    RegTile<DK, DV> nS1;
+    RegTile<C, DV> nU;
+    nS1.load(ws.dS1 + (size_t)u * DK * DV);
+    nU.load(ws.U + uC * DV);
     __syncthreads();
     for (int cb = 0; cb < DK / 16; ++cb) {
         f4 e = {0, 0, 0, 0}, q = {0, 0, 0, 0};
@@ -719,8 +725,14 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     }
     __syncthreads();
     // phase 2: dKh = U dS1^T, dAq = tril(dO U^T)
-    lds_load<DK, DV, LV>(r1, ws.dS1 + (size_t)u * DK * DV);
-    lds_load<C, DV, LV>(b1, ws.U + uC * DV);
+    nS1.template store<LV>(r1);
+    nU.template store<LV>(b1);
+    // phase 3's inputs, in flight during phase 2's products (A once, for both copies)
+    RegTile<C, DV> nR, ndU;
+    RegTile<C, C> nA;
+    nR.load(ws.R + uC * DV);
+    ndU.load(ws.dU + uC * DV);
+    nA.load(ws.A + uC * C);
     __syncthreads();
     for (int cb = 0; cb < DK / 16; ++cb) {
         f4 acc = {0, 0, 0, 0};
@@ -741,9 +753,9 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     __syncthreads();
     // phase 3: dA = dU R^T; X = A^T dA; dM = -strict_tril(X A^T)
     float *dAs = r1, *A80 = r1 + C * 80, *A68 = b1, *Xs = b2;
-    lds_load<C, DV, LV>(b1, ws.R + uC * DV);
-    lds_load<C, DV, LV>(b2, ws.dU + uC * DV);
-    lds_load<C, C, 80>(A80, ws.A + uC * C);
+    nR.template store<LV>(b1);
+    ndU.template store<LV>(b2);
+    nA.template store<80>(A80);
     __syncthreads();
     f4 dA[4];
 #pragma unroll
@@ -756,7 +768,7 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
         for (int s = 0; s < 4; ++s) dAs[(16 * w + 4 * gg + s) * 80 + 16 * ib + rr] = dA[ib][s];
-    lds_load<C, C, 68>(A68, ws.A + uC * C);
+    nA.template store<68>(A68);
     __syncthreads();
     // X[i][s] = sum_t A[t][i] dA[t][s] (A[t][i] = 0 for t < i): rows i of block w
 #pragma unroll
