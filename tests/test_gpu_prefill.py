@@ -143,6 +143,14 @@ def test_bf16_persistent_units_with_ragged_tail():
                        init_state=True))
 
 
+def test_bf16_one_unit_per_work_group_with_ragged_tail():
+    """2064 chunk-local units (16 key heads x 129 chunks, T = 8200 = 128 x 64 + 8): more than
+    four per resident work-group, so each work-group takes one unit; the last chunk holds 8
+    tokens."""
+    full_check(GDNSpec(B=1, T=8200, Hk=16, Hv=64, Dk=128, Dv=128, dtype="bf16", seed=287,
+                       init_state=True))
+
+
 def test_f32_persistent_units_with_ragged_tail():
     """fp32, d_k = 128: 512 chunk-local units (2 x 16 key heads x 16 chunks) where the kernel's
     registers allow one work-group per CU, so each walks two units; T = 1000 leaves a ragged
