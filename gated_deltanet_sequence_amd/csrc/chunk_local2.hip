@@ -46,7 +46,8 @@ size_t gdn2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, bool f32, voi
     const size_t oA = off;  off = align256(off + vunits * NPAIR * 64 * 8 * esz);
     const size_t oAq = off; off = align256(off + vunits * NPAIR * 64 * 8 * esz);
     const size_t oG = off;  off = align256(off + vunits * Dk * 4);
-    const size_t oZ = off;  off = align256(off + (size_t)B * T * Hv * Dv * esz);
+    // Z = sigmoid(write) v: float32 only (the bfloat16 scan forms it from v and write)
+    const size_t oZ = off;  off = align256(off + (f32 ? (size_t)B * T * Hv * Dv * esz : 0));
     if (ws) {
         char *p = (char *)base;
         ws->eimg = p + oE;
@@ -56,7 +57,7 @@ size_t gdn2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, bool f32, voi
         ws->apair = p + oA;
         ws->qpair = p + oAq;
         ws->gc = (float *)(p + oG);
-        ws->z = p + oZ;
+        ws->z = f32 ? p + oZ : nullptr;
         ws->bytes = off;
     }
     return off;
@@ -113,10 +114,10 @@ template <int CTRL> __device__ __forceinline__ float quad_perm(float x) {
 template <int DK, int DV>
 __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
     int T, int Hk, int Hv, int NC, float scale, const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
-    const bf16_t *__restrict__ v, const bf16_t *__restrict__ a, const bf16_t *__restrict__ erase,
-    const bf16_t *__restrict__ write, const float *__restrict__ A_log, _Float16 *__restrict__ eimg,
+    const bf16_t *__restrict__ a, const bf16_t *__restrict__ erase, const float *__restrict__ A_log,
+    _Float16 *__restrict__ eimg,
     _Float16 *__restrict__ khimg, _Float16 *__restrict__ qimg, _Float16 *__restrict__ apair,
-    _Float16 *__restrict__ qpair, float *__restrict__ gc, _Float16 *__restrict__ z) {
+    _Float16 *__restrict__ qpair, float *__restrict__ gc) {
     typedef Cl2Cfg<DK> CF;
     constexpr int NKQ = CF::NKQ;
     __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
@@ -132,15 +133,15 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
     const size_t vu = ((size_t)bb * Hv + hv) * NC + n;
     constexpr float LOG2E = 1.4426950408889634f;
 
-    // ---- 1. gates and key-side operands of the chunk into LDS (zero past T);
-    //         z = sigmoid(write) v to the workspace.  Every load of the phase
-    //         is issued before any arithmetic; a thread sees the same 8
-    //         channels in each of its rows (256 is a multiple of DK / 8 and
-    //         DV / 8), so their decay rates exp(A_log) are loaded once.  g is
+    // ---- 1. gates and key-side operands of the chunk into LDS (zero past T)
+    //         (z = sigmoid(write) v is formed by the scan's state waves).  Every
+    //         load of the phase is issued before any arithmetic; a thread sees
+    //         the same 8 channels in each of its rows (256 is a multiple of
+    //         DK / 8), so their decay rates exp(A_log) are loaded once.  g is
     //         kept in log2 units (g log2 e) so that every decay is one exp2.
-    constexpr int PK = C * (DK / 8) / 256, PV = C * (DV / 8) / 256;
-    const int c8k = (tid % (DK / 8)) * 8, c8v = (tid % (DV / 8)) * 8;
-    u16x8 rq[PK], rk[PK], ra[PK], re[PK], rv[PV], rw[PV];
+    constexpr int PK = C * (DK / 8) / 256;
+    const int c8k = (tid % (DK / 8)) * 8;
+    u16x8 rq[PK], rk[PK], ra[PK], re[PK];
     f4 Alo, Ahi;
     ld8(A_log, (size_t)hv * DK + c8k, Alo, Ahi);
 #pragma unroll
@@ -154,16 +155,6 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
             rk[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(k) + kq);
             ra[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(a) + ka);
             re[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(erase) + ka);
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < PV; ++it) {
-        const int t = t0 + (tid + 256 * it) / (DV / 8);
-        rv[it] = rw[it] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (t < T) {
-            const size_t kv = (((size_t)bb * T + t) * Hv + hv) * DV + c8v;
-            rv[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(v) + kv);
-            rw[it] = *reinterpret_cast<const u16x8 *>(reinterpret_cast<const uint16_t *>(write) + kv);
         }
     }
     float rate[8];  // exp(A_log) log2 e
@@ -187,16 +178,6 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
         *reinterpret_cast<h8 *>(El + hsw<DK>(r, c8k)) = eh;
         *reinterpret_cast<h8 *>(Kl + hsw<DK>(r, c8k)) = kh;
         *reinterpret_cast<h8 *>(Ql + hsw<DK>(r, c8k)) = qh;
-    }
-#pragma unroll
-    for (int it = 0; it < PV; ++it) {
-        const int t = t0 + (tid + 256 * it) / (DV / 8);
-        if (t < T) {
-            h8 zh;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) zh[j] = (_Float16)(sigmoid_fast(bf16_to_f32(rw[it][j])) * bf16_to_f32(rv[it][j]));
-            *reinterpret_cast<h8 *>(z + (((size_t)bb * T + t) * Hv + hv) * DV + c8v) = zh;
-        }
     }
     __syncthreads();
 
@@ -434,10 +415,10 @@ static hipError_t launch_cl2_t(const Gdn2Args &p, const Gdn2Workspace &ws, hipSt
     const int NC = (p.T + C - 1) / C;
     const unsigned units = (unsigned)(p.B * p.Hv * NC);
     hipLaunchKernelGGL((chunk_local2_kernel<DK, DV>), dim3(units), dim3(256), 0, s, p.T, p.Hk, p.Hv, NC, p.scale,
-                       (const bf16_t *)p.q, (const bf16_t *)p.k, (const bf16_t *)p.v, (const bf16_t *)p.a,
-                       (const bf16_t *)p.erase, (const bf16_t *)p.write, p.A_log, (_Float16 *)ws.eimg,
+                       (const bf16_t *)p.q, (const bf16_t *)p.k, (const bf16_t *)p.a,
+                       (const bf16_t *)p.erase, p.A_log, (_Float16 *)ws.eimg,
                        (_Float16 *)ws.khimg, (_Float16 *)ws.qimg, (_Float16 *)ws.apair, (_Float16 *)ws.qpair,
-                       ws.gc, (_Float16 *)ws.z);
+                       ws.gc);
     return hipGetLastError();
 }
 

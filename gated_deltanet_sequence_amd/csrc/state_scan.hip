@@ -410,18 +410,21 @@ struct SplitCfg {
     // for the channel-wise decay e^{G_C} per key channel; the output waves'
     // gamma record (none for the channel-wise decay, folded into its Q image)
     static constexpr int STK_BYTES = G2 ? DK * 4 : C * 8, OTK_BYTES = G2 ? 0 : C * 8;
-    static constexpr int TILE_BYTES = C * NCOL * 2;                // V (or Z) tile, 16-bit elements
+    static constexpr int TILE_BYTES = C * NCOL * 2;                // V (or write-logit) tile, bfloat16
     static constexpr int VSPR = NCOL * 2 / 16;                     // 16-byte slots per V row
     static constexpr int VEPS = 8;                                 // elements per slot
     // State-wave inputs: the image for P = K S (K; Et for the channel-wise
     // decay), the image of the state update's K^T operands (the same K image;
-    // a separate Kh image for the channel-wise decay), V (Z), Ae, the record.
+    // a separate Kh image for the channel-wise decay), V (and for the
+    // channel-wise decay the write-gate logits: z = sigmoid(write) v is formed
+    // by the state waves), Ae, the record.
     // Output-wave inputs: the Q image, Ao, gamma.  Every stream has NSB (NOB)
     // LDS buffers, issued NSB-1 (NOB-1) chunks ahead: 3 for the scalar decay,
     // 2 for the channel-wise decay (its two state images fill LDS).  The
     // hand-over is single-buffered (two barriers per chunk).
     static constexpr int S_K = 0, S_KH = G2 ? S_K + IMG_BYTES : S_K, S_V = S_KH + IMG_BYTES,
-                         S_A = S_V + TILE_BYTES, S_TK = S_A + FRAG_BYTES, S_BUF = S_TK + STK_BYTES;
+                         S_W = S_V + TILE_BYTES, S_A = S_W + (G2 ? TILE_BYTES : 0), S_TK = S_A + FRAG_BYTES,
+                         S_BUF = S_TK + STK_BYTES;
     static constexpr int O_Q = 0, O_F = O_Q + IMG_BYTES, O_TK = O_F + FRAG_BYTES, O_BUF = O_TK + OTK_BYTES;
     // hand-over: S (d_k x 16) and R' (64 x 16) of each column tile as operand pairs, 1 KB each
     static constexpr int X_S = 0, X_R = NT * NKQ * 1024, X_BUF = X_R + NT * 2 * 1024;
@@ -433,7 +436,7 @@ struct SplitCfg {
     static constexpr int IMG_UNITS = IMG_BYTES / 1024, FRAG_UNITS = FRAG_BYTES / 1024,
                          TILE_UNITS = TILE_BYTES / 1024;
     // loads per chunk of the state loader and of the output loader
-    static constexpr int STATE_LOADS = IMG_UNITS * (G2 ? 2 : 1) + TILE_UNITS + FRAG_UNITS + 1,
+    static constexpr int STATE_LOADS = (IMG_UNITS + TILE_UNITS) * (G2 ? 2 : 1) + FRAG_UNITS + 1,
                          OUT_LOADS = IMG_UNITS + FRAG_UNITS + (G2 ? 0 : 1);
     static_assert((NSB - 1) * STATE_LOADS < 64 && (NOB - 1) * OUT_LOADS < 64, "vmcnt");
     static_assert(VSPR >= 4 && (VSPR & (VSPR - 1)) == 0, "V slots");
@@ -448,7 +451,7 @@ struct SplitCfg {
 template <typename TIn, int DK, int NL, bool G2, int NT>
 struct SplitLoader {
     typedef SplitCfg<TIn, DK, NL, G2, NT> CF;
-    __amdgpu_buffer_rsrc_t vres, rq, rk, rkh, ra, rf, rtk, rgc;
+    __amdgpu_buffer_rsrc_t vres, wres, rq, rk, rkh, ra, rf, rtk, rgc;
     int lane;
     unsigned vcol;  // element offset of this group's first V column in a token row
     unsigned vrow;  // elements per token row of V (Hv * d_v)
@@ -479,10 +482,11 @@ struct SplitLoader {
         if (lane < CF::STK_BYTES / 16) copy(G2 ? rgc : rtk, base + CF::S_TK, n * CF::STK_BYTES);
     }
     // the channel-wise decay's state-wave inputs in two portions by the time
-    // the state waves read them: "early" (the Et image, Z, A; read one chunk
-    // ahead, during the previous chunk's state update) and "late" (the Kh
-    // image and e^{G_C}; read during the chunk's own phases A and B)
-    static constexpr int EARLY_LOADS = CF::IMG_UNITS + CF::TILE_UNITS + CF::FRAG_UNITS,
+    // the state waves read them: "early" (the Et image, V and the write
+    // logits, A; read one chunk ahead, during the previous chunk's state
+    // update) and "late" (the Kh image and e^{G_C}; read during the chunk's own
+    // phases A and B)
+    static constexpr int EARLY_LOADS = CF::IMG_UNITS + 2 * CF::TILE_UNITS + CF::FRAG_UNITS,
                          LATE_LOADS = CF::IMG_UNITS + 1;
     __device__ __forceinline__ void stage_early(char *smem, int n, int buf) const {
         char *base = smem + CF::OFF_S + buf * CF::S_BUF;
@@ -496,6 +500,7 @@ struct SplitLoader {
             const int piece = (slot % CF::VSPR) ^ ((row >> 2) & (CF::VSPR - 1));
             const unsigned voff = ((unsigned)(n * C + row) * vrow + vcol + piece * CF::VEPS) * (unsigned)sizeof(TIn);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void_t *)(base + CF::S_V + u * 1024), 16, (int)voff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)(base + CF::S_W + u * 1024), 16, (int)voff, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < CF::FRAG_UNITS; ++u) copy(ra, base + CF::S_A + u * 1024, fo + u * 1024);
@@ -522,8 +527,8 @@ struct SplitLoader {
 
 template <typename TIn, int DK, int DV, int NL, bool G2, int NT_>
 __global__ __launch_bounds__(64 * (NT_ + 2 + NL)) void scan_split_kernel(
-    int T, int Hk, int Hv, int NC, const void *__restrict__ v, const float *__restrict__ tok,
-    const _Float16 *__restrict__ apair, const _Float16 *__restrict__ qpair,
+    int T, int Hk, int Hv, int NC, const void *__restrict__ v, const void *__restrict__ wlog,
+    const float *__restrict__ tok, const _Float16 *__restrict__ apair, const _Float16 *__restrict__ qpair,
     const _Float16 *__restrict__ qimg, const _Float16 *__restrict__ kimg,
     const _Float16 *__restrict__ khimg, const float *__restrict__ gcrec,
     const float *__restrict__ S0, TIn *__restrict__ out, float *__restrict__ ST) {
@@ -563,6 +568,7 @@ __global__ __launch_bounds__(64 * (NT_ + 2 + NL)) void scan_split_kernel(
         const size_t iu0 = G2 ? vu0 : ku0;  // images per value head (channel-wise decay) or per key head
         SplitLoader<TIn, DK, NL, G2, NT> ld;
         ld.vres = rsrc((const char *)v + (size_t)bb * seq_elems * 2, seq_elems * 2);
+        if constexpr (G2) ld.wres = rsrc((const char *)wlog + (size_t)bb * seq_elems * 2, seq_elems * 2);
         ld.rq = rsrc(qimg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
         ld.rk = rsrc(kimg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
         if constexpr (G2) ld.rkh = rsrc(khimg + iu0 * C * DK, (size_t)NC * CF::IMG_BYTES);
@@ -809,11 +815,11 @@ __global__ __launch_bounds__(64 * (NT_ + 2 + NL)) void scan_split_kernel(
     // (after the barrier that publishes chunk n): NRD separate reads.  (The
     // channel-wise e^{G_C} per state row is read in phase B, where it is used.)
     h8 kf[NKQ][4];
-    s4 vt[4];
+    s4 vt[4], wt[4];  // V and (channel-wise decay) write-logit columns
     f4 ga[4];  // gamma of rows 16r + 4g + i (scalar decay)
     float gC;  // gamma_C (scalar decay)
     h8 afr[NPAIR];
-    constexpr int NRD = 4 * NKQ + 4 + (G2 ? 0 : 4 + 1) + NPAIR;
+    constexpr int NRD = 4 * NKQ + 4 + (G2 ? 4 : 4 + 1) + NPAIR;
     auto read_item = [&](int sbi, int it) {  // sbi: state buffer of the chunk
         const char *base = smem + CF::OFF_S + sbi * CF::S_BUF;
         const float *Tq = reinterpret_cast<const float *>(base + CF::S_TK);
@@ -822,8 +828,12 @@ __global__ __launch_bounds__(64 * (NT_ + 2 + NL)) void scan_split_kernel(
         } else if ((it -= 4 * NKQ) < 4) {
             vt[it] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + CF::S_V + vt_off[it]));
         } else if (G2) {
-            it -= 4;
-            afr[it] = *reinterpret_cast<const h8 *>(reinterpret_cast<const E *>(base + CF::S_A) + lane * 8 + it * 512);
+            if ((it -= 4) < 4) {
+                wt[it] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(base + CF::S_W + vt_off[it]));
+            } else {
+                it -= 4;
+                afr[it] = *reinterpret_cast<const h8 *>(reinterpret_cast<const E *>(base + CF::S_A) + lane * 8 + it * 512);
+            }
         } else if ((it -= 4) < 4) {
             ga[it] = *reinterpret_cast<const f4 *>(Tq + 16 * it + 4 * g);
         } else if ((it -= 4) < 1) {
@@ -889,8 +899,10 @@ __global__ __launch_bounds__(64 * (NT_ + 2 + NL)) void scan_split_kernel(
         // (row tiles 2q, 2q+1 form operand pair q, handed over as one 1 KB block)
         auto resid = [&](int rr) {
             f4 x;
-            if constexpr (G2) {  // Z (float16) - Et S; the whole 4-vector is reinterpreted
-                x = __builtin_convertvector(__builtin_bit_cast(h4, vt[rr]), f4);
+            if constexpr (G2) {  // z - Et S with z = sigmoid(write) v (bfloat16 inputs)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    x[i] = bf16_to_f32((uint16_t)vt[rr][i]) * sigmoid_fast(bf16_to_f32((uint16_t)wt[rr][i]));
                 Rb[rr] = to_h4(x - P[rr]);
             } else {  // V (bfloat16) - gamma K S
 #pragma unroll
@@ -1003,13 +1015,15 @@ static hipError_t launch_scan_t(const PrefillArgs &p, const PrefillWorkspace &ws
             typedef SplitCfg<TIn, DK, NL, false, 4> CF4;
             const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / CF4::NCOL));
             hipLaunchKernelGGL((scan_split_kernel<TIn, DK, DV, NL, false, 4>), dim3(blocks), dim3(64 * (4 + 2 + NL)),
-                               0, s, p.T, p.Hk, p.Hv, NC, p.v, ws.tok, (const E *)ws.apair, (const E *)ws.qpair,
+                               0, s, p.T, p.Hk, p.Hv, NC, p.v, (const void *)nullptr, ws.tok, (const E *)ws.apair,
+                               (const E *)ws.qpair,
                                (const E *)ws.qimg, (const E *)ws.kimg, (const E *)nullptr, (const float *)nullptr,
                                p.S0, (TIn *)p.out, p.ST);
         } else {
             const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<TIn, DK, NL, false, 2>::NCOL));
             hipLaunchKernelGGL((scan_split_kernel<TIn, DK, DV, NL, false, 2>), dim3(blocks), dim3(64 * (2 + 2 + NL)),
-                               0, s, p.T, p.Hk, p.Hv, NC, p.v, ws.tok, (const E *)ws.apair, (const E *)ws.qpair,
+                               0, s, p.T, p.Hk, p.Hv, NC, p.v, (const void *)nullptr, ws.tok, (const E *)ws.apair,
+                               (const E *)ws.qpair,
                                (const E *)ws.qimg, (const E *)ws.kimg, (const E *)nullptr, (const float *)nullptr,
                                p.S0, (TIn *)p.out, p.ST);
         }
@@ -1047,7 +1061,7 @@ static hipError_t launch_scan2_t(const Gdn2Args &p, const Gdn2Workspace &ws, hip
     const int NC = (p.T + C - 1) / C;
     const unsigned blocks = (unsigned)(p.B * p.Hv * (DV / SplitCfg<bf16_t, DK, NL, true, 2>::NCOL));
     hipLaunchKernelGGL((scan_split_kernel<bf16_t, DK, DV, NL, true, 2>), dim3(blocks), dim3(64 * (2 + 2 + NL)), 0, s,
-                       p.T, p.Hk, p.Hv, NC, (const void *)ws.z, (const float *)nullptr,
+                       p.T, p.Hk, p.Hv, NC, p.v, p.write, (const float *)nullptr,
                        (const _Float16 *)ws.apair, (const _Float16 *)ws.qpair, (const _Float16 *)ws.qimg,
                        (const _Float16 *)ws.eimg, (const _Float16 *)ws.khimg, ws.gc, p.S0, (bf16_t *)p.out, p.ST);
     return hipGetLastError();
