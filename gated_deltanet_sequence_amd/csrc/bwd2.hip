@@ -124,6 +124,19 @@ template <> struct In4<float> {
     __device__ __forceinline__ f4 get() const { return x; }
 };
 
+// One input element held raw in registers between its load and its use.
+template <typename TIn> struct In1;
+template <> struct In1<bf16_t> {
+    uint16_t x;
+    __device__ __forceinline__ void load(const bf16_t *p, size_t i) { x = reinterpret_cast<const uint16_t *>(p)[i]; }
+    __device__ __forceinline__ float get() const { return bf16_to_f32(x); }
+};
+template <> struct In1<float> {
+    float x;
+    __device__ __forceinline__ void load(const float *p, size_t i) { x = p[i]; }
+    __device__ __forceinline__ float get() const { return x; }
+};
+
 // A ROWS x COLS float32 tile (row-major, contiguous) held in registers between
 // its global load and its LDS store: the scans load the next chunk's operands
 // while computing the current one.
@@ -165,9 +178,9 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv), hk = hv / (p.Hv / p.Hk);
     const int t0 = n * C, L = min(C, p.T - t0);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4;
-    const TIn *v = static_cast<const TIn *>(p.v), *wr = static_cast<const TIn *>(p.write);
 
-    // 1. gates: G (log2 units, 0 past T), e = sigmoid(erase) k, qs = scale q, k; z to the workspace.
+    // 1. gates: G (log2 units, 0 past T), e = sigmoid(erase) k, qs = scale q, k (z = sigmoid(write) v
+    //    is formed by the forward scan from the inputs).
     //    Thread = (4 channels, a group of RPT consecutive rows); rows past T read the last
     //    token (L >= 1) and are zeroed, so every load is unconditional.  The in-chunk prefix
     //    of g is taken over the thread's rows, then the totals of the earlier row groups
@@ -220,33 +233,6 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
         for (int x = 0; x < rg; ++x) off += *reinterpret_cast<const f4 *>(tot + x * DK + c);
 #pragma unroll
         for (int x = 0; x < RPT; ++x) *reinterpret_cast<f4 *>(Gs + (rg * RPT + x) * LS + c) = gr[x] + off;
-    }
-    float *Zu = ws.Z + (size_t)u * C * DV;
-    // v and the write logits: all loads before the first store to Z (the compiler
-    // cannot move a load above a store that might alias it)
-    constexpr int ZIT = C * DV / 8 / 256;
-    In8<TIn> zv[ZIT], zw[ZIT];
-#pragma unroll
-    for (int it = 0; it < ZIT; ++it) {
-        const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
-        const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
-        zv[it].load(v, kv);
-        zw[it].load(wr, kv);
-    }
-#pragma unroll
-    for (int it = 0; it < ZIT; ++it) {
-        const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8;
-        f4 vl, vh, wl, wh;
-        zv[it].get(vl, vh);
-        zw[it].get(wl, wh);
-        const float on = t < L ? 1.f : 0.f;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            vl[x] = sigmoid_fast(wl[x]) * vl[x] * on;
-            vh[x] = sigmoid_fast(wh[x]) * vh[x] * on;
-        }
-        *reinterpret_cast<f4 *>(Zu + t * DV + j) = vl;
-        *reinterpret_cast<f4 *>(Zu + t * DV + j + 4) = vh;
     }
     __syncthreads();
     // 3. images, gamma_C and the diagonal of Aq (q_t . k_t, no decay)
@@ -412,7 +398,7 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
 // g2b_fwd_scan: one work-group per (sequence, value head, 32 value columns);
 // wave w holds the state tiles (c-blocks 2w', j-blocks) as MFMA accumulators.
 // ---------------------------------------------------------------------------
-template <int DK, int DV>
+template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws) {
     constexpr int LE = DK + 4, LK = DK + 16, LA = 68, LB = 48, NS = DV / 32, NT = DK / 32;
     __shared__ __attribute__((aligned(16))) float Ets[C * LE], Khs[C * LK], As[C * LA], Ss[DK * LB], Rs[C * LB],
@@ -439,6 +425,23 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
 #pragma unroll
         for (int s = 0; s < 4; ++s) Ss[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = S[x][s];
     }
+    // this lane's v and write-logit elements of chunk m (rows past T read the last
+    // token and are zeroed at use): loaded one chunk ahead, raw, for z = sigmoid(write) v
+    const TIn *vin = static_cast<const TIn *>(p.v), *win = static_cast<const TIn *>(p.write);
+    In1<TIn> zv[2][4], zw[2][4];
+    auto load_z = [&](int m) {
+        const int tm = m * C, Lm = min(C, p.T - tm);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int t = min(16 * w + 4 * gg + s, Lm - 1);
+                const size_t kv = (((size_t)bb * p.T + tm + t) * p.Hv + hv) * DV + j0 + 16 * jb + rr;
+                zv[jb][s].load(vin, kv);
+                zw[jb][s].load(win, kv);
+            }
+    };
+    if (NC > 0) load_z(0);
     for (int n = 0; n < NC; ++n) {
         const size_t u = unit_of(bb, hv, n, p.Hv, NC);
         float *Snu = ws.Sn + u * DK * DV;
@@ -448,13 +451,14 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
 #pragma unroll
             for (int s = 0; s < 4; ++s) Snu[(16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = S[x][s];
         }
-        // this lane's Z elements and decay factors, loaded ahead of the staging
-        const float *Zu = ws.Z + u * C * DV, *gCu = ws.gC + u * DK;
+        const float *gCu = ws.gC + u * DK;
+        const int L = min(C, p.T - n * C);
         float zr[2][4], gcr[NT][4];
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) zr[jb][s] = Zu[(16 * w + 4 * gg + s) * DV + j0 + 16 * jb + rr];
+            for (int s = 0; s < 4; ++s)
+                zr[jb][s] = zv[jb][s].get() * sigmoid_fast(zw[jb][s].get()) * (16 * w + 4 * gg + s < L ? 1.f : 0.f);
 #pragma unroll
         for (int x = 0; x < NT; ++x)
 #pragma unroll
@@ -462,6 +466,9 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
         lds_load<C, DK, LE>(Ets, ws.Et + u * C * DK);
         lds_load<C, DK, LK>(Khs, ws.Kh + u * C * DK);
         lds_load<C, C, LA>(As, ws.A + u * C * C);
+        // the next chunk's z inputs: issued after the tiles' loads (which wait for every
+        // load issued before them), in flight during this chunk's products
+        if (n + 1 < NC) load_z(n + 1);
         __syncthreads();
         // R = Z - Et S (rows of block w)
         float *Ru = ws.R + u * C * DV, *Uu = ws.U + u * C * DV;
@@ -1081,7 +1088,7 @@ hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t
     rec(0);
     hipLaunchKernelGGL((g2b_prep<TIn, DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
     rec(1);
-    hipLaunchKernelGGL((g2b_fwd_scan<DK, DV>), dim3(slices), dim3(256), 0, s, p, ws);
+    hipLaunchKernelGGL((g2b_fwd_scan<TIn, DK, DV>), dim3(slices), dim3(256), 0, s, p, ws);
     rec(2);
     hipLaunchKernelGGL((g2b_bwd_scan<TIn, DK, DV>), dim3(slices), dim3(256), 0, s, p, ws);
     rec(3);
@@ -1122,7 +1129,7 @@ size_t bwd2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, B
     w.Qt = w.dQt = take(U * C * Dk);
     w.Kh = w.dKh = take(U * C * Dk);
     w.gC = w.dgC = take(U * Dk);
-    w.Z = w.dM = take(U * C * Dv);    // dM: C x C per unit, within C x Dv (Dv >= 64 = C)
+    w.dM = take(U * C * C);
     w.R = take(U * C * Dv);
     w.U = w.dAl = take(U * C * Dv);   // dAl: Dk per unit
     w.dU = take(U * C * Dv);

@@ -78,7 +78,7 @@ struct Bwd2Workspace {
     float *A, *Aq;                 // [U][64][64]: (I + M)^{-1}; A_qk (scale folded into q)
     float *Et, *Qt, *Kh;           // [U][64][Dk]: e^{G} e, e^{G} scale q, e^{G_C - G} k
     float *gC;                     // [U][Dk]: e^{G_C}
-    float *Z, *U, *R, *dU, *dR;    // [U][64][Dv]
+    float *U, *R, *dU, *dR;        // [U][64][Dv]
     float *Sn, *dS1;               // [U][Dk][Dv]: state before the chunk; its gradient after
     float *dEt, *dQt, *dKh;        // [U][64][Dk]
     float *dgC;                    // [U][Dk]

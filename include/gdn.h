@@ -188,7 +188,7 @@ gdn_status gdn2_chunk_fwd(const gdn_dims *d, const void *q, const void *k, const
  *                   so zero when B == 0 or T == 0 (it is written then too)
  *   d_initial_state [B,Hv,Dk,Dv] float32 (written), or NULL to skip it
  *   workspace       device scratch of at least gdn2_chunk_bwd_workspace_bytes(d)
- *                   bytes, 256-byte aligned (about 0.42 MB per (sequence, value
+ *                   bytes, 256-byte aligned (about 0.41 MB per (sequence, value
  *                   head, 64 tokens) at Dk = Dv = 128: the forward is recomputed
  *                   in float32 and its per-chunk states are kept).
  * All arithmetic is float32; the inputs and d_out are bfloat16 or float32

@@ -428,9 +428,9 @@ def test_bwd2_workspace_bytes():
     units = 64 * 128
     # per unit, float32, with the gradients written into the space of buffers already read
     # for the last time: A, A_qk | dA_qk (64 x 64); Et | dEt, Qt | dQt, Kh | dKh (64 x Dk);
-    # Z | dM, R, U | dA_log part, dU, dR (64 x Dv); S_n | dq, dS_{n+1} | dk (Dk x Dv; dq and dk
-    # per value head [B,T,Hv,Dk] fit there); e^{G_C} | its gradient (Dk)
-    need = units * 4 * (2 * 64 * 64 + 3 * 64 * 128 + 5 * 64 * 128 + 2 * 128 * 128 + 128)
+    # dM (64 x 64); R, U | dA_log part, dU, dR (64 x Dv); S_n | dq, dS_{n+1} | dk (Dk x Dv; dq
+    # and dk per value head [B,T,Hv,Dk] fit there); e^{G_C} | its gradient (Dk)
+    need = units * 4 * (3 * 64 * 64 + 3 * 64 * 128 + 4 * 64 * 128 + 2 * 128 * 128 + 128)
     assert need <= n < need + 13 * 256
     assert n < 3.5e9
     # float32 inputs: the same float32 workspace
