@@ -838,6 +838,10 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
         pdK[x] = ws.dKh[ub + (r0 + x) * DK + c];
     }
     const float pgC = ws.dgC[(size_t)u * DK + c];
+    // dM and dA_qk tiles, loaded with the rest and stored to LDS after the gates
+    RegTile<C, C, LOCAL_NT> rM, rAq;
+    rM.load(ws.dM + (size_t)u * C * C);
+    rAq.load(ws.dAq + (size_t)u * C * C);
 
     // gates of the wave's rows; the in-chunk prefix of g runs over them, then the
     // totals of the earlier row groups are added
@@ -862,8 +866,8 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
         Qs[t * 64 + cl] = qv;
     }
     blk[w * 64 + cl] = grun;
-    lds_load<C, C, C, LOCAL_NT>(dMs, ws.dM + (size_t)u * C * C);
-    lds_load<C, C, C, LOCAL_NT>(dAqs, ws.dAq + (size_t)u * C * C);
+    rM.template store<C>(dMs);
+    rAq.template store<C>(dAqs);
     __syncthreads();
     {
         float off = 0.f;
@@ -1009,17 +1013,27 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
     if (cg == 0) {
         const TIn *v = static_cast<const TIn *>(p.v), *wr = static_cast<const TIn *>(p.write);
         const float *dRu = ws.dR + (size_t)u * C * DV;
+        // every load of the loop first (the stores to dv and d_write could alias them)
+        constexpr int NIT = C * DV / 8 / LOCAL_NT;
+        In8<TIn> xv[NIT], xw[NIT];
+        f4 dzl[NIT][2];
 #pragma unroll
-        for (int it = 0; it < C * DV / 8 / LOCAL_NT; ++it) {
+        for (int it = 0; it < NIT; ++it) {
+            const int i = tid + LOCAL_NT * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
+            const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
+            xv[it].load(v, kv);
+            xw[it].load(wr, kv);
+            dzl[it][0] = *reinterpret_cast<const f4 *>(dRu + t * DV + j);
+            dzl[it][1] = *reinterpret_cast<const f4 *>(dRu + t * DV + j + 4);
+        }
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
             const int i = tid + LOCAL_NT * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
             const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
             f4 vv[2], om[2];
-            In8<TIn> xv, xw;
-            xv.load(v, kv);
-            xw.load(wr, kv);
-            xv.get(vv[0], vv[1]);
-            xw.get(om[0], om[1]);
-            f4 dz[2] = {*reinterpret_cast<const f4 *>(dRu + t * DV + j), *reinterpret_cast<const f4 *>(dRu + t * DV + j + 4)};
+            xv[it].get(vv[0], vv[1]);
+            xw[it].get(om[0], om[1]);
+            const f4 (&dz)[2] = dzl[it];
             if (t < L) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
