@@ -22,8 +22,10 @@
 //   dG_t += e_t de^M_t + qs_t dqs^A_t - k_t dk^P_t  (+ the image terms),
 // then dg = reverse in-chunk prefix of dG, and the gates' own derivatives.
 //
-// Every quantity is float32 (the inputs are bfloat16 or float32).  The work is
-// split over six launches:
+// Every quantity is float32 (the inputs are bfloat16 or float32); the products
+// over the value columns in g2b_products take their float32 operands split into
+// two bfloat16 halves (three bfloat16 matrix-core products per float32 product,
+// about 2^-16 relative).  The work is split over six launches:
 //   g2b_prep       per chunk: gates, images, M and Aq, A = (I + M)^{-1}
 //   g2b_fwd_scan   per (sequence, head, 32 value columns): S_n, R, U over the chunks
 //   g2b_bwd_scan   the same slices in reverse: dS_{n+1}, dU, dR; dS_0
@@ -34,6 +36,8 @@
 // pair below the diagonal is split at the block's first row r (i < r <= t) into
 // e^{G_t - G_r} e^{G_r - G_i}; inside a diagonal block it is either taken
 // directly or split at dyadic sub-blocks (first token of the second half).
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -666,12 +670,86 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
 }
 
 // ---------------------------------------------------------------------------
-// g2b_products: one work-group per chunk.  Wave w owns the rows of block w.
+// Split-bfloat16 products.  A float32 x is held as hi = bf16(x) and
+// lo = bf16(x - hi) (round to nearest even both times), so that x = hi + lo to
+// about 2^-17 relative; a product x y is then formed as hi_x hi_y + hi_x lo_y +
+// lo_x hi_y on the 16x16x32 bfloat16 matrix cores with a float32 accumulator
+// (the dropped lo_x lo_y is below 2^-16 |x y|): three 32-deep products in place
+// of eight 4-deep float32 ones.
 // ---------------------------------------------------------------------------
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f4 mfma_bf16_k32(bf8v a, bf8v b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 4 float32 values to their hi and lo halves (8 bytes each)
+__device__ __forceinline__ void split4(f4 x, u16x4 &hi, u16x4 &lo) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const __bf16 h = (__bf16)x[j];
+        hi[j] = __builtin_bit_cast(uint16_t, h);
+        lo[j] = __builtin_bit_cast(uint16_t, (__bf16)(x[j] - (float)h));
+    }
+}
+
+// acc += A(16 x K) B(K x 16), A(m, k) at ah/al[m * LA + k], B(k, n) at bh/bl[n * LB + k]
+// (both contraction-contiguous, split halves in LDS).  Lane l supplies row / column l%16,
+// contraction elements 8 (l/16) .. 8 (l/16) + 7 of each 32-deep step.  ALO = false: A is
+// exact in bfloat16 (its lo half is zero and is not read).
+template <int K, int LA, int LB, bool ALO>
+__device__ __forceinline__ void mma_x3(f4 &acc, const uint16_t *ah, const uint16_t *al, const uint16_t *bh,
+                                       const uint16_t *bl) {
+    const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+    const int oa = r * LA + 8 * g, ob = r * LB + 8 * g;
+#pragma unroll
+    for (int k = 0; k < K; k += 32) {
+        const bf8v a_h = *reinterpret_cast<const bf8v *>(ah + oa + k);
+        const bf8v b_h = *reinterpret_cast<const bf8v *>(bh + ob + k);
+        const bf8v b_l = *reinterpret_cast<const bf8v *>(bl + ob + k);
+        if constexpr (ALO) acc = mfma_bf16_k32(*reinterpret_cast<const bf8v *>(al + oa + k), b_h, acc);
+        acc = mfma_bf16_k32(a_h, b_l, acc);
+        acc = mfma_bf16_k32(a_h, b_h, acc);
+    }
+}
+
+// A ROWS x COLS float32 register tile (see RegTile) stored split: rows of stride LS
+template <int ROWS, int COLS, int LS>
+__device__ __forceinline__ void store_split(const RegTile<ROWS, COLS> &t, uint16_t *hi, uint16_t *lo, float f = 1.f) {
+#pragma unroll
+    for (int j = 0; j < RegTile<ROWS, COLS>::PER; ++j) {
+        const int i = threadIdx.x + j * 256, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
+        u16x4 h, l;
+        split4(t.x[j] * f, h, l);
+        *reinterpret_cast<u16x4 *>(hi + r * LS + c) = h;
+        *reinterpret_cast<u16x4 *>(lo + r * LS + c) = l;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// g2b_products: one work-group per chunk.  Wave w owns the rows of block w.
+// The products over the value columns (dEt, dQt, dKh, dAq, dA) take split
+// operands; the 64-deep ones of dM stay on the float32 matrix cores.
+// ---------------------------------------------------------------------------
+template <int DK, int DV> struct ProdLds {
+    static constexpr int KP = DV + 8;                      // split row stride (elements)
+    static constexpr int S_ = 0, P_ = 2 * DK * KP, O_ = P_ + 2 * C * KP, END = O_ + 2 * C * KP;
+    static constexpr int BYTES_SPLIT = END * 2;
+    // phase 3 float32 tiles: dA [C][80], A [C][80], A [C][68], X [C][68]
+    static constexpr int BYTES_F32 = 4 * (2 * C * 80 + 2 * C * 68);
+    static constexpr int BYTES = BYTES_SPLIT > BYTES_F32 ? BYTES_SPLIT : BYTES_F32;
+};
+
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws) {
-    constexpr int LV = DV + 4, R1 = (DK * LV > 2 * C * 80) ? DK * LV : 2 * C * 80;
-    __shared__ __attribute__((aligned(16))) float r1[R1], b1[C * LV], b2[C * LV];
+    typedef ProdLds<DK, DV> PL;
+    constexpr int KP = PL::KP;
+    constexpr bool DO_LO = !std::is_same<TIn, bf16_t>::value;  // dO is exact in bfloat16 for bf16 inputs
+    __shared__ __attribute__((aligned(16))) uint16_t lds[PL::BYTES / 2];
+    // phase 1: Sn in S, -dR in P, dO in O; phase 2: dS1 in S, U in P, dO in O;
+    // phase 3: dU in P, R in O, then the float32 tiles from the start
+    uint16_t *SH = lds + PL::S_, *SL = SH + DK * KP, *PH = lds + PL::P_, *PLo = PH + C * KP, *OH = lds + PL::O_,
+             *OL = OH + C * KP;
     const int u = blockIdx.x, NC = p.NC;
     const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv);
     const int t0 = n * C, L = min(C, p.T - t0);
@@ -688,17 +766,28 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
             const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
             xo[it].load(dout, (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j);
         }
-        lds_load<DK, DV, LV>(r1, ws.Sn + (size_t)u * DK * DV);
-        lds_load<C, DV, LV>(b1, ws.dR + uC * DV, -1.f);
+        RegTile<DK, DV> rS;
+        RegTile<C, DV> rR;
+        rS.load(ws.Sn + (size_t)u * DK * DV);
+        rR.load(ws.dR + uC * DV);
 #pragma unroll
         for (int it = 0; it < C * DV / 8 / 256; ++it) {
             const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8;
             f4 lo, hi;
             xo[it].get(lo, hi);
             const float on = t < L ? 1.f : 0.f;
-            *reinterpret_cast<f4 *>(b2 + t * LV + j) = lo * on;
-            *reinterpret_cast<f4 *>(b2 + t * LV + j + 4) = hi * on;
+            u16x4 h0, l0, h1, l1;
+            split4(lo * on, h0, l0);
+            split4(hi * on, h1, l1);
+            *reinterpret_cast<u16x4 *>(OH + t * KP + j) = h0;
+            *reinterpret_cast<u16x4 *>(OH + t * KP + j + 4) = h1;
+            if constexpr (DO_LO) {
+                *reinterpret_cast<u16x4 *>(OL + t * KP + j) = l0;
+                *reinterpret_cast<u16x4 *>(OL + t * KP + j + 4) = l1;
+            }
         }
+        store_split<DK, DV, KP>(rS, SH, SL);
+        store_split<C, DV, KP>(rR, PH, PLo, -1.f);
     }
     // phase 2's inputs, in flight during phase 1's products (one work-group per CU:
     // nothing else would hide a phase's loads)
@@ -709,8 +798,8 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     __syncthreads();
     for (int cb = 0; cb < DK / 16; ++cb) {
         f4 e = {0, 0, 0, 0}, q = {0, 0, 0, 0};
-        mma<DV, LV, 1, 1, LV>(e, b1 + 16 * w * LV, r1 + 16 * cb * LV);
-        mma<DV, LV, 1, 1, LV>(q, b2 + 16 * w * LV, r1 + 16 * cb * LV);
+        mma_x3<DV, KP, KP, true>(e, PH + 16 * w * KP, PLo + 16 * w * KP, SH + 16 * cb * KP, SL + 16 * cb * KP);
+        mma_x3<DV, KP, KP, DO_LO>(q, OH + 16 * w * KP, OL + 16 * w * KP, SH + 16 * cb * KP, SL + 16 * cb * KP);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const size_t o = (uC + 16 * w + 4 * gg + s) * DK + 16 * cb + rr;
@@ -724,16 +813,19 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < DV / 2; j += 4) {
-            const f4 x = *reinterpret_cast<const f4 *>(d1 + j), y = *reinterpret_cast<const f4 *>(r1 + c * LV + h * (DV / 2) + j);
-            s += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+            const f4 x = *reinterpret_cast<const f4 *>(d1 + j);
+            const int o = c * KP + h * (DV / 2) + j;
+            const u16x4 yh = *reinterpret_cast<const u16x4 *>(SH + o), yl = *reinterpret_cast<const u16x4 *>(SL + o);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s += x[k] * (bf16_to_f32(yh[k]) + bf16_to_f32(yl[k]));
         }
         s += __shfl_xor(s, 1);
         if (!h) ws.dgC[(size_t)u * DK + c] = s;
     }
     __syncthreads();
     // phase 2: dKh = U dS1^T, dAq = tril(dO U^T)
-    nS1.template store<LV>(r1);
-    nU.template store<LV>(b1);
+    store_split<DK, DV, KP>(nS1, SH, SL);
+    store_split<C, DV, KP>(nU, PH, PLo);
     // phase 3's inputs, in flight during phase 2's products (A once, for both copies)
     RegTile<C, DV> nR, ndU;
     RegTile<C, C> nA;
@@ -743,14 +835,15 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     __syncthreads();
     for (int cb = 0; cb < DK / 16; ++cb) {
         f4 acc = {0, 0, 0, 0};
-        mma<DV, LV, 1, 1, LV>(acc, b1 + 16 * w * LV, r1 + 16 * cb * LV);
+        mma_x3<DV, KP, KP, true>(acc, PH + 16 * w * KP, PLo + 16 * w * KP, SH + 16 * cb * KP, SL + 16 * cb * KP);
 #pragma unroll
         for (int s = 0; s < 4; ++s) ws.dKh[(uC + 16 * w + 4 * gg + s) * DK + 16 * cb + rr] = acc[s];
     }
     float *dAqu = ws.dAq + uC * C;
     for (int ib = 0; ib < 4; ++ib) {
         f4 acc = {0, 0, 0, 0};
-        if (ib <= w) mma<DV, LV, 1, 1, LV>(acc, b2 + 16 * w * LV, b1 + 16 * ib * LV);
+        if (ib <= w)
+            mma_x3<DV, KP, KP, DO_LO>(acc, OH + 16 * w * KP, OL + 16 * w * KP, PH + 16 * ib * KP, PLo + 16 * ib * KP);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int t = 16 * w + 4 * gg + s, i = 16 * ib + rr;
@@ -759,22 +852,23 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     }
     __syncthreads();
     // phase 3: dA = dU R^T; X = A^T dA; dM = -strict_tril(X A^T)
-    float *dAs = r1, *A80 = r1 + C * 80, *A68 = b1, *Xs = b2;
-    nR.template store<LV>(b1);
-    ndU.template store<LV>(b2);
-    nA.template store<80>(A80);
+    store_split<C, DV, KP>(ndU, PH, PLo);
+    store_split<C, DV, KP>(nR, OH, OL);
     __syncthreads();
     f4 dA[4];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
         dA[ib] = f4{0, 0, 0, 0};
-        mma<DV, LV, 1, 1, LV>(dA[ib], b2 + 16 * w * LV, b1 + 16 * ib * LV);
+        mma_x3<DV, KP, KP, true>(dA[ib], PH + 16 * w * KP, PLo + 16 * w * KP, OH + 16 * ib * KP, OL + 16 * ib * KP);
     }
     __syncthreads();
+    float *f32s = reinterpret_cast<float *>(lds);
+    float *dAs = f32s, *A80 = f32s + C * 80, *A68 = f32s + 2 * C * 80, *Xs = A68 + C * 68;
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
         for (int s = 0; s < 4; ++s) dAs[(16 * w + 4 * gg + s) * 80 + 16 * ib + rr] = dA[ib][s];
+    nA.template store<80>(A80);
     nA.template store<68>(A68);
     __syncthreads();
     // X[i][s] = sum_t A[t][i] dA[t][s] (A[t][i] = 0 for t < i): rows i of block w
@@ -784,7 +878,6 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
         mma<C, 1, 80, 80, 1>(acc, A80 + 16 * w, dAs + 16 * sb);
         dA[sb] = acc;  // reuse the registers for X
     }
-    __syncthreads();  // Xs aliases b2, read by nobody now; A68 stays
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
@@ -1122,13 +1215,13 @@ hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t
 
 // Buffers whose lives do not overlap share memory.  Lives (W = written, R = read):
 //   A: prep W, fwd/bwd scans and products R;  Aq, Et, Qt, Kh, gC: prep W, scans R;
-//   Z: prep W, forward scan R;  Sn, R, U: forward scan W, products R;
+//   Sn, R, U: forward scan W, products R;
 //   dS1, dU: reverse scan W, products R;  dR: reverse scan W, products and local R;
 //   dEt, dQt, dKh, dgC, dAq, dM: products W, local R;  dqh, dkh, dAl: local W, reduce R.
 // So products writes into the space of buffers last read by the scans (dEt into Et, dQt
-// into Qt, dKh into Kh, dgC into gC, dAq into Aq, dM into Z), and local into the space of
-// buffers last read by products (dqh into Sn, dkh into dS1, dAl into U).  No kernel reads
-// a buffer whose space it writes through another name.
+// into Qt, dKh into Kh, dgC into gC, dAq into Aq; dM has its own), and local into the
+// space of buffers last read by products (dqh into Sn, dkh into dS1, dAl into U).  No
+// kernel reads a buffer whose space it writes through another name.
 size_t bwd2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, Bwd2Workspace *ws) {
     const size_t NC = ((size_t)T + C - 1) / C, U = (size_t)B * Hv * NC;
     size_t off = 0;
