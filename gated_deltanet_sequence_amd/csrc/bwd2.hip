@@ -23,9 +23,10 @@
 // then dg = reverse in-chunk prefix of dG, and the gates' own derivatives.
 //
 // Every quantity is float32 (the inputs are bfloat16 or float32); the products
-// over the value columns in g2b_products take their float32 operands split into
-// two bfloat16 halves (three bfloat16 matrix-core products per float32 product,
-// about 2^-16 relative).  The work is split over six launches:
+// over the value columns in g2b_products and those of the reverse scan take their
+// float32 operands split into two bfloat16 halves (three bfloat16 matrix-core
+// products per float32 product, about 2^-16 relative).  The work is split over
+// six launches:
 //   g2b_prep       per chunk: gates, images, M and Aq, A = (I + M)^{-1}
 //   g2b_fwd_scan   per (sequence, head, 32 value columns): S_n, R, U over the chunks
 //   g2b_bwd_scan   the same slices in reverse: dS_{n+1}, dU, dR; dS_0
@@ -517,159 +518,6 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
 }
 
 // ---------------------------------------------------------------------------
-// g2b_bwd_scan: the same slices, chunks in reverse; dS in MFMA accumulators.
-// ---------------------------------------------------------------------------
-template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws) {
-    constexpr int LQ = 80, LKA = DK + 4, LKB = DK + 16, LB = 48, NS = DV / 32, NT = DK / 32;
-    // bA: A_qk, then A; bK1: Kh (stride LKA), then -Et (stride LKB); bK2: Qt
-    __shared__ __attribute__((aligned(16))) float bA[C * LQ], bK1[C * LKB], bK2[C * LKB], Os[C * LB],
-        dSs[DK * LB], dUs[C * LB], dRs[C * LB];
-    const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
-    const TIn *dout = static_cast<const TIn *>(p.dout);
-    // gradient of the final state: every load issued before any is used
-    f4 dS[NT];
-    if (p.dST) {
-#pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                dS[x][s] = p.dST[(((size_t)bb * p.Hv + hv) * DK + 16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr];
-        }
-    } else {
-#pragma unroll
-        for (int x = 0; x < NT; ++x) dS[x] = f4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int x = 0; x < NT; ++x) {
-        const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) dSs[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = dS[x][s];
-    }
-    // dO slice of chunk n: 64 rows x 32 columns, 8 per thread (rows past T read the last
-    // token and are zeroed when stored)
-    const int ot = tid >> 2, oj = (tid & 3) * 8;
-    auto load_do = [&](int n) {
-        const int L = min(C, p.T - n * C), tl = min(ot, L - 1);
-        In8<TIn> x;
-        x.load(dout, (((size_t)bb * p.T + n * C + tl) * p.Hv + hv) * DV + j0 + oj);
-        return x;
-    };
-    auto store_do = [&](const In8<TIn> &x, int n) {
-        const int L = min(C, p.T - n * C);
-        f4 lo, hi;
-        x.get(lo, hi);
-        const float on = ot < L ? 1.f : 0.f;
-        *reinterpret_cast<f4 *>(Os + ot * LB + oj) = lo * on;
-        *reinterpret_cast<f4 *>(Os + ot * LB + oj + 4) = hi * on;
-    };
-    // staged for the chunk about to run: A_qk in bA, Kh in bK1, dO in Os
-    RegTile<C, C> rAq, rA;
-    RegTile<C, DK> rKh, rQ, rE;
-    In8<TIn> rdo;
-    {
-        const size_t u = unit_of(bb, hv, NC - 1, p.Hv, NC);
-        rAq.load(ws.Aq + u * C * C);
-        rKh.load(ws.Kh + u * C * DK);
-        rdo = load_do(NC - 1);
-        rAq.template store<LQ>(bA);
-        rKh.template store<LKA>(bK1);
-        store_do(rdo, NC - 1);
-    }
-    for (int n = NC - 1; n >= 0; --n) {
-        const size_t u = unit_of(bb, hv, n, p.Hv, NC);
-        float *dS1u = ws.dS1 + u * DK * DV;
-#pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) dS1u[(16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = dS[x][s];
-        }
-        float gcr[NT][4];
-#pragma unroll
-        for (int x = 0; x < NT; ++x)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) gcr[x][s] = ws.gC[u * DK + 16 * ((w * NT + x) >> 1) + 4 * gg + s];
-        __syncthreads();
-        // this chunk's A, Qt, Et in flight while dU is computed
-        rA.load(ws.A + u * C * C);
-        rQ.load(ws.Qt + u * C * DK);
-        rE.load(ws.Et + u * C * DK);
-        // dU = Aq^T dO + Kh dS  (Aq is zero above the diagonal)
-        float *dUu = ws.dU + u * C * DV, *dRu = ws.dR + u * C * DV;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            f4 acc = {0, 0, 0, 0};
-            mma<C, 1, LQ, LB, 1>(acc, bA + 16 * w, Os + 16 * jb);
-            mma<DK, LKA, 1, LB, 1>(acc, bK1 + 16 * w * LKA, dSs + 16 * jb);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
-                dUs[t * LB + j] = acc[s];
-                dUu[t * DV + j0 + j] = acc[s];
-            }
-        }
-        __syncthreads();
-        rA.template store<LQ>(bA);
-        rQ.template store<LKB>(bK2);
-        rE.template store<LKB>(bK1, -1.f);
-        // the next chunk's A_qk, Kh and dO in flight while this one finishes
-        if (n > 0) {
-            const size_t un = u - 1;
-            rAq.load(ws.Aq + un * C * C);
-            rKh.load(ws.Kh + un * C * DK);
-            rdo = load_do(n - 1);
-        }
-        __syncthreads();
-        // dR = A^T dU;  dS = gamma_C . dS + Qt^T dO
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            f4 acc = {0, 0, 0, 0};
-            mma<C, 1, LQ, LB, 1>(acc, bA + 16 * w, dUs + 16 * jb);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
-                dRs[t * LB + j] = acc[s];
-                dRu[t * DV + j0 + j] = acc[s];
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) dS[x][s] *= gcr[x][s];
-            mma<C, 1, LKB, LB, 1>(dS[x], bK2 + 16 * cb, Os + 16 * jb);
-        }
-        __syncthreads();
-        // dS -= Et^T dR  (bK1 holds -Et)
-#pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-            mma<C, 1, LKB, LB, 1>(dS[x], bK1 + 16 * cb, dRs + 16 * jb);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) dSs[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = dS[x][s];
-        }
-        __syncthreads();
-        if (n > 0) {
-            rAq.template store<LQ>(bA);
-            rKh.template store<LKA>(bK1);
-            store_do(rdo, n - 1);
-        }
-    }
-    if (p.dS0) {
-#pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                p.dS0[(((size_t)bb * p.Hv + hv) * DK + 16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = dS[x][s];
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Split-bfloat16 products.  A float32 x is held as hi = bf16(x) and
 // lo = bf16(x - hi) (round to nearest even both times), so that x = hi + lo to
 // about 2^-17 relative; a product x y is then formed as hi_x hi_y + hi_x lo_y +
@@ -723,6 +571,246 @@ __device__ __forceinline__ void store_split(const RegTile<ROWS, COLS> &t, uint16
         split4(t.x[j] * f, h, l);
         *reinterpret_cast<u16x4 *>(hi + r * LS + c) = h;
         *reinterpret_cast<u16x4 *>(lo + r * LS + c) = l;
+    }
+}
+
+// k-block operands of one 32-deep split product (see the MFMA layouts in
+// gdn_device.h): lane (g, r) = (l/16, l%16) holds, for the two 16-deep blocks
+// kb0, kb0 + 1 of the step, the 4 values k = 16 kb + 4 g + 0..3 of row / column r
+// -- the rows an accumulator tile holds, so accumulator tiles are operands as
+// they are.
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4v lds_s4v;
+struct KOp {
+    u16x4 h0, h1, l0, l1;
+};
+__device__ __forceinline__ bf8v cat8(u16x4 a, u16x4 b) {
+    return __builtin_bit_cast(bf8v, u16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+}
+// acc += A B over one 32-deep step; ALO / BLO: the operand has a lo half
+template <bool ALO, bool BLO>
+__device__ __forceinline__ f4 x3_step(f4 acc, const KOp &a, const KOp &b) {
+    const bf8v ah = cat8(a.h0, a.h1), bh = cat8(b.h0, b.h1);
+    if constexpr (ALO) acc = mfma_bf16_k32(cat8(a.l0, a.l1), bh, acc);
+    if constexpr (BLO) acc = mfma_bf16_k32(ah, cat8(b.l0, b.l1), acc);
+    return mfma_bf16_k32(ah, bh, acc);
+}
+// from a split tile X[m][k] with k contiguous (row stride S): row m0 + r
+template <int S, bool LO>
+__device__ __forceinline__ KOp op_row(const uint16_t *h, const uint16_t *l, int m0, int kb0) {
+    const int ln = threadIdx.x & 63, o = (m0 + (ln & 15)) * S + 16 * kb0 + 4 * (ln >> 4);
+    KOp x;
+    x.h0 = *reinterpret_cast<const u16x4 *>(h + o);
+    x.h1 = *reinterpret_cast<const u16x4 *>(h + o + 16);
+    if constexpr (LO) {
+        x.l0 = *reinterpret_cast<const u16x4 *>(l + o);
+        x.l1 = *reinterpret_cast<const u16x4 *>(l + o + 16);
+    }
+    return x;
+}
+// from a split tile T[k][m] with m contiguous (row stride S), read transposed
+// (ds_read_b64_tr_b16: in each 16-lane group, lane 4i + q points at 4 values,
+// columns 4q .. 4q+3 of row i of a 4 x 16 block, and lane j receives column j of
+// the 4 rows): column m0 + r
+__device__ __forceinline__ u16x4 lds_tr4(const uint16_t *p) {
+    return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v *)p));
+}
+template <int S, bool LO>
+__device__ __forceinline__ KOp op_tr(const uint16_t *h, const uint16_t *l, int m0, int kb0) {
+    const int ln = threadIdx.x & 63, r = ln & 15;
+    const int o = (16 * kb0 + 4 * (ln >> 4) + (r >> 2)) * S + m0 + 4 * (r & 3);
+    KOp x;
+    x.h0 = lds_tr4(h + o);
+    x.h1 = lds_tr4(h + o + 16 * S);
+    if constexpr (LO) {
+        x.l0 = lds_tr4(l + o);
+        x.l1 = lds_tr4(l + o + 16 * S);
+    }
+    return x;
+}
+// an accumulator tile (rows 16 kb + 4 g + s, column 16 jb + r) into a split
+// transposed store XT[n][k] (row stride S): 8 bytes per half and lane
+template <int S>
+__device__ __forceinline__ void store_acc_t(f4 x, uint16_t *h, uint16_t *l, int kb, int jb) {
+    const int ln = threadIdx.x & 63, o = (16 * jb + (ln & 15)) * S + 16 * kb + 4 * (ln >> 4);
+    u16x4 xh, xl;
+    split4(x, xh, xl);
+    *reinterpret_cast<u16x4 *>(h + o) = xh;
+    *reinterpret_cast<u16x4 *>(l + o) = xl;
+}
+
+// ---------------------------------------------------------------------------
+// g2b_bwd_scan: the same slices, chunks in reverse; dS in MFMA accumulators.
+// ---------------------------------------------------------------------------
+// The reverse scan's products take split operands.  Its LDS (16-bit elements,
+// each split tile a hi and a lo array):
+// A_qk then A [C][C]; Kh then -Et [C][DK]; Qt [C][DK]; dO [C][32]; and the
+// transposed dS [32][DK], dU, dR [32][C] of the chunk.
+template <int DK> struct BwdScanLds {
+    static constexpr int SA = C + 8, SK = DK + 8, SO = 32 + 8, SS = DK + 8, SU = C + 8;
+    static constexpr int A_ = 0, K1_ = A_ + 2 * C * SA, K2_ = K1_ + 2 * C * SK, O_ = K2_ + 2 * C * SK,
+                         S_ = O_ + 2 * C * SO, U_ = S_ + 2 * 32 * SS, R_ = U_ + 2 * 32 * SU, END = R_ + 2 * 32 * SU;
+};
+
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws) {
+    typedef BwdScanLds<DK> BL;
+    constexpr int SA = BL::SA, SK = BL::SK, SO = BL::SO, SS = BL::SS, SU = BL::SU;
+    constexpr int NS = DV / 32, NT = DK / 32;
+    constexpr bool DO_LO = !std::is_same<TIn, bf16_t>::value;  // dO is exact in bfloat16 for bf16 inputs
+    __shared__ __attribute__((aligned(16))) uint16_t lds[BL::END];
+    uint16_t *AH = lds + BL::A_, *AL = AH + C * SA, *K1H = lds + BL::K1_, *K1L = K1H + C * SK;
+    uint16_t *K2H = lds + BL::K2_, *K2L = K2H + C * SK, *OH = lds + BL::O_, *OL = OH + C * SO;
+    uint16_t *DSH = lds + BL::S_, *DSL = DSH + 32 * SS, *DUH = lds + BL::U_, *DUL = DUH + 32 * SU;
+    uint16_t *DRH = lds + BL::R_, *DRL = DRH + 32 * SU;
+    const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
+    const TIn *dout = static_cast<const TIn *>(p.dout);
+    // gradient of the final state: every load issued before any is used.  Wave w
+    // holds the tiles (channel block cb, column block jb) id = w NT + x, cb = id / 2.
+    f4 dS[NT];
+    if (p.dST) {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                dS[x][s] = p.dST[(((size_t)bb * p.Hv + hv) * DK + 16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr];
+        }
+    } else {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) dS[x] = f4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int x = 0; x < NT; ++x) {
+        const int id = w * NT + x;
+        store_acc_t<SS>(dS[x], DSH, DSL, id >> 1, id & 1);
+    }
+    // dO slice of chunk n: 64 rows x 32 columns, 8 per thread (rows past T read the last
+    // token and are zeroed when stored)
+    const int ot = tid >> 2, oj = (tid & 3) * 8;
+    auto load_do = [&](int n) {
+        const int L = min(C, p.T - n * C), tl = min(ot, L - 1);
+        In8<TIn> x;
+        x.load(dout, (((size_t)bb * p.T + n * C + tl) * p.Hv + hv) * DV + j0 + oj);
+        return x;
+    };
+    auto store_do = [&](const In8<TIn> &x, int n) {
+        const int L = min(C, p.T - n * C);
+        f4 lo, hi;
+        x.get(lo, hi);
+        const float on = ot < L ? 1.f : 0.f;
+        u16x4 h0, l0, h1, l1;
+        split4(lo * on, h0, l0);
+        split4(hi * on, h1, l1);
+        *reinterpret_cast<u16x8 *>(OH + ot * SO + oj) = u16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        if constexpr (DO_LO)
+            *reinterpret_cast<u16x8 *>(OL + ot * SO + oj) = u16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+    };
+    // staged for the chunk about to run: A_qk, Kh, dO
+    RegTile<C, C> rAq, rA;
+    RegTile<C, DK> rKh, rQ, rE;
+    In8<TIn> rdo;
+    {
+        const size_t u = unit_of(bb, hv, NC - 1, p.Hv, NC);
+        rAq.load(ws.Aq + u * C * C);
+        rKh.load(ws.Kh + u * C * DK);
+        rdo = load_do(NC - 1);
+        store_split<C, C, SA>(rAq, AH, AL);
+        store_split<C, DK, SK>(rKh, K1H, K1L);
+        store_do(rdo, NC - 1);
+    }
+    for (int n = NC - 1; n >= 0; --n) {
+        const size_t u = unit_of(bb, hv, n, p.Hv, NC);
+        float *dS1u = ws.dS1 + u * DK * DV;
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) dS1u[(16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = dS[x][s];
+        }
+        float gcr[NT][4];
+#pragma unroll
+        for (int x = 0; x < NT; ++x)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) gcr[x][s] = ws.gC[u * DK + 16 * ((w * NT + x) >> 1) + 4 * gg + s];
+        __syncthreads();
+        // this chunk's A, Qt, Et in flight while dU is computed
+        rA.load(ws.A + u * C * C);
+        rQ.load(ws.Qt + u * C * DK);
+        rE.load(ws.Et + u * C * DK);
+        // dU = Aq^T dO + Kh dS  (rows of block w)
+        float *dUu = ws.dU + u * C * DV, *dRu = ws.dR + u * C * DV;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            f4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < C / 16; kb += 2)
+                acc = x3_step<true, DO_LO>(acc, op_tr<SA, true>(AH, AL, 16 * w, kb), op_tr<SO, DO_LO>(OH, OL, 16 * jb, kb));
+#pragma unroll
+            for (int kb = 0; kb < DK / 16; kb += 2)
+                acc = x3_step<true, true>(acc, op_row<SK, true>(K1H, K1L, 16 * w, kb), op_row<SS, true>(DSH, DSL, 16 * jb, kb));
+            store_acc_t<SU>(acc, DUH, DUL, w, jb);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) dUu[(16 * w + 4 * gg + s) * DV + j0 + 16 * jb + rr] = acc[s];
+        }
+        __syncthreads();
+        store_split<C, C, SA>(rA, AH, AL);
+        store_split<C, DK, SK>(rQ, K2H, K2L);
+        store_split<C, DK, SK>(rE, K1H, K1L, -1.f);
+        // the next chunk's A_qk, Kh and dO in flight while this one finishes
+        if (n > 0) {
+            const size_t un = u - 1;
+            rAq.load(ws.Aq + un * C * C);
+            rKh.load(ws.Kh + un * C * DK);
+            rdo = load_do(n - 1);
+        }
+        __syncthreads();
+        // dR = A^T dU;  dS = gamma_C . dS + Qt^T dO
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            f4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < C / 16; kb += 2)
+                acc = x3_step<true, true>(acc, op_tr<SA, true>(AH, AL, 16 * w, kb), op_row<SU, true>(DUH, DUL, 16 * jb, kb));
+            store_acc_t<SU>(acc, DRH, DRL, w, jb);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) dRu[(16 * w + 4 * gg + s) * DV + j0 + 16 * jb + rr] = acc[s];
+        }
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) dS[x][s] *= gcr[x][s];
+#pragma unroll
+            for (int kb = 0; kb < C / 16; kb += 2)
+                dS[x] = x3_step<true, DO_LO>(dS[x], op_tr<SK, true>(K2H, K2L, 16 * cb, kb), op_tr<SO, DO_LO>(OH, OL, 16 * jb, kb));
+        }
+        __syncthreads();
+        // dS -= Et^T dR  (the Et tile holds -Et)
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int kb = 0; kb < C / 16; kb += 2)
+                dS[x] = x3_step<true, true>(dS[x], op_tr<SK, true>(K1H, K1L, 16 * cb, kb), op_row<SU, true>(DRH, DRL, 16 * jb, kb));
+            store_acc_t<SS>(dS[x], DSH, DSL, cb, jb);
+        }
+        __syncthreads();
+        if (n > 0) {
+            store_split<C, C, SA>(rAq, AH, AL);
+            store_split<C, DK, SK>(rKh, K1H, K1L);
+            store_do(rdo, n - 1);
+        }
+    }
+    if (p.dS0) {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                p.dS0[(((size_t)bb * p.Hv + hv) * DK + 16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = dS[x][s];
+        }
     }
 }
 
