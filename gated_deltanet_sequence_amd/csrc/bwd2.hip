@@ -22,11 +22,10 @@
 //   dG_t += e_t de^M_t + qs_t dqs^A_t - k_t dk^P_t  (+ the image terms),
 // then dg = reverse in-chunk prefix of dG, and the gates' own derivatives.
 //
-// Every quantity is float32 (the inputs are bfloat16 or float32); the products
-// over the value columns in g2b_products and those of the reverse scan take their
-// float32 operands split into two bfloat16 halves (three bfloat16 matrix-core
-// products per float32 product, about 2^-16 relative).  The work is split over
-// six launches:
+// Every quantity is float32 (the inputs are bfloat16 or float32); the products of
+// both scans and those over the value columns in g2b_products take their float32
+// operands split into two bfloat16 halves (three bfloat16 matrix-core products per
+// float32 product, about 2^-16 relative).  The work is split over six launches:
 //   g2b_prep       per chunk: gates, images, M and Aq, A = (I + M)^{-1}
 //   g2b_fwd_scan   per (sequence, head, 32 value columns): S_n, R, U over the chunks
 //   g2b_bwd_scan   the same slices in reverse: dS_{n+1}, dU, dR; dS_0
@@ -400,124 +399,6 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
 }
 
 // ---------------------------------------------------------------------------
-// g2b_fwd_scan: one work-group per (sequence, value head, 32 value columns);
-// wave w holds the state tiles (c-blocks 2w', j-blocks) as MFMA accumulators.
-// ---------------------------------------------------------------------------
-template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws) {
-    constexpr int LE = DK + 4, LK = DK + 16, LA = 68, LB = 48, NS = DV / 32, NT = DK / 32;
-    __shared__ __attribute__((aligned(16))) float Ets[C * LE], Khs[C * LK], As[C * LA], Ss[DK * LB], Rs[C * LB],
-        Us[C * LB];
-    const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
-    // initial state: every load issued before any is used (one wait, not one per element)
-    f4 S[NT];
-    if (p.S0) {
-#pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                S[x][s] = p.S0[(((size_t)bb * p.Hv + hv) * DK + 16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr];
-        }
-    } else {
-#pragma unroll
-        for (int x = 0; x < NT; ++x) S[x] = f4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int x = 0; x < NT; ++x) {
-        const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) Ss[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = S[x][s];
-    }
-    // this lane's v and write-logit elements of chunk m (rows past T read the last
-    // token and are zeroed at use): loaded one chunk ahead, raw, for z = sigmoid(write) v
-    const TIn *vin = static_cast<const TIn *>(p.v), *win = static_cast<const TIn *>(p.write);
-    In1<TIn> zv[2][4], zw[2][4];
-    auto load_z = [&](int m) {
-        const int tm = m * C, Lm = min(C, p.T - tm);
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int t = min(16 * w + 4 * gg + s, Lm - 1);
-                const size_t kv = (((size_t)bb * p.T + tm + t) * p.Hv + hv) * DV + j0 + 16 * jb + rr;
-                zv[jb][s].load(vin, kv);
-                zw[jb][s].load(win, kv);
-            }
-    };
-    if (NC > 0) load_z(0);
-    for (int n = 0; n < NC; ++n) {
-        const size_t u = unit_of(bb, hv, n, p.Hv, NC);
-        float *Snu = ws.Sn + u * DK * DV;
-#pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Snu[(16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = S[x][s];
-        }
-        const float *gCu = ws.gC + u * DK;
-        const int L = min(C, p.T - n * C);
-        float zr[2][4], gcr[NT][4];
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                zr[jb][s] = zv[jb][s].get() * sigmoid_fast(zw[jb][s].get()) * (16 * w + 4 * gg + s < L ? 1.f : 0.f);
-#pragma unroll
-        for (int x = 0; x < NT; ++x)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) gcr[x][s] = gCu[16 * ((w * NT + x) >> 1) + 4 * gg + s];
-        lds_load<C, DK, LE>(Ets, ws.Et + u * C * DK);
-        lds_load<C, DK, LK>(Khs, ws.Kh + u * C * DK);
-        lds_load<C, C, LA>(As, ws.A + u * C * C);
-        // the next chunk's z inputs: issued after the tiles' loads (which wait for every
-        // load issued before them), in flight during this chunk's products
-        if (n + 1 < NC) load_z(n + 1);
-        __syncthreads();
-        // R = Z - Et S (rows of block w)
-        float *Ru = ws.R + u * C * DV, *Uu = ws.U + u * C * DV;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            f4 acc = {0, 0, 0, 0};
-            mma<DK, LE, 1, LB, 1>(acc, Ets + 16 * w * LE, Ss + 16 * jb);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
-                const float rv = zr[jb][s] - acc[s];
-                Rs[t * LB + j] = rv;
-                Ru[t * DV + j0 + j] = rv;
-            }
-        }
-        __syncthreads();
-        // U = A R (A lower triangular: columns up to the block's last row)
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            f4 acc = {0, 0, 0, 0};
-            mma<C, LA, 1, LB, 1>(acc, As + 16 * w * LA, Rs + 16 * jb);  // A is zero above the diagonal
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int t = 16 * w + 4 * gg + s, j = 16 * jb + rr;
-                Us[t * LB + j] = acc[s];
-                Uu[t * DV + j0 + j] = acc[s];
-            }
-        }
-        __syncthreads();
-        // S = gamma_C . S + Kh^T U
-#pragma unroll
-        for (int x = 0; x < NT; ++x) {
-            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) S[x][s] *= gcr[x][s];
-            mma<C, 1, LK, LB, 1>(S[x], Khs + 16 * cb, Us + 16 * jb);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Ss[(16 * cb + 4 * gg + s) * LB + 16 * jb + rr] = S[x][s];
-        }
-        __syncthreads();
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Split-bfloat16 products.  A float32 x is held as hi = bf16(x) and
 // lo = bf16(x - hi) (round to nearest even both times), so that x = hi + lo to
 // about 2^-17 relative; a product x y is then formed as hi_x hi_y + hi_x lo_y +
@@ -637,6 +518,159 @@ __device__ __forceinline__ void store_acc_t(f4 x, uint16_t *h, uint16_t *l, int 
     split4(x, xh, xl);
     *reinterpret_cast<u16x4 *>(h + o) = xh;
     *reinterpret_cast<u16x4 *>(l + o) = xl;
+}
+
+// ROWS x COLS float32 block (row-major, contiguous) into split LDS rows of stride LS,
+// times f; loads in batches of 8 per thread as lds_load.
+template <int ROWS, int COLS, int LS>
+__device__ __forceinline__ void lds_load_split(uint16_t *hi, uint16_t *lo, const float *__restrict__ src, float f = 1.f) {
+    constexpr int N = ROWS * COLS / 4, PER = N / 256, BT = PER < 8 ? PER : 8;
+    static_assert(N % 256 == 0 && PER % BT == 0, "block size");
+#pragma unroll
+    for (int b0 = 0; b0 < PER; b0 += BT) {
+        f4 x[BT];
+#pragma unroll
+        for (int j = 0; j < BT; ++j)
+            x[j] = *reinterpret_cast<const f4 *>(src + (size_t)(threadIdx.x + (b0 + j) * 256) * 4);
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            const int i = threadIdx.x + (b0 + j) * 256, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
+            u16x4 h, l;
+            split4(x[j] * f, h, l);
+            *reinterpret_cast<u16x4 *>(hi + r * LS + c) = h;
+            *reinterpret_cast<u16x4 *>(lo + r * LS + c) = l;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// g2b_fwd_scan: one work-group per (sequence, value head, 32 value columns);
+// wave w holds the state tiles (c-blocks 2w', j-blocks) as MFMA accumulators.
+// Its products take split operands.  LDS (16-bit elements, each split tile a
+// hi and a lo array): Et, Kh [C][DK], A [C][C], and the transposed S [32][DK],
+// R, U [32][C] of the chunk.
+// ---------------------------------------------------------------------------
+template <int DK> struct FwdScanLds {
+    static constexpr int SK = DK + 8, SA = C + 8, SS = DK + 8, SU = C + 8;
+    static constexpr int E_ = 0, K_ = E_ + 2 * C * SK, A_ = K_ + 2 * C * SK, S_ = A_ + 2 * C * SA,
+                         R_ = S_ + 2 * 32 * SS, U_ = R_ + 2 * 32 * SU, END = U_ + 2 * 32 * SU;
+};
+
+template <typename TIn, int DK, int DV>
+__global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws) {
+    typedef FwdScanLds<DK> FL;
+    constexpr int SK = FL::SK, SA = FL::SA, SS = FL::SS, SU = FL::SU, NS = DV / 32, NT = DK / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[FL::END];
+    uint16_t *EH = lds + FL::E_, *EL = EH + C * SK, *KH = lds + FL::K_, *KL = KH + C * SK, *AH = lds + FL::A_,
+             *AL = AH + C * SA, *SH = lds + FL::S_, *SL = SH + 32 * SS, *RH = lds + FL::R_, *RL = RH + 32 * SU,
+             *UH = lds + FL::U_, *UL = UH + 32 * SU;
+    const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
+    // initial state: every load issued before any is used (one wait, not one per element)
+    f4 S[NT];
+    if (p.S0) {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                S[x][s] = p.S0[(((size_t)bb * p.Hv + hv) * DK + 16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr];
+        }
+    } else {
+#pragma unroll
+        for (int x = 0; x < NT; ++x) S[x] = f4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int x = 0; x < NT; ++x) {
+        const int id = w * NT + x;
+        store_acc_t<SS>(S[x], SH, SL, id >> 1, id & 1);
+    }
+    // this lane's v and write-logit elements of chunk m (rows past T read the last
+    // token and are zeroed at use): loaded one chunk ahead, raw, for z = sigmoid(write) v
+    const TIn *vin = static_cast<const TIn *>(p.v), *win = static_cast<const TIn *>(p.write);
+    In1<TIn> zv[2][4], zw[2][4];
+    auto load_z = [&](int m) {
+        const int tm = m * C, Lm = min(C, p.T - tm);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int t = min(16 * w + 4 * gg + s, Lm - 1);
+                const size_t kv = (((size_t)bb * p.T + tm + t) * p.Hv + hv) * DV + j0 + 16 * jb + rr;
+                zv[jb][s].load(vin, kv);
+                zw[jb][s].load(win, kv);
+            }
+    };
+    if (NC > 0) load_z(0);
+    for (int n = 0; n < NC; ++n) {
+        const size_t u = unit_of(bb, hv, n, p.Hv, NC);
+        float *Snu = ws.Sn + u * DK * DV;
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Snu[(16 * cb + 4 * gg + s) * DV + j0 + 16 * jb + rr] = S[x][s];
+        }
+        const float *gCu = ws.gC + u * DK;
+        const int L = min(C, p.T - n * C);
+        float zr[2][4], gcr[NT][4];
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                zr[jb][s] = zv[jb][s].get() * sigmoid_fast(zw[jb][s].get()) * (16 * w + 4 * gg + s < L ? 1.f : 0.f);
+#pragma unroll
+        for (int x = 0; x < NT; ++x)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) gcr[x][s] = gCu[16 * ((w * NT + x) >> 1) + 4 * gg + s];
+        lds_load_split<C, DK, SK>(EH, EL, ws.Et + u * C * DK);
+        lds_load_split<C, DK, SK>(KH, KL, ws.Kh + u * C * DK);
+        lds_load_split<C, C, SA>(AH, AL, ws.A + u * C * C);
+        // the next chunk's z inputs: issued after the tiles' loads (which wait for every
+        // load issued before them), in flight during this chunk's products
+        if (n + 1 < NC) load_z(n + 1);
+        __syncthreads();
+        // R = Z - Et S (rows of block w)
+        float *Ru = ws.R + u * C * DV, *Uu = ws.U + u * C * DV;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            f4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < DK / 16; kb += 2)
+                acc = x3_step<true, true>(acc, op_row<SK, true>(EH, EL, 16 * w, kb), op_row<SS, true>(SH, SL, 16 * jb, kb));
+            f4 rv;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) rv[s] = zr[jb][s] - acc[s];
+            store_acc_t<SU>(rv, RH, RL, w, jb);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Ru[(16 * w + 4 * gg + s) * DV + j0 + 16 * jb + rr] = rv[s];
+        }
+        __syncthreads();
+        // U = A R
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            f4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int kb = 0; kb < C / 16; kb += 2)
+                acc = x3_step<true, true>(acc, op_row<SA, true>(AH, AL, 16 * w, kb), op_row<SU, true>(RH, RL, 16 * jb, kb));
+            store_acc_t<SU>(acc, UH, UL, w, jb);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Uu[(16 * w + 4 * gg + s) * DV + j0 + 16 * jb + rr] = acc[s];
+        }
+        __syncthreads();
+        // S = gamma_C . S + Kh^T U
+#pragma unroll
+        for (int x = 0; x < NT; ++x) {
+            const int id = w * NT + x, cb = id >> 1, jb = id & 1;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) S[x][s] *= gcr[x][s];
+#pragma unroll
+            for (int kb = 0; kb < C / 16; kb += 2)
+                S[x] = x3_step<true, true>(S[x], op_tr<SK, true>(KH, KL, 16 * cb, kb), op_row<SU, true>(UH, UL, 16 * jb, kb));
+            store_acc_t<SS>(S[x], SH, SL, cb, jb);
+        }
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------
