@@ -169,14 +169,19 @@ __device__ __forceinline__ size_t unit_of(int bb, int hv, int n, int Hv, int NC)
 }
 
 // ---------------------------------------------------------------------------
-// g2b_prep: one work-group of 4 waves per (sequence, value head, chunk)
+// g2b_prep: one work-group of 4 waves per (sequence, value head, chunk).  The
+// key channels are taken 64 at a time (M, Aq and the diagonal of Aq are sums
+// over them, accumulated across the halves), so that the tiles take 74 KB of
+// LDS and two work-groups share a CU.
 // ---------------------------------------------------------------------------
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
-    constexpr int LS = DK + 4;  // conflict-free for lanes (row = l%16, col = l/16)
+    constexpr int DH = 64, NH = DK / DH;  // channels per pass, passes
+    constexpr int LS = DH + 4;            // conflict-free for lanes (row = l%16, col = l/16)
     __shared__ __attribute__((aligned(16))) float sm[4 * C * LS + C];
     float *Gs = sm, *Es = Gs + C * LS, *Qs = Es + C * LS, *Ks = Qs + C * LS, *dd = Ks + C * LS;
     float *Ms = Es, *As = Qs, *Xt = Ks;  // after the tiles: M, A (stride 68), 4 x [16][48] scratch
+    static_assert(LS == 68 && C * LS >= 4 * 16 * 48, "M, A and the scratch reuse the tile space");
 
     const int u = blockIdx.x, NC = p.NC;
     const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv), hk = hv / (p.Hv / p.Hk);
@@ -185,147 +190,157 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
 
     // 1. gates: G (log2 units, 0 past T), e = sigmoid(erase) k, qs = scale q, k (z = sigmoid(write) v
     //    is formed by the forward scan from the inputs).
-    //    Thread = (4 channels, a group of RPT consecutive rows); rows past T read the last
-    //    token (L >= 1) and are zeroed, so every load is unconditional.  The in-chunk prefix
-    //    of g is taken over the thread's rows, then the totals of the earlier row groups
-    //    are added.
-    constexpr int NQ = DK / 4, NRG = 256 / NQ, RPT = C / NRG;
-    __shared__ float tot[NRG * DK];
+    //    Thread = (4 channels of the pass, a group of RPT consecutive rows); rows past T read
+    //    the last token (L >= 1) and are zeroed, so every load is unconditional.  The in-chunk
+    //    prefix of g is taken over the thread's rows, then the totals of the earlier row
+    //    groups are added.  Both passes' loads are issued before any is used.
+    constexpr int NQ = DH / 4, NRG = 256 / NQ, RPT = C / NRG;
+    __shared__ float tot[NRG * DH];
+    const int cq = (tid % NQ) * 4, rg = tid / NQ;
+    In4<TIn> rk[NH][RPT], rq[NH][RPT], ra[NH][RPT], re[NH][RPT];
+    f4 al[NH];
     {
         const TIn *qb = static_cast<const TIn *>(p.q), *kb = static_cast<const TIn *>(p.k);
         const TIn *ab = static_cast<const TIn *>(p.a), *eb = static_cast<const TIn *>(p.erase);
-        const int c = (tid % NQ) * 4, rg = tid / NQ;
-        const f4 al = *reinterpret_cast<const f4 *>(p.A_log + (size_t)hv * DK + c);
-        f4 rate;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rate[j] = -exp_fast(al[j]) * LOG2E;
-        f4 run = {0, 0, 0, 0}, gr[RPT];
-        // every row's loads issued before any is used (converted in the loop below):
-        // interleaved with the arithmetic, only a few were in flight at a time
-        In4<TIn> rk[RPT], rq[RPT], ra[RPT], re[RPT];
+        for (int h = 0; h < NH; ++h) {
+            const int c = DH * h + cq;
+            al[h] = *reinterpret_cast<const f4 *>(p.A_log + (size_t)hv * DK + c);
 #pragma unroll
-        for (int x = 0; x < RPT; ++x) {
-            const int tl = min(rg * RPT + x, L - 1);
-            const size_t kq = (((size_t)bb * p.T + t0 + tl) * p.Hk + hk) * DK + c;
-            const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
-            rk[x].load(kb, kq);
-            rq[x].load(qb, kq);
-            ra[x].load(ab, ka);
-            re[x].load(eb, ka);
-        }
-#pragma unroll
-        for (int x = 0; x < RPT; ++x) {
-            const int t = rg * RPT + x;
-            const f4 kk = rk[x].get(), qq = rq[x].get(), aa = ra[x].get(), ee = re[x].get();
-            const float on = t < L ? 1.f : 0.f;
-            f4 ev, qv, kv;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                run[j] += rate[j] * softplus_fast(aa[j]) * on;
-                ev[j] = sigmoid_fast(ee[j]) * kk[j] * on;
-                qv[j] = p.scale * qq[j] * on;
-                kv[j] = kk[j] * on;
+            for (int x = 0; x < RPT; ++x) {
+                const int tl = min(rg * RPT + x, L - 1);
+                const size_t kq = (((size_t)bb * p.T + t0 + tl) * p.Hk + hk) * DK + c;
+                const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
+                rk[h][x].load(kb, kq);
+                rq[h][x].load(qb, kq);
+                ra[h][x].load(ab, ka);
+                re[h][x].load(eb, ka);
             }
-            gr[x] = run;
-            *reinterpret_cast<f4 *>(Es + t * LS + c) = ev;
-            *reinterpret_cast<f4 *>(Qs + t * LS + c) = qv;
-            *reinterpret_cast<f4 *>(Ks + t * LS + c) = kv;
-        }
-        *reinterpret_cast<f4 *>(tot + rg * DK + c) = run;
-        __syncthreads();
-        f4 off = {0, 0, 0, 0};
-        for (int x = 0; x < rg; ++x) off += *reinterpret_cast<const f4 *>(tot + x * DK + c);
-#pragma unroll
-        for (int x = 0; x < RPT; ++x) *reinterpret_cast<f4 *>(Gs + (rg * RPT + x) * LS + c) = gr[x] + off;
-    }
-    __syncthreads();
-    // 3. images, gamma_C and the diagonal of Aq (q_t . k_t, no decay)
-    {
-        const size_t ub = (size_t)u * C * DK;
-        for (int i = tid; i < C * DK / 4; i += 256) {
-            const int t = i / (DK / 4), c = (i % (DK / 4)) * 4;
-            const f4 G = *reinterpret_cast<const f4 *>(Gs + t * LS + c);
-            const f4 GC = *reinterpret_cast<const f4 *>(Gs + (C - 1) * LS + c);
-            f4 eg, kg;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                eg[j] = ex2(G[j]);
-                kg[j] = ex2(GC[j] - G[j]);
-            }
-            *reinterpret_cast<f4 *>(ws.Et + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Es + t * LS + c) * eg;
-            *reinterpret_cast<f4 *>(ws.Qt + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Qs + t * LS + c) * eg;
-            *reinterpret_cast<f4 *>(ws.Kh + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Ks + t * LS + c) * kg;
-        }
-        for (int c = tid; c < DK; c += 256) ws.gC[(size_t)u * DK + c] = ex2(Gs[(C - 1) * LS + c]);
-        if (tid < C) {
-            float s = 0.f;
-            for (int c = 0; c < DK; ++c) s += Qs[tid * LS + c] * Ks[tid * LS + c];
-            dd[tid] = s;
         }
     }
-    __syncthreads();
-    // 4. M and Aq.  Tiles below the diagonal (bt > bi), reference row r = 16 bt:
-    //    sum_c [e_t e^{G_t - G_r}] [k_i e^{G_r - G_i}].  Wave w takes tiles w, w + 4.
     // tile ti = 0..5 below the diagonal, row by row: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
     // (computed: a constexpr table was placed in global memory and loaded per use)
     auto obt = [](int ti) { return ti < 1 ? 1 : ti < 3 ? 2 : 3; };
     auto obi = [&](int ti) { const int bt = obt(ti); return ti - bt * (bt - 1) / 2; };
-    f4 mO[2], qO[2];
+    f4 mO[2], qO[2], mD = {0, 0, 0, 0}, qD = {0, 0, 0, 0};
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        mO[x] = qO[x] = f4{0, 0, 0, 0};
-        const int ti = w + 4 * x;
-        if (ti < 6) {
-            const int bt = obt(ti), bi = obi(ti), r = 16 * bt, t = 16 * bt + rr, i = 16 * bi + rr;
+    for (int x = 0; x < 2; ++x) mO[x] = qO[x] = f4{0, 0, 0, 0};
+    float ddacc = 0.f;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        if (h > 0) __syncthreads();  // the previous pass is done with the tiles
+        {
+            f4 rate;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rate[j] = -exp_fast(al[h][j]) * LOG2E;
+            f4 run = {0, 0, 0, 0}, gr[RPT];
+#pragma unroll
+            for (int x = 0; x < RPT; ++x) {
+                const int t = rg * RPT + x;
+                const f4 kk = rk[h][x].get(), qq = rq[h][x].get(), aa = ra[h][x].get(), ee = re[h][x].get();
+                const float on = t < L ? 1.f : 0.f;
+                f4 ev, qv, kv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    run[j] += rate[j] * softplus_fast(aa[j]) * on;
+                    ev[j] = sigmoid_fast(ee[j]) * kk[j] * on;
+                    qv[j] = p.scale * qq[j] * on;
+                    kv[j] = kk[j] * on;
+                }
+                gr[x] = run;
+                *reinterpret_cast<f4 *>(Es + t * LS + cq) = ev;
+                *reinterpret_cast<f4 *>(Qs + t * LS + cq) = qv;
+                *reinterpret_cast<f4 *>(Ks + t * LS + cq) = kv;
+            }
+            *reinterpret_cast<f4 *>(tot + rg * DH + cq) = run;
+            __syncthreads();
+            f4 off = {0, 0, 0, 0};
+            for (int x = 0; x < rg; ++x) off += *reinterpret_cast<const f4 *>(tot + x * DH + cq);
+#pragma unroll
+            for (int x = 0; x < RPT; ++x) *reinterpret_cast<f4 *>(Gs + (rg * RPT + x) * LS + cq) = gr[x] + off;
+        }
+        __syncthreads();
+        // 3. images, gamma_C and the diagonal of Aq (q_t . k_t, no decay) for the pass's channels
+        {
+            const size_t ub = (size_t)u * C * DK + DH * h;
+            for (int i = tid; i < C * DH / 4; i += 256) {
+                const int t = i / (DH / 4), c = (i % (DH / 4)) * 4;
+                const f4 G = *reinterpret_cast<const f4 *>(Gs + t * LS + c);
+                const f4 GC = *reinterpret_cast<const f4 *>(Gs + (C - 1) * LS + c);
+                f4 eg, kg;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    eg[j] = ex2(G[j]);
+                    kg[j] = ex2(GC[j] - G[j]);
+                }
+                *reinterpret_cast<f4 *>(ws.Et + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Es + t * LS + c) * eg;
+                *reinterpret_cast<f4 *>(ws.Qt + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Qs + t * LS + c) * eg;
+                *reinterpret_cast<f4 *>(ws.Kh + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Ks + t * LS + c) * kg;
+            }
+            for (int c = tid; c < DH; c += 256) ws.gC[(size_t)u * DK + DH * h + c] = ex2(Gs[(C - 1) * LS + c]);
+            if (tid < C) {
 #pragma unroll 8
-            for (int c0 = 0; c0 < DK; c0 += 4) {
-                const int c = c0 + gg;
-                const float Gr = Gs[r * LS + c];
-                const float ft = ex2(Gs[t * LS + c] - Gr), b = Ks[i * LS + c] * ex2(Gr - Gs[i * LS + c]);
-                mO[x] = mfma_f32_k4(Es[t * LS + c] * ft, b, mO[x]);
-                qO[x] = mfma_f32_k4(Qs[t * LS + c] * ft, b, qO[x]);
+                for (int c = 0; c < DH; ++c) ddacc += Qs[tid * LS + c] * Ks[tid * LS + c];
+            }
+        }
+        // 4. M and Aq over the pass's channels.  Tiles below the diagonal (bt > bi),
+        //    reference row r = 16 bt: sum_c [e_t e^{G_t - G_r}] [k_i e^{G_r - G_i}].  Wave w
+        //    takes tiles w, w + 4.
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int ti = w + 4 * x;
+            if (ti < 6) {
+                const int bt = obt(ti), bi = obi(ti), r = 16 * bt, t = 16 * bt + rr, i = 16 * bi + rr;
+#pragma unroll 8
+                for (int c0 = 0; c0 < DH; c0 += 4) {
+                    const int c = c0 + gg;
+                    const float Gr = Gs[r * LS + c];
+                    const float ft = ex2(Gs[t * LS + c] - Gr), b = Ks[i * LS + c] * ex2(Gr - Gs[i * LS + c]);
+                    mO[x] = mfma_f32_k4(Es[t * LS + c] * ft, b, mO[x]);
+                    qO[x] = mfma_f32_k4(Qs[t * LS + c] * ft, b, qO[x]);
+                }
+            }
+        }
+        //    Diagonal tile w: dyadic levels (half sizes 8, 4, 2, 1); a pair (t > i) of
+        //    the tile belongs to the level whose 2h-block holds both with i in the
+        //    first and t in the second half; reference = first token of that half.
+        {
+            const int base = 16 * w, t = base + rr, i = base + rr;
+#pragma unroll
+            for (int hl = 8; hl >= 1; hl >>= 1) {
+                const bool tsec = (rr & hl) != 0;
+                const int rt = base + (rr & ~(hl - 1)), ri = base + ((rr | hl) & ~(hl - 1));
+                f4 aM = {0, 0, 0, 0}, aQ = {0, 0, 0, 0};
+#pragma unroll 8
+                for (int c0 = 0; c0 < DH; c0 += 4) {
+                    const int c = c0 + gg;
+                    float ae = 0.f, aq = 0.f, b = 0.f;
+                    if (tsec) {
+                        const float ft = ex2(Gs[t * LS + c] - Gs[rt * LS + c]);
+                        ae = Es[t * LS + c] * ft;
+                        aq = Qs[t * LS + c] * ft;
+                    } else {
+                        b = Ks[i * LS + c] * ex2(Gs[ri * LS + c] - Gs[i * LS + c]);
+                    }
+                    aM = mfma_f32_k4(ae, b, aM);
+                    aQ = mfma_f32_k4(aq, b, aQ);
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int tl = 4 * gg + s;
+                    if (((tl ^ rr) & ~(2 * hl - 1)) == 0 && (tl & hl) && !(rr & hl)) {
+                        mD[s] += aM[s];
+                        qD[s] += aQ[s];
+                    }
+                }
             }
         }
     }
-    //    Diagonal tile w: dyadic levels (half sizes 8, 4, 2, 1); a pair (t > i) of
-    //    the tile belongs to the level whose 2h-block holds both with i in the
-    //    first and t in the second half; reference = first token of that half.
-    f4 mD = {0, 0, 0, 0}, qD = {0, 0, 0, 0};
-    {
-        const int base = 16 * w, t = base + rr, i = base + rr;
+    if (tid < C) dd[tid] = ddacc;
+    __syncthreads();  // Es, Qs, Ks are reused below; dd complete
 #pragma unroll
-        for (int h = 8; h >= 1; h >>= 1) {
-            const bool tsec = (rr & h) != 0;
-            const int rt = base + (rr & ~(h - 1)), ri = base + ((rr | h) & ~(h - 1));
-            f4 aM = {0, 0, 0, 0}, aQ = {0, 0, 0, 0};
-#pragma unroll 8
-            for (int c0 = 0; c0 < DK; c0 += 4) {
-                const int c = c0 + gg;
-                float ae = 0.f, aq = 0.f, b = 0.f;
-                if (tsec) {
-                    const float ft = ex2(Gs[t * LS + c] - Gs[rt * LS + c]);
-                    ae = Es[t * LS + c] * ft;
-                    aq = Qs[t * LS + c] * ft;
-                } else {
-                    b = Ks[i * LS + c] * ex2(Gs[ri * LS + c] - Gs[i * LS + c]);
-                }
-                aM = mfma_f32_k4(ae, b, aM);
-                aQ = mfma_f32_k4(aq, b, aQ);
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int tl = 4 * gg + s;
-                if (((tl ^ rr) & ~(2 * h - 1)) == 0 && (tl & h) && !(rr & h)) {
-                    mD[s] += aM[s];
-                    qD[s] += aQ[s];
-                }
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            if (4 * gg + s == rr) qD[s] += dd[base + rr];
-    }
-    __syncthreads();  // Es, Qs, Ks are reused below
+    for (int s = 0; s < 4; ++s)
+        if (4 * gg + s == rr) qD[s] += dd[16 * w + rr];
     // Aq to the workspace (zero above the diagonal); M into LDS (zero on and above)
     {
         float *Aqu = ws.Aq + (size_t)u * C * C;
