@@ -141,16 +141,19 @@ template <> struct In1<float> {
     __device__ __forceinline__ float get() const { return x; }
 };
 
-// A ROWS x COLS float32 tile (row-major, contiguous) held in registers between
-// its global load and its LDS store: the scans load the next chunk's operands
-// while computing the current one.
-template <int ROWS, int COLS, int NT = 256> struct RegTile {
+// A ROWS x COLS float32 tile (row-major, source rows SS floats apart) held in
+// registers between its global load and its LDS store: the scans load the next
+// chunk's operands while computing the current one.
+template <int ROWS, int COLS, int NT = 256, int SS = COLS> struct RegTile {
     static constexpr int PER = ROWS * COLS / 4 / NT;
     static_assert(ROWS * COLS / 4 % NT == 0, "tile size");
     f4 x[PER];
     __device__ __forceinline__ void load(const float *__restrict__ src) {
 #pragma unroll
-        for (int j = 0; j < PER; ++j) x[j] = *reinterpret_cast<const f4 *>(src + (size_t)(threadIdx.x + j * NT) * 4);
+        for (int j = 0; j < PER; ++j) {
+            const int i = threadIdx.x + j * NT, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
+            x[j] = *reinterpret_cast<const f4 *>(src + (size_t)r * SS + c);
+        }
     }
     template <int LS> __device__ __forceinline__ void store(float *dst, float f = 1.f) const {
 #pragma unroll
@@ -458,10 +461,11 @@ __device__ __forceinline__ void mma_x3(f4 &acc, const uint16_t *ah, const uint16
 }
 
 // A ROWS x COLS float32 register tile (see RegTile) stored split: rows of stride LS
-template <int ROWS, int COLS, int LS>
-__device__ __forceinline__ void store_split(const RegTile<ROWS, COLS> &t, uint16_t *hi, uint16_t *lo, float f = 1.f) {
+template <int ROWS, int COLS, int LS, int SS = COLS>
+__device__ __forceinline__ void store_split(const RegTile<ROWS, COLS, 256, SS> &t, uint16_t *hi, uint16_t *lo,
+                                            float f = 1.f) {
 #pragma unroll
-    for (int j = 0; j < RegTile<ROWS, COLS>::PER; ++j) {
+    for (int j = 0; j < RegTile<ROWS, COLS, 256, SS>::PER; ++j) {
         const int i = threadIdx.x + j * 256, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
         u16x4 h, l;
         split4(t.x[j] * f, h, l);
@@ -866,13 +870,17 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
 // ---------------------------------------------------------------------------
 // g2b_products: one work-group per chunk.  Wave w owns the rows of block w.
 // The products over the value columns (dEt, dQt, dKh, dAq, dA) take split
-// operands; the 64-deep ones of dM stay on the float32 matrix cores.
+// operands, the value columns in passes of DH (each pass's tiles staged in LDS,
+// the sums kept in the accumulators across passes), so that a work-group takes
+// 74 KB of LDS and two share a CU; the 64-deep products of dM stay on the float32
+// matrix cores.
 // ---------------------------------------------------------------------------
 template <int DK, int DV> struct ProdLds {
-    static constexpr int KP = DV + 8;                      // split row stride (elements)
+    static constexpr int DH = DV < 64 ? DV : 64;           // value columns per pass
+    static constexpr int KP = DH + 8;                      // split row stride (elements)
     static constexpr int S_ = 0, P_ = 2 * DK * KP, O_ = P_ + 2 * C * KP, END = O_ + 2 * C * KP;
     static constexpr int BYTES_SPLIT = END * 2;
-    // phase 3 float32 tiles: dA [C][80], A [C][80], A [C][68], X [C][68]
+    // dM stage, float32 tiles: dA [C][80], A [C][80], A [C][68], X [C][68]
     static constexpr int BYTES_F32 = 4 * (2 * C * 80 + 2 * C * 68);
     static constexpr int BYTES = BYTES_SPLIT > BYTES_F32 ? BYTES_SPLIT : BYTES_F32;
 };
@@ -880,133 +888,162 @@ template <int DK, int DV> struct ProdLds {
 template <typename TIn, int DK, int DV>
 __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws) {
     typedef ProdLds<DK, DV> PL;
-    constexpr int KP = PL::KP;
+    constexpr int DH = PL::DH, NP = DV / DH, KP = PL::KP, NCB = DK / 16, NS = 3 * NP;
+    constexpr int NO = C * DH / 8 / 256;                                  // dO loads per thread and pass
     constexpr bool DO_LO = !std::is_same<TIn, bf16_t>::value;  // dO is exact in bfloat16 for bf16 inputs
     __shared__ __attribute__((aligned(16))) uint16_t lds[PL::BYTES / 2];
-    // phase 1: Sn in S, -dR in P, dO in O; phase 2: dS1 in S, U in P, dO in O;
-    // phase 3: dU in P, R in O, then the float32 tiles from the start
+    // stage 0: Sn in S, -dR in P, dO in O; stage 1: dS1 in S, U in P, dO in O;
+    // stage 2: dU in P, R in O (each for the value columns of one pass); then the
+    // float32 tiles of dM from the start
     uint16_t *SH = lds + PL::S_, *SL = SH + DK * KP, *PH = lds + PL::P_, *PLo = PH + C * KP, *OH = lds + PL::O_,
              *OL = OH + C * KP;
     const int u = blockIdx.x, NC = p.NC;
     const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv);
     const int t0 = n * C, L = min(C, p.T - t0);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4;
-    const size_t uC = (size_t)u * C;
+    const size_t uC = (size_t)u * C, uS = (size_t)u * DK * DV;
     const TIn *dout = static_cast<const TIn *>(p.dout);
 
-    // phase 1: dEt = -dR Sn^T, dQt = dO Sn^T, dgamma_C = rowsum(dS1 . Sn)
-    {
-        // dO: 8 values per load (rows past T read the last token, zeroed)
-        In8<TIn> xo[C * DV / 8 / 256];
+    // the next step's tiles, in registers from their global loads to their LDS stores
+    RegTile<DK, DH, 256, DV> rS;
+    RegTile<C, DH, 256, DV> rP, rO;
+    In8<TIn> xo[NO];  // dO (rows past T read the last token and are zeroed at the store)
+    RegTile<C, C> rA;
+    // step s: stage s / NP over the value columns j0 = DH (s % NP) ..
+    auto load_step = [&](int s) {
+        const int st = s / NP, j0 = DH * (s % NP);
+        if (st < 2) {
+            rS.load((st == 0 ? ws.Sn : ws.dS1) + uS + j0);
+            rP.load((st == 0 ? ws.dR : ws.U) + uC * DV + j0);
 #pragma unroll
-        for (int it = 0; it < C * DV / 8 / 256; ++it) {
-            const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
-            xo[it].load(dout, (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j);
-        }
-        RegTile<DK, DV> rS;
-        RegTile<C, DV> rR;
-        rS.load(ws.Sn + (size_t)u * DK * DV);
-        rR.load(ws.dR + uC * DV);
-#pragma unroll
-        for (int it = 0; it < C * DV / 8 / 256; ++it) {
-            const int i = tid + 256 * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8;
-            f4 lo, hi;
-            xo[it].get(lo, hi);
-            const float on = t < L ? 1.f : 0.f;
-            u16x4 h0, l0, h1, l1;
-            split4(lo * on, h0, l0);
-            split4(hi * on, h1, l1);
-            *reinterpret_cast<u16x4 *>(OH + t * KP + j) = h0;
-            *reinterpret_cast<u16x4 *>(OH + t * KP + j + 4) = h1;
-            if constexpr (DO_LO) {
-                *reinterpret_cast<u16x4 *>(OL + t * KP + j) = l0;
-                *reinterpret_cast<u16x4 *>(OL + t * KP + j + 4) = l1;
+            for (int it = 0; it < NO; ++it) {
+                const int i = tid + 256 * it, t = i / (DH / 8), j = (i % (DH / 8)) * 8, tl = min(t, L - 1);
+                xo[it].load(dout, (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j0 + j);
             }
+        } else {
+            rP.load(ws.dU + uC * DV + j0);
+            rO.load(ws.R + uC * DV + j0);
         }
-        store_split<DK, DV, KP>(rS, SH, SL);
-        store_split<C, DV, KP>(rR, PH, PLo, -1.f);
-    }
-    // phase 2's inputs, in flight during phase 1's products (one work-group per CU:
-    // nothing else would hide a phase's loads)
-    RegTile<DK, DV> nS1;
-    RegTile<C, DV> nU;
-    nS1.load(ws.dS1 + (size_t)u * DK * DV);
-    nU.load(ws.U + uC * DV);
-    __syncthreads();
-    for (int cb = 0; cb < DK / 16; ++cb) {
-        f4 e = {0, 0, 0, 0}, q = {0, 0, 0, 0};
-        mma_x3<DV, KP, KP, true>(e, PH + 16 * w * KP, PLo + 16 * w * KP, SH + 16 * cb * KP, SL + 16 * cb * KP);
-        mma_x3<DV, KP, KP, DO_LO>(q, OH + 16 * w * KP, OL + 16 * w * KP, SH + 16 * cb * KP, SL + 16 * cb * KP);
+    };
+    auto store_step = [&](int s) {
+        const int st = s / NP;
+        if (st < 2) {
+            store_split<DK, DH, KP, DV>(rS, SH, SL);
+            store_split<C, DH, KP, DV>(rP, PH, PLo, st == 0 ? -1.f : 1.f);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const size_t o = (uC + 16 * w + 4 * gg + s) * DK + 16 * cb + rr;
-            ws.dEt[o] = e[s];
-            ws.dQt[o] = q[s];
+            for (int it = 0; it < NO; ++it) {
+                const int i = tid + 256 * it, t = i / (DH / 8), j = (i % (DH / 8)) * 8;
+                f4 lo, hi;
+                xo[it].get(lo, hi);
+                const float on = t < L ? 1.f : 0.f;
+                u16x4 h0, l0, h1, l1;
+                split4(lo * on, h0, l0);
+                split4(hi * on, h1, l1);
+                *reinterpret_cast<u16x4 *>(OH + t * KP + j) = h0;
+                *reinterpret_cast<u16x4 *>(OH + t * KP + j + 4) = h1;
+                if constexpr (DO_LO) {
+                    *reinterpret_cast<u16x4 *>(OL + t * KP + j) = l0;
+                    *reinterpret_cast<u16x4 *>(OL + t * KP + j + 4) = l1;
+                }
+            }
+        } else {
+            store_split<C, DH, KP, DV>(rP, PH, PLo);
+            store_split<C, DH, KP, DV>(rO, OH, OL);
+        }
+    };
+
+    f4 e[NCB], q[NCB], kh[NCB], aq[4], dA[4];
+#pragma unroll
+    for (int x = 0; x < NCB; ++x) e[x] = q[x] = kh[x] = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) aq[x] = dA[x] = f4{0, 0, 0, 0};
+    float dgs = 0.f;  // dgamma_C partial: channel tid / 2, half tid % 2 of each pass's columns
+
+    load_step(0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int st = s / NP, j0 = DH * (s % NP);
+        if (s > 0) __syncthreads();  // the previous step's products are done with the LDS
+        store_step(s);
+        __syncthreads();
+        if (s + 1 < NS) load_step(s + 1);
+        if (s + 1 == NS) rA.load(ws.A + uC * C);
+        if (st == 0) {
+            // dEt = -dR Sn^T, dQt = dO Sn^T; dgamma_C = rowsum(dS1 . Sn)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                mma_x3<DH, KP, KP, true>(e[cb], PH + 16 * w * KP, PLo + 16 * w * KP, SH + 16 * cb * KP,
+                                         SL + 16 * cb * KP);
+                mma_x3<DH, KP, KP, DO_LO>(q[cb], OH + 16 * w * KP, OL + 16 * w * KP, SH + 16 * cb * KP,
+                                          SL + 16 * cb * KP);
+            }
+            if (tid < 2 * DK) {
+                const int c = tid >> 1, h = tid & 1;
+                const float *d1 = ws.dS1 + uS + (size_t)c * DV + j0 + h * (DH / 2);
+#pragma unroll
+                for (int j = 0; j < DH / 2; j += 4) {
+                    const f4 x = *reinterpret_cast<const f4 *>(d1 + j);
+                    const int o = c * KP + h * (DH / 2) + j;
+                    const u16x4 yh = *reinterpret_cast<const u16x4 *>(SH + o), yl = *reinterpret_cast<const u16x4 *>(SL + o);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) dgs += x[k] * (bf16_to_f32(yh[k]) + bf16_to_f32(yl[k]));
+                }
+            }
+            if (s % NP == NP - 1) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const size_t o = (uC + 16 * w + 4 * gg + x) * DK + 16 * cb + rr;
+                        ws.dEt[o] = e[cb][x];
+                        ws.dQt[o] = q[cb][x];
+                    }
+                const float d2 = dgs + __shfl_xor(dgs, 1);
+                if (tid < 2 * DK && !(tid & 1)) ws.dgC[(size_t)u * DK + (tid >> 1)] = d2;
+            }
+        } else if (st == 1) {
+            // dKh = U dS1^T, dAq = tril(dO U^T)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                mma_x3<DH, KP, KP, true>(kh[cb], PH + 16 * w * KP, PLo + 16 * w * KP, SH + 16 * cb * KP,
+                                         SL + 16 * cb * KP);
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib)
+                if (ib <= w)
+                    mma_x3<DH, KP, KP, DO_LO>(aq[ib], OH + 16 * w * KP, OL + 16 * w * KP, PH + 16 * ib * KP,
+                                              PLo + 16 * ib * KP);
+            if (s % NP == NP - 1) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) ws.dKh[(uC + 16 * w + 4 * gg + x) * DK + 16 * cb + rr] = kh[cb][x];
+                float *dAqu = ws.dAq + uC * C;
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int t = 16 * w + 4 * gg + x, i = 16 * ib + rr;
+                        dAqu[t * C + i] = i <= t ? aq[ib][x] : 0.f;
+                    }
+            }
+        } else {
+            // dA = dU R^T
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib)
+                mma_x3<DH, KP, KP, true>(dA[ib], PH + 16 * w * KP, PLo + 16 * w * KP, OH + 16 * ib * KP,
+                                         OL + 16 * ib * KP);
         }
     }
-    if (tid < 2 * DK) {
-        const int c = tid >> 1, h = tid & 1;
-        const float *d1 = ws.dS1 + ((size_t)u * DK + c) * DV + h * (DV / 2);
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < DV / 2; j += 4) {
-            const f4 x = *reinterpret_cast<const f4 *>(d1 + j);
-            const int o = c * KP + h * (DV / 2) + j;
-            const u16x4 yh = *reinterpret_cast<const u16x4 *>(SH + o), yl = *reinterpret_cast<const u16x4 *>(SL + o);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) s += x[k] * (bf16_to_f32(yh[k]) + bf16_to_f32(yl[k]));
-        }
-        s += __shfl_xor(s, 1);
-        if (!h) ws.dgC[(size_t)u * DK + c] = s;
-    }
     __syncthreads();
-    // phase 2: dKh = U dS1^T, dAq = tril(dO U^T)
-    store_split<DK, DV, KP>(nS1, SH, SL);
-    store_split<C, DV, KP>(nU, PH, PLo);
-    // phase 3's inputs, in flight during phase 2's products (A once, for both copies)
-    RegTile<C, DV> nR, ndU;
-    RegTile<C, C> nA;
-    nR.load(ws.R + uC * DV);
-    ndU.load(ws.dU + uC * DV);
-    nA.load(ws.A + uC * C);
-    __syncthreads();
-    for (int cb = 0; cb < DK / 16; ++cb) {
-        f4 acc = {0, 0, 0, 0};
-        mma_x3<DV, KP, KP, true>(acc, PH + 16 * w * KP, PLo + 16 * w * KP, SH + 16 * cb * KP, SL + 16 * cb * KP);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) ws.dKh[(uC + 16 * w + 4 * gg + s) * DK + 16 * cb + rr] = acc[s];
-    }
-    float *dAqu = ws.dAq + uC * C;
-    for (int ib = 0; ib < 4; ++ib) {
-        f4 acc = {0, 0, 0, 0};
-        if (ib <= w)
-            mma_x3<DV, KP, KP, DO_LO>(acc, OH + 16 * w * KP, OL + 16 * w * KP, PH + 16 * ib * KP, PLo + 16 * ib * KP);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int t = 16 * w + 4 * gg + s, i = 16 * ib + rr;
-            dAqu[t * C + i] = i <= t ? acc[s] : 0.f;
-        }
-    }
-    __syncthreads();
-    // phase 3: dA = dU R^T; X = A^T dA; dM = -strict_tril(X A^T)
-    store_split<C, DV, KP>(ndU, PH, PLo);
-    store_split<C, DV, KP>(nR, OH, OL);
-    __syncthreads();
-    f4 dA[4];
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
-        dA[ib] = f4{0, 0, 0, 0};
-        mma_x3<DV, KP, KP, true>(dA[ib], PH + 16 * w * KP, PLo + 16 * w * KP, OH + 16 * ib * KP, OL + 16 * ib * KP);
-    }
-    __syncthreads();
+    // X = A^T dA; dM = -strict_tril(X A^T), in float32
     float *f32s = reinterpret_cast<float *>(lds);
     float *dAs = f32s, *A80 = f32s + C * 80, *A68 = f32s + 2 * C * 80, *Xs = A68 + C * 68;
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) dAs[(16 * w + 4 * gg + s) * 80 + 16 * ib + rr] = dA[ib][s];
-    nA.template store<80>(A80);
-    nA.template store<68>(A68);
+        for (int x = 0; x < 4; ++x) dAs[(16 * w + 4 * gg + x) * 80 + 16 * ib + rr] = dA[ib][x];
+    rA.template store<80>(A80);
+    rA.template store<68>(A68);
     __syncthreads();
     // X[i][s] = sum_t A[t][i] dA[t][s] (A[t][i] = 0 for t < i): rows i of block w
 #pragma unroll
@@ -1018,7 +1055,7 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) Xs[(16 * w + 4 * gg + s) * 68 + 16 * sb + rr] = dA[sb][s];
+        for (int x = 0; x < 4; ++x) Xs[(16 * w + 4 * gg + x) * 68 + 16 * sb + rr] = dA[sb][x];
     __syncthreads();
     // dM[i][q] = -sum_s X[i][s] A[q][s] (A[q][s] = 0 for s > q), strictly lower
     float *dMu = ws.dM + uC * C;
@@ -1026,9 +1063,9 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
         f4 acc = {0, 0, 0, 0};
         if (qb <= w) mma<C, 68, 1, 1, 68>(acc, Xs + 16 * w * 68, A68 + 16 * qb * 68);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int i = 16 * w + 4 * gg + s, qq = 16 * qb + rr;
-            dMu[i * C + qq] = qq < i ? -acc[s] : 0.f;
+        for (int x = 0; x < 4; ++x) {
+            const int i = 16 * w + 4 * gg + x, qq = 16 * qb + rr;
+            dMu[i * C + qq] = qq < i ? -acc[x] : 0.f;
         }
     }
 }
