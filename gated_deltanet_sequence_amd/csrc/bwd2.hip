@@ -30,7 +30,7 @@
 //   g2b_fwd_scan   per (sequence, head, 32 value columns): S_n, R, U over the chunks
 //   g2b_bwd_scan   the same slices in reverse: dS_{n+1}, dU, dR; dS_0
 //   g2b_products   per chunk: dEt, dQt, dKh, dgamma_C, dAq, dM
-//   g2b_local      per (chunk, 64 key channels): pairwise decay sums, gate chain
+//   g2b_local      per (chunk, 32 key channels): pairwise decay sums, gate chain
 //   g2b_reduce     dq, dk over the value heads of a key head; dA_log over chunks
 // Decay factors never exceed 1: a product e^{G_t - G_i} over a 16-token block
 // pair below the diagonal is split at the block's first row r (i < r <= t) into
@@ -1071,49 +1071,55 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
 }
 
 // ---------------------------------------------------------------------------
-// g2b_local: one work-group of 8 waves per (chunk, 64 key channels).  Wave w
-// owns rows 8w .. 8w+7, half of 16-token block b = w/2: first the block pairs
-// below the diagonal on the matrix cores for block b and two of its four
-// 16-channel tiles (rows t of block b against every earlier block, rows i of
-// block b against every later block), then the pairs inside block b that its
-// own rows take part in, on the vector unit (lane = channel), then the chain
-// rule for its rows.
+// g2b_local: one work-group of 4 waves per (chunk, 32 key channels), the
+// channel groups of a chunk on one XCD (their reads of the chunk's dM and dA_qk
+// meet in its L2).  Wave w owns 16-token block b = w: first the block pairs
+// below the diagonal on the matrix cores for block b and both 16-channel tiles
+// (rows t of block b against every earlier block, rows i of block b against
+// every later block); then, lane = (channel, half of the block), the pairs
+// inside block b that its 8 rows take part in, on the vector unit; then the
+// chain rule for those rows.  73 KB of LDS: two work-groups share a CU.
 // ---------------------------------------------------------------------------
-constexpr int LOCAL_NT = 512;
+constexpr int LOCAL_NT = 256, LOCAL_CH = 32;
 
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
-    constexpr int CG = DK / 64, NW = LOCAL_NT / 64;
-    __shared__ __attribute__((aligned(16))) float Gs[C * 64], Ks[C * 64], Es[C * 64], Qs[C * 64], dMs[C * C],
-        dAqs[C * C], Te[C * 64], Tq[C * 64], Ik[C * 64], blk[NW * 64], gcp[NW * 64], alp[NW * 64];
-    const int cg = blockIdx.x % CG, u = blockIdx.x / CG, NC = p.NC;
+__global__ __launch_bounds__(LOCAL_NT, 2) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
+    constexpr int CG = DK / LOCAL_CH, NRG = 2 * (LOCAL_NT / 64);  // channel groups; row groups of 8 tokens
+    constexpr int LS = LOCAL_CH + 4;  // channel-tile row stride: the two half-waves' rows on disjoint banks
+    constexpr int MS = C + 4;         // dM / dA_qk row stride: conflict-free matrix-core A operands
+    __shared__ __attribute__((aligned(16))) float Gs[C * LS], Ks[C * LS], Es[C * LS], Qs[C * LS], dMs[C * MS],
+        dAqs[C * MS], blk[NRG * LOCAL_CH], gcp[NRG * LOCAL_CH], alp[NRG * LOCAL_CH];
+    // work-group -> (unit, channel group): work-group i runs on XCD i % 8, so units go
+    // eight at a time across the XCDs with the channel groups of each on one of them
+    const int units = p.B * p.Hv * p.NC, full = units / 8 * 8 * CG;
+    int u, cg;
+    if ((int)blockIdx.x < full) {
+        const int j = blockIdx.x / 8;
+        u = 8 * (j / CG) + (int)blockIdx.x % 8;
+        cg = j % CG;
+    } else {
+        const int r = (int)blockIdx.x - full;
+        u = units / 8 * 8 + r / CG;
+        cg = r % CG;
+    }
+    const int NC = p.NC;
     const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv), hk = hv / (p.Hv / p.Hk);
     const int t0 = n * C, L = min(C, p.T - t0);
-    const int tid = threadIdx.x, w = tid >> 6, cl = tid & 63, c = 64 * cg + cl, rr = cl & 15, gg = cl >> 4;
-    const int b = w >> 1, half = w & 1, r0 = 8 * w;  // block, half of it, first own row
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4;
+    const int cl = lane & 31, half = lane >> 5, c = LOCAL_CH * cg + cl;
+    const int b = w, rg = 2 * w + half, r0 = 8 * rg;  // block, row group, first own row
     const TIn *q = static_cast<const TIn *>(p.q), *k = static_cast<const TIn *>(p.k);
     const TIn *a = static_cast<const TIn *>(p.a), *er = static_cast<const TIn *>(p.erase);
     const float Al = p.A_log[(size_t)hv * DK + c], rate = exp_fast(Al);
 
-    // inputs of the chain rule, loaded first so that their latency overlaps the pair sums
-    const size_t ub = (size_t)u * C * DK;
-    float pdE[8], pdQ[8], pdK[8];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-        pdE[x] = ws.dEt[ub + (r0 + x) * DK + c];
-        pdQ[x] = ws.dQt[ub + (r0 + x) * DK + c];
-        pdK[x] = ws.dKh[ub + (r0 + x) * DK + c];
-    }
-    const float pgC = ws.dgC[(size_t)u * DK + c];
     // dM and dA_qk tiles, loaded with the rest and stored to LDS after the gates
     RegTile<C, C, LOCAL_NT> rM, rAq;
     rM.load(ws.dM + (size_t)u * C * C);
     rAq.load(ws.dAq + (size_t)u * C * C);
 
-    // gates of the wave's rows; the in-chunk prefix of g runs over them, then the
+    // gates of the lane's rows; the in-chunk prefix of g runs over them, then the
     // totals of the earlier row groups are added
-    // (the logits a and the erase gate stay in registers for the chain rule: reloading
-    // them there, inside its row-bounds branch, waited for each row's loads in turn)
+    // (the logits a and the erase gate stay in registers for the chain rule)
     float grun = 0.f, gpre[8], a_row[8], beta_row[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
@@ -1128,19 +1134,19 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
         const float ev = beta_row[x] * kv;
         const float qv = p.scale * io<TIn>::ld(q, kq) * on;
         gpre[x] = grun;
-        Ks[t * 64 + cl] = kv;
-        Es[t * 64 + cl] = ev;
-        Qs[t * 64 + cl] = qv;
+        Ks[t * LS + cl] = kv;
+        Es[t * LS + cl] = ev;
+        Qs[t * LS + cl] = qv;
     }
-    blk[w * 64 + cl] = grun;
-    rM.template store<C>(dMs);
-    rAq.template store<C>(dAqs);
+    blk[rg * LOCAL_CH + cl] = grun;
+    rM.template store<MS>(dMs);
+    rAq.template store<MS>(dAqs);
     __syncthreads();
     {
         float off = 0.f;
-        for (int x = 0; x < w; ++x) off += blk[x * 64 + cl];
+        for (int x = 0; x < rg; ++x) off += blk[x * LOCAL_CH + cl];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) Gs[(r0 + x) * 64 + cl] = gpre[x] + off;
+        for (int x = 0; x < 8; ++x) Gs[(r0 + x) * LS + cl] = gpre[x] + off;
     }
     __syncthreads();
 
@@ -1150,91 +1156,132 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
     //     de_t  = e^{G_t - G_r} sum_{i < r} dM_ti  k_i e^{G_r - G_i}, dqs_t likewise with dAq
     //   rows i of block b, each later block b2 with reference r = 16 b2:
     //     dk_i += e^{G_r - G_i} sum_{t in b2} dM_ti e_t e^{G_t - G_r} + dAq_ti qs_t e^{G_t - G_r}
-    for (int ct = 2 * half; ct < 2 * half + 2; ++ct) {
+    // each tile's sums go to lane = (channel, half) as soon as they are complete: row
+    // 16 b + 8 half + x of channel cl is element x % 4 of tile cl / 16 in lane
+    // 16 (2 half + x / 4) + cl % 16
+    float sde[8], sdq[8], sdk[8];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
         const int cc = 16 * ct + rr;
-        f4 aE = {0, 0, 0, 0}, aQ = {0, 0, 0, 0}, aK = {0, 0, 0, 0};
+        f4 e4 = {0, 0, 0, 0}, q4 = {0, 0, 0, 0}, k4 = {0, 0, 0, 0};
         if (b > 0) {
             const int r = 16 * b;
-            const float Gr = Gs[r * 64 + cc];
+            const float Gr = Gs[r * LS + cc];
             // kept rolled: unrolled by whole 16-row blocks it measured slower
 #pragma unroll 1
             for (int i0 = 0; i0 < r; i0 += 4) {
                 const int i = i0 + gg;
-                const float bv = Ks[i * 64 + cc] * ex2(Gr - Gs[i * 64 + cc]);
-                aE = mfma_f32_k4(dMs[(r + rr) * C + i], bv, aE);
-                aQ = mfma_f32_k4(dAqs[(r + rr) * C + i], bv, aQ);
+                const float bv = Ks[i * LS + cc] * ex2(Gr - Gs[i * LS + cc]);
+                e4 = mfma_f32_k4(dMs[(r + rr) * MS + i], bv, e4);
+                q4 = mfma_f32_k4(dAqs[(r + rr) * MS + i], bv, q4);
             }
         }
         for (int b2 = b + 1; b2 < 4; ++b2) {
             const int r = 16 * b2;
-            const float Gr = Gs[r * 64 + cc];
+            const float Gr = Gs[r * LS + cc];
             f4 acc = {0, 0, 0, 0};
 #pragma unroll
             for (int k0 = 0; k0 < 16; k0 += 4) {
                 const int t = r + k0 + gg;
-                const float f = ex2(Gs[t * 64 + cc] - Gr);
-                acc = mfma_f32_k4(dMs[t * C + 16 * b + rr], Es[t * 64 + cc] * f, acc);
-                acc = mfma_f32_k4(dAqs[t * C + 16 * b + rr], Qs[t * 64 + cc] * f, acc);
+                const float f = ex2(Gs[t * LS + cc] - Gr);
+                acc = mfma_f32_k4(dMs[t * MS + 16 * b + rr], Es[t * LS + cc] * f, acc);
+                acc = mfma_f32_k4(dAqs[t * MS + 16 * b + rr], Qs[t * LS + cc] * f, acc);
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int i = 16 * b + 4 * gg + s;
-                aK[s] += acc[s] * ex2(Gs[r * 64 + 16 * ct + rr] - Gs[i * 64 + 16 * ct + rr]);
+                k4[s] += acc[s] * ex2(Gr - Gs[i * LS + cc]);
             }
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int t = 16 * b + 4 * gg + s, ch = 16 * ct + rr;
-            const float F = b > 0 ? ex2(Gs[t * 64 + ch] - Gs[16 * b * 64 + ch]) : 0.f;
-            Te[t * 64 + ch] = aE[s] * F;
-            Tq[t * 64 + ch] = aQ[s] * F;
-            Ik[t * 64 + ch] = aK[s];
+            const int t = 16 * b + 4 * gg + s;
+            const float F = b > 0 ? ex2(Gs[t * LS + cc] - Gs[16 * b * LS + cc]) : 0.f;
+            e4[s] *= F;
+            q4[s] *= F;
+        }
+        const bool mine = (cl >> 4) == ct;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int src = 4 * (16 * (2 * half + (x >> 2)) + (cl & 15)), s = x & 3;
+            auto take = [&](float v) {
+                return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
+            };
+            const float ve = take(e4[s]), vq = take(q4[s]), vk = take(k4[s]);
+            if (ct == 0 || mine) {
+                sde[x] = ve;
+                sdq[x] = vq;
+                sdk[x] = vk;
+            }
         }
     }
-    __syncthreads();
 
-    // pairs inside block b that the wave's rows take part in, lane = channel:
-    // E = e^{G_t - G_i}, i <= t; as t the rows r0.., as i the same rows
-    float sde[8], sdq[8], sdk[8];
+    // inputs of the chain rule, loaded here so that their latency overlaps the pair sums
+    const size_t ub = (size_t)u * C * DK;
+    float pdE[8], pdQ[8], pdK[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        pdE[x] = ws.dEt[ub + (r0 + x) * DK + c];
+        pdQ[x] = ws.dQt[ub + (r0 + x) * DK + c];
+        pdK[x] = ws.dKh[ub + (r0 + x) * DK + c];
+    }
+    const float pgC = ws.dgC[(size_t)u * DK + c];
+
+    // pairs inside block b that the lane's rows take part in (lane = channel):
+    // E = e^{G_t - G_i}, i <= t.  First the 8 x 8 sub-block of the lane's own half
+    // (as t the rows r0.., as i the same rows) ...
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
         const int t = r0 + x;
-        sde[x] = Te[t * 64 + cl];
-        sdq[x] = Tq[t * 64 + cl];
-        sdk[x] = Ik[t * 64 + cl];
-    }
-    const int base = 16 * b;
+        const float Gt = Gs[t * LS + cl];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-        const int tl = 8 * half + x, t = base + tl;
-        const float Gt = Gs[t * 64 + cl];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int o = base + j;
-            const float Go = Gs[o * 64 + cl];
-            if (j <= tl) {  // o = i <= t: row t's sums
-                const float E = ex2(Gt - Go), ko = Ks[o * 64 + cl];
-                if (j < tl) sde[x] += dMs[t * C + o] * ko * E;
-                sdq[x] += dAqs[t * C + o] * ko * E;
+        for (int j = 0; j < 8; ++j) {
+            const int o = r0 + j;
+            const float Go = Gs[o * LS + cl];
+            if (j <= x) {  // o = i <= t: row t's sums
+                const float E = ex2(Gt - Go), ko = Ks[o * LS + cl];
+                if (j < x) sde[x] += dMs[t * MS + o] * ko * E;
+                sdq[x] += dAqs[t * MS + o] * ko * E;
             }
-            if (j >= tl) {  // o = t >= i with i = this row: row i's sum
+            if (j >= x) {  // o = t >= i with i = this row: row i's sum
                 const float E = ex2(Go - Gt);
-                float y = dAqs[o * C + t] * Qs[o * 64 + cl];
-                if (j > tl) y += dMs[o * C + t] * Es[o * 64 + cl];
+                float y = dAqs[o * MS + t] * Qs[o * LS + cl];
+                if (j > x) y += dMs[o * MS + t] * Es[o * LS + cl];
                 sdk[x] += y * E;
             }
         }
     }
+    // ... then the other half's rows o: earlier tokens for half 1 (de, dqs of its
+    // rows), later ones for half 0 (dk of its rows).  Both sides are summed in
+    // every lane: dM, dA_qk are zero where a side does not apply (strictly lower /
+    // lower triangular), and e^{-|G_t - G_o|} is the decay factor of either side
+    // (G does not increase along the chunk).
+    {
+        const int ob = 16 * b + 8 * (1 - half);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int t = r0 + x;
+            const float Gt = Gs[t * LS + cl];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int o = ob + j;
+                const float E = ex2(-fabsf(Gt - Gs[o * LS + cl])), kE = Ks[o * LS + cl] * E;
+                sde[x] += dMs[t * MS + o] * kE;
+                sdq[x] += dAqs[t * MS + o] * kE;
+                sdk[x] += (dAqs[o * MS + t] * Qs[o * LS + cl] + dMs[o * MS + t] * Es[o * LS + cl]) * E;
+            }
+        }
+    }
 
-    // chain rule for the wave's rows
-    const float GC = Gs[(C - 1) * 64 + cl];
+    // chain rule for the lane's rows
+    const float GC = Gs[(C - 1) * LS + cl];
     float dG[8], de[8], dq[8], dk[8], sKK = 0.f, bsum = 0.f;
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
         const int t = r0 + x;
-        const float G = Gs[t * 64 + cl], eg = ex2(G), kg = ex2(GC - G);
+        const float G = Gs[t * LS + cl], eg = ex2(G), kg = ex2(GC - G);
         const float dEt = pdE[x], dQt = pdQ[x], dKh = pdK[x];
-        const float e = Es[t * 64 + cl], qs = Qs[t * 64 + cl], kk = Ks[t * 64 + cl];
+        const float e = Es[t * LS + cl], qs = Qs[t * LS + cl], kk = Ks[t * LS + cl];
         const float te = sde[x], tq = sdq[x], ik = sdk[x];
         de[x] = eg * dEt + te;
         dq[x] = eg * dQt + tq;
@@ -1244,14 +1291,14 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
         sKK += dKh * khv;
         bsum += dG[x];
     }
-    blk[w * 64 + cl] = bsum;
-    gcp[w * 64 + cl] = sKK;
+    blk[rg * LOCAL_CH + cl] = bsum;
+    gcp[rg * LOCAL_CH + cl] = sKK;
     __syncthreads();
     // dg_t = sum_{r >= t} dG_r; G_C (the last row) also enters through K-hat and gamma_C
     float carry = pgC * ex2(GC);
 #pragma unroll
-    for (int x = 0; x < NW; ++x) carry += gcp[x * 64 + cl];
-    for (int x = w + 1; x < NW; ++x) carry += blk[x * 64 + cl];
+    for (int x = 0; x < NRG; ++x) carry += gcp[x * LOCAL_CH + cl];
+    for (int x = rg + 1; x < NRG; ++x) carry += blk[x * LOCAL_CH + cl];
     float alsum = 0.f;
 #pragma unroll
     for (int x = 7; x >= 0; --x) {
@@ -1260,7 +1307,7 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
         if (t < L) {
             const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
             const float av = a_row[x], beta = beta_row[x];
-            const float kk = Ks[t * 64 + cl];
+            const float kk = Ks[t * LS + cl];
             const float dg = carry;  // natural-log units
             p.da[ka] = -dg * rate * sigmoid_fast(av);
             alsum += dg * (-rate * softplus_fast(av));
@@ -1269,40 +1316,45 @@ __global__ __launch_bounds__(LOCAL_NT) void g2b_local(Bwd2Args p, Bwd2Workspace 
             ws.dkh[ka] = dk[x] + de[x] * beta;
         }
     }
-    alp[w * 64 + cl] = alsum;
+    alp[rg * LOCAL_CH + cl] = alsum;
     __syncthreads();
-    if (w == 0) {
+    if (tid < LOCAL_CH) {
         float sa = 0.f;
 #pragma unroll
-        for (int x = 0; x < NW; ++x) sa += alp[x * 64 + cl];
+        for (int x = 0; x < NRG; ++x) sa += alp[x * LOCAL_CH + cl];
         ws.dAl[(size_t)u * DK + c] = sa;
     }
-    // dz = dR -> dv, d_write (the first channel group of each chunk)
-    if (cg == 0) {
+    // dz = dR -> dv, d_write for the group's share of the value columns
+    {
+        constexpr int DVG = DV / CG, ITEMS = C * DVG / 8, NIT = (ITEMS + LOCAL_NT - 1) / LOCAL_NT;
+        static_assert(DVG % 8 == 0, "value columns per channel group");
         const TIn *v = static_cast<const TIn *>(p.v), *wr = static_cast<const TIn *>(p.write);
         const float *dRu = ws.dR + (size_t)u * C * DV;
         // every load of the loop first (the stores to dv and d_write could alias them)
-        constexpr int NIT = C * DV / 8 / LOCAL_NT;
         In8<TIn> xv[NIT], xw[NIT];
         f4 dzl[NIT][2];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int i = tid + LOCAL_NT * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
-            const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
-            xv[it].load(v, kv);
-            xw[it].load(wr, kv);
-            dzl[it][0] = *reinterpret_cast<const f4 *>(dRu + t * DV + j);
-            dzl[it][1] = *reinterpret_cast<const f4 *>(dRu + t * DV + j + 4);
+            const int i = tid + LOCAL_NT * it, t = i / (DVG / 8), j = DVG * cg + (i % (DVG / 8)) * 8,
+                      tl = min(t, L - 1);
+            if (i < ITEMS) {
+                const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
+                xv[it].load(v, kv);
+                xw[it].load(wr, kv);
+                dzl[it][0] = *reinterpret_cast<const f4 *>(dRu + t * DV + j);
+                dzl[it][1] = *reinterpret_cast<const f4 *>(dRu + t * DV + j + 4);
+            }
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int i = tid + LOCAL_NT * it, t = i / (DV / 8), j = (i % (DV / 8)) * 8, tl = min(t, L - 1);
-            const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
-            f4 vv[2], om[2];
-            xv[it].get(vv[0], vv[1]);
-            xw[it].get(om[0], om[1]);
-            const f4 (&dz)[2] = dzl[it];
-            if (t < L) {
+            const int i = tid + LOCAL_NT * it, t = i / (DVG / 8), j = DVG * cg + (i % (DVG / 8)) * 8,
+                      tl = min(t, L - 1);
+            if (i < ITEMS && t < L) {
+                const size_t kv = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DV + j;
+                f4 vv[2], om[2];
+                xv[it].get(vv[0], vv[1]);
+                xw[it].get(om[0], om[1]);
+                const f4 (&dz)[2] = dzl[it];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     f4 o1, o2;
@@ -1376,7 +1428,7 @@ hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t
     rec(3);
     hipLaunchKernelGGL((g2b_products<TIn, DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
     rec(4);
-    hipLaunchKernelGGL((g2b_local<TIn, DK, DV>), dim3(units * (DK / 64)), dim3(LOCAL_NT), 0, s, p, ws);
+    hipLaunchKernelGGL((g2b_local<TIn, DK, DV>), dim3(units * (DK / LOCAL_CH)), dim3(LOCAL_NT), 0, s, p, ws);
     rec(5);
     const size_t nq = (size_t)p.B * p.T * p.Hk * DK / 256 + 1;
     hipLaunchKernelGGL((g2b_reduce<DK>), dim3((unsigned)(nq < 65536 ? nq : 65536)), dim3(256), 0, s, p, ws);
