@@ -164,6 +164,17 @@ template <int ROWS, int COLS, int NT = 256, int SS = COLS> struct RegTile {
     }
 };
 
+// work-group barrier for hand-offs through LDS only: each wave's LDS accesses
+// complete before it (lgkmcnt(0)), while its global loads and stores stay in
+// flight (__syncthreads() waits for those too, which drained every prefetch at
+// the next barrier)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // 2^x on the hardware unit (arguments here are <= 0: every decay factor is at most 1)
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -461,12 +472,12 @@ __device__ __forceinline__ void mma_x3(f4 &acc, const uint16_t *ah, const uint16
 }
 
 // A ROWS x COLS float32 register tile (see RegTile) stored split: rows of stride LS
-template <int ROWS, int COLS, int LS, int SS = COLS>
-__device__ __forceinline__ void store_split(const RegTile<ROWS, COLS, 256, SS> &t, uint16_t *hi, uint16_t *lo,
+template <int ROWS, int COLS, int LS, int SS = COLS, int NT = 256>
+__device__ __forceinline__ void store_split(const RegTile<ROWS, COLS, NT, SS> &t, uint16_t *hi, uint16_t *lo,
                                             float f = 1.f) {
 #pragma unroll
-    for (int j = 0; j < RegTile<ROWS, COLS, 256, SS>::PER; ++j) {
-        const int i = threadIdx.x + j * 256, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
+    for (int j = 0; j < RegTile<ROWS, COLS, NT, SS>::PER; ++j) {
+        const int i = threadIdx.x + j * NT, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
         u16x4 h, l;
         split4(t.x[j] * f, h, l);
         *reinterpret_cast<u16x4 *>(hi + r * LS + c) = h;
@@ -541,19 +552,19 @@ __device__ __forceinline__ void store_acc_t(f4 x, uint16_t *h, uint16_t *l, int 
 
 // ROWS x COLS float32 block (row-major, contiguous) into split LDS rows of stride LS,
 // times f; loads in batches of 8 per thread as lds_load.
-template <int ROWS, int COLS, int LS>
+template <int ROWS, int COLS, int LS, int NT = 256>
 __device__ __forceinline__ void lds_load_split(uint16_t *hi, uint16_t *lo, const float *__restrict__ src, float f = 1.f) {
-    constexpr int N = ROWS * COLS / 4, PER = N / 256, BT = PER < 8 ? PER : 8;
-    static_assert(N % 256 == 0 && PER % BT == 0, "block size");
+    constexpr int N = ROWS * COLS / 4, PER = N / NT, BT = PER < 8 ? PER : 8;
+    static_assert(N % NT == 0 && PER % BT == 0, "block size");
 #pragma unroll
     for (int b0 = 0; b0 < PER; b0 += BT) {
         f4 x[BT];
 #pragma unroll
         for (int j = 0; j < BT; ++j)
-            x[j] = *reinterpret_cast<const f4 *>(src + (size_t)(threadIdx.x + (b0 + j) * 256) * 4);
+            x[j] = *reinterpret_cast<const f4 *>(src + (size_t)(threadIdx.x + (b0 + j) * NT) * 4);
 #pragma unroll
         for (int j = 0; j < BT; ++j) {
-            const int i = threadIdx.x + (b0 + j) * 256, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
+            const int i = threadIdx.x + (b0 + j) * NT, r = i / (COLS / 4), c = (i % (COLS / 4)) * 4;
             u16x4 h, l;
             split4(x[j] * f, h, l);
             *reinterpret_cast<u16x4 *>(hi + r * LS + c) = h;
@@ -563,8 +574,10 @@ __device__ __forceinline__ void lds_load_split(uint16_t *hi, uint16_t *lo, const
 }
 
 // ---------------------------------------------------------------------------
-// g2b_fwd_scan: one work-group per (sequence, value head, 32 value columns);
-// wave w holds the state tiles (c-blocks 2w', j-blocks) as MFMA accumulators.
+// g2b_fwd_scan: one work-group of 8 waves per (sequence, value head, 32 value
+// columns) (two waves per SIMD: one alone left every latency of the chunk's
+// dependent products exposed); wave w holds state tiles as MFMA accumulators
+// and the R, U tile (row block w % 4, column block w / 4).
 // Its products take split operands.  LDS (16-bit elements, each split tile a
 // hi and a lo array): Et, Kh [C][DK], A [C][C], and the transposed S [32][DK],
 // R, U [32][C] of the chunk.
@@ -575,16 +588,36 @@ template <int DK> struct FwdScanLds {
                          R_ = S_ + 2 * 32 * SS, U_ = R_ + 2 * 32 * SU, END = U_ + 2 * 32 * SU;
 };
 
+constexpr int SCAN_NT = 512;
+
+// work-group -> (head = sequence * H_v + value head, column slice): work-group i runs on
+// XCD i % 8, so heads go eight at a time across the XCDs with the slices of each
+// (which read the same per-chunk tiles) on one of them
+__device__ __forceinline__ void scan_slice(int heads, int ns, int &head, int &js) {
+    const int full = heads / 8 * 8 * ns, i = (int)blockIdx.x;
+    if (i < full) {
+        const int j = i / 8;
+        head = 8 * (j / ns) + i % 8;
+        js = j % ns;
+    } else {
+        head = heads / 8 * 8 + (i - full) / ns;
+        js = (i - full) % ns;
+    }
+}
+
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws) {
+__global__ __launch_bounds__(SCAN_NT) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws) {
     typedef FwdScanLds<DK> FL;
-    constexpr int SK = FL::SK, SA = FL::SA, SS = FL::SS, SU = FL::SU, NS = DV / 32, NT = DK / 32;
+    constexpr int SK = FL::SK, SA = FL::SA, SS = FL::SS, SU = FL::SU, NS = DV / 32, NT = DK / 16 * 2 / (SCAN_NT / 64);
     __shared__ __attribute__((aligned(16))) uint16_t lds[FL::END];
     uint16_t *EH = lds + FL::E_, *EL = EH + C * SK, *KH = lds + FL::K_, *KL = KH + C * SK, *AH = lds + FL::A_,
              *AL = AH + C * SA, *SH = lds + FL::S_, *SL = SH + 32 * SS, *RH = lds + FL::R_, *RL = RH + 32 * SU,
              *UH = lds + FL::U_, *UL = UH + 32 * SU;
-    const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
+    int head, js;
+    scan_slice(p.B * p.Hv, NS, head, js);
+    const int hv = head % p.Hv, bb = head / p.Hv, j0 = 32 * js;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
+    const int rb = w & 3, ob = w >> 2;  // the wave's R, U tile: row block, column block
     // initial state: every load issued before any is used (one wait, not one per element)
     f4 S[NT];
     if (p.S0) {
@@ -607,20 +640,30 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
     // this lane's v and write-logit elements of chunk m (rows past T read the last
     // token and are zeroed at use): loaded one chunk ahead, raw, for z = sigmoid(write) v
     const TIn *vin = static_cast<const TIn *>(p.v), *win = static_cast<const TIn *>(p.write);
-    In1<TIn> zv[2][4], zw[2][4];
+    In1<TIn> zv[4], zw[4];
     auto load_z = [&](int m) {
         const int tm = m * C, Lm = min(C, p.T - tm);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int t = min(16 * w + 4 * gg + s, Lm - 1);
-                const size_t kv = (((size_t)bb * p.T + tm + t) * p.Hv + hv) * DV + j0 + 16 * jb + rr;
-                zv[jb][s].load(vin, kv);
-                zw[jb][s].load(win, kv);
-            }
+        for (int s = 0; s < 4; ++s) {
+            const int t = min(16 * rb + 4 * gg + s, Lm - 1);
+            const size_t kv = (((size_t)bb * p.T + tm + t) * p.Hv + hv) * DV + j0 + 16 * ob + rr;
+            zv[s].load(vin, kv);
+            zw[s].load(win, kv);
+        }
     };
-    if (NC > 0) load_z(0);
+    // the chunk's Et, Kh, A tiles: loaded a whole chunk ahead, into registers
+    RegTile<C, DK, SCAN_NT> tE, tK;
+    RegTile<C, C, SCAN_NT> tA;
+    auto load_tiles = [&](int m) {
+        const size_t um = unit_of(bb, hv, m, p.Hv, NC);
+        tE.load(ws.Et + um * C * DK);
+        tK.load(ws.Kh + um * C * DK);
+        tA.load(ws.A + um * C * C);
+    };
+    if (NC > 0) {
+        load_z(0);
+        load_tiles(0);
+    }
     for (int n = 0; n < NC; ++n) {
         const size_t u = unit_of(bb, hv, n, p.Hv, NC);
         float *Snu = ws.Sn + u * DK * DV;
@@ -632,51 +675,49 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
         }
         const float *gCu = ws.gC + u * DK;
         const int L = min(C, p.T - n * C);
-        float zr[2][4], gcr[NT][4];
+        float zr[4], gcr[NT][4];
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                zr[jb][s] = zv[jb][s].get() * sigmoid_fast(zw[jb][s].get()) * (16 * w + 4 * gg + s < L ? 1.f : 0.f);
+        for (int s = 0; s < 4; ++s)
+            zr[s] = zv[s].get() * sigmoid_fast(zw[s].get()) * (16 * rb + 4 * gg + s < L ? 1.f : 0.f);
 #pragma unroll
         for (int x = 0; x < NT; ++x)
 #pragma unroll
             for (int s = 0; s < 4; ++s) gcr[x][s] = gCu[16 * ((w * NT + x) >> 1) + 4 * gg + s];
-        lds_load_split<C, DK, SK>(EH, EL, ws.Et + u * C * DK);
-        lds_load_split<C, DK, SK>(KH, KL, ws.Kh + u * C * DK);
-        lds_load_split<C, C, SA>(AH, AL, ws.A + u * C * C);
-        // the next chunk's z inputs: issued after the tiles' loads (which wait for every
-        // load issued before them), in flight during this chunk's products
-        if (n + 1 < NC) load_z(n + 1);
-        __syncthreads();
-        // R = Z - Et S (rows of block w)
+        store_split<C, DK, SK>(tE, EH, EL);
+        store_split<C, DK, SK>(tK, KH, KL);
+        store_split<C, C, SA>(tA, AH, AL);
+        // the next chunk's inputs, in flight during this chunk's products
+        if (n + 1 < NC) {
+            load_z(n + 1);
+            load_tiles(n + 1);
+        }
+        lds_barrier();
+        // R = Z - Et S (the wave's tile)
         float *Ru = ws.R + u * C * DV, *Uu = ws.U + u * C * DV;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
+        {
             f4 acc = {0, 0, 0, 0};
 #pragma unroll
             for (int kb = 0; kb < DK / 16; kb += 2)
-                acc = x3_step<true, true>(acc, op_row<SK, true>(EH, EL, 16 * w, kb), op_row<SS, true>(SH, SL, 16 * jb, kb));
+                acc = x3_step<true, true>(acc, op_row<SK, true>(EH, EL, 16 * rb, kb), op_row<SS, true>(SH, SL, 16 * ob, kb));
             f4 rv;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) rv[s] = zr[jb][s] - acc[s];
-            store_acc_t<SU>(rv, RH, RL, w, jb);
+            for (int s = 0; s < 4; ++s) rv[s] = zr[s] - acc[s];
+            store_acc_t<SU>(rv, RH, RL, rb, ob);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) Ru[(16 * w + 4 * gg + s) * DV + j0 + 16 * jb + rr] = rv[s];
+            for (int s = 0; s < 4; ++s) Ru[(16 * rb + 4 * gg + s) * DV + j0 + 16 * ob + rr] = rv[s];
         }
-        __syncthreads();
+        lds_barrier();
         // U = A R
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
+        {
             f4 acc = {0, 0, 0, 0};
 #pragma unroll
             for (int kb = 0; kb < C / 16; kb += 2)
-                acc = x3_step<true, true>(acc, op_row<SA, true>(AH, AL, 16 * w, kb), op_row<SU, true>(RH, RL, 16 * jb, kb));
-            store_acc_t<SU>(acc, UH, UL, w, jb);
+                acc = x3_step<true, true>(acc, op_row<SA, true>(AH, AL, 16 * rb, kb), op_row<SU, true>(RH, RL, 16 * ob, kb));
+            store_acc_t<SU>(acc, UH, UL, rb, ob);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) Uu[(16 * w + 4 * gg + s) * DV + j0 + 16 * jb + rr] = acc[s];
+            for (int s = 0; s < 4; ++s) Uu[(16 * rb + 4 * gg + s) * DV + j0 + 16 * ob + rr] = acc[s];
         }
-        __syncthreads();
+        lds_barrier();
         // S = gamma_C . S + Kh^T U
 #pragma unroll
         for (int x = 0; x < NT; ++x) {
@@ -688,12 +729,13 @@ __global__ __launch_bounds__(256) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspace ws
                 S[x] = x3_step<true, true>(S[x], op_tr<SK, true>(KH, KL, 16 * cb, kb), op_row<SU, true>(UH, UL, 16 * jb, kb));
             store_acc_t<SS>(S[x], SH, SL, cb, jb);
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
 // ---------------------------------------------------------------------------
-// g2b_bwd_scan: the same slices, chunks in reverse; dS in MFMA accumulators.
+// g2b_bwd_scan: the same slices and waves, chunks in reverse; dS in MFMA
+// accumulators, the wave's dU, dR tile as in the forward scan.
 // ---------------------------------------------------------------------------
 // The reverse scan's products take split operands.  Its LDS (16-bit elements,
 // each split tile a hi and a lo array):
@@ -706,18 +748,21 @@ template <int DK> struct BwdScanLds {
 };
 
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws) {
+__global__ __launch_bounds__(SCAN_NT) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws) {
     typedef BwdScanLds<DK> BL;
     constexpr int SA = BL::SA, SK = BL::SK, SO = BL::SO, SS = BL::SS, SU = BL::SU;
-    constexpr int NS = DV / 32, NT = DK / 32;
+    constexpr int NS = DV / 32, NT = DK / 16 * 2 / (SCAN_NT / 64);
     constexpr bool DO_LO = !std::is_same<TIn, bf16_t>::value;  // dO is exact in bfloat16 for bf16 inputs
     __shared__ __attribute__((aligned(16))) uint16_t lds[BL::END];
     uint16_t *AH = lds + BL::A_, *AL = AH + C * SA, *K1H = lds + BL::K1_, *K1L = K1H + C * SK;
     uint16_t *K2H = lds + BL::K2_, *K2L = K2H + C * SK, *OH = lds + BL::O_, *OL = OH + C * SO;
     uint16_t *DSH = lds + BL::S_, *DSL = DSH + 32 * SS, *DUH = lds + BL::U_, *DUL = DUH + 32 * SU;
     uint16_t *DRH = lds + BL::R_, *DRL = DRH + 32 * SU;
-    const int js = blockIdx.x % NS, hv = (blockIdx.x / NS) % p.Hv, bb = blockIdx.x / (NS * p.Hv), j0 = 32 * js;
+    int head, js;
+    scan_slice(p.B * p.Hv, NS, head, js);
+    const int hv = head % p.Hv, bb = head / p.Hv, j0 = 32 * js;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4, NC = p.NC;
+    const int rb = w & 3, ob = w >> 2;  // the wave's dU, dR tile: row block, column block
     const TIn *dout = static_cast<const TIn *>(p.dout);
     // gradient of the final state: every load issued before any is used.  Wave w
     // holds the tiles (channel block cb, column block jb) id = w NT + x, cb = id / 2.
@@ -739,16 +784,18 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
         const int id = w * NT + x;
         store_acc_t<SS>(dS[x], DSH, DSL, id >> 1, id & 1);
     }
-    // dO slice of chunk n: 64 rows x 32 columns, 8 per thread (rows past T read the last
-    // token and are zeroed when stored)
-    const int ot = tid >> 2, oj = (tid & 3) * 8;
+    // dO slice of chunk n: 64 rows x 32 columns, 8 per thread of the first 256 (rows past T
+    // read the last token and are zeroed when stored)
+    const int ot = (tid & 255) >> 2, oj = (tid & 3) * 8;
+    const bool dot = tid < 256;
     auto load_do = [&](int n) {
         const int L = min(C, p.T - n * C), tl = min(ot, L - 1);
         In8<TIn> x;
-        x.load(dout, (((size_t)bb * p.T + n * C + tl) * p.Hv + hv) * DV + j0 + oj);
+        if (dot) x.load(dout, (((size_t)bb * p.T + n * C + tl) * p.Hv + hv) * DV + j0 + oj);
         return x;
     };
     auto store_do = [&](const In8<TIn> &x, int n) {
+        if (!dot) return;
         const int L = min(C, p.T - n * C);
         f4 lo, hi;
         x.get(lo, hi);
@@ -761,8 +808,8 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
             *reinterpret_cast<u16x8 *>(OL + ot * SO + oj) = u16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
     };
     // staged for the chunk about to run: A_qk, Kh, dO
-    RegTile<C, C> rAq, rA;
-    RegTile<C, DK> rKh, rQ, rE;
+    RegTile<C, C, SCAN_NT> rAq, rA;
+    RegTile<C, DK, SCAN_NT> rKh, rQ, rE;
     In8<TIn> rdo;
     {
         const size_t u = unit_of(bb, hv, NC - 1, p.Hv, NC);
@@ -772,6 +819,9 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
         store_split<C, C, SA>(rAq, AH, AL);
         store_split<C, DK, SK>(rKh, K1H, K1L);
         store_do(rdo, NC - 1);
+        rA.load(ws.A + u * C * C);
+        rQ.load(ws.Qt + u * C * DK);
+        rE.load(ws.Et + u * C * DK);
     }
     for (int n = NC - 1; n >= 0; --n) {
         const size_t u = unit_of(bb, hv, n, p.Hv, NC);
@@ -787,48 +837,46 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
         for (int x = 0; x < NT; ++x)
 #pragma unroll
             for (int s = 0; s < 4; ++s) gcr[x][s] = ws.gC[u * DK + 16 * ((w * NT + x) >> 1) + 4 * gg + s];
-        __syncthreads();
-        // this chunk's A, Qt, Et in flight while dU is computed
-        rA.load(ws.A + u * C * C);
-        rQ.load(ws.Qt + u * C * DK);
-        rE.load(ws.Et + u * C * DK);
-        // dU = Aq^T dO + Kh dS  (rows of block w)
+        lds_barrier();
+        // dU = Aq^T dO + Kh dS  (the wave's tile)
         float *dUu = ws.dU + u * C * DV, *dRu = ws.dR + u * C * DV;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
+        {
             f4 acc = {0, 0, 0, 0};
 #pragma unroll
             for (int kb = 0; kb < C / 16; kb += 2)
-                acc = x3_step<true, DO_LO>(acc, op_tr<SA, true>(AH, AL, 16 * w, kb), op_tr<SO, DO_LO>(OH, OL, 16 * jb, kb));
+                acc = x3_step<true, DO_LO>(acc, op_tr<SA, true>(AH, AL, 16 * rb, kb), op_tr<SO, DO_LO>(OH, OL, 16 * ob, kb));
 #pragma unroll
             for (int kb = 0; kb < DK / 16; kb += 2)
-                acc = x3_step<true, true>(acc, op_row<SK, true>(K1H, K1L, 16 * w, kb), op_row<SS, true>(DSH, DSL, 16 * jb, kb));
-            store_acc_t<SU>(acc, DUH, DUL, w, jb);
+                acc = x3_step<true, true>(acc, op_row<SK, true>(K1H, K1L, 16 * rb, kb), op_row<SS, true>(DSH, DSL, 16 * ob, kb));
+            store_acc_t<SU>(acc, DUH, DUL, rb, ob);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) dUu[(16 * w + 4 * gg + s) * DV + j0 + 16 * jb + rr] = acc[s];
+            for (int s = 0; s < 4; ++s) dUu[(16 * rb + 4 * gg + s) * DV + j0 + 16 * ob + rr] = acc[s];
         }
-        __syncthreads();
+        lds_barrier();
         store_split<C, C, SA>(rA, AH, AL);
         store_split<C, DK, SK>(rQ, K2H, K2L);
         store_split<C, DK, SK>(rE, K1H, K1L, -1.f);
-        // the next chunk's A_qk, Kh and dO in flight while this one finishes
+        // the next chunk's tiles in flight while this one finishes (A, Qt, Et a whole
+        // chunk ahead of their use)
         if (n > 0) {
             const size_t un = u - 1;
             rAq.load(ws.Aq + un * C * C);
             rKh.load(ws.Kh + un * C * DK);
             rdo = load_do(n - 1);
+            rA.load(ws.A + un * C * C);
+            rQ.load(ws.Qt + un * C * DK);
+            rE.load(ws.Et + un * C * DK);
         }
-        __syncthreads();
+        lds_barrier();
         // dR = A^T dU;  dS = gamma_C . dS + Qt^T dO
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
+        {
             f4 acc = {0, 0, 0, 0};
 #pragma unroll
             for (int kb = 0; kb < C / 16; kb += 2)
-                acc = x3_step<true, true>(acc, op_tr<SA, true>(AH, AL, 16 * w, kb), op_row<SU, true>(DUH, DUL, 16 * jb, kb));
-            store_acc_t<SU>(acc, DRH, DRL, w, jb);
+                acc = x3_step<true, true>(acc, op_tr<SA, true>(AH, AL, 16 * rb, kb), op_row<SU, true>(DUH, DUL, 16 * ob, kb));
+            store_acc_t<SU>(acc, DRH, DRL, rb, ob);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) dRu[(16 * w + 4 * gg + s) * DV + j0 + 16 * jb + rr] = acc[s];
+            for (int s = 0; s < 4; ++s) dRu[(16 * rb + 4 * gg + s) * DV + j0 + 16 * ob + rr] = acc[s];
         }
 #pragma unroll
         for (int x = 0; x < NT; ++x) {
@@ -839,7 +887,7 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
             for (int kb = 0; kb < C / 16; kb += 2)
                 dS[x] = x3_step<true, DO_LO>(dS[x], op_tr<SK, true>(K2H, K2L, 16 * cb, kb), op_tr<SO, DO_LO>(OH, OL, 16 * jb, kb));
         }
-        __syncthreads();
+        lds_barrier();
         // dS -= Et^T dR  (the Et tile holds -Et)
 #pragma unroll
         for (int x = 0; x < NT; ++x) {
@@ -849,7 +897,7 @@ __global__ __launch_bounds__(256) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspace ws
                 dS[x] = x3_step<true, true>(dS[x], op_tr<SK, true>(K1H, K1L, 16 * cb, kb), op_row<SU, true>(DRH, DRL, 16 * jb, kb));
             store_acc_t<SS>(dS[x], DSH, DSL, cb, jb);
         }
-        __syncthreads();
+        lds_barrier();
         if (n > 0) {
             store_split<C, C, SA>(rAq, AH, AL);
             store_split<C, DK, SK>(rKh, K1H, K1L);
@@ -963,9 +1011,9 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int st = s / NP, j0 = DH * (s % NP);
-        if (s > 0) __syncthreads();  // the previous step's products are done with the LDS
+        if (s > 0) lds_barrier();  // the previous step's products are done with the LDS
         store_step(s);
-        __syncthreads();
+        lds_barrier();
         if (s + 1 < NS) load_step(s + 1);
         if (s + 1 == NS) rA.load(ws.A + uC * C);
         if (st == 0) {
@@ -1034,7 +1082,7 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
                                          OL + 16 * ib * KP);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // X = A^T dA; dM = -strict_tril(X A^T), in float32
     float *f32s = reinterpret_cast<float *>(lds);
     float *dAs = f32s, *A80 = f32s + C * 80, *A68 = f32s + 2 * C * 80, *Xs = A68 + C * 68;
@@ -1044,7 +1092,7 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
         for (int x = 0; x < 4; ++x) dAs[(16 * w + 4 * gg + x) * 80 + 16 * ib + rr] = dA[ib][x];
     rA.template store<80>(A80);
     rA.template store<68>(A68);
-    __syncthreads();
+    lds_barrier();
     // X[i][s] = sum_t A[t][i] dA[t][s] (A[t][i] = 0 for t < i): rows i of block w
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
@@ -1056,7 +1104,7 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
     for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
         for (int x = 0; x < 4; ++x) Xs[(16 * w + 4 * gg + x) * 68 + 16 * sb + rr] = dA[sb][x];
-    __syncthreads();
+    lds_barrier();
     // dM[i][q] = -sum_s X[i][s] A[q][s] (A[q][s] = 0 for s > q), strictly lower
     float *dMu = ws.dM + uC * C;
     for (int qb = 0; qb < 4; ++qb) {
@@ -1422,9 +1470,9 @@ hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t
     rec(0);
     hipLaunchKernelGGL((g2b_prep<TIn, DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
     rec(1);
-    hipLaunchKernelGGL((g2b_fwd_scan<TIn, DK, DV>), dim3(slices), dim3(256), 0, s, p, ws);
+    hipLaunchKernelGGL((g2b_fwd_scan<TIn, DK, DV>), dim3(slices), dim3(SCAN_NT), 0, s, p, ws);
     rec(2);
-    hipLaunchKernelGGL((g2b_bwd_scan<TIn, DK, DV>), dim3(slices), dim3(256), 0, s, p, ws);
+    hipLaunchKernelGGL((g2b_bwd_scan<TIn, DK, DV>), dim3(slices), dim3(SCAN_NT), 0, s, p, ws);
     rec(3);
     hipLaunchKernelGGL((g2b_products<TIn, DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
     rec(4);
