@@ -686,10 +686,14 @@ __global__ __launch_bounds__(SCAN_NT) void g2b_fwd_scan(Bwd2Args p, Bwd2Workspac
         store_split<C, DK, SK>(tE, EH, EL);
         store_split<C, DK, SK>(tK, KH, KL);
         store_split<C, C, SA>(tA, AH, AL);
-        // the next chunk's inputs, in flight during this chunk's products
-        if (n + 1 < NC) {
-            load_z(n + 1);
-            load_tiles(n + 1);
+        // the next chunk's inputs, in flight during this chunk's products.  Issued on
+        // every chunk (the last one reloads itself, unused): behind a branch, the paths
+        // joined with different loads in flight and the compiler's wait at the join, for a
+        // value loaded before them, became a wait for every load, the prefetch included.
+        {
+            const int nn = min(n + 1, NC - 1);
+            load_z(nn);
+            load_tiles(nn);
         }
         lds_barrier();
         // R = Z - Et S (the wave's tile)
@@ -857,12 +861,14 @@ __global__ __launch_bounds__(SCAN_NT) void g2b_bwd_scan(Bwd2Args p, Bwd2Workspac
         store_split<C, DK, SK>(rQ, K2H, K2L);
         store_split<C, DK, SK>(rE, K1H, K1L, -1.f);
         // the next chunk's tiles in flight while this one finishes (A, Qt, Et a whole
-        // chunk ahead of their use)
-        if (n > 0) {
-            const size_t un = u - 1;
+        // chunk ahead of their use); issued on every chunk (chunk 0 reloads itself,
+        // unused), for the reason given in the forward scan
+        {
+            const int nn = max(n - 1, 0);
+            const size_t un = unit_of(bb, hv, nn, p.Hv, NC);
             rAq.load(ws.Aq + un * C * C);
             rKh.load(ws.Kh + un * C * DK);
-            rdo = load_do(n - 1);
+            rdo = load_do(nn);
             rA.load(ws.A + un * C * C);
             rQ.load(ws.Qt + un * C * DK);
             rE.load(ws.Et + un * C * DK);
