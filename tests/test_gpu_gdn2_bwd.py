@@ -83,6 +83,13 @@ def test_batch_and_key_head_groups():
     full_check(g2(B=2, T=130, Hk=2, Hv=6, Dk=128, Dv=128, seed=520, init_state=True))
 
 
+def test_work_group_mapping_tails_small_heads():
+    """d = 64 (two 32-channel groups per chunk in the local launch, two column slices per head
+    in the scans) with 9 value heads over 4 chunks: 36 chunk units and 9 heads, neither a
+    multiple of the 8 the launches group by, so both the grouped and the tail mappings run."""
+    full_check(g2(B=1, T=200, Hk=3, Hv=9, Dk=64, Dv=64, seed=524, init_state=True))
+
+
 def test_no_initial_state_no_final_gradient():
     full_check(g2(B=1, T=140, Hk=1, Hv=2, Dk=128, Dv=128, seed=521), d_state=False)
 
