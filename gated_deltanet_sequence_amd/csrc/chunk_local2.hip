@@ -65,8 +65,9 @@ size_t gdn2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, bool f32, voi
 
 template <int DK>
 struct Cl2Cfg {
+    static constexpr int NT = 512;                     // threads per work-group (8 waves)
     static constexpr int NKQ = DK / 32;                // 32-deep contraction steps over the key channels
-    static constexpr int NP = 256 / DK, LEN = C / NP;  // prefix-sum parts per channel, tokens per part
+    static constexpr int NP = NT / DK, LEN = C / NP;   // prefix-sum parts per channel, tokens per part
     // LDS: G (float) and e, k, q (float16) as [C][DK] row-major with the
     // 16-byte pieces of each row XOR-swizzled by the row (no padding): 80 KB
     // at DK = 128, so two work-groups share a compute unit.
@@ -112,7 +113,7 @@ template <int CTRL> __device__ __forceinline__ float quad_perm(float x) {
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
+__global__ __launch_bounds__(512, 4) void chunk_local2_kernel(
     int T, int Hk, int Hv, int NC, float scale, const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bf16_t *__restrict__ a, const bf16_t *__restrict__ erase, const float *__restrict__ A_log,
     _Float16 *__restrict__ eimg,
@@ -136,17 +137,17 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
     // ---- 1. gates and key-side operands of the chunk into LDS (zero past T)
     //         (z = sigmoid(write) v is formed by the scan's state waves).  Every
     //         load of the phase is issued before any arithmetic; a thread sees
-    //         the same 8 channels in each of its rows (256 is a multiple of
+    //         the same 8 channels in each of its rows (512 is a multiple of
     //         DK / 8), so their decay rates exp(A_log) are loaded once.  g is
     //         kept in log2 units (g log2 e) so that every decay is one exp2.
-    constexpr int PK = C * (DK / 8) / 256;
+    constexpr int NT = CF::NT, PK = C * (DK / 8) / NT;
     const int c8k = (tid % (DK / 8)) * 8;
     u16x8 rq[PK], rk[PK], ra[PK], re[PK];
     f4 Alo, Ahi;
     ld8(A_log, (size_t)hv * DK + c8k, Alo, Ahi);
 #pragma unroll
     for (int it = 0; it < PK; ++it) {
-        const int t = t0 + (tid + 256 * it) / (DK / 8);
+        const int t = t0 + (tid + NT * it) / (DK / 8);
         rq[it] = rk[it] = ra[it] = re[it] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
         if (t < T) {
             const size_t kq = (((size_t)bb * T + t) * Hk + hk) * DK + c8k;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
     for (int j = 0; j < 8; ++j) rate[j] = exp_fast(j < 4 ? Alo[j] : Ahi[j - 4]) * LOG2E;
 #pragma unroll
     for (int it = 0; it < PK; ++it) {
-        const int r = (tid + 256 * it) / (DK / 8), t = t0 + r;
+        const int r = (tid + NT * it) / (DK / 8), t = t0 + r;
         float gv[8];
         h8 eh, kh, qh;
 #pragma unroll
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
     //         columns lc .. lc+3 and lc+16 .. lc+19 (perm_col), lc = 32(P/4) + 4(P%4)
 #pragma unroll
     for (int it = 0; it < PK; ++it) {
-        const int idx = tid + 256 * it, r = idx / (DK / 8), P = idx % (DK / 8);
+        const int idx = tid + NT * it, r = idx / (DK / 8), P = idx % (DK / 8);
         const int lc = 32 * (P / 4) + 4 * (P % 4);
         h8 eo, ko, qo;
 #pragma unroll
@@ -241,11 +242,12 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
     //         once for its tiles: wave 0 (1,0) (it alone runs the inverse
     //         afterwards), wave 1 (2,0) (2,1), wave 2 (3,0) (3,1), wave 3 (3,2).
     //         The results stay in registers until the e/k/q space is free.
-    const int oI = w == 0 ? 1 : w == 1 ? 2 : 3, oJ0 = w == 3 ? 2 : 0, onj = (w == 1 || w == 2) ? 2 : 1;
+    const int wo = w - 4;  // waves 4..7 take the tiles below the diagonal, waves 0..3 the diagonal ones
+    const int oI = wo == 0 ? 1 : wo == 1 ? 2 : 3, oJ0 = wo == 3 ? 2 : 0, onj = (wo == 1 || wo == 2) ? 2 : 1;
     f4 oM[2], oQ[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) oM[h] = oQ[h] = f4{0, 0, 0, 0};
-    {
+    if (w >= 4) {
         const int ref = 16 * oI, tr = 16 * oI + m;
 #pragma unroll
         for (int kq = 0; kq < NKQ; ++kq) {
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
     //         One product per level and matrix; each level's accumulator keeps
     //         only its own pairs.  The diagonal of A_qk (no decay) is q.k.
     f4 dM = {0, 0, 0, 0}, dQ = {0, 0, 0, 0};
-    {
+    if (w < 4) {
         const int r0 = 16 * w, t = r0 + m;
         f4 aM[4], aQ[4];
 #pragma unroll
@@ -334,15 +336,18 @@ __global__ __launch_bounds__(256, 2) void chunk_local2_kernel(
             if (4 * g + s == m) dQ[s] += dq;
     }
     __syncthreads();  // G, e, k, q are dead: the tiles take their space
+    if (w >= 4) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        if (h < onj) {
-            *reinterpret_cast<f4 *>(Ms + tri_index(oI, oJ0 + h) * 256 + m * 16 + 4 * g) = oM[h];
-            *reinterpret_cast<f4 *>(Qs + tri_index(oI, oJ0 + h) * 256 + m * 16 + 4 * g) = oQ[h];
+        for (int h = 0; h < 2; ++h) {
+            if (h < onj) {
+                *reinterpret_cast<f4 *>(Ms + tri_index(oI, oJ0 + h) * 256 + m * 16 + 4 * g) = oM[h];
+                *reinterpret_cast<f4 *>(Qs + tri_index(oI, oJ0 + h) * 256 + m * 16 + 4 * g) = oQ[h];
+            }
         }
+    } else {
+        *reinterpret_cast<f4 *>(Ms + tri_index(w, w) * 256 + m * 16 + 4 * g) = dM;
+        *reinterpret_cast<f4 *>(Qs + tri_index(w, w) * 256 + m * 16 + 4 * g) = dQ;
     }
-    *reinterpret_cast<f4 *>(Ms + tri_index(w, w) * 256 + m * 16 + 4 * g) = dM;
-    *reinterpret_cast<f4 *>(Qs + tri_index(w, w) * 256 + m * 16 + 4 * g) = dQ;
     __syncthreads();
     if (w != 0) return;
 
@@ -414,7 +419,7 @@ template <int DK, int DV>
 static hipError_t launch_cl2_t(const Gdn2Args &p, const Gdn2Workspace &ws, hipStream_t s) {
     const int NC = (p.T + C - 1) / C;
     const unsigned units = (unsigned)(p.B * p.Hv * NC);
-    hipLaunchKernelGGL((chunk_local2_kernel<DK, DV>), dim3(units), dim3(256), 0, s, p.T, p.Hk, p.Hv, NC, p.scale,
+    hipLaunchKernelGGL((chunk_local2_kernel<DK, DV>), dim3(units), dim3(Cl2Cfg<DK>::NT), 0, s, p.T, p.Hk, p.Hv, NC, p.scale,
                        (const bf16_t *)p.q, (const bf16_t *)p.k, (const bf16_t *)p.a,
                        (const bf16_t *)p.erase, p.A_log, (_Float16 *)ws.eimg,
                        (_Float16 *)ws.khimg, (_Float16 *)ws.qimg, (_Float16 *)ws.apair, (_Float16 *)ws.qpair,
