@@ -1494,14 +1494,16 @@ hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t
 }  // namespace
 
 // Buffers whose lives do not overlap share memory.  Lives (W = written, R = read):
-//   A: prep W, fwd/bwd scans and products R;  Aq, Et, Qt, Kh, gC: prep W, scans R;
+//   A: prep W, fwd/bwd scans and products R (products last);  Aq, Et, Qt, Kh, gC: prep W, scans R;
 //   Sn, R, U: forward scan W, products R;
 //   dS1, dU: reverse scan W, products R;  dR: reverse scan W, products and local R;
 //   dEt, dQt, dKh, dgC, dAq, dM: products W, local R;  dqh, dkh, dAl: local W, reduce R.
 // So products writes into the space of buffers last read by the scans (dEt into Et, dQt
-// into Qt, dKh into Kh, dgC into gC, dAq into Aq; dM has its own), and local into the
-// space of buffers last read by products (dqh into Sn, dkh into dS1, dAl into U).  No
-// kernel reads a buffer whose space it writes through another name.
+// into Qt, dKh into Kh, dgC into gC, dAq into Aq) or by itself (dM into A: a work-group
+// reads its chunk's A before it writes that chunk's dM), and local into the
+// space of buffers last read by products (dqh into Sn, dkh into dS1, dAl into U).  The
+// only kernel that writes the space of a buffer it reads is products (dM over A), each
+// work-group in its own chunk's part, after its last read of it.
 size_t bwd2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, Bwd2Workspace *ws) {
     const size_t NC = ((size_t)T + C - 1) / C, U = (size_t)B * Hv * NC;
     size_t off = 0;
@@ -1511,13 +1513,12 @@ size_t bwd2_workspace_layout(int B, int T, int Hv, int Dk, int Dv, void *base, B
         return p;
     };
     Bwd2Workspace w{};
-    w.A = take(U * C * C);
+    w.A = w.dM = take(U * C * C);
     w.Aq = w.dAq = take(U * C * C);
     w.Et = w.dEt = take(U * C * Dk);
     w.Qt = w.dQt = take(U * C * Dk);
     w.Kh = w.dKh = take(U * C * Dk);
     w.gC = w.dgC = take(U * Dk);
-    w.dM = take(U * C * C);
     w.R = take(U * C * Dv);
     w.U = w.dAl = take(U * C * Dv);   // dAl: Dk per unit
     w.dU = take(U * C * Dv);
