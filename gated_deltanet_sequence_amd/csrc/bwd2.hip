@@ -183,13 +183,16 @@ __device__ __forceinline__ size_t unit_of(int bb, int hv, int n, int Hv, int NC)
 }
 
 // ---------------------------------------------------------------------------
-// g2b_prep: one work-group of 4 waves per (sequence, value head, chunk).  The
+// g2b_prep: one work-group of 8 waves per (sequence, value head, chunk).  The
 // key channels are taken 64 at a time (M, Aq and the diagonal of Aq are sums
-// over them, accumulated across the halves), so that the tiles take 74 KB of
-// LDS and two work-groups share a CU.
+// over them, accumulated across the halves), so that the tiles take 78 KB of
+// LDS and two work-groups share a CU (four waves per SIMD); waves 0..3 take the
+// diagonal tiles of M and Aq while waves 4..7 take those below the diagonal.
 // ---------------------------------------------------------------------------
+constexpr int PREP_NT = 512;
+
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
+__global__ __launch_bounds__(PREP_NT, 4) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     constexpr int DH = 64, NH = DK / DH;  // channels per pass, passes
     constexpr int LS = DH + 4;            // conflict-free for lanes (row = l%16, col = l/16)
     __shared__ __attribute__((aligned(16))) float sm[4 * C * LS + C];
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     //    the last token (L >= 1) and are zeroed, so every load is unconditional.  The in-chunk
     //    prefix of g is taken over the thread's rows, then the totals of the earlier row
     //    groups are added.  Both passes' loads are issued before any is used.
-    constexpr int NQ = DH / 4, NRG = 256 / NQ, RPT = C / NRG;
+    constexpr int NQ = DH / 4, NRG = PREP_NT / NQ, RPT = C / NRG;
     __shared__ float tot[NRG * DH];
     const int cq = (tid % NQ) * 4, rg = tid / NQ;
     In4<TIn> rk[NH][RPT], rq[NH][RPT], ra[NH][RPT], re[NH][RPT];
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
         // 3. images, gamma_C and the diagonal of Aq (q_t . k_t, no decay) for the pass's channels
         {
             const size_t ub = (size_t)u * C * DK + DH * h;
-            for (int i = tid; i < C * DH / 4; i += 256) {
+            for (int i = tid; i < C * DH / 4; i += PREP_NT) {
                 const int t = i / (DH / 4), c = (i % (DH / 4)) * 4;
                 const f4 G = *reinterpret_cast<const f4 *>(Gs + t * LS + c);
                 const f4 GC = *reinterpret_cast<const f4 *>(Gs + (C - 1) * LS + c);
@@ -291,19 +294,19 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
                 *reinterpret_cast<f4 *>(ws.Qt + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Qs + t * LS + c) * eg;
                 *reinterpret_cast<f4 *>(ws.Kh + ub + t * DK + c) = *reinterpret_cast<const f4 *>(Ks + t * LS + c) * kg;
             }
-            for (int c = tid; c < DH; c += 256) ws.gC[(size_t)u * DK + DH * h + c] = ex2(Gs[(C - 1) * LS + c]);
+            for (int c = tid; c < DH; c += PREP_NT) ws.gC[(size_t)u * DK + DH * h + c] = ex2(Gs[(C - 1) * LS + c]);
             if (tid < C) {
 #pragma unroll 8
                 for (int c = 0; c < DH; ++c) ddacc += Qs[tid * LS + c] * Ks[tid * LS + c];
             }
         }
         // 4. M and Aq over the pass's channels.  Tiles below the diagonal (bt > bi),
-        //    reference row r = 16 bt: sum_c [e_t e^{G_t - G_r}] [k_i e^{G_r - G_i}].  Wave w
-        //    takes tiles w, w + 4.
+        //    reference row r = 16 bt: sum_c [e_t e^{G_t - G_r}] [k_i e^{G_r - G_i}].  Waves
+        //    4..7 take tiles w - 4 and w (while waves 0..3 take the diagonal tiles).
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            const int ti = w + 4 * x;
-            if (ti < 6) {
+            const int ti = w - 4 + 4 * x;
+            if (w >= 4 && ti < 6) {
                 const int bt = obt(ti), bi = obi(ti), r = 16 * bt, t = 16 * bt + rr, i = 16 * bi + rr;
 #pragma unroll 8
                 for (int c0 = 0; c0 < DH; c0 += 4) {
@@ -315,10 +318,10 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
                 }
             }
         }
-        //    Diagonal tile w: dyadic levels (half sizes 8, 4, 2, 1); a pair (t > i) of
-        //    the tile belongs to the level whose 2h-block holds both with i in the
-        //    first and t in the second half; reference = first token of that half.
-        {
+        //    Diagonal tile w (waves 0..3): dyadic levels (half sizes 8, 4, 2, 1); a pair
+        //    (t > i) of the tile belongs to the level whose 2h-block holds both with i in
+        //    the first and t in the second half; reference = first token of that half.
+        if (w < 4) {
             const int base = 16 * w, t = base + rr, i = base + rr;
 #pragma unroll
             for (int hl = 8; hl >= 1; hl >>= 1) {
@@ -352,18 +355,20 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
     }
     if (tid < C) dd[tid] = ddacc;
     __syncthreads();  // Es, Qs, Ks are reused below; dd complete
+    if (w < 4) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        if (4 * gg + s == rr) qD[s] += dd[16 * w + rr];
+        for (int s = 0; s < 4; ++s)
+            if (4 * gg + s == rr) qD[s] += dd[16 * w + rr];
+    }
     // Aq to the workspace (zero above the diagonal); M into LDS (zero on and above)
     {
         float *Aqu = ws.Aq + (size_t)u * C * C;
-        for (int i = tid; i < C * 68; i += 256) Ms[i] = 0.f;
+        for (int i = tid; i < C * 68; i += PREP_NT) Ms[i] = 0.f;
         __syncthreads();
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            const int ti = w + 4 * x;
-            if (ti < 6) {
+            const int ti = w - 4 + 4 * x;
+            if (w >= 4 && ti < 6) {
                 const int bt = obt(ti), bi = obi(ti);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
@@ -374,18 +379,20 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
                 }
             }
         }
+        if (w < 4) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int t = 16 * w + 4 * gg + s, i = 16 * w + rr;
-            Ms[t * 68 + i] = mD[s];
-            Aqu[t * C + i] = qD[s];
+            for (int s = 0; s < 4; ++s) {
+                const int t = 16 * w + 4 * gg + s, i = 16 * w + rr;
+                Ms[t * 68 + i] = mD[s];
+                Aqu[t * C + i] = qD[s];
+            }
         }
     }
     __syncthreads();
     // 5. A = (I + M)^{-1}: diagonal 16 x 16 blocks by forward substitution (wave w,
     //    lane j < 16 owns column j of block w), then block rows 1..3:
     //    A_bj = -A_bb sum_{m=j}^{b-1} M_bm A_mj.
-    if (lane < 16) {
+    if (w < 4 && lane < 16) {
         const int base = 16 * w, j = lane;
         float x[16];
 #pragma unroll
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
         for (int t = 0; t < 16; ++t) As[(base + t) * 68 + base + j] = x[t];
     }
     // zero the blocks above the diagonal of A
-    for (int i = tid; i < C * C; i += 256) {
+    for (int i = tid; i < C * C; i += PREP_NT) {
         const int t = i / C, c = i % C;
         if ((c >> 4) > (t >> 4)) As[t * 68 + c] = 0.f;
     }
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(256) void g2b_prep(Bwd2Args p, Bwd2Workspace ws) {
         __syncthreads();
     }
     float *Au = ws.A + (size_t)u * C * C;
-    for (int i = tid; i < C * C / 4; i += 256) {
+    for (int i = tid; i < C * C / 4; i += PREP_NT) {
         const int t = i / (C / 4), c = (i % (C / 4)) * 4;
         *reinterpret_cast<f4 *>(Au + t * C + c) = *reinterpret_cast<const f4 *>(As + t * 68 + c);
     }
@@ -1474,7 +1481,7 @@ hipError_t launch_bwd2_t(const Bwd2Args &p, const Bwd2Workspace &ws, hipStream_t
         if (ev && e == hipSuccess) e = hipEventRecord(ev[i], s);
     };
     rec(0);
-    hipLaunchKernelGGL((g2b_prep<TIn, DK, DV>), dim3(units), dim3(256), 0, s, p, ws);
+    hipLaunchKernelGGL((g2b_prep<TIn, DK, DV>), dim3(units), dim3(PREP_NT), 0, s, p, ws);
     rec(1);
     hipLaunchKernelGGL((g2b_fwd_scan<TIn, DK, DV>), dim3(slices), dim3(SCAN_NT), 0, s, p, ws);
     rec(2);
