@@ -1132,22 +1132,24 @@ __global__ __launch_bounds__(256) void g2b_products(Bwd2Args p, Bwd2Workspace ws
 }
 
 // ---------------------------------------------------------------------------
-// g2b_local: one work-group of 4 waves per (chunk, 32 key channels), the
+// g2b_local: one work-group of 8 waves per (chunk, 32 key channels), the
 // channel groups of a chunk on one XCD (their reads of the chunk's dM and dA_qk
-// meet in its L2).  Wave w owns 16-token block b = w: first the block pairs
-// below the diagonal on the matrix cores for block b and both 16-channel tiles
-// (rows t of block b against every earlier block, rows i of block b against
-// every later block); then, lane = (channel, half of the block), the pairs
-// inside block b that its 8 rows take part in, on the vector unit; then the
-// chain rule for those rows.  73 KB of LDS: two work-groups share a CU.
+// meet in its L2).  Wave w owns 16-token block b = w / 2 and 16-channel tile
+// ct = w % 2, in the matrix-core accumulator layout throughout: lane (g, r)
+// holds tokens 16 b + 4 g + s (s = 0..3) of channel 16 ct + r.  First the
+// block pairs below the diagonal on the matrix cores (rows t of block b
+// against every earlier block, rows i of block b against every later block),
+// whose accumulators are then the lane's own sums; then the pairs inside block
+// b on the vector unit; then the chain rule.  76 KB of LDS and at most 128
+// registers: two work-groups share a CU at four waves per SIMD.
 // ---------------------------------------------------------------------------
-constexpr int LOCAL_NT = 256, LOCAL_CH = 32;
+constexpr int LOCAL_NT = 512, LOCAL_CH = 32;
 
 template <typename TIn, int DK, int DV>
-__global__ __launch_bounds__(LOCAL_NT, 2) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
-    constexpr int CG = DK / LOCAL_CH, NRG = 2 * (LOCAL_NT / 64);  // channel groups; row groups of 8 tokens
-    constexpr int LS = LOCAL_CH + 4;  // channel-tile row stride: the two half-waves' rows on disjoint banks
-    constexpr int MS = C + 4;         // dM / dA_qk row stride: conflict-free matrix-core A operands
+__global__ __launch_bounds__(LOCAL_NT, 4) void g2b_local(Bwd2Args p, Bwd2Workspace ws) {
+    constexpr int CG = DK / LOCAL_CH, NRG = C / 4;  // channel groups; row groups of 4 tokens
+    constexpr int LS = LOCAL_CH + 4;  // channel-tile row stride: a wave's 4 token groups on disjoint banks
+    constexpr int MS = C + 4;         // dM / dA_qk row stride
     __shared__ __attribute__((aligned(16))) float Gs[C * LS], Ks[C * LS], Es[C * LS], Qs[C * LS], dMs[C * MS],
         dAqs[C * MS], blk[NRG * LOCAL_CH], gcp[NRG * LOCAL_CH], alp[NRG * LOCAL_CH];
     // work-group -> (unit, channel group): work-group i runs on XCD i % 8, so units go
@@ -1167,8 +1169,8 @@ __global__ __launch_bounds__(LOCAL_NT, 2) void g2b_local(Bwd2Args p, Bwd2Workspa
     const int n = u % NC, hv = (u / NC) % p.Hv, bb = u / (NC * p.Hv), hk = hv / (p.Hv / p.Hk);
     const int t0 = n * C, L = min(C, p.T - t0);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, rr = lane & 15, gg = lane >> 4;
-    const int cl = lane & 31, half = lane >> 5, c = LOCAL_CH * cg + cl;
-    const int b = w, rg = 2 * w + half, r0 = 8 * rg;  // block, row group, first own row
+    const int b = w >> 1, ct = w & 1, cc = 16 * ct + rr, c = LOCAL_CH * cg + cc;
+    const int r0 = 16 * b + 4 * gg, rgi = 4 * b + gg;  // the lane's first token; its row group
     const TIn *q = static_cast<const TIn *>(p.q), *k = static_cast<const TIn *>(p.k);
     const TIn *a = static_cast<const TIn *>(p.a), *er = static_cast<const TIn *>(p.erase);
     const float Al = p.A_log[(size_t)hv * DK + c], rate = exp_fast(Al);
@@ -1178,12 +1180,12 @@ __global__ __launch_bounds__(LOCAL_NT, 2) void g2b_local(Bwd2Args p, Bwd2Workspa
     rM.load(ws.dM + (size_t)u * C * C);
     rAq.load(ws.dAq + (size_t)u * C * C);
 
-    // gates of the lane's rows; the in-chunk prefix of g runs over them, then the
-    // totals of the earlier row groups are added
-    // (the logits a and the erase gate stay in registers for the chain rule)
-    float grun = 0.f, gpre[8], a_row[8], beta_row[8];
+    // gates of the lane's tokens; the in-chunk prefix of g runs over them, then the
+    // totals of the earlier row groups are added (the logits a and the erase gate
+    // stay in registers for the chain rule)
+    float grun = 0.f, gpre[4], a_row[4], beta_row[4];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int x = 0; x < 4; ++x) {
         const int t = r0 + x, tl = min(t, L - 1);
         const size_t kq = (((size_t)bb * p.T + t0 + tl) * p.Hk + hk) * DK + c;
         const size_t ka = (((size_t)bb * p.T + t0 + tl) * p.Hv + hv) * DK + c;
@@ -1192,157 +1194,118 @@ __global__ __launch_bounds__(LOCAL_NT, 2) void g2b_local(Bwd2Args p, Bwd2Workspa
         a_row[x] = io<TIn>::ld(a, ka);
         beta_row[x] = sigmoid_fast(io<TIn>::ld(er, ka));
         grun += -rate * softplus_fast(a_row[x]) * LOG2E * on;
-        const float ev = beta_row[x] * kv;
-        const float qv = p.scale * io<TIn>::ld(q, kq) * on;
         gpre[x] = grun;
-        Ks[t * LS + cl] = kv;
-        Es[t * LS + cl] = ev;
-        Qs[t * LS + cl] = qv;
+        Ks[t * LS + cc] = kv;
+        Es[t * LS + cc] = beta_row[x] * kv;
+        Qs[t * LS + cc] = p.scale * io<TIn>::ld(q, kq) * on;
     }
-    blk[rg * LOCAL_CH + cl] = grun;
+    blk[rgi * LOCAL_CH + cc] = grun;
     rM.template store<MS>(dMs);
     rAq.template store<MS>(dAqs);
     __syncthreads();
     {
         float off = 0.f;
-        for (int x = 0; x < rg; ++x) off += blk[x * LOCAL_CH + cl];
+        for (int x = 0; x < rgi; ++x) off += blk[x * LOCAL_CH + cc];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) Gs[(r0 + x) * LS + cl] = gpre[x] + off;
+        for (int x = 0; x < 4; ++x) Gs[(r0 + x) * LS + cc] = gpre[x] + off;
     }
     __syncthreads();
 
-    // block pairs below the diagonal, 16 channels at a time (MFMA: lane supplies
-    // A[rr][gg], B[gg][rr]; accumulator element s is row 4 gg + s, channel rr).
-    //   rows t of block b, reference r = 16 b (i < r <= t):
-    //     de_t  = e^{G_t - G_r} sum_{i < r} dM_ti  k_i e^{G_r - G_i}, dqs_t likewise with dAq
-    //   rows i of block b, each later block b2 with reference r = 16 b2:
-    //     dk_i += e^{G_r - G_i} sum_{t in b2} dM_ti e_t e^{G_t - G_r} + dAq_ti qs_t e^{G_t - G_r}
-    // each tile's sums go to lane = (channel, half) as soon as they are complete: row
-    // 16 b + 8 half + x of channel cl is element x % 4 of tile cl / 16 in lane
-    // 16 (2 half + x / 4) + cl % 16
-    float sde[8], sdq[8], sdk[8];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        const int cc = 16 * ct + rr;
-        f4 e4 = {0, 0, 0, 0}, q4 = {0, 0, 0, 0}, k4 = {0, 0, 0, 0};
-        if (b > 0) {
-            const int r = 16 * b;
-            const float Gr = Gs[r * LS + cc];
-            // kept rolled: unrolled by whole 16-row blocks it measured slower
-#pragma unroll 1
-            for (int i0 = 0; i0 < r; i0 += 4) {
-                const int i = i0 + gg;
-                const float bv = Ks[i * LS + cc] * ex2(Gr - Gs[i * LS + cc]);
-                e4 = mfma_f32_k4(dMs[(r + rr) * MS + i], bv, e4);
-                q4 = mfma_f32_k4(dAqs[(r + rr) * MS + i], bv, q4);
-            }
-        }
-        for (int b2 = b + 1; b2 < 4; ++b2) {
-            const int r = 16 * b2;
-            const float Gr = Gs[r * LS + cc];
-            f4 acc = {0, 0, 0, 0};
-#pragma unroll
-            for (int k0 = 0; k0 < 16; k0 += 4) {
-                const int t = r + k0 + gg;
-                const float f = ex2(Gs[t * LS + cc] - Gr);
-                acc = mfma_f32_k4(dMs[t * MS + 16 * b + rr], Es[t * LS + cc] * f, acc);
-                acc = mfma_f32_k4(dAqs[t * MS + 16 * b + rr], Qs[t * LS + cc] * f, acc);
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int i = 16 * b + 4 * gg + s;
-                k4[s] += acc[s] * ex2(Gr - Gs[i * LS + cc]);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int t = 16 * b + 4 * gg + s;
-            const float F = b > 0 ? ex2(Gs[t * LS + cc] - Gs[16 * b * LS + cc]) : 0.f;
-            e4[s] *= F;
-            q4[s] *= F;
-        }
-        const bool mine = (cl >> 4) == ct;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            const int src = 4 * (16 * (2 * half + (x >> 2)) + (cl & 15)), s = x & 3;
-            auto take = [&](float v) {
-                return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
-            };
-            const float ve = take(e4[s]), vq = take(q4[s]), vk = take(k4[s]);
-            if (ct == 0 || mine) {
-                sde[x] = ve;
-                sdq[x] = vq;
-                sdk[x] = vk;
-            }
-        }
-    }
-
-    // inputs of the chain rule, loaded here so that their latency overlaps the pair sums
+    // inputs of the chain rule, in flight during the pair sums
     const size_t ub = (size_t)u * C * DK;
-    float pdE[8], pdQ[8], pdK[8];
+    float pdE[4], pdQ[4], pdK[4];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int x = 0; x < 4; ++x) {
         pdE[x] = ws.dEt[ub + (r0 + x) * DK + c];
         pdQ[x] = ws.dQt[ub + (r0 + x) * DK + c];
         pdK[x] = ws.dKh[ub + (r0 + x) * DK + c];
     }
     const float pgC = ws.dgC[(size_t)u * DK + c];
 
-    // pairs inside block b that the lane's rows take part in (lane = channel):
-    // E = e^{G_t - G_i}, i <= t.  First the 8 x 8 sub-block of the lane's own half
-    // (as t the rows r0.., as i the same rows) ...
+    // block pairs below the diagonal (MFMA: lane supplies A[rr][gg], B[gg][rr]; the
+    // accumulator element s is token 16 b + 4 gg + s, channel cc):
+    //   rows t of block b, reference r = 16 b (i < r <= t):
+    //     de_t  = e^{G_t - G_r} sum_{i < r} dM_ti  k_i e^{G_r - G_i}, dqs_t likewise with dAq
+    //   rows i of block b, each later block b2 with reference r = 16 b2:
+    //     dk_i += e^{G_r - G_i} sum_{t in b2} dM_ti e_t e^{G_t - G_r} + dAq_ti qs_t e^{G_t - G_r}
+    f4 sde = {0, 0, 0, 0}, sdq = {0, 0, 0, 0}, sdk = {0, 0, 0, 0};
+    if (b > 0) {
+        const int r = 16 * b;
+        const float Gr = Gs[r * LS + cc];
+        // kept rolled: unrolled by whole 16-row blocks it measured slower
+#pragma unroll 1
+        for (int i0 = 0; i0 < r; i0 += 4) {
+            const int i = i0 + gg;
+            const float bv = Ks[i * LS + cc] * ex2(Gr - Gs[i * LS + cc]);
+            sde = mfma_f32_k4(dMs[(r + rr) * MS + i], bv, sde);
+            sdq = mfma_f32_k4(dAqs[(r + rr) * MS + i], bv, sdq);
+        }
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-        const int t = r0 + x;
-        const float Gt = Gs[t * LS + cl];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int o = r0 + j;
-            const float Go = Gs[o * LS + cl];
-            if (j <= x) {  // o = i <= t: row t's sums
-                const float E = ex2(Gt - Go), ko = Ks[o * LS + cl];
-                if (j < x) sde[x] += dMs[t * MS + o] * ko * E;
-                sdq[x] += dAqs[t * MS + o] * ko * E;
-            }
-            if (j >= x) {  // o = t >= i with i = this row: row i's sum
-                const float E = ex2(Go - Gt);
-                float y = dAqs[o * MS + t] * Qs[o * LS + cl];
-                if (j > x) y += dMs[o * MS + t] * Es[o * LS + cl];
-                sdk[x] += y * E;
-            }
+        for (int s = 0; s < 4; ++s) {
+            const float F = ex2(Gs[(r0 + s) * LS + cc] - Gr);
+            sde[s] *= F;
+            sdq[s] *= F;
         }
     }
-    // ... then the other half's rows o: earlier tokens for half 1 (de, dqs of its
-    // rows), later ones for half 0 (dk of its rows).  Both sides are summed in
-    // every lane: dM, dA_qk are zero where a side does not apply (strictly lower /
-    // lower triangular), and e^{-|G_t - G_o|} is the decay factor of either side
-    // (G does not increase along the chunk).
+    for (int b2 = b + 1; b2 < 4; ++b2) {
+        const int r = 16 * b2;
+        const float Gr = Gs[r * LS + cc];
+        f4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+            const int t = r + k0 + gg;
+            const float f = ex2(Gs[t * LS + cc] - Gr);
+            acc = mfma_f32_k4(dMs[t * MS + 16 * b + rr], Es[t * LS + cc] * f, acc);
+            acc = mfma_f32_k4(dAqs[t * MS + 16 * b + rr], Qs[t * LS + cc] * f, acc);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sdk[s] += acc[s] * ex2(Gr - Gs[(r0 + s) * LS + cc]);
+    }
+
+    // pairs inside block b, for each of the lane's tokens t and every token o of the
+    // block: as t (o <= t) the de, dqs sums, as i (o >= t) the dk sum.  Both sides are
+    // summed for every pair: dM (strictly lower) and dA_qk (lower) are zero where a side
+    // does not apply, and e^{-|G_t - G_o|} is the decay factor of either side (G does
+    // not increase along the chunk).  dM[o][t..t+3], dA_qk[o][t..t+3]: one read each.
     {
-        const int ob = 16 * b + 8 * (1 - half);
+        float Gt[4];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            const int t = r0 + x;
-            const float Gt = Gs[t * LS + cl];
+        for (int s = 0; s < 4; ++s) Gt[s] = Gs[(r0 + s) * LS + cc];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int o = ob + j;
-                const float E = ex2(-fabsf(Gt - Gs[o * LS + cl])), kE = Ks[o * LS + cl] * E;
-                sde[x] += dMs[t * MS + o] * kE;
-                sdq[x] += dAqs[t * MS + o] * kE;
-                sdk[x] += (dAqs[o * MS + t] * Qs[o * LS + cl] + dMs[o * MS + t] * Es[o * LS + cl]) * E;
+        for (int j0 = 0; j0 < 16; j0 += 4) {
+            const int o0 = 16 * b + j0;
+            f4 mt[4], qt[4];  // dM[t][o0..o0+3], dA_qk[t][o0..o0+3] for the lane's tokens t
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                mt[s] = *reinterpret_cast<const f4 *>(dMs + (r0 + s) * MS + o0);
+                qt[s] = *reinterpret_cast<const f4 *>(dAqs + (r0 + s) * MS + o0);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int o = o0 + jj;
+                const float Go = Gs[o * LS + cc], ko = Ks[o * LS + cc], qo = Qs[o * LS + cc], eo = Es[o * LS + cc];
+                const f4 mo = *reinterpret_cast<const f4 *>(dMs + o * MS + r0);   // dM[o][t]
+                const f4 qq = *reinterpret_cast<const f4 *>(dAqs + o * MS + r0);  // dA_qk[o][t]
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const float E = ex2(-fabsf(Gt[s] - Go)), kE = ko * E;
+                    sde[s] += mt[s][jj] * kE;
+                    sdq[s] += qt[s][jj] * kE;
+                    sdk[s] += (qq[s] * qo + mo[s] * eo) * E;
+                }
             }
         }
     }
 
-    // chain rule for the lane's rows
-    const float GC = Gs[(C - 1) * LS + cl];
-    float dG[8], de[8], dq[8], dk[8], sKK = 0.f, bsum = 0.f;
+    // chain rule for the lane's tokens
+    const float GC = Gs[(C - 1) * LS + cc];
+    float dG[4], de[4], dq[4], dk[4], sKK = 0.f, bsum = 0.f;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int x = 0; x < 4; ++x) {
         const int t = r0 + x;
-        const float G = Gs[t * LS + cl], eg = ex2(G), kg = ex2(GC - G);
+        const float G = Gs[t * LS + cc], eg = ex2(G), kg = ex2(GC - G);
         const float dEt = pdE[x], dQt = pdQ[x], dKh = pdK[x];
-        const float e = Es[t * LS + cl], qs = Qs[t * LS + cl], kk = Ks[t * LS + cl];
+        const float e = Es[t * LS + cc], qs = Qs[t * LS + cc], kk = Ks[t * LS + cc];
         const float te = sde[x], tq = sdq[x], ik = sdk[x];
         de[x] = eg * dEt + te;
         dq[x] = eg * dQt + tq;
@@ -1352,23 +1315,23 @@ __global__ __launch_bounds__(LOCAL_NT, 2) void g2b_local(Bwd2Args p, Bwd2Workspa
         sKK += dKh * khv;
         bsum += dG[x];
     }
-    blk[rg * LOCAL_CH + cl] = bsum;
-    gcp[rg * LOCAL_CH + cl] = sKK;
+    blk[rgi * LOCAL_CH + cc] = bsum;
+    gcp[rgi * LOCAL_CH + cc] = sKK;
     __syncthreads();
     // dg_t = sum_{r >= t} dG_r; G_C (the last row) also enters through K-hat and gamma_C
     float carry = pgC * ex2(GC);
 #pragma unroll
-    for (int x = 0; x < NRG; ++x) carry += gcp[x * LOCAL_CH + cl];
-    for (int x = rg + 1; x < NRG; ++x) carry += blk[x * LOCAL_CH + cl];
+    for (int x = 0; x < NRG; ++x) carry += gcp[x * LOCAL_CH + cc];
+    for (int x = rgi + 1; x < NRG; ++x) carry += blk[x * LOCAL_CH + cc];
     float alsum = 0.f;
 #pragma unroll
-    for (int x = 7; x >= 0; --x) {
+    for (int x = 3; x >= 0; --x) {
         carry += dG[x];
         const int t = r0 + x;
         if (t < L) {
             const size_t ka = (((size_t)bb * p.T + t0 + t) * p.Hv + hv) * DK + c;
             const float av = a_row[x], beta = beta_row[x];
-            const float kk = Ks[t * LS + cl];
+            const float kk = Ks[t * LS + cc];
             const float dg = carry;  // natural-log units
             p.da[ka] = -dg * rate * sigmoid_fast(av);
             alsum += dg * (-rate * softplus_fast(av));
@@ -1377,13 +1340,13 @@ __global__ __launch_bounds__(LOCAL_NT, 2) void g2b_local(Bwd2Args p, Bwd2Workspa
             ws.dkh[ka] = dk[x] + de[x] * beta;
         }
     }
-    alp[rg * LOCAL_CH + cl] = alsum;
+    alp[rgi * LOCAL_CH + cc] = alsum;
     __syncthreads();
     if (tid < LOCAL_CH) {
         float sa = 0.f;
 #pragma unroll
-        for (int x = 0; x < NRG; ++x) sa += alp[x * LOCAL_CH + cl];
-        ws.dAl[(size_t)u * DK + c] = sa;
+        for (int x = 0; x < NRG; ++x) sa += alp[x * LOCAL_CH + tid];
+        ws.dAl[(size_t)u * DK + LOCAL_CH * cg + tid] = sa;
     }
     // dz = dR -> dv, d_write for the group's share of the value columns
     {
